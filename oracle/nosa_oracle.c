@@ -1,0 +1,231 @@
+/*
+ * NOSA decode-step oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this library. The GPU path neither links
+ * nor calls it, and it shares no code with the GPU path.
+ *
+ * Plain, single-threaded fp64 loops. Inputs arrive as float32 arrays whose
+ * values are the exact input values (bfloat16 inputs are bfloat16-exact
+ * float32); every arithmetic step below is done in double and nothing is
+ * rounded back. It follows "NOSA: Native and Offloadable Sparse Attention"
+ * (technical summary pages, section Methodology, subsection "1. Algorithm:
+ * NOSA"), step by step, for one row = one (batch, KV head) pair:
+ *
+ *   pooling      two-stage pooling: mean inside each sub-block, then max over
+ *                the block's sub-blocks (bullet "Block-Wise Implementation");
+ *   Gamma_e      query-agnostic selection of k_e blocks by their pooled,
+ *                pre-exponential eviction scores (bullets "Dual-Selection
+ *                Mechanism" and "ED-DMA"); with static per-token scores and
+ *                a candidate set that only grows, the k_e greatest candidates
+ *                are exactly what a never-readmit eviction policy keeps, so
+ *                the oracle uses that stateless definition;
+ *   Gamma_q      the k_q greatest of the remaining candidates by the
+ *                query-aware pooled score (same bullet, "Query-Aware
+ *                Selection");
+ *   attention    plain softmax over the tokens of the selected blocks plus the
+ *                newest (partial) block, with the eviction score added to the
+ *                logit so that its exponential happens only in the softmax
+ *                (bullet "ED-DMA").
+ *
+ * Readings of points the pages leave open (the group of G query heads sums
+ * its per-head block scores; per-head max over sub-blocks comes before that
+ * sum; scores are scaled by `scale` with no softmax; the newest block is
+ * always attended and is not a candidate; equal scores rank the lower block
+ * index first) are listed in the repository's design notes.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Sub-block mean of keys: kbar[i*D + d] = mean over the `sub` tokens of
+   sub-block i of block j of K[token][d]; K is [tokens][D] with row stride D. */
+void oracle_pool_keys(const float *K, int D, int block, int sub, int j, double *kbar)
+{
+    int m = block / sub;
+    for (int i = 0; i < m; ++i) {
+        for (int d = 0; d < D; ++d) {
+            double s = 0.0;
+            for (int u = 0; u < sub; ++u)
+                s += (double)K[(int64_t)(j * block + i * sub + u) * D + d];
+            kbar[i * D + d] = s / (double)sub;
+        }
+    }
+}
+
+/* Pooled eviction score of block j: max over its sub-blocks of the mean of
+   the per-token (pre-exponential) eviction scores. */
+double oracle_block_evict(const float *e, int block, int sub, int j)
+{
+    int m = block / sub;
+    double best = -INFINITY;
+    for (int i = 0; i < m; ++i) {
+        double s = 0.0;
+        for (int u = 0; u < sub; ++u)
+            s += (double)e[j * block + i * sub + u];
+        double mean = s / (double)sub;
+        if (mean > best)
+            best = mean;
+    }
+    return best;
+}
+
+/* Query-aware pooled score of block j for a group of G query heads q[h][D]:
+   sum over heads of (max over sub-blocks of scale * q_h . kbar_i). */
+double oracle_block_score(const float *q, int G, int D, const float *K, int block, int sub,
+                          int j, double scale)
+{
+    int m = block / sub;
+    double *kbar = (double *)malloc(sizeof(double) * (size_t)m * (size_t)D);
+    oracle_pool_keys(K, D, block, sub, j, kbar);
+    double total = 0.0;
+    for (int h = 0; h < G; ++h) {
+        double best = -INFINITY;
+        for (int i = 0; i < m; ++i) {
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d)
+                dot += (double)q[h * D + d] * kbar[i * D + d];
+            double a = scale * dot;
+            if (a > best)
+                best = a;
+        }
+        total += best;
+    }
+    free(kbar);
+    return total;
+}
+
+/* a ranks above b: greater score, or equal score and lower index. */
+static int ranks_above(const double *x, int a, int b)
+{
+    return x[a] > x[b] || (x[a] == x[b] && a < b);
+}
+
+/* The k greatest of the allowed indices 0..n-1 under the order above, by
+   repeated selection of the best remaining one. Writes them to out[] in
+   ascending index order and returns how many there are (min(k, #allowed)).
+   allowed == NULL allows every index. */
+int oracle_topk(const double *x, const unsigned char *allowed, int n, int k, int *out)
+{
+    unsigned char *taken = (unsigned char *)calloc((size_t)(n > 0 ? n : 1), 1);
+    int cnt = 0;
+    for (int r = 0; r < k; ++r) {
+        int best = -1;
+        for (int j = 0; j < n; ++j) {
+            if ((allowed && !allowed[j]) || taken[j])
+                continue;
+            if (best < 0 || ranks_above(x, j, best))
+                best = j;
+        }
+        if (best < 0)
+            break;
+        taken[best] = 1;
+        ++cnt;
+    }
+    int w = 0;
+    for (int j = 0; j < n; ++j)
+        if (taken[j])
+            out[w++] = j;
+    free(taken);
+    return cnt;
+}
+
+/* Softmax attention of G query heads over an explicit token list.
+   z_i = scale * q_h . K[tok_i] + e[tok_i]; out[h] = sum_i softmax(z)_i V[tok_i].
+   The eviction score enters as an additive logit, so its exponential is taken
+   only inside the softmax. Tokens are visited in the order given. */
+void oracle_attend_tokens(const float *q, int G, int D, const float *K, const float *V,
+                          const float *e, const int *tok, int n_tok, double scale, double *out)
+{
+    double *z = (double *)malloc(sizeof(double) * (size_t)(n_tok > 0 ? n_tok : 1));
+    for (int h = 0; h < G; ++h) {
+        double mx = -INFINITY;
+        for (int i = 0; i < n_tok; ++i) {
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d)
+                dot += (double)q[h * D + d] * (double)K[(int64_t)tok[i] * D + d];
+            z[i] = scale * dot + (e ? (double)e[tok[i]] : 0.0);
+            if (z[i] > mx)
+                mx = z[i];
+        }
+        double den = 0.0;
+        for (int i = 0; i < n_tok; ++i) {
+            z[i] = exp(z[i] - mx);
+            den += z[i];
+        }
+        for (int d = 0; d < D; ++d) {
+            double num = 0.0;
+            for (int i = 0; i < n_tok; ++i)
+                num += z[i] * (double)V[(int64_t)tok[i] * D + d];
+            out[h * D + d] = num / den;
+        }
+    }
+    free(z);
+}
+
+/* One decode step for one row.
+ *
+ * n_tokens tokens exist (the newest one was appended this step). Candidate
+ * blocks are 0..c-1 with c = (n_tokens - 1) / block; block c holds tokens
+ * [c*block, n_tokens) and is always attended.
+ *
+ * Inputs: q [G][D], K and V [>= n_tokens][D], e [>= n_tokens].
+ * Outputs: ge[] (Gamma_e, ascending, returns its size in *n_ge), gq[]
+ * (Gamma_q, ascending, *n_gq), out [G][D]; E[c] and S[c] receive every
+ * candidate's pooled eviction and query-aware scores when not NULL.
+ * Returns c. */
+int oracle_step_row(int n_tokens, int G, int D, int block, int sub, int k_e, int k_q,
+                    double scale, const float *q, const float *K, const float *V,
+                    const float *e, int *ge, int *n_ge, int *gq, int *n_gq, double *out,
+                    double *E, double *S)
+{
+    int c = (n_tokens - 1) / block;
+    int cc = c > 0 ? c : 1;
+    double *Eb = (double *)malloc(sizeof(double) * (size_t)cc);
+    double *Sb = (double *)malloc(sizeof(double) * (size_t)cc);
+    unsigned char *rest = (unsigned char *)malloc((size_t)cc);
+
+    for (int j = 0; j < c; ++j) {
+        Eb[j] = oracle_block_evict(e, block, sub, j);
+        Sb[j] = oracle_block_score(q, G, D, K, block, sub, j, scale);
+    }
+
+    /* Gamma_e: the k_e greatest candidates by pooled eviction score. */
+    *n_ge = oracle_topk(Eb, NULL, c, k_e, ge);
+
+    /* Gamma_q: the k_q greatest of the candidates outside Gamma_e. */
+    for (int j = 0; j < c; ++j)
+        rest[j] = 1;
+    for (int i = 0; i < *n_ge; ++i)
+        rest[ge[i]] = 0;
+    *n_gq = oracle_topk(Sb, rest, c, k_q, gq);
+
+    /* Tokens attended: every token of every selected block, ascending, then
+       the newest block's tokens. */
+    unsigned char *pick = (unsigned char *)calloc((size_t)cc, 1);
+    for (int i = 0; i < *n_ge; ++i)
+        pick[ge[i]] = 1;
+    for (int i = 0; i < *n_gq; ++i)
+        pick[gq[i]] = 1;
+    int *tok = (int *)malloc(sizeof(int) * (size_t)((*n_ge + *n_gq) * block + block));
+    int nt = 0;
+    for (int j = 0; j < c; ++j)
+        if (pick[j])
+            for (int u = 0; u < block; ++u)
+                tok[nt++] = j * block + u;
+    for (int u = c * block; u < n_tokens; ++u)
+        tok[nt++] = u;
+    oracle_attend_tokens(q, G, D, K, V, e, tok, nt, scale, out);
+
+    if (E)
+        memcpy(E, Eb, sizeof(double) * (size_t)c);
+    if (S)
+        memcpy(S, Sb, sizeof(double) * (size_t)c);
+    free(tok);
+    free(pick);
+    free(rest);
+    free(Sb);
+    free(Eb);
+    return c;
+}

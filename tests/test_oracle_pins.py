@@ -1,0 +1,315 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test names what fixes the expected result: a hand-worked case, a textbook
+routine, brute force, a closed form, or an invariant the NOSA pages state
+(technical summary, Methodology, "1. Algorithm: NOSA").
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from harness import oracle_trace, boundary_ok
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# top-k: brute force over tiny inputs, with forced ties
+# ---------------------------------------------------------------------------
+
+def test_topk_matches_bruteforce_sort_with_ties():
+    rng = np.random.default_rng(7)
+    for n in range(0, 11):
+        for trial in range(6):
+            # few distinct values -> many ties; equal scores must rank the lower index first
+            x = rng.integers(-2, 3, size=n).astype(np.float64)
+            allowed = rng.integers(0, 2, size=n).astype(bool) if trial % 2 else np.ones(n, bool)
+            for k in range(0, n + 2):
+                want = sorted(sorted((j for j in range(n) if allowed[j]),
+                                     key=lambda j: (-x[j], j))[:k])
+                got = oracle.topk(x, k, allowed if trial % 2 else None)
+                assert got == want, (n, k, x, allowed)
+
+
+def test_topk_tie_rule_lower_index_wins():
+    assert oracle.topk([5.0, 5.0, 5.0, 1.0], 2) == [0, 1]
+    assert oracle.topk([1.0, 5.0, 5.0, 5.0], 1) == [1]
+    assert oracle.topk([0.0] * 6, 3, [0, 1, 0, 1, 1, 1]) == [1, 3, 4]
+
+
+def test_topk_every_subset_small():
+    # every subset of n <= 6 candidates, every k: the chosen set is the k best
+    x = np.array([0.3, -1.0, 0.3, 2.0, 0.0, 2.0])
+    for n in range(1, 7):
+        for mask in itertools.product([0, 1], repeat=n):
+            for k in range(n + 1):
+                got = oracle.topk(x[:n], k, list(mask))
+                cand = [j for j in range(n) if mask[j]]
+                want = sorted(sorted(cand, key=lambda j: (-x[j], j))[:k])
+                assert got == want
+
+
+def test_select_by_pre_exp_equals_select_by_exp():
+    # ED-DMA selects on pre-exponential scores; exp is monotone, so the
+    # selected set equals selection on exponentiated scores when both are finite.
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        x = rng.normal(0, 3, size=40)
+        for k in (1, 5, 17, 39):
+            assert oracle.topk(x, k) == oracle.topk(np.exp(x), k)
+
+
+# ---------------------------------------------------------------------------
+# two-stage pooling: hand case and reductions to plain routines
+# ---------------------------------------------------------------------------
+
+def _hand():
+    with open(os.path.join(GOLD, "pool_hand.json")) as f:
+        return json.load(f)
+
+
+def test_pool_eviction_hand_case():
+    h = _hand()
+    e = np.zeros(64, np.float32)
+    e[0] = 16.0
+    e[16:32] = 2.0
+    e[32:48] = -1.0
+    e[48:64:2], e[49:64:2] = 3.0, -3.0
+    E = oracle.block_evict(e, h["block"], h["sub_block"], 0)
+    assert E == h["expected_E"]
+    assert E not in (h["wrong_max_then_mean"], h["wrong_block_mean"], h["wrong_token_max"])
+
+
+def test_pool_score_hand_case():
+    h = _hand()
+    a0, a1 = h["keys"]["a0"], h["keys"]["a1"]
+    K = np.zeros((64, 2), np.float32)
+    for i in range(4):
+        K[16 * i:16 * i + 16, 0] = a0[i]
+        K[16 * i:16 * i + 16, 1] = a1[i]
+    # make sub-block 0 non-constant with the same mean (mean pooling, not max)
+    K[0:16:2, 0] += 2.0
+    K[1:16:2, 0] -= 2.0
+    q = np.array(h["queries"], np.float32)
+    S = oracle.block_score(q, K, h["block"], h["sub_block"], 0, h["scale"])
+    assert S == h["expected_S"]
+    assert S != h["wrong_max_of_sum"]
+    kbar = oracle.pool_keys(K, 64, 16, 0)
+    np.testing.assert_array_equal(kbar[:, 0], a0)
+    np.testing.assert_array_equal(kbar[:, 1], a1)
+
+
+def test_pool_reduces_to_mean_when_sub_block_is_block():
+    rng = np.random.default_rng(11)
+    K = rng.normal(size=(256, 16)).astype(np.float32)
+    e = rng.normal(size=256).astype(np.float32)
+    q = rng.normal(size=(1, 16)).astype(np.float32)
+    for j in range(4):
+        blk = K[64 * j:64 * j + 64].astype(np.float64)
+        want = 0.3 * float(q[0].astype(np.float64) @ blk.mean(axis=0))
+        assert oracle.block_score(q, K, 64, 64, j, 0.3) == pytest.approx(want, rel=1e-12, abs=1e-12)
+        assert oracle.block_evict(e, 64, 64, j) == pytest.approx(
+            float(e[64 * j:64 * j + 64].astype(np.float64).mean()), rel=1e-12, abs=1e-13)
+
+
+def test_pool_reduces_to_token_max_when_sub_block_is_one():
+    rng = np.random.default_rng(12)
+    K = rng.normal(size=(128, 8)).astype(np.float32)
+    e = rng.normal(size=128).astype(np.float32)
+    q = rng.normal(size=(2, 8)).astype(np.float32)
+    for j in range(2):
+        blk = K[64 * j:64 * j + 64].astype(np.float64)
+        want = sum(float(np.max(0.5 * (blk @ q[h].astype(np.float64)))) for h in range(2))
+        assert oracle.block_score(q, K, 64, 1, j, 0.5) == pytest.approx(want, rel=1e-12)
+        assert oracle.block_evict(e, 64, 1, j) == float(e[64 * j:64 * j + 64].max())
+
+
+# ---------------------------------------------------------------------------
+# attention: textbook reductions and closed forms
+# ---------------------------------------------------------------------------
+
+def _sdpa(q, K, V, e, n, scale):
+    """torch's scaled_dot_product_attention on CPU in float64 with an additive mask."""
+    qt = torch.from_numpy(q.astype(np.float64))[None, :, None, :]          # [1, G, 1, D]
+    kt = torch.from_numpy(K[:n].astype(np.float64))[None, None].expand(1, q.shape[0], n, -1)
+    vt = torch.from_numpy(V[:n].astype(np.float64))[None, None].expand(1, q.shape[0], n, -1)
+    mask = torch.from_numpy(e[:n].astype(np.float64))[None, None, None, :]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+    return o[0, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("n_tokens", [1, 63, 64, 65, 640, 2000])
+def test_sparse_equals_dense_when_budget_covers_all(n_tokens):
+    rng = np.random.default_rng(n_tokens)
+    D, G = 64, 4
+    K = rng.normal(size=(n_tokens, D)).astype(np.float32)
+    V = rng.normal(size=(n_tokens, D)).astype(np.float32)
+    e = rng.normal(size=n_tokens).astype(np.float32)
+    q = rng.normal(size=(G, D)).astype(np.float32)
+    c = (n_tokens - 1) // 64
+    res = oracle.step_row(n_tokens, q, K, V, e, 64, 16, 4, max(c, 1), 0.125)
+    assert res.selected == list(range(c))
+    np.testing.assert_allclose(res.out, _sdpa(q, K, V, e, n_tokens, 0.125), rtol=1e-12, atol=1e-13)
+
+
+def test_constant_values_give_constant_output():
+    rng = np.random.default_rng(5)
+    n = 1000
+    K = rng.normal(size=(n, 32)).astype(np.float32)
+    V = np.tile(rng.normal(size=(1, 32)).astype(np.float32), (n, 1))
+    e = rng.normal(size=n).astype(np.float32) * 5
+    q = rng.normal(size=(3, 32)).astype(np.float32)
+    res = oracle.step_row(n, q, K, V, e, 64, 16, 3, 2, 0.2)
+    np.testing.assert_allclose(res.out, np.tile(V[:1].astype(np.float64), (3, 1)), rtol=1e-13)
+
+
+def test_zero_keys_zero_bias_give_mean_of_attended_values():
+    rng = np.random.default_rng(6)
+    n = 777
+    K = np.zeros((n, 16), np.float32)
+    V = rng.normal(size=(n, 16)).astype(np.float32)
+    e = np.zeros(n, np.float32)
+    q = rng.normal(size=(2, 16)).astype(np.float32)
+    res = oracle.step_row(n, q, K, V, e, 64, 16, 2, 3, 0.25)
+    toks = [t for j in res.selected for t in range(64 * j, 64 * j + 64)] + \
+        list(range(64 * res.n_cand, n))
+    want = V[toks].astype(np.float64).mean(axis=0)
+    np.testing.assert_allclose(res.out, np.tile(want, (2, 1)), rtol=1e-12, atol=1e-14)
+
+
+def test_eviction_bias_is_a_log_multiplicity():
+    # Adding ln(m) to a token's logit weighs it exactly like m copies of that
+    # token with no bias: the bias enters inside the exponential (ED-DMA).
+    rng = np.random.default_rng(9)
+    n, D = 40, 8
+    K = rng.normal(size=(n, D)).astype(np.float32)
+    V = rng.normal(size=(n, D)).astype(np.float32)
+    q = rng.normal(size=(2, D)).astype(np.float32)
+    mult = rng.integers(1, 5, size=n)
+    e = np.log(mult).astype(np.float32)
+    # float32 rounding of ln(m) perturbs weights by < 1e-7 relative
+    got = oracle.attend_tokens(q, K, V, e, np.arange(n), 0.3)
+    rep = np.repeat(np.arange(n), mult)
+    want = oracle.attend_tokens(q, K, V, None, rep, 0.3)
+    np.testing.assert_allclose(got, want, rtol=2e-7, atol=2e-7)
+    # and the sign matters: a negative bias of ln(m) is not the same
+    bad = oracle.attend_tokens(q, K, V, -e, np.arange(n), 0.3)
+    assert np.max(np.abs(bad - want)) > 1e-3
+
+
+def test_large_biases_stay_finite_and_shift_invariant():
+    rng = np.random.default_rng(10)
+    n = 300
+    K = rng.normal(size=(n, 16)).astype(np.float32)
+    V = rng.normal(size=(n, 16)).astype(np.float32)
+    q = rng.normal(size=(2, 16)).astype(np.float32)
+    e = rng.uniform(-100, 100, size=n).astype(np.float32)
+    a = oracle.attend_tokens(q, K, V, e, np.arange(n), 0.25)
+    b = oracle.attend_tokens(q, K, V, (e - 50).astype(np.float32), np.arange(n), 0.25)
+    assert np.all(np.isfinite(a))
+    np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-9)
+    # softmax concentrates on the largest logit when it dominates by > 40 nats
+    i = int(np.argmax(e))
+    z = 0.25 * (K.astype(np.float64) @ q.T.astype(np.float64)) + e[:, None]
+    top2 = np.sort(z, axis=0)[-2:]
+    for h in range(2):
+        if top2[1, h] - top2[0, h] > 40 and int(np.argmax(z[:, h])) == i:
+            np.testing.assert_allclose(a[h], V[i], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# invariants over traces: strict eviction, locality bound, swap lists
+# ---------------------------------------------------------------------------
+
+def _incremental_gamma_e(E_of, counts, k_e):
+    """The method's route to Gamma_e: keep k_e blocks; a new candidate replaces
+    the lowest-ranked kept block if it ranks above it, else is evicted at once."""
+    def above(a, b):
+        return E_of[a] > E_of[b] or (E_of[a] == E_of[b] and a < b)
+    kept, out, seen = [], [], 0
+    for c in counts:
+        for x in range(seen, c):
+            if len(kept) < k_e:
+                kept.append(x)
+                continue
+            if k_e == 0:
+                continue
+            low = kept[0]
+            for y in kept[1:]:
+                if above(low, y):
+                    low = y
+            if above(x, low):
+                kept[kept.index(low)] = x
+        seen = c
+        out.append(sorted(kept))
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "small_f32", "small_offload"])
+def test_trace_invariants(name):
+    w = synth.WORKLOADS[name]
+    tr = oracle_trace(w, steps=list(range(w.steps)), margins=True, swaps=True)
+    for r in tr.rows:
+        prev_sel = None
+        evicted = set()
+        counts = [w.n_cand(t) for t in tr.steps]
+        E_all = tr.step[(tr.steps[-1], r)].E
+        inc = _incremental_gamma_e(E_all, counts, w.k_e)
+        for i, t in enumerate(tr.steps):
+            res = tr.step[(t, r)]
+            ge = set(res.gamma_e)
+            # strict eviction: a block that left Gamma_e never comes back
+            assert not (ge & evicted), (t, r)
+            evicted |= set(range(res.n_cand)) - ge
+            # stateless definition == the method's incremental eviction
+            assert res.gamma_e == inc[i]
+            # Gamma_q avoids Gamma_e; sizes are the budgets (or all candidates)
+            assert not (set(res.gamma_q) & ge)
+            assert len(res.gamma_e) == min(w.k_e, res.n_cand)
+            assert len(res.selected) == min(w.k, res.n_cand)
+            sw = tr.swap[(t, r)]
+            # after the swap the cache holds exactly the selection
+            assert sorted(b for b in sw.slot_block if b >= 0) == res.selected
+            if prev_sel is not None:
+                assert sw.fetch_block == sorted(set(res.selected) - set(prev_sel))
+                # locality bound on steps that complete no new block
+                if w.n_cand(t) == w.n_cand(t - 1) and res.n_cand >= w.k:
+                    assert sw.gamma >= w.k_e / w.k
+            else:
+                assert sw.fetch_block == res.selected
+            prev_sel = res.selected
+        # the margin recipe held at every boundary that was used
+        for t in tr.steps:
+            res = tr.step[(t, r)]
+            assert boundary_ok(res.E, w.k_e)[0]
+            rest = np.array([j not in set(res.gamma_e) for j in range(res.n_cand)], bool)
+            assert boundary_ok(res.S[rest], w.k_q)[0]
+
+
+def test_swap_cache_bruteforce():
+    # random selections; check the slot rule against a direct set computation
+    rng = np.random.default_rng(1)
+    k = 6
+    cache = oracle.SlotCache(k)
+    prev = set()
+    slots = [-1] * k
+    for t in range(200):
+        sel = sorted(rng.choice(20, size=rng.integers(0, k + 1), replace=False).tolist())
+        res = cache.step(sel)
+        fetch = sorted(set(sel) - {b for b in slots if b >= 0})
+        free = [s for s in range(k) if slots[s] < 0 or slots[s] not in sel]
+        assert res.fetch_block == fetch
+        assert res.fetch_slot == free[:len(fetch)]
+        for b, s in zip(fetch, free):
+            slots[s] = b
+        slots = [b if b in sel else -1 for b in slots]
+        assert res.slot_block == slots
+        assert res.gamma == len(set(sel) & prev) / k
+        prev = set(sel)
