@@ -1,0 +1,218 @@
+/*
+ * nosa.h — C ABI of the NOSA per-decode-step block-sparse attention path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is NOSA ("NOSA: Native and Offloadable Sparse Attention",
+ * technical summary pages, section Methodology). One decode step of one layer
+ * runs, per row = one (batch, KV head) pair:
+ *
+ *   nosa_pool_blocks    sub-block mean / block max pooling of a newly complete
+ *                       block (Methodology, "1. Algorithm", bullet
+ *                       "Block-Wise Implementation")
+ *   nosa_score_blocks   query-aware pooled block scores (bullets "Dual-Selection
+ *                       Mechanism", "Block-Wise Implementation")
+ *   nosa_select         Gamma_e: k_e blocks by pre-exponential eviction score
+ *                       with strict eviction (bullets "Dual-Selection
+ *                       Mechanism", "ED-DMA", "Locality Guarantee");
+ *                       Gamma_q: top k_q of the rest by query-aware score
+ *   nosa_swap_diff      set difference between the new selection and the
+ *                       blocks cached in HBM (Methodology, "2. System: NOSI",
+ *                       bullet "Optimized Memory Layout")
+ *   nosa_fetch_blocks   copy of the missing blocks from pinned host memory
+ *                       into HBM by a GPU kernel (bullet "High-Bandwidth
+ *                       Communication")
+ *   nosa_sparse_decode  attention over the selected blocks plus the newest
+ *                       block, the eviction score added to each logit so its
+ *                       exponential happens only in the softmax (bullet
+ *                       "ED-DMA")
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership: the caller owns every buffer. Device buffers are plain device
+ *   pointers; "pinned host" buffers come from nosa_host_alloc. The library
+ *   keeps no allocation and no mutable state between calls.
+ * Streams: every call only enqueues work on `stream` (a hipStream_t, may be
+ *   NULL for the null stream) and never synchronises. Host-side arguments
+ *   (shape, step) are read during the call and may be reused afterwards.
+ * Errors: arguments are validated on the host before anything is launched;
+ *   a bad argument returns NOSA_ERR_INVALID_ARGUMENT (or NOSA_ERR_UNSUPPORTED
+ *   for a valid but unimplemented shape) and launches nothing. A failed
+ *   launch returns NOSA_ERR_HIP. Device *data* (block ids in lists) is trusted:
+ *   out-of-range ids are undefined behaviour. No C++ exception crosses the ABI.
+ * Rows: row r = b * n_kv_heads + g. Query heads g*G .. g*G+G-1 (G =
+ *   n_q_heads / n_kv_heads) share KV head g.
+ * Blocks: block j holds tokens [j*S, j*S + S), S = block_size. After a step
+ *   has appended its token there are n_tokens tokens; the candidate blocks
+ *   are 0 .. n_cand-1 with n_cand = (n_tokens - 1) / S; block n_cand (the
+ *   newest, 1..S tokens) is always attended and is never a candidate.
+ *
+ * Layouts (element type = shape.dtype unless stated)
+ * --------------------------------------------------
+ * q, out     [batch][n_q_heads][D]
+ * KV block   one block-unit of 2*S*D elements: the K tile [S][D] (token
+ *            major) followed by the V tile stored transposed, [D][S]. A
+ *            "KV buffer" is [rows][row_blocks][2*S*D]; the full KV, an HBM
+ *            block cache (k slots per row) and the newest-block buffer (one
+ *            block per row) all use it with their own row_blocks.
+ * e_tok      float32 [rows][e_row_stride]: per-token eviction scores,
+ *            pre-exponential.
+ * kbar       float32 [rows][D/4][m*max_blocks][4], m = S / sub_block: the
+ *            mean key of sub-block i of block j is at [.][d/4][m*j+i][d%4].
+ * e_blk      float32 [rows][max_blocks]: pooled eviction score per block.
+ * s_q        float32 [rows][max_blocks]: query-aware score per block.
+ * bitmaps    uint32 [rows][W], W = (max_blocks + 31) / 32; bit j%32 of word
+ *            j/32 stands for block j.
+ * sel        int32 [rows][k]: selected block ids ascending, -1 padded;
+ *            n_sel int32 [rows].
+ * slot_block int32 [rows][k]: block held by each cache slot, -1 = empty.
+ * block_slot int32 [rows][max_blocks]: slot of each cached block, -1 = none.
+ */
+#ifndef NOSA_H
+#define NOSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t nosa_status;
+enum {
+    NOSA_OK = 0,
+    NOSA_ERR_INVALID_ARGUMENT = 1,
+    NOSA_ERR_UNSUPPORTED = 2,
+    NOSA_ERR_HIP = 3,
+    NOSA_ERR_WORKSPACE = 4
+};
+
+/* element types of q, K, V and out */
+enum { NOSA_F32 = 0, NOSA_BF16 = 1 };
+
+/* which source the decode reads selected blocks from */
+enum { NOSA_KV_FULL = 0, NOSA_KV_CACHE = 1 };
+
+/* decode kernel choice (nosa_shape.decode_kernel) */
+enum { NOSA_DECODE_AUTO = 0, NOSA_DECODE_VALU = 1, NOSA_DECODE_MFMA = 2 };
+
+/* Problem shape, in the pages' terms: block size, sub-block size, budgets
+ * k = k_e + k_q, and GQA groups (n_q_heads / n_kv_heads).
+ * Supported: block_size 64, sub_block 16, head_dim 64 or 128, G <= 8,
+ * k <= 128, max_blocks <= 4096. */
+typedef struct nosa_shape {
+    int32_t batch;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t sub_block;
+    int32_t k_e;           /* query-agnostic (eviction) budget, blocks */
+    int32_t k_q;           /* query-aware budget, blocks */
+    int32_t max_blocks;    /* capacity of per-row block arrays */
+    int32_t dtype;         /* NOSA_F32 or NOSA_BF16 */
+    int32_t decode_kernel; /* NOSA_DECODE_* */
+    float scale;           /* logit scale; 0 means 1/sqrt(head_dim) */
+} nosa_shape;
+
+/* Where the decode is: read on the host during each call. */
+typedef struct nosa_step {
+    int32_t n_tokens;    /* tokens present, including the one appended this step */
+    int32_t n_cand_prev; /* candidate blocks at the previous step; -1: no previous
+                            step, so nosa_select (re)initialises Gamma_e */
+} nosa_step;
+
+/* Pool blocks [blk_begin, blk_end) of every row: kbar gets each sub-block's
+ * mean key (float32 sum, then times 1/sub_block), e_blk the max over the
+ * block's sub-blocks of the mean per-token eviction score (Methodology,
+ * "Block-Wise Implementation": mean inside sub-blocks, then max over the
+ * block). Block j of row r is read from the KV buffer `kv` at block index
+ * kv_first_block + (j - blk_begin) of that row (kv_row_blocks blocks per row),
+ * so the same call pools from the full KV or from the newest-block buffer.
+ * kv may be a device pointer or the device alias of pinned host memory. */
+nosa_status nosa_pool_blocks(const nosa_shape *shape, const void *kv, int64_t kv_row_blocks,
+                             int32_t kv_first_block, const float *e_tok, int64_t e_row_stride,
+                             int32_t blk_begin, int32_t blk_end, float *kbar, float *e_blk,
+                             void *stream);
+
+/* Query-aware block scores for candidates 0 .. n_cand-1 of every row:
+ * s_q[r][j] = sum over the G heads of the row of max over sub-blocks i of
+ * scale * q_h . kbar[j,i] (Methodology, "Dual-Selection Mechanism" and
+ * "Block-Wise Implementation"). Entries j >= n_cand are left untouched. */
+nosa_status nosa_score_blocks(const nosa_shape *shape, const void *q, const float *kbar,
+                              const nosa_step *step, float *s_q, void *stream);
+
+/* Dual selection for every row (Methodology, "Dual-Selection Mechanism",
+ * "Locality Guarantee", "ED-DMA").
+ * Gamma_e (bitmap ge_bits, in/out) keeps k_e blocks ranked by e_blk, the
+ * pre-exponential eviction score. With step->n_cand_prev < 0 it is rebuilt
+ * as the k_e best of all candidates and every other candidate is marked in
+ * ev_bits (evicted). Otherwise each new candidate n_cand_prev .. n_cand-1 in
+ * turn either enters, replacing the lowest-ranked member if it ranks above
+ * it (the member moves to ev_bits), or is evicted at once; an evicted block
+ * never re-enters. Ranking: higher score first, equal scores lower id first.
+ * Gamma_q: the k_q best of the candidates outside Gamma_e by s_q (evicted
+ * blocks are eligible). Outputs sel/n_sel (ascending union) and sel_bits. */
+nosa_status nosa_select(const nosa_shape *shape, const float *s_q, const float *e_blk,
+                        const nosa_step *step, uint32_t *ge_bits, uint32_t *ev_bits,
+                        int32_t *sel, int32_t *n_sel, uint32_t *sel_bits, void *stream);
+
+/* Set difference against the HBM block cache of k = k_e + k_q slots per row
+ * (Methodology, "2. System: NOSI", "Optimized Memory Layout").
+ * fetch = selected blocks not cached (ascending); free = slots that are
+ * empty or hold a block no longer selected (ascending); fetch[i] goes to
+ * free[i]; leftover free slots become empty. Updates slot_block and
+ * block_slot (in/out; start with every entry -1), writes fetch_block /
+ * fetch_slot [rows][k] and n_fetch [rows], and adds to counters
+ * uint64 [rows][2]: {blocks fetched, selected blocks already cached}. */
+nosa_status nosa_swap_diff(const nosa_shape *shape, const int32_t *sel, const int32_t *n_sel,
+                           const uint32_t *sel_bits, int32_t *slot_block, int32_t *block_slot,
+                           int32_t *fetch_block, int32_t *fetch_slot, int32_t *n_fetch,
+                           uint64_t *counters, void *stream);
+
+/* Copy fetch_block[r][i] of the source KV buffer to slot fetch_slot[r][i] of
+ * the destination KV buffer, for i < n_fetch[r] (at most max_fetch), every
+ * row (Methodology, "High-Bandwidth Communication"). The copy is a GPU kernel
+ * with 16-byte loads; src_kv is normally the device alias of pinned host
+ * memory (nosa_host_alloc), so the loads travel over PCIe. Whole blocks of
+ * 2*S*D elements are moved; layout inside a block is preserved. */
+nosa_status nosa_fetch_blocks(const nosa_shape *shape, const void *src_kv, int64_t src_row_blocks,
+                              const int32_t *fetch_block, const int32_t *fetch_slot,
+                              const int32_t *n_fetch, int32_t max_fetch, void *dst_kv,
+                              int64_t dst_row_blocks, void *stream);
+
+/* Workspace bytes nosa_sparse_decode needs for this shape (split-K partials). */
+size_t nosa_decode_workspace_size(const nosa_shape *shape);
+
+/* Sparse decode attention for every query head (Methodology, "ED-DMA"):
+ * over the tokens T of the listed blocks plus the newest block (block n_cand,
+ * tokens [S*n_cand, n_tokens)),
+ *   z_i = scale * q_h . k_i + e_tok[r][i],  out_h = sum_i softmax(z)_i v_i.
+ * kv_mode NOSA_KV_FULL: entry i < n_list[r] of row r is block list[r*k + i]
+ *   of the KV buffer kv (kv_row_blocks per row); entries are block ids.
+ * kv_mode NOSA_KV_CACHE: entry i < k is slot i of the cache kv; list is the
+ *   slot_block table (block id per slot, -1 = empty, skipped); n_list unused.
+ * The newest block of row r is block 0 of row r of cur_kv (cur_row_blocks
+ *   blocks per row); for the full KV pass kv advanced by n_cand blocks.
+ * Split-K partials go to ws (at least nosa_decode_workspace_size bytes);
+ * a fixed-order combine writes out (float32 accumulate, bf16 RNE store). */
+nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *kv,
+                               int64_t kv_row_blocks, int32_t kv_mode, const int32_t *list,
+                               const int32_t *n_list, const void *cur_kv, int64_t cur_row_blocks,
+                               const nosa_step *step, const float *e_tok, int64_t e_row_stride,
+                               void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Pinned host memory readable by GPU kernels: *host is the host address,
+ * *dev the device alias to pass as a kernel source. coherent != 0 asks for
+ * fine-grained (coherent) memory. Free with nosa_host_free. */
+nosa_status nosa_host_alloc(size_t bytes, int32_t coherent, void **host, void **dev);
+nosa_status nosa_host_free(void *host);
+
+const char *nosa_status_string(nosa_status s);
+/* Text of the last HIP error seen by a call on this thread ("" if none). */
+const char *nosa_last_error(void);
+int32_t nosa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NOSA_H */

@@ -1,0 +1,104 @@
+"""The C-ABI library loads, exports every entry point its header declares,
+and rejects bad arguments on the host before launching anything (no GPU
+needed for these checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "nosa.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(nosa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_path_entry_points():
+    names = _declared()
+    for n in ("nosa_score_blocks", "nosa_select", "nosa_swap_diff", "nosa_fetch_blocks",
+              "nosa_sparse_decode", "nosa_pool_blocks"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    from trainable_block_sparse_nosa_amd import _lib
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(_lib.EXPORTS) == set(_declared())
+
+
+def _shape(**kw):
+    from trainable_block_sparse_nosa_amd import _lib as L
+    a = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, k_e=4, k_q=4, max_blocks=64,
+             dtype=L.NOSA_BF16)
+    a.update(kw)
+    return L.make_shape(**a)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(n_q_heads=7), 1),           # heads not a multiple of KV heads
+    (dict(head_dim=96), 2),           # unsupported head_dim
+    (dict(k_e=100, k_q=100), 1),      # budget above capacity
+    (dict(k_e=0, k_q=0), 1),          # empty budget
+    (dict(dtype=5), 1),
+    (dict(block_size=48), 2),
+    (dict(sub_block=24), 1),          # block not a multiple of sub-block
+    (dict(n_q_heads=32, n_kv_heads=2), 2),  # G = 16 > 8
+    (dict(max_blocks=5000, k_e=4), 2),
+    (dict(dtype=0, head_dim=128), 2),  # float32 supports head_dim 64 only
+])
+def test_invalid_shapes_rejected(bad, status):
+    from trainable_block_sparse_nosa_amd import _lib as L
+    sh = _shape(**bad)
+    assert L.lib().nosa_decode_workspace_size(ctypes.byref(sh)) == 0
+    st = L.make_step(100, -1)
+    rc = L.lib().nosa_score_blocks(ctypes.byref(sh), 16, 16, ctypes.byref(st), 16, None)
+    assert rc == status
+
+
+def test_invalid_pointers_and_steps_rejected():
+    from trainable_block_sparse_nosa_amd import _lib as L
+    lib = L.lib()
+    sh = _shape()
+    ok_step = L.make_step(100, -1)
+    # null pointers
+    assert lib.nosa_score_blocks(ctypes.byref(sh), None, 16, ctypes.byref(ok_step), 16, None) == 1
+    assert lib.nosa_select(ctypes.byref(sh), 16, 16, ctypes.byref(ok_step), None, 16, 16, 16, 16,
+                           None) == 1
+    # a step beyond the block capacity
+    big = L.make_step(64 * 64 + 1, -1)
+    assert lib.nosa_score_blocks(ctypes.byref(sh), 16, 16, ctypes.byref(big), 16, None) == 1
+    # previous candidate count above the current one
+    back = L.make_step(200, 10)
+    assert lib.nosa_select(ctypes.byref(sh), 16, 16, ctypes.byref(back), 16, 16, 16, 16, 16,
+                           None) == 1
+    # pooling outside the capacity / inconsistent strides
+    assert lib.nosa_pool_blocks(ctypes.byref(sh), 16, 64, 0, 16, 64 * 64, 0, 65, 16, 16, None) == 1
+    assert lib.nosa_pool_blocks(ctypes.byref(sh), 16, 4, 2, 16, 64 * 64, 0, 3, 16, 16, None) == 1
+    assert lib.nosa_pool_blocks(ctypes.byref(sh), 16, 64, 0, 16, 100, 0, 3, 16, 16, None) == 1
+    # fetch list longer than the budget
+    assert lib.nosa_fetch_blocks(ctypes.byref(sh), 16, 64, 16, 16, 16, 9, 16, 8, None) == 1
+    # decode: small workspace, misaligned pointers, bad mode, e stride too short
+    ws = lib.nosa_decode_workspace_size(ctypes.byref(sh))
+    assert ws > 0
+    st = L.make_step(100, 0)
+    args = lambda **o: dict(dict(q=16, kv=16, rb=64, mode=0, lst=16, nl=16, cur=16, crb=64,
+                                 e=16, es=4096, out=16, ws=16, wsb=ws), **o)
+    def call(a):
+        return lib.nosa_sparse_decode(ctypes.byref(sh), a["q"], a["kv"], a["rb"], a["mode"],
+                                      a["lst"], a["nl"], a["cur"], a["crb"], ctypes.byref(st),
+                                      a["e"], a["es"], a["out"], a["ws"], a["wsb"], None)
+    assert call(args(wsb=ws - 4)) == 4
+    assert call(args(q=17)) == 1
+    assert call(args(mode=3)) == 1
+    assert call(args(es=99)) == 1
+    assert call(args(mode=1, rb=7)) == 1      # cache smaller than k slots
+    assert call(args(nl=None)) == 1           # full mode needs the list length
+    # host allocation needs a size
+    h, d = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.nosa_host_alloc(0, 0, ctypes.byref(h), ctypes.byref(d)) == 1
+    assert lib.nosa_status_string(2) == b"unsupported shape"

@@ -1,0 +1,125 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Bar: selections (Gamma_e, Gamma_q, their union), swap lists and slot tables
+bit-exact; attention outputs within rtol 1e-5 / atol 1e-6 for float32 inputs
+and rtol 2e-2 / atol 2e-3 for bfloat16 inputs; pooled scores within the
+float32 accumulation error (well inside the 1e-4 selection margin).
+"""
+import numpy as np
+import pytest
+
+import synth
+from harness import oracle_trace
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(rtol=1e-5, atol=1e-6), "bf16": dict(rtol=2e-2, atol=2e-3)}
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gpu_harness
+    return gpu_harness
+
+
+def _compare_step(w, tr, t, r, got, check_swap=True, check_slots=True):
+    """Compare one (step, row) of the GPU snapshot `got` with the oracle."""
+    import gpu_harness as gh
+    ref = tr.step[(t, r)]
+    c = ref.n_cand
+    where = f"{w.name} t={t} row={r}"
+    # pooled scores: float32 accumulation of float32/bf16 inputs
+    if c:
+        np.testing.assert_allclose(got["e_blk"][r, :c], ref.E, rtol=0, atol=2e-6, err_msg=where)
+        rms = float(np.sqrt(np.mean(ref.S ** 2)))
+        np.testing.assert_allclose(got["s_q"][r, :c], ref.S, rtol=2e-6, atol=2e-6 * rms,
+                                   err_msg=where)
+    # selections: bit-exact
+    assert gh.bits_to_list(got["ge_bits"][r]) == ref.gamma_e, where
+    n = int(got["n_sel"][r])
+    assert got["sel"][r, :n].tolist() == ref.selected, where
+    assert (got["sel"][r, n:] == -1).all(), where
+    assert gh.bits_to_list(got["sel_bits"][r]) == ref.selected, where
+    # strict eviction bookkeeping: evicted = candidates outside Gamma_e
+    assert gh.bits_to_list(got["ev_bits"][r]) == sorted(set(range(c)) - set(ref.gamma_e)), where
+    if check_swap:
+        sw = tr.swap[(t, r)]
+        nf = int(got["n_fetch"][r])
+        assert got["fetch_block"][r, :nf].tolist() == sw.fetch_block, where
+        if check_slots:
+            assert got["fetch_slot"][r, :nf].tolist() == sw.fetch_slot, where
+            assert got["slot_block"][r].tolist() == sw.slot_block, where
+    # attention output of the row's G query heads
+    b, g = divmod(r, w.n_kv_heads)
+    G = w.group
+    out = got["out"][b, g * G:(g + 1) * G]
+    np.testing.assert_allclose(out, ref.out, err_msg=where, **TOL[w.dtype])
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "small_f32", "small_bf16", "small_offload"])
+def test_parity_all_steps_all_rows(name):
+    gh = _gpu()
+    w = synth.WORKLOADS[name]
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov)
+    _, res = gh.run(w, inp, list(range(w.steps)))
+    for t in range(w.steps):
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, res[t])
+
+
+EDGE = {
+    # fewer tokens than one block at the start: no candidates, then one
+    "short_context": dict(context=10, steps=70, k_e=2, k_q=2),
+    # the budget covers every candidate: sparse == dense over all tokens
+    "budget_covers_all": dict(context=500, steps=30, k_e=4, k_q=8),
+    # query-aware only / eviction only
+    "no_eviction_budget": dict(context=1500, steps=20, k_e=0, k_q=6),
+    "no_query_budget": dict(context=1500, steps=20, k_e=6, k_q=0),
+    # GQA extremes and head_dim 64 in bf16
+    "gqa1_d64": dict(n_q_heads=3, n_kv_heads=3, head_dim=64, context=1300, steps=20),
+    "gqa8": dict(n_q_heads=16, n_kv_heads=2, context=1300, steps=20),
+    # ragged: context ends one token before a block boundary
+    "ragged_boundary": dict(context=2047, steps=3, k_e=5, k_q=5),
+    # the largest supported budget
+    "k128": dict(context=9000, steps=4, k_e=96, k_q=32),
+}
+
+
+@pytest.mark.parametrize("edge", sorted(EDGE))
+def test_parity_edge_cases(edge):
+    gh = _gpu()
+    base = synth.WORKLOADS["small_bf16"]
+    w = base.scaled(name="edge_" + edge, seed=3000 + sorted(EDGE).index(edge), **EDGE[edge])
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov)
+    _, res = gh.run(w, inp, list(range(w.steps)))
+    for t in range(w.steps):
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, res[t])
+
+
+def test_offload_edge_gqa1_short():
+    gh = _gpu()
+    w = synth.WORKLOADS["small_offload"].scaled(name="edge_offload_short", seed=3100,
+                                               n_q_heads=2, n_kv_heads=2, context=100, steps=40,
+                                               k_e=2, k_q=3)
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov)
+    _, res = gh.run(w, inp, list(range(w.steps)))
+    for t in range(w.steps):
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, res[t])
+
+
+def test_deterministic_rerun():
+    gh = _gpu()
+    w = synth.WORKLOADS["small_bf16"]
+    inp = gh.upload(w)
+    _, a = gh.run(w, inp, list(range(w.steps)))
+    _, b = gh.run(w, inp, list(range(w.steps)))
+    for t in a:
+        for key in a[t]:
+            np.testing.assert_array_equal(a[t][key], b[t][key], err_msg=f"{key} t={t}")

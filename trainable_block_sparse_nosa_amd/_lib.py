@@ -1,0 +1,185 @@
+"""ctypes binding of libnosa.so: the C ABI declared in include/nosa.h.
+
+Argument marshalling only. Pointers may be given as torch tensors (their
+data_ptr is passed), plain integers, or None for NULL; streams as
+torch.cuda.Stream, an integer handle, or None for the current torch stream.
+Every function raises NosaError on a non-zero status. There is no fallback:
+if libnosa.so is missing, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnosa.so")
+
+NOSA_OK = 0
+NOSA_ERR_INVALID_ARGUMENT = 1
+NOSA_ERR_UNSUPPORTED = 2
+NOSA_ERR_HIP = 3
+NOSA_ERR_WORKSPACE = 4
+NOSA_F32 = 0
+NOSA_BF16 = 1
+NOSA_KV_FULL = 0
+NOSA_KV_CACHE = 1
+NOSA_DECODE_AUTO = 0
+NOSA_DECODE_VALU = 1
+NOSA_DECODE_MFMA = 2
+
+EXPORTS = (
+    "nosa_pool_blocks", "nosa_score_blocks", "nosa_select", "nosa_swap_diff",
+    "nosa_fetch_blocks", "nosa_decode_workspace_size", "nosa_sparse_decode",
+    "nosa_host_alloc", "nosa_host_free", "nosa_status_string", "nosa_last_error",
+    "nosa_version",
+)
+
+
+class NosaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = _L.nosa_status_string(status).decode()
+        detail = _L.nosa_last_error().decode()
+        super().__init__(f"{fn}: {msg}" + (f" ({detail})" if detail and status == NOSA_ERR_HIP else ""))
+
+
+class nosa_shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "n_q_heads", "n_kv_heads", "head_dim", "block_size", "sub_block", "k_e", "k_q",
+        "max_blocks", "dtype", "decode_kernel")] + [("scale", ctypes.c_float)]
+
+
+class nosa_step(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int32), ("n_cand_prev", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m trainable_block_sparse_nosa_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    SH, ST = ctypes.POINTER(nosa_shape), ctypes.POINTER(nosa_step)
+    sig = {
+        "nosa_pool_blocks": [SH, P, I64, I32, P, I64, I32, I32, P, P, P],
+        "nosa_score_blocks": [SH, P, P, ST, P, P],
+        "nosa_select": [SH, P, P, ST, P, P, P, P, P, P],
+        "nosa_swap_diff": [SH, P, P, P, P, P, P, P, P, P, P],
+        "nosa_fetch_blocks": [SH, P, I64, P, P, P, I32, P, I64, P],
+        "nosa_sparse_decode": [SH, P, P, I64, I32, P, P, P, I64, ST, P, I64, P, P, SZ, P],
+        "nosa_host_alloc": [SZ, I32, ctypes.POINTER(P), ctypes.POINTER(P)],
+        "nosa_host_free": [P],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int32
+    L.nosa_decode_workspace_size.argtypes = [SH]
+    L.nosa_decode_workspace_size.restype = SZ
+    L.nosa_status_string.argtypes = [ctypes.c_int32]
+    L.nosa_status_string.restype = ctypes.c_char_p
+    L.nosa_last_error.argtypes = []
+    L.nosa_last_error.restype = ctypes.c_char_p
+    L.nosa_version.argtypes = []
+    L.nosa_version.restype = ctypes.c_int32
+    return L
+
+
+_L = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _L
+
+
+def _p(x):
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def _s(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _chk(fn: str, status: int):
+    if status != NOSA_OK:
+        raise NosaError(fn, status)
+
+
+def make_shape(batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks, dtype,
+               block_size=64, sub_block=16, decode_kernel=NOSA_DECODE_AUTO, scale=0.0) -> nosa_shape:
+    return nosa_shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, sub_block, k_e, k_q,
+                      max_blocks, dtype, decode_kernel, scale)
+
+
+def make_step(n_tokens: int, n_cand_prev: int) -> nosa_step:
+    return nosa_step(n_tokens, n_cand_prev)
+
+
+def nosa_pool_blocks(shape, kv, kv_row_blocks, kv_first_block, e_tok, e_row_stride, blk_begin,
+                     blk_end, kbar, e_blk, stream=None):
+    _chk("nosa_pool_blocks", _L.nosa_pool_blocks(
+        ctypes.byref(shape), _p(kv), kv_row_blocks, kv_first_block, _p(e_tok), e_row_stride,
+        blk_begin, blk_end, _p(kbar), _p(e_blk), _s(stream)))
+
+
+def nosa_score_blocks(shape, q, kbar, step, s_q, stream=None):
+    _chk("nosa_score_blocks", _L.nosa_score_blocks(
+        ctypes.byref(shape), _p(q), _p(kbar), ctypes.byref(step), _p(s_q), _s(stream)))
+
+
+def nosa_select(shape, s_q, e_blk, step, ge_bits, ev_bits, sel, n_sel, sel_bits, stream=None):
+    _chk("nosa_select", _L.nosa_select(
+        ctypes.byref(shape), _p(s_q), _p(e_blk), ctypes.byref(step), _p(ge_bits), _p(ev_bits),
+        _p(sel), _p(n_sel), _p(sel_bits), _s(stream)))
+
+
+def nosa_swap_diff(shape, sel, n_sel, sel_bits, slot_block, block_slot, fetch_block, fetch_slot,
+                   n_fetch, counters, stream=None):
+    _chk("nosa_swap_diff", _L.nosa_swap_diff(
+        ctypes.byref(shape), _p(sel), _p(n_sel), _p(sel_bits), _p(slot_block), _p(block_slot),
+        _p(fetch_block), _p(fetch_slot), _p(n_fetch), _p(counters), _s(stream)))
+
+
+def nosa_fetch_blocks(shape, src_kv, src_row_blocks, fetch_block, fetch_slot, n_fetch, max_fetch,
+                      dst_kv, dst_row_blocks, stream=None):
+    _chk("nosa_fetch_blocks", _L.nosa_fetch_blocks(
+        ctypes.byref(shape), _p(src_kv), src_row_blocks, _p(fetch_block), _p(fetch_slot),
+        _p(n_fetch), max_fetch, _p(dst_kv), dst_row_blocks, _s(stream)))
+
+
+def nosa_decode_workspace_size(shape) -> int:
+    n = _L.nosa_decode_workspace_size(ctypes.byref(shape))
+    if n == 0:
+        raise NosaError("nosa_decode_workspace_size", NOSA_ERR_INVALID_ARGUMENT)
+    return n
+
+
+def nosa_sparse_decode(shape, q, kv, kv_row_blocks, kv_mode, list_, n_list, cur_kv,
+                       cur_row_blocks, step, e_tok, e_row_stride, out, ws, ws_bytes, stream=None):
+    _chk("nosa_sparse_decode", _L.nosa_sparse_decode(
+        ctypes.byref(shape), _p(q), _p(kv), kv_row_blocks, kv_mode, _p(list_), _p(n_list),
+        _p(cur_kv), cur_row_blocks, ctypes.byref(step), _p(e_tok), e_row_stride, _p(out), _p(ws),
+        ws_bytes, _s(stream)))
+
+
+def nosa_host_alloc(nbytes: int, coherent: bool = False) -> tuple[int, int]:
+    h, d = ctypes.c_void_p(), ctypes.c_void_p()
+    _chk("nosa_host_alloc", _L.nosa_host_alloc(nbytes, 1 if coherent else 0,
+                                               ctypes.byref(h), ctypes.byref(d)))
+    return h.value, d.value
+
+
+def nosa_host_free(host: int):
+    _chk("nosa_host_free", _L.nosa_host_free(host))
+
+
+def nosa_version() -> int:
+    return _L.nosa_version()

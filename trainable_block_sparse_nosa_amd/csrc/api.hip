@@ -1,0 +1,277 @@
+// C ABI of the NOSA decode path: argument validation, dispatch, launches.
+#include <math.h>
+
+#include <string>
+#include <type_traits>
+
+#include "kernels.h"
+
+using namespace nosa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+nosa_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return NOSA_OK;
+    g_last_error = hipGetErrorString(e);
+    return NOSA_ERR_HIP;
+}
+
+nosa_status make_dims(const nosa_shape *s, Dims *dm) {
+    if (!s) return NOSA_ERR_INVALID_ARGUMENT;
+    if (s->batch <= 0 || s->n_q_heads <= 0 || s->n_kv_heads <= 0 || s->head_dim <= 0 ||
+        s->block_size <= 0 || s->sub_block <= 0 || s->k_e < 0 || s->k_q < 0 ||
+        s->max_blocks <= 0)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (s->n_q_heads % s->n_kv_heads) return NOSA_ERR_INVALID_ARGUMENT;
+    if (s->block_size % s->sub_block) return NOSA_ERR_INVALID_ARGUMENT;
+    if (s->k_e + s->k_q <= 0 || s->k_e + s->k_q > s->max_blocks) return NOSA_ERR_INVALID_ARGUMENT;
+    if (s->dtype != NOSA_F32 && s->dtype != NOSA_BF16) return NOSA_ERR_INVALID_ARGUMENT;
+    if (s->decode_kernel < NOSA_DECODE_AUTO || s->decode_kernel > NOSA_DECODE_MFMA)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (!(s->scale >= 0.f) || isinf(s->scale)) return NOSA_ERR_INVALID_ARGUMENT;
+    const int G = s->n_q_heads / s->n_kv_heads;
+    if (s->block_size != 64 || s->sub_block != 16) return NOSA_ERR_UNSUPPORTED;
+    if (s->head_dim != 64 && s->head_dim != 128) return NOSA_ERR_UNSUPPORTED;
+    if (s->dtype == NOSA_F32 && s->head_dim != 64) return NOSA_ERR_UNSUPPORTED;
+    if (G > 8 || s->k_e + s->k_q > 128 || s->max_blocks > 4096) return NOSA_ERR_UNSUPPORTED;
+    if ((int64_t)s->batch * s->n_kv_heads > 65535) return NOSA_ERR_UNSUPPORTED;
+    dm->B = s->batch;
+    dm->Hq = s->n_q_heads;
+    dm->Hkv = s->n_kv_heads;
+    dm->G = G;
+    dm->D = s->head_dim;
+    dm->S = s->block_size;
+    dm->sub = s->sub_block;
+    dm->m = s->block_size / s->sub_block;
+    dm->k_e = s->k_e;
+    dm->k_q = s->k_q;
+    dm->k = s->k_e + s->k_q;
+    dm->max_blocks = s->max_blocks;
+    dm->W = (s->max_blocks + 31) / 32;
+    dm->rows = s->batch * s->n_kv_heads;
+    dm->dtype = s->dtype;
+    dm->scale = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
+    return NOSA_OK;
+}
+
+// Step fields checked against the shape: returns n_cand or -1.
+int step_cand(const Dims &dm, const nosa_step *st) {
+    if (!st || st->n_tokens <= 0) return -1;
+    const int n_cand = (st->n_tokens - 1) / dm.S;
+    if (n_cand >= dm.max_blocks) return -1;
+    if (st->n_cand_prev > n_cand) return -1;
+    return n_cand;
+}
+
+template <typename F> nosa_status by_type_dim(const Dims &dm, F &&f) {
+    if (dm.dtype == NOSA_F32)
+        return f((float *)nullptr, std::integral_constant<int, 64>{});
+    if (dm.D == 64) return f((bf16_t *)nullptr, std::integral_constant<int, 64>{});
+    return f((bf16_t *)nullptr, std::integral_constant<int, 128>{});
+}
+
+template <typename F> nosa_status by_group(const Dims &dm, F &&f) {
+    switch (dm.G) {
+    case 1: return f(std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 3: return f(std::integral_constant<int, 3>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+    case 5: return f(std::integral_constant<int, 5>{});
+    case 6: return f(std::integral_constant<int, 6>{});
+    case 7: return f(std::integral_constant<int, 7>{});
+    case 8: return f(std::integral_constant<int, 8>{});
+    default: return NOSA_ERR_UNSUPPORTED;
+    }
+}
+
+size_t decode_ws_bytes(const Dims &dm, const DecodePlan &pl) {
+    const size_t parts = (size_t)dm.rows * pl.n_chunks * dm.G;
+    return parts * dm.D * sizeof(float) + parts * 2 * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+nosa_status nosa_pool_blocks(const nosa_shape *shape, const void *kv, int64_t kv_row_blocks,
+                             int32_t kv_first_block, const float *e_tok, int64_t e_row_stride,
+                             int32_t blk_begin, int32_t blk_end, float *kbar, float *e_blk,
+                             void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!kv || !e_tok || !kbar || !e_blk) return NOSA_ERR_INVALID_ARGUMENT;
+    if (blk_begin < 0 || blk_end < blk_begin || blk_end > dm.max_blocks || kv_first_block < 0 ||
+        kv_row_blocks < kv_first_block + (blk_end - blk_begin) ||
+        e_row_stride < (int64_t)blk_end * dm.S)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (blk_end == blk_begin) return NOSA_OK;
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        return hip_status(launch_pool<T, decltype(dc)::value>(
+            dm, kv, kv_row_blocks, kv_first_block, e_tok, e_row_stride, blk_begin, blk_end, kbar,
+            e_blk, (hipStream_t)stream));
+    });
+}
+
+nosa_status nosa_score_blocks(const nosa_shape *shape, const void *q, const float *kbar,
+                              const nosa_step *step, float *s_q, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!q || !kbar || !s_q) return NOSA_ERR_INVALID_ARGUMENT;
+    const int n_cand = step_cand(dm, step);
+    if (n_cand < 0) return NOSA_ERR_INVALID_ARGUMENT;
+    if (n_cand == 0) return NOSA_OK;
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        constexpr int D = decltype(dc)::value;
+        return by_group(dm, [&](auto gc) -> nosa_status {
+            return hip_status(launch_score<T, D, decltype(gc)::value>(dm, q, kbar, n_cand, s_q,
+                                                                       (hipStream_t)stream));
+        });
+    });
+}
+
+nosa_status nosa_select(const nosa_shape *shape, const float *s_q, const float *e_blk,
+                        const nosa_step *step, uint32_t *ge_bits, uint32_t *ev_bits, int32_t *sel,
+                        int32_t *n_sel, uint32_t *sel_bits, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!s_q || !e_blk || !ge_bits || !ev_bits || !sel || !n_sel || !sel_bits)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    const int n_cand = step_cand(dm, step);
+    if (n_cand < 0) return NOSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_select(dm, s_q, e_blk, n_cand, step->n_cand_prev, ge_bits, ev_bits,
+                                    sel, n_sel, sel_bits, (hipStream_t)stream));
+}
+
+nosa_status nosa_swap_diff(const nosa_shape *shape, const int32_t *sel, const int32_t *n_sel,
+                           const uint32_t *sel_bits, int32_t *slot_block, int32_t *block_slot,
+                           int32_t *fetch_block, int32_t *fetch_slot, int32_t *n_fetch,
+                           uint64_t *counters, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!sel || !n_sel || !sel_bits || !slot_block || !block_slot || !fetch_block ||
+        !fetch_slot || !n_fetch || !counters)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_swap(dm, sel, n_sel, sel_bits, slot_block, block_slot, fetch_block,
+                                  fetch_slot, n_fetch, counters, (hipStream_t)stream));
+}
+
+nosa_status nosa_fetch_blocks(const nosa_shape *shape, const void *src_kv, int64_t src_row_blocks,
+                              const int32_t *fetch_block, const int32_t *fetch_slot,
+                              const int32_t *n_fetch, int32_t max_fetch, void *dst_kv,
+                              int64_t dst_row_blocks, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!src_kv || !fetch_block || !fetch_slot || !n_fetch || !dst_kv)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (max_fetch < 0 || max_fetch > dm.k || src_row_blocks <= 0 || dst_row_blocks <= 0)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (max_fetch == 0) return NOSA_OK;
+    return hip_status(launch_fetch(dm, src_kv, src_row_blocks, fetch_block, fetch_slot, n_fetch,
+                                   max_fetch, dst_kv, dst_row_blocks, (hipStream_t)stream));
+}
+
+size_t nosa_decode_workspace_size(const nosa_shape *shape) {
+    Dims dm;
+    if (make_dims(shape, &dm) != NOSA_OK) return 0;
+    return decode_ws_bytes(dm, decode_plan(dm));
+}
+
+nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *kv,
+                               int64_t kv_row_blocks, int32_t kv_mode, const int32_t *list,
+                               const int32_t *n_list, const void *cur_kv, int64_t cur_row_blocks,
+                               const nosa_step *step, const float *e_tok, int64_t e_row_stride,
+                               void *out, void *ws, size_t ws_bytes, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!q || !cur_kv || !e_tok || !out || !ws) return NOSA_ERR_INVALID_ARGUMENT;
+    if (kv_mode != NOSA_KV_FULL && kv_mode != NOSA_KV_CACHE) return NOSA_ERR_INVALID_ARGUMENT;
+    if (!kv || !list || (kv_mode == NOSA_KV_FULL && !n_list)) return NOSA_ERR_INVALID_ARGUMENT;
+    if (kv_mode == NOSA_KV_CACHE && kv_row_blocks < dm.k) return NOSA_ERR_INVALID_ARGUMENT;
+    if (kv_row_blocks <= 0 || cur_row_blocks <= 0) return NOSA_ERR_INVALID_ARGUMENT;
+    const int n_cand = step_cand(dm, step);
+    if (n_cand < 0 || e_row_stride < step->n_tokens) return NOSA_ERR_INVALID_ARGUMENT;
+    if (kv_mode == NOSA_KV_FULL && kv_row_blocks < n_cand + 1) return NOSA_ERR_INVALID_ARGUMENT;
+    const DecodePlan pl = decode_plan(dm);
+    if (ws_bytes < decode_ws_bytes(dm, pl)) return NOSA_ERR_WORKSPACE;
+    if (((uintptr_t)q | (uintptr_t)kv | (uintptr_t)cur_kv | (uintptr_t)ws) & 15u)
+        return NOSA_ERR_INVALID_ARGUMENT;
+
+    DecodeArgs a;
+    a.q = q;
+    a.kv = kv;
+    a.kv_row_blocks = kv_row_blocks;
+    a.kv_mode = kv_mode;
+    a.list = list;
+    a.n_list = n_list;
+    a.cur = cur_kv;
+    a.cur_row_blocks = cur_row_blocks;
+    a.n_tokens = step->n_tokens;
+    a.n_cand = n_cand;
+    a.e_tok = e_tok;
+    a.e_stride = e_row_stride;
+    a.out = out;
+    a.ws_o = static_cast<float *>(ws);
+    a.ws_ml = a.ws_o + (size_t)dm.rows * pl.n_chunks * dm.G * dm.D;
+    const hipStream_t st = (hipStream_t)stream;
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        constexpr int D = decltype(dc)::value;
+        return by_group(dm, [&](auto gc) -> nosa_status {
+            constexpr int G = decltype(gc)::value;
+            hipError_t e = launch_decode_valu<T, D, G>(dm, pl, a, st);
+            if (e != hipSuccess) return hip_status(e);
+            return hip_status(launch_combine<T, D, G>(dm, pl, a, st));
+        });
+    });
+}
+
+nosa_status nosa_host_alloc(size_t bytes, int32_t coherent, void **host, void **dev) {
+    if (!host || !dev || bytes == 0) return NOSA_ERR_INVALID_ARGUMENT;
+    *host = nullptr;
+    *dev = nullptr;
+    unsigned flags = hipHostMallocMapped | (coherent ? hipHostMallocCoherent : hipHostMallocNonCoherent);
+    void *h = nullptr;
+    hipError_t e = hipHostMalloc(&h, bytes, flags);
+    if (e != hipSuccess) return hip_status(e);
+    void *d = nullptr;
+    e = hipHostGetDevicePointer(&d, h, 0);
+    if (e != hipSuccess) {
+        (void)hipHostFree(h);
+        return hip_status(e);
+    }
+    *host = h;
+    *dev = d;
+    return NOSA_OK;
+}
+
+nosa_status nosa_host_free(void *host) {
+    if (!host) return NOSA_ERR_INVALID_ARGUMENT;
+    return hip_status(hipHostFree(host));
+}
+
+const char *nosa_status_string(nosa_status s) {
+    switch (s) {
+    case NOSA_OK: return "ok";
+    case NOSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case NOSA_ERR_UNSUPPORTED: return "unsupported shape";
+    case NOSA_ERR_HIP: return "HIP error";
+    case NOSA_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+    }
+}
+
+const char *nosa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t nosa_version(void) { return 100; }
+
+}  // extern "C"

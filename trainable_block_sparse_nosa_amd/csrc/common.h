@@ -1,0 +1,106 @@
+// Device helpers shared by the NOSA gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "nosa.h"
+
+namespace nosa {
+
+// Host-validated, derived shape passed by value to every kernel.
+struct Dims {
+    int B, Hq, Hkv, G, D, S, sub, m;
+    int k_e, k_q, k;
+    int max_blocks, W;  // per-row block capacity, bitmap words per row
+    int rows;
+    int dtype;
+    float scale;
+};
+
+using bf16_t = uint16_t;  // bfloat16 storage
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(uint32_t h16) { return __uint_as_float(h16 << 16); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float -> bfloat16, round to nearest even (inputs are finite).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float ldf(const T *p);
+template <> __device__ __forceinline__ float ldf<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float ldf<bf16_t>(const bf16_t *p) { return bf2f(*p); }
+
+template <typename T> __device__ __forceinline__ T stf(float v);
+template <> __device__ __forceinline__ float stf<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t stf<bf16_t>(float v) { return f2bf(v); }
+
+// Eight consecutive elements as floats from a 16-byte-aligned address (bf16)
+// or two 16-byte loads (fp32).
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16_t> {
+    __device__ __forceinline__ static void load(const bf16_t *p, float (&x)[8]) {
+        uint4 v = *reinterpret_cast<const uint4 *>(p);
+        x[0] = bf_lo(v.x); x[1] = bf_hi(v.x); x[2] = bf_lo(v.y); x[3] = bf_hi(v.y);
+        x[4] = bf_lo(v.z); x[5] = bf_hi(v.z); x[6] = bf_lo(v.w); x[7] = bf_hi(v.w);
+    }
+};
+template <> struct Vec8<float> {
+    __device__ __forceinline__ static void load(const float *p, float (&x)[8]) {
+        float4 a = reinterpret_cast<const float4 *>(p)[0];
+        float4 b = reinterpret_cast<const float4 *>(p)[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+};
+
+// Total order used by every selection: a higher score ranks first, an equal
+// score ranks the lower block id first. Keys compare as unsigned integers.
+__device__ __forceinline__ uint32_t orderable(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t rank_key(float score, int j) {
+    return ((uint64_t)orderable(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+__device__ __forceinline__ int key_index(uint64_t key) {
+    return (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
+}
+
+// DPP lane permutations inside groups of four lanes (quad_perm controls).
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int QUAD_SWAP1 = 0xB1;  // [1,0,3,2]
+constexpr int QUAD_SWAP2 = 0x4E;  // [2,3,0,1]
+
+__device__ __forceinline__ float quad_max(float v) {
+    v = fmaxf(v, dpp_f<QUAD_SWAP1>(v));
+    v = fmaxf(v, dpp_f<QUAD_SWAP2>(v));
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const unsigned lane = threadIdx.x & 63u;
+    return lane ? (~0ull >> (64u - lane)) : 0ull;
+}
+
+}  // namespace nosa

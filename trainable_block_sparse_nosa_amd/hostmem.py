@@ -1,0 +1,39 @@
+"""Pinned host memory that GPU kernels read directly (over PCIe)."""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib as L
+
+
+class PinnedBuffer:
+    """``nbytes`` of pinned, device-mapped host memory.
+
+    ``host`` is the host address, ``dev`` the device alias that kernels take
+    as a source pointer; ``array(dtype, shape)`` views the memory from numpy.
+    """
+
+    def __init__(self, nbytes: int, coherent: bool = False):
+        self.nbytes = int(nbytes)
+        self.host, self.dev = L.nosa_host_alloc(self.nbytes, coherent)
+
+    def array(self, dtype, shape) -> np.ndarray:
+        dtype = np.dtype(dtype)
+        n = int(np.prod(shape))
+        if n * dtype.itemsize > self.nbytes:
+            raise ValueError("view larger than the buffer")
+        raw = (ctypes.c_uint8 * (n * dtype.itemsize)).from_address(self.host)
+        return np.frombuffer(raw, dtype=dtype, count=n).reshape(shape)
+
+    def free(self):
+        if self.host:
+            L.nosa_host_free(self.host)
+            self.host = self.dev = 0
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass

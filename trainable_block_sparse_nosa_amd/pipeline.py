@@ -1,0 +1,172 @@
+"""Host-side sequencing of the NOSA decode path for one layer.
+
+Every stage of a step runs in the library's kernels; this module allocates
+the device buffers (through torch) and issues the C-ABI calls in order, all
+on one stream with no host synchronisation inside a step.
+
+Per decode step (NOSA technical summary, Methodology):
+  pool      a block that just became complete joins the candidates: its
+            sub-block mean keys and pooled eviction score are computed once
+  score     query-aware pooled score of every candidate block
+  select    Gamma_e (eviction budget, strict eviction) and Gamma_q (top k_q)
+  swap      set difference against the blocks cached in HBM
+  fetch     (offloaded KV) copy of the missing blocks from pinned host memory
+  decode    attention over the selection plus the newest block, eviction
+            score as an additive logit
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+BLOCK = 64
+SUB_BLOCK = 16
+
+
+def pack_blocks(K: np.ndarray, V: np.ndarray, n_blocks: int) -> np.ndarray:
+    """Block-unit layout of one row: [n_blocks, 2*64*D] with, per block, the K
+    tile [64][D] followed by the V tile transposed [D][64]. Tokens beyond the
+    input are zero. Works on float32 or bfloat16-bit (uint16) arrays."""
+    n, D = K.shape
+    pad = n_blocks * BLOCK - n
+    if pad < 0:
+        raise ValueError("more tokens than blocks")
+    if pad:
+        K = np.concatenate([K, np.zeros((pad, D), K.dtype)])
+        V = np.concatenate([V, np.zeros((pad, D), V.dtype)])
+    Kb = K.reshape(n_blocks, BLOCK * D)
+    Vt = V.reshape(n_blocks, BLOCK, D).transpose(0, 2, 1).reshape(n_blocks, D * BLOCK)
+    return np.ascontiguousarray(np.concatenate([Kb, Vt], axis=1))
+
+
+def torch_dtype(dtype: int):
+    return torch.float32 if dtype == L.NOSA_F32 else torch.bfloat16
+
+
+class DecodeLayer:
+    """Device state and call sequence of one layer.
+
+    kv:     resident mode: device tensor [rows, kv_row_blocks, 2*64*D];
+            offload mode: integer device alias of pinned host memory with the
+            same layout.
+    e_tok:  device float32 tensor [rows, e_row_stride].
+    """
+
+    def __init__(self, *, batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks, dtype,
+                 kv, kv_row_blocks, e_tok, offload=False, decode_kernel=L.NOSA_DECODE_AUTO,
+                 scale=0.0, device="cuda"):
+        self.shape = L.make_shape(batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks,
+                                  dtype, decode_kernel=decode_kernel, scale=scale)
+        self.rows = batch * n_kv_heads
+        self.k = k_e + k_q
+        self.D = head_dim
+        self.G = n_q_heads // n_kv_heads
+        self.max_blocks = max_blocks
+        self.W = (max_blocks + 31) // 32
+        self.dtype = dtype
+        self.offload = offload
+        self.kv = kv
+        self.kv_row_blocks = kv_row_blocks
+        self.e_tok = e_tok
+        self.e_stride = e_tok.shape[1]
+        self.block_elems = 2 * BLOCK * head_dim
+        self.elem_bytes = 4 if dtype == L.NOSA_F32 else 2
+        dev = torch.device(device)
+        R, k, W = self.rows, self.k, self.W
+        f32, i32 = torch.float32, torch.int32
+        self.kbar = torch.zeros(R, head_dim // 4, 4 * max_blocks, 4, dtype=f32, device=dev)
+        self.e_blk = torch.zeros(R, max_blocks, dtype=f32, device=dev)
+        self.s_q = torch.zeros(R, max_blocks, dtype=f32, device=dev)
+        self.ge_bits = torch.zeros(R, W, dtype=i32, device=dev)
+        self.ev_bits = torch.zeros(R, W, dtype=i32, device=dev)
+        self.sel_bits = torch.zeros(R, W, dtype=i32, device=dev)
+        self.sel = torch.full((R, k), -1, dtype=i32, device=dev)
+        self.n_sel = torch.zeros(R, dtype=i32, device=dev)
+        self.slot_block = torch.full((R, k), -1, dtype=i32, device=dev)
+        self.block_slot = torch.full((R, max_blocks), -1, dtype=i32, device=dev)
+        self.fetch_block = torch.full((R, k), -1, dtype=i32, device=dev)
+        self.fetch_slot = torch.full((R, k), -1, dtype=i32, device=dev)
+        self.n_fetch = torch.zeros(R, dtype=i32, device=dev)
+        self.counters = torch.zeros(R, 2, dtype=torch.int64, device=dev)
+        self.ws_bytes = L.nosa_decode_workspace_size(self.shape)
+        self.ws = torch.empty(self.ws_bytes // 4 + 4, dtype=f32, device=dev)
+        self.out = torch.empty(batch, n_q_heads, head_dim, dtype=torch_dtype(dtype), device=dev)
+        if offload:
+            self.cache = torch.empty(R, k, self.block_elems, dtype=torch_dtype(dtype), device=dev)
+            self.cur = torch.empty(R, 1, self.block_elems, dtype=torch_dtype(dtype), device=dev)
+            # one-entry fetch list that loads the newest block into `cur`
+            self.cur_fb = torch.zeros(R, k, dtype=i32, device=dev)
+            self.cur_fs = torch.zeros(R, k, dtype=i32, device=dev)
+            self.cur_nf = torch.ones(R, dtype=i32, device=dev)
+        self.n_cand_prev = -1
+        self.n_tokens = 0
+
+    # -- helpers -------------------------------------------------------------
+    def _kv_ptr(self, block: int) -> int:
+        base = self.kv if isinstance(self.kv, int) else self.kv.data_ptr()
+        return base + block * self.block_elems * self.elem_bytes
+
+    def _load_cur(self, block: int, stream=None):
+        self.cur_fb[:, 0].fill_(block)
+        L.nosa_fetch_blocks(self.shape, self.kv, self.kv_row_blocks, self.cur_fb, self.cur_fs,
+                            self.cur_nf, 1, self.cur, 1, stream)
+
+    # -- call sequence -------------------------------------------------------
+    def start(self, n_tokens: int, stream=None):
+        """Prefill stand-in: pool the complete blocks of the first n_tokens - 1
+        tokens (the candidates of the step that brings n_tokens) and, with
+        offloaded KV, load the newest block."""
+        c0 = (n_tokens - 1) // BLOCK
+        if c0 > 0:
+            L.nosa_pool_blocks(self.shape, self.kv, self.kv_row_blocks, 0, self.e_tok,
+                               self.e_stride, 0, c0, self.kbar, self.e_blk, stream)
+        if self.offload:
+            self._load_cur(c0, stream)
+        self.n_cand_prev = -1
+        self.pooled = c0
+
+    def step(self, q: torch.Tensor, n_tokens: int, stream=None, swap: bool = True) -> torch.Tensor:
+        """One decode step at n_tokens tokens (the newest appended by this step)."""
+        c = (n_tokens - 1) // BLOCK
+        if c > self.pooled:
+            if self.offload:
+                assert c == self.pooled + 1, "offloaded KV grows by one block per step"
+                # the completed block is the newest-block buffer's content
+                L.nosa_pool_blocks(self.shape, self.cur, 1, 0, self.e_tok, self.e_stride,
+                                   self.pooled, c, self.kbar, self.e_blk, stream)
+                self._load_cur(c, stream)
+            else:
+                L.nosa_pool_blocks(self.shape, self.kv, self.kv_row_blocks, self.pooled,
+                                   self.e_tok, self.e_stride, self.pooled, c, self.kbar,
+                                   self.e_blk, stream)
+            self.pooled = c
+        st = L.make_step(n_tokens, self.n_cand_prev)
+        L.nosa_score_blocks(self.shape, q, self.kbar, st, self.s_q, stream)
+        L.nosa_select(self.shape, self.s_q, self.e_blk, st, self.ge_bits, self.ev_bits, self.sel,
+                      self.n_sel, self.sel_bits, stream)
+        if swap or self.offload:
+            L.nosa_swap_diff(self.shape, self.sel, self.n_sel, self.sel_bits, self.slot_block,
+                             self.block_slot, self.fetch_block, self.fetch_slot, self.n_fetch,
+                             self.counters, stream)
+        if self.offload:
+            L.nosa_fetch_blocks(self.shape, self.kv, self.kv_row_blocks, self.fetch_block,
+                                self.fetch_slot, self.n_fetch, self.k, self.cache, self.k, stream)
+            L.nosa_sparse_decode(self.shape, q, self.cache, self.k, L.NOSA_KV_CACHE,
+                                 self.slot_block, None, self.cur, 1, st, self.e_tok,
+                                 self.e_stride, self.out, self.ws, self.ws_bytes, stream)
+        else:
+            L.nosa_sparse_decode(self.shape, q, self.kv, self.kv_row_blocks, L.NOSA_KV_FULL,
+                                 self.sel, self.n_sel, self._kv_ptr(c), self.kv_row_blocks, st,
+                                 self.e_tok, self.e_stride, self.out, self.ws, self.ws_bytes,
+                                 stream)
+        self.n_cand_prev = c
+        self.n_tokens = n_tokens
+        return self.out
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)
