@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of the NOSA per-decode-step path on one MI355X.
+
+A step is one pass of the whole path over one batch: pooling of a block that
+just became complete (every 64 steps), block scoring, dual selection (Gamma_e
+and Gamma_q), set difference against the cached blocks, block fetch from
+pinned host memory (offloaded workloads only) and sparse decode attention.
+
+Default workload: batch 8, 32 query / 8 KV heads, head_dim 128, 32k-token
+context, blocks of 64 with sub-blocks of 16, budget k = 48 + 16, bf16, KV in
+HBM. Inputs are synthetic (seeded Philox streams), already resident in HBM
+when the timed region starts.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode steps/s + attn HBM GB/s (% peak); swap GB/s (% PCIe)"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bf16_1layer_32k")
+    ap.add_argument("--decode-kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the oracle sample (0 = skip)")
+    ap.add_argument("--no-stage-breakdown", action="store_true")
+    return ap.parse_args()
+
+
+def decode_bytes(w, n_tokens: int, n_sel: int) -> int:
+    """Algorithmic HBM bytes of one attention launch over all rows: the K and V
+    of every selected block and of the newest block's tokens, one float32
+    eviction score per attended token, the queries and the outputs."""
+    elem = 4 if w.dtype == "f32" else 2
+    c = (n_tokens - 1) // 64
+    cur = n_tokens - 64 * c
+    toks = n_sel * 64 + cur
+    per_row = toks * 2 * w.head_dim * elem + toks * 4
+    qo = 2 * w.batch * w.n_q_heads * w.head_dim * elem
+    return w.rows * per_row + qo
+
+
+def cpu_baseline(w, seconds: float, steps_avail: int):
+    """Time the fp64 oracle (single thread) on a bounded sample of row-steps of
+    the same workload (rows in order, step 0 first, then step 1, ...) and scale
+    the mean time per row-step to whole steps of all rows."""
+    import oracle
+    import synth
+    sc = 1.0 / math.sqrt(w.head_dim)
+    done, t_used = 0, 0.0
+    rows = {}
+    t = 0
+    while t_used < seconds and t < steps_avail:
+        q_t = synth.queries_step(w, 0, t)
+        for r in range(w.rows):
+            b, g = divmod(r, w.n_kv_heads)
+            if r not in rows:
+                rows[r] = (synth.keys_row(w, 0, b, g), synth.values_row(w, 0, b, g),
+                           synth.evict_row(w, 0, b, g))
+            K, V, e = rows[r]
+            q = q_t[b, g * w.group:(g + 1) * w.group]
+            t0 = time.perf_counter()
+            oracle.step_row(w.n_tokens(t), q, K, V, e, 64, 16, w.k_e, w.k_q, sc)
+            t_used += time.perf_counter() - t0
+            done += 1
+            if t_used >= seconds:
+                break
+        t += 1
+    per_row_step = t_used / done
+    return {
+        "value": 1.0 / (per_row_step * w.rows), "unit": "steps/s", "cores": 1, "kind": "oracle",
+        "sample": f"{done} row-steps of {w.name} (all {w.rows} rows of steps 0..{t - 1}, "
+                  f"row-major), {t_used:.1f} s of single-threaded fp64 oracle time, scaled "
+                  f"to {w.rows} rows per step",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(rows shard across GPUs with no exchange; only the one-GPU share is measured)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from trainable_block_sparse_nosa_amd import _lib as L
+    from trainable_block_sparse_nosa_amd.hostmem import PinnedBuffer
+    from trainable_block_sparse_nosa_amd.pipeline import DecodeLayer, pack_blocks
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    base = synth.WORKLOADS[args.workload]
+    T = args.warmup + args.steps
+    w = base.scaled(steps=max(base.steps, T))
+    kind = {"auto": L.NOSA_DECODE_AUTO, "valu": L.NOSA_DECODE_VALU,
+            "mfma": L.NOSA_DECODE_MFMA}[args.decode_kernel]
+    log(f"workload {w.name}: rows={w.rows} G={w.group} D={w.head_dim} ctx={w.context} "
+        f"k={w.k_e}+{w.k_q} steps={T} offload={w.offload}")
+
+    # ---- inputs (untimed) ----
+    t0 = time.time()
+    nb = w.nb_max
+    BE = 2 * 64 * w.head_dim
+    elem = 4 if w.dtype == "f32" else 2
+
+    def conv(x):
+        return np.ascontiguousarray(x, np.float32) if w.dtype == "f32" else synth.bf16_bits(x)
+
+    def row_blocks(r):
+        b, g = divmod(r, w.n_kv_heads)
+        return pack_blocks(conv(synth.keys_row(w, 0, b, g)), conv(synth.values_row(w, 0, b, g)), nb)
+
+    def to_dev(a):
+        if w.dtype == "f32":
+            return torch.from_numpy(a).to(dev)
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    host = None
+    if w.offload:
+        host = PinnedBuffer(w.rows * nb * BE * elem)
+        view = host.array(np.float32 if w.dtype == "f32" else np.uint16, (w.rows, nb, BE))
+
+        def fill(r):
+            view[r] = row_blocks(r)
+        synth.parallel_map(fill, range(w.rows), 16)
+        kv, kv_ptr = host, host.dev
+    else:
+        kv = torch.empty(w.rows, nb, BE, dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16,
+                         device=dev)
+        for r0 in range(0, w.rows, 16):
+            rr = list(range(r0, min(w.rows, r0 + 16)))
+            for r, p in zip(rr, synth.parallel_map(row_blocks, rr, 16)):
+                kv[r].copy_(to_dev(p))
+        kv_ptr = kv
+    e = np.stack(synth.parallel_map(lambda r: synth.evict_row(w, 0, *divmod(r, w.n_kv_heads)),
+                                    range(w.rows), 16))
+    e_tok = torch.from_numpy(e).to(dev)
+    q = to_dev(np.stack(synth.parallel_map(lambda t: conv(synth.queries_step(w, 0, t)), range(T), 16)))
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+
+    layer = DecodeLayer(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                        head_dim=w.head_dim, k_e=w.k_e, k_q=w.k_q, max_blocks=nb,
+                        dtype=L.NOSA_F32 if w.dtype == "f32" else L.NOSA_BF16, kv=kv_ptr,
+                        kv_row_blocks=nb, e_tok=e_tok, offload=w.offload, decode_kernel=kind)
+    stream = torch.cuda.current_stream()
+
+    # ---- warmup (untimed) ----
+    layer.start(w.n_tokens(0), stream)
+    for t in range(args.warmup):
+        layer.step(q[t], w.n_tokens(t), stream)
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    # ---- timed region: exactly args.steps steps ----
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    slot = {"i": 0}
+
+    def decode_events(name, fn, *a):
+        if name == "decode":
+            e0, e1 = ev[slot["i"]]
+            e0.record(stream)
+            fn(*a)
+            e1.record(stream)
+        else:
+            fn(*a)
+
+    layer.stage_hook = decode_events
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        slot["i"] = i
+        layer.step(q[args.warmup + i], w.n_tokens(args.warmup + i), stream)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    layer.stage_hook = None
+    elapsed = t_end - t_start
+    n_sel = layer.n_sel.cpu().numpy()
+    dec_bytes = []
+    for i in range(args.steps):
+        dec_bytes.append(decode_bytes(w, w.n_tokens(args.warmup + i), int(np.min(n_sel))))
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    bytes_avg = sum(dec_bytes) / len(dec_bytes)
+    achieved = bytes_avg / dec_avg_s / 1e9
+    steps_per_s = args.steps / elapsed
+    log(f"timed {args.steps} steps in {elapsed * 1e3:.1f} ms: {steps_per_s:.1f} steps/s, "
+        f"attention {dec_avg_s * 1e6:.1f} us/launch, {achieved:.0f} GB/s")
+
+    counters = layer.counters.cpu().numpy()
+    steps_total = args.warmup + args.steps
+    gamma_mean = float(counters[:, 1].sum()) / (w.rows * w.k * steps_total)
+
+    # ---- stage breakdown (separate, untimed pass with events between stages) ----
+    stages = None
+    if not args.no_stage_breakdown:
+        stages = stage_breakdown(layer, w, q, args.warmup, min(args.steps, 50), stream)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("timing the oracle sample on the host")
+        cpu = cpu_baseline(w, args.cpu_seconds, T)
+
+    result = {
+        "metric": METRIC,
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "layers": w.n_layers, "batch": w.batch, "n_q_heads": w.n_q_heads,
+            "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": w.context,
+            "block": 64, "sub_block": 16, "k_e": w.k_e, "k_q": w.k_q,
+            "kv": "pinned host" if w.offload else "hbm", "decode_kernel": args.decode_kernel,
+        },
+        "roofline": {
+            "kernel": "sparse decode attention (nosa_sparse_decode: split-K partial + combine)",
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "avg_launch_us": dec_avg_s * 1e6, "algorithmic_bytes_per_launch": bytes_avg,
+        },
+        "attn_us_per_layer_step": dec_avg_s * 1e6,
+        "gamma_mean": gamma_mean,
+        "cpu_baseline": cpu,
+    }
+    if stages:
+        result["stages_us"] = stages
+    print(json.dumps(result), flush=True)
+
+
+def stage_breakdown(layer, w, q, t0: int, n: int, stream):
+    """Per-stage GPU time (us per call) from events placed around each stage's
+    launch, on a replay of the timed steps from a fresh start."""
+    import torch
+    pending = []
+
+    def hook(name, fn, *a):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn(*a)
+        e1.record(stream)
+        pending.append((name, e0, e1))
+
+    layer.start(w.n_tokens(0), stream)
+    for t in range(t0):
+        layer.step(q[t], w.n_tokens(t), stream)
+    layer.stage_hook = hook
+    try:
+        for t in range(t0, t0 + n):
+            layer.step(q[t], w.n_tokens(t), stream)
+        torch.cuda.synchronize()
+    finally:
+        layer.stage_hook = None
+    acc, cnt = {}, {}
+    for name, e0, e1 in pending:
+        acc[name] = acc.get(name, 0.0) + e0.elapsed_time(e1) * 1e3
+        cnt[name] = cnt.get(name, 0) + 1
+    return {k: acc[k] / cnt[k] for k in acc}
+
+
+if __name__ == "__main__":
+    main()

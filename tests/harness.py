@@ -82,6 +82,8 @@ class OracleTrace:
     ov: Overrides
     step: dict = field(default_factory=dict)     # (t, row) -> oracle.RowStep
     swap: dict = field(default_factory=dict)     # (t, row) -> oracle.SwapResult
+    # magnitude of the terms a pooled score sums: scale * sum_h |q_h| * max_token |k|
+    term_scale: dict = field(default_factory=dict)  # (t, row) -> float
 
 
 def oracle_trace(w: Workload, layer: int = 0, rows=None, steps=None, ov: Overrides | None = None,
@@ -104,6 +106,7 @@ def oracle_trace(w: Workload, layer: int = 0, rows=None, steps=None, ov: Overrid
         e = enforce_evict_margins(w, layer, b, g, steps, ov) if margins else \
             synth.evict_row(w, layer, b, g, ov)
         cache = oracle.SlotCache(w.k)
+        kmax = float(np.sqrt(np.max(np.sum(K.astype(np.float64) ** 2, axis=1))))
         for t in steps:
             for _ in range(64):
                 q = group_q(w, layer, t, b, g, ov)
@@ -120,6 +123,8 @@ def oracle_trace(w: Workload, layer: int = 0, rows=None, steps=None, ov: Overrid
             else:
                 raise RuntimeError("could not enforce query margins")
             tr.step[(t, r)] = res
+            qn = float(np.sum(np.sqrt(np.sum(q.astype(np.float64) ** 2, axis=1))))
+            tr.term_scale[(t, r)] = sc * qn * kmax
             if swaps:
                 tr.swap[(t, r)] = cache.step(res.selected)
     return tr

@@ -42,7 +42,7 @@ def _shape(**kw):
 @pytest.mark.parametrize("bad,status", [
     (dict(n_q_heads=7), 1),           # heads not a multiple of KV heads
     (dict(head_dim=96), 2),           # unsupported head_dim
-    (dict(k_e=100, k_q=100), 1),      # budget above capacity
+    (dict(k_e=100, k_q=100), 2),      # budget above 128 blocks
     (dict(k_e=0, k_q=0), 1),          # empty budget
     (dict(dtype=5), 1),
     (dict(block_size=48), 2),

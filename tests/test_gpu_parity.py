@@ -30,12 +30,14 @@ def _compare_step(w, tr, t, r, got, check_swap=True, check_slots=True):
     ref = tr.step[(t, r)]
     c = ref.n_cand
     where = f"{w.name} t={t} row={r}"
-    # pooled scores: float32 accumulation of float32/bf16 inputs
+    # pooled scores: float32 accumulation. A D-term float32 dot product errs by
+    # about sqrt(D) * 2^-24 times the magnitude of its terms; 2e-6 of the term
+    # scale covers D = 128 with room, and stays far inside the 1e-4 selection
+    # margin the inputs are drawn with.
     if c:
         np.testing.assert_allclose(got["e_blk"][r, :c], ref.E, rtol=0, atol=2e-6, err_msg=where)
-        rms = float(np.sqrt(np.mean(ref.S ** 2)))
-        np.testing.assert_allclose(got["s_q"][r, :c], ref.S, rtol=2e-6, atol=2e-6 * rms,
-                                   err_msg=where)
+        np.testing.assert_allclose(got["s_q"][r, :c], ref.S, rtol=0,
+                                   atol=2e-6 * tr.term_scale[(t, r)], err_msg=where)
     # selections: bit-exact
     assert gh.bits_to_list(got["ge_bits"][r]) == ref.gamma_e, where
     n = int(got["n_sel"][r])

@@ -26,7 +26,7 @@ nosa_status make_dims(const nosa_shape *s, Dims *dm) {
         return NOSA_ERR_INVALID_ARGUMENT;
     if (s->n_q_heads % s->n_kv_heads) return NOSA_ERR_INVALID_ARGUMENT;
     if (s->block_size % s->sub_block) return NOSA_ERR_INVALID_ARGUMENT;
-    if (s->k_e + s->k_q <= 0 || s->k_e + s->k_q > s->max_blocks) return NOSA_ERR_INVALID_ARGUMENT;
+    if (s->k_e + s->k_q <= 0) return NOSA_ERR_INVALID_ARGUMENT;
     if (s->dtype != NOSA_F32 && s->dtype != NOSA_BF16) return NOSA_ERR_INVALID_ARGUMENT;
     if (s->decode_kernel < NOSA_DECODE_AUTO || s->decode_kernel > NOSA_DECODE_MFMA)
         return NOSA_ERR_INVALID_ARGUMENT;

@@ -104,16 +104,25 @@ class DecodeLayer:
             self.cur_nf = torch.ones(R, dtype=i32, device=dev)
         self.n_cand_prev = -1
         self.n_tokens = 0
+        # optional callable(stage_name, fn, *args): runs fn(*args); a caller
+        # may wrap the launch (for example with timing events)
+        self.stage_hook = None
 
     # -- helpers -------------------------------------------------------------
+    def _run(self, name, fn, *args):
+        if self.stage_hook is None:
+            fn(*args)
+        else:
+            self.stage_hook(name, fn, *args)
+
     def _kv_ptr(self, block: int) -> int:
         base = self.kv if isinstance(self.kv, int) else self.kv.data_ptr()
         return base + block * self.block_elems * self.elem_bytes
 
     def _load_cur(self, block: int, stream=None):
         self.cur_fb[:, 0].fill_(block)
-        L.nosa_fetch_blocks(self.shape, self.kv, self.kv_row_blocks, self.cur_fb, self.cur_fs,
-                            self.cur_nf, 1, self.cur, 1, stream)
+        self._run("fetch_newest", L.nosa_fetch_blocks, self.shape, self.kv, self.kv_row_blocks,
+                  self.cur_fb, self.cur_fs, self.cur_nf, 1, self.cur, 1, stream)
 
     # -- call sequence -------------------------------------------------------
     def start(self, n_tokens: int, stream=None):
@@ -136,33 +145,33 @@ class DecodeLayer:
             if self.offload:
                 assert c == self.pooled + 1, "offloaded KV grows by one block per step"
                 # the completed block is the newest-block buffer's content
-                L.nosa_pool_blocks(self.shape, self.cur, 1, 0, self.e_tok, self.e_stride,
-                                   self.pooled, c, self.kbar, self.e_blk, stream)
+                self._run("pool", L.nosa_pool_blocks, self.shape, self.cur, 1, 0, self.e_tok,
+                          self.e_stride, self.pooled, c, self.kbar, self.e_blk, stream)
                 self._load_cur(c, stream)
             else:
-                L.nosa_pool_blocks(self.shape, self.kv, self.kv_row_blocks, self.pooled,
-                                   self.e_tok, self.e_stride, self.pooled, c, self.kbar,
-                                   self.e_blk, stream)
+                self._run("pool", L.nosa_pool_blocks, self.shape, self.kv, self.kv_row_blocks,
+                          self.pooled, self.e_tok, self.e_stride, self.pooled, c, self.kbar,
+                          self.e_blk, stream)
             self.pooled = c
         st = L.make_step(n_tokens, self.n_cand_prev)
-        L.nosa_score_blocks(self.shape, q, self.kbar, st, self.s_q, stream)
-        L.nosa_select(self.shape, self.s_q, self.e_blk, st, self.ge_bits, self.ev_bits, self.sel,
-                      self.n_sel, self.sel_bits, stream)
+        self._run("score", L.nosa_score_blocks, self.shape, q, self.kbar, st, self.s_q, stream)
+        self._run("select", L.nosa_select, self.shape, self.s_q, self.e_blk, st, self.ge_bits,
+                  self.ev_bits, self.sel, self.n_sel, self.sel_bits, stream)
         if swap or self.offload:
-            L.nosa_swap_diff(self.shape, self.sel, self.n_sel, self.sel_bits, self.slot_block,
-                             self.block_slot, self.fetch_block, self.fetch_slot, self.n_fetch,
-                             self.counters, stream)
+            self._run("swap", L.nosa_swap_diff, self.shape, self.sel, self.n_sel, self.sel_bits,
+                      self.slot_block, self.block_slot, self.fetch_block, self.fetch_slot,
+                      self.n_fetch, self.counters, stream)
         if self.offload:
-            L.nosa_fetch_blocks(self.shape, self.kv, self.kv_row_blocks, self.fetch_block,
-                                self.fetch_slot, self.n_fetch, self.k, self.cache, self.k, stream)
-            L.nosa_sparse_decode(self.shape, q, self.cache, self.k, L.NOSA_KV_CACHE,
-                                 self.slot_block, None, self.cur, 1, st, self.e_tok,
-                                 self.e_stride, self.out, self.ws, self.ws_bytes, stream)
+            self._run("fetch", L.nosa_fetch_blocks, self.shape, self.kv, self.kv_row_blocks,
+                      self.fetch_block, self.fetch_slot, self.n_fetch, self.k, self.cache, self.k,
+                      stream)
+            self._run("decode", L.nosa_sparse_decode, self.shape, q, self.cache, self.k,
+                      L.NOSA_KV_CACHE, self.slot_block, None, self.cur, 1, st, self.e_tok,
+                      self.e_stride, self.out, self.ws, self.ws_bytes, stream)
         else:
-            L.nosa_sparse_decode(self.shape, q, self.kv, self.kv_row_blocks, L.NOSA_KV_FULL,
-                                 self.sel, self.n_sel, self._kv_ptr(c), self.kv_row_blocks, st,
-                                 self.e_tok, self.e_stride, self.out, self.ws, self.ws_bytes,
-                                 stream)
+            self._run("decode", L.nosa_sparse_decode, self.shape, q, self.kv, self.kv_row_blocks,
+                      L.NOSA_KV_FULL, self.sel, self.n_sel, self._kv_ptr(c), self.kv_row_blocks,
+                      st, self.e_tok, self.e_stride, self.out, self.ws, self.ws_bytes, stream)
         self.n_cand_prev = c
         self.n_tokens = n_tokens
         return self.out
