@@ -50,10 +50,13 @@
  * --------------------------------------------------
  * q, out     [batch][n_q_heads][D]
  * KV block   one block-unit of 2*S*D elements: the K tile [S][D] (token
- *            major) followed by the V tile stored transposed, [D][S]. A
- *            "KV buffer" is [rows][row_blocks][2*S*D]; the full KV, an HBM
- *            block cache (k slots per row) and the newest-block buffer (one
- *            block per row) all use it with their own row_blocks.
+ *            major) followed by the V tile stored transposed, [D][S], whose
+ *            row positions hold the block's tokens in this order: inside
+ *            each half of 32, positions 8j..8j+7 hold tokens 4j..4j+3 and
+ *            16+4j..16+4j+3 of that half (the order the MFMA decode consumes
+ *            them in). A "KV buffer" is [rows][row_blocks][2*S*D]; the full
+ *            KV, an HBM block cache (k slots per row) and the newest-block
+ *            buffer (one block per row) all use it with their own row_blocks.
  * e_tok      float32 [rows][e_row_stride]: per-token eviction scores,
  *            pre-exponential.
  * kbar       float32 [rows][D/4][m*max_blocks][4], m = S / sub_block: the
@@ -180,7 +183,8 @@ nosa_status nosa_fetch_blocks(const nosa_shape *shape, const void *src_kv, int64
                               const int32_t *n_fetch, int32_t max_fetch, void *dst_kv,
                               int64_t dst_row_blocks, void *stream);
 
-/* Workspace bytes nosa_sparse_decode needs for this shape (split-K partials). */
+/* Workspace bytes nosa_sparse_decode needs for this shape (split-K partials).
+ * Calls that overlap in time need separate workspaces. */
 size_t nosa_decode_workspace_size(const nosa_shape *shape);
 
 /* Sparse decode attention for every query head (Methodology, "ED-DMA"):
@@ -193,8 +197,10 @@ size_t nosa_decode_workspace_size(const nosa_shape *shape);
  *   slot_block table (block id per slot, -1 = empty, skipped); n_list unused.
  * The newest block of row r is block 0 of row r of cur_kv (cur_row_blocks
  *   blocks per row); for the full KV pass kv advanced by n_cand blocks.
- * Split-K partials go to ws (at least nosa_decode_workspace_size bytes);
- * a fixed-order combine writes out (float32 accumulate, bf16 RNE store). */
+ * Split-K partials go to ws (at least nosa_decode_workspace_size bytes); a
+ * second kernel merges each row's partials in a fixed order and writes out
+ * (float32 accumulation, bf16 stores round to nearest even). shape.decode_kernel picks the partial kernel: MFMA (bf16
+ * only; the default for bf16) or VALU (the default for float32). */
 nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *kv,
                                int64_t kv_row_blocks, int32_t kv_mode, const int32_t *list,
                                const int32_t *n_list, const void *cur_kv, int64_t cur_row_blocks,

@@ -118,9 +118,9 @@ def snapshot(layer: DecodeLayer, w: Workload) -> dict:
 
 
 def run(w: Workload, inp: GpuInputs, steps, layer: DecodeLayer | None = None,
-        collect=None, swap=True):
+        collect=None, swap=True, decode_kernel=L.NOSA_DECODE_AUTO):
     """Run steps 0..max(steps) in order; snapshot the steps listed in ``collect``."""
-    layer = layer or make_layer(w, inp)
+    layer = layer or make_layer(w, inp, decode_kernel)
     T = max(steps) + 1
     collect = set(steps if collect is None else collect)
     layer.start(w.n_tokens(0))

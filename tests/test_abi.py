@@ -10,6 +10,20 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def _no_gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+# These tests hand made-up pointers to the entry points to check that host-side
+# validation rejects them; they must never run where a kernel could launch.
+fake_pointers = pytest.mark.skipif(not _no_gpu_visible(),
+                                   reason="made-up pointers are only passed where no GPU exists")
+
+
 def _declared():
     with open(os.path.join(ROOT, "include", "nosa.h")) as f:
         text = f.read()
@@ -39,6 +53,7 @@ def _shape(**kw):
     return L.make_shape(**a)
 
 
+@fake_pointers
 @pytest.mark.parametrize("bad,status", [
     (dict(n_q_heads=7), 1),           # heads not a multiple of KV heads
     (dict(head_dim=96), 2),           # unsupported head_dim
@@ -60,10 +75,12 @@ def test_invalid_shapes_rejected(bad, status):
     assert rc == status
 
 
+@fake_pointers
 def test_invalid_pointers_and_steps_rejected():
     from trainable_block_sparse_nosa_amd import _lib as L
     lib = L.lib()
-    sh = _shape()
+    # the VALU plan needs the largest workspace, so a short one fails its check
+    sh = _shape(decode_kernel=L.NOSA_DECODE_VALU)
     ok_step = L.make_step(100, -1)
     # null pointers
     assert lib.nosa_score_blocks(ctypes.byref(sh), None, 16, ctypes.byref(ok_step), 16, None) == 1
@@ -102,3 +119,7 @@ def test_invalid_pointers_and_steps_rejected():
     h, d = ctypes.c_void_p(), ctypes.c_void_p()
     assert lib.nosa_host_alloc(0, 0, ctypes.byref(h), ctypes.byref(d)) == 1
     assert lib.nosa_status_string(2) == b"unsupported shape"
+    # MFMA decode is bf16 only
+    f32 = _shape(dtype=L.NOSA_F32, head_dim=64, decode_kernel=L.NOSA_DECODE_MFMA)
+    assert lib.nosa_sparse_decode(ctypes.byref(f32), 16, 16, 64, 0, 16, 16, 16, 64,
+                                  ctypes.byref(st), 16, 4096, 16, 16, 1 << 30, None) == 2

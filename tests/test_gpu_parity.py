@@ -72,6 +72,20 @@ def test_parity_all_steps_all_rows(name):
             _compare_step(w, tr, t, r, res[t])
 
 
+@pytest.mark.parametrize("name", ["small_bf16", "small_offload"])
+def test_parity_valu_kernel_bf16(name):
+    """The VALU decode kernel on bf16 inputs (the default there is MFMA)."""
+    gh = _gpu()
+    from trainable_block_sparse_nosa_amd import _lib as L
+    w = synth.WORKLOADS[name]
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov)
+    _, res = gh.run(w, inp, list(range(w.steps)), decode_kernel=L.NOSA_DECODE_VALU)
+    for t in range(w.steps):
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, res[t])
+
+
 EDGE = {
     # fewer tokens than one block at the start: no candidates, then one
     "short_context": dict(context=10, steps=70, k_e=2, k_q=2),

@@ -86,9 +86,17 @@ template <typename F> nosa_status by_group(const Dims &dm, F &&f) {
     }
 }
 
+// Workspace: the partial outputs [rows][n_chunks][G][D] and the partial
+// (max, sum) [rows][n_chunks][G][2], float32.
 size_t decode_ws_bytes(const Dims &dm, const DecodePlan &pl) {
     const size_t parts = (size_t)dm.rows * pl.n_chunks * dm.G;
     return parts * dm.D * sizeof(float) + parts * 2 * sizeof(float);
+}
+
+size_t decode_ws_bytes_max(const Dims &dm) {
+    const size_t a = decode_ws_bytes(dm, decode_plan(dm, NOSA_DECODE_VALU));
+    const size_t b = decode_ws_bytes(dm, decode_plan(dm, NOSA_DECODE_MFMA));
+    return a > b ? a : b;
 }
 
 }  // namespace
@@ -182,7 +190,7 @@ nosa_status nosa_fetch_blocks(const nosa_shape *shape, const void *src_kv, int64
 size_t nosa_decode_workspace_size(const nosa_shape *shape) {
     Dims dm;
     if (make_dims(shape, &dm) != NOSA_OK) return 0;
-    return decode_ws_bytes(dm, decode_plan(dm));
+    return decode_ws_bytes_max(dm);
 }
 
 nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *kv,
@@ -201,7 +209,9 @@ nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const voi
     const int n_cand = step_cand(dm, step);
     if (n_cand < 0 || e_row_stride < step->n_tokens) return NOSA_ERR_INVALID_ARGUMENT;
     if (kv_mode == NOSA_KV_FULL && kv_row_blocks < n_cand + 1) return NOSA_ERR_INVALID_ARGUMENT;
-    const DecodePlan pl = decode_plan(dm);
+    const int kind = decode_kind(dm, shape->decode_kernel);
+    if (kind == NOSA_DECODE_MFMA && dm.dtype != NOSA_BF16) return NOSA_ERR_UNSUPPORTED;
+    const DecodePlan pl = decode_plan(dm, kind);
     if (ws_bytes < decode_ws_bytes(dm, pl)) return NOSA_ERR_WORKSPACE;
     if (((uintptr_t)q | (uintptr_t)kv | (uintptr_t)cur_kv | (uintptr_t)ws) & 15u)
         return NOSA_ERR_INVALID_ARGUMENT;
@@ -228,9 +238,11 @@ nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const voi
         constexpr int D = decltype(dc)::value;
         return by_group(dm, [&](auto gc) -> nosa_status {
             constexpr int G = decltype(gc)::value;
-            hipError_t e = launch_decode_valu<T, D, G>(dm, pl, a, st);
-            if (e != hipSuccess) return hip_status(e);
-            return hip_status(launch_combine<T, D, G>(dm, pl, a, st));
+            if constexpr (std::is_same<T, bf16_t>::value) {
+                if (kind == NOSA_DECODE_MFMA)
+                    return hip_status(launch_decode_mfma<D, G>(dm, pl, a, st));
+            }
+            return hip_status(launch_decode_valu<T, D, G>(dm, pl, a, st));
         });
     });
 }

@@ -34,7 +34,8 @@ struct DecodePlan {
     int cb;        // entries per chunk
     int n_chunks;  // chunks per row
 };
-DecodePlan decode_plan(const Dims &dm);
+int decode_kind(const Dims &dm, int requested);  // NOSA_DECODE_VALU or _MFMA
+DecodePlan decode_plan(const Dims &dm, int kind);
 
 struct DecodeArgs {
     const void *q;
@@ -59,8 +60,5 @@ hipError_t launch_decode_valu(const Dims &dm, const DecodePlan &pl, const Decode
 template <int D, int G>
 hipError_t launch_decode_mfma(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
                               hipStream_t st);
-template <typename T, int D, int G>
-hipError_t launch_combine(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
-                          hipStream_t st);
 
 }  // namespace nosa

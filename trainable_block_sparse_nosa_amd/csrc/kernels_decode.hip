@@ -1,33 +1,295 @@
 // Sparse decode attention with the ED-DMA logit bias, split-K over blocks.
 //
 // NOSA technical summary, Methodology, "1. Algorithm: NOSA", bullet "ED-DMA":
-// eviction scores are kept pre-exponential through selection and their
+// eviction scores stay pre-exponential through selection and their
 // exponential happens in the attention softmax; here each token's score is
 // added to its logit, z = scale * q.k + e, and softmax(z) weighs the values.
 //
-// Work split: one workgroup per (chunk of list entries, row). For every
-// block of its chunk a workgroup stages the K tile [64][D] and the V^T tile
-// [D][64] in LDS with coalesced 16-byte loads, computes the G x 64 logits,
-// updates a running (max, sum, output) per head (online softmax) and keeps
-// its partial in a workspace. A second kernel merges the partials of a row in
-// chunk order, so results do not depend on scheduling.
+// Work split: one workgroup per (chunk of list entries, row); entries
+// 0..k-1 are the selected blocks, entry k the newest block. Each workgroup
+// keeps an online-softmax state (max, sum, output) per head and writes it to
+// the workspace as its chunk's partial; a second kernel merges each row's
+// partials in chunk order and writes the output. The merge order is fixed,
+// so results do not depend on scheduling. (Merging inside the first kernel
+// would need device-scope fences, which on a multi-XCD part write back and
+// invalidate L2; the kernel boundary gives the same ordering for free.)
+//
+// Two kernels compute the partials:
+//  * MFMA (bf16): the G query heads of a row are padded to a 16-wide tile
+//    and S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16 (P
+//    enters as a bf16 hi + lo pair, so the weights keep ~16 bits). The
+//    K and V tiles are read straight into MFMA operand registers with 16-byte
+//    loads; the V tile's token order inside each 32-token half is stored so
+//    that the probabilities a lane holds after S^T are exactly the 8 k-slots
+//    it feeds to O^T (no cross-lane shuffles).
+//  * VALU (float32 and bf16): K and V tiles staged in LDS, fp32 FMAs.
 #include "kernels.h"
 
 namespace nosa {
 
-DecodePlan decode_plan(const Dims &dm) {
-    // Enough workgroups to cover 256 CUs several times over, and no fewer
-    // than one block per chunk.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVES = 4;         // waves per workgroup
+constexpr int MAX_CHUNKS = 129;  // k + 1 entries, one per chunk at most
+
+// Position of token `tok` (0..63) inside a row of the stored V^T tile: within
+// each 32-token half, positions 8g..8g+7 hold tokens 4g..4g+3, 16+4g..16+4g+3.
+__host__ __device__ constexpr int vt_token_at(int pos) {
+    return 32 * (pos / 32) + 16 * ((pos % 8) / 4) + 4 * ((pos % 32) / 8) + pos % 4;
+}
+
+DecodePlan decode_plan(const Dims &dm, int kind) {
     const int entries = dm.k + 1;
-    const long total = (long)dm.rows * entries;
-    int cb = 1;
-    while (cb < 16 && total / (cb * 2) >= 2048) cb *= 2;
     DecodePlan p;
-    p.cb = cb;
-    p.n_chunks = (entries + cb - 1) / cb;
+    if (kind == NOSA_DECODE_MFMA) {
+        p.cb = WAVES;  // one block per wave
+    } else {
+        // enough workgroups to cover 256 CUs several times over
+        const long total = (long)dm.rows * entries;
+        int cb = 1;
+        while (cb < 16 && total / (cb * 2) >= 2048) cb *= 2;
+        p.cb = cb;
+    }
+    p.n_chunks = (entries + p.cb - 1) / p.cb;
     return p;
 }
 
+int decode_kind(const Dims &dm, int requested) {
+    if (requested == NOSA_DECODE_AUTO) return dm.dtype == NOSA_BF16 ? NOSA_DECODE_MFMA : NOSA_DECODE_VALU;
+    return requested;
+}
+
+// ---------------------------------------------------------------------------
+// Combine: one workgroup per row merges the row's chunk partials in chunk
+// order. All (max, sum) pairs are loaded at once into LDS; each thread then
+// accumulates its outputs over the chunks with independent loads.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256)
+combine_kernel(Dims dm, int n_chunks, const float *__restrict__ ws_o,
+               const float *__restrict__ ws_ml, T *__restrict__ out) {
+    __shared__ float ml[MAX_CHUNKS * G * 2];
+    __shared__ float wgt[MAX_CHUNKS * G];
+    __shared__ float Lsh[G];
+    const int tid = threadIdx.x, r = blockIdx.x;
+    const float *mlr = ws_ml + (int64_t)r * n_chunks * G * 2;
+    for (int i = tid; i < n_chunks * G * 2; i += blockDim.x) ml[i] = mlr[i];
+    __syncthreads();
+    if (tid < G) {
+        const int h = tid;
+        float M = -INFINITY;
+        for (int c = 0; c < n_chunks; ++c)
+            if (ml[(c * G + h) * 2 + 1] > 0.f) M = fmaxf(M, ml[(c * G + h) * 2]);
+        float L = 0.f;
+        for (int c = 0; c < n_chunks; ++c) {
+            const float l = ml[(c * G + h) * 2 + 1];
+            const float wc = l > 0.f ? __expf(ml[(c * G + h) * 2] - M) : 0.f;
+            wgt[c * G + h] = wc;
+            L = fmaf(l, wc, L);
+        }
+        Lsh[h] = L;
+    }
+    __syncthreads();
+    const float *po = ws_o + (int64_t)r * n_chunks * G * D;
+    const int b = r / dm.Hkv, g = r % dm.Hkv;
+    for (int p = tid; p < G * D; p += blockDim.x) {
+        const int h = p / D;
+        float O = 0.f;
+#pragma unroll 8
+        for (int c = 0; c < n_chunks; ++c) O = fmaf(po[(int64_t)c * G * D + p], wgt[c * G + h], O);
+        out[((int64_t)b * dm.Hq + (int64_t)g * G) * D + p] = stf<T>(O / Lsh[h]);
+    }
+}
+
+// Resolve list entry e of row r: data pointer, block id and valid tokens.
+// Returns false when the entry holds no block.
+template <typename T>
+__device__ __forceinline__ bool resolve_entry(int e, int k, int cnt_e, int r, int kv_mode,
+                                              const T *kv, int64_t kv_row_blocks,
+                                              const int32_t *list, const T *cur,
+                                              int64_t cur_row_blocks, int n_tokens, int n_cand,
+                                              int64_t BE, const T *&blk, int &bid, int &valid) {
+    if (e > k) return false;
+    if (e == k) {
+        blk = cur + (int64_t)r * cur_row_blocks * BE;
+        bid = n_cand;
+        valid = n_tokens - n_cand * 64;
+        return true;
+    }
+    if (e >= cnt_e) return false;
+    bid = list[(int64_t)r * k + e];
+    if (bid < 0 || bid >= n_cand) return false;  // only candidates are ever listed
+    const int64_t at = kv_mode == NOSA_KV_FULL ? bid : e;
+    blk = kv + ((int64_t)r * kv_row_blocks + at) * BE;
+    valid = 64;
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA partial kernel (bf16). Wave w of workgroup `chunk` handles entry
+// chunk*4 + w. Lane l: col = l % 16 (head in S^T / O^T), grp = l / 16.
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ void __launch_bounds__(256)
+decode_mfma_kernel(Dims dm, int n_chunks, const bf16_t *__restrict__ q,
+                   const bf16_t *__restrict__ kv, int64_t kv_row_blocks, int kv_mode,
+                   const int32_t *__restrict__ list, const int32_t *__restrict__ n_list,
+                   const bf16_t *__restrict__ cur, int64_t cur_row_blocks, int n_tokens,
+                   int n_cand, const float *__restrict__ e_tok, int64_t e_stride,
+                   float *__restrict__ ws_o, float *__restrict__ ws_ml) {
+    static_assert(G <= 16, "the group is one 16-wide MFMA tile");
+    constexpr int S = 64, KS = D / 32, DT = D / 16;
+    constexpr int64_t BE = 2 * S * D;
+    __shared__ float wm[WAVES][G], wl[WAVES][G];
+    __shared__ float wo[WAVES][D][G];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int r = blockIdx.y, chunk = blockIdx.x;
+    const int b = r / dm.Hkv, g = r % dm.Hkv;
+    const int k = dm.k;
+    const int cnt_e = kv_mode == NOSA_KV_FULL ? n_list[r] : k;
+    const float *er = e_tok + (int64_t)r * e_stride;
+
+    // B operand of S^T = K Q^T: lane holds q[head col][32s + 8grp .. +7]
+    bf16x8 qop[KS];
+    {
+        const bf16_t *qh = q + ((int64_t)b * dm.Hq + (int64_t)g * G + col) * D + 8 * grp;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (col < G) {
+                qop[s] = *reinterpret_cast<const bf16x8 *>(qh + 32 * s);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) qop[s][j] = (__bf16)0.f;
+            }
+        }
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const bf16_t *blk;
+    int bid, valid;
+    const int e = chunk * WAVES + wave;
+    if (resolve_entry(e, k, cnt_e, r, kv_mode, kv, kv_row_blocks, list, cur, cur_row_blocks,
+                      n_tokens, n_cand, BE, blk, bid, valid)) {
+        const bf16_t *Kt = blk;           // [64][D]
+        const bf16_t *Vt = blk + S * D;   // [D][64], token order vt_token_at
+        bf16x8 kop[4][KS], vop[DT][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                kop[t][s] = *reinterpret_cast<const bf16x8 *>(Kt + (16 * t + col) * D + 32 * s + 8 * grp);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                vop[dt][s] = *reinterpret_cast<const bf16x8 *>(Vt + (16 * dt + col) * S + 32 * s + 8 * grp);
+        float ev[4][4];
+        const float *eb = er + (int64_t)bid * S + 4 * grp;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                ev[t][u] = 16 * t + 4 * grp + u < valid ? eb[16 * t + u] : 0.f;
+
+        // S^T tile t: lane holds logits of tokens 16t + 4grp + u for head col
+        f32x4 sc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[t][s], qop[s], sc[t], 0, 0, 0);
+        }
+        float z[4][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool ok = 16 * t + 4 * grp + u < valid;
+                z[t][u] = ok ? fmaf(sc[t][u], dm.scale, ev[t][u]) : -INFINITY;
+                mx = fmaxf(mx, z[t][u]);
+            }
+        // the 64 tokens of head col live in lanes col, col+16, col+32, col+48
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
+        // P as a sum of two bf16 operands (hi + lo) keeps ~16 mantissa bits
+        bf16x8 pop[2], plo[2];
+        float ps = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float p = z[t][u] == -INFINITY ? 0.f : __expf(z[t][u] - m_new);
+                const __bf16 hi = (__bf16)p;
+                pop[t / 2][(t % 2) * 4 + u] = hi;
+                plo[t / 2][(t % 2) * 4 + u] = (__bf16)(p - (float)hi);
+                ps += p;
+            }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        l_run = l_run * alpha + ps;
+        m_run = m_new;
+        // O^T tile dt: lane holds dims 16dt + 4grp + u for head col
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            o[dt] *= alpha;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt][s], pop[s], o[dt], 0, 0, 0);
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt][s], plo[s], o[dt], 0, 0, 0);
+            }
+        }
+    }
+
+    // merge the four waves' states
+    if (col < G) {
+        if (grp == 0) {
+            wm[wave][col] = m_run;
+            wl[wave][col] = l_run;
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) wo[wave][16 * dt + 4 * grp + u][col] = o[dt][u];
+    }
+    __syncthreads();
+    const int64_t base = ((int64_t)r * n_chunks + chunk) * G;
+    for (int p = threadIdx.x; p < G * D; p += blockDim.x) {
+        const int h = p / D, d = p % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w)
+            if (wl[w][h] > 0.f) M = fmaxf(M, wm[w][h]);
+        float O = 0.f, L = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            if (wl[w][h] > 0.f) {
+                const float c = __expf(wm[w][h] - M);
+                O = fmaf(wo[w][d][h], c, O);
+                L = fmaf(wl[w][h], c, L);
+            }
+        }
+        ws_o[base * D + p] = O;
+        if (d == 0) {
+            ws_ml[(base + h) * 2 + 0] = M;
+            ws_ml[(base + h) * 2 + 1] = L;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// VALU partial kernel (float32 and bf16): K and V^T tiles staged in LDS.
+// ---------------------------------------------------------------------------
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256)
 decode_valu_kernel(Dims dm, int cb, int n_chunks, const T *__restrict__ q,
@@ -37,11 +299,11 @@ decode_valu_kernel(Dims dm, int cb, int n_chunks, const T *__restrict__ q,
                    const float *__restrict__ e_tok, int64_t e_stride, float *__restrict__ ws_o,
                    float *__restrict__ ws_ml) {
     constexpr int S = 64;
-    constexpr int EPV = 16 / sizeof(T);     // elements per 16-byte vector
-    constexpr int KP = D + EPV;             // padded LDS row of the K tile
-    constexpr int VP = S + EPV;             // padded LDS row of the V^T tile
+    constexpr int EPV = 16 / sizeof(T);       // elements per 16-byte vector
+    constexpr int KP = D + EPV;               // padded LDS row of the K tile
+    constexpr int VP = S + EPV;               // padded LDS row of the V^T tile
     constexpr int NPT = (G * D + 255) / 256;  // outputs per thread
-    constexpr int64_t BE = 2 * S * D;       // elements per block-unit
+    constexpr int64_t BE = 2 * S * D;         // elements per block-unit
     __shared__ __attribute__((aligned(16))) T Ks[S * KP];
     __shared__ __attribute__((aligned(16))) T Vs[D * VP];
     __shared__ __attribute__((aligned(16))) float qs[G * D];
@@ -59,37 +321,25 @@ decode_valu_kernel(Dims dm, int cb, int n_chunks, const T *__restrict__ q,
     for (int i = 0; i < NPT; ++i) o[i] = 0.f;
 
     const int k = dm.k;
-    const int cnt = kv_mode == NOSA_KV_FULL ? n_list[r] : k;
+    const int cnt_e = kv_mode == NOSA_KV_FULL ? n_list[r] : k;
     const int e0 = chunk * cb, e1 = min(e0 + cb, k + 1);
     const float *er = e_tok + (int64_t)r * e_stride;
 
     for (int e = e0; e < e1; ++e) {
         const T *blk;
         int bid, valid;
-        if (e == k) {
-            blk = cur + (int64_t)r * cur_row_blocks * BE;
-            bid = n_cand;
-            valid = n_tokens - n_cand * S;
-        } else {
-            if (e >= cnt) continue;
-            bid = list[(int64_t)r * k + e];
-            if (bid < 0 || bid >= n_cand) continue;  // only candidates are ever listed
-            const int64_t at = kv_mode == NOSA_KV_FULL ? bid : e;
-            blk = kv + ((int64_t)r * kv_row_blocks + at) * BE;
-            valid = S;
-        }
+        if (!resolve_entry(e, k, cnt_e, r, kv_mode, kv, kv_row_blocks, list, cur, cur_row_blocks,
+                           n_tokens, n_cand, BE, blk, bid, valid))
+            continue;  // uniform over the workgroup
         __syncthreads();  // the previous block's readers are done with LDS
-        // stage K [S][D] and V^T [D][S]: 16-byte vectors, consecutive threads
-        // take consecutive vectors of the block
         constexpr int KV_VEC = S * D / EPV;
         for (int v = tid; v < KV_VEC; v += 256) {
-            const int row = v / (D / EPV), col = (v % (D / EPV)) * EPV;
-            *reinterpret_cast<uint4 *>(Ks + row * KP + col) =
-                reinterpret_cast<const uint4 *>(blk)[v];
+            const int row = v / (D / EPV), c = (v % (D / EPV)) * EPV;
+            *reinterpret_cast<uint4 *>(Ks + row * KP + c) = reinterpret_cast<const uint4 *>(blk)[v];
         }
         for (int v = tid; v < KV_VEC; v += 256) {
-            const int row = v / (S / EPV), col = (v % (S / EPV)) * EPV;
-            *reinterpret_cast<uint4 *>(Vs + row * VP + col) =
+            const int row = v / (S / EPV), c = (v % (S / EPV)) * EPV;
+            *reinterpret_cast<uint4 *>(Vs + row * VP + c) =
                 reinterpret_cast<const uint4 *>(blk + S * D)[v];
         }
         __syncthreads();
@@ -137,7 +387,8 @@ decode_valu_kernel(Dims dm, int cb, int n_chunks, const T *__restrict__ q,
         }
         __syncthreads();
 
-        // P.V: thread <-> (head, dim)
+        // P.V: thread <-> (head, dim); V^T positions 8j..8j+7 of half s hold
+        // tokens 32s+4j..+3 and 32s+16+4j..+3
 #pragma unroll
         for (int i = 0; i < NPT; ++i) {
             const int p = tid + i * 256;
@@ -148,8 +399,9 @@ decode_valu_kernel(Dims dm, int cb, int n_chunks, const T *__restrict__ q,
                 for (int t = 0; t < S; t += 8) {
                     float x[8];
                     Vec8<T>::load(Vs + d * VP + t, x);
-                    const float4 p0 = *reinterpret_cast<const float4 *>(ps + h * S + t);
-                    const float4 p1 = *reinterpret_cast<const float4 *>(ps + h * S + t + 4);
+                    const int t0 = vt_token_at(t);
+                    const float4 p0 = *reinterpret_cast<const float4 *>(ps + h * S + t0);
+                    const float4 p1 = *reinterpret_cast<const float4 *>(ps + h * S + t0 + 16);
                     acc = fmaf(p0.x, x[0], acc); acc = fmaf(p0.y, x[1], acc);
                     acc = fmaf(p0.z, x[2], acc); acc = fmaf(p0.w, x[3], acc);
                     acc = fmaf(p1.x, x[4], acc); acc = fmaf(p1.y, x[5], acc);
@@ -172,34 +424,6 @@ decode_valu_kernel(Dims dm, int cb, int n_chunks, const T *__restrict__ q,
     }
 }
 
-// Merge a row's chunk partials in chunk order.
-template <typename T, int D, int G>
-__global__ void __launch_bounds__(256)
-combine_kernel(Dims dm, int n_chunks, const float *__restrict__ ws_o,
-               const float *__restrict__ ws_ml, T *__restrict__ out) {
-    const int r = blockIdx.x;
-    const int b = r / dm.Hkv, g = r % dm.Hkv;
-    for (int p = threadIdx.x; p < G * D; p += blockDim.x) {
-        const int h = p / D, d = p % D;
-        float M = -INFINITY;
-        for (int c = 0; c < n_chunks; ++c) {
-            const int64_t at = (((int64_t)r * n_chunks + c) * G + h) * 2;
-            if (ws_ml[at + 1] > 0.f) M = fmaxf(M, ws_ml[at]);
-        }
-        float L = 0.f, O = 0.f;
-        for (int c = 0; c < n_chunks; ++c) {
-            const int64_t at = ((int64_t)r * n_chunks + c) * G + h;
-            const float l = ws_ml[at * 2 + 1];
-            if (l > 0.f) {
-                const float w = __expf(ws_ml[at * 2] - M);
-                L = fmaf(l, w, L);
-                O = fmaf(ws_o[at * D + d], w, O);
-            }
-        }
-        out[((int64_t)b * dm.Hq + (int64_t)g * G + h) * D + d] = stf<T>(O / L);
-    }
-}
-
 template <typename T, int D, int G>
 hipError_t launch_decode_valu(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
                               hipStream_t st) {
@@ -209,29 +433,47 @@ hipError_t launch_decode_valu(const Dims &dm, const DecodePlan &pl, const Decode
                        a.kv_row_blocks, a.kv_mode, a.list, a.n_list,
                        static_cast<const T *>(a.cur), a.cur_row_blocks, a.n_tokens, a.n_cand,
                        a.e_tok, a.e_stride, a.ws_o, a.ws_ml);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((combine_kernel<T, D, G>), dim3(dm.rows), dim3(256), 0, st, dm, pl.n_chunks,
+                       a.ws_o, a.ws_ml, static_cast<T *>(a.out));
     return hipGetLastError();
 }
 
-template <typename T, int D, int G>
-hipError_t launch_combine(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
-                          hipStream_t st) {
-    hipLaunchKernelGGL((combine_kernel<T, D, G>), dim3(dm.rows), dim3(256), 0, st, dm,
-                       pl.n_chunks, a.ws_o, a.ws_ml, static_cast<T *>(a.out));
+template <int D, int G>
+hipError_t launch_decode_mfma(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
+                              hipStream_t st) {
+    dim3 grid(pl.n_chunks, dm.rows);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G>), grid, dim3(256), 0, st, dm, pl.n_chunks,
+                       static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.kv),
+                       a.kv_row_blocks, a.kv_mode, a.list, a.n_list,
+                       static_cast<const bf16_t *>(a.cur), a.cur_row_blocks, a.n_tokens,
+                       a.n_cand, a.e_tok, a.e_stride, a.ws_o, a.ws_ml);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((combine_kernel<bf16_t, D, G>), dim3(dm.rows), dim3(256), 0, st, dm,
+                       pl.n_chunks, a.ws_o, a.ws_ml, static_cast<bf16_t *>(a.out));
     return hipGetLastError();
 }
 
 #define NOSA_DEC_INST(T, D, G)                                                                 \
     template hipError_t launch_decode_valu<T, D, G>(const Dims &, const DecodePlan &,          \
-                                                    const DecodeArgs &, hipStream_t);          \
-    template hipError_t launch_combine<T, D, G>(const Dims &, const DecodePlan &,              \
-                                                const DecodeArgs &, hipStream_t);
+                                                    const DecodeArgs &, hipStream_t);
 #define NOSA_DEC_ALLG(T, D)                                                                    \
     NOSA_DEC_INST(T, D, 1) NOSA_DEC_INST(T, D, 2) NOSA_DEC_INST(T, D, 3)                       \
     NOSA_DEC_INST(T, D, 4) NOSA_DEC_INST(T, D, 5) NOSA_DEC_INST(T, D, 6)                       \
     NOSA_DEC_INST(T, D, 7) NOSA_DEC_INST(T, D, 8)
 NOSA_DEC_ALLG(float, 64)
-NOSA_DEC_ALLG(float, 128)
 NOSA_DEC_ALLG(bf16_t, 64)
 NOSA_DEC_ALLG(bf16_t, 128)
+
+#define NOSA_MFMA_INST(D, G)                                                                   \
+    template hipError_t launch_decode_mfma<D, G>(const Dims &, const DecodePlan &,             \
+                                                 const DecodeArgs &, hipStream_t);
+#define NOSA_MFMA_ALLG(D)                                                                      \
+    NOSA_MFMA_INST(D, 1) NOSA_MFMA_INST(D, 2) NOSA_MFMA_INST(D, 3) NOSA_MFMA_INST(D, 4)        \
+    NOSA_MFMA_INST(D, 5) NOSA_MFMA_INST(D, 6) NOSA_MFMA_INST(D, 7) NOSA_MFMA_INST(D, 8)
+NOSA_MFMA_ALLG(64)
+NOSA_MFMA_ALLG(128)
 
 }  // namespace nosa

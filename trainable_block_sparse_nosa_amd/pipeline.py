@@ -27,10 +27,17 @@ BLOCK = 64
 SUB_BLOCK = 16
 
 
+# Token held at each position of a stored V^T row: inside each half of 32,
+# positions 8j..8j+7 hold tokens 4j..4j+3 and 16+4j..16+4j+3.
+VT_TOKEN_AT = np.array([32 * (p // 32) + 16 * ((p % 8) // 4) + 4 * ((p % 32) // 8) + p % 4
+                        for p in range(BLOCK)])
+
+
 def pack_blocks(K: np.ndarray, V: np.ndarray, n_blocks: int) -> np.ndarray:
     """Block-unit layout of one row: [n_blocks, 2*64*D] with, per block, the K
-    tile [64][D] followed by the V tile transposed [D][64]. Tokens beyond the
-    input are zero. Works on float32 or bfloat16-bit (uint16) arrays."""
+    tile [64][D] followed by the V tile transposed, [D][64], its positions in
+    the VT_TOKEN_AT token order. Tokens beyond the input are zero. Works on
+    float32 or bfloat16-bit (uint16) arrays."""
     n, D = K.shape
     pad = n_blocks * BLOCK - n
     if pad < 0:
@@ -39,7 +46,8 @@ def pack_blocks(K: np.ndarray, V: np.ndarray, n_blocks: int) -> np.ndarray:
         K = np.concatenate([K, np.zeros((pad, D), K.dtype)])
         V = np.concatenate([V, np.zeros((pad, D), V.dtype)])
     Kb = K.reshape(n_blocks, BLOCK * D)
-    Vt = V.reshape(n_blocks, BLOCK, D).transpose(0, 2, 1).reshape(n_blocks, D * BLOCK)
+    Vb = V.reshape(n_blocks, BLOCK, D)[:, VT_TOKEN_AT, :]
+    Vt = Vb.transpose(0, 2, 1).reshape(n_blocks, D * BLOCK)
     return np.ascontiguousarray(np.concatenate([Kb, Vt], axis=1))
 
 
