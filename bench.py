@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle sample (0 = skip)")
     ap.add_argument("--no-stage-breakdown", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 4 device-to-device copies of 512 MiB (a reference kernel "
+                         "of known traffic for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -57,6 +60,29 @@ def decode_bytes(w, n_tokens: int, n_sel: int) -> int:
     per_row = toks * 2 * w.head_dim * elem + toks * 4
     qo = 2 * w.batch * w.n_q_heads * w.head_dim * elem
     return w.rows * per_row + qo
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per attention call recorded from rocprofv3 byte counters for
+    this workload, if the kernel sources are unchanged since; else None."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", f"decode_step_{workload}.md")
+    csrc = os.path.join(ROOT, "trainable_block_sparse_nosa_amd", "csrc")
+    if not os.path.exists(prof):
+        return None
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    fields = {}
+    with open(prof) as fh:
+        for line in fh:
+            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256_16"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(w, seconds: float, steps_avail: int):
@@ -179,6 +205,15 @@ def main():
     torch.cuda.synchronize()
     log("warmup done")
 
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 4 x 512 MiB device-to-device")
+
     # ---- timed region: exactly args.steps steps ----
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -251,7 +286,7 @@ def main():
         "roofline": {
             "kernel": "sparse decode attention (nosa_sparse_decode: split-K partial + combine)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name),
             "avg_launch_us": dec_avg_s * 1e6, "algorithmic_bytes_per_launch": bytes_avg,
         },
         "attn_us_per_layer_step": dec_avg_s * 1e6,
