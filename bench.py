@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle sample (0 = skip)")
     ap.add_argument("--no-stage-breakdown", action="store_true")
+    ap.add_argument("--offload-steps", type=int, default=60,
+                    help="steps of the offloaded 128k-context leg (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 4 device-to-device copies of 512 MiB (a reference kernel "
                          "of known traffic for hardware byte counters)")
@@ -120,14 +122,8 @@ def cpu_baseline(w, seconds: float, steps_avail: int):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
-              "(rows shard across GPUs with no exchange; only the one-GPU share is measured)",
-              file=sys.stderr)
-        sys.exit(2)
-
+def setup(w, args, dev):
+    """Generate the workload's inputs (untimed) and build its layer."""
     import numpy as np
     import torch
 
@@ -136,22 +132,7 @@ def main():
     from trainable_block_sparse_nosa_amd.hostmem import PinnedBuffer
     from trainable_block_sparse_nosa_amd.pipeline import DecodeLayer, pack_blocks
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    base = synth.WORKLOADS[args.workload]
     T = args.warmup + args.steps
-    w = base.scaled(steps=max(base.steps, T))
-    kind = {"auto": L.NOSA_DECODE_AUTO, "valu": L.NOSA_DECODE_VALU,
-            "mfma": L.NOSA_DECODE_MFMA}[args.decode_kernel]
-    log(f"workload {w.name}: rows={w.rows} G={w.group} D={w.head_dim} ctx={w.context} "
-        f"k={w.k_e}+{w.k_q} steps={T} offload={w.offload}")
-
-    # ---- inputs (untimed) ----
-    t0 = time.time()
     nb = w.nb_max
     BE = 2 * 64 * w.head_dim
     elem = 4 if w.dtype == "f32" else 2
@@ -168,7 +149,7 @@ def main():
             return torch.from_numpy(a).to(dev)
         return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
 
-    host = None
+    t0 = time.time()
     if w.offload:
         host = PinnedBuffer(w.rows * nb * BE * elem)
         view = host.array(np.float32 if w.dtype == "f32" else np.uint16, (w.rows, nb, BE))
@@ -190,20 +171,125 @@ def main():
     e_tok = torch.from_numpy(e).to(dev)
     q = to_dev(np.stack(synth.parallel_map(lambda t: conv(synth.queries_step(w, 0, t)), range(T), 16)))
     torch.cuda.synchronize()
-    log(f"inputs ready in {time.time() - t0:.1f} s")
-
+    log(f"{w.name}: inputs ready in {time.time() - t0:.1f} s")
+    kind = {"auto": L.NOSA_DECODE_AUTO, "valu": L.NOSA_DECODE_VALU,
+            "mfma": L.NOSA_DECODE_MFMA}[args.decode_kernel]
     layer = DecodeLayer(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
                         head_dim=w.head_dim, k_e=w.k_e, k_q=w.k_q, max_blocks=nb,
                         dtype=L.NOSA_F32 if w.dtype == "f32" else L.NOSA_BF16, kv=kv_ptr,
                         kv_row_blocks=nb, e_tok=e_tok, offload=w.offload, decode_kernel=kind)
-    stream = torch.cuda.current_stream()
+    return layer, q, kv
 
-    # ---- warmup (untimed) ----
+
+def timed_run(layer, w, q, args, stream, event_stages=("decode",)):
+    """Warm up, then time exactly args.steps steps; HIP events bracket the
+    listed stages in every timed step. Returns (elapsed s, {stage: [ms]},
+    blocks fetched during the timed steps)."""
+    import torch
     layer.start(w.n_tokens(0), stream)
     for t in range(args.warmup):
         layer.step(q[t], w.n_tokens(t), stream)
     torch.cuda.synchronize()
-    log("warmup done")
+    fetched0 = int(layer.counters[:, 0].sum().item())
+    ev = {s: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for s in event_stages}
+    cur = {"i": 0}
+
+    def hook(name, fn, *a):
+        if name in ev:
+            e0, e1 = ev[name][cur["i"]]
+            e0.record(stream)
+            fn(*a)
+            e1.record(stream)
+        else:
+            fn(*a)
+
+    layer.stage_hook = hook
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        cur["i"] = i
+        layer.step(q[args.warmup + i], w.n_tokens(args.warmup + i), stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    layer.stage_hook = None
+    fetched = int(layer.counters[:, 0].sum().item()) - fetched0
+    ms = {s: [a.elapsed_time(b) for a, b in ev[s]] for s in ev}
+    return elapsed, ms, fetched
+
+
+def h2d_peak_gbs(dev, nbytes=1 << 30, reps=5):
+    """hipMemcpyAsync from pinned host memory to HBM (torch pinned tensor)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    return best
+
+
+def offload_leg(args, dev, stream):
+    """The 128k-context offloaded workload: steps/s and swap GB/s of the fetch
+    kernel against the measured pinned-host-to-HBM copy bandwidth."""
+    import synth
+    base = synth.WORKLOADS["offload_1layer_128k"]
+    w = base.scaled(steps=max(base.steps, args.warmup + args.offload_steps))
+    sub = argparse.Namespace(**vars(args))
+    sub.steps = args.offload_steps
+    layer, q, kv = setup(w, sub, dev)
+    elapsed, ms, fetched = timed_run(layer, w, q, sub, stream, event_stages=("fetch", "decode"))
+    fetch_s = sum(ms["fetch"]) / 1e3
+    block_bytes = 2 * 64 * w.head_dim * 2
+    swap_gbs = fetched * block_bytes / fetch_s / 1e9
+    peak = h2d_peak_gbs(dev)
+    out = {
+        "workload": w.name, "steps": sub.steps, "steps_per_s": sub.steps / elapsed,
+        "ms_per_step": elapsed / sub.steps * 1e3,
+        "fetched_mib_per_step": fetched * block_bytes / sub.steps / 2**20,
+        "fetch_us_per_step": fetch_s / sub.steps * 1e6,
+        "swap_gbs": swap_gbs, "h2d_memcpy_gbs": peak, "frac_of_h2d": swap_gbs / peak,
+        "attn_us_per_step": sum(ms["decode"]) / len(ms["decode"]) * 1e3,
+    }
+    kv.free()
+    del layer, q
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(rows shard across GPUs with no exchange; only the one-GPU share is measured)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    base = synth.WORKLOADS[args.workload]
+    T = args.warmup + args.steps
+    w = base.scaled(steps=max(base.steps, T))
+    log(f"workload {w.name}: rows={w.rows} G={w.group} D={w.head_dim} ctx={w.context} "
+        f"k={w.k_e}+{w.k_q} steps={T} offload={w.offload}")
+    layer, q, kv = setup(w, args, dev)
 
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -214,50 +300,33 @@ def main():
         del src, dst
         log("copy calibration: 4 x 512 MiB device-to-device")
 
-    # ---- timed region: exactly args.steps steps ----
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    slot = {"i": 0}
-
-    def decode_events(name, fn, *a):
-        if name == "decode":
-            e0, e1 = ev[slot["i"]]
-            e0.record(stream)
-            fn(*a)
-            e1.record(stream)
-        else:
-            fn(*a)
-
-    layer.stage_hook = decode_events
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        slot["i"] = i
-        layer.step(q[args.warmup + i], w.n_tokens(args.warmup + i), stream)
-    torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    layer.stage_hook = None
-    elapsed = t_end - t_start
+    elapsed, ms, _ = timed_run(layer, w, q, args, stream)
     n_sel = layer.n_sel.cpu().numpy()
-    dec_bytes = []
-    for i in range(args.steps):
-        dec_bytes.append(decode_bytes(w, w.n_tokens(args.warmup + i), int(np.min(n_sel))))
-    dec_ms = [a.elapsed_time(b) for a, b in ev]
-    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    dec_bytes = [decode_bytes(w, w.n_tokens(args.warmup + i), int(np.min(n_sel)))
+                 for i in range(args.steps)]
+    dec_avg_s = sum(ms["decode"]) / len(ms["decode"]) / 1e3
     bytes_avg = sum(dec_bytes) / len(dec_bytes)
     achieved = bytes_avg / dec_avg_s / 1e9
     steps_per_s = args.steps / elapsed
     log(f"timed {args.steps} steps in {elapsed * 1e3:.1f} ms: {steps_per_s:.1f} steps/s, "
-        f"attention {dec_avg_s * 1e6:.1f} us/launch, {achieved:.0f} GB/s")
+        f"attention {dec_avg_s * 1e6:.1f} us/call, {achieved:.0f} GB/s")
 
     counters = layer.counters.cpu().numpy()
-    steps_total = args.warmup + args.steps
-    gamma_mean = float(counters[:, 1].sum()) / (w.rows * w.k * steps_total)
+    gamma_mean = float(counters[:, 1].sum()) / (w.rows * w.k * T)
 
-    # ---- stage breakdown (separate, untimed pass with events between stages) ----
     stages = None
     if not args.no_stage_breakdown:
         stages = stage_breakdown(layer, w, q, args.warmup, min(args.steps, 50), stream)
+    if not w.offload:
+        del layer, q, kv
+        torch.cuda.empty_cache()
+
+    swap = None
+    if args.offload_steps > 0 and not w.offload:
+        log("offload leg: offload_1layer_128k")
+        swap = offload_leg(args, dev, stream)
+        log(f"offload: {swap['steps_per_s']:.1f} steps/s, swap {swap['swap_gbs']:.1f} GB/s "
+            f"= {100 * swap['frac_of_h2d']:.1f} % of hipMemcpy H2D {swap['h2d_memcpy_gbs']:.1f} GB/s")
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -291,6 +360,7 @@ def main():
         },
         "attn_us_per_layer_step": dec_avg_s * 1e6,
         "gamma_mean": gamma_mean,
+        "swap": swap,
         "cpu_baseline": cpu,
     }
     if stages:

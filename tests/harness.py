@@ -87,7 +87,7 @@ class OracleTrace:
 
 
 def oracle_trace(w: Workload, layer: int = 0, rows=None, steps=None, ov: Overrides | None = None,
-                 margins: bool = True, swaps: bool = True) -> OracleTrace:
+                 margins: bool = True, swaps: bool = True, workers: int = 8) -> OracleTrace:
     """Run the oracle on the given rows and steps, enforcing margins first.
 
     With ``swaps`` the steps must be 0..T-1 in order so the slot cache can be
@@ -100,13 +100,15 @@ def oracle_trace(w: Workload, layer: int = 0, rows=None, steps=None, ov: Overrid
         assert steps == list(range(len(steps))), "swap replay needs steps 0..T-1"
     tr = OracleTrace(w, layer, steps, rows, ov)
     sc = scale_of(w)
-    for r in rows:
+
+    def one_row(r):
         b, g = divmod(r, w.n_kv_heads)
         K, V = row_kv(w, layer, b, g)
         e = enforce_evict_margins(w, layer, b, g, steps, ov) if margins else \
             synth.evict_row(w, layer, b, g, ov)
         cache = oracle.SlotCache(w.k)
         kmax = float(np.sqrt(np.max(np.sum(K.astype(np.float64) ** 2, axis=1))))
+        out_step, out_swap, out_scale = {}, {}, {}
         for t in steps:
             for _ in range(64):
                 q = group_q(w, layer, t, b, g, ov)
@@ -122,9 +124,16 @@ def oracle_trace(w: Workload, layer: int = 0, rows=None, steps=None, ov: Overrid
                 ov.query[key] = ov.query.get(key, 0) + 1
             else:
                 raise RuntimeError("could not enforce query margins")
-            tr.step[(t, r)] = res
+            out_step[(t, r)] = res
             qn = float(np.sum(np.sqrt(np.sum(q.astype(np.float64) ** 2, axis=1))))
-            tr.term_scale[(t, r)] = sc * qn * kmax
+            out_scale[(t, r)] = sc * qn * kmax
             if swaps:
-                tr.swap[(t, r)] = cache.step(res.selected)
+                out_swap[(t, r)] = cache.step(res.selected)
+        return out_step, out_swap, out_scale
+
+    # rows are independent; the oracle's C calls release the GIL
+    for st, sw, ts in synth.parallel_map(one_row, rows, min(workers, max(1, len(rows)))):
+        tr.step.update(st)
+        tr.swap.update(sw)
+        tr.term_scale.update(ts)
     return tr
