@@ -166,8 +166,9 @@ def setup(w, args, dev):
             for r, p in zip(rr, synth.parallel_map(row_blocks, rr, 16)):
                 kv[r].copy_(to_dev(p))
         kv_ptr = kv
-    e = np.stack(synth.parallel_map(lambda r: synth.evict_row(w, 0, *divmod(r, w.n_kv_heads)),
-                                    range(w.rows), 16))
+    e = np.zeros((w.rows, nb * 64), np.float32)   # rows padded to whole blocks
+    e[:, :w.n_max] = np.stack(synth.parallel_map(
+        lambda r: synth.evict_row(w, 0, *divmod(r, w.n_kv_heads)), range(w.rows), 16))
     e_tok = torch.from_numpy(e).to(dev)
     q = to_dev(np.stack(synth.parallel_map(lambda t: conv(synth.queries_step(w, 0, t)), range(T), 16)))
     torch.cuda.synchronize()

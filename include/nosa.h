@@ -58,7 +58,9 @@
  *            KV, an HBM block cache (k slots per row) and the newest-block
  *            buffer (one block per row) all use it with their own row_blocks.
  * e_tok      float32 [rows][e_row_stride]: per-token eviction scores,
- *            pre-exponential.
+ *            pre-exponential. nosa_sparse_decode reads them a block at a
+ *            time: e_tok is 16-byte aligned, e_row_stride a multiple of 4 and
+ *            at least S * (n_cand + 1) (values past n_tokens are ignored).
  * kbar       float32 [rows][D/4][m*max_blocks][4], m = S / sub_block: the
  *            mean key of sub-block i of block j is at [.][d/4][m*j+i][d%4].
  * e_blk      float32 [rows][max_blocks]: pooled eviction score per block.

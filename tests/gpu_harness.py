@@ -76,7 +76,8 @@ def upload(w: Workload, layer: int = 0, ov: Overrides | None = None, steps: int 
             for r, p in zip(rr, parts):
                 kv[r].copy_(to_device(p, w, device))
         kv_ptr = kv
-    e = np.stack(synth.parallel_map(
+    e = np.zeros((rows, nb * 64), np.float32)   # rows padded to whole blocks
+    e[:, :w.n_max] = np.stack(synth.parallel_map(
         lambda r: synth.evict_row(w, layer, *divmod(r, w.n_kv_heads), ov), range(rows), workers))
     e_tok = torch.from_numpy(e).to(device)
     qs = synth.parallel_map(lambda t: storage(synth.queries_step(w, layer, t, ov), w), range(T),

@@ -112,7 +112,9 @@ def test_invalid_pointers_and_steps_rejected():
     assert call(args(wsb=ws - 4)) == 4
     assert call(args(q=17)) == 1
     assert call(args(mode=3)) == 1
-    assert call(args(es=99)) == 1
+    assert call(args(es=99)) == 1             # shorter than the blocks present
+    assert call(args(es=130)) == 1            # not a multiple of 4
+    assert call(args(e=20)) == 1              # not 16-byte aligned
     assert call(args(mode=1, rb=7)) == 1      # cache smaller than k slots
     assert call(args(nl=None)) == 1           # full mode needs the list length
     # host allocation needs a size

@@ -12,7 +12,8 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libnosa.so")
+# NOSA_LIB_PATH may point at another build of the same library (same ABI)
+LIB_PATH = os.environ.get("NOSA_LIB_PATH") or os.path.join(_PKG, "libnosa.so")
 
 NOSA_OK = 0
 NOSA_ERR_INVALID_ARGUMENT = 1

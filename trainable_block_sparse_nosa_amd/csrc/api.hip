@@ -207,7 +207,11 @@ nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const voi
     if (kv_mode == NOSA_KV_CACHE && kv_row_blocks < dm.k) return NOSA_ERR_INVALID_ARGUMENT;
     if (kv_row_blocks <= 0 || cur_row_blocks <= 0) return NOSA_ERR_INVALID_ARGUMENT;
     const int n_cand = step_cand(dm, step);
-    if (n_cand < 0 || e_row_stride < step->n_tokens) return NOSA_ERR_INVALID_ARGUMENT;
+    if (n_cand < 0) return NOSA_ERR_INVALID_ARGUMENT;
+    // eviction-score rows cover whole blocks and are 16-byte aligned
+    if (e_row_stride < (int64_t)(n_cand + 1) * dm.S || (e_row_stride & 3) ||
+        ((uintptr_t)e_tok & 15u))
+        return NOSA_ERR_INVALID_ARGUMENT;
     if (kv_mode == NOSA_KV_FULL && kv_row_blocks < n_cand + 1) return NOSA_ERR_INVALID_ARGUMENT;
     const int kind = decode_kind(dm, shape->decode_kernel);
     if (kind == NOSA_DECODE_MFMA && dm.dtype != NOSA_BF16) return NOSA_ERR_UNSUPPORTED;

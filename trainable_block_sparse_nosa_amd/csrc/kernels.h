@@ -33,6 +33,7 @@ hipError_t launch_fetch(const Dims &dm, const void *src, int64_t src_row_blocks,
 struct DecodePlan {
     int cb;        // entries per chunk
     int n_chunks;  // chunks per row
+    int npw;       // MFMA kernel: blocks per wave (1, 2, 4 or 8)
 };
 int decode_kind(const Dims &dm, int requested);  // NOSA_DECODE_VALU or _MFMA
 DecodePlan decode_plan(const Dims &dm, int kind);

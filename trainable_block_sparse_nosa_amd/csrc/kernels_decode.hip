@@ -43,15 +43,27 @@ DecodePlan decode_plan(const Dims &dm, int kind) {
     const int entries = dm.k + 1;
     DecodePlan p;
     if (kind == NOSA_DECODE_MFMA) {
-        p.cb = WAVES;  // one block per wave
+        // blocks per wave: enough waves to fill the chip once (one resident
+        // wave per SIMD at this kernel's register use), at most 8
+        const long total = (long)dm.rows * entries;
+        // One block per wave measured fastest: at ~210 registers two waves
+        // share a SIMD and every wave issues all of its block's loads at once;
+        // walking several blocks per wave with a second register set for the
+        // next block drops to one wave per SIMD and was slower.
+        (void)total;
+        const int npw = 1;
+        p.npw = npw;
+        p.n_chunks = (entries + WAVES * npw - 1) / (WAVES * npw);
+        p.cb = (entries + p.n_chunks - 1) / p.n_chunks;  // balanced chunks
     } else {
         // enough workgroups to cover 256 CUs several times over
         const long total = (long)dm.rows * entries;
         int cb = 1;
         while (cb < 16 && total / (cb * 2) >= 2048) cb *= 2;
         p.cb = cb;
+        p.npw = 0;
+        p.n_chunks = (entries + p.cb - 1) / p.cb;
     }
-    p.n_chunks = (entries + p.cb - 1) / p.cb;
     return p;
 }
 
@@ -61,45 +73,49 @@ int decode_kind(const Dims &dm, int requested) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine: one workgroup per row merges the row's chunk partials in chunk
-// order. All (max, sum) pairs are loaded at once into LDS; each thread then
-// accumulates its outputs over the chunks with independent loads.
+// Combine: one workgroup per (row, head), one thread per dimension, merges
+// the row's chunk partials in chunk order. Lane c of each wave loads chunk
+// c's (max, sum); wave reductions give the row maximum and the denominator,
+// and each chunk's weight is read back from its lane. The partial outputs'
+// loads are issued together with those: one memory round trip, no LDS.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int G>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(D)
 combine_kernel(Dims dm, int n_chunks, const float *__restrict__ ws_o,
                const float *__restrict__ ws_ml, T *__restrict__ out) {
-    __shared__ float ml[MAX_CHUNKS * G * 2];
-    __shared__ float wgt[MAX_CHUNKS * G];
-    __shared__ float Lsh[G];
-    const int tid = threadIdx.x, r = blockIdx.x;
-    const float *mlr = ws_ml + (int64_t)r * n_chunks * G * 2;
-    for (int i = tid; i < n_chunks * G * 2; i += blockDim.x) ml[i] = mlr[i];
-    __syncthreads();
-    if (tid < G) {
-        const int h = tid;
+    constexpr int CREG = 33;  // chunks held in registers (every MFMA plan fits)
+    const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x, lane = threadIdx.x & 63;
+    const float *ml = ws_ml + ((int64_t)r * n_chunks * G + h) * 2;  // chunk c at ml[c*G*2]
+    const float *po = ws_o + ((int64_t)r * n_chunks * G + h) * D + d;  // chunk c at po[c*G*D]
+    float O = 0.f, L;
+    if (n_chunks <= CREG) {
+        float ov[CREG];
+#pragma unroll
+        for (int c = 0; c < CREG; ++c)
+            if (c < n_chunks) ov[c] = po[(int64_t)c * G * D];
+        const float mv = lane < n_chunks ? ml[lane * G * 2] : -INFINITY;
+        const float lv = lane < n_chunks ? ml[lane * G * 2 + 1] : 0.f;
+        const float M = wave_max(lv > 0.f ? mv : -INFINITY);
+        const float wc = lv > 0.f ? __expf(mv - M) : 0.f;
+        L = wave_sum(lv * wc);
+#pragma unroll
+        for (int c = 0; c < CREG; ++c)
+            if (c < n_chunks)
+                O = fmaf(ov[c], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wc), c)), O);
+    } else {
         float M = -INFINITY;
+        L = 0.f;
         for (int c = 0; c < n_chunks; ++c)
-            if (ml[(c * G + h) * 2 + 1] > 0.f) M = fmaxf(M, ml[(c * G + h) * 2]);
-        float L = 0.f;
+            if (ml[c * G * 2 + 1] > 0.f) M = fmaxf(M, ml[c * G * 2]);
         for (int c = 0; c < n_chunks; ++c) {
-            const float l = ml[(c * G + h) * 2 + 1];
-            const float wc = l > 0.f ? __expf(ml[(c * G + h) * 2] - M) : 0.f;
-            wgt[c * G + h] = wc;
+            const float l = ml[c * G * 2 + 1];
+            const float wc = l > 0.f ? __expf(ml[c * G * 2] - M) : 0.f;
             L = fmaf(l, wc, L);
+            O = fmaf(po[(int64_t)c * G * D], wc, O);
         }
-        Lsh[h] = L;
     }
-    __syncthreads();
-    const float *po = ws_o + (int64_t)r * n_chunks * G * D;
     const int b = r / dm.Hkv, g = r % dm.Hkv;
-    for (int p = tid; p < G * D; p += blockDim.x) {
-        const int h = p / D;
-        float O = 0.f;
-#pragma unroll 8
-        for (int c = 0; c < n_chunks; ++c) O = fmaf(po[(int64_t)c * G * D + p], wgt[c * G + h], O);
-        out[((int64_t)b * dm.Hq + (int64_t)g * G) * D + p] = stf<T>(O / Lsh[h]);
-    }
+    out[((int64_t)b * dm.Hq + (int64_t)g * G + h) * D + d] = stf<T>(O / L);
 }
 
 // Resolve list entry e of row r: data pointer, block id and valid tokens.
@@ -117,9 +133,8 @@ __device__ __forceinline__ bool resolve_entry(int e, int k, int cnt_e, int r, in
         valid = n_tokens - n_cand * 64;
         return true;
     }
-    if (e >= cnt_e) return false;
-    bid = list[(int64_t)r * k + e];
-    if (bid < 0 || bid >= n_cand) return false;  // only candidates are ever listed
+    bid = list[(int64_t)r * k + e];  // issued before the count is known
+    if (e >= cnt_e || bid < 0 || bid >= n_cand) return false;  // only candidates are listed
     const int64_t at = kv_mode == NOSA_KV_FULL ? bid : e;
     blk = kv + ((int64_t)r * kv_row_blocks + at) * BE;
     valid = 64;
@@ -127,12 +142,102 @@ __device__ __forceinline__ bool resolve_entry(int e, int k, int cnt_e, int r, in
 }
 
 // ---------------------------------------------------------------------------
-// MFMA partial kernel (bf16). Wave w of workgroup `chunk` handles entry
-// chunk*4 + w. Lane l: col = l % 16 (head in S^T / O^T), grp = l / 16.
+// MFMA partial kernel (bf16). Chunk c of a row covers entries
+// [c*epc, min((c+1)*epc, k+1)); wave w takes entries c*epc + w + 4i. While a
+// wave computes one block, the next block's operands are already loading into
+// a second register set. Lane l: col = l % 16 (head in S^T / O^T),
+// grp = l / 16.
 // ---------------------------------------------------------------------------
-template <int D, int G>
+template <int D>
+struct BlockRegs {
+    bf16x8 k[4][D / 32];  // A operands of S^T = K Q^T, tile t = tokens 16t..16t+15
+    bf16x8 v[D / 16][2];  // A operands of O^T = V^T P^T, d-tile dt, token half s
+    f32x4 e[4];           // eviction scores of tokens 16t + 4grp + u
+    int valid;            // tokens of this block that exist (0: no block)
+};
+
+template <int D>
+__device__ __forceinline__ void load_block(BlockRegs<D> &br, const bf16_t *blk, const float *eb,
+                                           int valid, int col, int grp) {
+    constexpr int S = 64, KS = D / 32, DT = D / 16;
+    const bf16_t *Kt = blk;          // [64][D]
+    const bf16_t *Vt = blk + S * D;  // [D][64], token order vt_token_at
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            br.k[t][s] = *reinterpret_cast<const bf16x8 *>(Kt + (16 * t + col) * D + 32 * s + 8 * grp);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            br.v[dt][s] = *reinterpret_cast<const bf16x8 *>(Vt + (16 * dt + col) * S + 32 * s + 8 * grp);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) br.e[t] = *reinterpret_cast<const f32x4 *>(eb + 16 * t + 4 * grp);
+    br.valid = valid;
+}
+
+template <int D>
+__device__ __forceinline__ void attend_block(const BlockRegs<D> &br, const bf16x8 (&qop)[D / 32],
+                                             float scale, int grp, float &m_run, float &l_run,
+                                             f32x4 (&o)[D / 16]) {
+    constexpr int KS = D / 32, DT = D / 16;
+    // S^T tile t: lane holds logits of tokens 16t + 4grp + u for head col
+    f32x4 sc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(br.k[t][s], qop[s], sc[t], 0, 0, 0);
+    }
+    float z[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool ok = 16 * t + 4 * grp + u < br.valid;
+            z[t][u] = ok ? fmaf(sc[t][u], scale, br.e[t][u]) : -INFINITY;
+            mx = fmaxf(mx, z[t][u]);
+        }
+    // the 64 tokens of head col live in lanes col, col+16, col+32, col+48
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
+    // P as a sum of two bf16 operands (hi + lo) keeps ~16 mantissa bits
+    bf16x8 phi[2], plo[2];
+    float ps = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float p = z[t][u] == -INFINITY ? 0.f : __expf(z[t][u] - m_new);
+            const __bf16 hi = (__bf16)p;
+            phi[t / 2][(t % 2) * 4 + u] = hi;
+            plo[t / 2][(t % 2) * 4 + u] = (__bf16)(p - (float)hi);
+            ps += p;
+        }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    // O^T tile dt: lane holds dims 16dt + 4grp + u for head col
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        o[dt] *= alpha;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(br.v[dt][s], phi[s], o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(br.v[dt][s], plo[s], o[dt], 0, 0, 0);
+        }
+    }
+}
+
+template <int D, int G, int NPW, bool PREFETCH>
 __global__ void __launch_bounds__(256)
-decode_mfma_kernel(Dims dm, int n_chunks, const bf16_t *__restrict__ q,
+decode_mfma_kernel(Dims dm, int epc, int n_chunks, const bf16_t *__restrict__ q,
                    const bf16_t *__restrict__ kv, int64_t kv_row_blocks, int kv_mode,
                    const int32_t *__restrict__ list, const int32_t *__restrict__ n_list,
                    const bf16_t *__restrict__ cur, int64_t cur_row_blocks, int n_tokens,
@@ -144,27 +249,26 @@ decode_mfma_kernel(Dims dm, int n_chunks, const bf16_t *__restrict__ q,
     __shared__ float wm[WAVES][G], wl[WAVES][G];
     __shared__ float wo[WAVES][D][G];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // the wave index is uniform: block ids come from scalar loads
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, grp = lane >> 4;
     const int r = blockIdx.y, chunk = blockIdx.x;
     const int b = r / dm.Hkv, g = r % dm.Hkv;
     const int k = dm.k;
     const int cnt_e = kv_mode == NOSA_KV_FULL ? n_list[r] : k;
     const float *er = e_tok + (int64_t)r * e_stride;
+    const int e_end = min((chunk + 1) * epc, k + 1);
 
-    // B operand of S^T = K Q^T: lane holds q[head col][32s + 8grp .. +7]
+    // B operand of S^T = K Q^T: lane holds q[head col][32s + 8grp .. +7].
+    // Padding columns (col >= G) repeat head G-1: their softmax reductions
+    // stay within their own column and their outputs are never stored.
     bf16x8 qop[KS];
     {
-        const bf16_t *qh = q + ((int64_t)b * dm.Hq + (int64_t)g * G + col) * D + 8 * grp;
+        const int hc = col < G ? col : G - 1;
+        const bf16_t *qh = q + ((int64_t)b * dm.Hq + (int64_t)g * G + hc) * D + 8 * grp;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            if (col < G) {
-                qop[s] = *reinterpret_cast<const bf16x8 *>(qh + 32 * s);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) qop[s][j] = (__bf16)0.f;
-            }
-        }
+        for (int s = 0; s < KS; ++s) qop[s] = *reinterpret_cast<const bf16x8 *>(qh + 32 * s);
     }
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -172,82 +276,29 @@ decode_mfma_kernel(Dims dm, int n_chunks, const bf16_t *__restrict__ q,
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const bf16_t *blk;
-    int bid, valid;
-    const int e = chunk * WAVES + wave;
-    if (resolve_entry(e, k, cnt_e, r, kv_mode, kv, kv_row_blocks, list, cur, cur_row_blocks,
-                      n_tokens, n_cand, BE, blk, bid, valid)) {
-        const bf16_t *Kt = blk;           // [64][D]
-        const bf16_t *Vt = blk + S * D;   // [D][64], token order vt_token_at
-        bf16x8 kop[4][KS], vop[DT][2];
+    BlockRegs<D> buf[PREFETCH ? 2 : 1];
+    auto fetch = [&](int i, BlockRegs<D> &br) {
+        const int e = chunk * epc + wave + WAVES * i;
+        const bf16_t *blk;
+        int bid, valid;
+        if (e < e_end && resolve_entry(e, k, cnt_e, r, kv_mode, kv, kv_row_blocks, list, cur,
+                                       cur_row_blocks, n_tokens, n_cand, BE, blk, bid, valid))
+            load_block<D>(br, blk, er + (int64_t)bid * S, valid, col, grp);
+        else
+            br.valid = 0;
+    };
+    if constexpr (PREFETCH) {
+        fetch(0, buf[0]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                kop[t][s] = *reinterpret_cast<const bf16x8 *>(Kt + (16 * t + col) * D + 32 * s + 8 * grp);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                vop[dt][s] = *reinterpret_cast<const bf16x8 *>(Vt + (16 * dt + col) * S + 32 * s + 8 * grp);
-        float ev[4][4];
-        const float *eb = er + (int64_t)bid * S + 4 * grp;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                ev[t][u] = 16 * t + 4 * grp + u < valid ? eb[16 * t + u] : 0.f;
-
-        // S^T tile t: lane holds logits of tokens 16t + 4grp + u for head col
-        f32x4 sc[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[t][s], qop[s], sc[t], 0, 0, 0);
+        for (int i = 0; i < NPW; ++i) {
+            if (i + 1 < NPW) fetch(i + 1, buf[(i + 1) & 1]);
+            if (buf[i & 1].valid > 0)
+                attend_block<D>(buf[i & 1], qop, dm.scale, grp, m_run, l_run, o);
         }
-        float z[4][4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bool ok = 16 * t + 4 * grp + u < valid;
-                z[t][u] = ok ? fmaf(sc[t][u], dm.scale, ev[t][u]) : -INFINITY;
-                mx = fmaxf(mx, z[t][u]);
-            }
-        // the 64 tokens of head col live in lanes col, col+16, col+32, col+48
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
-        // P as a sum of two bf16 operands (hi + lo) keeps ~16 mantissa bits
-        bf16x8 pop[2], plo[2];
-        float ps = 0.f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float p = z[t][u] == -INFINITY ? 0.f : __expf(z[t][u] - m_new);
-                const __bf16 hi = (__bf16)p;
-                pop[t / 2][(t % 2) * 4 + u] = hi;
-                plo[t / 2][(t % 2) * 4 + u] = (__bf16)(p - (float)hi);
-                ps += p;
-            }
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
-        l_run = l_run * alpha + ps;
-        m_run = m_new;
-        // O^T tile dt: lane holds dims 16dt + 4grp + u for head col
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            o[dt] *= alpha;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt][s], pop[s], o[dt], 0, 0, 0);
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt][s], plo[s], o[dt], 0, 0, 0);
-            }
+    } else {
+        for (int i = 0; i < NPW; ++i) {
+            fetch(i, buf[0]);
+            if (buf[0].valid > 0) attend_block<D>(buf[0], qop, dm.scale, grp, m_run, l_run, o);
         }
     }
 
@@ -266,18 +317,20 @@ decode_mfma_kernel(Dims dm, int n_chunks, const bf16_t *__restrict__ q,
     const int64_t base = ((int64_t)r * n_chunks + chunk) * G;
     for (int p = threadIdx.x; p < G * D; p += blockDim.x) {
         const int h = p / D, d = p % D;
+        float mw[WAVES], lw[WAVES];
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w)
-            if (wl[w][h] > 0.f) M = fmaxf(M, wm[w][h]);
+        for (int w = 0; w < WAVES; ++w) {
+            mw[w] = wm[w][h];
+            lw[w] = wl[w][h];
+            M = fmaxf(M, lw[w] > 0.f ? mw[w] : -INFINITY);
+        }
         float O = 0.f, L = 0.f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
-            if (wl[w][h] > 0.f) {
-                const float c = __expf(wm[w][h] - M);
-                O = fmaf(wo[w][d][h], c, O);
-                L = fmaf(wl[w][h], c, L);
-            }
+            const float c = lw[w] > 0.f ? __expf(mw[w] - M) : 0.f;
+            O = fmaf(wo[w][d][h], c, O);
+            L = fmaf(lw[w], c, L);
         }
         ws_o[base * D + p] = O;
         if (d == 0) {
@@ -435,7 +488,7 @@ hipError_t launch_decode_valu(const Dims &dm, const DecodePlan &pl, const Decode
                        a.e_tok, a.e_stride, a.ws_o, a.ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((combine_kernel<T, D, G>), dim3(dm.rows), dim3(256), 0, st, dm, pl.n_chunks,
+    hipLaunchKernelGGL((combine_kernel<T, D, G>), dim3(dm.rows, G), dim3(D), 0, st, dm, pl.n_chunks,
                        a.ws_o, a.ws_ml, static_cast<T *>(a.out));
     return hipGetLastError();
 }
@@ -444,14 +497,22 @@ template <int D, int G>
 hipError_t launch_decode_mfma(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
                               hipStream_t st) {
     dim3 grid(pl.n_chunks, dm.rows);
-    hipLaunchKernelGGL((decode_mfma_kernel<D, G>), grid, dim3(256), 0, st, dm, pl.n_chunks,
-                       static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.kv),
-                       a.kv_row_blocks, a.kv_mode, a.list, a.n_list,
-                       static_cast<const bf16_t *>(a.cur), a.cur_row_blocks, a.n_tokens,
-                       a.n_cand, a.e_tok, a.e_stride, a.ws_o, a.ws_ml);
+#define NOSA_MFMA_LAUNCH(NPW)                                                                  \
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G, NPW, false>), grid, dim3(256), 0, st, dm, pl.cb, \
+                       pl.n_chunks, static_cast<const bf16_t *>(a.q),                          \
+                       static_cast<const bf16_t *>(a.kv), a.kv_row_blocks, a.kv_mode, a.list,  \
+                       a.n_list, static_cast<const bf16_t *>(a.cur), a.cur_row_blocks,         \
+                       a.n_tokens, a.n_cand, a.e_tok, a.e_stride, a.ws_o, a.ws_ml)
+    switch (pl.npw) {
+    case 1: NOSA_MFMA_LAUNCH(1); break;
+    case 2: NOSA_MFMA_LAUNCH(2); break;
+    case 4: NOSA_MFMA_LAUNCH(4); break;
+    default: NOSA_MFMA_LAUNCH(8); break;
+    }
+#undef NOSA_MFMA_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((combine_kernel<bf16_t, D, G>), dim3(dm.rows), dim3(256), 0, st, dm,
+    hipLaunchKernelGGL((combine_kernel<bf16_t, D, G>), dim3(dm.rows, G), dim3(D), 0, st, dm,
                        pl.n_chunks, a.ws_o, a.ws_ml, static_cast<bf16_t *>(a.out));
     return hipGetLastError();
 }
