@@ -174,6 +174,15 @@ nosa_status nosa_swap_diff(const nosa_shape *shape, const int32_t *sel, const in
                            int32_t *fetch_block, int32_t *fetch_slot, int32_t *n_fetch,
                            uint64_t *counters, void *stream);
 
+/* nosa_select followed by nosa_swap_diff, in one launch: the same outputs
+ * and state updates as the two calls in sequence. */
+nosa_status nosa_select_swap(const nosa_shape *shape, const float *s_q, const float *e_blk,
+                             const nosa_step *step, uint32_t *ge_bits, uint32_t *ev_bits,
+                             int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
+                             int32_t *slot_block, int32_t *block_slot, int32_t *fetch_block,
+                             int32_t *fetch_slot, int32_t *n_fetch, uint64_t *counters,
+                             void *stream);
+
 /* Copy fetch_block[r][i] of the source KV buffer to slot fetch_slot[r][i] of
  * the destination KV buffer, for i < n_fetch[r] (at most max_fetch), every
  * row (Methodology, "High-Bandwidth Communication"). The copy is a GPU kernel

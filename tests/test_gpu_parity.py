@@ -86,6 +86,19 @@ def test_parity_valu_kernel_bf16(name):
             _compare_step(w, tr, t, r, res[t])
 
 
+@pytest.mark.parametrize("name", ["small_f32", "small_offload"])
+def test_parity_separate_select_and_swap(name):
+    """nosa_select then nosa_swap_diff as two calls (the pipeline fuses them)."""
+    gh = _gpu()
+    w = synth.WORKLOADS[name]
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov)
+    _, res = gh.run(w, inp, list(range(w.steps)), fuse_select_swap=False)
+    for t in range(w.steps):
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, res[t])
+
+
 EDGE = {
     # fewer tokens than one block at the start: no candidates, then one
     "short_context": dict(context=10, steps=70, k_e=2, k_q=2),
@@ -99,8 +112,10 @@ EDGE = {
     "gqa8": dict(n_q_heads=16, n_kv_heads=2, context=1300, steps=20),
     # ragged: context ends one token before a block boundary
     "ragged_boundary": dict(context=2047, steps=3, k_e=5, k_q=5),
-    # the largest supported budget
+    # the largest supported budget (eviction budget above 64: LDS top-k at start)
     "k128": dict(context=9000, steps=4, k_e=96, k_q=32),
+    # query-aware budget above 64: LDS top-k every step
+    "kq_large": dict(context=9000, steps=70, k_e=20, k_q=80),
 }
 
 

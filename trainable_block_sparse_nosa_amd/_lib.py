@@ -29,7 +29,7 @@ NOSA_DECODE_VALU = 1
 NOSA_DECODE_MFMA = 2
 
 EXPORTS = (
-    "nosa_pool_blocks", "nosa_score_blocks", "nosa_select", "nosa_swap_diff",
+    "nosa_pool_blocks", "nosa_score_blocks", "nosa_select", "nosa_select_swap", "nosa_swap_diff",
     "nosa_fetch_blocks", "nosa_decode_workspace_size", "nosa_sparse_decode",
     "nosa_host_alloc", "nosa_host_free", "nosa_status_string", "nosa_last_error",
     "nosa_version",
@@ -64,6 +64,7 @@ def _load() -> ctypes.CDLL:
         "nosa_pool_blocks": [SH, P, I64, I32, P, I64, I32, I32, P, P, P],
         "nosa_score_blocks": [SH, P, P, ST, P, P],
         "nosa_select": [SH, P, P, ST, P, P, P, P, P, P],
+        "nosa_select_swap": [SH, P, P, ST, P, P, P, P, P, P, P, P, P, P, P, P],
         "nosa_swap_diff": [SH, P, P, P, P, P, P, P, P, P, P],
         "nosa_fetch_blocks": [SH, P, I64, P, P, P, I32, P, I64, P],
         "nosa_sparse_decode": [SH, P, P, I64, I32, P, P, P, I64, ST, P, I64, P, P, SZ, P],
@@ -140,6 +141,14 @@ def nosa_select(shape, s_q, e_blk, step, ge_bits, ev_bits, sel, n_sel, sel_bits,
     _chk("nosa_select", _L.nosa_select(
         ctypes.byref(shape), _p(s_q), _p(e_blk), ctypes.byref(step), _p(ge_bits), _p(ev_bits),
         _p(sel), _p(n_sel), _p(sel_bits), _s(stream)))
+
+
+def nosa_select_swap(shape, s_q, e_blk, step, ge_bits, ev_bits, sel, n_sel, sel_bits, slot_block,
+                     block_slot, fetch_block, fetch_slot, n_fetch, counters, stream=None):
+    _chk("nosa_select_swap", _L.nosa_select_swap(
+        ctypes.byref(shape), _p(s_q), _p(e_blk), ctypes.byref(step), _p(ge_bits), _p(ev_bits),
+        _p(sel), _p(n_sel), _p(sel_bits), _p(slot_block), _p(block_slot), _p(fetch_block),
+        _p(fetch_slot), _p(n_fetch), _p(counters), _s(stream)))
 
 
 def nosa_swap_diff(shape, sel, n_sel, sel_bits, slot_block, block_slot, fetch_block, fetch_slot,

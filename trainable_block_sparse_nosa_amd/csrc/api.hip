@@ -154,7 +154,26 @@ nosa_status nosa_select(const nosa_shape *shape, const float *s_q, const float *
     const int n_cand = step_cand(dm, step);
     if (n_cand < 0) return NOSA_ERR_INVALID_ARGUMENT;
     return hip_status(launch_select(dm, s_q, e_blk, n_cand, step->n_cand_prev, ge_bits, ev_bits,
-                                    sel, n_sel, sel_bits, (hipStream_t)stream));
+                                    sel, n_sel, sel_bits, nullptr, (hipStream_t)stream));
+}
+
+nosa_status nosa_select_swap(const nosa_shape *shape, const float *s_q, const float *e_blk,
+                             const nosa_step *step, uint32_t *ge_bits, uint32_t *ev_bits,
+                             int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
+                             int32_t *slot_block, int32_t *block_slot, int32_t *fetch_block,
+                             int32_t *fetch_slot, int32_t *n_fetch, uint64_t *counters,
+                             void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!s_q || !e_blk || !ge_bits || !ev_bits || !sel || !n_sel || !sel_bits || !slot_block ||
+        !block_slot || !fetch_block || !fetch_slot || !n_fetch || !counters)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    const int n_cand = step_cand(dm, step);
+    if (n_cand < 0) return NOSA_ERR_INVALID_ARGUMENT;
+    const SwapPtrs sw{slot_block, block_slot, fetch_block, fetch_slot, n_fetch, counters};
+    return hip_status(launch_select(dm, s_q, e_blk, n_cand, step->n_cand_prev, ge_bits, ev_bits,
+                                    sel, n_sel, sel_bits, &sw, (hipStream_t)stream));
 }
 
 nosa_status nosa_swap_diff(const nosa_shape *shape, const int32_t *sel, const int32_t *n_sel,
@@ -167,8 +186,8 @@ nosa_status nosa_swap_diff(const nosa_shape *shape, const int32_t *sel, const in
     if (!sel || !n_sel || !sel_bits || !slot_block || !block_slot || !fetch_block ||
         !fetch_slot || !n_fetch || !counters)
         return NOSA_ERR_INVALID_ARGUMENT;
-    return hip_status(launch_swap(dm, sel, n_sel, sel_bits, slot_block, block_slot, fetch_block,
-                                  fetch_slot, n_fetch, counters, (hipStream_t)stream));
+    const SwapPtrs sw{slot_block, block_slot, fetch_block, fetch_slot, n_fetch, counters};
+    return hip_status(launch_swap(dm, sel, n_sel, sel_bits, sw, (hipStream_t)stream));
 }
 
 nosa_status nosa_fetch_blocks(const nosa_shape *shape, const void *src_kv, int64_t src_row_blocks,

@@ -14,14 +14,18 @@ template <typename T, int D, int G>
 hipError_t launch_score(const Dims &dm, const void *q, const float *kbar, int n_cand, float *s_q,
                         hipStream_t st);
 
+struct SwapPtrs {
+    int32_t *slot_block, *block_slot, *fetch_block, *fetch_slot, *n_fetch;
+    uint64_t *counters;
+};
+
+// swap == nullptr: selection only; else the set difference runs in the same launch
 hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, int n_cand,
                          int n_prev, uint32_t *ge, uint32_t *ev, int32_t *sel, int32_t *n_sel,
-                         uint32_t *sel_bits, hipStream_t st);
+                         uint32_t *sel_bits, const SwapPtrs *swap, hipStream_t st);
 
 hipError_t launch_swap(const Dims &dm, const int32_t *sel, const int32_t *n_sel,
-                       const uint32_t *sel_bits, int32_t *slot_block, int32_t *block_slot,
-                       int32_t *fetch_block, int32_t *fetch_slot, int32_t *n_fetch,
-                       uint64_t *counters, hipStream_t st);
+                       const uint32_t *sel_bits, const SwapPtrs &swap, hipStream_t st);
 
 hipError_t launch_fetch(const Dims &dm, const void *src, int64_t src_row_blocks,
                         const int32_t *fblk, const int32_t *fslot, const int32_t *nfetch,

@@ -66,7 +66,7 @@ class DecodeLayer:
 
     def __init__(self, *, batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks, dtype,
                  kv, kv_row_blocks, e_tok, offload=False, decode_kernel=L.NOSA_DECODE_AUTO,
-                 scale=0.0, device="cuda"):
+                 scale=0.0, device="cuda", fuse_select_swap=True):
         self.shape = L.make_shape(batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks,
                                   dtype, decode_kernel=decode_kernel, scale=scale)
         self.rows = batch * n_kv_heads
@@ -110,6 +110,7 @@ class DecodeLayer:
             self.cur_fb = torch.zeros(R, k, dtype=i32, device=dev)
             self.cur_fs = torch.zeros(R, k, dtype=i32, device=dev)
             self.cur_nf = torch.ones(R, dtype=i32, device=dev)
+        self.fuse_select_swap = fuse_select_swap
         self.n_cand_prev = -1
         self.n_tokens = 0
         # optional callable(stage_name, fn, *args): runs fn(*args); a caller
@@ -163,12 +164,18 @@ class DecodeLayer:
             self.pooled = c
         st = L.make_step(n_tokens, self.n_cand_prev)
         self._run("score", L.nosa_score_blocks, self.shape, q, self.kbar, st, self.s_q, stream)
-        self._run("select", L.nosa_select, self.shape, self.s_q, self.e_blk, st, self.ge_bits,
-                  self.ev_bits, self.sel, self.n_sel, self.sel_bits, stream)
-        if swap or self.offload:
-            self._run("swap", L.nosa_swap_diff, self.shape, self.sel, self.n_sel, self.sel_bits,
+        if (swap or self.offload) and self.fuse_select_swap:
+            self._run("select", L.nosa_select_swap, self.shape, self.s_q, self.e_blk, st,
+                      self.ge_bits, self.ev_bits, self.sel, self.n_sel, self.sel_bits,
                       self.slot_block, self.block_slot, self.fetch_block, self.fetch_slot,
                       self.n_fetch, self.counters, stream)
+        else:
+            self._run("select", L.nosa_select, self.shape, self.s_q, self.e_blk, st, self.ge_bits,
+                      self.ev_bits, self.sel, self.n_sel, self.sel_bits, stream)
+            if swap or self.offload:
+                self._run("swap", L.nosa_swap_diff, self.shape, self.sel, self.n_sel,
+                          self.sel_bits, self.slot_block, self.block_slot, self.fetch_block,
+                          self.fetch_slot, self.n_fetch, self.counters, stream)
         if self.offload:
             self._run("fetch", L.nosa_fetch_blocks, self.shape, self.kv, self.kv_row_blocks,
                       self.fetch_block, self.fetch_slot, self.n_fetch, self.k, self.cache, self.k,
