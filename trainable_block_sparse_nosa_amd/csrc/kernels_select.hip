@@ -95,78 +95,109 @@ score_kernel(Dims dm, const T *__restrict__ q, const float *__restrict__ kbar, i
 }
 
 // ---------------------------------------------------------------------------
-// Select: one workgroup (8 waves) per row.
-//  * top-k with k <= 64: each wave sorts 64 rank keys at a time across its
-//    lanes (bitonic network on lane shuffles, no barriers) and keeps a
-//    running sorted top-64; wave 0 then merges the 8 waves' lists.
-//  * top-k with k > 64 (an eviction budget above 64 at initialisation):
-//    bitonic sort of all keys in LDS.
+// Select: one workgroup (8 waves) per row. Keys are 64-bit rank keys
+// (orderable score << 32 | ~index), so a larger key ranks first and no two
+// keys are equal; 0 marks "not a candidate".
+//  * top-k with k <= 64: every thread holds its candidates' keys in registers
+//    (candidate j = tid + 512 i). Each wave finds the smallest key T of its own
+//    top-k by a most-significant-bit-first search with ballots and popcounts
+//    (stopping as soon as exactly k of its keys are >= the prefix); its keys
+//    >= T go to LDS; each of these <= 8k survivors then counts how many
+//    survivors are larger, and the ones with fewer than k above them are the
+//    row's top-k. No sorting, two barriers.
+//  * top-k with k > 64 (an eviction budget above 64 at initialisation, or a
+//    query budget above 64): bitonic sort of all keys in LDS.
 //  * Gamma_e after initialisation: each new candidate in turn replaces the
 //    lowest-ranked member if it ranks above it, else it is evicted.
 //  * the ascending selection list comes from a popcount prefix scan.
 //  * optionally the set difference against the block cache runs in the same
-//    workgroup (wave 0), saving a launch and a round trip per step.
+//    workgroup (wave 0), from the selection bitmap and the slot table alone.
 // ---------------------------------------------------------------------------
 constexpr int SELECT_THREADS = 512;
 constexpr int SELECT_WAVES = SELECT_THREADS / 64;
 constexpr int MAX_W = 128;   // 4096 blocks
 constexpr int MAX_K = 128;
 constexpr int WAVE_TOPK = 64;
+constexpr int KEYS_PER_THREAD = 4096 / SELECT_THREADS;
 
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
-// Sort the wave's 64 keys (one per lane) descending: lane 0 holds the largest.
-__device__ uint64_t wave_sort_desc(uint64_t x) {
-    const int lane = threadIdx.x & 63;
+// Smallest key of the wave's top-k among the keys held in x[0..m) of every
+// lane (0 = no key). Returns 0 when the wave holds at most k keys (then all
+// of its non-zero keys qualify).
+template <int M>
+__device__ uint64_t wave_kth_key(const uint64_t (&x)[M], int k) {
+    int n = 0;
 #pragma unroll
-    for (int k2 = 2; k2 <= 64; k2 <<= 1) {
+    for (int i = 0; i < M; ++i) n += __popcll(__ballot(x[i] != 0ull));
+    if (n <= k) return 0ull;
+    uint64_t t = 0ull;
+    for (int b = 63; b >= 0; --b) {
+        const uint64_t cand = t | (1ull << b);
+        int c = 0;
 #pragma unroll
-        for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
-            const uint64_t y = __shfl_xor(x, j2, 64);
-            const bool desc = (lane & k2) == 0;
-            const bool lower = (lane & j2) == 0;
-            x = (lower == desc) ? umax64(x, y) : umin64(x, y);
+        for (int i = 0; i < M; ++i) c += __popcll(__ballot(x[i] >= cand));
+        if (c >= k) {
+            t = cand;
+            if (c == k) break;  // exactly the top-k are >= t
         }
     }
-    return x;
+    return t;
 }
 
-// a and b sorted descending across the wave -> the 64 largest of both,
-// sorted descending (max against the reversed list gives a bitonic
-// sequence holding them, which a half-cleaner cascade sorts).
-__device__ uint64_t wave_merge_top(uint64_t a, uint64_t b) {
+// Top-k (k <= 64) of the keys x[0..M) held by every thread of the block:
+// sets the selected indices' bits in `bits` (LDS). Returns nothing; the
+// caller synchronises before reading `bits`.
+template <int M>
+__device__ void block_topk(const uint64_t (&x)[M], int k, uint64_t *surv, int *n_surv,
+                           uint32_t *bits) {
     const int lane = threadIdx.x & 63;
-    uint64_t x = umax64(a, __shfl(b, 63 - lane, 64));
+    if (threadIdx.x == 0) *n_surv = 0;
+    __syncthreads();
+    const uint64_t t = wave_kth_key<M>(x, k);
+    const uint64_t lt = lanemask_lt();
 #pragma unroll
-    for (int j2 = 32; j2 > 0; j2 >>= 1) {
-        const uint64_t y = __shfl_xor(x, j2, 64);
-        x = (lane & j2) == 0 ? umax64(x, y) : umin64(x, y);
+    for (int i = 0; i < M; ++i) {
+        const bool keep = x[i] != 0ull && x[i] >= t;
+        const uint64_t m = __ballot(keep);
+        int base = 0;
+        if (lane == 0 && m) base = atomicAdd(n_surv, __popcll(m));
+        base = __shfl(base, 0, 64);
+        if (keep) surv[base + __popcll(m & lt)] = x[i];
     }
-    return x;
+    __syncthreads();
+    const int ns = *n_surv;
+    for (int i = threadIdx.x; i < ns; i += blockDim.x) {
+        const uint64_t me = surv[i];
+        int above = 0;
+        for (int j = 0; j < ns; ++j) above += surv[j] > me;
+        if (above < k) {
+            const int idx = key_index(me);
+            atomicOr(&bits[idx >> 5], 1u << (idx & 31));
+        }
+    }
 }
 
-// The 64 largest keys of key_of(0..n-1) (0 = not a candidate), sorted
-// descending, into top[0..64) in LDS.
+// Keys of candidates tid + 512 i (i < M) from key_of(j, i); then block_topk.
+template <int M, typename KeyFn>
+__device__ void topk_m(int n, int k, KeyFn key_of, uint64_t *surv, int *n_surv, uint32_t *bits) {
+    uint64_t x[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int j = threadIdx.x + SELECT_THREADS * i;
+        x[i] = j < n ? key_of(j, i) : 0ull;
+    }
+    block_topk<M>(x, k, surv, n_surv, bits);
+}
+
+// Dispatch on how many keys each thread holds (uniform over the block).
 template <typename KeyFn>
-__device__ void topk_waves(int n, KeyFn key_of, uint64_t *lists, uint64_t *top) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    uint64_t best = 0ull;
-    for (int base = wave * 64; base < n; base += SELECT_WAVES * 64) {
-        const int j = base + lane;
-        uint64_t x = j < n ? key_of(j) : 0ull;
-        if (__ballot(x != 0ull) == 0ull) continue;
-        best = wave_merge_top(best, wave_sort_desc(x));
-    }
-    lists[wave * 64 + lane] = best;
-    __syncthreads();
-    if (wave == 0) {
-        uint64_t acc = lists[lane];
-        for (int w = 1; w < SELECT_WAVES; ++w) acc = wave_merge_top(acc, lists[w * 64 + lane]);
-        top[lane] = acc;
-    }
-    __syncthreads();
+__device__ void topk_dispatch(int n, int k, KeyFn key_of, uint64_t *surv, int *n_surv,
+                              uint32_t *bits) {
+    if (n <= SELECT_THREADS) topk_m<1>(n, k, key_of, surv, n_surv, bits);
+    else if (n <= 2 * SELECT_THREADS) topk_m<2>(n, k, key_of, surv, n_surv, bits);
+    else if (n <= 4 * SELECT_THREADS) topk_m<4>(n, k, key_of, surv, n_surv, bits);
+    else topk_m<8>(n, k, key_of, surv, n_surv, bits);
 }
 
 __device__ void bitonic_desc(uint64_t *keys, int P) {
@@ -216,40 +247,58 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// Set difference of one row, run by one wave. sel (ascending, ns entries)
-// and bits may live in LDS or global memory. Every output address is written
-// once: free slot i receives fetched block i (or becomes empty), the blocks
-// they held lose their slot, the fetched blocks gain one.
-__device__ void swap_row(const Dims &dm, int r, const int32_t *sel, int ns, const uint32_t *bits,
-                         int32_t *__restrict__ slot_block, int32_t *__restrict__ block_slot,
-                         int32_t *__restrict__ fetch_block, int32_t *__restrict__ fetch_slot,
-                         int32_t *__restrict__ n_fetch, uint64_t *__restrict__ counters,
-                         int *fb, int *fs, int *fo) {
-    const int lane = threadIdx.x & 63, k = dm.k;
-    int32_t *sbk = slot_block + (int64_t)r * k;
-    int32_t *bsl = block_slot + (int64_t)r * dm.max_blocks;
+struct SwapArgs {
+    int32_t *slot_block, *block_slot, *fetch_block, *fetch_slot, *n_fetch;
+    uint64_t *counters;
+};
+
+// Set difference of one row, run by one wave. `bits` (LDS or global) is the
+// selection bitmap; slot l of the cache holds slots[l] (lane l and l + 64,
+// already loaded). `res` is an LDS bitmap of W words for the cached set.
+// Fetch list = selected and not cached, ascending; free slots = empty or
+// holding an unselected block, ascending; fetched block i goes to free slot
+// i, leftover free slots become empty. Every output address is written once.
+__device__ void swap_row(const Dims &dm, int r, const uint32_t *bits, int s0, int s1,
+                         uint32_t *res, int *fb, int *fs, int *fo, const SwapArgs &sw) {
+    const int lane = threadIdx.x & 63, k = dm.k, W = dm.W;
     const uint64_t lt = lanemask_lt();
-    ns = min(max(ns, 0), k);
+    for (int w = lane; w < W; w += 64) res[w] = 0u;
+    wave_sync_lds();
+    if (lane < k && s0 >= 0 && s0 < dm.max_blocks) atomicOr(&res[s0 >> 5], 1u << (s0 & 31));
+    if (lane + 64 < k && s1 >= 0 && s1 < dm.max_blocks) atomicOr(&res[s1 >> 5], 1u << (s1 & 31));
+    wave_sync_lds();
+    // fetch list: set bits of (selected & ~cached), two words per lane, ascending
     int nf = 0, kept = 0;
-    for (int base = 0; base < ns; base += 64) {
-        const int i = base + lane;
-        const int blk = i < ns ? sel[i] : -1;
-        const bool ok = blk >= 0 && blk < dm.max_blocks;
-        const bool need = ok && bsl[blk] < 0;
-        const uint64_t m = __ballot(need);
-        if (need) fb[nf + __popcll(m & lt)] = blk;
-        nf += __popcll(m);
-        kept += __popcll(__ballot(ok && !need));
-    }
-    int nfree = 0;
-    for (int base = 0; base < k; base += 64) {
-        const int sl = base + lane;
-        int blk = -1;
-        bool fr = false;
-        if (sl < k) {
-            blk = sbk[sl];
-            fr = blk < 0 || blk >= dm.max_blocks || !((bits[blk >> 5] >> (blk & 31)) & 1u);
+    for (int base = 0; base < W; base += 128) {
+        const int w0 = base + 2 * lane, w1 = w0 + 1;
+        const uint32_t b0 = w0 < W ? bits[w0] : 0u, b1 = w1 < W ? bits[w1] : 0u;
+        const uint32_t f0 = b0 & ~(w0 < W ? res[w0] : 0u);
+        const uint32_t f1 = b1 & ~(w1 < W ? res[w1] : 0u);
+        kept += __popc(b0 & ~f0) + __popc(b1 & ~f1);
+        const int cnt = __popc(f0) + __popc(f1);
+        int inc = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
         }
+        int pos = nf + inc - cnt;
+        uint32_t m = f0;
+        while (m && pos < MAX_K) { fb[pos++] = w0 * 32 + __ffs(m) - 1; m &= m - 1u; }
+        m = f1;
+        while (m && pos < MAX_K) { fb[pos++] = w1 * 32 + __ffs(m) - 1; m &= m - 1u; }
+        nf += __shfl(inc, 63, 64);
+    }
+    for (int o = 32; o > 0; o >>= 1) kept += __shfl_xor(kept, o, 64);
+    nf = min(nf, k);
+    // free slots, ascending
+    int nfree = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int sl = lane + 64 * h;
+        const int blk = h ? s1 : s0;
+        bool fr = false;
+        if (sl < k) fr = blk < 0 || blk >= dm.max_blocks || !((bits[blk >> 5] >> (blk & 31)) & 1u);
         const uint64_t m = __ballot(fr);
         if (fr) {
             const int at = nfree + __popcll(m & lt);
@@ -259,6 +308,8 @@ __device__ void swap_row(const Dims &dm, int r, const int32_t *sel, int ns, cons
         nfree += __popcll(m);
     }
     wave_sync_lds();
+    int32_t *sbk = sw.slot_block + (int64_t)r * k;
+    int32_t *bsl = sw.block_slot + (int64_t)r * dm.max_blocks;
     for (int i = lane; i < nfree; i += 64) {
         const int sl = fs[i], old = fo[i];
         if (old >= 0 && old < dm.max_blocks) bsl[old] = -1;
@@ -269,23 +320,18 @@ __device__ void swap_row(const Dims &dm, int r, const int32_t *sel, int ns, cons
             sbk[sl] = -1;
         }
     }
-    int32_t *fbo = fetch_block + (int64_t)r * k;
-    int32_t *fso = fetch_slot + (int64_t)r * k;
+    int32_t *fbo = sw.fetch_block + (int64_t)r * k;
+    int32_t *fso = sw.fetch_slot + (int64_t)r * k;
     for (int i = lane; i < k; i += 64) {
         fbo[i] = i < nf ? fb[i] : -1;
         fso[i] = i < nf ? fs[i] : -1;
     }
     if (lane == 0) {
-        n_fetch[r] = nf;
-        counters[2 * r] += (uint64_t)nf;
-        counters[2 * r + 1] += (uint64_t)kept;
+        sw.n_fetch[r] = nf;
+        sw.counters[2 * r] += (uint64_t)nf;
+        sw.counters[2 * r + 1] += (uint64_t)kept;
     }
 }
-
-struct SwapArgs {
-    int32_t *slot_block, *block_slot, *fetch_block, *fetch_slot, *n_fetch;
-    uint64_t *counters;
-};
 
 __global__ void __launch_bounds__(SELECT_THREADS)
 select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ e_blk, int n_cand,
@@ -293,12 +339,12 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
               int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
               uint32_t *__restrict__ sel_bits, SwapArgs sw) {
     extern __shared__ uint64_t keys[];  // P keys, only when a budget exceeds 64
-    __shared__ uint32_t ge[MAX_W], ev[MAX_W], sb[MAX_W];
-    __shared__ uint64_t lists[SELECT_WAVES * 64], top[64];
+    __shared__ uint32_t ge[MAX_W], ev[MAX_W], sb[MAX_W], res[MAX_W];
+    __shared__ uint64_t surv[SELECT_WAVES * WAVE_TOPK];
+    __shared__ int n_surv;
     __shared__ uint64_t red64[SELECT_WAVES];
     __shared__ int red32[SELECT_WAVES];
-    __shared__ int sel_l[MAX_K], fb[MAX_K], fs[MAX_K], fo[MAX_K];
-    __shared__ int n_sel_l;
+    __shared__ int fb[MAX_K], fs[MAX_K], fo[MAX_K];
     const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -308,17 +354,27 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
     uint32_t *ge_g = ge_bits + (int64_t)r * W;
     uint32_t *ev_g = ev_bits + (int64_t)r * W;
 
+    // independent loads first: this thread's scores, the cache's slot table
+    float sv[KEYS_PER_THREAD];
+#pragma unroll
+    for (int i = 0; i < KEYS_PER_THREAD; ++i) {
+        const int j = tid + SELECT_THREADS * i;
+        sv[i] = j < n_cand ? Sq[j] : 0.f;
+    }
+    int s0 = -1, s1 = -1;
+    if (sw.slot_block && wave == 0) {
+        if (lane < dm.k) s0 = sw.slot_block[(int64_t)r * dm.k + lane];
+        if (lane + 64 < dm.k) s1 = sw.slot_block[(int64_t)r * dm.k + lane + 64];
+    }
+
     // ---- Gamma_e ----
     if (n_prev < 0) {
         for (int w = tid; w < W; w += nt) { ge[w] = 0u; ev[w] = 0u; }
         __syncthreads();
         const int ke = min(dm.k_e, n_cand);
         if (ke > 0 && dm.k_e <= WAVE_TOPK) {
-            topk_waves(n_cand, [&](int j) { return rank_key(E[j], j); }, lists, top);
-            if (tid < ke) {
-                const int j = key_index(top[tid]);
-                atomicOr(&ge[j >> 5], 1u << (j & 31));
-            }
+            topk_dispatch(n_cand, ke, [&](int j, int) { return rank_key(E[j], j); }, surv,
+                          &n_surv, ge);
         } else if (ke > 0) {
             for (int i = tid; i < P; i += nt) keys[i] = i < n_cand ? rank_key(E[i], i) : 0ull;
             __syncthreads();
@@ -381,22 +437,22 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
     }
 
     // ---- Gamma_q: best k_q of the candidates outside Gamma_e ----
-    for (int w = tid; w < W; w += nt) sb[w] = ge[w];
     int ne_loc = 0;
-    for (int w = tid; w < W; w += nt) ne_loc += __popc(ge[w]);
-    const int n_e = block_sum_int(ne_loc, red32);
+    for (int w = tid; w < W; w += nt) {
+        sb[w] = ge[w];
+        ne_loc += __popc(ge[w]);
+    }
+    const int n_e = block_sum_int(ne_loc, red32);  // also orders the sb copies
     const int kq = min(dm.k_q, n_cand - n_e);
-    auto q_key = [&](int j) -> uint64_t {
-        return ((ge[j >> 5] >> (j & 31)) & 1u) ? 0ull : rank_key(Sq[j], j);
-    };
     if (kq > 0 && dm.k_q <= WAVE_TOPK) {
-        topk_waves(n_cand, q_key, lists, top);
-        if (tid < kq) {
-            const int j = key_index(top[tid]);
-            atomicOr(&sb[j >> 5], 1u << (j & 31));
-        }
+        topk_dispatch(n_cand, kq, [&](int j, int i) -> uint64_t {
+            return ((ge[j >> 5] >> (j & 31)) & 1u) ? 0ull : rank_key(sv[i], j);
+        }, surv, &n_surv, sb);
     } else if (kq > 0) {
-        for (int i = tid; i < P; i += nt) keys[i] = i < n_cand ? q_key(i) : 0ull;
+        for (int i = tid; i < P; i += nt) {
+            const bool ok = i < n_cand && !((ge[i >> 5] >> (i & 31)) & 1u);
+            keys[i] = ok ? rank_key(Sq[i], i) : 0ull;
+        }
         __syncthreads();
         bitonic_desc(keys, P);
         for (int i = tid; i < kq; i += nt) {
@@ -427,41 +483,31 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
         int32_t *out = sel + (int64_t)r * dm.k;
         uint32_t bits = w0;
         while (bits && pos < dm.k) {
-            const int j = 2 * lane * 32 + __ffs(bits) - 1;
+            out[pos++] = 2 * lane * 32 + __ffs(bits) - 1;
             bits &= bits - 1u;
-            out[pos] = j;
-            sel_l[pos++] = j;
         }
         bits = w1;
         while (bits && pos < dm.k) {
-            const int j = (2 * lane + 1) * 32 + __ffs(bits) - 1;
+            out[pos++] = (2 * lane + 1) * 32 + __ffs(bits) - 1;
             bits &= bits - 1u;
-            out[pos] = j;
-            sel_l[pos++] = j;
         }
         const int total = min(__shfl(inc, 63, 64), dm.k);
         for (int i = total + lane; i < dm.k; i += 64) out[i] = -1;
-        if (lane == 0) {
-            n_sel[r] = total;
-            n_sel_l = total;
-        }
-        if (sw.slot_block) {
-            wave_sync_lds();
-            swap_row(dm, r, sel_l, n_sel_l, sb, sw.slot_block, sw.block_slot, sw.fetch_block,
-                     sw.fetch_slot, sw.n_fetch, sw.counters, fb, fs, fo);
-        }
+        if (lane == 0) n_sel[r] = total;
+        if (sw.slot_block) swap_row(dm, r, sb, s0, s1, res, fb, fs, fo, sw);
     }
 }
 
-// Stand-alone set difference: one wave per row, inputs from global memory.
+// Stand-alone set difference: one wave per row, selection bitmap and slot
+// table from global memory.
 __global__ void __launch_bounds__(64)
-swap_kernel(Dims dm, const int32_t *__restrict__ sel, const int32_t *__restrict__ n_sel,
-            const uint32_t *__restrict__ sel_bits, SwapArgs sw) {
+swap_kernel(Dims dm, const uint32_t *__restrict__ sel_bits, SwapArgs sw) {
+    __shared__ uint32_t res[MAX_W];
     __shared__ int fb[MAX_K], fs[MAX_K], fo[MAX_K];
-    const int r = blockIdx.x;
-    swap_row(dm, r, sel + (int64_t)r * dm.k, n_sel[r], sel_bits + (int64_t)r * dm.W,
-             sw.slot_block, sw.block_slot, sw.fetch_block, sw.fetch_slot, sw.n_fetch,
-             sw.counters, fb, fs, fo);
+    const int r = blockIdx.x, lane = threadIdx.x;
+    const int s0 = lane < dm.k ? sw.slot_block[(int64_t)r * dm.k + lane] : -1;
+    const int s1 = lane + 64 < dm.k ? sw.slot_block[(int64_t)r * dm.k + lane + 64] : -1;
+    swap_row(dm, r, sel_bits + (int64_t)r * dm.W, s0, s1, res, fb, fs, fo, sw);
 }
 
 // ---------------------------------------------------------------------------
@@ -541,9 +587,11 @@ hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, i
 
 hipError_t launch_swap(const Dims &dm, const int32_t *sel, const int32_t *n_sel,
                        const uint32_t *sel_bits, const SwapPtrs &swap, hipStream_t st) {
+    (void)sel;
+    (void)n_sel;  // the bitmap carries the same selection
     SwapArgs sw{swap.slot_block, swap.block_slot, swap.fetch_block, swap.fetch_slot, swap.n_fetch,
                 swap.counters};
-    hipLaunchKernelGGL(swap_kernel, dim3(dm.rows), dim3(64), 0, st, dm, sel, n_sel, sel_bits, sw);
+    hipLaunchKernelGGL(swap_kernel, dim3(dm.rows), dim3(64), 0, st, dm, sel_bits, sw);
     return hipGetLastError();
 }
 
