@@ -166,12 +166,24 @@ __device__ void block_topk(const uint64_t (&x)[M], int k, uint64_t *surv, int *n
         if (keep) surv[base + __popcll(m & lt)] = x[i];
     }
     __syncthreads();
+    // four threads per survivor, each counting the larger survivors in a
+    // quarter of the list (two keys per 16-byte LDS read), quad-summed
     const int ns = *n_surv;
-    for (int i = threadIdx.x; i < ns; i += blockDim.x) {
-        const uint64_t me = surv[i];
+    const int q4 = ((ns + 7) / 8) * 2;  // keys per quarter, even
+    for (int base = 0; base < ns * 4; base += blockDim.x) {
+        const int i = (base + threadIdx.x) >> 2, part = threadIdx.x & 3;
+        const uint64_t me = i < ns ? surv[i] : ~0ull;
         int above = 0;
-        for (int j = 0; j < ns; ++j) above += surv[j] > me;
-        if (above < k) {
+        const int j0 = part * q4, j1 = min(j0 + q4, ns);
+        int j = j0;
+        for (; j + 1 < j1; j += 2) {
+            const ulonglong2 two = *reinterpret_cast<const ulonglong2 *>(surv + j);
+            above += (two.x > me) + (two.y > me);
+        }
+        if (j < j1) above += surv[j] > me;
+        above += __shfl_xor(above, 1, 64);
+        above += __shfl_xor(above, 2, 64);
+        if (i < ns && part == 0 && above < k) {
             const int idx = key_index(me);
             atomicOr(&bits[idx >> 5], 1u << (idx & 31));
         }
@@ -340,11 +352,12 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
               uint32_t *__restrict__ sel_bits, SwapArgs sw) {
     extern __shared__ uint64_t keys[];  // P keys, only when a budget exceeds 64
     __shared__ uint32_t ge[MAX_W], ev[MAX_W], sb[MAX_W], res[MAX_W];
-    __shared__ uint64_t surv[SELECT_WAVES * WAVE_TOPK];
+    __shared__ __attribute__((aligned(16))) uint64_t surv[SELECT_WAVES * WAVE_TOPK + 2];
     __shared__ int n_surv;
     __shared__ uint64_t red64[SELECT_WAVES];
     __shared__ int red32[SELECT_WAVES];
     __shared__ int fb[MAX_K], fs[MAX_K], fo[MAX_K];
+    __shared__ int woff[MAX_W + 1];
     const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -468,8 +481,8 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
         ev_g[w] = ev[w];
         sel_bits[(int64_t)r * W + w] = sb[w];
     }
+    // word offsets of the selection (one wave scans <= 128 words, two per lane)
     if (wave == 0) {
-        // lane l holds words 2l and 2l+1; exclusive prefix of their popcounts
         const uint32_t w0 = 2 * lane < W ? sb[2 * lane] : 0u;
         const uint32_t w1 = 2 * lane + 1 < W ? sb[2 * lane + 1] : 0u;
         const int cnt = __popc(w0) + __popc(w1);
@@ -479,23 +492,24 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
             const int y = __shfl_up(inc, o, 64);
             if (lane >= o) inc += y;
         }
-        int pos = inc - cnt;
-        int32_t *out = sel + (int64_t)r * dm.k;
-        uint32_t bits = w0;
-        while (bits && pos < dm.k) {
-            out[pos++] = 2 * lane * 32 + __ffs(bits) - 1;
-            bits &= bits - 1u;
-        }
-        bits = w1;
-        while (bits && pos < dm.k) {
-            out[pos++] = (2 * lane + 1) * 32 + __ffs(bits) - 1;
-            bits &= bits - 1u;
-        }
-        const int total = min(__shfl(inc, 63, 64), dm.k);
-        for (int i = total + lane; i < dm.k; i += 64) out[i] = -1;
-        if (lane == 0) n_sel[r] = total;
-        if (sw.slot_block) swap_row(dm, r, sb, s0, s1, res, fb, fs, fo, sw);
+        if (2 * lane < W) woff[2 * lane] = inc - cnt;
+        if (2 * lane + 1 < W) woff[2 * lane + 1] = inc - cnt + __popc(w0);
+        if (lane == 63) woff[MAX_W] = inc;
     }
+    __syncthreads();
+    // every thread places its own selected candidates
+    int32_t *out = sel + (int64_t)r * dm.k;
+    const int total = min(woff[MAX_W], dm.k);
+    for (int j = tid; j < n_cand; j += nt) {
+        const uint32_t word = sb[j >> 5];
+        if ((word >> (j & 31)) & 1u) {
+            const int pos = woff[j >> 5] + __popc(word & ((1u << (j & 31)) - 1u));
+            if (pos < dm.k) out[pos] = j;
+        }
+    }
+    for (int i = total + tid; i < dm.k; i += nt) out[i] = -1;
+    if (tid == 0) n_sel[r] = total;
+    if (sw.slot_block && wave == 0) swap_row(dm, r, sb, s0, s1, res, fb, fs, fo, sw);
 }
 
 // Stand-alone set difference: one wave per row, selection bitmap and slot
