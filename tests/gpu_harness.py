@@ -86,6 +86,36 @@ def upload(w: Workload, layer: int = 0, ov: Overrides | None = None, steps: int 
     return GpuInputs(w, kv, kv_ptr, nb, e_tok, q)
 
 
+def upload_slabs(w: Workload, workers: int = 16) -> list:
+    """Pinned host KV of every slab: [(PinnedBuffer, device alias)]."""
+    nb = w.nb_max
+    BE = 2 * 64 * w.head_dim
+    out = []
+    for slab in range(w.kv_slabs):
+        buf = PinnedBuffer(w.rows * nb * BE * 2)
+        view = buf.array(np.uint16, (w.rows, nb, BE))
+
+        def fill(r, slab=slab, view=view):
+            view[r] = _row_blocks(w, slab, r, nb)
+        synth.parallel_map(fill, range(w.rows), workers)
+        out.append((buf, buf.dev))
+    return out
+
+
+def upload_layer(w: Workload, layer: int, kv, ov: Overrides | None, steps: int,
+                 device="cuda", workers: int = 16) -> GpuInputs:
+    """Eviction scores and queries of one layer; KV from an existing slab."""
+    nb = w.nb_max
+    e = np.zeros((w.rows, nb * 64), np.float32)
+    e[:, :w.n_max] = np.stack(synth.parallel_map(
+        lambda r: synth.evict_row(w, layer, *divmod(r, w.n_kv_heads), ov), range(w.rows), workers))
+    e_tok = torch.from_numpy(e).to(device)
+    qs = synth.parallel_map(lambda t: storage(synth.queries_step(w, layer, t, ov), w), range(steps),
+                            workers)
+    q = to_device(np.stack(qs), w, device)
+    return GpuInputs(w, kv[0], kv[1], nb, e_tok, q)
+
+
 def make_layer(w: Workload, inp: GpuInputs, decode_kernel=L.NOSA_DECODE_AUTO,
                fuse_select_swap=True) -> DecodeLayer:
     return DecodeLayer(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,

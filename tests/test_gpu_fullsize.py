@@ -50,3 +50,39 @@ def test_fullsize_bf16_3b_64k():
 
 def test_fullsize_offload_1layer_128k():
     _fullsize("offload_1layer_128k", rows=[0, 77, 127], steps=256)
+
+
+def test_fullsize_offload_8b_32layer_32k():
+    """32 layers x batch 64 x 8 KV heads, all five stages per layer per step,
+    steps 0..65 (a block completes at step 64); sampled layers and rows are
+    checked at every step."""
+    gh = _gpu()
+    w = synth.WORKLOADS["offload_8b_32layer_32k"]
+    steps = 66
+    layers_checked = {0: [0, 300, 511], 17: [5, 257], 31: [0, 511]}
+    traces = {}
+    for l, rows in layers_checked.items():
+        print(f"[fullsize] 8b: oracle layer {l} rows {rows}", flush=True)
+        traces[l] = oracle_trace(w, layer=l, rows=rows, steps=list(range(steps)))
+    print("[fullsize] 8b: pinned host KV slabs", flush=True)
+    slabs = gh.upload_slabs(w)
+    layers, inputs = [], []
+    for l in range(w.n_layers):
+        ov = traces[l].ov if l in traces else None
+        inp = gh.upload_layer(w, l, slabs[l % w.kv_slabs], ov, steps)
+        inputs.append(inp)
+        layers.append(gh.make_layer(w, inp))
+    print("[fullsize] 8b: running 32 layers", flush=True)
+    for layer in layers:
+        layer.start(w.n_tokens(0))
+    for t in range(steps):
+        for l, layer in enumerate(layers):
+            layer.step(inputs[l].q[t], w.n_tokens(t))
+            if l in traces:
+                got = gh.snapshot(layer, w)
+                for r in layers_checked[l]:
+                    _compare_step(w, traces[l], t, r, got)
+        if t % 16 == 0:
+            print(f"[fullsize] 8b: step {t} done", flush=True)
+    for buf, _ in slabs:
+        buf.free()
