@@ -183,6 +183,22 @@ nosa_status nosa_select_swap(const nosa_shape *shape, const float *s_q, const fl
                              int32_t *fetch_slot, int32_t *n_fetch, uint64_t *counters,
                              void *stream);
 
+/* nosa_select (and, when the six cache pointers are given, the set
+ * difference as in nosa_select_swap) that also writes the two parts of the
+ * selection as ascending lists: ge_list int32 [rows][k_e] (Gamma_e) with
+ * n_ge [rows], and gq_list int32 [rows][k_q] (Gamma_q) with n_gq [rows],
+ * -1 padded. The cache pointers are all NULL or all non-NULL. A step that
+ * completes no block leaves Gamma_e unchanged (strict eviction only acts on
+ * new candidates), so the previous step's ge_list already names this step's
+ * eviction set: attention over it can start before this step's scores. */
+nosa_status nosa_select_parts(const nosa_shape *shape, const float *s_q, const float *e_blk,
+                              const nosa_step *step, uint32_t *ge_bits, uint32_t *ev_bits,
+                              int32_t *sel, int32_t *n_sel, uint32_t *sel_bits, int32_t *ge_list,
+                              int32_t *n_ge, int32_t *gq_list, int32_t *n_gq,
+                              int32_t *slot_block, int32_t *block_slot, int32_t *fetch_block,
+                              int32_t *fetch_slot, int32_t *n_fetch, uint64_t *counters,
+                              void *stream);
+
 /* Copy fetch_block[r][i] of the source KV buffer to slot fetch_slot[r][i] of
  * the destination KV buffer, for i < n_fetch[r] (at most max_fetch), every
  * row (Methodology, "High-Bandwidth Communication"). The copy is a GPU kernel
@@ -194,9 +210,15 @@ nosa_status nosa_fetch_blocks(const nosa_shape *shape, const void *src_kv, int64
                               const int32_t *n_fetch, int32_t max_fetch, void *dst_kv,
                               int64_t dst_row_blocks, void *stream);
 
-/* Workspace bytes nosa_sparse_decode needs for this shape (split-K partials).
- * Calls that overlap in time need separate workspaces. */
+/* Workspace bytes the attention calls need for this shape: split-K partials
+ * of up to k + 2 chunks per row (one call over the whole selection, or two
+ * partial calls over its parts). Calls that overlap in time need separate
+ * workspaces, or disjoint chunk ranges of one (nosa_decode_partial). */
 size_t nosa_decode_workspace_size(const nosa_shape *shape);
+
+/* Chunks a partial-attention call over list_len list entries (plus the
+ * newest block when with_newest = 1) occupies; -1 for invalid arguments. */
+int32_t nosa_decode_chunks(const nosa_shape *shape, int32_t list_len, int32_t with_newest);
 
 /* Sparse decode attention for every query head (Methodology, "ED-DMA"):
  * over the tokens T of the listed blocks plus the newest block (block n_cand,
@@ -217,6 +239,27 @@ nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const voi
                                const int32_t *n_list, const void *cur_kv, int64_t cur_row_blocks,
                                const nosa_step *step, const float *e_tok, int64_t e_row_stride,
                                void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* The first half of nosa_sparse_decode over an arbitrary block list: for
+ * every row, attention partials (running max, sum and weighted values per
+ * head) over list entries 0 .. list_len-1 of row r (list[r*list_stride + i];
+ * NOSA_KV_FULL: block ids, the first n_list[r] valid; NOSA_KV_CACHE: slot i
+ * holds block list[...], -1 skipped) and, when with_newest = 1, the newest
+ * block. They fill workspace chunks chunk0 .. chunk0 + nosa_decode_chunks()-1.
+ * Two calls over disjoint lists and disjoint chunk ranges may run
+ * concurrently on different streams; nosa_decode_combine then merges.
+ * kv may be NULL when list_len is 0. */
+nosa_status nosa_decode_partial(const nosa_shape *shape, const void *q, const void *kv,
+                                int64_t kv_row_blocks, int32_t kv_mode, const int32_t *list,
+                                const int32_t *n_list, int32_t list_stride, int32_t list_len,
+                                int32_t with_newest, const void *cur_kv, int64_t cur_row_blocks,
+                                const nosa_step *step, const float *e_tok, int64_t e_row_stride,
+                                void *ws, size_t ws_bytes, int32_t chunk0, void *stream);
+
+/* The second half: merges workspace chunks 0 .. n_chunks-1 of every row in
+ * chunk order and writes out [batch][n_q_heads][D]. */
+nosa_status nosa_decode_combine(const nosa_shape *shape, int32_t n_chunks, void *out, void *ws,
+                                size_t ws_bytes, void *stream);
 
 /* Pinned host memory readable by GPU kernels: *host is the host address,
  * *dev the device alias to pass as a kernel source. coherent != 0 asks for

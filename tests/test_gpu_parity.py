@@ -99,6 +99,21 @@ def test_parity_separate_select_and_swap(name):
             _compare_step(w, tr, t, r, res[t])
 
 
+@pytest.mark.parametrize("name", ["tiny_f32", "small_f32", "small_bf16"])
+def test_parity_overlapped_decode(name):
+    """Eviction-set attention on a side stream, query-set attention after the
+    selection, then the merge (nosa_select_parts, nosa_decode_partial x2,
+    nosa_decode_combine)."""
+    gh = _gpu()
+    w = synth.WORKLOADS[name]
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov)
+    _, res = gh.run(w, inp, list(range(w.steps)), overlap=True)
+    for t in range(w.steps):
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, res[t])
+
+
 EDGE = {
     # fewer tokens than one block at the start: no candidates, then one
     "short_context": dict(context=10, steps=70, k_e=2, k_q=2),
@@ -119,14 +134,15 @@ EDGE = {
 }
 
 
+@pytest.mark.parametrize("overlap", [False, True])
 @pytest.mark.parametrize("edge", sorted(EDGE))
-def test_parity_edge_cases(edge):
+def test_parity_edge_cases(edge, overlap):
     gh = _gpu()
     base = synth.WORKLOADS["small_bf16"]
     w = base.scaled(name="edge_" + edge, seed=3000 + sorted(EDGE).index(edge), **EDGE[edge])
     tr = oracle_trace(w)
     inp = gh.upload(w, ov=tr.ov)
-    _, res = gh.run(w, inp, list(range(w.steps)))
+    _, res = gh.run(w, inp, list(range(w.steps)), overlap=overlap)
     for t in range(w.steps):
         for r in range(w.rows):
             _compare_step(w, tr, t, r, res[t])
@@ -143,6 +159,34 @@ def test_offload_edge_gqa1_short():
     for t in range(w.steps):
         for r in range(w.rows):
             _compare_step(w, tr, t, r, res[t])
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "small_offload", "small_f32"])
+def test_one_call_decode_matches_split_calls(name):
+    """nosa_sparse_decode (partial + merge in one call) gives the same bits as
+    the pipeline's nosa_decode_partial + nosa_decode_combine."""
+    gh = _gpu()
+    from trainable_block_sparse_nosa_amd import _lib as L
+    w = synth.WORKLOADS[name]
+    inp = gh.upload(w)
+    layer, _ = gh.run(w, inp, list(range(w.steps)), collect=[])
+    t = w.steps - 1
+    c = w.n_cand(t)
+    st = L.make_step(w.n_tokens(t), c)
+    ref = layer.out.clone()
+    out = torch.empty_like(ref)
+    if w.offload:
+        L.nosa_sparse_decode(layer.shape, inp.q[t], layer.cache, layer.k, L.NOSA_KV_CACHE,
+                             layer.slot_block, None, layer.cur, 1, st, layer.e_tok,
+                             layer.e_stride, out, layer.ws, layer.ws_bytes)
+    else:
+        L.nosa_sparse_decode(layer.shape, inp.q[t], layer.kv, layer.kv_row_blocks,
+                             L.NOSA_KV_FULL, layer.sel, layer.n_sel, layer._kv_ptr(c),
+                             layer.kv_row_blocks, st, layer.e_tok, layer.e_stride, out, layer.ws,
+                             layer.ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16 if w.dtype == "bf16" else torch.int32),
+                       ref.view(torch.int16 if w.dtype == "bf16" else torch.int32))
 
 
 def test_deterministic_rerun():

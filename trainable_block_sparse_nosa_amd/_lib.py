@@ -30,7 +30,8 @@ NOSA_DECODE_MFMA = 2
 
 EXPORTS = (
     "nosa_pool_blocks", "nosa_score_blocks", "nosa_select", "nosa_select_swap", "nosa_swap_diff",
-    "nosa_fetch_blocks", "nosa_decode_workspace_size", "nosa_sparse_decode",
+    "nosa_select_parts", "nosa_fetch_blocks", "nosa_decode_workspace_size", "nosa_decode_chunks",
+    "nosa_sparse_decode", "nosa_decode_partial", "nosa_decode_combine",
     "nosa_host_alloc", "nosa_host_free", "nosa_status_string", "nosa_last_error",
     "nosa_version",
 )
@@ -68,6 +69,11 @@ def _load() -> ctypes.CDLL:
         "nosa_swap_diff": [SH, P, P, P, P, P, P, P, P, P, P],
         "nosa_fetch_blocks": [SH, P, I64, P, P, P, I32, P, I64, P],
         "nosa_sparse_decode": [SH, P, P, I64, I32, P, P, P, I64, ST, P, I64, P, P, SZ, P],
+        "nosa_select_parts": [SH, P, P, ST] + [P] * 15 + [P],
+        "nosa_decode_chunks": [SH, I32, I32],
+        "nosa_decode_partial": [SH, P, P, I64, I32, P, P, I32, I32, I32, P, I64, ST, P, I64, P, SZ,
+                                I32, P],
+        "nosa_decode_combine": [SH, I32, P, P, SZ, P],
         "nosa_host_alloc": [SZ, I32, ctypes.POINTER(P), ctypes.POINTER(P)],
         "nosa_host_free": [P],
     }
@@ -75,6 +81,7 @@ def _load() -> ctypes.CDLL:
         f = getattr(L, name)
         f.argtypes = args
         f.restype = ctypes.c_int32
+    L.nosa_decode_chunks.restype = ctypes.c_int32
     L.nosa_decode_workspace_size.argtypes = [SH]
     L.nosa_decode_workspace_size.restype = SZ
     L.nosa_status_string.argtypes = [ctypes.c_int32]
@@ -149,6 +156,37 @@ def nosa_select_swap(shape, s_q, e_blk, step, ge_bits, ev_bits, sel, n_sel, sel_
         ctypes.byref(shape), _p(s_q), _p(e_blk), ctypes.byref(step), _p(ge_bits), _p(ev_bits),
         _p(sel), _p(n_sel), _p(sel_bits), _p(slot_block), _p(block_slot), _p(fetch_block),
         _p(fetch_slot), _p(n_fetch), _p(counters), _s(stream)))
+
+
+def nosa_select_parts(shape, s_q, e_blk, step, ge_bits, ev_bits, sel, n_sel, sel_bits, ge_list,
+                      n_ge, gq_list, n_gq, slot_block=None, block_slot=None, fetch_block=None,
+                      fetch_slot=None, n_fetch=None, counters=None, stream=None):
+    _chk("nosa_select_parts", _L.nosa_select_parts(
+        ctypes.byref(shape), _p(s_q), _p(e_blk), ctypes.byref(step), _p(ge_bits), _p(ev_bits),
+        _p(sel), _p(n_sel), _p(sel_bits), _p(ge_list), _p(n_ge), _p(gq_list), _p(n_gq),
+        _p(slot_block), _p(block_slot), _p(fetch_block), _p(fetch_slot), _p(n_fetch),
+        _p(counters), _s(stream)))
+
+
+def nosa_decode_chunks(shape, list_len, with_newest) -> int:
+    n = _L.nosa_decode_chunks(ctypes.byref(shape), list_len, with_newest)
+    if n < 0:
+        raise NosaError("nosa_decode_chunks", NOSA_ERR_INVALID_ARGUMENT)
+    return n
+
+
+def nosa_decode_partial(shape, q, kv, kv_row_blocks, kv_mode, list_, n_list, list_stride,
+                        list_len, with_newest, cur_kv, cur_row_blocks, step, e_tok, e_row_stride,
+                        ws, ws_bytes, chunk0, stream=None):
+    _chk("nosa_decode_partial", _L.nosa_decode_partial(
+        ctypes.byref(shape), _p(q), _p(kv), kv_row_blocks, kv_mode, _p(list_), _p(n_list),
+        list_stride, list_len, with_newest, _p(cur_kv), cur_row_blocks, ctypes.byref(step),
+        _p(e_tok), e_row_stride, _p(ws), ws_bytes, chunk0, _s(stream)))
+
+
+def nosa_decode_combine(shape, n_chunks, out, ws, ws_bytes, stream=None):
+    _chk("nosa_decode_combine", _L.nosa_decode_combine(
+        ctypes.byref(shape), n_chunks, _p(out), _p(ws), ws_bytes, _s(stream)))
 
 
 def nosa_swap_diff(shape, sel, n_sel, sel_bits, slot_block, block_slot, fetch_block, fetch_slot,

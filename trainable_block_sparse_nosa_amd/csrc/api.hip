@@ -86,17 +86,77 @@ template <typename F> nosa_status by_group(const Dims &dm, F &&f) {
     }
 }
 
-// Workspace: the partial outputs [rows][n_chunks][G][D] and the partial
-// (max, sum) [rows][n_chunks][G][2], float32.
-size_t decode_ws_bytes(const Dims &dm, const DecodePlan &pl) {
-    const size_t parts = (size_t)dm.rows * pl.n_chunks * dm.G;
+// Workspace: partial outputs [rows][chunk_cap][G][D], then partial (max, sum)
+// [rows][chunk_cap][G][2], float32.
+size_t decode_ws_bytes(const Dims &dm) {
+    const size_t parts = (size_t)dm.rows * decode_chunk_cap(dm) * dm.G;
     return parts * dm.D * sizeof(float) + parts * 2 * sizeof(float);
 }
 
-size_t decode_ws_bytes_max(const Dims &dm) {
-    const size_t a = decode_ws_bytes(dm, decode_plan(dm, NOSA_DECODE_VALU));
-    const size_t b = decode_ws_bytes(dm, decode_plan(dm, NOSA_DECODE_MFMA));
-    return a > b ? a : b;
+// Validation shared by the attention entry points; fills everything in `a`
+// except the list description and the chunk placement.
+nosa_status decode_common(const Dims &dm, int kind, const void *q, const void *kv,
+                          int64_t kv_row_blocks, int32_t kv_mode, const void *cur_kv,
+                          int64_t cur_row_blocks, const nosa_step *step, const float *e_tok,
+                          int64_t e_row_stride, void *ws, size_t ws_bytes, DecodeArgs &a) {
+    if (!q || !cur_kv || !e_tok || !ws) return NOSA_ERR_INVALID_ARGUMENT;
+    if (kv_mode != NOSA_KV_FULL && kv_mode != NOSA_KV_CACHE) return NOSA_ERR_INVALID_ARGUMENT;
+    if (kind == NOSA_DECODE_MFMA && dm.dtype != NOSA_BF16) return NOSA_ERR_UNSUPPORTED;
+    if (kv_row_blocks <= 0 || cur_row_blocks <= 0) return NOSA_ERR_INVALID_ARGUMENT;
+    const int n_cand = step_cand(dm, step);
+    if (n_cand < 0) return NOSA_ERR_INVALID_ARGUMENT;
+    // eviction-score rows cover whole blocks and are 16-byte aligned
+    if (e_row_stride < (int64_t)(n_cand + 1) * dm.S || (e_row_stride & 3) ||
+        ((uintptr_t)e_tok & 15u))
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (kv_mode == NOSA_KV_FULL && kv && kv_row_blocks < n_cand + 1) return NOSA_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < decode_ws_bytes(dm)) return NOSA_ERR_WORKSPACE;
+    if (((uintptr_t)q | (uintptr_t)kv | (uintptr_t)cur_kv | (uintptr_t)ws) & 15u)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    a = DecodeArgs{};
+    a.q = q;
+    a.kv = kv;
+    a.kv_row_blocks = kv_row_blocks;
+    a.kv_mode = kv_mode;
+    a.cur = cur_kv;
+    a.cur_row_blocks = cur_row_blocks;
+    a.n_tokens = step->n_tokens;
+    a.n_cand = n_cand;
+    a.e_tok = e_tok;
+    a.e_stride = e_row_stride;
+    a.chunk_cap = decode_chunk_cap(dm);
+    a.ws_o = static_cast<float *>(ws);
+    a.ws_ml = a.ws_o + (size_t)dm.rows * a.chunk_cap * dm.G * dm.D;
+    return NOSA_OK;
+}
+
+nosa_status launch_partial(const Dims &dm, int kind, const DecodePlan &pl, const DecodeArgs &a,
+                           hipStream_t st) {
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        constexpr int D = decltype(dc)::value;
+        return by_group(dm, [&](auto gc) -> nosa_status {
+            constexpr int G = decltype(gc)::value;
+            if constexpr (std::is_same<T, bf16_t>::value) {
+                if (kind == NOSA_DECODE_MFMA)
+                    return hip_status(launch_decode_mfma<D, G>(dm, pl, a, st));
+            }
+            return hip_status(launch_decode_valu<T, D, G>(dm, pl, a, st));
+        });
+    });
+}
+
+nosa_status launch_merge(const Dims &dm, int n_chunks, const DecodeArgs &a, void *out,
+                         hipStream_t st) {
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        constexpr int D = decltype(dc)::value;
+        return by_group(dm, [&](auto gc) -> nosa_status {
+            constexpr int G = decltype(gc)::value;
+            return hip_status(
+                launch_combine<T, D, G>(dm, n_chunks, a.chunk_cap, a.ws_o, a.ws_ml, out, st));
+        });
+    });
 }
 
 }  // namespace
@@ -154,7 +214,7 @@ nosa_status nosa_select(const nosa_shape *shape, const float *s_q, const float *
     const int n_cand = step_cand(dm, step);
     if (n_cand < 0) return NOSA_ERR_INVALID_ARGUMENT;
     return hip_status(launch_select(dm, s_q, e_blk, n_cand, step->n_cand_prev, ge_bits, ev_bits,
-                                    sel, n_sel, sel_bits, nullptr, (hipStream_t)stream));
+                                    sel, n_sel, sel_bits, nullptr, nullptr, (hipStream_t)stream));
 }
 
 nosa_status nosa_select_swap(const nosa_shape *shape, const float *s_q, const float *e_blk,
@@ -173,7 +233,32 @@ nosa_status nosa_select_swap(const nosa_shape *shape, const float *s_q, const fl
     if (n_cand < 0) return NOSA_ERR_INVALID_ARGUMENT;
     const SwapPtrs sw{slot_block, block_slot, fetch_block, fetch_slot, n_fetch, counters};
     return hip_status(launch_select(dm, s_q, e_blk, n_cand, step->n_cand_prev, ge_bits, ev_bits,
-                                    sel, n_sel, sel_bits, &sw, (hipStream_t)stream));
+                                    sel, n_sel, sel_bits, &sw, nullptr, (hipStream_t)stream));
+}
+
+nosa_status nosa_select_parts(const nosa_shape *shape, const float *s_q, const float *e_blk,
+                              const nosa_step *step, uint32_t *ge_bits, uint32_t *ev_bits,
+                              int32_t *sel, int32_t *n_sel, uint32_t *sel_bits, int32_t *ge_list,
+                              int32_t *n_ge, int32_t *gq_list, int32_t *n_gq,
+                              int32_t *slot_block, int32_t *block_slot, int32_t *fetch_block,
+                              int32_t *fetch_slot, int32_t *n_fetch, uint64_t *counters,
+                              void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!s_q || !e_blk || !ge_bits || !ev_bits || !sel || !n_sel || !sel_bits || !n_ge ||
+        !n_gq || (dm.k_e > 0 && !ge_list) || (dm.k_q > 0 && !gq_list))
+        return NOSA_ERR_INVALID_ARGUMENT;
+    const bool any_swap = slot_block || block_slot || fetch_block || fetch_slot || n_fetch || counters;
+    const bool all_swap = slot_block && block_slot && fetch_block && fetch_slot && n_fetch && counters;
+    if (any_swap && !all_swap) return NOSA_ERR_INVALID_ARGUMENT;
+    const int n_cand = step_cand(dm, step);
+    if (n_cand < 0) return NOSA_ERR_INVALID_ARGUMENT;
+    const SelectLists parts{ge_list, n_ge, gq_list, n_gq};
+    const SwapPtrs sw{slot_block, block_slot, fetch_block, fetch_slot, n_fetch, counters};
+    return hip_status(launch_select(dm, s_q, e_blk, n_cand, step->n_cand_prev, ge_bits, ev_bits,
+                                    sel, n_sel, sel_bits, all_swap ? &sw : nullptr, &parts,
+                                    (hipStream_t)stream));
 }
 
 nosa_status nosa_swap_diff(const nosa_shape *shape, const int32_t *sel, const int32_t *n_sel,
@@ -209,7 +294,15 @@ nosa_status nosa_fetch_blocks(const nosa_shape *shape, const void *src_kv, int64
 size_t nosa_decode_workspace_size(const nosa_shape *shape) {
     Dims dm;
     if (make_dims(shape, &dm) != NOSA_OK) return 0;
-    return decode_ws_bytes_max(dm);
+    return decode_ws_bytes(dm);
+}
+
+int32_t nosa_decode_chunks(const nosa_shape *shape, int32_t list_len, int32_t with_newest) {
+    Dims dm;
+    if (make_dims(shape, &dm) != NOSA_OK || list_len < 0 || list_len > dm.k ||
+        (with_newest != 0 && with_newest != 1))
+        return -1;
+    return decode_plan(dm, decode_kind(dm, shape->decode_kernel), list_len + with_newest).n_chunks;
 }
 
 nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *kv,
@@ -220,54 +313,74 @@ nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const voi
     Dims dm;
     nosa_status s = make_dims(shape, &dm);
     if (s != NOSA_OK) return s;
-    if (!q || !cur_kv || !e_tok || !out || !ws) return NOSA_ERR_INVALID_ARGUMENT;
-    if (kv_mode != NOSA_KV_FULL && kv_mode != NOSA_KV_CACHE) return NOSA_ERR_INVALID_ARGUMENT;
-    if (!kv || !list || (kv_mode == NOSA_KV_FULL && !n_list)) return NOSA_ERR_INVALID_ARGUMENT;
+    if (!out || !kv || !list || (kv_mode == NOSA_KV_FULL && !n_list))
+        return NOSA_ERR_INVALID_ARGUMENT;
     if (kv_mode == NOSA_KV_CACHE && kv_row_blocks < dm.k) return NOSA_ERR_INVALID_ARGUMENT;
-    if (kv_row_blocks <= 0 || cur_row_blocks <= 0) return NOSA_ERR_INVALID_ARGUMENT;
-    const int n_cand = step_cand(dm, step);
-    if (n_cand < 0) return NOSA_ERR_INVALID_ARGUMENT;
-    // eviction-score rows cover whole blocks and are 16-byte aligned
-    if (e_row_stride < (int64_t)(n_cand + 1) * dm.S || (e_row_stride & 3) ||
-        ((uintptr_t)e_tok & 15u))
-        return NOSA_ERR_INVALID_ARGUMENT;
-    if (kv_mode == NOSA_KV_FULL && kv_row_blocks < n_cand + 1) return NOSA_ERR_INVALID_ARGUMENT;
     const int kind = decode_kind(dm, shape->decode_kernel);
-    if (kind == NOSA_DECODE_MFMA && dm.dtype != NOSA_BF16) return NOSA_ERR_UNSUPPORTED;
-    const DecodePlan pl = decode_plan(dm, kind);
-    if (ws_bytes < decode_ws_bytes(dm, pl)) return NOSA_ERR_WORKSPACE;
-    if (((uintptr_t)q | (uintptr_t)kv | (uintptr_t)cur_kv | (uintptr_t)ws) & 15u)
-        return NOSA_ERR_INVALID_ARGUMENT;
-
     DecodeArgs a;
-    a.q = q;
-    a.kv = kv;
-    a.kv_row_blocks = kv_row_blocks;
-    a.kv_mode = kv_mode;
+    s = decode_common(dm, kind, q, kv, kv_row_blocks, kv_mode, cur_kv, cur_row_blocks, step, e_tok,
+                      e_row_stride, ws, ws_bytes, a);
+    if (s != NOSA_OK) return s;
     a.list = list;
-    a.n_list = n_list;
-    a.cur = cur_kv;
-    a.cur_row_blocks = cur_row_blocks;
-    a.n_tokens = step->n_tokens;
-    a.n_cand = n_cand;
-    a.e_tok = e_tok;
-    a.e_stride = e_row_stride;
-    a.out = out;
-    a.ws_o = static_cast<float *>(ws);
-    a.ws_ml = a.ws_o + (size_t)dm.rows * pl.n_chunks * dm.G * dm.D;
+    a.n_list = kv_mode == NOSA_KV_FULL ? n_list : nullptr;
+    a.list_stride = dm.k;
+    a.list_len = dm.k;
+    a.with_newest = 1;
+    a.chunk0 = 0;
+    const DecodePlan pl = decode_plan(dm, kind, dm.k + 1);
+    a.cb = pl.cb;
     const hipStream_t st = (hipStream_t)stream;
-    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
-        using T = std::remove_pointer_t<decltype(tp)>;
-        constexpr int D = decltype(dc)::value;
-        return by_group(dm, [&](auto gc) -> nosa_status {
-            constexpr int G = decltype(gc)::value;
-            if constexpr (std::is_same<T, bf16_t>::value) {
-                if (kind == NOSA_DECODE_MFMA)
-                    return hip_status(launch_decode_mfma<D, G>(dm, pl, a, st));
-            }
-            return hip_status(launch_decode_valu<T, D, G>(dm, pl, a, st));
-        });
-    });
+    s = launch_partial(dm, kind, pl, a, st);
+    if (s != NOSA_OK) return s;
+    return launch_merge(dm, pl.n_chunks, a, out, st);
+}
+
+nosa_status nosa_decode_partial(const nosa_shape *shape, const void *q, const void *kv,
+                                int64_t kv_row_blocks, int32_t kv_mode, const int32_t *list,
+                                const int32_t *n_list, int32_t list_stride, int32_t list_len,
+                                int32_t with_newest, const void *cur_kv, int64_t cur_row_blocks,
+                                const nosa_step *step, const float *e_tok, int64_t e_row_stride,
+                                void *ws, size_t ws_bytes, int32_t chunk0, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (list_len < 0 || list_len > dm.k || (with_newest != 0 && with_newest != 1))
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (list_len > 0 && (!kv || !list || list_stride < list_len ||
+                         (kv_mode == NOSA_KV_FULL && !n_list)))
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (kv_mode == NOSA_KV_CACHE && list_len > 0 && kv_row_blocks < list_len)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    const int kind = decode_kind(dm, shape->decode_kernel);
+    DecodeArgs a;
+    s = decode_common(dm, kind, q, kv ? kv : cur_kv, kv ? kv_row_blocks : cur_row_blocks,
+                      kv_mode, cur_kv, cur_row_blocks, step, e_tok, e_row_stride, ws, ws_bytes, a);
+    if (s != NOSA_OK) return s;
+    const DecodePlan pl = decode_plan(dm, kind, list_len + with_newest);
+    if (chunk0 < 0 || chunk0 + pl.n_chunks > a.chunk_cap) return NOSA_ERR_INVALID_ARGUMENT;
+    a.list = list;
+    a.n_list = kv_mode == NOSA_KV_FULL ? n_list : nullptr;
+    a.list_stride = list_stride;
+    a.list_len = list_len;
+    a.with_newest = with_newest;
+    a.chunk0 = chunk0;
+    a.cb = pl.cb;
+    return launch_partial(dm, kind, pl, a, (hipStream_t)stream);
+}
+
+nosa_status nosa_decode_combine(const nosa_shape *shape, int32_t n_chunks, void *out, void *ws,
+                                size_t ws_bytes, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!out || !ws || (((uintptr_t)ws) & 15u)) return NOSA_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < decode_ws_bytes(dm)) return NOSA_ERR_WORKSPACE;
+    if (n_chunks < 1 || n_chunks > decode_chunk_cap(dm)) return NOSA_ERR_INVALID_ARGUMENT;
+    DecodeArgs a{};
+    a.chunk_cap = decode_chunk_cap(dm);
+    a.ws_o = static_cast<float *>(ws);
+    a.ws_ml = a.ws_o + (size_t)dm.rows * a.chunk_cap * dm.G * dm.D;
+    return launch_merge(dm, n_chunks, a, out, (hipStream_t)stream);
 }
 
 nosa_status nosa_host_alloc(size_t bytes, int32_t coherent, void **host, void **dev) {

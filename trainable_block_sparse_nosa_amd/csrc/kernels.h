@@ -19,10 +19,16 @@ struct SwapPtrs {
     uint64_t *counters;
 };
 
-// swap == nullptr: selection only; else the set difference runs in the same launch
+struct SelectLists {
+    int32_t *ge_list, *n_ge, *gq_list, *n_gq;
+};
+
+// swap == nullptr: selection only; else the set difference runs in the same
+// launch. parts != nullptr: also write Gamma_e and Gamma_q as ascending lists.
 hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, int n_cand,
                          int n_prev, uint32_t *ge, uint32_t *ev, int32_t *sel, int32_t *n_sel,
-                         uint32_t *sel_bits, const SwapPtrs *swap, hipStream_t st);
+                         uint32_t *sel_bits, const SwapPtrs *swap, const SelectLists *parts,
+                         hipStream_t st);
 
 hipError_t launch_swap(const Dims &dm, const int32_t *sel, const int32_t *n_sel,
                        const uint32_t *sel_bits, const SwapPtrs &swap, hipStream_t st);
@@ -31,16 +37,18 @@ hipError_t launch_fetch(const Dims &dm, const void *src, int64_t src_row_blocks,
                         const int32_t *fblk, const int32_t *fslot, const int32_t *nfetch,
                         int max_fetch, void *dst, int64_t dst_row_blocks, hipStream_t st);
 
-// Split-K plan of the decode: list entries 0..k-1 are the selected blocks and
-// entry k is the newest block; a chunk of `cb` consecutive entries is one
-// workgroup.
+// Split-K plan of one partial-attention call: its entries are list entries
+// 0..list_len-1 plus (optionally) the newest block as entry list_len; a
+// chunk of `cb` consecutive entries is one workgroup.
 struct DecodePlan {
     int cb;        // entries per chunk
-    int n_chunks;  // chunks per row
-    int npw;       // MFMA kernel: blocks per wave (1, 2, 4 or 8)
+    int n_chunks;  // chunks of this call
 };
 int decode_kind(const Dims &dm, int requested);  // NOSA_DECODE_VALU or _MFMA
-DecodePlan decode_plan(const Dims &dm, int kind);
+DecodePlan decode_plan(const Dims &dm, int kind, int entries);
+// Workspace rows hold this many chunk partials: enough for the whole
+// selection plus the newest block in one call, or split over two calls.
+inline int decode_chunk_cap(const Dims &dm) { return dm.k + 2; }
 
 struct DecodeArgs {
     const void *q;
@@ -48,15 +56,20 @@ struct DecodeArgs {
     int64_t kv_row_blocks;
     int kv_mode;
     const int32_t *list;
-    const int32_t *n_list;
+    const int32_t *n_list;  // per-row entry counts (NOSA_KV_FULL), else null
+    int list_stride;        // list row stride
+    int list_len;           // list entries per row
+    int with_newest;        // 1: entry list_len is the newest block
     const void *cur;
     int64_t cur_row_blocks;
     int n_tokens, n_cand;
     const float *e_tok;
     int64_t e_stride;
-    void *out;
-    float *ws_o;   // [rows][n_chunks][G][D]
-    float *ws_ml;  // [rows][n_chunks][G][2]
+    float *ws_o;   // [rows][chunk_cap][G][D]
+    float *ws_ml;  // [rows][chunk_cap][G][2]
+    int chunk0;    // first workspace chunk of this call
+    int chunk_cap;
+    int cb;        // entries per chunk (from the plan)
 };
 
 template <typename T, int D, int G>
@@ -65,5 +78,8 @@ hipError_t launch_decode_valu(const Dims &dm, const DecodePlan &pl, const Decode
 template <int D, int G>
 hipError_t launch_decode_mfma(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
                               hipStream_t st);
+template <typename T, int D, int G>
+hipError_t launch_combine(const Dims &dm, int n_chunks, int chunk_cap, const float *ws_o,
+                          const float *ws_ml, void *out, hipStream_t st);
 
 }  // namespace nosa

@@ -5,8 +5,9 @@
 // exponential happens in the attention softmax; here each token's score is
 // added to its logit, z = scale * q.k + e, and softmax(z) weighs the values.
 //
-// Work split: one workgroup per (chunk of list entries, row); entries
-// 0..k-1 are the selected blocks, entry k the newest block. Each workgroup
+// Work split: one workgroup per (chunk of entries, row). A call's entries are
+// the blocks of a list (the whole selection, or one part of it) plus, when
+// asked, the newest block. Each workgroup
 // keeps an online-softmax state (max, sum, output) per head and writes it to
 // the workspace as its chunk's partial; a second kernel merges each row's
 // partials in chunk order and writes the output. The merge order is fixed,
@@ -30,8 +31,7 @@ namespace nosa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int WAVES = 4;         // waves per workgroup
-constexpr int MAX_CHUNKS = 129;  // k + 1 entries, one per chunk at most
+constexpr int WAVES = 4;  // waves per workgroup of the MFMA kernel
 
 // Position of token `tok` (0..63) inside a row of the stored V^T tile: within
 // each 32-token half, positions 8g..8g+7 hold tokens 4g..4g+3, 16+4g..16+4g+3.
@@ -39,21 +39,19 @@ __host__ __device__ constexpr int vt_token_at(int pos) {
     return 32 * (pos / 32) + 16 * ((pos % 8) / 4) + 4 * ((pos % 32) / 8) + pos % 4;
 }
 
-DecodePlan decode_plan(const Dims &dm, int kind) {
-    const int entries = dm.k + 1;
+DecodePlan decode_plan(const Dims &dm, int kind, int entries) {
     DecodePlan p;
+    if (entries <= 0) {
+        p.cb = 1;
+        p.n_chunks = 0;
+        return p;
+    }
     if (kind == NOSA_DECODE_MFMA) {
-        // blocks per wave: enough waves to fill the chip once (one resident
-        // wave per SIMD at this kernel's register use), at most 8
-        const long total = (long)dm.rows * entries;
-        // One block per wave measured fastest: at ~210 registers two waves
+        // One block per wave measured fastest: at ~200 registers two waves
         // share a SIMD and every wave issues all of its block's loads at once;
-        // walking several blocks per wave with a second register set for the
-        // next block drops to one wave per SIMD and was slower.
-        (void)total;
-        const int npw = 1;
-        p.npw = npw;
-        p.n_chunks = (entries + WAVES * npw - 1) / (WAVES * npw);
+        // walking several blocks per wave (with or without a second register
+        // set for the next block) and 1-, 2- or 8-wave workgroups were slower.
+        p.n_chunks = (entries + WAVES - 1) / WAVES;
         p.cb = (entries + p.n_chunks - 1) / p.n_chunks;  // balanced chunks
     } else {
         // enough workgroups to cover 256 CUs several times over
@@ -61,7 +59,6 @@ DecodePlan decode_plan(const Dims &dm, int kind) {
         int cb = 1;
         while (cb < 16 && total / (cb * 2) >= 2048) cb *= 2;
         p.cb = cb;
-        p.npw = 0;
         p.n_chunks = (entries + p.cb - 1) / p.cb;
     }
     return p;
@@ -81,14 +78,14 @@ int decode_kind(const Dims &dm, int requested) {
 // ---------------------------------------------------------------------------
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(D)
-combine_kernel(Dims dm, int n_chunks, const float *__restrict__ ws_o,
+combine_kernel(Dims dm, int n_chunks, int chunk_cap, const float *__restrict__ ws_o,
                const float *__restrict__ ws_ml, T *__restrict__ out) {
     constexpr int CREG = 33;  // chunks held in registers (every MFMA plan fits)
     const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x, lane = threadIdx.x & 63;
-    const float *ml = ws_ml + ((int64_t)r * n_chunks * G + h) * 2;  // chunk c at ml[c*G*2]
-    const float *po = ws_o + ((int64_t)r * n_chunks * G + h) * D + d;  // chunk c at po[c*G*D]
+    const float *ml = ws_ml + ((int64_t)r * chunk_cap * G + h) * 2;  // chunk c at ml[c*G*2]
+    const float *po = ws_o + ((int64_t)r * chunk_cap * G + h) * D + d;  // chunk c at po[c*G*D]
     float O = 0.f, L;
-    if (n_chunks <= CREG) {
+    if (n_chunks <= CREG && n_chunks <= 64) {
         float ov[CREG];
 #pragma unroll
         for (int c = 0; c < CREG; ++c)
@@ -118,35 +115,30 @@ combine_kernel(Dims dm, int n_chunks, const float *__restrict__ ws_o,
     out[((int64_t)b * dm.Hq + (int64_t)g * G + h) * D + d] = stf<T>(O / L);
 }
 
-// Resolve list entry e of row r: data pointer, block id and valid tokens.
+// Resolve entry e of row r: data pointer, block id and valid tokens.
 // Returns false when the entry holds no block.
 template <typename T>
-__device__ __forceinline__ bool resolve_entry(int e, int k, int cnt_e, int r, int kv_mode,
-                                              const T *kv, int64_t kv_row_blocks,
-                                              const int32_t *list, const T *cur,
-                                              int64_t cur_row_blocks, int n_tokens, int n_cand,
+__device__ __forceinline__ bool resolve_entry(const DecodeArgs &a, int e, int cnt_e, int r,
                                               int64_t BE, const T *&blk, int &bid, int &valid) {
-    if (e > k) return false;
-    if (e == k) {
-        blk = cur + (int64_t)r * cur_row_blocks * BE;
-        bid = n_cand;
-        valid = n_tokens - n_cand * 64;
+    if (a.with_newest && e == a.list_len) {
+        blk = static_cast<const T *>(a.cur) + (int64_t)r * a.cur_row_blocks * BE;
+        bid = a.n_cand;
+        valid = a.n_tokens - a.n_cand * 64;
         return true;
     }
-    bid = list[(int64_t)r * k + e];  // issued before the count is known
-    if (e >= cnt_e || bid < 0 || bid >= n_cand) return false;  // only candidates are listed
-    const int64_t at = kv_mode == NOSA_KV_FULL ? bid : e;
-    blk = kv + ((int64_t)r * kv_row_blocks + at) * BE;
+    if (e >= a.list_len) return false;
+    bid = a.list[(int64_t)r * a.list_stride + e];  // issued before the count is known
+    if (e >= cnt_e || bid < 0 || bid >= a.n_cand) return false;  // only candidates are listed
+    const int64_t at = a.kv_mode == NOSA_KV_FULL ? bid : e;
+    blk = static_cast<const T *>(a.kv) + ((int64_t)r * a.kv_row_blocks + at) * BE;
     valid = 64;
     return true;
 }
 
 // ---------------------------------------------------------------------------
 // MFMA partial kernel (bf16). Chunk c of a row covers entries
-// [c*epc, min((c+1)*epc, k+1)); wave w takes entries c*epc + w + 4i. While a
-// wave computes one block, the next block's operands are already loading into
-// a second register set. Lane l: col = l % 16 (head in S^T / O^T),
-// grp = l / 16.
+// [c*epc, min((c+1)*epc, entries)); wave w takes entry c*epc + w.
+// Lane l: col = l % 16 (head in S^T / O^T), grp = l / 16.
 // ---------------------------------------------------------------------------
 template <int D>
 struct BlockRegs {
@@ -235,14 +227,9 @@ __device__ __forceinline__ void attend_block(const BlockRegs<D> &br, const bf16x
     }
 }
 
-template <int D, int G, int NPW, bool PREFETCH>
+template <int D, int G>
 __global__ void __launch_bounds__(256)
-decode_mfma_kernel(Dims dm, int epc, int n_chunks, const bf16_t *__restrict__ q,
-                   const bf16_t *__restrict__ kv, int64_t kv_row_blocks, int kv_mode,
-                   const int32_t *__restrict__ list, const int32_t *__restrict__ n_list,
-                   const bf16_t *__restrict__ cur, int64_t cur_row_blocks, int n_tokens,
-                   int n_cand, const float *__restrict__ e_tok, int64_t e_stride,
-                   float *__restrict__ ws_o, float *__restrict__ ws_ml) {
+decode_mfma_kernel(Dims dm, DecodeArgs a) {
     static_assert(G <= 16, "the group is one 16-wide MFMA tile");
     constexpr int S = 64, KS = D / 32, DT = D / 16;
     constexpr int64_t BE = 2 * S * D;
@@ -255,10 +242,11 @@ decode_mfma_kernel(Dims dm, int epc, int n_chunks, const bf16_t *__restrict__ q,
     const int col = lane & 15, grp = lane >> 4;
     const int r = blockIdx.y, chunk = blockIdx.x;
     const int b = r / dm.Hkv, g = r % dm.Hkv;
-    const int k = dm.k;
-    const int cnt_e = kv_mode == NOSA_KV_FULL ? n_list[r] : k;
-    const float *er = e_tok + (int64_t)r * e_stride;
-    const int e_end = min((chunk + 1) * epc, k + 1);
+    const int epc = a.cb;
+    const int cnt_e = a.n_list ? min(a.n_list[r], a.list_len) : a.list_len;
+    const float *er = a.e_tok + (int64_t)r * a.e_stride;
+    const int e_end = min((chunk + 1) * epc, a.list_len + a.with_newest);
+    const bf16_t *q = static_cast<const bf16_t *>(a.q);
 
     // B operand of S^T = K Q^T: lane holds q[head col][32s + 8grp .. +7].
     // Padding columns (col >= G) repeat head G-1: their softmax reductions
@@ -276,29 +264,15 @@ decode_mfma_kernel(Dims dm, int epc, int n_chunks, const bf16_t *__restrict__ q,
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    BlockRegs<D> buf[PREFETCH ? 2 : 1];
-    auto fetch = [&](int i, BlockRegs<D> &br) {
-        const int e = chunk * epc + wave + WAVES * i;
+    // one entry per wave: all of the block's loads are in flight at once
+    {
+        BlockRegs<D> br;
+        const int e = chunk * epc + wave;
         const bf16_t *blk;
         int bid, valid;
-        if (e < e_end && resolve_entry(e, k, cnt_e, r, kv_mode, kv, kv_row_blocks, list, cur,
-                                       cur_row_blocks, n_tokens, n_cand, BE, blk, bid, valid))
+        if (e < e_end && resolve_entry<bf16_t>(a, e, cnt_e, r, BE, blk, bid, valid)) {
             load_block<D>(br, blk, er + (int64_t)bid * S, valid, col, grp);
-        else
-            br.valid = 0;
-    };
-    if constexpr (PREFETCH) {
-        fetch(0, buf[0]);
-#pragma unroll
-        for (int i = 0; i < NPW; ++i) {
-            if (i + 1 < NPW) fetch(i + 1, buf[(i + 1) & 1]);
-            if (buf[i & 1].valid > 0)
-                attend_block<D>(buf[i & 1], qop, dm.scale, grp, m_run, l_run, o);
-        }
-    } else {
-        for (int i = 0; i < NPW; ++i) {
-            fetch(i, buf[0]);
-            if (buf[0].valid > 0) attend_block<D>(buf[0], qop, dm.scale, grp, m_run, l_run, o);
+            attend_block<D>(br, qop, dm.scale, grp, m_run, l_run, o);
         }
     }
 
@@ -314,7 +288,8 @@ decode_mfma_kernel(Dims dm, int epc, int n_chunks, const bf16_t *__restrict__ q,
             for (int u = 0; u < 4; ++u) wo[wave][16 * dt + 4 * grp + u][col] = o[dt][u];
     }
     __syncthreads();
-    const int64_t base = ((int64_t)r * n_chunks + chunk) * G;
+    const int64_t base = ((int64_t)r * a.chunk_cap + a.chunk0 + chunk) * G;
+    float *ws_o = a.ws_o, *ws_ml = a.ws_ml;
     for (int p = threadIdx.x; p < G * D; p += blockDim.x) {
         const int h = p / D, d = p % D;
         float mw[WAVES], lw[WAVES];
@@ -345,12 +320,7 @@ decode_mfma_kernel(Dims dm, int epc, int n_chunks, const bf16_t *__restrict__ q,
 // ---------------------------------------------------------------------------
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256)
-decode_valu_kernel(Dims dm, int cb, int n_chunks, const T *__restrict__ q,
-                   const T *__restrict__ kv, int64_t kv_row_blocks, int kv_mode,
-                   const int32_t *__restrict__ list, const int32_t *__restrict__ n_list,
-                   const T *__restrict__ cur, int64_t cur_row_blocks, int n_tokens, int n_cand,
-                   const float *__restrict__ e_tok, int64_t e_stride, float *__restrict__ ws_o,
-                   float *__restrict__ ws_ml) {
+decode_valu_kernel(Dims dm, DecodeArgs a) {
     constexpr int S = 64;
     constexpr int EPV = 16 / sizeof(T);       // elements per 16-byte vector
     constexpr int KP = D + EPV;               // padded LDS row of the K tile
@@ -366,23 +336,21 @@ decode_valu_kernel(Dims dm, int cb, int n_chunks, const T *__restrict__ q,
     const int tid = threadIdx.x;
     const int r = blockIdx.y, chunk = blockIdx.x;
     const int b = r / dm.Hkv, g = r % dm.Hkv;
-    const T *qr = q + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
+    const T *qr = static_cast<const T *>(a.q) + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
     for (int p = tid; p < G * D; p += 256) qs[p] = ldf(qr + p) * dm.scale;
     if (tid < G) { m_sh[tid] = -INFINITY; l_sh[tid] = 0.f; }
     float o[NPT];
 #pragma unroll
     for (int i = 0; i < NPT; ++i) o[i] = 0.f;
 
-    const int k = dm.k;
-    const int cnt_e = kv_mode == NOSA_KV_FULL ? n_list[r] : k;
-    const int e0 = chunk * cb, e1 = min(e0 + cb, k + 1);
-    const float *er = e_tok + (int64_t)r * e_stride;
+    const int cnt_e = a.n_list ? min(a.n_list[r], a.list_len) : a.list_len;
+    const int e0 = chunk * a.cb, e1 = min(e0 + a.cb, a.list_len + a.with_newest);
+    const float *er = a.e_tok + (int64_t)r * a.e_stride;
 
     for (int e = e0; e < e1; ++e) {
         const T *blk;
         int bid, valid;
-        if (!resolve_entry(e, k, cnt_e, r, kv_mode, kv, kv_row_blocks, list, cur, cur_row_blocks,
-                           n_tokens, n_cand, BE, blk, bid, valid))
+        if (!resolve_entry<T>(a, e, cnt_e, r, BE, blk, bid, valid))
             continue;  // uniform over the workgroup
         __syncthreads();  // the previous block's readers are done with LDS
         constexpr int KV_VEC = S * D / EPV;
@@ -465,61 +433,49 @@ decode_valu_kernel(Dims dm, int cb, int n_chunks, const T *__restrict__ q,
         }
     }
     __syncthreads();
-    const int64_t base = ((int64_t)r * n_chunks + chunk) * G;
+    const int64_t base = ((int64_t)r * a.chunk_cap + a.chunk0 + chunk) * G;
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
         const int p = tid + i * 256;
-        if (p < G * D) ws_o[base * D + p] = o[i];
+        if (p < G * D) a.ws_o[base * D + p] = o[i];
     }
     if (tid < G) {
-        ws_ml[(base + tid) * 2 + 0] = m_sh[tid];
-        ws_ml[(base + tid) * 2 + 1] = l_sh[tid];
+        a.ws_ml[(base + tid) * 2 + 0] = m_sh[tid];
+        a.ws_ml[(base + tid) * 2 + 1] = l_sh[tid];
     }
 }
 
 template <typename T, int D, int G>
 hipError_t launch_decode_valu(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
                               hipStream_t st) {
-    dim3 grid(pl.n_chunks, dm.rows);
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, G>), grid, dim3(256), 0, st, dm, pl.cb,
-                       pl.n_chunks, static_cast<const T *>(a.q), static_cast<const T *>(a.kv),
-                       a.kv_row_blocks, a.kv_mode, a.list, a.n_list,
-                       static_cast<const T *>(a.cur), a.cur_row_blocks, a.n_tokens, a.n_cand,
-                       a.e_tok, a.e_stride, a.ws_o, a.ws_ml);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((combine_kernel<T, D, G>), dim3(dm.rows, G), dim3(D), 0, st, dm, pl.n_chunks,
-                       a.ws_o, a.ws_ml, static_cast<T *>(a.out));
+    if (pl.n_chunks == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, G>), dim3(pl.n_chunks, dm.rows), dim3(256), 0, st,
+                       dm, a);
     return hipGetLastError();
 }
 
 template <int D, int G>
 hipError_t launch_decode_mfma(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
                               hipStream_t st) {
-    dim3 grid(pl.n_chunks, dm.rows);
-#define NOSA_MFMA_LAUNCH(NPW)                                                                  \
-    hipLaunchKernelGGL((decode_mfma_kernel<D, G, NPW, false>), grid, dim3(256), 0, st, dm, pl.cb, \
-                       pl.n_chunks, static_cast<const bf16_t *>(a.q),                          \
-                       static_cast<const bf16_t *>(a.kv), a.kv_row_blocks, a.kv_mode, a.list,  \
-                       a.n_list, static_cast<const bf16_t *>(a.cur), a.cur_row_blocks,         \
-                       a.n_tokens, a.n_cand, a.e_tok, a.e_stride, a.ws_o, a.ws_ml)
-    switch (pl.npw) {
-    case 1: NOSA_MFMA_LAUNCH(1); break;
-    case 2: NOSA_MFMA_LAUNCH(2); break;
-    case 4: NOSA_MFMA_LAUNCH(4); break;
-    default: NOSA_MFMA_LAUNCH(8); break;
-    }
-#undef NOSA_MFMA_LAUNCH
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((combine_kernel<bf16_t, D, G>), dim3(dm.rows, G), dim3(D), 0, st, dm,
-                       pl.n_chunks, a.ws_o, a.ws_ml, static_cast<bf16_t *>(a.out));
+    if (pl.n_chunks == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G>), dim3(pl.n_chunks, dm.rows),
+                       dim3(256), 0, st, dm, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+hipError_t launch_combine(const Dims &dm, int n_chunks, int chunk_cap, const float *ws_o,
+                          const float *ws_ml, void *out, hipStream_t st) {
+    hipLaunchKernelGGL((combine_kernel<T, D, G>), dim3(dm.rows, G), dim3(D), 0, st, dm, n_chunks,
+                       chunk_cap, ws_o, ws_ml, static_cast<T *>(out));
     return hipGetLastError();
 }
 
 #define NOSA_DEC_INST(T, D, G)                                                                 \
     template hipError_t launch_decode_valu<T, D, G>(const Dims &, const DecodePlan &,          \
-                                                    const DecodeArgs &, hipStream_t);
+                                                    const DecodeArgs &, hipStream_t);          \
+    template hipError_t launch_combine<T, D, G>(const Dims &, int, int, const float *,         \
+                                                const float *, void *, hipStream_t);
 #define NOSA_DEC_ALLG(T, D)                                                                    \
     NOSA_DEC_INST(T, D, 1) NOSA_DEC_INST(T, D, 2) NOSA_DEC_INST(T, D, 3)                       \
     NOSA_DEC_INST(T, D, 4) NOSA_DEC_INST(T, D, 5) NOSA_DEC_INST(T, D, 6)                       \

@@ -264,6 +264,10 @@ struct SwapArgs {
     uint64_t *counters;
 };
 
+struct ListArgs {
+    int32_t *ge_list, *n_ge, *gq_list, *n_gq;  // n_ge null: not requested
+};
+
 // Set difference of one row, run by one wave. `bits` (LDS or global) is the
 // selection bitmap; slot l of the cache holds slots[l] (lane l and l + 64,
 // already loaded). `res` is an LDS bitmap of W words for the cached set.
@@ -349,7 +353,7 @@ __global__ void __launch_bounds__(SELECT_THREADS)
 select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ e_blk, int n_cand,
               int n_prev, int P, uint32_t *__restrict__ ge_bits, uint32_t *__restrict__ ev_bits,
               int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
-              uint32_t *__restrict__ sel_bits, SwapArgs sw) {
+              uint32_t *__restrict__ sel_bits, SwapArgs sw, ListArgs lists) {
     extern __shared__ uint64_t keys[];  // P keys, only when a budget exceeds 64
     __shared__ uint32_t ge[MAX_W], ev[MAX_W], sb[MAX_W], res[MAX_W];
     __shared__ __attribute__((aligned(16))) uint64_t surv[SELECT_WAVES * WAVE_TOPK + 2];
@@ -357,7 +361,7 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
     __shared__ uint64_t red64[SELECT_WAVES];
     __shared__ int red32[SELECT_WAVES];
     __shared__ int fb[MAX_K], fs[MAX_K], fo[MAX_K];
-    __shared__ int woff[MAX_W + 1];
+    __shared__ int woff[3 * (MAX_W + 1)];
     const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -481,33 +485,64 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
         ev_g[w] = ev[w];
         sel_bits[(int64_t)r * W + w] = sb[w];
     }
-    // word offsets of the selection (one wave scans <= 128 words, two per lane)
+    // word offsets of the selection, of Gamma_e and of Gamma_q (one wave scans
+    // <= 128 words, two per lane)
     if (wave == 0) {
-        const uint32_t w0 = 2 * lane < W ? sb[2 * lane] : 0u;
-        const uint32_t w1 = 2 * lane + 1 < W ? sb[2 * lane + 1] : 0u;
-        const int cnt = __popc(w0) + __popc(w1);
-        int inc = cnt;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += y;
+        for (int li = 0; li < 3; ++li) {
+            auto word = [&](int w) -> uint32_t {
+                if (w >= W) return 0u;
+                return li == 0 ? sb[w] : (li == 1 ? ge[w] : (sb[w] & ~ge[w]));
+            };
+            const uint32_t w0 = word(2 * lane), w1 = word(2 * lane + 1);
+            const int cnt = __popc(w0) + __popc(w1);
+            int inc = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(inc, o, 64);
+                if (lane >= o) inc += y;
+            }
+            int *wo = woff + li * (MAX_W + 1);
+            if (2 * lane < W) wo[2 * lane] = inc - cnt;
+            if (2 * lane + 1 < W) wo[2 * lane + 1] = inc - cnt + __popc(w0);
+            if (lane == 63) wo[MAX_W] = inc;
         }
-        if (2 * lane < W) woff[2 * lane] = inc - cnt;
-        if (2 * lane + 1 < W) woff[2 * lane + 1] = inc - cnt + __popc(w0);
-        if (lane == 63) woff[MAX_W] = inc;
     }
     __syncthreads();
-    // every thread places its own selected candidates
+    // every thread places its own selected candidates (union, and each part
+    // when asked for)
     int32_t *out = sel + (int64_t)r * dm.k;
     const int total = min(woff[MAX_W], dm.k);
+    const int *wo_e = woff + (MAX_W + 1), *wo_q = woff + 2 * (MAX_W + 1);
     for (int j = tid; j < n_cand; j += nt) {
         const uint32_t word = sb[j >> 5];
-        if ((word >> (j & 31)) & 1u) {
-            const int pos = woff[j >> 5] + __popc(word & ((1u << (j & 31)) - 1u));
+        const uint32_t bit = 1u << (j & 31), below = bit - 1u;
+        if (word & bit) {
+            const int pos = woff[j >> 5] + __popc(word & below);
             if (pos < dm.k) out[pos] = j;
+            if (lists.n_ge) {
+                const uint32_t we = ge[j >> 5];
+                if (we & bit) {
+                    const int pe = wo_e[j >> 5] + __popc(we & below);
+                    if (pe < dm.k_e) lists.ge_list[(int64_t)r * dm.k_e + pe] = j;
+                } else {
+                    const uint32_t wq = word & ~we;
+                    const int pq = wo_q[j >> 5] + __popc(wq & below);
+                    if (pq < dm.k_q) lists.gq_list[(int64_t)r * dm.k_q + pq] = j;
+                }
+            }
         }
     }
     for (int i = total + tid; i < dm.k; i += nt) out[i] = -1;
+    if (lists.n_ge) {
+        const int ne = min(wo_e[MAX_W], dm.k_e), nq = min(wo_q[MAX_W], dm.k_q);
+        for (int i = ne + tid; i < dm.k_e; i += nt) lists.ge_list[(int64_t)r * dm.k_e + i] = -1;
+        for (int i = nq + tid; i < dm.k_q; i += nt) lists.gq_list[(int64_t)r * dm.k_q + i] = -1;
+        if (tid == 0) {
+            lists.n_ge[r] = ne;
+            lists.n_gq[r] = nq;
+        }
+    }
     if (tid == 0) n_sel[r] = total;
     if (sw.slot_block && wave == 0) swap_row(dm, r, sb, s0, s1, res, fb, fs, fo, sw);
 }
@@ -578,7 +613,8 @@ hipError_t launch_score(const Dims &dm, const void *q, const float *kbar, int n_
 
 hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, int n_cand,
                          int n_prev, uint32_t *ge, uint32_t *ev, int32_t *sel, int32_t *n_sel,
-                         uint32_t *sel_bits, const SwapPtrs *swap, hipStream_t st) {
+                         uint32_t *sel_bits, const SwapPtrs *swap, const SelectLists *parts,
+                         hipStream_t st) {
     // LDS keys only when a budget is above what the register top-k holds
     int P = 0;
     if ((n_prev < 0 && dm.k_e > WAVE_TOPK) || dm.k_q > WAVE_TOPK) {
@@ -594,8 +630,10 @@ hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, i
         sw.n_fetch = swap->n_fetch;
         sw.counters = swap->counters;
     }
+    ListArgs li{};
+    if (parts) li = ListArgs{parts->ge_list, parts->n_ge, parts->gq_list, parts->n_gq};
     hipLaunchKernelGGL(select_kernel, dim3(dm.rows), dim3(SELECT_THREADS), P * sizeof(uint64_t),
-                       st, dm, s_q, e_blk, n_cand, n_prev, P, ge, ev, sel, n_sel, sel_bits, sw);
+                       st, dm, s_q, e_blk, n_cand, n_prev, P, ge, ev, sel, n_sel, sel_bits, sw, li);
     return hipGetLastError();
 }
 

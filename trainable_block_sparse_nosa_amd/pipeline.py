@@ -66,7 +66,7 @@ class DecodeLayer:
 
     def __init__(self, *, batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks, dtype,
                  kv, kv_row_blocks, e_tok, offload=False, decode_kernel=L.NOSA_DECODE_AUTO,
-                 scale=0.0, device="cuda", fuse_select_swap=True):
+                 scale=0.0, device="cuda", fuse_select_swap=True, overlap=False):
         self.shape = L.make_shape(batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks,
                                   dtype, decode_kernel=decode_kernel, scale=scale)
         self.rows = batch * n_kv_heads
@@ -101,6 +101,7 @@ class DecodeLayer:
         self.n_fetch = torch.zeros(R, dtype=i32, device=dev)
         self.counters = torch.zeros(R, 2, dtype=torch.int64, device=dev)
         self.ws_bytes = L.nosa_decode_workspace_size(self.shape)
+        self.chunks_all = L.nosa_decode_chunks(self.shape, self.k, 1)
         self.ws = torch.empty(self.ws_bytes // 4 + 4, dtype=f32, device=dev)
         self.out = torch.empty(batch, n_q_heads, head_dim, dtype=torch_dtype(dtype), device=dev)
         if offload:
@@ -111,6 +112,24 @@ class DecodeLayer:
             self.cur_fs = torch.zeros(R, k, dtype=i32, device=dev)
             self.cur_nf = torch.ones(R, dtype=i32, device=dev)
         self.fuse_select_swap = fuse_select_swap
+        # Overlap (KV in HBM): on a step that completes no block, attention over
+        # the eviction set (unchanged since the previous step) and the newest
+        # block runs on a side stream while the scores and the selection run on
+        # the caller's stream; the query-aware part follows the selection and a
+        # combine merges both.
+        self.overlap = overlap and not offload
+        if self.overlap:
+            ke, kq = max(k_e, 1), max(k_q, 1)
+            self.side = torch.cuda.Stream(device=dev)
+            self.ge_list = [torch.full((R, ke), -1, dtype=i32, device=dev) for _ in range(2)]
+            self.n_ge = [torch.zeros(R, dtype=i32, device=dev) for _ in range(2)]
+            self.gq_list = torch.full((R, kq), -1, dtype=i32, device=dev)
+            self.n_gq = torch.zeros(R, dtype=i32, device=dev)
+            self.chunks_e = L.nosa_decode_chunks(self.shape, k_e, 1)
+            self.chunks_q = L.nosa_decode_chunks(self.shape, k_q, 0)
+            self.step_done = torch.cuda.Event()
+            self.side_done = torch.cuda.Event()
+            self.parity = 0
         self.n_cand_prev = -1
         self.n_tokens = 0
         # optional callable(stage_name, fn, *args): runs fn(*args); a caller
@@ -119,6 +138,7 @@ class DecodeLayer:
 
     # -- helpers -------------------------------------------------------------
     def _run(self, name, fn, *args):
+        """Issue one ABI call; its last argument is the stream it runs on."""
         if self.stage_hook is None:
             fn(*args)
         else:
@@ -163,6 +183,11 @@ class DecodeLayer:
                           self.e_blk, stream)
             self.pooled = c
         st = L.make_step(n_tokens, self.n_cand_prev)
+        if self.overlap:
+            self._step_overlap(q, n_tokens, c, st, stream, swap)
+            self.n_cand_prev = c
+            self.n_tokens = n_tokens
+            return self.out
         self._run("score", L.nosa_score_blocks, self.shape, q, self.kbar, st, self.s_q, stream)
         if (swap or self.offload) and self.fuse_select_swap:
             self._run("select", L.nosa_select_swap, self.shape, self.s_q, self.e_blk, st,
@@ -180,16 +205,56 @@ class DecodeLayer:
             self._run("fetch", L.nosa_fetch_blocks, self.shape, self.kv, self.kv_row_blocks,
                       self.fetch_block, self.fetch_slot, self.n_fetch, self.k, self.cache, self.k,
                       stream)
-            self._run("decode", L.nosa_sparse_decode, self.shape, q, self.cache, self.k,
-                      L.NOSA_KV_CACHE, self.slot_block, None, self.cur, 1, st, self.e_tok,
-                      self.e_stride, self.out, self.ws, self.ws_bytes, stream)
+            self._run("decode", L.nosa_decode_partial, self.shape, q, self.cache, self.k,
+                      L.NOSA_KV_CACHE, self.slot_block, None, self.k, self.k, 1, self.cur, 1, st,
+                      self.e_tok, self.e_stride, self.ws, self.ws_bytes, 0, stream)
         else:
-            self._run("decode", L.nosa_sparse_decode, self.shape, q, self.kv, self.kv_row_blocks,
-                      L.NOSA_KV_FULL, self.sel, self.n_sel, self._kv_ptr(c), self.kv_row_blocks,
-                      st, self.e_tok, self.e_stride, self.out, self.ws, self.ws_bytes, stream)
+            self._run("decode", L.nosa_decode_partial, self.shape, q, self.kv, self.kv_row_blocks,
+                      L.NOSA_KV_FULL, self.sel, self.n_sel, self.k, self.k, 1, self._kv_ptr(c),
+                      self.kv_row_blocks, st, self.e_tok, self.e_stride, self.ws, self.ws_bytes, 0,
+                      stream)
+        self._run("combine", L.nosa_decode_combine, self.shape, self.chunks_all, self.out,
+                  self.ws, self.ws_bytes, stream)
         self.n_cand_prev = c
         self.n_tokens = n_tokens
         return self.out
+
+    def _step_overlap(self, q, n_tokens, c, st, stream, swap):
+        main = stream if stream is not None else torch.cuda.current_stream()
+        cur, prev = self.parity, self.parity ^ 1
+        k_e, k_q, rb = self.shape.k_e, self.shape.k_q, self.kv_row_blocks
+        # Gamma_e changes only when candidates arrive (or at the first step)
+        side = self.n_cand_prev >= 0 and c == self.n_cand_prev
+
+        def part_e(lst, n_lst, on):
+            self._run("decode_e", L.nosa_decode_partial, self.shape, q, self.kv, rb,
+                      L.NOSA_KV_FULL, lst, n_lst, max(k_e, 1), k_e, 1, self._kv_ptr(c), rb, st,
+                      self.e_tok, self.e_stride, self.ws, self.ws_bytes, 0, on)
+
+        if side:
+            # the previous step is complete: its lists are final, the workspace is free
+            self.side.wait_event(self.step_done)
+            part_e(self.ge_list[prev], self.n_ge[prev], self.side)
+            self.side_done.record(self.side)
+        self._run("score", L.nosa_score_blocks, self.shape, q, self.kbar, st, self.s_q, main)
+        cache = (self.slot_block, self.block_slot, self.fetch_block, self.fetch_slot,
+                 self.n_fetch, self.counters) if swap else (None,) * 6
+        self._run("select", L.nosa_select_parts, self.shape, self.s_q, self.e_blk, st,
+                  self.ge_bits, self.ev_bits, self.sel, self.n_sel, self.sel_bits,
+                  self.ge_list[cur], self.n_ge[cur], self.gq_list, self.n_gq, *cache, main)
+        if not side:
+            part_e(self.ge_list[cur], self.n_ge[cur], main)
+        if self.chunks_q:
+            self._run("decode_q", L.nosa_decode_partial, self.shape, q, self.kv, rb,
+                      L.NOSA_KV_FULL, self.gq_list, self.n_gq, max(k_q, 1), k_q, 0,
+                      self._kv_ptr(c), rb, st, self.e_tok, self.e_stride, self.ws, self.ws_bytes,
+                      self.chunks_e, main)
+        if side:
+            main.wait_event(self.side_done)
+        self._run("combine", L.nosa_decode_combine, self.shape, self.chunks_e + self.chunks_q,
+                  self.out, self.ws, self.ws_bytes, main)
+        self.step_done.record(main)
+        self.parity ^= 1
 
 
 def default_scale(head_dim: int) -> float:
