@@ -272,6 +272,10 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
         int bid, valid;
         if (e < e_end && resolve_entry<bf16_t>(a, e, cnt_e, r, BE, blk, bid, valid)) {
             load_block<D>(br, blk, er + (int64_t)bid * S, valid, col, grp);
+            // keep every load of the block ahead of the math: without this the
+            // scheduler interleaves loads with MFMAs to save registers and the
+            // block is no longer in flight at once
+            __builtin_amdgcn_sched_barrier(0);
             attend_block<D>(br, qop, dm.scale, grp, m_run, l_run, o);
         }
     }
