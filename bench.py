@@ -99,7 +99,8 @@ def cpu_baseline(w, seconds: float, steps_avail: int):
             K, V, e = rows[r]
             q = q_t[b, g * w.group:(g + 1) * w.group]
             t0 = time.perf_counter()
-            oracle.step_row(w.n_tokens(t), q, K, V, e, 64, 16, w.k_e, w.k_q, sc)
+            oracle.step_row(w.n_tokens(t), q, K, V, e, 64, 16, w.k_e, w.k_q, sc,
+                            pooled_bf16=w.dtype == "bf16")
             t_used += time.perf_counter() - t0
             done += 1
             if t_used >= seconds:
@@ -178,6 +179,57 @@ def setup(w, args, dev):
 ATTN_STAGES = ("decode", "decode_e", "decode_q")
 
 
+class HipTimingEvents:
+    """A pool of HIP timing events created with hipEventDisableSystemFence:
+    recording one does not write back and invalidate the caches, so bracketing
+    every timed launch costs the step little. Uses the HIP runtime that torch
+    has already loaded (the one libnosa.so resolves to as well)."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n: int):
+        import ctypes
+        import torch
+        torch.cuda.init()
+        path = None
+        with open("/proc/self/maps") as fh:
+            for line in fh:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self._c = ctypes
+        self.hip = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [P, P]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+        self.hip.hipEventDestroy.argtypes = [P]
+        self.events = []
+        for _ in range(n):
+            e = P()
+            self._chk(self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE))
+            self.events.append(e)
+
+    @staticmethod
+    def _chk(rc):
+        if rc != 0:
+            raise RuntimeError(f"HIP event call failed with error {rc}")
+
+    def record(self, i: int, stream_handle: int):
+        self._chk(self.hip.hipEventRecord(self.events[i], stream_handle))
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = self._c.c_float()
+        self._chk(self.hip.hipEventElapsedTime(self._c.byref(ms), self.events[i], self.events[j]))
+        return ms.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
 def timed_run(layer, w, q, args, stream, event_stages=ATTN_STAGES):
     """Warm up, then time exactly args.steps steps. HIP events, recorded on the
     stream each call runs on, bracket the listed stages in every timed step.
@@ -190,17 +242,17 @@ def timed_run(layer, w, q, args, stream, event_stages=ATTN_STAGES):
     fetched0 = int(layer.counters[:, 0].sum().item())
     pending = []
     cur = {"i": 0}
-    pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(3 * args.steps + 8)]
+    ev = HipTimingEvents(2 * (3 * args.steps + 8))
 
     def hook(name, fn, *a):
         if name in event_stages:
             on = a[-1] if a[-1] is not None else torch.cuda.current_stream()
-            e0, e1 = pool[len(pending)]
-            e0.record(on)
+            h = on.cuda_stream if hasattr(on, "cuda_stream") else int(on)
+            i0 = 2 * len(pending)
+            ev.record(i0, h)
             fn(*a)
-            e1.record(on)
-            pending.append((name, cur["i"], e0, e1))
+            ev.record(i0 + 1, h)
+            pending.append((name, cur["i"], i0, i0 + 1))
         else:
             fn(*a)
 
@@ -214,7 +266,9 @@ def timed_run(layer, w, q, args, stream, event_stages=ATTN_STAGES):
     elapsed = time.perf_counter() - t_start
     layer.stage_hook = None
     fetched = int(layer.counters[:, 0].sum().item()) - fetched0
-    return elapsed, [(n, i, a.elapsed_time(b)) for n, i, a, b in pending], fetched
+    times = [(n, i, ev.elapsed_ms(a, b)) for n, i, a, b in pending]
+    ev.close()
+    return elapsed, times, fetched
 
 
 def attn_bytes(w, stage: str, n_tokens: int, n_blocks: int) -> int:

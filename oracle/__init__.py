@@ -50,19 +50,24 @@ def lib():
     with _lock:
         if _lib is None:
             L = ctypes.CDLL(build())
-            L.oracle_pool_keys.argtypes = [_f, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _d]
+            L.oracle_round_bf16.argtypes = [ctypes.c_double]
+            L.oracle_round_bf16.restype = ctypes.c_double
+            L.oracle_pool_keys.argtypes = [_f, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, _d]
             L.oracle_pool_keys.restype = None
             L.oracle_block_evict.argtypes = [_f, ctypes.c_int, ctypes.c_int, ctypes.c_int]
             L.oracle_block_evict.restype = ctypes.c_double
             L.oracle_block_score.argtypes = [_f, ctypes.c_int, ctypes.c_int, _f, ctypes.c_int,
-                                             ctypes.c_int, ctypes.c_int, ctypes.c_double]
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                             ctypes.c_int]
             L.oracle_block_score.restype = ctypes.c_double
             L.oracle_topk.argtypes = [_d, _u8, ctypes.c_int, ctypes.c_int, _i]
             L.oracle_topk.restype = ctypes.c_int
             L.oracle_attend_tokens.argtypes = [_f, ctypes.c_int, ctypes.c_int, _f, _f, _f, _i,
                                                ctypes.c_int, ctypes.c_double, _d]
             L.oracle_attend_tokens.restype = None
-            L.oracle_step_row.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double, _f, _f, _f, _f,
+            L.oracle_step_row.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_int,
+                                                              _f, _f, _f, _f,
                                                               _i, _i, _i, _i, _d, _d, _d]
             L.oracle_step_row.restype = ctypes.c_int
             _lib = L
@@ -92,12 +97,18 @@ def _f32(a) -> np.ndarray:
 # single operations (for pins and for margin checks)
 # ---------------------------------------------------------------------------
 
-def pool_keys(K: np.ndarray, block: int, sub: int, j: int) -> np.ndarray:
-    """Sub-block means of block j's keys: [block // sub, D] fp64."""
+def round_bf16(x: float) -> float:
+    """x rounded to the nearest bfloat16 value, ties to even."""
+    return lib().oracle_round_bf16(float(x))
+
+
+def pool_keys(K: np.ndarray, block: int, sub: int, j: int, pooled_bf16: bool = False) -> np.ndarray:
+    """Sub-block means of block j's keys: [block // sub, D] fp64 (rounded to
+    the nearest bfloat16 when pooled_bf16)."""
     K = _f32(K)
     D = K.shape[1]
     out = np.zeros((block // sub, D), dtype=np.float64)
-    lib().oracle_pool_keys(_pf(K), D, block, sub, j, _pd(out))
+    lib().oracle_pool_keys(_pf(K), D, block, sub, j, int(pooled_bf16), _pd(out))
     return out
 
 
@@ -107,11 +118,12 @@ def block_evict(e: np.ndarray, block: int, sub: int, j: int) -> float:
     return lib().oracle_block_evict(_pf(e), block, sub, j)
 
 
-def block_score(q: np.ndarray, K: np.ndarray, block: int, sub: int, j: int, scale: float) -> float:
+def block_score(q: np.ndarray, K: np.ndarray, block: int, sub: int, j: int, scale: float,
+                pooled_bf16: bool = False) -> float:
     """Query-aware pooled score of block j for the query heads q [G, D]."""
     q, K = _f32(q), _f32(K)
     G, D = q.shape
-    return lib().oracle_block_score(_pf(q), G, D, _pf(K), block, sub, j, scale)
+    return lib().oracle_block_score(_pf(q), G, D, _pf(K), block, sub, j, scale, int(pooled_bf16))
 
 
 def topk(x, k: int, allowed=None) -> list[int]:
@@ -161,10 +173,11 @@ class RowStep:
 
 
 def step_row(n_tokens: int, q, K, V, e, block: int, sub: int, k_e: int, k_q: int,
-             scale: float) -> RowStep:
+             scale: float, pooled_bf16: bool = False) -> RowStep:
     """Selection and attention output of one row at one decode step.
 
-    q [G, D]; K, V [>= n_tokens, D]; e [>= n_tokens]. All fp64 inside.
+    q [G, D]; K, V [>= n_tokens, D]; e [>= n_tokens]. All fp64 inside;
+    pooled_bf16 keeps the pooled key means in bfloat16 (bfloat16 keys).
     """
     q, K, V, e = _f32(q), _f32(K), _f32(V), _f32(e)
     G, D = q.shape
@@ -176,7 +189,8 @@ def step_row(n_tokens: int, q, K, V, e, block: int, sub: int, k_e: int, k_q: int
     out = np.zeros((G, D), dtype=np.float64)
     E = np.zeros(max(c, 1), dtype=np.float64)
     S = np.zeros(max(c, 1), dtype=np.float64)
-    lib().oracle_step_row(n_tokens, G, D, block, sub, k_e, k_q, scale, _pf(q), _pf(K), _pf(V),
+    lib().oracle_step_row(n_tokens, G, D, block, sub, k_e, k_q, scale, int(pooled_bf16),
+                          _pf(q), _pf(K), _pf(V),
                           _pf(e), _pi(ge), _pi(nge), _pi(gq), _pi(ngq), _pd(out), _pd(E), _pd(S))
     return RowStep(c, [int(v) for v in ge[: nge[0]]], [int(v) for v in gq[: ngq[0]]], out,
                    E[:c].copy(), S[:c].copy())

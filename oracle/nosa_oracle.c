@@ -32,16 +32,44 @@
  * its per-head block scores; per-head max over sub-blocks comes before that
  * sum; scores are scaled by `scale` with no softmax; the newest block is
  * always attended and is not a candidate; equal scores rank the lower block
- * index first) are listed in the repository's design notes.
+ * index first; with bfloat16 keys the pooled sub-block means are kept in
+ * bfloat16, i.e. the exact mean rounded to the nearest bfloat16, ties to
+ * even, and the query-aware score is computed from those rounded means) are
+ * listed in the repository's design notes. The one rounding step, the
+ * pooled means with `pooled_bf16` set, is a quantisation of the stored
+ * pooled keys, not an arithmetic shortcut: the score is still computed in
+ * double from the quantised means.
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
+/* x rounded to the nearest bfloat16 value, ties to the even one. bfloat16
+   has 8 significant bits and float32's exponent range: in the binade
+   [2^(e-1), 2^e) its values are the multiples of 2^(e-8), and below the
+   smallest normal (2^-126) the multiples of 2^-133. Rounding is to the
+   nearest such multiple (rint: ties to even under the default rounding
+   mode). Results beyond the largest finite bfloat16 do not occur for means
+   of bfloat16 inputs. */
+double oracle_round_bf16(double x)
+{
+    if (x == 0.0 || !isfinite(x))
+        return x;
+    int e;
+    frexp(x, &e);
+    int q = e - 8;
+    if (q < -133)
+        q = -133;
+    double ulp = ldexp(1.0, q);
+    return rint(x / ulp) * ulp;
+}
+
 /* Sub-block mean of keys: kbar[i*D + d] = mean over the `sub` tokens of
-   sub-block i of block j of K[token][d]; K is [tokens][D] with row stride D. */
-void oracle_pool_keys(const float *K, int D, int block, int sub, int j, double *kbar)
+   sub-block i of block j of K[token][d]; K is [tokens][D] with row stride D.
+   pooled_bf16: the mean is then rounded to the nearest bfloat16. */
+void oracle_pool_keys(const float *K, int D, int block, int sub, int j, int pooled_bf16,
+                      double *kbar)
 {
     int m = block / sub;
     for (int i = 0; i < m; ++i) {
@@ -49,7 +77,8 @@ void oracle_pool_keys(const float *K, int D, int block, int sub, int j, double *
             double s = 0.0;
             for (int u = 0; u < sub; ++u)
                 s += (double)K[(int64_t)(j * block + i * sub + u) * D + d];
-            kbar[i * D + d] = s / (double)sub;
+            double mean = s / (double)sub;
+            kbar[i * D + d] = pooled_bf16 ? oracle_round_bf16(mean) : mean;
         }
     }
 }
@@ -74,11 +103,11 @@ double oracle_block_evict(const float *e, int block, int sub, int j)
 /* Query-aware pooled score of block j for a group of G query heads q[h][D]:
    sum over heads of (max over sub-blocks of scale * q_h . kbar_i). */
 double oracle_block_score(const float *q, int G, int D, const float *K, int block, int sub,
-                          int j, double scale)
+                          int j, double scale, int pooled_bf16)
 {
     int m = block / sub;
     double *kbar = (double *)malloc(sizeof(double) * (size_t)m * (size_t)D);
-    oracle_pool_keys(K, D, block, sub, j, kbar);
+    oracle_pool_keys(K, D, block, sub, j, pooled_bf16, kbar);
     double total = 0.0;
     for (int h = 0; h < G; ++h) {
         double best = -INFINITY;
@@ -176,9 +205,9 @@ void oracle_attend_tokens(const float *q, int G, int D, const float *K, const fl
  * candidate's pooled eviction and query-aware scores when not NULL.
  * Returns c. */
 int oracle_step_row(int n_tokens, int G, int D, int block, int sub, int k_e, int k_q,
-                    double scale, const float *q, const float *K, const float *V,
-                    const float *e, int *ge, int *n_ge, int *gq, int *n_gq, double *out,
-                    double *E, double *S)
+                    double scale, int pooled_bf16, const float *q, const float *K,
+                    const float *V, const float *e, int *ge, int *n_ge, int *gq, int *n_gq,
+                    double *out, double *E, double *S)
 {
     int c = (n_tokens - 1) / block;
     int cc = c > 0 ? c : 1;
@@ -188,7 +217,7 @@ int oracle_step_row(int n_tokens, int G, int D, int block, int sub, int k_e, int
 
     for (int j = 0; j < c; ++j) {
         Eb[j] = oracle_block_evict(e, block, sub, j);
-        Sb[j] = oracle_block_score(q, G, D, K, block, sub, j, scale);
+        Sb[j] = oracle_block_score(q, G, D, K, block, sub, j, scale, pooled_bf16);
     }
 
     /* Gamma_e: the k_e greatest candidates by pooled eviction score. */

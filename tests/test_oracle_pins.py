@@ -106,6 +106,55 @@ def test_pool_score_hand_case():
     np.testing.assert_array_equal(kbar[:, 1], a1)
 
 
+def test_round_bf16_matches_bit_rounding_of_float32():
+    """The oracle's bfloat16 rounding (nearest multiple of the bfloat16
+    spacing) against the bit-level round-half-to-even of float32 values."""
+    rng = np.random.default_rng(21)
+    x = (rng.normal(size=4000) * np.exp2(rng.integers(-140, 60, size=4000))).astype(np.float32)
+    # exact ties: float32 values whose dropped half-word is 0x8000
+    u = rng.integers(0, 2 ** 31, size=500, dtype=np.uint64).astype(np.uint32)
+    u = (u & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    x = np.concatenate([x, u.view(np.float32), -u.view(np.float32)])
+    x = x[np.isfinite(x)]
+    want = synth.rne_bf16(x)
+    got = np.array([oracle.round_bf16(float(v)) for v in x], dtype=np.float64)
+    np.testing.assert_array_equal(got, want.astype(np.float64))
+
+
+def test_round_bf16_of_doubles():
+    """Values that float32 cannot hold: a first rounding to float32 would turn
+    1 + 2^-8 + 2^-30 into the tie 1 + 2^-8 and round it down."""
+    r = oracle.round_bf16
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7
+    assert r(-(1.0 + 2.0 ** -8 + 2.0 ** -30)) == -(1.0 + 2.0 ** -7)
+    assert r(1.0 + 2.0 ** -8) == 1.0                      # tie, even mantissa below
+    assert r(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6      # tie, even mantissa above
+    assert r(1.0 + 2.0 ** -8 - 2.0 ** -40) == 1.0
+    assert r(2.0 ** -134) == 0.0                          # half the smallest subnormal
+    assert r(3 * 2.0 ** -134) == 2.0 ** -132              # tie between 1 and 2 spacings
+    assert r(255.5) == 256.0 and r(254.5) == 254.0        # spacing 1 below 256, 2 above
+    assert r(0.0) == 0.0
+
+
+def test_pool_keys_bf16_rounding_hand_case():
+    """Sub-block means of bfloat16 keys, kept in bfloat16: 1 and 1 + 2^-7 are
+    neighbours, so a mean of 1 + 2^-9 rounds down, 1 + 2^-8 is a tie (down to
+    the even 1) and 1 + 3 * 2^-9 rounds up."""
+    hi = 1.0 + 2.0 ** -7
+    K = np.ones((64, 1), np.float32)
+    K[0:4, 0] = hi          # sub-block 0: mean 1 + 2^-9
+    K[16:24, 0] = hi        # sub-block 1: mean 1 + 2^-8
+    K[32:44, 0] = hi        # sub-block 2: mean 1 + 3 * 2^-9
+    exact = oracle.pool_keys(K, 64, 16, 0)[:, 0]
+    np.testing.assert_array_equal(exact, [1 + 2.0 ** -9, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -9, 1.0])
+    kept = oracle.pool_keys(K, 64, 16, 0, pooled_bf16=True)[:, 0]
+    np.testing.assert_array_equal(kept, [1.0, 1.0, hi, 1.0])
+    q = np.ones((1, 1), np.float32)
+    assert oracle.block_score(q, K, 64, 16, 0, 1.0) == 1 + 3 * 2.0 ** -9
+    assert oracle.block_score(q, K, 64, 16, 0, 1.0, pooled_bf16=True) == hi
+    assert oracle.block_score(-q, K, 64, 16, 0, 1.0, pooled_bf16=True) == -1.0
+
+
 def test_pool_reduces_to_mean_when_sub_block_is_block():
     rng = np.random.default_rng(11)
     K = rng.normal(size=(256, 16)).astype(np.float32)
