@@ -61,8 +61,12 @@
  *            pre-exponential. nosa_sparse_decode reads them a block at a
  *            time: e_tok is 16-byte aligned, e_row_stride a multiple of 4 and
  *            at least S * (n_cand + 1) (values past n_tokens are ignored).
- * kbar       float32 [rows][D/4][m*max_blocks][4], m = S / sub_block: the
- *            mean key of sub-block i of block j is at [.][d/4][m*j+i][d%4].
+ * kbar       pooled keys in the KV dtype, V = 16 / element size dimensions
+ *            per 16-byte vector (4 for float32, 8 for bfloat16):
+ *            [rows][D/V][m*max_blocks][V], m = S / sub_block; the mean key of
+ *            sub-block i of block j is at [.][d/V][m*j+i][d%V]. bfloat16
+ *            means are the exact mean rounded once to the nearest bfloat16
+ *            (ties to even); float32 means are a float32 sum times 1/16.
  * e_blk      float32 [rows][max_blocks]: pooled eviction score per block.
  * s_q        float32 [rows][max_blocks]: query-aware score per block.
  * bitmaps    uint32 [rows][W], W = (max_blocks + 31) / 32; bit j%32 of word
@@ -127,7 +131,7 @@ typedef struct nosa_step {
 } nosa_step;
 
 /* Pool blocks [blk_begin, blk_end) of every row: kbar gets each sub-block's
- * mean key (float32 sum, then times 1/sub_block), e_blk the max over the
+ * mean key in the KV dtype (layout and rounding above), e_blk the max over the
  * block's sub-blocks of the mean per-token eviction score (Methodology,
  * "Block-Wise Implementation": mean inside sub-blocks, then max over the
  * block). Block j of row r is read from the KV buffer `kv` at block index
@@ -136,14 +140,14 @@ typedef struct nosa_step {
  * kv may be a device pointer or the device alias of pinned host memory. */
 nosa_status nosa_pool_blocks(const nosa_shape *shape, const void *kv, int64_t kv_row_blocks,
                              int32_t kv_first_block, const float *e_tok, int64_t e_row_stride,
-                             int32_t blk_begin, int32_t blk_end, float *kbar, float *e_blk,
+                             int32_t blk_begin, int32_t blk_end, void *kbar, float *e_blk,
                              void *stream);
 
 /* Query-aware block scores for candidates 0 .. n_cand-1 of every row:
  * s_q[r][j] = sum over the G heads of the row of max over sub-blocks i of
  * scale * q_h . kbar[j,i] (Methodology, "Dual-Selection Mechanism" and
  * "Block-Wise Implementation"). Entries j >= n_cand are left untouched. */
-nosa_status nosa_score_blocks(const nosa_shape *shape, const void *q, const float *kbar,
+nosa_status nosa_score_blocks(const nosa_shape *shape, const void *q, const void *kbar,
                               const nosa_step *step, float *s_q, void *stream);
 
 /* Dual selection for every row (Methodology, "Dual-Selection Mechanism",

@@ -60,6 +60,37 @@ def _compare_step(w, tr, t, r, got, check_swap=True, check_slots=True):
     np.testing.assert_allclose(out, ref.out, err_msg=where, **TOL[w.dtype])
 
 
+@pytest.mark.parametrize("name", ["small_f32", "small_bf16", "small_offload"])
+def test_pooled_keys(name):
+    """Pooled sub-block means after the prefill pooling and the steps that
+    complete further blocks: bfloat16 means bit-exact against the oracle's
+    exact mean rounded to bfloat16, float32 means within float32 summation
+    error."""
+    import oracle
+    from harness import row_kv
+    gh = _gpu()
+    w = synth.WORKLOADS[name]
+    inp = gh.upload(w)
+    steps = 72 if w.steps >= 72 else w.steps
+    layer, _ = gh.run(w, inp, list(range(steps)))
+    c = w.n_cand(steps - 1)
+    assert c > w.n_cand(0), "the steps complete at least one block"
+    D = w.head_dim
+    kb = layer.kbar.float().cpu().numpy()          # [rows][D/V][4*max_blocks][V]
+    kb = kb.transpose(0, 2, 1, 3).reshape(w.rows, -1, D)
+    for r in range(w.rows):
+        b, g = divmod(r, w.n_kv_heads)
+        K, _ = row_kv(w, 0, b, g)
+        for j in range(c):
+            ref = oracle.pool_keys(K, w.block, w.sub_block, j, pooled_bf16=w.dtype == "bf16")
+            got = kb[r, 4 * j:4 * j + 4].astype(np.float64)
+            where = f"{name} row={r} block={j}"
+            if w.dtype == "bf16":
+                np.testing.assert_array_equal(got, ref, err_msg=where)
+            else:
+                np.testing.assert_allclose(got, ref, rtol=0, atol=2e-6, err_msg=where)
+
+
 @pytest.mark.parametrize("name", ["tiny_f32", "small_f32", "small_bf16", "small_offload"])
 def test_parity_all_steps_all_rows(name):
     gh = _gpu()

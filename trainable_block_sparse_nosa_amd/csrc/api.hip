@@ -165,7 +165,7 @@ extern "C" {
 
 nosa_status nosa_pool_blocks(const nosa_shape *shape, const void *kv, int64_t kv_row_blocks,
                              int32_t kv_first_block, const float *e_tok, int64_t e_row_stride,
-                             int32_t blk_begin, int32_t blk_end, float *kbar, float *e_blk,
+                             int32_t blk_begin, int32_t blk_end, void *kbar, float *e_blk,
                              void *stream) {
     Dims dm;
     nosa_status s = make_dims(shape, &dm);
@@ -184,7 +184,7 @@ nosa_status nosa_pool_blocks(const nosa_shape *shape, const void *kv, int64_t kv
     });
 }
 
-nosa_status nosa_score_blocks(const nosa_shape *shape, const void *q, const float *kbar,
+nosa_status nosa_score_blocks(const nosa_shape *shape, const void *q, const void *kbar,
                               const nosa_step *step, float *s_q, void *stream) {
     Dims dm;
     nosa_status s = make_dims(shape, &dm);

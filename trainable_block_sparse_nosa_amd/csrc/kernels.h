@@ -8,10 +8,10 @@ namespace nosa {
 template <typename T, int D>
 hipError_t launch_pool(const Dims &dm, const void *kv, int64_t kv_row_blocks, int kv_first,
                        const float *e_tok, int64_t e_stride, int blk_begin, int blk_end,
-                       float *kbar, float *e_blk, hipStream_t st);
+                       void *kbar, float *e_blk, hipStream_t st);
 
 template <typename T, int D, int G>
-hipError_t launch_score(const Dims &dm, const void *q, const float *kbar, int n_cand, float *s_q,
+hipError_t launch_score(const Dims &dm, const void *q, const void *kbar, int n_cand, float *s_q,
                         hipStream_t st);
 
 struct SwapPtrs {

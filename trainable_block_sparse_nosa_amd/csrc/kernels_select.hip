@@ -9,27 +9,82 @@
 namespace nosa {
 
 // ---------------------------------------------------------------------------
+// Pooled keys are stored in the KV dtype T, V = 16 / sizeof(T) dimensions per
+// 16-byte vector: kbar[row][D/V][m * max_blocks][V] (dimension vectors
+// outermost, so a wave whose lanes hold consecutive sub-blocks reads 1 KiB
+// contiguous per load).
+// ---------------------------------------------------------------------------
+template <typename T> struct KbarVec;
+template <> struct KbarVec<float> {
+    static constexpr int V = 4;
+    __device__ __forceinline__ static void load(const float *p, float (&x)[4]) {
+        const float4 v = *reinterpret_cast<const float4 *>(p);
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    }
+};
+template <> struct KbarVec<bf16_t> {
+    static constexpr int V = 8;
+    __device__ __forceinline__ static void load(const bf16_t *p, float (&x)[8]) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(p);
+        x[0] = bf_lo(v.x); x[1] = bf_hi(v.x); x[2] = bf_lo(v.y); x[3] = bf_hi(v.y);
+        x[4] = bf_lo(v.z); x[5] = bf_hi(v.z); x[6] = bf_lo(v.w); x[7] = bf_hi(v.w);
+    }
+};
+
+// x (double) rounded to the nearest bfloat16, ties to even, with one
+// rounding: x is first rounded to float32 by rounding to odd (truncate, then
+// set the last bit if anything was dropped), which float32's 16 extra bits
+// make innocuous for the final round-to-nearest-even (Boldo and Melquiond,
+// "Emulation of FMA and correctly rounded sums: proved algorithms using
+// rounding to odd", IEEE Trans. Computers 57(4), 2008).
+__device__ __forceinline__ bf16_t bf16_rne_from_double(double x) {
+    float f = (float)x;
+    if ((double)f != x) {
+        uint32_t u = __float_as_uint(f);
+        if (fabs((double)f) > fabs(x)) u -= 1u;  // rounded away from zero: step back
+        f = __uint_as_float(u | 1u);
+    }
+    return f2bf(f);
+}
+
+// Sub-block mean of 16 keys in the storage type: float32 keys sum in float32;
+// bfloat16 keys sum exactly in double (16 values with 8 significant bits) and
+// the exact mean is rounded once to bfloat16.
+template <typename T> __device__ __forceinline__ T pooled_mean(const T *k, int stride);
+template <> __device__ __forceinline__ float pooled_mean<float>(const float *k, int stride) {
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s += k[u * stride];
+    return s * (1.0f / 16);
+}
+template <> __device__ __forceinline__ bf16_t pooled_mean<bf16_t>(const bf16_t *k, int stride) {
+    double s = 0.0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s += (double)bf2f(k[u * stride]);
+    return bf16_rne_from_double(s * (1.0 / 16));
+}
+
+// ---------------------------------------------------------------------------
 // Pool: one workgroup per (block, row). Sub-block means of the keys go to the
-// dim-quad-major kbar layout; the eviction scores get mean-then-max pooling.
+// kbar layout above; the eviction scores get mean-then-max pooling.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 pool_kernel(Dims dm, const T *__restrict__ kv, int64_t kv_row_blocks, int kv_first,
             const float *__restrict__ e_tok, int64_t e_stride, int blk_begin,
-            float *__restrict__ kbar, float *__restrict__ e_blk) {
-    constexpr int S = 64, SUB = 16, M = S / SUB;
+            T *__restrict__ kbar, float *__restrict__ e_blk) {
+    constexpr int S = 64, SUB = 16, M = S / SUB, V = KbarVec<T>::V;
+    static_assert(SUB == 16, "pooled_mean sums 16 tokens");
     __shared__ float emean[M];
     const int r = blockIdx.y;
     const int j = blk_begin + blockIdx.x;
     const T *K = kv + ((int64_t)r * kv_row_blocks + kv_first + blockIdx.x) * (int64_t)(2 * S * D);
-    const int64_t ld_sb = (int64_t)M * dm.max_blocks;  // sub-blocks per dim-quad plane
-    float *kb = kbar + (int64_t)r * (D / 4) * ld_sb * 4;
+    const int64_t ld_sb = (int64_t)M * dm.max_blocks;  // sub-blocks per dimension-vector plane
+    T *kb = kbar + (int64_t)r * D * ld_sb;
     for (int p = threadIdx.x; p < M * D; p += blockDim.x) {
         const int i = p / D, d = p % D;
-        float s = 0.f;
-#pragma unroll
-        for (int u = 0; u < SUB; ++u) s += ldf(K + (i * SUB + u) * D + d);
-        kb[((int64_t)(d / 4) * ld_sb + (int64_t)(M * j + i)) * 4 + (d % 4)] = s * (1.0f / SUB);
+        kb[((int64_t)(d / V) * ld_sb + (int64_t)(M * j + i)) * V + (d % V)] =
+            pooled_mean<T>(K + (i * SUB) * D + d, D);
     }
     if (threadIdx.x < M) {
         const float *e = e_tok + (int64_t)r * e_stride + (int64_t)j * S + threadIdx.x * SUB;
@@ -48,43 +103,40 @@ pool_kernel(Dims dm, const T *__restrict__ kv, int64_t kv_row_blocks, int kv_fir
 }
 
 // ---------------------------------------------------------------------------
-// Score: lane <-> sub-block. Each lane walks the head dimension four floats
-// at a time; a wave's loads cover 64 consecutive sub-blocks (1 KiB). The
-// group's G dot products stay in registers; the block max over the 4
+// Score: lane <-> sub-block. Each lane walks the head dimension one 16-byte
+// vector at a time; a wave's loads cover 64 consecutive sub-blocks (1 KiB).
+// The group's G dot products stay in registers; the block max over the 4
 // sub-blocks is a DPP quad reduction, then the heads are summed.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256)
-score_kernel(Dims dm, const T *__restrict__ q, const float *__restrict__ kbar, int n_cand,
+score_kernel(Dims dm, const T *__restrict__ q, const T *__restrict__ kbar, int n_cand,
              float *__restrict__ s_q) {
-    constexpr int M = 4;
-    __shared__ float4 qs[G][D / 4];
+    constexpr int M = 4, V = KbarVec<T>::V;
+    __shared__ float qs[G][D];
     const int r = blockIdx.y;
     const int b = r / dm.Hkv, g = r % dm.Hkv;
     const T *qr = q + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
     for (int p = threadIdx.x; p < G * D; p += blockDim.x)
-        reinterpret_cast<float *>(qs)[p] = ldf(qr + p) * dm.scale;
+        (&qs[0][0])[p] = ldf(qr + p) * dm.scale;
     __syncthreads();
 
     const int nsb = M * n_cand;
     const int sb = blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t ld_sb = (int64_t)M * dm.max_blocks;
-    const float4 *kb = reinterpret_cast<const float4 *>(kbar) + (int64_t)r * (D / 4) * ld_sb;
+    const T *kb = kbar + (int64_t)r * D * ld_sb;
     float acc[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) acc[h] = 0.f;
     if (sb < nsb) {
 #pragma unroll 8
-        for (int dq = 0; dq < D / 4; ++dq) {
-            const float4 v = kb[(int64_t)dq * ld_sb + sb];
+        for (int dv = 0; dv < D / V; ++dv) {
+            float x[V];
+            KbarVec<T>::load(kb + ((int64_t)dv * ld_sb + sb) * V, x);
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float4 w = qs[h][dq];
-                acc[h] = fmaf(w.x, v.x, acc[h]);
-                acc[h] = fmaf(w.y, v.y, acc[h]);
-                acc[h] = fmaf(w.z, v.z, acc[h]);
-                acc[h] = fmaf(w.w, v.w, acc[h]);
-            }
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int u = 0; u < V; ++u) acc[h] = fmaf(qs[h][dv * V + u], x[u], acc[h]);
         }
     }
     // every lane takes part in the quad reductions (n_cand*4 keeps quads whole)
@@ -594,20 +646,20 @@ fetch_kernel(const u32x4 *__restrict__ src, int64_t src_row_blocks, const int32_
 template <typename T, int D>
 hipError_t launch_pool(const Dims &dm, const void *kv, int64_t kv_row_blocks, int kv_first,
                        const float *e_tok, int64_t e_stride, int blk_begin, int blk_end,
-                       float *kbar, float *e_blk, hipStream_t st) {
+                       void *kbar, float *e_blk, hipStream_t st) {
     dim3 grid(blk_end - blk_begin, dm.rows);
     hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(256), 0, st, dm,
                        static_cast<const T *>(kv), kv_row_blocks, kv_first, e_tok, e_stride,
-                       blk_begin, kbar, e_blk);
+                       blk_begin, static_cast<T *>(kbar), e_blk);
     return hipGetLastError();
 }
 
 template <typename T, int D, int G>
-hipError_t launch_score(const Dims &dm, const void *q, const float *kbar, int n_cand, float *s_q,
+hipError_t launch_score(const Dims &dm, const void *q, const void *kbar, int n_cand, float *s_q,
                         hipStream_t st) {
     dim3 grid((4 * n_cand + 255) / 256, dm.rows);
     hipLaunchKernelGGL((score_kernel<T, D, G>), grid, dim3(256), 0, st, dm,
-                       static_cast<const T *>(q), kbar, n_cand, s_q);
+                       static_cast<const T *>(q), static_cast<const T *>(kbar), n_cand, s_q);
     return hipGetLastError();
 }
 
@@ -661,7 +713,7 @@ hipError_t launch_fetch(const Dims &dm, const void *src, int64_t src_row_blocks,
 
 #define NOSA_POOL_INST(T, D)                                                                   \
     template hipError_t launch_pool<T, D>(const Dims &, const void *, int64_t, int,            \
-                                          const float *, int64_t, int, int, float *, float *,  \
+                                          const float *, int64_t, int, int, void *, float *,   \
                                           hipStream_t);
 NOSA_POOL_INST(float, 64)
 NOSA_POOL_INST(float, 128)
@@ -669,7 +721,7 @@ NOSA_POOL_INST(bf16_t, 64)
 NOSA_POOL_INST(bf16_t, 128)
 
 #define NOSA_SCORE_INST(T, D, G)                                                               \
-    template hipError_t launch_score<T, D, G>(const Dims &, const void *, const float *, int,  \
+    template hipError_t launch_score<T, D, G>(const Dims &, const void *, const void *, int,   \
                                               float *, hipStream_t);
 #define NOSA_SCORE_ALLG(T, D)                                                                  \
     NOSA_SCORE_INST(T, D, 1) NOSA_SCORE_INST(T, D, 2) NOSA_SCORE_INST(T, D, 3)                 \

@@ -86,7 +86,10 @@ class DecodeLayer:
         dev = torch.device(device)
         R, k, W = self.rows, self.k, self.W
         f32, i32 = torch.float32, torch.int32
-        self.kbar = torch.zeros(R, head_dim // 4, 4 * max_blocks, 4, dtype=f32, device=dev)
+        # pooled keys in the KV dtype, 16-byte vectors of V dimensions
+        V = 16 // (4 if dtype == L.NOSA_F32 else 2)
+        self.kbar = torch.zeros(R, head_dim // V, 4 * max_blocks, V,
+                                dtype=f32 if dtype == L.NOSA_F32 else torch.bfloat16, device=dev)
         self.e_blk = torch.zeros(R, max_blocks, dtype=f32, device=dev)
         self.s_q = torch.zeros(R, max_blocks, dtype=f32, device=dev)
         self.ge_bits = torch.zeros(R, W, dtype=i32, device=dev)
