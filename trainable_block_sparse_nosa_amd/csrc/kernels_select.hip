@@ -326,7 +326,7 @@ struct ListArgs {
 // Fetch list = selected and not cached, ascending; free slots = empty or
 // holding an unselected block, ascending; fetched block i goes to free slot
 // i, leftover free slots become empty. Every output address is written once.
-__device__ void swap_row(const Dims &dm, int r, const uint32_t *bits, int s0, int s1,
+__device__ void swap_row(const Dims &dm, int r, const uint32_t *bits, int s0, int s1, uint64_t cnt,
                          uint32_t *res, int *fb, int *fs, int *fo, const SwapArgs &sw) {
     const int lane = threadIdx.x & 63, k = dm.k, W = dm.W;
     const uint64_t lt = lanemask_lt();
@@ -394,10 +394,12 @@ __device__ void swap_row(const Dims &dm, int r, const uint32_t *bits, int s0, in
         fbo[i] = i < nf ? fb[i] : -1;
         fso[i] = i < nf ? fs[i] : -1;
     }
+    // cnt: lane 0 holds the running fetch count, lane 1 the running kept count
     if (lane == 0) {
         sw.n_fetch[r] = nf;
-        sw.counters[2 * r] += (uint64_t)nf;
-        sw.counters[2 * r + 1] += (uint64_t)kept;
+        sw.counters[2 * r] = cnt + (uint64_t)nf;
+    } else if (lane == 1) {
+        sw.counters[2 * r + 1] = cnt + (uint64_t)kept;
     }
 }
 
@@ -431,9 +433,11 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
         sv[i] = j < n_cand ? Sq[j] : 0.f;
     }
     int s0 = -1, s1 = -1;
+    uint64_t cnt = 0ull;
     if (sw.slot_block && wave == 0) {
         if (lane < dm.k) s0 = sw.slot_block[(int64_t)r * dm.k + lane];
         if (lane + 64 < dm.k) s1 = sw.slot_block[(int64_t)r * dm.k + lane + 64];
+        if (lane < 2) cnt = sw.counters[2 * r + lane];
     }
 
     // ---- Gamma_e ----
@@ -596,7 +600,7 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
         }
     }
     if (tid == 0) n_sel[r] = total;
-    if (sw.slot_block && wave == 0) swap_row(dm, r, sb, s0, s1, res, fb, fs, fo, sw);
+    if (sw.slot_block && wave == 0) swap_row(dm, r, sb, s0, s1, cnt, res, fb, fs, fo, sw);
 }
 
 // Stand-alone set difference: one wave per row, selection bitmap and slot
@@ -608,7 +612,8 @@ swap_kernel(Dims dm, const uint32_t *__restrict__ sel_bits, SwapArgs sw) {
     const int r = blockIdx.x, lane = threadIdx.x;
     const int s0 = lane < dm.k ? sw.slot_block[(int64_t)r * dm.k + lane] : -1;
     const int s1 = lane + 64 < dm.k ? sw.slot_block[(int64_t)r * dm.k + lane + 64] : -1;
-    swap_row(dm, r, sel_bits + (int64_t)r * dm.W, s0, s1, res, fb, fs, fo, sw);
+    const uint64_t cnt = lane < 2 ? sw.counters[2 * r + lane] : 0ull;
+    swap_row(dm, r, sel_bits + (int64_t)r * dm.W, s0, s1, cnt, res, fb, fs, fo, sw);
 }
 
 // ---------------------------------------------------------------------------
