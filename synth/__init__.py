@@ -204,7 +204,8 @@ def evict_row(w: Workload, layer: int, b: int, g: int, ov: Overrides | None = No
     """Per-token eviction logits of row (b, g): [n_max] float32 ~ N(0, 1)."""
     e = stream(w.seed, "E", layer, b, g).standard_normal(w.n_max, dtype=np.float32)
     if ov is not None:
-        for (l, bb, gg, j), a in ov.evict.items():
+        # a snapshot: other threads may add overrides for their own rows
+        for (l, bb, gg, j), a in list(ov.evict.items()):
             if (l, bb, gg) == (layer, b, g) and a > 0:
                 lo, hi = j * w.block, min((j + 1) * w.block, w.n_max)
                 e[lo:hi] = stream(w.seed, "E", layer, b, g, j, a).standard_normal(
@@ -221,7 +222,7 @@ def queries_step(w: Workload, layer: int, t: int, ov: Overrides | None = None) -
         (w.batch, w.n_q_heads, w.head_dim), dtype=np.float32)
     if ov is not None:
         G = w.group
-        for (l, tt, b, g), a in ov.query.items():
+        for (l, tt, b, g), a in list(ov.query.items()):
             if (l, tt) == (layer, t) and a > 0:
                 z[b, g * G:(g + 1) * G] = stream(w.seed, "Q", layer, t, b, g, a).standard_normal(
                     (G, w.head_dim), dtype=np.float32)

@@ -154,6 +154,10 @@ __device__ __forceinline__ void load_block(BlockRegs<D> &br, const bf16_t *blk, 
     constexpr int S = 64, KS = D / 32, DT = D / 16;
     const bf16_t *Kt = blk;          // [64][D]
     const bf16_t *Vt = blk + S * D;  // [D][64], token order vt_token_at
+    // eviction scores first: the QK^T MFMAs and the softmax then wait only for
+    // the K loads (waits are in issue order), not for V as well
+#pragma unroll
+    for (int t = 0; t < 4; ++t) br.e[t] = *reinterpret_cast<const f32x4 *>(eb + 16 * t + 4 * grp);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -164,8 +168,6 @@ __device__ __forceinline__ void load_block(BlockRegs<D> &br, const bf16_t *blk, 
 #pragma unroll
         for (int s = 0; s < 2; ++s)
             br.v[dt][s] = *reinterpret_cast<const bf16x8 *>(Vt + (16 * dt + col) * S + 32 * s + 8 * grp);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) br.e[t] = *reinterpret_cast<const f32x4 *>(eb + 16 * t + 4 * grp);
     br.valid = valid;
 }
 
