@@ -62,9 +62,10 @@
  *            time: e_tok is 16-byte aligned, e_row_stride a multiple of 4 and
  *            at least S * (n_cand + 1) (values past n_tokens are ignored).
  * kbar       pooled keys in the KV dtype, V = 16 / element size dimensions
- *            per 16-byte vector (4 for float32, 8 for bfloat16):
- *            [rows][D/V][m*max_blocks][V], m = S / sub_block; the mean key of
- *            sub-block i of block j is at [.][d/V][m*j+i][d%V]. bfloat16
+ *            per 16-byte vector (4 for float32, 8 for bfloat16), in quads of
+ *            4 blocks: [rows][Q][D/V][16][V], Q = ceil(max_blocks / 4); the
+ *            mean key of sub-block i of block j (sb = 4*j + i) is at
+ *            [.][sb/16][d/V][sb%16][d%V]. bfloat16
  *            means are the exact mean rounded once to the nearest bfloat16
  *            (ties to even); float32 means are a float32 sum times 1/16.
  * e_blk      float32 [rows][max_blocks]: pooled eviction score per block.
@@ -186,6 +187,20 @@ nosa_status nosa_select_swap(const nosa_shape *shape, const float *s_q, const fl
                              int32_t *slot_block, int32_t *block_slot, int32_t *fetch_block,
                              int32_t *fetch_slot, int32_t *n_fetch, uint64_t *counters,
                              void *stream);
+
+/* nosa_score_blocks and nosa_select (and, when the six cache pointers are
+ * given, the set difference as in nosa_select_swap) in one launch: one
+ * workgroup per row computes the row's query-aware scores into on-chip memory
+ * and selects from them, with no round trip of the scores through memory
+ * between two launches. s_q still receives the scores. Outputs and state
+ * updates are those of the separate calls. The cache pointers are all NULL
+ * or all non-NULL. */
+nosa_status nosa_score_select(const nosa_shape *shape, const void *q, const void *kbar,
+                              const float *e_blk, const nosa_step *step, float *s_q,
+                              uint32_t *ge_bits, uint32_t *ev_bits, int32_t *sel, int32_t *n_sel,
+                              uint32_t *sel_bits, int32_t *slot_block, int32_t *block_slot,
+                              int32_t *fetch_block, int32_t *fetch_slot, int32_t *n_fetch,
+                              uint64_t *counters, void *stream);
 
 /* nosa_select (and, when the six cache pointers are given, the set
  * difference as in nosa_select_swap) that also writes the two parts of the

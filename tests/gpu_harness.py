@@ -117,12 +117,13 @@ def upload_layer(w: Workload, layer: int, kv, ov: Overrides | None, steps: int,
 
 
 def make_layer(w: Workload, inp: GpuInputs, decode_kernel=L.NOSA_DECODE_AUTO,
-               fuse_select_swap=True, overlap=False) -> DecodeLayer:
+               fuse_select_swap=True, overlap=False, fuse_score=None) -> DecodeLayer:
     return DecodeLayer(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
                        head_dim=w.head_dim, k_e=w.k_e, k_q=w.k_q, max_blocks=inp.nb,
                        dtype=nosa_dtype(w), kv=inp.kv_ptr, kv_row_blocks=inp.nb,
                        e_tok=inp.e_tok, offload=w.offload, decode_kernel=decode_kernel,
-                       fuse_select_swap=fuse_select_swap, overlap=overlap)
+                       fuse_select_swap=fuse_select_swap, fuse_score=fuse_score,
+                       overlap=overlap)
 
 
 def bits_to_list(words: np.ndarray) -> list:
@@ -152,9 +153,9 @@ def snapshot(layer: DecodeLayer, w: Workload) -> dict:
 
 def run(w: Workload, inp: GpuInputs, steps, layer: DecodeLayer | None = None,
         collect=None, swap=True, decode_kernel=L.NOSA_DECODE_AUTO, fuse_select_swap=True,
-        overlap=False):
+        overlap=False, fuse_score=None):
     """Run steps 0..max(steps) in order; snapshot the steps listed in ``collect``."""
-    layer = layer or make_layer(w, inp, decode_kernel, fuse_select_swap, overlap)
+    layer = layer or make_layer(w, inp, decode_kernel, fuse_select_swap, overlap, fuse_score)
     T = max(steps) + 1
     collect = set(steps if collect is None else collect)
     layer.start(w.n_tokens(0))

@@ -86,6 +86,13 @@ def test_invalid_pointers_and_steps_rejected():
     assert lib.nosa_score_blocks(ctypes.byref(sh), None, 16, ctypes.byref(ok_step), 16, None) == 1
     assert lib.nosa_select(ctypes.byref(sh), 16, 16, ctypes.byref(ok_step), None, 16, 16, 16, 16,
                            None) == 1
+    # fused score + select: null inputs, cache pointers given only in part
+    P = [16] * 12
+    assert lib.nosa_score_select(ctypes.byref(sh), None, 16, 16, ctypes.byref(ok_step), *P,
+                                 None) == 1
+    part = [16] * 6 + [16, 16, 16, None, 16, 16]
+    assert lib.nosa_score_select(ctypes.byref(sh), 16, 16, 16, ctypes.byref(ok_step), *part,
+                                 None) == 1
     # a step beyond the block capacity
     big = L.make_step(64 * 64 + 1, -1)
     assert lib.nosa_score_blocks(ctypes.byref(sh), 16, 16, ctypes.byref(big), 16, None) == 1

@@ -76,8 +76,8 @@ def test_pooled_keys(name):
     c = w.n_cand(steps - 1)
     assert c > w.n_cand(0), "the steps complete at least one block"
     D = w.head_dim
-    kb = layer.kbar.float().cpu().numpy()          # [rows][D/V][4*max_blocks][V]
-    kb = kb.transpose(0, 2, 1, 3).reshape(w.rows, -1, D)
+    kb = layer.kbar.float().cpu().numpy()          # [rows][quads][D/V][16][V]
+    kb = kb.transpose(0, 1, 3, 2, 4).reshape(w.rows, -1, D)  # [rows][sub-block][D]
     for r in range(w.rows):
         b, g = divmod(r, w.n_kv_heads)
         K, _ = row_kv(w, 0, b, g)
@@ -117,9 +117,37 @@ def test_parity_valu_kernel_bf16(name):
             _compare_step(w, tr, t, r, res[t])
 
 
+@pytest.mark.parametrize("name", ["small_bf16", "small_offload"])
+def test_parity_separate_score_kernel(name):
+    """nosa_score_blocks then nosa_select_swap as two launches (the pipeline
+    scores and selects in one launch, nosa_score_select)."""
+    gh = _gpu()
+    w = synth.WORKLOADS[name]
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov)
+    _, res = gh.run(w, inp, list(range(w.steps)), fuse_score=False)
+    for t in range(w.steps):
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, res[t])
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "small_f32"])
+def test_parity_fused_score_select_f32(name):
+    """nosa_score_select on float32 inputs (its VALU scoring; the pipeline
+    fuses by default only for bf16, where the scores run on MFMA)."""
+    gh = _gpu()
+    w = synth.WORKLOADS[name]
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov)
+    _, res = gh.run(w, inp, list(range(w.steps)), fuse_score=True)
+    for t in range(w.steps):
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, res[t])
+
+
 @pytest.mark.parametrize("name", ["small_f32", "small_offload"])
 def test_parity_separate_select_and_swap(name):
-    """nosa_select then nosa_swap_diff as two calls (the pipeline fuses them)."""
+    """nosa_score_blocks, nosa_select, then nosa_swap_diff as three calls."""
     gh = _gpu()
     w = synth.WORKLOADS[name]
     tr = oracle_trace(w)

@@ -30,7 +30,7 @@ NOSA_DECODE_MFMA = 2
 
 EXPORTS = (
     "nosa_pool_blocks", "nosa_score_blocks", "nosa_select", "nosa_select_swap", "nosa_swap_diff",
-    "nosa_select_parts", "nosa_fetch_blocks", "nosa_decode_workspace_size", "nosa_decode_chunks",
+    "nosa_select_parts", "nosa_score_select", "nosa_fetch_blocks", "nosa_decode_workspace_size", "nosa_decode_chunks",
     "nosa_sparse_decode", "nosa_decode_partial", "nosa_decode_combine",
     "nosa_host_alloc", "nosa_host_free", "nosa_status_string", "nosa_last_error",
     "nosa_version",
@@ -57,7 +57,7 @@ class nosa_step(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m trainable_block_sparse_nosa_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python trainable_block_sparse_nosa_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     SH, ST = ctypes.POINTER(nosa_shape), ctypes.POINTER(nosa_step)
@@ -70,6 +70,7 @@ def _load() -> ctypes.CDLL:
         "nosa_fetch_blocks": [SH, P, I64, P, P, P, I32, P, I64, P],
         "nosa_sparse_decode": [SH, P, P, I64, I32, P, P, P, I64, ST, P, I64, P, P, SZ, P],
         "nosa_select_parts": [SH, P, P, ST] + [P] * 15 + [P],
+        "nosa_score_select": [SH, P, P, P, ST] + [P] * 12 + [P],
         "nosa_decode_chunks": [SH, I32, I32],
         "nosa_decode_partial": [SH, P, P, I64, I32, P, P, I32, I32, I32, P, I64, ST, P, I64, P, SZ,
                                 I32, P],
@@ -166,6 +167,16 @@ def nosa_select_parts(shape, s_q, e_blk, step, ge_bits, ev_bits, sel, n_sel, sel
         _p(sel), _p(n_sel), _p(sel_bits), _p(ge_list), _p(n_ge), _p(gq_list), _p(n_gq),
         _p(slot_block), _p(block_slot), _p(fetch_block), _p(fetch_slot), _p(n_fetch),
         _p(counters), _s(stream)))
+
+
+def nosa_score_select(shape, q, kbar, e_blk, step, s_q, ge_bits, ev_bits, sel, n_sel, sel_bits,
+                      slot_block=None, block_slot=None, fetch_block=None, fetch_slot=None,
+                      n_fetch=None, counters=None, stream=None):
+    _chk("nosa_score_select", _L.nosa_score_select(
+        ctypes.byref(shape), _p(q), _p(kbar), _p(e_blk), ctypes.byref(step), _p(s_q),
+        _p(ge_bits), _p(ev_bits), _p(sel), _p(n_sel), _p(sel_bits), _p(slot_block),
+        _p(block_slot), _p(fetch_block), _p(fetch_slot), _p(n_fetch), _p(counters),
+        _s(stream)))
 
 
 def nosa_decode_chunks(shape, list_len, with_newest) -> int:

@@ -1,6 +1,6 @@
 """Build libnosa.so (HIP, gfx950) in-tree.
 
-    python -m trainable_block_sparse_nosa_amd.build
+    python trainable_block_sparse_nosa_amd/build.py
 
 Every HIP source is compiled with packed-fp32 instruction selection disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass warns

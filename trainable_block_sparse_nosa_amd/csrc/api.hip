@@ -261,6 +261,34 @@ nosa_status nosa_select_parts(const nosa_shape *shape, const float *s_q, const f
                                     (hipStream_t)stream));
 }
 
+nosa_status nosa_score_select(const nosa_shape *shape, const void *q, const void *kbar,
+                              const float *e_blk, const nosa_step *step, float *s_q,
+                              uint32_t *ge_bits, uint32_t *ev_bits, int32_t *sel, int32_t *n_sel,
+                              uint32_t *sel_bits, int32_t *slot_block, int32_t *block_slot,
+                              int32_t *fetch_block, int32_t *fetch_slot, int32_t *n_fetch,
+                              uint64_t *counters, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!q || !kbar || !s_q || !e_blk || !ge_bits || !ev_bits || !sel || !n_sel || !sel_bits)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    const bool any_swap = slot_block || block_slot || fetch_block || fetch_slot || n_fetch || counters;
+    const bool all_swap = slot_block && block_slot && fetch_block && fetch_slot && n_fetch && counters;
+    if (any_swap && !all_swap) return NOSA_ERR_INVALID_ARGUMENT;
+    const int n_cand = step_cand(dm, step);
+    if (n_cand < 0) return NOSA_ERR_INVALID_ARGUMENT;
+    const SwapPtrs sw{slot_block, block_slot, fetch_block, fetch_slot, n_fetch, counters};
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        constexpr int D = decltype(dc)::value;
+        return by_group(dm, [&](auto gc) -> nosa_status {
+            return hip_status(launch_score_select<T, D, decltype(gc)::value>(
+                dm, q, kbar, s_q, e_blk, n_cand, step->n_cand_prev, ge_bits, ev_bits, sel, n_sel,
+                sel_bits, all_swap ? &sw : nullptr, (hipStream_t)stream));
+        });
+    });
+}
+
 nosa_status nosa_swap_diff(const nosa_shape *shape, const int32_t *sel, const int32_t *n_sel,
                            const uint32_t *sel_bits, int32_t *slot_block, int32_t *block_slot,
                            int32_t *fetch_block, int32_t *fetch_slot, int32_t *n_fetch,

@@ -22,6 +22,9 @@ struct Dims {
 
 using bf16_t = uint16_t;  // bfloat16 storage
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// MFMA operand types: eight bf16 (A/B of 16x16x32 bf16), four fp32 (C/D)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(uint32_t h16) { return __uint_as_float(h16 << 16); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -30,6 +30,14 @@ hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, i
                          uint32_t *sel_bits, const SwapPtrs *swap, const SelectLists *parts,
                          hipStream_t st);
 
+// Scores computed by the selecting workgroup (one per row), written to s_q
+// as well, then the selection (and the set difference when swap != nullptr).
+template <typename T, int D, int G>
+hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, float *s_q,
+                               const float *e_blk, int n_cand, int n_prev, uint32_t *ge,
+                               uint32_t *ev, int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
+                               const SwapPtrs *swap, hipStream_t st);
+
 hipError_t launch_swap(const Dims &dm, const int32_t *sel, const int32_t *n_sel,
                        const uint32_t *sel_bits, const SwapPtrs &swap, hipStream_t st);
 

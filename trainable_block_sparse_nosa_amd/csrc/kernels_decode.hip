@@ -28,8 +28,6 @@
 
 namespace nosa {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVES = 4;  // waves per workgroup of the MFMA kernel
 

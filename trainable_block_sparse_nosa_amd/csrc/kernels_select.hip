@@ -10,26 +10,42 @@ namespace nosa {
 
 // ---------------------------------------------------------------------------
 // Pooled keys are stored in the KV dtype T, V = 16 / sizeof(T) dimensions per
-// 16-byte vector: kbar[row][D/V][m * max_blocks][V] (dimension vectors
-// outermost, so a wave whose lanes hold consecutive sub-blocks reads 1 KiB
-// contiguous per load).
+// 16-byte vector, grouped by quads of blocks (16 sub-blocks):
+// kbar[row][Q][D/V][16][V], Q = ceil(max_blocks / 4); sub-block sb = 4 j + i
+// of block j is slot sb % 16 of quad sb / 16. A quad is 16 * D elements in one
+// piece, laid out as the A operand tiles of a 16 x 16 x 32 MFMA want them: one
+// load instruction of a wave (16 sub-blocks x 4 dimension vectors) reads 1 KiB
+// contiguous.
 // ---------------------------------------------------------------------------
 template <typename T> struct KbarVec;
 template <> struct KbarVec<float> {
     static constexpr int V = 4;
+    __device__ __forceinline__ static void unpack(const uint4 &v, float (&x)[4]) {
+        x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+        x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+    }
     __device__ __forceinline__ static void load(const float *p, float (&x)[4]) {
-        const float4 v = *reinterpret_cast<const float4 *>(p);
-        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+        unpack(*reinterpret_cast<const uint4 *>(p), x);
     }
 };
 template <> struct KbarVec<bf16_t> {
     static constexpr int V = 8;
-    __device__ __forceinline__ static void load(const bf16_t *p, float (&x)[8]) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(p);
+    __device__ __forceinline__ static void unpack(const uint4 &v, float (&x)[8]) {
         x[0] = bf_lo(v.x); x[1] = bf_hi(v.x); x[2] = bf_lo(v.y); x[3] = bf_hi(v.y);
         x[4] = bf_lo(v.z); x[5] = bf_hi(v.z); x[6] = bf_lo(v.w); x[7] = bf_hi(v.w);
     }
+    __device__ __forceinline__ static void load(const bf16_t *p, float (&x)[8]) {
+        unpack(*reinterpret_cast<const uint4 *>(p), x);
+    }
 };
+
+// Element offset of dimension vector dv of sub-block sb in row r.
+template <typename T, int D>
+__device__ __forceinline__ int64_t kbar_vec(const Dims &dm, int r, int sb, int dv) {
+    constexpr int V = KbarVec<T>::V;
+    const int64_t quads = (dm.max_blocks + 3) / 4;
+    return (((int64_t)r * quads + (sb >> 4)) * (D / V) + dv) * (16 * V) + (int64_t)(sb & 15) * V;
+}
 
 // x (double) rounded to the nearest bfloat16, ties to even, with one
 // rounding: x is first rounded to float32 by rounding to odd (truncate, then
@@ -79,11 +95,9 @@ pool_kernel(Dims dm, const T *__restrict__ kv, int64_t kv_row_blocks, int kv_fir
     const int r = blockIdx.y;
     const int j = blk_begin + blockIdx.x;
     const T *K = kv + ((int64_t)r * kv_row_blocks + kv_first + blockIdx.x) * (int64_t)(2 * S * D);
-    const int64_t ld_sb = (int64_t)M * dm.max_blocks;  // sub-blocks per dimension-vector plane
-    T *kb = kbar + (int64_t)r * D * ld_sb;
     for (int p = threadIdx.x; p < M * D; p += blockDim.x) {
         const int i = p / D, d = p % D;
-        kb[((int64_t)(d / V) * ld_sb + (int64_t)(M * j + i)) * V + (d % V)] =
+        kbar[kbar_vec<T, D>(dm, r, M * j + i, d / V) + (d % V)] =
             pooled_mean<T>(K + (i * SUB) * D + d, D);
     }
     if (threadIdx.x < M) {
@@ -123,8 +137,6 @@ score_kernel(Dims dm, const T *__restrict__ q, const T *__restrict__ kbar, int n
 
     const int nsb = M * n_cand;
     const int sb = blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t ld_sb = (int64_t)M * dm.max_blocks;
-    const T *kb = kbar + (int64_t)r * D * ld_sb;
     float acc[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) acc[h] = 0.f;
@@ -132,7 +144,7 @@ score_kernel(Dims dm, const T *__restrict__ q, const T *__restrict__ kbar, int n
 #pragma unroll 8
         for (int dv = 0; dv < D / V; ++dv) {
             float x[V];
-            KbarVec<T>::load(kb + ((int64_t)dv * ld_sb + sb) * V, x);
+            KbarVec<T>::load(kbar + kbar_vec<T, D>(dm, r, sb, dv), x);
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -171,18 +183,28 @@ constexpr int MAX_W = 128;   // 4096 blocks
 constexpr int MAX_K = 128;
 constexpr int WAVE_TOPK = 64;
 constexpr int KEYS_PER_THREAD = 4096 / SELECT_THREADS;
+static_assert(MAX_W <= SELECT_THREADS, "one bitmap word per thread");
 
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
-// Smallest key of the wave's top-k among the keys held in x[0..m) of every
-// lane (0 = no key). Returns 0 when the wave holds at most k keys (then all
-// of its non-zero keys qualify).
+// Smallest key of the wave's top-k among the keys held in x[0..M) of every
+// lane (0 = no key). When the wave holds at most k keys, all of them qualify
+// and the smallest is returned.
 template <int M>
 __device__ uint64_t wave_kth_key(const uint64_t (&x)[M], int k) {
     int n = 0;
 #pragma unroll
     for (int i = 0; i < M; ++i) n += __popcll(__ballot(x[i] != 0ull));
-    if (n <= k) return 0ull;
+    if (n <= k) {
+        // every key qualifies: the smallest one (~0 when there is none)
+        uint64_t mn = ~0ull;
+#pragma unroll
+        for (int i = 0; i < M; ++i)
+            if (x[i] != 0ull) mn = umin64(mn, x[i]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mn = umin64(mn, __shfl_xor(mn, o, 64));
+        return mn;
+    }
     uint64_t t = 0ull;
     for (int b = 63; b >= 0; --b) {
         const uint64_t cand = t | (1ull << b);
@@ -200,12 +222,24 @@ __device__ uint64_t wave_kth_key(const uint64_t (&x)[M], int k) {
 // Top-k (k <= 64) of the keys x[0..M) held by every thread of the block:
 // sets the selected indices' bits in `bits` (LDS). Returns nothing; the
 // caller synchronises before reading `bits`.
+// k-th key (k <= 64) among the survivors surv[0..ns) by wave 0, with M2
+// survivors per lane.
+template <int M2>
+__device__ uint64_t survivors_kth(const uint64_t *surv, int ns, int k) {
+    const int lane = threadIdx.x & 63;
+    uint64_t y[M2];
+#pragma unroll
+    for (int i = 0; i < M2; ++i) y[i] = lane + 64 * i < ns ? surv[lane + 64 * i] : 0ull;
+    return wave_kth_key<M2>(y, k);
+}
+
 template <int M>
 __device__ void block_topk(const uint64_t (&x)[M], int k, uint64_t *surv, int *n_surv,
-                           uint32_t *bits) {
+                           uint64_t *thr, uint32_t *bits) {
     const int lane = threadIdx.x & 63;
     if (threadIdx.x == 0) *n_surv = 0;
     __syncthreads();
+    // each wave's own top-k go to LDS: together they hold the row's top-k
     const uint64_t t = wave_kth_key<M>(x, k);
     const uint64_t lt = lanemask_lt();
 #pragma unroll
@@ -218,25 +252,23 @@ __device__ void block_topk(const uint64_t (&x)[M], int k, uint64_t *surv, int *n
         if (keep) surv[base + __popcll(m & lt)] = x[i];
     }
     __syncthreads();
-    // four threads per survivor, each counting the larger survivors in a
-    // quarter of the list (two keys per 16-byte LDS read), quad-summed
-    const int ns = *n_surv;
-    const int q4 = ((ns + 7) / 8) * 2;  // keys per quarter, even
-    for (int base = 0; base < ns * 4; base += blockDim.x) {
-        const int i = (base + threadIdx.x) >> 2, part = threadIdx.x & 3;
-        const uint64_t me = i < ns ? surv[i] : ~0ull;
-        int above = 0;
-        const int j0 = part * q4, j1 = min(j0 + q4, ns);
-        int j = j0;
-        for (; j + 1 < j1; j += 2) {
-            const ulonglong2 two = *reinterpret_cast<const ulonglong2 *>(surv + j);
-            above += (two.x > me) + (two.y > me);
-        }
-        if (j < j1) above += surv[j] > me;
-        above += __shfl_xor(above, 1, 64);
-        above += __shfl_xor(above, 2, 64);
-        if (i < ns && part == 0 && above < k) {
-            const int idx = key_index(me);
+    // the row's k-th key is the k-th among the survivors (a key left out by
+    // its wave has k survivors of that wave above it); wave 0 finds it
+    if (threadIdx.x < 64) {
+        const int ns = *n_surv;  // <= SELECT_WAVES * k
+        uint64_t T;
+        if (ns <= 64) T = survivors_kth<1>(surv, ns, k);
+        else if (ns <= 128) T = survivors_kth<2>(surv, ns, k);
+        else if (ns <= 256) T = survivors_kth<4>(surv, ns, k);
+        else T = survivors_kth<8>(surv, ns, k);
+        if (threadIdx.x == 0) *thr = T;
+    }
+    __syncthreads();
+    const uint64_t T = *thr;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        if (x[i] != 0ull && x[i] >= T) {
+            const int idx = key_index(x[i]);
             atomicOr(&bits[idx >> 5], 1u << (idx & 31));
         }
     }
@@ -244,24 +276,25 @@ __device__ void block_topk(const uint64_t (&x)[M], int k, uint64_t *surv, int *n
 
 // Keys of candidates tid + 512 i (i < M) from key_of(j, i); then block_topk.
 template <int M, typename KeyFn>
-__device__ void topk_m(int n, int k, KeyFn key_of, uint64_t *surv, int *n_surv, uint32_t *bits) {
+__device__ void topk_m(int n, int k, KeyFn key_of, uint64_t *surv, int *n_surv, uint64_t *thr,
+                       uint32_t *bits) {
     uint64_t x[M];
 #pragma unroll
     for (int i = 0; i < M; ++i) {
         const int j = threadIdx.x + SELECT_THREADS * i;
         x[i] = j < n ? key_of(j, i) : 0ull;
     }
-    block_topk<M>(x, k, surv, n_surv, bits);
+    block_topk<M>(x, k, surv, n_surv, thr, bits);
 }
 
 // Dispatch on how many keys each thread holds (uniform over the block).
 template <typename KeyFn>
 __device__ void topk_dispatch(int n, int k, KeyFn key_of, uint64_t *surv, int *n_surv,
-                              uint32_t *bits) {
-    if (n <= SELECT_THREADS) topk_m<1>(n, k, key_of, surv, n_surv, bits);
-    else if (n <= 2 * SELECT_THREADS) topk_m<2>(n, k, key_of, surv, n_surv, bits);
-    else if (n <= 4 * SELECT_THREADS) topk_m<4>(n, k, key_of, surv, n_surv, bits);
-    else topk_m<8>(n, k, key_of, surv, n_surv, bits);
+                              uint64_t *thr, uint32_t *bits) {
+    if (n <= SELECT_THREADS) topk_m<1>(n, k, key_of, surv, n_surv, thr, bits);
+    else if (n <= 2 * SELECT_THREADS) topk_m<2>(n, k, key_of, surv, n_surv, thr, bits);
+    else if (n <= 4 * SELECT_THREADS) topk_m<4>(n, k, key_of, surv, n_surv, thr, bits);
+    else topk_m<8>(n, k, key_of, surv, n_surv, thr, bits);
 }
 
 __device__ void bitonic_desc(uint64_t *keys, int P) {
@@ -403,8 +436,161 @@ __device__ void swap_row(const Dims &dm, int r, const uint32_t *bits, int s0, in
     }
 }
 
+// Where a row's query-aware scores come from.
+// ScoresGlobal: s_q as written by score_kernel.
+struct ScoresGlobal {
+    const float *s_q;
+    __device__ __forceinline__ const float *row(const Dims &dm, int r, int) const {
+        return s_q + (int64_t)r * dm.max_blocks;
+    }
+};
+
+// ScoresFused: computed by the selecting workgroup itself into LDS (and
+// written to s_q as well), with the same arithmetic as score_kernel: lane <->
+// sub-block, U sub-blocks per thread per pass with all their 16-byte loads in
+// flight, DPP quad max over a block's sub-blocks, then the head sum. Needs the
+// whole workgroup (barriers inside).
+template <typename T, int D, int G>
+struct ScoresFused {
+    const T *q;
+    const T *kbar;
+    float *s_q;
+    __device__ const float *row(const Dims &dm, int r, int n_cand) const {
+        constexpr int M = 4, V = KbarVec<T>::V, NV = D / V, U = sizeof(T) == 2 ? 2 : 1;
+        __shared__ float qs[G][D];
+        __shared__ float sc[MAX_W * 32];
+        const int tid = threadIdx.x, nt = blockDim.x;
+        const int b = r / dm.Hkv, g = r % dm.Hkv;
+        const T *qr = q + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
+        for (int p = tid; p < G * D; p += nt) (&qs[0][0])[p] = ldf(qr + p) * dm.scale;
+        __syncthreads();
+        const int nsb = M * n_cand;
+        float *out = s_q + (int64_t)r * dm.max_blocks;
+        for (int base = 0; base < nsb; base += U * nt) {
+            // compiler-only memory barrier: keeps the LDS reads of q inside the
+            // pass (hoisted out of it, G * D floats would not fit in registers)
+            __asm__ volatile("" ::: "memory");
+            uint4 raw[U][NV];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int sb = base + u * nt + tid;
+                if (sb < nsb) {
+#pragma unroll
+                    for (int dv = 0; dv < NV; ++dv)
+                        raw[u][dv] = *reinterpret_cast<const uint4 *>(kbar + kbar_vec<T, D>(dm, r, sb, dv));
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int sb = base + u * nt + tid;
+                float acc[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) acc[h] = 0.f;
+                if (sb < nsb) {
+#pragma unroll
+                    for (int dv = 0; dv < NV; ++dv) {
+                        float x[V];
+                        KbarVec<T>::unpack(raw[u][dv], x);
+#pragma unroll
+                        for (int h = 0; h < G; ++h)
+#pragma unroll
+                            for (int e = 0; e < V; ++e)
+                                acc[h] = fmaf(qs[h][dv * V + e], x[e], acc[h]);
+                    }
+                }
+                // every lane takes part in the quad reductions (nt keeps quads whole)
+                float sum = 0.f;
+#pragma unroll
+                for (int h = 0; h < G; ++h) sum += quad_max(acc[h]);
+                if (sb < nsb && (sb & (M - 1)) == 0) {
+                    sc[sb / M] = sum;
+                    out[sb / M] = sum;
+                }
+            }
+        }
+        __syncthreads();
+        return sc;
+    }
+};
+
+// ScoresFusedMfma (bf16): the same scores with the dot products on the
+// matrix cores. A wave takes tiles of 16 sub-blocks (a quad of blocks): S =
+// K̄ Q^T on v_mfma_f32_16x16x32_bf16, the A operand being one 16-byte vector of
+// the pooled keys per lane (sub-block 16 tile + l % 16, dimensions 32 s +
+// 8 (l / 16) .. + 7: the quad's vectors as stored), B the group's queries with
+// the heads padded to 16 by zeros. The output tile puts a block's 4 sub-blocks
+// in one lane's 4 accumulators (rows 4 (l / 16) + r), so the block max is
+// in-lane, and the head sum a reduction over the 16 lanes of a row group.
+// The scale multiplies the fp32 dot product.
+template <int D, int G>
+struct ScoresFusedMfma {
+    const bf16_t *q;
+    const bf16_t *kbar;
+    float *s_q;
+    __device__ const float *row(const Dims &dm, int r, int n_cand) const {
+        constexpr int KS = D / 32, TPI = 4;  // k-steps; tiles per pass per wave
+        static_assert(G <= 16, "the group is one 16-wide MFMA tile");
+        __shared__ float sc[MAX_W * 32];
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int nw = blockDim.x >> 6;
+        const int col = lane & 15, grp = lane >> 4;
+        const int b = r / dm.Hkv, g = r % dm.Hkv;
+        // B operand: lane holds q[head col][32 s + 8 grp .. + 7]; zero past G
+        bf16x8 qop[KS];
+        {
+            const bf16_t *qh = q + ((int64_t)b * dm.Hq + (int64_t)g * G + (col < G ? col : 0)) * D +
+                               8 * grp;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                qop[s] = *reinterpret_cast<const bf16x8 *>(qh + 32 * s);
+                if (col >= G) qop[s] = bf16x8{};
+            }
+        }
+        const int nsb = 4 * n_cand;
+        // row r's quads of 16 sub-blocks, in bf16x8 vectors: [Q][D/8][16]
+        const bf16x8 *kb = reinterpret_cast<const bf16x8 *>(kbar + kbar_vec<bf16_t, D>(dm, r, 0, 0));
+        float *out = s_q + (int64_t)r * dm.max_blocks;
+        const int n_tiles = (nsb + 15) / 16;
+        for (int t0 = wave * TPI; t0 < n_tiles; t0 += nw * TPI) {
+            bf16x8 a[TPI][KS];
+#pragma unroll
+            for (int u = 0; u < TPI; ++u) {
+                const int sb = 16 * (t0 + u) + col;
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    a[u][s] = sb < nsb ? kb[((int64_t)(t0 + u) * (D / 8) + 4 * s + grp) * 16 + col]
+                                       : bf16x8{};
+            }
+#pragma unroll
+            for (int u = 0; u < TPI; ++u) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][s], qop[s], acc, 0, 0, 0);
+                // rows 4 grp .. 4 grp + 3 = the sub-blocks of block 4 (t0 + u) + grp
+                const float sc4 = dm.scale;
+                float m = fmaxf(fmaxf(acc[0] * sc4, acc[1] * sc4), fmaxf(acc[2] * sc4, acc[3] * sc4));
+                m = col < G ? m : 0.f;
+                m += __shfl_xor(m, 8, 16);
+                m += __shfl_xor(m, 4, 16);
+                m += __shfl_xor(m, 2, 16);
+                m += __shfl_xor(m, 1, 16);
+                const int blk = 4 * (t0 + u) + grp;
+                if (col == 0 && blk < n_cand) {
+                    sc[blk] = m;
+                    out[blk] = m;
+                }
+            }
+        }
+        __syncthreads();
+        return sc;
+    }
+};
+
+template <typename Src>
 __global__ void __launch_bounds__(SELECT_THREADS)
-select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ e_blk, int n_cand,
+select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand,
               int n_prev, int P, uint32_t *__restrict__ ge_bits, uint32_t *__restrict__ ev_bits,
               int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
               uint32_t *__restrict__ sel_bits, SwapArgs sw, ListArgs lists) {
@@ -412,32 +598,39 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
     __shared__ uint32_t ge[MAX_W], ev[MAX_W], sb[MAX_W], res[MAX_W];
     __shared__ __attribute__((aligned(16))) uint64_t surv[SELECT_WAVES * WAVE_TOPK + 2];
     __shared__ int n_surv;
+    __shared__ uint64_t thr;
     __shared__ uint64_t red64[SELECT_WAVES];
     __shared__ int red32[SELECT_WAVES];
     __shared__ int fb[MAX_K], fs[MAX_K], fo[MAX_K];
-    __shared__ int woff[3 * (MAX_W + 1)];
     const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int W = dm.W;
     const float *E = e_blk + (int64_t)r * dm.max_blocks;
-    const float *Sq = s_q + (int64_t)r * dm.max_blocks;
     uint32_t *ge_g = ge_bits + (int64_t)r * W;
     uint32_t *ev_g = ev_bits + (int64_t)r * W;
 
-    // independent loads first: this thread's scores, the cache's slot table
-    float sv[KEYS_PER_THREAD];
-#pragma unroll
-    for (int i = 0; i < KEYS_PER_THREAD; ++i) {
-        const int j = tid + SELECT_THREADS * i;
-        sv[i] = j < n_cand ? Sq[j] : 0.f;
-    }
+    // independent loads first: the cache's slot table and counters, then this
+    // thread's scores
     int s0 = -1, s1 = -1;
     uint64_t cnt = 0ull;
     if (sw.slot_block && wave == 0) {
         if (lane < dm.k) s0 = sw.slot_block[(int64_t)r * dm.k + lane];
         if (lane + 64 < dm.k) s1 = sw.slot_block[(int64_t)r * dm.k + lane + 64];
         if (lane < 2) cnt = sw.counters[2 * r + lane];
+    }
+    // the eviction state: word tid (W <= MAX_W <= the workgroup size)
+    uint32_t ge_w = 0u, ev_w = 0u;
+    if (n_prev >= 0 && tid < W) {
+        ge_w = ge_g[tid];
+        ev_w = ev_g[tid];
+    }
+    const float *Sq = src.row(dm, r, n_cand);
+    float sv[KEYS_PER_THREAD];
+#pragma unroll
+    for (int i = 0; i < KEYS_PER_THREAD; ++i) {
+        const int j = tid + SELECT_THREADS * i;
+        sv[i] = j < n_cand ? Sq[j] : 0.f;
     }
 
     // ---- Gamma_e ----
@@ -447,7 +640,7 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
         const int ke = min(dm.k_e, n_cand);
         if (ke > 0 && dm.k_e <= WAVE_TOPK) {
             topk_dispatch(n_cand, ke, [&](int j, int) { return rank_key(E[j], j); }, surv,
-                          &n_surv, ge);
+                          &n_surv, &thr, ge);
         } else if (ke > 0) {
             for (int i = tid; i < P; i += nt) keys[i] = i < n_cand ? rank_key(E[i], i) : 0ull;
             __syncthreads();
@@ -467,12 +660,12 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
         __syncthreads();
     } else {
         // state only ever holds blocks that were candidates at the previous step
-        for (int w = tid; w < W; w += nt) {
-            const int lo = w * 32;
+        if (tid < W) {
+            const int lo = tid * 32;
             const uint32_t prev = lo + 32 <= n_prev ? 0xFFFFFFFFu
                                 : (lo >= n_prev ? 0u : ((1u << (n_prev - lo)) - 1u));
-            ge[w] = ge_g[w] & prev;
-            ev[w] = ev_g[w] & prev;
+            ge[tid] = ge_w & prev;
+            ev[tid] = ev_w & prev;
         }
         __syncthreads();
         for (int x = n_prev; x < n_cand; ++x) {
@@ -510,17 +703,18 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
     }
 
     // ---- Gamma_q: best k_q of the candidates outside Gamma_e ----
-    int ne_loc = 0;
-    for (int w = tid; w < W; w += nt) {
-        sb[w] = ge[w];
-        ne_loc += __popc(ge[w]);
-    }
-    const int n_e = block_sum_int(ne_loc, red32);  // also orders the sb copies
+    // every wave counts Gamma_e itself (no barrier); the copies into sb are
+    // ordered before the top-k's updates by the top-k's first barrier
+    for (int w = tid; w < W; w += nt) sb[w] = ge[w];
+    int ne_loc = (lane < W ? __popc(ge[lane]) : 0) + (lane + 64 < W ? __popc(ge[lane + 64]) : 0);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ne_loc += __shfl_xor(ne_loc, o, 64);
+    const int n_e = __builtin_amdgcn_readfirstlane(ne_loc);
     const int kq = min(dm.k_q, n_cand - n_e);
     if (kq > 0 && dm.k_q <= WAVE_TOPK) {
         topk_dispatch(n_cand, kq, [&](int j, int i) -> uint64_t {
             return ((ge[j >> 5] >> (j & 31)) & 1u) ? 0ull : rank_key(sv[i], j);
-        }, surv, &n_surv, sb);
+        }, surv, &n_surv, &thr, sb);
     } else if (kq > 0) {
         for (int i = tid; i < P; i += nt) {
             const bool ok = i < n_cand && !((ge[i >> 5] >> (i & 31)) & 1u);
@@ -541,66 +735,41 @@ select_kernel(Dims dm, const float *__restrict__ s_q, const float *__restrict__ 
         ev_g[w] = ev[w];
         sel_bits[(int64_t)r * W + w] = sb[w];
     }
-    // word offsets of the selection, of Gamma_e and of Gamma_q (one wave scans
-    // <= 128 words, two per lane)
-    if (wave == 0) {
+    if (wave != 0) return;
+    // wave 0 writes the ascending lists: the union, and each part when asked
+    // for. Lane l holds bitmap words 2l and 2l+1 (<= 128 words); a prefix sum
+    // of their popcounts places each lane's candidates.
+    const int w0 = 2 * lane, w1 = 2 * lane + 1;
+    auto place = [&](uint32_t a0, uint32_t a1, int32_t *dst, int cap) -> int {
+        const int cnt = __popc(a0) + __popc(a1);
+        int inc = cnt;
 #pragma unroll
-        for (int li = 0; li < 3; ++li) {
-            auto word = [&](int w) -> uint32_t {
-                if (w >= W) return 0u;
-                return li == 0 ? sb[w] : (li == 1 ? ge[w] : (sb[w] & ~ge[w]));
-            };
-            const uint32_t w0 = word(2 * lane), w1 = word(2 * lane + 1);
-            const int cnt = __popc(w0) + __popc(w1);
-            int inc = cnt;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(inc, o, 64);
-                if (lane >= o) inc += y;
-            }
-            int *wo = woff + li * (MAX_W + 1);
-            if (2 * lane < W) wo[2 * lane] = inc - cnt;
-            if (2 * lane + 1 < W) wo[2 * lane + 1] = inc - cnt + __popc(w0);
-            if (lane == 63) wo[MAX_W] = inc;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
         }
-    }
-    __syncthreads();
-    // every thread places its own selected candidates (union, and each part
-    // when asked for)
-    int32_t *out = sel + (int64_t)r * dm.k;
-    const int total = min(woff[MAX_W], dm.k);
-    const int *wo_e = woff + (MAX_W + 1), *wo_q = woff + 2 * (MAX_W + 1);
-    for (int j = tid; j < n_cand; j += nt) {
-        const uint32_t word = sb[j >> 5];
-        const uint32_t bit = 1u << (j & 31), below = bit - 1u;
-        if (word & bit) {
-            const int pos = woff[j >> 5] + __popc(word & below);
-            if (pos < dm.k) out[pos] = j;
-            if (lists.n_ge) {
-                const uint32_t we = ge[j >> 5];
-                if (we & bit) {
-                    const int pe = wo_e[j >> 5] + __popc(we & below);
-                    if (pe < dm.k_e) lists.ge_list[(int64_t)r * dm.k_e + pe] = j;
-                } else {
-                    const uint32_t wq = word & ~we;
-                    const int pq = wo_q[j >> 5] + __popc(wq & below);
-                    if (pq < dm.k_q) lists.gq_list[(int64_t)r * dm.k_q + pq] = j;
-                }
-            }
-        }
-    }
-    for (int i = total + tid; i < dm.k; i += nt) out[i] = -1;
+        int pos = inc - cnt;
+        for (uint32_t m = a0; m; m &= m - 1u, ++pos)
+            if (pos < cap) dst[pos] = 32 * w0 + __ffs(m) - 1;
+        for (uint32_t m = a1; m; m &= m - 1u, ++pos)
+            if (pos < cap) dst[pos] = 32 * w1 + __ffs(m) - 1;
+        const int n = __shfl(inc, 63, 64);
+        for (int i = min(n, cap) + lane; i < cap; i += 64) dst[i] = -1;
+        return min(n, cap);
+    };
+    const uint32_t s0w = w0 < W ? sb[w0] : 0u, s1w = w1 < W ? sb[w1] : 0u;
+    const int total = place(s0w, s1w, sel + (int64_t)r * dm.k, dm.k);
     if (lists.n_ge) {
-        const int ne = min(wo_e[MAX_W], dm.k_e), nq = min(wo_q[MAX_W], dm.k_q);
-        for (int i = ne + tid; i < dm.k_e; i += nt) lists.ge_list[(int64_t)r * dm.k_e + i] = -1;
-        for (int i = nq + tid; i < dm.k_q; i += nt) lists.gq_list[(int64_t)r * dm.k_q + i] = -1;
-        if (tid == 0) {
+        const uint32_t e0w = w0 < W ? ge[w0] : 0u, e1w = w1 < W ? ge[w1] : 0u;
+        const int ne = place(e0w, e1w, lists.ge_list + (int64_t)r * dm.k_e, dm.k_e);
+        const int nq = place(s0w & ~e0w, s1w & ~e1w, lists.gq_list + (int64_t)r * dm.k_q, dm.k_q);
+        if (lane == 0) {
             lists.n_ge[r] = ne;
             lists.n_gq[r] = nq;
         }
     }
-    if (tid == 0) n_sel[r] = total;
-    if (sw.slot_block && wave == 0) swap_row(dm, r, sb, s0, s1, cnt, res, fb, fs, fo, sw);
+    if (lane == 0) n_sel[r] = total;
+    if (sw.slot_block) swap_row(dm, r, sb, s0, s1, cnt, res, fb, fs, fo, sw);
 }
 
 // Stand-alone set difference: one wave per row, selection bitmap and slot
@@ -668,10 +837,12 @@ hipError_t launch_score(const Dims &dm, const void *q, const void *kbar, int n_c
     return hipGetLastError();
 }
 
-hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, int n_cand,
-                         int n_prev, uint32_t *ge, uint32_t *ev, int32_t *sel, int32_t *n_sel,
-                         uint32_t *sel_bits, const SwapPtrs *swap, const SelectLists *parts,
-                         hipStream_t st) {
+template <typename Src>
+static hipError_t launch_select_from(const Dims &dm, const Src &src, const float *e_blk,
+                                     int n_cand, int n_prev, uint32_t *ge, uint32_t *ev,
+                                     int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
+                                     const SwapPtrs *swap, const SelectLists *parts,
+                                     hipStream_t st) {
     // LDS keys only when a budget is above what the register top-k holds
     int P = 0;
     if ((n_prev < 0 && dm.k_e > WAVE_TOPK) || dm.k_q > WAVE_TOPK) {
@@ -689,9 +860,36 @@ hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, i
     }
     ListArgs li{};
     if (parts) li = ListArgs{parts->ge_list, parts->n_ge, parts->gq_list, parts->n_gq};
-    hipLaunchKernelGGL(select_kernel, dim3(dm.rows), dim3(SELECT_THREADS), P * sizeof(uint64_t),
-                       st, dm, s_q, e_blk, n_cand, n_prev, P, ge, ev, sel, n_sel, sel_bits, sw, li);
+    hipLaunchKernelGGL(select_kernel<Src>, dim3(dm.rows), dim3(SELECT_THREADS),
+                       P * sizeof(uint64_t), st, dm, src, e_blk, n_cand, n_prev, P, ge, ev, sel,
+                       n_sel, sel_bits, sw, li);
     return hipGetLastError();
+}
+
+hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, int n_cand,
+                         int n_prev, uint32_t *ge, uint32_t *ev, int32_t *sel, int32_t *n_sel,
+                         uint32_t *sel_bits, const SwapPtrs *swap, const SelectLists *parts,
+                         hipStream_t st) {
+    return launch_select_from(dm, ScoresGlobal{s_q}, e_blk, n_cand, n_prev, ge, ev, sel, n_sel,
+                              sel_bits, swap, parts, st);
+}
+
+template <typename T, int D, int G>
+hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, float *s_q,
+                               const float *e_blk, int n_cand, int n_prev, uint32_t *ge,
+                               uint32_t *ev, int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
+                               const SwapPtrs *swap, hipStream_t st) {
+    if constexpr (std::is_same_v<T, bf16_t>) {
+        const ScoresFusedMfma<D, G> src{static_cast<const bf16_t *>(q),
+                                        static_cast<const bf16_t *>(kbar), s_q};
+        return launch_select_from(dm, src, e_blk, n_cand, n_prev, ge, ev, sel, n_sel, sel_bits,
+                                  swap, nullptr, st);
+    } else {
+        const ScoresFused<T, D, G> src{static_cast<const T *>(q), static_cast<const T *>(kbar),
+                                       s_q};
+        return launch_select_from(dm, src, e_blk, n_cand, n_prev, ge, ev, sel, n_sel, sel_bits,
+                                  swap, nullptr, st);
+    }
 }
 
 hipError_t launch_swap(const Dims &dm, const int32_t *sel, const int32_t *n_sel,
@@ -727,7 +925,10 @@ NOSA_POOL_INST(bf16_t, 128)
 
 #define NOSA_SCORE_INST(T, D, G)                                                               \
     template hipError_t launch_score<T, D, G>(const Dims &, const void *, const void *, int,   \
-                                              float *, hipStream_t);
+                                              float *, hipStream_t);                           \
+    template hipError_t launch_score_select<T, D, G>(                                          \
+        const Dims &, const void *, const void *, float *, const float *, int, int, uint32_t *, \
+        uint32_t *, int32_t *, int32_t *, uint32_t *, const SwapPtrs *, hipStream_t);
 #define NOSA_SCORE_ALLG(T, D)                                                                  \
     NOSA_SCORE_INST(T, D, 1) NOSA_SCORE_INST(T, D, 2) NOSA_SCORE_INST(T, D, 3)                 \
     NOSA_SCORE_INST(T, D, 4) NOSA_SCORE_INST(T, D, 5) NOSA_SCORE_INST(T, D, 6)                 \

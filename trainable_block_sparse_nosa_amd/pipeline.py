@@ -66,7 +66,8 @@ class DecodeLayer:
 
     def __init__(self, *, batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks, dtype,
                  kv, kv_row_blocks, e_tok, offload=False, decode_kernel=L.NOSA_DECODE_AUTO,
-                 scale=0.0, device="cuda", fuse_select_swap=True, overlap=False):
+                 scale=0.0, device="cuda", fuse_select_swap=True, fuse_score=None,
+                 overlap=False):
         self.shape = L.make_shape(batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks,
                                   dtype, decode_kernel=decode_kernel, scale=scale)
         self.rows = batch * n_kv_heads
@@ -86,9 +87,10 @@ class DecodeLayer:
         dev = torch.device(device)
         R, k, W = self.rows, self.k, self.W
         f32, i32 = torch.float32, torch.int32
-        # pooled keys in the KV dtype, 16-byte vectors of V dimensions
+        # pooled keys in the KV dtype: quads of 4 blocks (16 sub-blocks), each
+        # [D / V][16][V] with V dimensions per 16-byte vector
         V = 16 // (4 if dtype == L.NOSA_F32 else 2)
-        self.kbar = torch.zeros(R, head_dim // V, 4 * max_blocks, V,
+        self.kbar = torch.zeros(R, (max_blocks + 3) // 4, head_dim // V, 16, V,
                                 dtype=f32 if dtype == L.NOSA_F32 else torch.bfloat16, device=dev)
         self.e_blk = torch.zeros(R, max_blocks, dtype=f32, device=dev)
         self.s_q = torch.zeros(R, max_blocks, dtype=f32, device=dev)
@@ -115,6 +117,11 @@ class DecodeLayer:
             self.cur_fs = torch.zeros(R, k, dtype=i32, device=dev)
             self.cur_nf = torch.ones(R, dtype=i32, device=dev)
         self.fuse_select_swap = fuse_select_swap
+        # scoring and selection in one launch (one workgroup per row); by
+        # default for bf16, whose scores run on the matrix cores there
+        if fuse_score is None:
+            fuse_score = dtype == L.NOSA_BF16
+        self.fuse_score = fuse_score and fuse_select_swap
         # Overlap (KV in HBM): on a step that completes no block, attention over
         # the eviction set (unchanged since the previous step) and the newest
         # block runs on a side stream while the scores and the selection run on
@@ -191,19 +198,26 @@ class DecodeLayer:
             self.n_cand_prev = c
             self.n_tokens = n_tokens
             return self.out
-        self._run("score", L.nosa_score_blocks, self.shape, q, self.kbar, st, self.s_q, stream)
-        if (swap or self.offload) and self.fuse_select_swap:
-            self._run("select", L.nosa_select_swap, self.shape, self.s_q, self.e_blk, st,
-                      self.ge_bits, self.ev_bits, self.sel, self.n_sel, self.sel_bits,
-                      self.slot_block, self.block_slot, self.fetch_block, self.fetch_slot,
-                      self.n_fetch, self.counters, stream)
+        if self.fuse_score:
+            cache = (self.slot_block, self.block_slot, self.fetch_block, self.fetch_slot,
+                     self.n_fetch, self.counters) if (swap or self.offload) else (None,) * 6
+            self._run("score_select", L.nosa_score_select, self.shape, q, self.kbar, self.e_blk,
+                      st, self.s_q, self.ge_bits, self.ev_bits, self.sel, self.n_sel,
+                      self.sel_bits, *cache, stream)
         else:
-            self._run("select", L.nosa_select, self.shape, self.s_q, self.e_blk, st, self.ge_bits,
-                      self.ev_bits, self.sel, self.n_sel, self.sel_bits, stream)
-            if swap or self.offload:
-                self._run("swap", L.nosa_swap_diff, self.shape, self.sel, self.n_sel,
-                          self.sel_bits, self.slot_block, self.block_slot, self.fetch_block,
-                          self.fetch_slot, self.n_fetch, self.counters, stream)
+            self._run("score", L.nosa_score_blocks, self.shape, q, self.kbar, st, self.s_q, stream)
+            if (swap or self.offload) and self.fuse_select_swap:
+                self._run("select", L.nosa_select_swap, self.shape, self.s_q, self.e_blk, st,
+                          self.ge_bits, self.ev_bits, self.sel, self.n_sel, self.sel_bits,
+                          self.slot_block, self.block_slot, self.fetch_block, self.fetch_slot,
+                          self.n_fetch, self.counters, stream)
+            else:
+                self._run("select", L.nosa_select, self.shape, self.s_q, self.e_blk, st,
+                          self.ge_bits, self.ev_bits, self.sel, self.n_sel, self.sel_bits, stream)
+                if swap or self.offload:
+                    self._run("swap", L.nosa_swap_diff, self.shape, self.sel, self.n_sel,
+                              self.sel_bits, self.slot_block, self.block_slot, self.fetch_block,
+                              self.fetch_slot, self.n_fetch, self.counters, stream)
         if self.offload:
             self._run("fetch", L.nosa_fetch_blocks, self.shape, self.kv, self.kv_row_blocks,
                       self.fetch_block, self.fetch_slot, self.n_fetch, self.k, self.cache, self.k,
