@@ -50,6 +50,10 @@ def parse():
                          "becomes a latency-bound launch of its own)")
     ap.add_argument("--offload-steps", type=int, default=60,
                     help="steps of the offloaded 128k-context leg (0 = skip)")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the locality ablation of the offload leg (budget splits "
+                         "k_e + k_q = k with k_e = 32 and 0, and per-block / per-token "
+                         "hipMemcpyAsync copies against the fetch kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 4 device-to-device copies of 512 MiB (a reference kernel "
                          "of known traffic for hardware byte counters)")
@@ -317,6 +321,8 @@ def offload_leg(args, dev, stream):
     block_bytes = 2 * 64 * w.head_dim * 2
     swap_gbs = fetched * block_bytes / fetch_s / 1e9
     peak = h2d_peak_gbs(dev)
+    counters = layer.counters.cpu().numpy()
+    T = sub.warmup + sub.steps
     out = {
         "workload": w.name, "steps": sub.steps, "steps_per_s": sub.steps / elapsed,
         "ms_per_step": elapsed / sub.steps * 1e3,
@@ -324,10 +330,80 @@ def offload_leg(args, dev, stream):
         "fetch_us_per_step": fetch_s / sub.steps * 1e6,
         "swap_gbs": swap_gbs, "h2d_memcpy_gbs": peak, "frac_of_h2d": swap_gbs / peak,
         "attn_partial_us_per_step": sum(dec_ms) / len(dec_ms) * 1e3,
+        "gamma_mean": float(counters[:, 1].sum()) / (w.rows * w.k * T),
     }
+    if not args.no_ablation:
+        out["ablation"] = locality_ablation(w, layer, q, kv, sub, dev, stream, out, block_bytes)
     kv.free()
     del layer, q
     return out
+
+
+def locality_ablation(w, layer, q, kv, sub, dev, stream, nosa_run, block_bytes):
+    """Same inputs, same budget k, other splits k_e + k_q: k_e = 0 is unconstrained
+    query-aware top-k (no locality bound); NOSA's k_e bounds gamma >= k_e / k and
+    with it the blocks fetched per step. Also the fetch kernel against copies
+    issued one block (32 KiB) or one token (K and V rows, 512 B) at a time."""
+    import numpy as np
+    import torch
+    from trainable_block_sparse_nosa_amd import _lib as L
+    from trainable_block_sparse_nosa_amd.pipeline import DecodeLayer
+    k = w.k
+    rows = [dict(k_e=w.k_e, k_q=w.k_q, gamma_bound=w.k_e / k, gamma_mean=nosa_run["gamma_mean"],
+                 fetched_mib_per_step=nosa_run["fetched_mib_per_step"],
+                 steps_per_s=nosa_run["steps_per_s"], ms_per_step=nosa_run["ms_per_step"])]
+    T = sub.warmup + sub.steps
+    for ke in (k // 2, 0):
+        if ke == w.k_e:
+            continue
+        lay = DecodeLayer(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                          head_dim=w.head_dim, k_e=ke, k_q=k - ke, max_blocks=w.nb_max,
+                          dtype=L.NOSA_BF16, kv=kv.dev, kv_row_blocks=w.nb_max,
+                          e_tok=layer.e_tok, offload=True)
+        elapsed, _, fetched = timed_run(lay, w, q, sub, stream, event_stages=())
+        cnt = lay.counters.cpu().numpy()
+        rows.append(dict(k_e=ke, k_q=k - ke, gamma_bound=ke / k,
+                         gamma_mean=float(cnt[:, 1].sum()) / (w.rows * k * T),
+                         fetched_mib_per_step=fetched * block_bytes / sub.steps / 2**20,
+                         steps_per_s=sub.steps / elapsed, ms_per_step=elapsed / sub.steps * 1e3))
+        log(f"ablation k_e={ke} k_q={k - ke}: {rows[-1]['steps_per_s']:.1f} steps/s, "
+            f"gamma {rows[-1]['gamma_mean']:.3f}, {rows[-1]['fetched_mib_per_step']:.1f} MiB/step")
+        del lay
+        torch.cuda.empty_cache()
+    # transfer granularity: the blocks the fetch kernel moved in the last step,
+    # copied by hipMemcpyAsync (torch copy_) one block, then one 512-B token, at a time
+    fb = layer.fetch_block.cpu().numpy()
+    nf = layer.n_fetch.cpu().numpy()
+    pairs = [(r, int(b)) for r in range(w.rows) for b in fb[r, :nf[r]]]
+    if not pairs:
+        return {"splits": rows, "granularity": None}
+    host = torch.from_numpy(kv.array(np.uint8, (w.rows, w.nb_max, block_bytes)))
+    dst = torch.empty(len(pairs), block_bytes, dtype=torch.uint8, device=dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i, (r, b) in enumerate(pairs):
+        dst[i].copy_(host[r, b], non_blocking=True)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    per_block_gbs = len(pairs) * block_bytes / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    tok = 512
+    n_tok = min(len(pairs) * (block_bytes // tok), 4096)   # a bounded sample of token copies
+    flat = host.view(-1)
+    ev0.record(stream)
+    for i in range(n_tok):
+        r, b = pairs[(i // (block_bytes // tok)) % len(pairs)]
+        o = ((r * w.nb_max + b) * block_bytes) + (i % (block_bytes // tok)) * tok
+        dst.view(-1)[i * tok:(i + 1) * tok].copy_(flat[o:o + tok], non_blocking=True)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    per_token_gbs = n_tok * tok / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del dst
+    return {"splits": rows,
+            "granularity": {"fetch_kernel_gbs": nosa_run["swap_gbs"],
+                            "memcpy_per_block_gbs": per_block_gbs,
+                            "memcpy_per_token_gbs": per_token_gbs,
+                            "blocks": len(pairs), "token_copies_sampled": n_tok}}
 
 
 def main():

@@ -14,9 +14,9 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-def _fullsize(name, rows, steps):
+def _fullsize(name, rows, steps, w=None):
     gh = _gpu()
-    w = synth.WORKLOADS[name]
+    w = w or synth.WORKLOADS[name]
     print(f"[fullsize] {name}: oracle on rows {rows}, steps 0..{steps - 1}", flush=True)
     tr = oracle_trace(w, rows=rows, steps=list(range(steps)))
     print(f"[fullsize] {name}: uploading inputs", flush=True)
@@ -50,6 +50,16 @@ def test_fullsize_bf16_3b_64k():
 
 def test_fullsize_offload_1layer_128k():
     _fullsize("offload_1layer_128k", rows=[0, 77, 127], steps=256)
+
+
+@pytest.mark.parametrize("k_e", [32, 0])
+def test_fullsize_offload_128k_budget_splits(k_e):
+    """The locality ablation's other splits of the same budget k = 64 on the
+    128k offload shape: k_e = 32, and k_e = 0 (query-aware top-k only, no
+    locality bound). Steps 0..65 cross a block boundary (step 63)."""
+    base = synth.WORKLOADS["offload_1layer_128k"]
+    w = base.scaled(k_e=k_e, k_q=base.k - k_e, name=f"offload_1layer_128k_ke{k_e}")
+    _fullsize(w.name, rows=[0, 77, 127], steps=66, w=w)
 
 
 def test_fullsize_offload_8b_32layer_32k():
