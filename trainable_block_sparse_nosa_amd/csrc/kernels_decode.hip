@@ -29,7 +29,10 @@
 namespace nosa {
 
 
-constexpr int WAVES = 4;  // waves per workgroup of the MFMA kernel
+// MFMA kernel: 8 waves per workgroup, about one workgroup per CU (at ~230
+// registers two waves share a SIMD, so 8 waves fill a CU).
+constexpr int WAVES = 8;
+constexpr int MFMA_TARGET_WGS = 256;
 
 // Position of token `tok` (0..63) inside a row of the stored V^T tile: within
 // each 32-token half, positions 8g..8g+7 hold tokens 4g..4g+3, 16+4g..16+4g+3.
@@ -45,12 +48,17 @@ DecodePlan decode_plan(const Dims &dm, int kind, int entries) {
         return p;
     }
     if (kind == NOSA_DECODE_MFMA) {
-        // One block per wave measured fastest: at ~200 registers two waves
-        // share a SIMD and every wave issues all of its block's loads at once;
-        // walking several blocks per wave (with or without a second register
-        // set for the next block) and 1-, 2- or 8-wave workgroups were slower.
-        p.n_chunks = (entries + WAVES - 1) / WAVES;
-        p.cb = (entries + p.n_chunks - 1) / p.n_chunks;  // balanced chunks
+        // Few, long chunks: each workgroup's waves walk a chunk's entries with
+        // a running softmax state, so a row leaves few partials behind. The
+        // partials are the kernel's only writes, and writes mixed into the
+        // read stream cost far more HBM time than their bytes (measured on the
+        // 64k workload: 33 chunks per row of 4 one-block waves took 202 us, a
+        // chunk per row 186 us; with the partial writes dropped, 178 us).
+        int nc = (MFMA_TARGET_WGS + dm.rows - 1) / dm.rows;
+        const int maxc = (entries + WAVES - 1) / WAVES;  // at least a block per wave
+        nc = nc < 1 ? 1 : (nc > maxc ? maxc : nc);
+        p.n_chunks = nc;
+        p.cb = (entries + nc - 1) / nc;
     } else {
         // enough workgroups to cover 256 CUs several times over
         const long total = (long)dm.rows * entries;
@@ -135,7 +143,9 @@ __device__ __forceinline__ bool resolve_entry(const DecodeArgs &a, int e, int cn
 
 // ---------------------------------------------------------------------------
 // MFMA partial kernel (bf16). Chunk c of a row covers entries
-// [c*epc, min((c+1)*epc, entries)); wave w takes entry c*epc + w.
+// [c*cb, min((c+1)*cb, entries)); wave w takes entries c*cb + w, + 8, ...,
+// one block at a time with all of its loads in flight, keeping a running
+// softmax state; the 8 waves merge through LDS into the chunk's partial.
 // Lane l: col = l % 16 (head in S^T / O^T), grp = l / 16.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -228,7 +238,7 @@ __device__ __forceinline__ void attend_block(const BlockRegs<D> &br, const bf16x
 }
 
 template <int D, int G>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * WAVES)
 decode_mfma_kernel(Dims dm, DecodeArgs a) {
     static_assert(G <= 16, "the group is one 16-wide MFMA tile");
     constexpr int S = 64, KS = D / 32, DT = D / 16;
@@ -242,10 +252,10 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
     const int col = lane & 15, grp = lane >> 4;
     const int r = blockIdx.y, chunk = blockIdx.x;
     const int b = r / dm.Hkv, g = r % dm.Hkv;
-    const int epc = a.cb;
     const int cnt_e = a.n_list ? min(a.n_list[r], a.list_len) : a.list_len;
     const float *er = a.e_tok + (int64_t)r * a.e_stride;
-    const int e_end = min((chunk + 1) * epc, a.list_len + a.with_newest);
+    const int e_beg = chunk * a.cb;
+    const int e_end = min(e_beg + a.cb, a.list_len + a.with_newest);
     const bf16_t *q = static_cast<const bf16_t *>(a.q);
 
     // B operand of S^T = K Q^T: lane holds q[head col][32s + 8grp .. +7].
@@ -264,13 +274,11 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // one entry per wave: all of the block's loads are in flight at once
-    {
+    for (int e = e_beg + wave; e < e_end; e += WAVES) {
         BlockRegs<D> br;
-        const int e = chunk * epc + wave;
         const bf16_t *blk;
         int bid, valid;
-        if (e < e_end && resolve_entry<bf16_t>(a, e, cnt_e, r, BE, blk, bid, valid)) {
+        if (resolve_entry<bf16_t>(a, e, cnt_e, r, BE, blk, bid, valid)) {
             load_block<D>(br, blk, er + (int64_t)bid * S, valid, col, grp);
             // keep every load of the block ahead of the math: without this the
             // scheduler interleaves loads with MFMAs to save registers and the
@@ -280,7 +288,7 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
         }
     }
 
-    // merge the four waves' states
+    // merge the waves' states
     if (col < G) {
         if (grp == 0) {
             wm[wave][col] = m_run;
@@ -463,7 +471,7 @@ hipError_t launch_decode_mfma(const Dims &dm, const DecodePlan &pl, const Decode
                               hipStream_t st) {
     if (pl.n_chunks == 0) return hipSuccess;
     hipLaunchKernelGGL((decode_mfma_kernel<D, G>), dim3(pl.n_chunks, dm.rows),
-                       dim3(256), 0, st, dm, a);
+                       dim3(64 * WAVES), 0, st, dm, a);
     return hipGetLastError();
 }
 
