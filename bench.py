@@ -119,8 +119,11 @@ def cpu_baseline(w, seconds: float, steps_avail: int):
     }
 
 
-def setup(w, args, dev):
-    """Generate the workload's inputs (untimed) and build its layer."""
+def setup(w, args, dev, device_append=False):
+    """Generate the workload's inputs (untimed) and build its layer. Returns
+    (layer, q, kv, new): with device_append, new = (k_new, v_new), each step's
+    token of every row [T][rows][D] on the GPU (appended by the step; a
+    completed block is written back to the host KV); else None."""
     import numpy as np
     import torch
 
@@ -172,12 +175,29 @@ def setup(w, args, dev):
     log(f"{w.name}: inputs ready in {time.time() - t0:.1f} s")
     kind = {"auto": L.NOSA_DECODE_AUTO, "valu": L.NOSA_DECODE_VALU,
             "mfma": L.NOSA_DECODE_MFMA}[args.decode_kernel]
+    new = None
+    if device_append:
+        def tokens(r):
+            b, g = divmod(r, w.n_kv_heads)
+            return (conv(synth.keys_row(w, 0, b, g)[w.context:w.context + T]),
+                    conv(synth.values_row(w, 0, b, g)[w.context:w.context + T]))
+        kvn = synth.parallel_map(tokens, range(w.rows), 16)
+        new = (to_dev(np.ascontiguousarray(np.stack([k for k, _ in kvn], 1))),
+               to_dev(np.ascontiguousarray(np.stack([v for _, v in kvn], 1))))
     layer = DecodeLayer(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
                         head_dim=w.head_dim, k_e=w.k_e, k_q=w.k_q, max_blocks=nb,
                         dtype=L.NOSA_F32 if w.dtype == "f32" else L.NOSA_BF16, kv=kv_ptr,
                         kv_row_blocks=nb, e_tok=e_tok, offload=w.offload, decode_kernel=kind,
-                        overlap=getattr(args, "overlap", False))
-    return layer, q, kv
+                        overlap=getattr(args, "overlap", False), device_append=device_append)
+    return layer, q, kv, new
+
+
+def run_step(layer, q, new, t, n_tokens, stream):
+    """Step t of a layer built by setup."""
+    if new is None:
+        layer.step(q[t], n_tokens, stream)
+    else:
+        layer.step(q[t], n_tokens, stream, k_new=new[0][t], v_new=new[1][t])
 
 
 ATTN_STAGES = ("decode", "decode_e", "decode_q")
@@ -234,14 +254,14 @@ class HipTimingEvents:
         self.events = []
 
 
-def timed_run(layer, w, q, args, stream, event_stages=ATTN_STAGES):
+def timed_run(layer, w, q, args, stream, event_stages=ATTN_STAGES, new=None):
     """Warm up, then time exactly args.steps steps. HIP events, recorded on the
     stream each call runs on, bracket the listed stages in every timed step.
     Returns (elapsed s, [(stage, step, ms)], blocks fetched in the timed steps)."""
     import torch
     layer.start(w.n_tokens(0), stream)
     for t in range(args.warmup):
-        layer.step(q[t], w.n_tokens(t), stream)
+        run_step(layer, q, new, t, w.n_tokens(t), stream)
     torch.cuda.synchronize()
     fetched0 = int(layer.counters[:, 0].sum().item())
     pending = []
@@ -265,7 +285,7 @@ def timed_run(layer, w, q, args, stream, event_stages=ATTN_STAGES):
     t_start = time.perf_counter()
     for i in range(args.steps):
         cur["i"] = i
-        layer.step(q[args.warmup + i], w.n_tokens(args.warmup + i), stream)
+        run_step(layer, q, new, args.warmup + i, w.n_tokens(args.warmup + i), stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     layer.stage_hook = None
@@ -308,14 +328,17 @@ def h2d_peak_gbs(dev, nbytes=1 << 30, reps=5):
 
 def offload_leg(args, dev, stream):
     """The 128k-context offloaded workload: steps/s and swap GB/s of the fetch
-    kernel against the measured pinned-host-to-HBM copy bandwidth."""
+    kernel against the measured pinned-host-to-HBM copy bandwidth. Each step's
+    token is appended on the GPU and a completed block is written back to the
+    host KV, so the loop is the whole offload cycle."""
     import synth
     base = synth.WORKLOADS["offload_1layer_128k"]
     w = base.scaled(steps=max(base.steps, args.warmup + args.offload_steps))
     sub = argparse.Namespace(**vars(args))
     sub.steps = args.offload_steps
-    layer, q, kv = setup(w, sub, dev)
-    elapsed, ev, fetched = timed_run(layer, w, q, sub, stream, event_stages=("fetch", "decode"))
+    layer, q, kv, new = setup(w, sub, dev, device_append=True)
+    elapsed, ev, fetched = timed_run(layer, w, q, sub, stream, event_stages=("fetch", "decode"),
+                                     new=new)
     fetch_s = sum(ms for n, _, ms in ev if n == "fetch") / 1e3
     dec_ms = [ms for n, _, ms in ev if n == "decode"]
     block_bytes = 2 * 64 * w.head_dim * 2
@@ -331,15 +354,17 @@ def offload_leg(args, dev, stream):
         "swap_gbs": swap_gbs, "h2d_memcpy_gbs": peak, "frac_of_h2d": swap_gbs / peak,
         "attn_partial_us_per_step": sum(dec_ms) / len(dec_ms) * 1e3,
         "gamma_mean": float(counters[:, 1].sum()) / (w.rows * w.k * T),
+        "device_append": True,
     }
     if not args.no_ablation:
-        out["ablation"] = locality_ablation(w, layer, q, kv, sub, dev, stream, out, block_bytes)
+        out["ablation"] = locality_ablation(w, layer, q, kv, sub, dev, stream, out, block_bytes,
+                                            new)
     kv.free()
     del layer, q
     return out
 
 
-def locality_ablation(w, layer, q, kv, sub, dev, stream, nosa_run, block_bytes):
+def locality_ablation(w, layer, q, kv, sub, dev, stream, nosa_run, block_bytes, new):
     """Same inputs, same budget k, other splits k_e + k_q: k_e = 0 is unconstrained
     query-aware top-k (no locality bound); NOSA's k_e bounds gamma >= k_e / k and
     with it the blocks fetched per step. Also the fetch kernel against copies
@@ -359,8 +384,8 @@ def locality_ablation(w, layer, q, kv, sub, dev, stream, nosa_run, block_bytes):
         lay = DecodeLayer(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
                           head_dim=w.head_dim, k_e=ke, k_q=k - ke, max_blocks=w.nb_max,
                           dtype=L.NOSA_BF16, kv=kv.dev, kv_row_blocks=w.nb_max,
-                          e_tok=layer.e_tok, offload=True)
-        elapsed, _, fetched = timed_run(lay, w, q, sub, stream, event_stages=())
+                          e_tok=layer.e_tok, offload=True, device_append=new is not None)
+        elapsed, _, fetched = timed_run(lay, w, q, sub, stream, event_stages=(), new=new)
         cnt = lay.counters.cpu().numpy()
         rows.append(dict(k_e=ke, k_q=k - ke, gamma_bound=ke / k,
                          gamma_mean=float(cnt[:, 1].sum()) / (w.rows * k * T),
@@ -431,7 +456,7 @@ def main():
     w = base.scaled(steps=max(base.steps, T))
     log(f"workload {w.name}: rows={w.rows} G={w.group} D={w.head_dim} ctx={w.context} "
         f"k={w.k_e}+{w.k_q} steps={T} offload={w.offload}")
-    layer, q, kv = setup(w, args, dev)
+    layer, q, kv, _ = setup(w, args, dev)
 
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)

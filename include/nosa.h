@@ -144,6 +144,22 @@ nosa_status nosa_pool_blocks(const nosa_shape *shape, const void *kv, int64_t kv
                              int32_t blk_begin, int32_t blk_end, void *kbar, float *e_blk,
                              void *stream);
 
+/* Write the newest token of every row into the block-unit KV buffer `kv`
+ * (device memory or the device alias of pinned host memory; kv_row_blocks
+ * blocks per row): token slot pos (0..S-1) of block `block` receives
+ * k_new[row][D] as row pos of the K tile and v_new[row][D] as column pos of
+ * the V^T tile in its stored token order. k_new and v_new are [rows][D] in the
+ * KV dtype, rows = batch * n_kv_heads. This is the KV-cache write the
+ * decode step assumes (the pages keep the cache in block-sized units;
+ * "2. System: NOSI", Optimized Memory Layout): with the newest-block buffer
+ * as `kv`, an offloaded cache takes new tokens on the GPU and a completed
+ * block goes to host memory with nosa_fetch_blocks (source: the newest-block
+ * buffer, destination: the host KV). Invalid arguments (pos or block out of
+ * range, NULL pointers) return NOSA_ERR_INVALID_ARGUMENT before any launch. */
+nosa_status nosa_append_tokens(const nosa_shape *shape, const void *k_new, const void *v_new,
+                               int32_t pos, void *kv, int64_t kv_row_blocks, int32_t block,
+                               void *stream);
+
 /* Query-aware block scores for candidates 0 .. n_cand-1 of every row:
  * s_q[r][j] = sum over the G heads of the row of max over sub-blocks i of
  * scale * q_h . kbar[j,i] (Methodology, "Dual-Selection Mechanism" and

@@ -41,18 +41,25 @@ class GpuInputs:
     nb: int
     e_tok: torch.Tensor   # [rows, n_max] float32
     q: torch.Tensor       # [T, batch, n_q_heads, D]
+    k_new: torch.Tensor = None  # [T, rows, D]: token context + t of every row (prefix_only)
+    v_new: torch.Tensor = None
 
 
-def _row_blocks(w: Workload, layer: int, r: int, nb: int) -> np.ndarray:
+def _row_blocks(w: Workload, layer: int, r: int, nb: int, n_tokens: int | None = None) -> np.ndarray:
+    """Block-unit KV of one row; with n_tokens, only its first n_tokens tokens."""
     b, g = divmod(r, w.n_kv_heads)
     slab = layer % w.kv_slabs
     K = storage(synth.keys_row(w, slab, b, g), w)
     V = storage(synth.values_row(w, slab, b, g), w)
+    if n_tokens is not None:
+        K, V = K[:n_tokens], V[:n_tokens]
     return pack_blocks(K, V, nb)
 
 
 def upload(w: Workload, layer: int = 0, ov: Overrides | None = None, steps: int | None = None,
-           device="cuda", workers: int = 16) -> GpuInputs:
+           device="cuda", workers: int = 16, prefix_only: bool = False) -> GpuInputs:
+    """Seeded inputs on the GPU. prefix_only: the KV holds the context tokens
+    only, and each step's token comes as k_new[t] / v_new[t] [rows][D]."""
     T = w.steps if steps is None else steps
     nb = w.nb_max
     BE = 2 * 64 * w.head_dim
@@ -63,7 +70,7 @@ def upload(w: Workload, layer: int = 0, ov: Overrides | None = None, steps: int 
         view = buf.array(np.float32 if w.dtype == "f32" else np.uint16, (rows, nb, BE))
 
         def fill(r):
-            view[r] = _row_blocks(w, layer, r, nb)
+            view[r] = _row_blocks(w, layer, r, nb, w.context if prefix_only else None)
         synth.parallel_map(fill, range(rows), workers)
         kv, kv_ptr = buf, buf.dev
     else:
@@ -72,7 +79,9 @@ def upload(w: Workload, layer: int = 0, ov: Overrides | None = None, steps: int 
         chunk = max(1, workers)
         for r0 in range(0, rows, chunk):
             rr = list(range(r0, min(rows, r0 + chunk)))
-            parts = synth.parallel_map(lambda r: _row_blocks(w, layer, r, nb), rr, workers)
+            parts = synth.parallel_map(
+                lambda r: _row_blocks(w, layer, r, nb, w.context if prefix_only else None), rr,
+                workers)
             for r, p in zip(rr, parts):
                 kv[r].copy_(to_device(p, w, device))
         kv_ptr = kv
@@ -83,7 +92,18 @@ def upload(w: Workload, layer: int = 0, ov: Overrides | None = None, steps: int 
     qs = synth.parallel_map(lambda t: storage(synth.queries_step(w, layer, t, ov), w), range(T),
                             workers)
     q = to_device(np.stack(qs), w, device)
-    return GpuInputs(w, kv, kv_ptr, nb, e_tok, q)
+    inp = GpuInputs(w, kv, kv_ptr, nb, e_tok, q)
+    if prefix_only:
+        def new_tokens(r):
+            b, g = divmod(r, w.n_kv_heads)
+            slab = layer % w.kv_slabs
+            lo, hi = w.context, w.context + T
+            return (storage(synth.keys_row(w, slab, b, g)[lo:hi], w),
+                    storage(synth.values_row(w, slab, b, g)[lo:hi], w))
+        kvn = synth.parallel_map(new_tokens, range(rows), workers)
+        inp.k_new = to_device(np.ascontiguousarray(np.stack([k for k, _ in kvn], 1)), w, device)
+        inp.v_new = to_device(np.ascontiguousarray(np.stack([v for _, v in kvn], 1)), w, device)
+    return inp
 
 
 def upload_slabs(w: Workload, workers: int = 16) -> list:
@@ -117,13 +137,14 @@ def upload_layer(w: Workload, layer: int, kv, ov: Overrides | None, steps: int,
 
 
 def make_layer(w: Workload, inp: GpuInputs, decode_kernel=L.NOSA_DECODE_AUTO,
-               fuse_select_swap=True, overlap=False, fuse_score=None) -> DecodeLayer:
+               fuse_select_swap=True, overlap=False, fuse_score=None,
+               device_append=False) -> DecodeLayer:
     return DecodeLayer(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
                        head_dim=w.head_dim, k_e=w.k_e, k_q=w.k_q, max_blocks=inp.nb,
                        dtype=nosa_dtype(w), kv=inp.kv_ptr, kv_row_blocks=inp.nb,
                        e_tok=inp.e_tok, offload=w.offload, decode_kernel=decode_kernel,
                        fuse_select_swap=fuse_select_swap, fuse_score=fuse_score,
-                       overlap=overlap)
+                       overlap=overlap, device_append=device_append)
 
 
 def bits_to_list(words: np.ndarray) -> list:
@@ -154,14 +175,21 @@ def snapshot(layer: DecodeLayer, w: Workload) -> dict:
 def run(w: Workload, inp: GpuInputs, steps, layer: DecodeLayer | None = None,
         collect=None, swap=True, decode_kernel=L.NOSA_DECODE_AUTO, fuse_select_swap=True,
         overlap=False, fuse_score=None):
-    """Run steps 0..max(steps) in order; snapshot the steps listed in ``collect``."""
-    layer = layer or make_layer(w, inp, decode_kernel, fuse_select_swap, overlap, fuse_score)
+    """Run steps 0..max(steps) in order; snapshot the steps listed in ``collect``.
+    Inputs uploaded with prefix_only feed each step's token through the
+    device-side append."""
+    append = inp.k_new is not None
+    layer = layer or make_layer(w, inp, decode_kernel, fuse_select_swap, overlap, fuse_score,
+                                device_append=append)
     T = max(steps) + 1
     collect = set(steps if collect is None else collect)
     layer.start(w.n_tokens(0))
     res = {}
     for t in range(T):
-        layer.step(inp.q[t], w.n_tokens(t), swap=swap)
+        if append:
+            layer.step(inp.q[t], w.n_tokens(t), swap=swap, k_new=inp.k_new[t], v_new=inp.v_new[t])
+        else:
+            layer.step(inp.q[t], w.n_tokens(t), swap=swap)
         if t in collect:
             res[t] = snapshot(layer, w)
     torch.cuda.synchronize()

@@ -93,6 +93,11 @@ def test_invalid_pointers_and_steps_rejected():
     part = [16] * 6 + [16, 16, 16, None, 16, 16]
     assert lib.nosa_score_select(ctypes.byref(sh), 16, 16, 16, ctypes.byref(ok_step), *part,
                                  None) == 1
+    # append: token slot and block out of range, null buffer
+    assert lib.nosa_append_tokens(ctypes.byref(sh), 16, 16, 64, 16, 4, 0, None) == 1
+    assert lib.nosa_append_tokens(ctypes.byref(sh), 16, 16, 3, 16, 4, 4, None) == 1
+    assert lib.nosa_append_tokens(ctypes.byref(sh), 16, 16, -1, 16, 4, 0, None) == 1
+    assert lib.nosa_append_tokens(ctypes.byref(sh), 16, 16, 3, None, 4, 0, None) == 1
     # a step beyond the block capacity
     big = L.make_step(64 * 64 + 1, -1)
     assert lib.nosa_score_blocks(ctypes.byref(sh), 16, 16, ctypes.byref(big), 16, None) == 1

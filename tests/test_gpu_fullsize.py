@@ -62,6 +62,36 @@ def test_fullsize_offload_128k_budget_splits(k_e):
     _fullsize(w.name, rows=[0, 77, 127], steps=66, w=w)
 
 
+def test_fullsize_offload_128k_device_append():
+    """The 128k offload shape with the host KV holding the context only: each
+    step's token is appended on the GPU and the block completed at step 63 is
+    written back to host memory; sampled rows match the oracle at every step
+    and the written-back block matches the tokens."""
+    from harness import row_kv
+    gh = _gpu()
+    w = synth.WORKLOADS["offload_1layer_128k"]
+    steps, rows = 66, [0, 77, 127]
+    tr = oracle_trace(w, rows=rows, steps=list(range(steps)))
+    inp = gh.upload(w, ov=tr.ov, steps=steps, prefix_only=True)
+    layer, res = gh.run(w, inp, list(range(steps)))
+    for t in range(steps):
+        for r in rows:
+            _compare_step(w, tr, t, r, res[t])
+    D, j = w.head_dim, w.n_cand(0)
+    assert w.n_cand(steps - 1) == j + 1
+    host = inp.kv.array(np.uint16, (w.rows, inp.nb, 2 * 64 * D))
+    vt = np.array([32 * (p // 32) + 16 * ((p % 8) // 4) + 4 * ((p % 32) // 8) + p % 4
+                   for p in range(64)])
+    for r in range(w.rows):
+        b, g = divmod(r, w.n_kv_heads)
+        K, V = row_kv(w, 0, b, g)
+        np.testing.assert_array_equal(host[r, j, :64 * D].reshape(64, D),
+                                      synth.bf16_bits(K[64 * j:64 * j + 64]), err_msg=f"row {r} K")
+        np.testing.assert_array_equal(host[r, j, 64 * D:].reshape(D, 64),
+                                      synth.bf16_bits(V[64 * j + vt]).T, err_msg=f"row {r} V")
+    inp.kv.free()
+
+
 def test_fullsize_offload_8b_32layer_32k():
     """32 layers x batch 64 x 8 KV heads, all five stages per layer per step,
     steps 0..65 (a block completes at step 64); sampled layers and rows are

@@ -117,6 +117,47 @@ def test_parity_valu_kernel_bf16(name):
             _compare_step(w, tr, t, r, res[t])
 
 
+def _vt_token_at(pos: int) -> int:
+    # stored V^T token order (the layout include/nosa.h documents)
+    return 32 * (pos // 32) + 16 * ((pos % 8) // 4) + 4 * ((pos % 32) // 8) + pos % 4
+
+
+@pytest.mark.parametrize("name", ["small_f32", "small_bf16", "small_offload"])
+def test_parity_device_append(name):
+    """The KV holds the context only; every step's token enters on the GPU
+    through nosa_append_tokens. Offloaded, a block completed during the run is
+    written back to host memory (and fetched from there when selected), so the
+    host bytes are checked against the tokens as well."""
+    from harness import row_kv
+    gh = _gpu()
+    w = synth.WORKLOADS[name]
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov, prefix_only=True)
+    layer, res = gh.run(w, inp, list(range(w.steps)))
+    for t in range(w.steps):
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, res[t])
+    c0, c1 = w.n_cand(0), w.n_cand(w.steps - 1)
+    assert c1 > c0, "the run completes a block"
+    if not w.offload:
+        return
+    D = w.head_dim
+    host = inp.kv.array(np.uint16, (w.rows, inp.nb, 2 * 64 * D))
+    pos = np.arange(64)
+    vt = np.array([_vt_token_at(p) for p in pos])
+    for r in range(w.rows):
+        b, g = divmod(r, w.n_kv_heads)
+        K, V = row_kv(w, 0, b, g)
+        for j in range(c0, c1):
+            blk = host[r, j]
+            k_tile = blk[:64 * D].reshape(64, D)
+            v_tile = blk[64 * D:].reshape(D, 64)
+            np.testing.assert_array_equal(k_tile, synth.bf16_bits(K[64 * j:64 * j + 64]),
+                                          err_msg=f"row {r} block {j} K")
+            np.testing.assert_array_equal(v_tile, synth.bf16_bits(V[64 * j + vt]).T,
+                                          err_msg=f"row {r} block {j} V")
+
+
 @pytest.mark.parametrize("name", ["small_bf16", "small_offload"])
 def test_parity_separate_score_kernel(name):
     """nosa_score_blocks then nosa_select_swap as two launches (the pipeline

@@ -30,7 +30,7 @@ NOSA_DECODE_MFMA = 2
 
 EXPORTS = (
     "nosa_pool_blocks", "nosa_score_blocks", "nosa_select", "nosa_select_swap", "nosa_swap_diff",
-    "nosa_select_parts", "nosa_score_select", "nosa_fetch_blocks", "nosa_decode_workspace_size", "nosa_decode_chunks",
+    "nosa_select_parts", "nosa_score_select", "nosa_fetch_blocks", "nosa_append_tokens", "nosa_decode_workspace_size", "nosa_decode_chunks",
     "nosa_sparse_decode", "nosa_decode_partial", "nosa_decode_combine",
     "nosa_host_alloc", "nosa_host_free", "nosa_status_string", "nosa_last_error",
     "nosa_version",
@@ -72,6 +72,7 @@ def _load() -> ctypes.CDLL:
         "nosa_select_parts": [SH, P, P, ST] + [P] * 15 + [P],
         "nosa_score_select": [SH, P, P, P, ST] + [P] * 12 + [P],
         "nosa_decode_chunks": [SH, I32, I32],
+        "nosa_append_tokens": [SH, P, P, I32, P, I64, I32, P],
         "nosa_decode_partial": [SH, P, P, I64, I32, P, P, I32, I32, I32, P, I64, ST, P, I64, P, SZ,
                                 I32, P],
         "nosa_decode_combine": [SH, I32, P, P, SZ, P],
@@ -212,6 +213,11 @@ def nosa_fetch_blocks(shape, src_kv, src_row_blocks, fetch_block, fetch_slot, n_
     _chk("nosa_fetch_blocks", _L.nosa_fetch_blocks(
         ctypes.byref(shape), _p(src_kv), src_row_blocks, _p(fetch_block), _p(fetch_slot),
         _p(n_fetch), max_fetch, _p(dst_kv), dst_row_blocks, _s(stream)))
+
+
+def nosa_append_tokens(shape, k_new, v_new, pos, kv, kv_row_blocks, block, stream=None):
+    _chk("nosa_append_tokens", _L.nosa_append_tokens(
+        ctypes.byref(shape), _p(k_new), _p(v_new), pos, _p(kv), kv_row_blocks, block, _s(stream)))
 
 
 def nosa_decode_workspace_size(shape) -> int:

@@ -319,6 +319,23 @@ nosa_status nosa_fetch_blocks(const nosa_shape *shape, const void *src_kv, int64
                                    max_fetch, dst_kv, dst_row_blocks, (hipStream_t)stream));
 }
 
+nosa_status nosa_append_tokens(const nosa_shape *shape, const void *k_new, const void *v_new,
+                               int32_t pos, void *kv, int64_t kv_row_blocks, int32_t block,
+                               void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!k_new || !v_new || !kv) return NOSA_ERR_INVALID_ARGUMENT;
+    if (pos < 0 || pos >= dm.S || kv_row_blocks <= 0 || block < 0 || block >= kv_row_blocks)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        constexpr int D = decltype(dc)::value;
+        return hip_status(launch_append<T, D>(dm, k_new, v_new, pos, kv, kv_row_blocks, block,
+                                              (hipStream_t)stream));
+    });
+}
+
 size_t nosa_decode_workspace_size(const nosa_shape *shape) {
     Dims dm;
     if (make_dims(shape, &dm) != NOSA_OK) return 0;

@@ -64,6 +64,22 @@ template <> struct Vec8<float> {
     }
 };
 
+// Token order of the stored V^T tile: position pos (0..63) of a V^T row
+// holds token vt_token_at(pos); within each 32-token half, positions
+// 8g..8g+7 hold tokens 4g..4g+3 and 16+4g..16+4g+3. vt_pos_of is the inverse.
+__host__ __device__ constexpr int vt_token_at(int pos) {
+    return 32 * (pos / 32) + 16 * ((pos % 8) / 4) + 4 * ((pos % 32) / 8) + pos % 4;
+}
+__host__ __device__ constexpr int vt_pos_of(int tok) {
+    return 32 * (tok / 32) + 8 * ((tok % 16) / 4) + 4 * ((tok % 32) / 16) + tok % 4;
+}
+constexpr bool vt_order_is_inverse() {
+    for (int p = 0; p < 64; ++p)
+        if (vt_pos_of(vt_token_at(p)) != p) return false;
+    return true;
+}
+static_assert(vt_order_is_inverse(), "vt_pos_of inverts vt_token_at");
+
 // Total order used by every selection: a higher score ranks first, an equal
 // score ranks the lower block id first. Keys compare as unsigned integers.
 __device__ __forceinline__ uint32_t orderable(float f) {

@@ -41,6 +41,10 @@ hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, 
 hipError_t launch_swap(const Dims &dm, const int32_t *sel, const int32_t *n_sel,
                        const uint32_t *sel_bits, const SwapPtrs &swap, hipStream_t st);
 
+template <typename T, int D>
+hipError_t launch_append(const Dims &dm, const void *k_new, const void *v_new, int pos, void *kv,
+                         int64_t kv_row_blocks, int block, hipStream_t st);
+
 hipError_t launch_fetch(const Dims &dm, const void *src, int64_t src_row_blocks,
                         const int32_t *fblk, const int32_t *fslot, const int32_t *nfetch,
                         int max_fetch, void *dst, int64_t dst_row_blocks, hipStream_t st);

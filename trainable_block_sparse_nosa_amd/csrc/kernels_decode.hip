@@ -34,12 +34,6 @@ namespace nosa {
 constexpr int WAVES = 8;
 constexpr int MFMA_TARGET_WGS = 256;
 
-// Position of token `tok` (0..63) inside a row of the stored V^T tile: within
-// each 32-token half, positions 8g..8g+7 hold tokens 4g..4g+3, 16+4g..16+4g+3.
-__host__ __device__ constexpr int vt_token_at(int pos) {
-    return 32 * (pos / 32) + 16 * ((pos % 8) / 4) + 4 * ((pos % 32) / 8) + pos % 4;
-}
-
 DecodePlan decode_plan(const Dims &dm, int kind, int entries) {
     DecodePlan p;
     if (entries <= 0) {

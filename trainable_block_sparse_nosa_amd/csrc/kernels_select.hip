@@ -797,6 +797,7 @@ fetch_kernel(const u32x4 *__restrict__ src, int64_t src_row_blocks, const int32_
     if (i >= nfetch[r]) return;
     const int b = fblk[(int64_t)r * k + i];
     const int s = fslot[(int64_t)r * k + i];
+    if (b < 0 || b >= src_row_blocks || s < 0 || s >= dst_row_blocks) return;  // not a block
     const u32x4 *sp = src + ((int64_t)r * src_row_blocks + b) * vec_per_block;
     u32x4 *dp = dst + ((int64_t)r * dst_row_blocks + s) * vec_per_block;
     for (int base = 0; base < vec_per_block; base += 8 * 256) {
@@ -812,6 +813,23 @@ fetch_kernel(const u32x4 *__restrict__ src, int64_t src_row_blocks, const int32_
             if (idx < vec_per_block) dp[idx] = v[u];
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Append: the newest token of every row enters token slot `pos` of block
+// `block` of a KV buffer: its key as row pos of the K tile, its value as
+// column vt_pos_of(pos) of the V^T tile. One workgroup per row, thread d
+// writes dimension d.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(D)
+append_kernel(const T *__restrict__ k_new, const T *__restrict__ v_new, int pos,
+              T *__restrict__ kv, int64_t kv_row_blocks, int block) {
+    constexpr int S = 64;
+    const int r = blockIdx.x, d = threadIdx.x;
+    T *blk = kv + ((int64_t)r * kv_row_blocks + block) * (int64_t)(2 * S * D);
+    blk[pos * D + d] = k_new[(int64_t)r * D + d];
+    blk[S * D + d * S + vt_pos_of(pos)] = v_new[(int64_t)r * D + d];
 }
 
 // ---------------------------------------------------------------------------
@@ -901,6 +919,21 @@ hipError_t launch_swap(const Dims &dm, const int32_t *sel, const int32_t *n_sel,
     hipLaunchKernelGGL(swap_kernel, dim3(dm.rows), dim3(64), 0, st, dm, sel_bits, sw);
     return hipGetLastError();
 }
+
+template <typename T, int D>
+hipError_t launch_append(const Dims &dm, const void *k_new, const void *v_new, int pos, void *kv,
+                         int64_t kv_row_blocks, int block, hipStream_t st) {
+    hipLaunchKernelGGL((append_kernel<T, D>), dim3(dm.rows), dim3(D), 0, st,
+                       static_cast<const T *>(k_new), static_cast<const T *>(v_new), pos,
+                       static_cast<T *>(kv), kv_row_blocks, block);
+    return hipGetLastError();
+}
+template hipError_t launch_append<float, 64>(const Dims &, const void *, const void *, int, void *,
+                                            int64_t, int, hipStream_t);
+template hipError_t launch_append<bf16_t, 64>(const Dims &, const void *, const void *, int,
+                                             void *, int64_t, int, hipStream_t);
+template hipError_t launch_append<bf16_t, 128>(const Dims &, const void *, const void *, int,
+                                              void *, int64_t, int, hipStream_t);
 
 hipError_t launch_fetch(const Dims &dm, const void *src, int64_t src_row_blocks,
                         const int32_t *fblk, const int32_t *fslot, const int32_t *nfetch,

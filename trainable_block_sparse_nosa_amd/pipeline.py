@@ -67,7 +67,7 @@ class DecodeLayer:
     def __init__(self, *, batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks, dtype,
                  kv, kv_row_blocks, e_tok, offload=False, decode_kernel=L.NOSA_DECODE_AUTO,
                  scale=0.0, device="cuda", fuse_select_swap=True, fuse_score=None,
-                 overlap=False):
+                 overlap=False, device_append=False):
         self.shape = L.make_shape(batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks,
                                   dtype, decode_kernel=decode_kernel, scale=scale)
         self.rows = batch * n_kv_heads
@@ -140,6 +140,17 @@ class DecodeLayer:
             self.step_done = torch.cuda.Event()
             self.side_done = torch.cuda.Event()
             self.parity = 0
+        # device_append: each step's token arrives as k_new / v_new [rows][D]
+        # on the GPU and is written into the newest block (the newest-block
+        # buffer when offloaded); with offloaded KV a completed block is then
+        # written back to host memory, so the host KV needs only the prefill
+        self.device_append = device_append
+        if device_append and offload:
+            # a one-entry fetch list per row ([rows][k] like every fetch list;
+            # column 0 used): source block 0 of the buffer, destination block
+            self.wb_fb = torch.zeros(R, k, dtype=i32, device=dev)
+            self.wb_fs = torch.zeros(R, k, dtype=i32, device=dev)
+            self.wb_nf = torch.ones(R, dtype=i32, device=dev)
         self.n_cand_prev = -1
         self.n_tokens = 0
         # optional callable(stage_name, fn, *args): runs fn(*args); a caller
@@ -158,8 +169,17 @@ class DecodeLayer:
         base = self.kv if isinstance(self.kv, int) else self.kv.data_ptr()
         return base + block * self.block_elems * self.elem_bytes
 
+    @staticmethod
+    def _fill(t: torch.Tensor, value: int, stream=None):
+        """t.fill_(value), ordered on `stream` (a torch stream or None)."""
+        if isinstance(stream, torch.cuda.Stream):
+            with torch.cuda.stream(stream):
+                t.fill_(value)
+        else:
+            t.fill_(value)
+
     def _load_cur(self, block: int, stream=None):
-        self.cur_fb[:, 0].fill_(block)
+        self._fill(self.cur_fb[:, 0], block, stream)
         self._run("fetch_newest", L.nosa_fetch_blocks, self.shape, self.kv, self.kv_row_blocks,
                   self.cur_fb, self.cur_fs, self.cur_nf, 1, self.cur, 1, stream)
 
@@ -177,21 +197,40 @@ class DecodeLayer:
         self.n_cand_prev = -1
         self.pooled = c0
 
-    def step(self, q: torch.Tensor, n_tokens: int, stream=None, swap: bool = True) -> torch.Tensor:
-        """One decode step at n_tokens tokens (the newest appended by this step)."""
+    def step(self, q: torch.Tensor, n_tokens: int, stream=None, swap: bool = True,
+             k_new=None, v_new=None) -> torch.Tensor:
+        """One decode step at n_tokens tokens (the newest appended by this step;
+        with device_append, k_new / v_new [rows][D] carry it)."""
         c = (n_tokens - 1) // BLOCK
+        if self.device_append and (k_new is None or v_new is None):
+            raise ValueError("device_append needs the step's k_new and v_new")
         if c > self.pooled:
             if self.offload:
                 assert c == self.pooled + 1, "offloaded KV grows by one block per step"
                 # the completed block is the newest-block buffer's content
                 self._run("pool", L.nosa_pool_blocks, self.shape, self.cur, 1, 0, self.e_tok,
                           self.e_stride, self.pooled, c, self.kbar, self.e_blk, stream)
-                self._load_cur(c, stream)
+                if self.device_append:
+                    # write it back to host block c - 1; the buffer starts block c
+                    self._fill(self.wb_fs[:, 0], c - 1, stream)
+                    self._run("write_back", L.nosa_fetch_blocks, self.shape, self.cur, 1,
+                              self.wb_fb, self.wb_fs, self.wb_nf, 1, self.kv,
+                              self.kv_row_blocks, stream)
+                else:
+                    self._load_cur(c, stream)
             else:
                 self._run("pool", L.nosa_pool_blocks, self.shape, self.kv, self.kv_row_blocks,
                           self.pooled, self.e_tok, self.e_stride, self.pooled, c, self.kbar,
                           self.e_blk, stream)
             self.pooled = c
+        if self.device_append:
+            pos = (n_tokens - 1) % BLOCK
+            if self.offload:
+                self._run("append", L.nosa_append_tokens, self.shape, k_new, v_new, pos, self.cur,
+                          1, 0, stream)
+            else:
+                self._run("append", L.nosa_append_tokens, self.shape, k_new, v_new, pos, self.kv,
+                          self.kv_row_blocks, c, stream)
         st = L.make_step(n_tokens, self.n_cand_prev)
         if self.overlap:
             self._step_overlap(q, n_tokens, c, st, stream, swap)
