@@ -55,6 +55,8 @@ def lib():
             L.oracle_pool_keys.argtypes = [_f, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, _d]
             L.oracle_pool_keys.restype = None
+            L.oracle_evict_logit.argtypes = [_f, _f, ctypes.c_int, ctypes.c_double]
+            L.oracle_evict_logit.restype = ctypes.c_double
             L.oracle_block_evict.argtypes = [_f, ctypes.c_int, ctypes.c_int, ctypes.c_int]
             L.oracle_block_evict.restype = ctypes.c_double
             L.oracle_block_score.argtypes = [_f, ctypes.c_int, ctypes.c_int, _f, ctypes.c_int,
@@ -110,6 +112,26 @@ def pool_keys(K: np.ndarray, block: int, sub: int, j: int, pooled_bf16: bool = F
     out = np.zeros((block // sub, D), dtype=np.float64)
     lib().oracle_pool_keys(_pf(K), D, block, sub, j, int(pooled_bf16), _pd(out))
     return out
+
+
+def evict_logit(x: np.ndarray, w: np.ndarray, bias: float = 0.0) -> float:
+    """Eviction-head logit of one token for one KV head: x . w + bias (double)."""
+    x, w = _f32(x), _f32(w)
+    assert x.shape == w.shape and x.ndim == 1
+    return lib().oracle_evict_logit(_pf(x), _pf(w), x.shape[0], float(bias))
+
+
+def qkv_split(qkv: np.ndarray, n_q_heads: int, n_kv_heads: int, head_dim: int):
+    """Split one token's fused projection output [(Hq + 2 Hkv) * D] into
+    q [Hq, D], k [Hkv, D], v [Hkv, D]: the query heads first, then the keys,
+    then the values (reading of the pages' QKV split)."""
+    D = head_dim
+    a = np.asarray(qkv)
+    assert a.shape == ((n_q_heads + 2 * n_kv_heads) * D,)
+    q = a[:n_q_heads * D].reshape(n_q_heads, D)
+    k = a[n_q_heads * D:(n_q_heads + n_kv_heads) * D].reshape(n_kv_heads, D)
+    v = a[(n_q_heads + n_kv_heads) * D:].reshape(n_kv_heads, D)
+    return q, k, v
 
 
 def block_evict(e: np.ndarray, block: int, sub: int, j: int) -> float:

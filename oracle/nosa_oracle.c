@@ -83,6 +83,19 @@ void oracle_pool_keys(const float *K, int D, int block, int sub, int j, int pool
     }
 }
 
+/* Eviction head of one KV head for one token (Methodology, "Dual-Selection
+   Mechanism": a head that scores tokens independently of the query; "ED-DMA":
+   the score stays pre-exponential). Reading taken, the pages giving no form:
+   a linear head on the token's hidden state, e = x . w + bias, one logit per
+   KV head. Summed in double. */
+double oracle_evict_logit(const float *x, const float *w, int hidden, double bias)
+{
+    double s = 0.0;
+    for (int i = 0; i < hidden; ++i)
+        s += (double)x[i] * (double)w[i];
+    return s + bias;
+}
+
 /* Pooled eviction score of block j: max over its sub-blocks of the mean of
    the per-token (pre-exponential) eviction scores. */
 double oracle_block_evict(const float *e, int block, int sub, int j)

@@ -155,6 +155,31 @@ def test_pool_keys_bf16_rounding_hand_case():
     assert oracle.block_score(-q, K, 64, 16, 0, 1.0, pooled_bf16=True) == -1.0
 
 
+def test_evict_logit_closed_forms():
+    """The eviction head is linear: one-hot inputs pick single weights, the
+    bias adds, scaling the input scales the logit, and a hand-made case."""
+    rng = np.random.default_rng(31)
+    w = rng.normal(size=64).astype(np.float32)
+    for i in (0, 17, 63):
+        x = np.zeros(64, np.float32)
+        x[i] = 1.0
+        assert oracle.evict_logit(x, w) == float(w[i])
+        assert oracle.evict_logit(x, w, -4.0) == float(w[i]) - 4.0
+    x = rng.normal(size=64).astype(np.float32)
+    assert oracle.evict_logit(2 * x, w) == 2 * oracle.evict_logit(x, w)
+    assert oracle.evict_logit(np.array([1, 2, 3], np.float32),
+                              np.array([0.5, -1, 0.25], np.float32), 1.0) == 0.25
+
+
+def test_qkv_split_order():
+    """Query heads, then key heads, then value heads, each head_dim wide."""
+    Hq, Hkv, D = 4, 2, 3
+    a = np.arange((Hq + 2 * Hkv) * D, dtype=np.float32)
+    q, k, v = oracle.qkv_split(a, Hq, Hkv, D)
+    assert q.shape == (4, 3) and k.shape == (2, 3) and v.shape == (2, 3)
+    assert q[1, 2] == 5 and k[0, 0] == 12 and k[1, 2] == 17 and v[0, 0] == 18 and v[1, 2] == 23
+
+
 def test_pool_reduces_to_mean_when_sub_block_is_block():
     rng = np.random.default_rng(11)
     K = rng.normal(size=(256, 16)).astype(np.float32)
