@@ -54,6 +54,9 @@ def parse():
                     help="skip the locality ablation of the offload leg (budget splits "
                          "k_e + k_q = k with k_e = 32 and 0, and per-block / per-token "
                          "hipMemcpyAsync copies against the fetch kernel)")
+    ap.add_argument("--no-ingest", action="store_true",
+                    help="skip the leg that runs the workload with the fused ingest launch "
+                         "(QKV split, eviction head, KV append, pooling) in every step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 4 device-to-device copies of 512 MiB (a reference kernel "
                          "of known traffic for hardware byte counters)")
@@ -193,11 +196,74 @@ def setup(w, args, dev, device_append=False):
 
 
 def run_step(layer, q, new, t, n_tokens, stream):
-    """Step t of a layer built by setup."""
+    """Step t of a layer built by setup (new: None, (k_new, v_new), or
+    ("ingest", qkv, x) for a layer with an eviction head)."""
     if new is None:
         layer.step(q[t], n_tokens, stream)
+    elif new[0] == "ingest":
+        layer.step(None, n_tokens, stream, qkv=new[1][t], x=new[2][t])
     else:
         layer.step(q[t], n_tokens, stream, k_new=new[0][t], v_new=new[1][t])
+
+
+def ingest_leg(w, args, dev, stream, main_steps_per_s):
+    """The same workload with the step before the path fused in (one launch per
+    step: QKV split, eviction head, KV append, pooling of a completed block):
+    its launch time and the whole step's rate. Hidden states, the fused
+    projection output and the eviction head are synthetic (hidden = Hq * D)."""
+    import numpy as np
+    import torch
+    import synth
+    from trainable_block_sparse_nosa_amd import _lib as L
+    from trainable_block_sparse_nosa_amd.pipeline import DecodeLayer
+    T = args.warmup + args.steps
+    layer, q, kv, new = setup(w, args, dev, device_append=True)
+    H = synth.hidden_size(w)
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    x = torch.randn(T, w.batch, H, generator=g).to(torch.bfloat16).to(dev)
+    qkv = torch.cat([q.view(T, w.batch, -1), new[0].view(T, w.batch, -1),
+                     new[1].view(T, w.batch, -1)], dim=2).contiguous()
+    wt = torch.from_numpy(synth.bf16_bits(synth.evict_head_weights(w, 0)).view(np.int16)).to(dev)
+    wt = wt.view(torch.bfloat16)
+    lay = DecodeLayer(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                      head_dim=w.head_dim, k_e=w.k_e, k_q=w.k_q, max_blocks=w.nb_max,
+                      dtype=L.NOSA_BF16, kv=kv, kv_row_blocks=w.nb_max, e_tok=layer.e_tok,
+                      offload=False, evict_head=(wt, None))
+    del layer
+    elapsed, ev, _ = timed_run(lay, w, q, args, stream, event_stages=("ingest",),
+                               new=("ingest", qkv, x))
+    ms = [m for n, _, m in ev if n == "ingest"]
+    # the same work unfused, for comparison: torch copies for the split, the
+    # append launch, a torch matmul for the head and its scatter into e_tok,
+    # the pool launch when a block completes
+    Hq, Hkv, D = w.n_q_heads, w.n_kv_heads, w.head_dim
+    wf = wt.float()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):   # library handles and kernels loaded outside the timing
+        torch.matmul(x[0].float(), wf.t())
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for t in range(args.steps):
+        n = w.n_tokens(args.warmup + t)
+        tok = n - 1
+        row = qkv[args.warmup + t]
+        lay.q_buf.copy_(row[:, :Hq * D].view(w.batch, Hq, D))
+        kn = row[:, Hq * D:(Hq + Hkv) * D].contiguous()
+        vn = row[:, (Hq + Hkv) * D:].contiguous()
+        L.nosa_append_tokens(lay.shape, kn, vn, tok % 64, kv, w.nb_max, tok // 64, stream)
+        lay.e_tok[:, tok] = torch.matmul(x[args.warmup + t].float(), wf.t()).reshape(-1)
+        if tok % 64 == 63:
+            L.nosa_pool_blocks(lay.shape, kv, w.nb_max, tok // 64, lay.e_tok, lay.e_stride,
+                               tok // 64, tok // 64 + 1, lay.kbar, lay.e_blk, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    out = {"steps_per_s": args.steps / elapsed, "ingest_us_avg": sum(ms) / len(ms) * 1e3,
+           "ingest_us_max": max(ms) * 1e3, "hidden": H,
+           "unfused_us_per_step": e0.elapsed_time(e1) * 1e3 / args.steps,
+           "vs_main_steps_per_s": args.steps / elapsed / main_steps_per_s}
+    del lay, kv, q, new, qkv, x
+    torch.cuda.empty_cache()
+    return out
 
 
 ATTN_STAGES = ("decode", "decode_e", "decode_q")
@@ -494,6 +560,12 @@ def main():
         del layer, q, kv
         torch.cuda.empty_cache()
 
+    ingest = None
+    if not args.no_ingest and not w.offload and w.dtype == "bf16":
+        log(f"ingest leg: {w.name} with the fused ingest launch")
+        ingest = ingest_leg(w, args, dev, stream, steps_per_s)
+        log(f"ingest: {ingest['steps_per_s']:.1f} steps/s, launch {ingest['ingest_us_avg']:.1f} us")
+
     swap = None
     if args.offload_steps > 0 and not w.offload:
         log("offload leg: offload_1layer_128k")
@@ -537,6 +609,7 @@ def main():
         "overlap": overlapped,
         "gamma_mean": gamma_mean,
         "swap": swap,
+        "ingest": ingest,
         "cpu_baseline": cpu,
     }
     if stages:

@@ -144,6 +144,31 @@ nosa_status nosa_pool_blocks(const nosa_shape *shape, const void *kv, int64_t kv
                              int32_t blk_begin, int32_t blk_end, void *kbar, float *e_blk,
                              void *stream);
 
+/* The step before the path, fused in one launch (Methodology, "2. System:
+ * NOSI", Kernel Fusion: eviction head, QKV split and pooling together), for
+ * token n_tokens - 1 of every row:
+ *  - qkv [batch][(Hq + 2*Hkv) * D] (KV dtype) is one token's fused projection
+ *    output, query heads first, then key heads, then value heads: the query
+ *    heads go to q_out [batch][Hq][D]; the row's key and value go into token
+ *    slot (n_tokens - 1) % S of block `block` of the KV buffer `kv`, as
+ *    nosa_append_tokens writes them;
+ *  - the eviction head (Dual-Selection Mechanism, query-agnostic part; kept
+ *    pre-exponential, ED-DMA): e = x[b] . w_evict[g] + b_evict[g] with x
+ *    [batch][hidden] and w_evict [n_kv_heads][hidden] in the KV dtype,
+ *    b_evict float32 [n_kv_heads] or NULL (zero), summed in float32, goes to
+ *    e_tok[row][n_tokens - 1];
+ *  - when that token completes its block j = (n_tokens - 1) / S, the block is
+ *    pooled exactly as nosa_pool_blocks pools it (kbar, e_blk), the other
+ *    tokens of the block being read from `kv` and e_tok.
+ * qkv and q_out are 16-byte aligned (x and w_evict may be, for vector loads);
+ * e_row_stride >= n_tokens; block in [0, kv_row_blocks); j < max_blocks.
+ * Invalid arguments return NOSA_ERR_INVALID_ARGUMENT before any launch. */
+nosa_status nosa_ingest_tokens(const nosa_shape *shape, const void *qkv, const void *x,
+                               const void *w_evict, const float *b_evict, int32_t hidden,
+                               int32_t n_tokens, void *q_out, void *kv, int64_t kv_row_blocks,
+                               int32_t block, float *e_tok, int64_t e_row_stride, void *kbar,
+                               float *e_blk, void *stream);
+
 /* Write the newest token of every row into the block-unit KV buffer `kv`
  * (device memory or the device alias of pinned host memory; kv_row_blocks
  * blocks per row): token slot pos (0..S-1) of block `block` receives

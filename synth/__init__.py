@@ -25,6 +25,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "rne_bf16", "bf16_bits", "stream",
     "keys_row", "values_row", "evict_row", "queries_step", "Overrides",
+    "hidden_size", "hidden_step", "evict_head_weights",
 ]
 
 
@@ -227,6 +228,24 @@ def queries_step(w: Workload, layer: int, t: int, ov: Overrides | None = None) -
                 z[b, g * G:(g + 1) * G] = stream(w.seed, "Q", layer, t, b, g, a).standard_normal(
                     (G, w.head_dim), dtype=np.float32)
     return _to_dtype(z, w.dtype)
+
+
+def hidden_size(w: Workload) -> int:
+    """Model width of the synthetic eviction head's input: n_q_heads * head_dim."""
+    return w.n_q_heads * w.head_dim
+
+
+def hidden_step(w: Workload, layer: int, t: int) -> np.ndarray:
+    """Hidden states of decode step t's token: [batch, hidden] ~ N(0, 1), input dtype."""
+    z = stream(w.seed, "X", layer, t).standard_normal((w.batch, hidden_size(w)), dtype=np.float32)
+    return _to_dtype(z, w.dtype)
+
+
+def evict_head_weights(w: Workload, layer: int) -> np.ndarray:
+    """Synthetic eviction-head weights [n_kv_heads, hidden] ~ N(0, 1/hidden), input dtype."""
+    H = hidden_size(w)
+    z = stream(w.seed, "WE", layer).standard_normal((w.n_kv_heads, H), dtype=np.float32)
+    return _to_dtype(z * np.float32(1.0 / np.sqrt(H)), w.dtype)
 
 
 def parallel_map(fn, items, workers: int = 8):

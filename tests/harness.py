@@ -52,11 +52,14 @@ def boundary_ok(x: np.ndarray, k: int, rel: float = MARGIN_REL) -> tuple[bool, i
 
 
 def enforce_evict_margins(w: Workload, layer: int, b: int, g: int, steps, ov: Overrides,
-                          max_attempts: int = 64):
-    """Redraw eviction-logit blocks until every Gamma_e boundary has its margin."""
+                          max_attempts: int = 64, evict_tail=None):
+    """Redraw eviction-logit blocks until every Gamma_e boundary has its margin.
+    evict_tail(b, g, e) may replace the logits of the decoded tokens."""
     counts = sorted({w.n_cand(t) for t in range(max(steps) + 1)})
     for _ in range(max_attempts * max(1, len(counts))):
         e = synth.evict_row(w, layer, b, g, ov)
+        if evict_tail is not None:
+            e = evict_tail(b, g, e)
         cmax = counts[-1]
         E = np.array([oracle.block_evict(e, w.block, w.sub_block, j) for j in range(cmax)])
         bad = None
@@ -87,7 +90,8 @@ class OracleTrace:
 
 
 def oracle_trace(w: Workload, layer: int = 0, rows=None, steps=None, ov: Overrides | None = None,
-                 margins: bool = True, swaps: bool = True, workers: int = 8) -> OracleTrace:
+                 margins: bool = True, swaps: bool = True, workers: int = 8,
+                 evict_tail=None) -> OracleTrace:
     """Run the oracle on the given rows and steps, enforcing margins first.
 
     With ``swaps`` the steps must be 0..T-1 in order so the slot cache can be
@@ -104,8 +108,12 @@ def oracle_trace(w: Workload, layer: int = 0, rows=None, steps=None, ov: Overrid
     def one_row(r):
         b, g = divmod(r, w.n_kv_heads)
         K, V = row_kv(w, layer, b, g)
-        e = enforce_evict_margins(w, layer, b, g, steps, ov) if margins else \
-            synth.evict_row(w, layer, b, g, ov)
+        if margins:
+            e = enforce_evict_margins(w, layer, b, g, steps, ov, evict_tail=evict_tail)
+        else:
+            e = synth.evict_row(w, layer, b, g, ov)
+            if evict_tail is not None:
+                e = evict_tail(b, g, e)
         cache = oracle.SlotCache(w.k)
         kmax = float(np.sqrt(np.max(np.sum(K.astype(np.float64) ** 2, axis=1))))
         out_step, out_swap, out_scale = {}, {}, {}

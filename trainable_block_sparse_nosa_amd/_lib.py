@@ -30,7 +30,8 @@ NOSA_DECODE_MFMA = 2
 
 EXPORTS = (
     "nosa_pool_blocks", "nosa_score_blocks", "nosa_select", "nosa_select_swap", "nosa_swap_diff",
-    "nosa_select_parts", "nosa_score_select", "nosa_fetch_blocks", "nosa_append_tokens", "nosa_decode_workspace_size", "nosa_decode_chunks",
+    "nosa_select_parts", "nosa_score_select", "nosa_fetch_blocks", "nosa_append_tokens",
+    "nosa_ingest_tokens", "nosa_decode_workspace_size", "nosa_decode_chunks",
     "nosa_sparse_decode", "nosa_decode_partial", "nosa_decode_combine",
     "nosa_host_alloc", "nosa_host_free", "nosa_status_string", "nosa_last_error",
     "nosa_version",
@@ -73,6 +74,7 @@ def _load() -> ctypes.CDLL:
         "nosa_score_select": [SH, P, P, P, ST] + [P] * 12 + [P],
         "nosa_decode_chunks": [SH, I32, I32],
         "nosa_append_tokens": [SH, P, P, I32, P, I64, I32, P],
+        "nosa_ingest_tokens": [SH, P, P, P, P, I32, I32, P, P, I64, I32, P, I64, P, P, P],
         "nosa_decode_partial": [SH, P, P, I64, I32, P, P, I32, I32, I32, P, I64, ST, P, I64, P, SZ,
                                 I32, P],
         "nosa_decode_combine": [SH, I32, P, P, SZ, P],
@@ -218,6 +220,14 @@ def nosa_fetch_blocks(shape, src_kv, src_row_blocks, fetch_block, fetch_slot, n_
 def nosa_append_tokens(shape, k_new, v_new, pos, kv, kv_row_blocks, block, stream=None):
     _chk("nosa_append_tokens", _L.nosa_append_tokens(
         ctypes.byref(shape), _p(k_new), _p(v_new), pos, _p(kv), kv_row_blocks, block, _s(stream)))
+
+
+def nosa_ingest_tokens(shape, qkv, x, w_evict, b_evict, hidden, n_tokens, q_out, kv,
+                       kv_row_blocks, block, e_tok, e_row_stride, kbar, e_blk, stream=None):
+    _chk("nosa_ingest_tokens", _L.nosa_ingest_tokens(
+        ctypes.byref(shape), _p(qkv), _p(x), _p(w_evict), _p(b_evict), hidden, n_tokens,
+        _p(q_out), _p(kv), kv_row_blocks, block, _p(e_tok), e_row_stride, _p(kbar), _p(e_blk),
+        _s(stream)))
 
 
 def nosa_decode_workspace_size(shape) -> int:

@@ -319,6 +319,33 @@ nosa_status nosa_fetch_blocks(const nosa_shape *shape, const void *src_kv, int64
                                    max_fetch, dst_kv, dst_row_blocks, (hipStream_t)stream));
 }
 
+nosa_status nosa_ingest_tokens(const nosa_shape *shape, const void *qkv, const void *x,
+                               const void *w_evict, const float *b_evict, int32_t hidden,
+                               int32_t n_tokens, void *q_out, void *kv, int64_t kv_row_blocks,
+                               int32_t block, float *e_tok, int64_t e_row_stride, void *kbar,
+                               float *e_blk, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!qkv || !x || !w_evict || !q_out || !kv || !e_tok || !kbar || !e_blk)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    const int tok = n_tokens - 1;
+    if (((reinterpret_cast<uintptr_t>(qkv) | reinterpret_cast<uintptr_t>(q_out)) & 15) != 0)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (hidden <= 0 || n_tokens <= 0 || kv_row_blocks <= 0 || block < 0 ||
+        block >= kv_row_blocks || e_row_stride < n_tokens || tok / dm.S >= dm.max_blocks)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        constexpr int D = decltype(dc)::value;
+        return by_group(dm, [&](auto gc) -> nosa_status {
+            return hip_status(launch_ingest<T, D, decltype(gc)::value>(
+                dm, qkv, x, w_evict, b_evict, hidden, tok, q_out, kv, kv_row_blocks, block, e_tok,
+                e_row_stride, kbar, e_blk, (hipStream_t)stream));
+        });
+    });
+}
+
 nosa_status nosa_append_tokens(const nosa_shape *shape, const void *k_new, const void *v_new,
                                int32_t pos, void *kv, int64_t kv_row_blocks, int32_t block,
                                void *stream) {

@@ -41,6 +41,12 @@ hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, 
 hipError_t launch_swap(const Dims &dm, const int32_t *sel, const int32_t *n_sel,
                        const uint32_t *sel_bits, const SwapPtrs &swap, hipStream_t st);
 
+template <typename T, int D, int G>
+hipError_t launch_ingest(const Dims &dm, const void *qkv, const void *x, const void *w_e,
+                         const float *b_e, int hidden, int tok, void *q_out, void *kv,
+                         int64_t kv_row_blocks, int block, float *e_tok, int64_t e_stride,
+                         void *kbar, float *e_blk, hipStream_t st);
+
 template <typename T, int D>
 hipError_t launch_append(const Dims &dm, const void *k_new, const void *v_new, int pos, void *kv,
                          int64_t kv_row_blocks, int block, hipStream_t st);

@@ -39,6 +39,12 @@ template <> struct KbarVec<bf16_t> {
     }
 };
 
+// A 16-byte vector as floats (4 float32 or 8 bfloat16).
+template <typename T>
+__device__ __forceinline__ void unpack16(const u32x4 &v, float (&x)[16 / sizeof(T)]) {
+    KbarVec<T>::unpack(uint4{v.x, v.y, v.z, v.w}, x);
+}
+
 // Element offset of dimension vector dv of sub-block sb in row r.
 template <typename T, int D>
 __device__ __forceinline__ int64_t kbar_vec(const Dims &dm, int r, int sb, int dv) {
@@ -63,21 +69,27 @@ __device__ __forceinline__ bf16_t bf16_rne_from_double(double x) {
     return f2bf(f);
 }
 
-// Sub-block mean of 16 keys in the storage type: float32 keys sum in float32;
-// bfloat16 keys sum exactly in double (16 values with 8 significant bits) and
-// the exact mean is rounded once to bfloat16.
-template <typename T> __device__ __forceinline__ T pooled_mean(const T *k, int stride);
-template <> __device__ __forceinline__ float pooled_mean<float>(const float *k, int stride) {
-    float s = 0.f;
+// Sub-block mean of 16 keys in the storage type, key u from get(u): float32
+// keys sum in float32; bfloat16 keys sum exactly in double (16 values with 8
+// significant bits) and the exact mean is rounded once to bfloat16. Tokens
+// are summed in order, so every caller gets identical bits.
+template <typename T, typename Get>
+__device__ __forceinline__ T pooled_mean_of(Get get) {
+    if constexpr (std::is_same_v<T, float>) {
+        float s = 0.f;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) s += k[u * stride];
-    return s * (1.0f / 16);
+        for (int u = 0; u < 16; ++u) s += get(u);
+        return s * (1.0f / 16);
+    } else {
+        double s = 0.0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s += (double)bf2f(get(u));
+        return bf16_rne_from_double(s * (1.0 / 16));
+    }
 }
-template <> __device__ __forceinline__ bf16_t pooled_mean<bf16_t>(const bf16_t *k, int stride) {
-    double s = 0.0;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) s += (double)bf2f(k[u * stride]);
-    return bf16_rne_from_double(s * (1.0 / 16));
+template <typename T>
+__device__ __forceinline__ T pooled_mean(const T *k, int stride) {
+    return pooled_mean_of<T>([&](int u) { return k[u * stride]; });
 }
 
 // ---------------------------------------------------------------------------
@@ -816,6 +828,106 @@ fetch_kernel(const u32x4 *__restrict__ src, int64_t src_row_blocks, const int32_
 }
 
 // ---------------------------------------------------------------------------
+// Ingest: the step before the path, fused (NOSI's kernel-fusion bullet: the
+// eviction head, the QKV split and pooling in one launch). One workgroup per
+// row, for the token `tok` of every row:
+//  * split: the row's G query heads of the fused projection output go to
+//    q_out; its key and value heads go into token slot tok % 64 of a block of
+//    the block-unit KV buffer (K row, V^T column in the stored order);
+//  * eviction head: e = x . w_g + b_g (float32 sum), written to e_tok;
+//  * when the token completes its block: the block's sub-block key means
+//    (pooled_mean_of, the same arithmetic and order as pool_kernel) and its
+//    max-of-means eviction score, with the new token taken from LDS and the
+//    block's other 63 tokens from memory.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256)
+ingest_kernel(Dims dm, const T *__restrict__ qkv, const T *__restrict__ x,
+              const T *__restrict__ w_e, const float *__restrict__ b_e, int hidden, int tok,
+              T *__restrict__ q_out, T *__restrict__ kv, int64_t kv_row_blocks, int block,
+              float *__restrict__ e_tok, int64_t e_stride, T *__restrict__ kbar,
+              float *__restrict__ e_blk) {
+    constexpr int S = 64, M = 4, V = KbarVec<T>::V, NW = 256 / 64;
+    __shared__ T knew[D];
+    __shared__ float red[NW];
+    __shared__ float e_new, emean[M];
+    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = r / dm.Hkv, g = r % dm.Hkv;
+    const int pos = tok % S, j = tok / S;
+    const T *src = qkv + (int64_t)b * (dm.Hq + 2 * dm.Hkv) * D;
+    T *qo = q_out + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
+    {
+        // the row's G query heads: G * D elements, 16-byte vectors (D * sizeof(T)
+        // is a multiple of 16, and so are the row and head offsets)
+        constexpr int EV = 16 / sizeof(T);
+        const u32x4 *qs = reinterpret_cast<const u32x4 *>(src + (int64_t)g * G * D);
+        u32x4 *qd = reinterpret_cast<u32x4 *>(qo);
+        for (int p = tid; p < G * D / EV; p += blockDim.x) qd[p] = qs[p];
+    }
+    T *blk = kv + ((int64_t)r * kv_row_blocks + block) * (int64_t)(2 * S * D);
+    for (int d = tid; d < D; d += blockDim.x) {
+        const T kval = src[(int64_t)(dm.Hq + g) * D + d];
+        const T vval = src[(int64_t)(dm.Hq + dm.Hkv + g) * D + d];
+        blk[pos * D + d] = kval;
+        blk[S * D + d * S + vt_pos_of(pos)] = vval;
+        knew[d] = kval;
+    }
+    // eviction head: 16-byte vectors when the rows allow them, else elements
+    const T *xr = x + (int64_t)b * hidden;
+    const T *wr = w_e + (int64_t)g * hidden;
+    float acc = 0.f;
+    constexpr int EV = 16 / sizeof(T);
+    if (hidden % EV == 0 && ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w_e)) & 15) == 0) {
+        const u32x4 *xv = reinterpret_cast<const u32x4 *>(xr);
+        const u32x4 *wv = reinterpret_cast<const u32x4 *>(wr);
+        for (int i = tid; i < hidden / EV; i += blockDim.x) {
+            const u32x4 a = xv[i], c = wv[i];
+            float fa[EV], fc[EV];
+            unpack16<T>(a, fa);
+            unpack16<T>(c, fc);
+#pragma unroll
+            for (int u = 0; u < EV; ++u) acc = fmaf(fa[u], fc[u], acc);
+        }
+    } else {
+        for (int i = tid; i < hidden; i += blockDim.x) acc = fmaf(ldf(xr + i), ldf(wr + i), acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) red[wave] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        float e = b_e ? b_e[g] : 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) e += red[w];
+        e_tok[(int64_t)r * e_stride + tok] = e;
+        e_new = e;
+    }
+    if (pos != S - 1) return;
+    __syncthreads();
+    // the block is complete: pool it
+    for (int p = tid; p < M * D; p += blockDim.x) {
+        const int i = p / D, d = p % D;
+        kbar[kbar_vec<T, D>(dm, r, M * j + i, d / V) + (d % V)] = pooled_mean_of<T>([&](int u) {
+            const int t = 16 * i + u;
+            return t == S - 1 ? knew[d] : blk[t * D + d];
+        });
+    }
+    if (tid < M) {
+        const float *er = e_tok + (int64_t)r * e_stride + (int64_t)j * S + tid * 16;
+        float s = 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s += (16 * tid + u == S - 1) ? e_new : er[u];
+        emean[tid] = s * (1.0f / 16);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float mx = emean[0];
+#pragma unroll
+        for (int i = 1; i < M; ++i) mx = fmaxf(mx, emean[i]);
+        e_blk[(int64_t)r * dm.max_blocks + j] = mx;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Append: the newest token of every row enters token slot `pos` of block
 // `block` of a KV buffer: its key as row pos of the K tile, its value as
 // column vt_pos_of(pos) of the V^T tile. One workgroup per row, thread d
@@ -920,6 +1032,19 @@ hipError_t launch_swap(const Dims &dm, const int32_t *sel, const int32_t *n_sel,
     return hipGetLastError();
 }
 
+template <typename T, int D, int G>
+hipError_t launch_ingest(const Dims &dm, const void *qkv, const void *x, const void *w_e,
+                         const float *b_e, int hidden, int tok, void *q_out, void *kv,
+                         int64_t kv_row_blocks, int block, float *e_tok, int64_t e_stride,
+                         void *kbar, float *e_blk, hipStream_t st) {
+    hipLaunchKernelGGL((ingest_kernel<T, D, G>), dim3(dm.rows), dim3(256), 0, st, dm,
+                       static_cast<const T *>(qkv), static_cast<const T *>(x),
+                       static_cast<const T *>(w_e), b_e, hidden, tok, static_cast<T *>(q_out),
+                       static_cast<T *>(kv), kv_row_blocks, block, e_tok, e_stride,
+                       static_cast<T *>(kbar), e_blk);
+    return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_append(const Dims &dm, const void *k_new, const void *v_new, int pos, void *kv,
                          int64_t kv_row_blocks, int block, hipStream_t st) {
@@ -959,6 +1084,10 @@ NOSA_POOL_INST(bf16_t, 128)
 #define NOSA_SCORE_INST(T, D, G)                                                               \
     template hipError_t launch_score<T, D, G>(const Dims &, const void *, const void *, int,   \
                                               float *, hipStream_t);                           \
+    template hipError_t launch_ingest<T, D, G>(const Dims &, const void *, const void *,       \
+                                               const void *, const float *, int, int, void *,  \
+                                               void *, int64_t, int, float *, int64_t, void *, \
+                                               float *, hipStream_t);                          \
     template hipError_t launch_score_select<T, D, G>(                                          \
         const Dims &, const void *, const void *, float *, const float *, int, int, uint32_t *, \
         uint32_t *, int32_t *, int32_t *, uint32_t *, const SwapPtrs *, hipStream_t);

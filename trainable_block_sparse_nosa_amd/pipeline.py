@@ -67,7 +67,7 @@ class DecodeLayer:
     def __init__(self, *, batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks, dtype,
                  kv, kv_row_blocks, e_tok, offload=False, decode_kernel=L.NOSA_DECODE_AUTO,
                  scale=0.0, device="cuda", fuse_select_swap=True, fuse_score=None,
-                 overlap=False, device_append=False):
+                 overlap=False, device_append=False, evict_head=None):
         self.shape = L.make_shape(batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks,
                                   dtype, decode_kernel=decode_kernel, scale=scale)
         self.rows = batch * n_kv_heads
@@ -144,6 +144,18 @@ class DecodeLayer:
         # on the GPU and is written into the newest block (the newest-block
         # buffer when offloaded); with offloaded KV a completed block is then
         # written back to host memory, so the host KV needs only the prefill
+        # evict_head = (w [n_kv_heads, hidden] KV dtype, b float32 [n_kv_heads]
+        # or None): steps take the token's fused projection output and hidden
+        # state instead (qkv, x), and one launch splits q / k / v, writes k and
+        # v into the newest block, runs the eviction head into e_tok and pools
+        # a block its token completes
+        self.evict_head = evict_head
+        if evict_head is not None:
+            if overlap:
+                raise ValueError("evict_head is not combined with overlap")
+            device_append = True
+            self.q_buf = torch.empty(batch, n_q_heads, head_dim, dtype=torch_dtype(dtype),
+                                     device=dev)
         self.device_append = device_append
         if device_append and offload:
             # a one-entry fetch list per row ([rows][k] like every fetch list;
@@ -197,12 +209,39 @@ class DecodeLayer:
         self.n_cand_prev = -1
         self.pooled = c0
 
+    def _write_back(self, block: int, stream=None):
+        """Newest-block buffer -> host KV block `block` (offloaded KV)."""
+        self._fill(self.wb_fs[:, 0], block, stream)
+        self._run("write_back", L.nosa_fetch_blocks, self.shape, self.cur, 1, self.wb_fb,
+                  self.wb_fs, self.wb_nf, 1, self.kv, self.kv_row_blocks, stream)
+
+    def _ingest(self, qkv, x, n_tokens: int, stream=None):
+        tok = n_tokens - 1
+        c = tok // BLOCK
+        w, b = self.evict_head
+        dst, rb, blk = (self.cur, 1, 0) if self.offload else (self.kv, self.kv_row_blocks, c)
+        self._run("ingest", L.nosa_ingest_tokens, self.shape, qkv, x, w, b, w.shape[1], n_tokens,
+                  self.q_buf, dst, rb, blk, self.e_tok, self.e_stride, self.kbar, self.e_blk,
+                  stream)
+        if tok % BLOCK == BLOCK - 1:
+            # the launch pooled block c; it is a candidate from the next step on
+            self.pooled = c + 1
+            if self.offload:
+                self._write_back(c, stream)
+
     def step(self, q: torch.Tensor, n_tokens: int, stream=None, swap: bool = True,
-             k_new=None, v_new=None) -> torch.Tensor:
+             k_new=None, v_new=None, qkv=None, x=None) -> torch.Tensor:
         """One decode step at n_tokens tokens (the newest appended by this step;
-        with device_append, k_new / v_new [rows][D] carry it)."""
+        with device_append, k_new / v_new [rows][D] carry it; with an eviction
+        head, qkv [batch][(Hq + 2 Hkv) D] and x [batch][hidden] do, and q is
+        taken from qkv)."""
         c = (n_tokens - 1) // BLOCK
-        if self.device_append and (k_new is None or v_new is None):
+        if self.evict_head is not None:
+            if qkv is None or x is None:
+                raise ValueError("a layer with an eviction head needs the step's qkv and x")
+            self._ingest(qkv, x, n_tokens, stream)
+            q = self.q_buf
+        elif self.device_append and (k_new is None or v_new is None):
             raise ValueError("device_append needs the step's k_new and v_new")
         if c > self.pooled:
             if self.offload:
@@ -212,10 +251,7 @@ class DecodeLayer:
                           self.e_stride, self.pooled, c, self.kbar, self.e_blk, stream)
                 if self.device_append:
                     # write it back to host block c - 1; the buffer starts block c
-                    self._fill(self.wb_fs[:, 0], c - 1, stream)
-                    self._run("write_back", L.nosa_fetch_blocks, self.shape, self.cur, 1,
-                              self.wb_fb, self.wb_fs, self.wb_nf, 1, self.kv,
-                              self.kv_row_blocks, stream)
+                    self._write_back(c - 1, stream)
                 else:
                     self._load_cur(c, stream)
             else:
@@ -223,7 +259,7 @@ class DecodeLayer:
                           self.pooled, self.e_tok, self.e_stride, self.pooled, c, self.kbar,
                           self.e_blk, stream)
             self.pooled = c
-        if self.device_append:
+        if self.device_append and self.evict_head is None:
             pos = (n_tokens - 1) % BLOCK
             if self.offload:
                 self._run("append", L.nosa_append_tokens, self.shape, k_new, v_new, pos, self.cur,
