@@ -68,6 +68,12 @@ def lib():
             L.oracle_attend_tokens.argtypes = [_f, ctypes.c_int, ctypes.c_int, _f, _f, _f, _i,
                                                ctypes.c_int, ctypes.c_double, _d]
             L.oracle_attend_tokens.restype = None
+            L.oracle_pool_queries.argtypes = [_f, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, _f]
+            L.oracle_pool_queries.restype = None
+            L.oracle_prefill_row.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_int,
+                                                                 _f, _f, _f, _f, _d, _i]
+            L.oracle_prefill_row.restype = ctypes.c_int
             L.oracle_step_row.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_int,
                                                               _f, _f, _f, _f,
                                                               _i, _i, _i, _i, _d, _d, _d]
@@ -263,3 +269,37 @@ class SlotCache:
         gamma = len(sel & self.prev) / self.k
         self.prev = sel
         return SwapResult(fetch, slots, list(self.slot_block), gamma)
+
+
+# ---------------------------------------------------------------------------
+# prefill (training-time forward) with the selection per query block
+# ---------------------------------------------------------------------------
+
+def pool_queries(q: np.ndarray, pooled_bf16: bool = False) -> np.ndarray:
+    """Pooled query of a query block, q [n, G, D] -> [G, D] (float32 values:
+    the exact mean rounded to bfloat16 with pooled_bf16, else to float)."""
+    q = _f32(q)
+    n, G, D = q.shape
+    out = np.zeros((G, D), np.float32)
+    lib().oracle_pool_queries(_pf(q), n, G, D, int(pooled_bf16), _pf(out))
+    return out
+
+
+@dataclass
+class Prefill:
+    out: np.ndarray      # [N, G, D] fp64
+    sel: np.ndarray      # [n_query_blocks, k] int32, ascending, -1 padded
+
+
+def prefill_row(q, K, V, e, block: int, sub: int, k_e: int, k_q: int, scale: float,
+                pooled_bf16: bool = False) -> Prefill:
+    """Causal prefill of one row with NOSA's selection per query block.
+    q [N, G, D]; K, V [N, D]; e [N]."""
+    q, K, V, e = _f32(q), _f32(K), _f32(V), _f32(e)
+    N, G, D = q.shape
+    nqb = -(-N // block)
+    out = np.zeros((N, G, D), np.float64)
+    sel = np.full((nqb, max(k_e + k_q, 1)), -1, np.int32)
+    lib().oracle_prefill_row(N, G, D, block, sub, k_e, k_q, scale, int(pooled_bf16), _pf(q),
+                             _pf(K), _pf(V), _pf(e), _pd(out), _pi(sel))
+    return Prefill(out, sel[:, :k_e + k_q])

@@ -271,3 +271,96 @@ int oracle_step_row(int n_tokens, int G, int D, int block, int sub, int k_e, int
     free(Eb);
     return c;
 }
+
+/* ------------------------------------------------------------------------
+ * Prefill (training-time forward) with the same selection per query block.
+ * Readings taken, the pages describing the trainable mechanism but not its
+ * forward over a whole sequence: queries come in blocks of `block` tokens;
+ * query block i selects among the complete blocks before it (0..i-1) exactly
+ * as a decode step with those candidates does (Gamma_e: the k_e greatest
+ * pooled eviction scores; Gamma_q: the k_q greatest of the rest by the
+ * query-aware score), the query-aware score being that of the block's pooled
+ * query (the mean of its tokens' queries per head, kept in the input dtype:
+ * rounded to the nearest bfloat16 for bfloat16 inputs, to the nearest float
+ * otherwise); every query token of the block attends the tokens of the
+ * selected blocks and, causally, the tokens of its own block up to itself.
+ * ------------------------------------------------------------------------ */
+
+/* Pooled query of n tokens q[u][h][d] (u < n): per (h, d) the mean over u. */
+void oracle_pool_queries(const float *q, int n, int G, int D, int pooled_bf16, float *out)
+{
+    for (int h = 0; h < G; ++h)
+        for (int d = 0; d < D; ++d) {
+            double s = 0.0;
+            for (int u = 0; u < n; ++u)
+                s += (double)q[((int64_t)u * G + h) * D + d];
+            double mean = s / (double)n;
+            out[h * D + d] = (float)(pooled_bf16 ? oracle_round_bf16(mean) : mean);
+        }
+}
+
+/* Prefill of one row: N tokens, q [N][G][D], K and V [N][D], e [N].
+   Writes out [N][G][D] and, for every query block i, its ascending selection
+   sel[i * (k_e + k_q) ...] (-1 padded). Returns the number of query blocks. */
+int oracle_prefill_row(int N, int G, int D, int block, int sub, int k_e, int k_q, double scale,
+                       int pooled_bf16, const float *q, const float *K, const float *V,
+                       const float *e, double *out, int *sel)
+{
+    int nqb = (N + block - 1) / block;
+    int k = k_e + k_q;
+    int cmax = nqb > 1 ? nqb - 1 : 1;
+    double *Eb = (double *)malloc(sizeof(double) * (size_t)cmax);
+    double *Sb = (double *)malloc(sizeof(double) * (size_t)cmax);
+    unsigned char *rest = (unsigned char *)malloc((size_t)cmax);
+    unsigned char *pick = (unsigned char *)malloc((size_t)cmax);
+    int *ge = (int *)malloc(sizeof(int) * (size_t)(k_e > 0 ? k_e : 1));
+    int *gq = (int *)malloc(sizeof(int) * (size_t)(k_q > 0 ? k_q : 1));
+    int *tok = (int *)malloc(sizeof(int) * (size_t)(k * block + block));
+    float *qbar = (float *)malloc(sizeof(float) * (size_t)G * (size_t)D);
+    for (int j = 0; j + 1 < nqb; ++j)
+        Eb[j] = oracle_block_evict(e, block, sub, j);
+    for (int i = 0; i < nqb; ++i) {
+        int lo = i * block, hi = lo + block < N ? lo + block : N;
+        int c = i;  /* candidates: blocks 0..i-1 */
+        oracle_pool_queries(q + (int64_t)lo * G * D, hi - lo, G, D, pooled_bf16, qbar);
+        for (int j = 0; j < c; ++j)
+            Sb[j] = oracle_block_score(qbar, G, D, K, block, sub, j, scale, pooled_bf16);
+        int n_ge = oracle_topk(Eb, NULL, c, k_e, ge);
+        for (int j = 0; j < c; ++j)
+            rest[j] = 1;
+        for (int t = 0; t < n_ge; ++t)
+            rest[ge[t]] = 0;
+        int n_gq = oracle_topk(Sb, rest, c, k_q, gq);
+        for (int j = 0; j < c; ++j)
+            pick[j] = 0;
+        for (int t = 0; t < n_ge; ++t)
+            pick[ge[t]] = 1;
+        for (int t = 0; t < n_gq; ++t)
+            pick[gq[t]] = 1;
+        int ns = 0, nt = 0;
+        for (int j = 0; j < c; ++j)
+            if (pick[j]) {
+                sel[i * k + ns++] = j;
+                for (int u = 0; u < block; ++u)
+                    tok[nt++] = j * block + u;
+            }
+        for (int t = ns; t < k; ++t)
+            sel[i * k + t] = -1;
+        for (int p = lo; p < hi; ++p) {
+            int m = nt;
+            for (int u = lo; u <= p; ++u)
+                tok[m++] = u;
+            oracle_attend_tokens(q + (int64_t)p * G * D, G, D, K, V, e, tok, m, scale,
+                                 out + (int64_t)p * G * D);
+        }
+    }
+    free(qbar);
+    free(tok);
+    free(gq);
+    free(ge);
+    free(pick);
+    free(rest);
+    free(Sb);
+    free(Eb);
+    return nqb;
+}

@@ -387,3 +387,88 @@ def test_swap_cache_bruteforce():
         assert res.slot_block == slots
         assert res.gamma == len(set(sel) & prev) / k
         prev = set(sel)
+
+
+# ---------------------------------------------------------------------------
+# prefill with the selection per query block
+# ---------------------------------------------------------------------------
+
+def _np_causal(q, K, V, e, scale, allowed):
+    """Textbook softmax attention of q [N, G, D]; allowed(p) -> key positions."""
+    N, G, D = q.shape
+    out = np.zeros((N, G, D))
+    Kd, Vd, ed = K.astype(np.float64), V.astype(np.float64), e.astype(np.float64)
+    for p in range(N):
+        idx = np.array(sorted(allowed(p)))
+        for h in range(G):
+            z = scale * (Kd[idx] @ q[p, h].astype(np.float64)) + ed[idx]
+            a = np.exp(z - z.max())
+            out[p, h] = (a / a.sum()) @ Vd[idx]
+    return out
+
+
+def test_prefill_is_dense_causal_when_the_budget_covers_every_block():
+    rng = np.random.default_rng(41)
+    N, G, D = 200, 2, 8
+    q = rng.normal(size=(N, G, D)).astype(np.float32)
+    K = rng.normal(size=(N, D)).astype(np.float32)
+    V = rng.normal(size=(N, D)).astype(np.float32)
+    e = rng.normal(size=N).astype(np.float32)
+    res = oracle.prefill_row(q, K, V, e, 64, 16, 2, 2, 0.35)
+    want = _np_causal(q, K, V, e, 0.35, lambda p: range(p + 1))
+    np.testing.assert_allclose(res.out, want, rtol=1e-12, atol=1e-12)
+    assert res.sel.tolist() == [[-1] * 4, [0, -1, -1, -1], [0, 1, -1, -1], [0, 1, 2, -1]]
+
+
+def test_prefill_eviction_selection_by_brute_force():
+    """k_q = 0: query block i attends the k_e blocks before it with the
+    largest max-of-sub-block-mean eviction score, plus its causal own block."""
+    rng = np.random.default_rng(42)
+    N, G, D, ke = 64 * 6 + 10, 1, 4, 2
+    q = rng.normal(size=(N, G, D)).astype(np.float32)
+    K = rng.normal(size=(N, D)).astype(np.float32)
+    V = rng.normal(size=(N, D)).astype(np.float32)
+    e = rng.normal(size=N).astype(np.float32)
+    E = [max(float(np.mean(e[64 * j + 16 * i:64 * j + 16 * i + 16].astype(np.float64)))
+             for i in range(4)) for j in range(N // 64)]
+    res = oracle.prefill_row(q, K, V, e, 64, 16, ke, 0, 0.5)
+    for i in range(N // 64 + 1):
+        best = sorted(sorted(range(i), key=lambda j: (-E[j], j))[:ke])
+        assert res.sel[i][:len(best)].tolist() == best
+    sel_of = {i: [j for j in res.sel[i] if j >= 0] for i in range(res.sel.shape[0])}
+    want = _np_causal(q, K, V, e, 0.5, lambda p: [64 * j + u for j in sel_of[p // 64]
+                                                  for u in range(64)]
+                      + list(range(64 * (p // 64), p + 1)))
+    np.testing.assert_allclose(res.out, want, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_query_selection_by_brute_force():
+    """k_e = 0: the k_q blocks with the largest score of the block's pooled
+    query (mean of its queries, as a float) against the sub-block key means."""
+    rng = np.random.default_rng(43)
+    N, G, D, kq, sc = 64 * 5 + 30, 2, 4, 2, 0.4
+    q = rng.normal(size=(N, G, D)).astype(np.float32)
+    K = rng.normal(size=(N, D)).astype(np.float32)
+    V = rng.normal(size=(N, D)).astype(np.float32)
+    e = rng.normal(size=N).astype(np.float32)
+    res = oracle.prefill_row(q, K, V, e, 64, 16, 0, kq, sc)
+    Kd = K.astype(np.float64)
+    for i in range(1, N // 64 + 1):
+        qb = q[64 * i:64 * i + 64].astype(np.float64).mean(axis=0).astype(np.float32)
+        np.testing.assert_array_equal(oracle.pool_queries(q[64 * i:64 * i + 64]), qb)
+        S = []
+        for j in range(i):
+            kb = Kd[64 * j:64 * j + 64].reshape(4, 16, D).mean(axis=1)
+            S.append(sum(max(sc * float(kb[s] @ qb[h].astype(np.float64)) for s in range(4))
+                         for h in range(G)))
+        best = sorted(sorted(range(i), key=lambda j: (-S[j], j))[:kq])
+        assert res.sel[i][:len(best)].tolist() == best
+
+
+def test_pool_queries_bf16():
+    """Integer inputs: the exact means are floats, so rounding them to bf16 is
+    the bit-level rounding of those floats."""
+    rng = np.random.default_rng(44)
+    q = rng.integers(-300, 300, size=(64, 2, 8)).astype(np.float32)
+    mean = q.astype(np.float64).mean(axis=0).astype(np.float32)
+    np.testing.assert_array_equal(oracle.pool_queries(q, pooled_bf16=True), synth.rne_bf16(mean))
