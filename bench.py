@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-ingest", action="store_true",
                     help="skip the leg that runs the workload with the fused ingest launch "
                          "(QKV split, eviction head, KV append, pooling) in every step")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the leg that prefills the workload's context with the selection "
+                         "per query block (block-sparse causal attention on the matrix cores)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 4 device-to-device copies of 512 MiB (a reference kernel "
                          "of known traffic for hardware byte counters)")
@@ -204,6 +207,74 @@ def run_step(layer, q, new, t, n_tokens, stream):
         layer.step(None, n_tokens, stream, qkv=new[1][t], x=new[2][t])
     else:
         layer.step(q[t], n_tokens, stream, k_new=new[0][t], v_new=new[1][t])
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(w, n_tokens: int, n_sel) -> float:
+    """Algorithmic matrix flops of the prefill attention: per query token and
+    head, 2 D for q.k and 2 D for p.v per attended token (the selected blocks'
+    64 tokens each, plus its own block up to itself)."""
+    G, D = w.group, w.head_dim
+    total = 0.0
+    nqb = -(-n_tokens // 64)
+    for i in range(nqb):
+        lo, hi = 64 * i, min(64 * i + 64, n_tokens)
+        own = sum(range(1, hi - lo + 1))                # causal tokens of the block's queries
+        sel_tokens = float(n_sel[i].sum()) * 64 * (hi - lo)  # summed over rows
+        total += (sel_tokens + own * w.rows) * G * 4 * D
+    return total
+
+
+def prefill_leg(w, args, dev, stream):
+    """The same workload's context prefilled with the selection per query
+    block (pool the blocks, pool the queries, select per query block, causal
+    block-sparse attention on the matrix cores), synthetic queries."""
+    import torch
+    from trainable_block_sparse_nosa_amd import _lib as L
+    N = w.context
+    sub = argparse.Namespace(**vars(args))
+    sub.steps, sub.warmup = 1, 0
+    layer, q, kv, _ = setup(w, sub, dev)
+    del q
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 7)
+    q_all = torch.empty(w.batch, N, w.n_q_heads, w.head_dim, dtype=torch.bfloat16, device=dev)
+    for b in range(w.batch):
+        q_all[b].copy_(torch.randn(N, w.n_q_heads, w.head_dim, generator=g).to(torch.bfloat16))
+    times = {}
+
+    def hook(name, fn, *a):
+        on = a[-1] if a[-1] is not None else torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(on)
+        fn(*a)
+        e1.record(on)
+        times.setdefault(name, []).append((e0, e1))
+
+    out, sel, n_sel = layer.prefill(q_all, N, stream)    # warm-up
+    torch.cuda.synchronize()
+    layer.stage_hook = hook
+    t0 = time.perf_counter()
+    out, sel, n_sel = layer.prefill(q_all, N, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    layer.stage_hook = None
+    ms = {k: sum(a.elapsed_time(b) for a, b in v) for k, v in times.items()}
+    flops = prefill_flops(w, N, n_sel.cpu().numpy())
+    att_s = ms["prefill_attention"] / 1e3
+    res = {
+        "workload": w.name, "n_tokens": N, "tokens_per_s": w.batch * N / wall,
+        "ms_total": wall * 1e3, "ms_pool_queries": ms.get("pool_queries"),
+        "ms_select": ms.get("prefill_select"), "ms_attention": ms["prefill_attention"],
+        "roofline": {"kernel": "prefill_mfma_kernel", "bound": "mfma",
+                     "achieved": flops / att_s / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flops / att_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "algorithmic_flops": flops},
+    }
+    del layer, kv, q_all, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def ingest_leg(w, args, dev, stream, main_steps_per_s):
@@ -566,6 +637,14 @@ def main():
         ingest = ingest_leg(w, args, dev, stream, steps_per_s)
         log(f"ingest: {ingest['steps_per_s']:.1f} steps/s, launch {ingest['ingest_us_avg']:.1f} us")
 
+    prefill = None
+    if not args.no_prefill and not w.offload and w.dtype == "bf16":
+        log(f"prefill leg: {w.name}, {w.context} tokens")
+        prefill = prefill_leg(w, args, dev, stream)
+        log(f"prefill: {prefill['tokens_per_s']:.0f} tokens/s, attention "
+            f"{prefill['ms_attention']:.1f} ms = {prefill['roofline']['achieved']:.0f} TFLOP/s, "
+            f"selection {prefill['ms_select']:.1f} ms")
+
     swap = None
     if args.offload_steps > 0 and not w.offload:
         log("offload leg: offload_1layer_128k")
@@ -610,6 +689,7 @@ def main():
         "gamma_mean": gamma_mean,
         "swap": swap,
         "ingest": ingest,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     if stages:

@@ -169,6 +169,42 @@ nosa_status nosa_ingest_tokens(const nosa_shape *shape, const void *qkv, const v
                                int32_t block, float *e_tok, int64_t e_row_stride, void *kbar,
                                float *e_blk, void *stream);
 
+/* ---- prefill (training-time forward) with the selection per query block ----
+ * The method is trainable and native (Methodology, "1. Algorithm: NOSA"): the
+ * same dual selection shapes attention over a whole sequence. Query blocks
+ * are the S-token blocks of the sequence; query block i selects among the
+ * complete blocks before it (0..i-1) as a decode step with those candidates
+ * does, scoring with the block's pooled query; its tokens attend the selected
+ * blocks and their own block causally. Call order: nosa_pool_blocks over the
+ * complete blocks, nosa_prefill_pool_queries, nosa_prefill_select,
+ * nosa_prefill_attention. */
+
+/* Pooled query of every query block: qbar [n_qb][batch][Hq][D] (KV dtype,
+ * n_qb = ceil(n_tokens / S)) is the mean over the block's tokens of q
+ * [batch][n_tokens][Hq][D], rounded once to the KV dtype. */
+nosa_status nosa_prefill_pool_queries(const nosa_shape *shape, const void *q, int32_t n_tokens,
+                                      void *qbar, void *stream);
+
+/* Selection of every query block i (candidates 0..i-1): sel [n_qb][rows][k]
+ * ascending, -1 padded, and n_sel [n_qb][rows], as nosa_score_select with no
+ * previous step would select for query qbar[i] (one launch per query block).
+ * s_q [rows][max_blocks] and state uint32 [3][rows][W] are scratch. */
+nosa_status nosa_prefill_select(const nosa_shape *shape, const void *qbar, const void *kbar,
+                                const float *e_blk, int32_t n_tokens, float *s_q,
+                                uint32_t *state, int32_t *sel, int32_t *n_sel, void *stream);
+
+/* Causal block-sparse attention of the whole sequence (bf16, matrix cores):
+ * out[b][p][h] = softmax over the tokens of query block i = p / S's selected
+ * blocks and of tokens S*i .. p of z = scale * q.k + e (e_tok as an additive
+ * logit, ED-DMA), times V. kv is the block-unit KV [rows][kv_row_blocks][2*S*D]
+ * (kv_row_blocks >= n_qb; the last block may be partial), e_tok [rows][stride]
+ * (stride >= n_qb * S, a multiple of 4), q and out [batch][n_tokens][Hq][D].
+ * float32: NOSA_ERR_UNSUPPORTED. */
+nosa_status nosa_prefill_attention(const nosa_shape *shape, const void *q, int32_t n_tokens,
+                                   const void *kv, int64_t kv_row_blocks, const float *e_tok,
+                                   int64_t e_row_stride, const int32_t *sel, const int32_t *n_sel,
+                                   void *out, void *stream);
+
 /* Write the newest token of every row into the block-unit KV buffer `kv`
  * (device memory or the device alias of pinned host memory; kv_row_blocks
  * blocks per row): token slot pos (0..S-1) of block `block` receives

@@ -25,7 +25,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "rne_bf16", "bf16_bits", "stream",
     "keys_row", "values_row", "evict_row", "queries_step", "Overrides",
-    "hidden_size", "hidden_step", "evict_head_weights",
+    "hidden_size", "hidden_step", "evict_head_weights", "prefill_queries",
 ]
 
 
@@ -227,6 +227,24 @@ def queries_step(w: Workload, layer: int, t: int, ov: Overrides | None = None) -
             if (l, tt) == (layer, t) and a > 0:
                 z[b, g * G:(g + 1) * G] = stream(w.seed, "Q", layer, t, b, g, a).standard_normal(
                     (G, w.head_dim), dtype=np.float32)
+    return _to_dtype(z, w.dtype)
+
+
+def prefill_queries(w: Workload, layer: int, n_tokens: int, ov: Overrides | None = None) -> np.ndarray:
+    """Queries of every token of a prefilled sequence: [batch, n_tokens, n_q_heads, D]
+    ~ N(0, 1) in the input dtype. ``ov.query[("prefill", layer, b, g, i)] = a``
+    regenerates query block i (its 64 tokens) of KV head g's query heads from
+    attempt a."""
+    z = stream(w.seed, "QP", layer, n_tokens).standard_normal(
+        (w.batch, n_tokens, w.n_q_heads, w.head_dim), dtype=np.float32)
+    if ov is not None:
+        G = w.group
+        for key, a in list(ov.query.items()):
+            if len(key) == 5 and key[0] == "prefill" and key[1] == layer and a > 0:
+                _, _, b, g, i = key
+                lo, hi = 64 * i, min(64 * i + 64, n_tokens)
+                z[b, lo:hi, g * G:(g + 1) * G] = stream(w.seed, "QP", layer, b, g, i, a).standard_normal(
+                    (hi - lo, G, w.head_dim), dtype=np.float32)
     return _to_dtype(z, w.dtype)
 
 

@@ -1,0 +1,102 @@
+"""Prefill (training-time forward) with NOSA's selection per query block:
+the HIP path (pooled queries, per-block selection, causal block-sparse MFMA
+attention) against the fp64 oracle through the C ABI. Selections bit-exact,
+outputs within the bf16 tolerance."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from harness import boundary_ok, row_kv
+from synth import Overrides, Workload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = dict(rtol=2e-2, atol=2e-3)
+
+# sequence length = context; one extra token keeps n_max above it
+PREFILL = {
+    # 16 query blocks (the last one 40 tokens), GQA 4, D 128
+    "prefill_bf16": Workload("prefill_bf16", 3001, 2, 8, 2, 128, 1000, 1, 3, 2, "bf16",
+                             key_offset_std=0.5),
+    # GQA 3, D 64, a k_q larger than k_e
+    "prefill_g3_d64": Workload("prefill_g3_d64", 3002, 1, 6, 2, 64, 700, 1, 2, 3, "bf16",
+                               key_offset_std=0.5),
+    # the budget covers every earlier block: dense causal attention
+    "prefill_dense": Workload("prefill_dense", 3003, 1, 4, 1, 128, 200, 1, 4, 4, "bf16"),
+}
+
+
+def _prefill_trace(w: Workload):
+    """Oracle prefill of every row, with the 1e-4 margins enforced at every
+    selection boundary (eviction blocks and query blocks redrawn as needed)."""
+    N, D, G = w.context, w.head_dim, w.group
+    nqb = -(-N // 64)
+    sc = 1.0 / math.sqrt(D)
+    ov = Overrides()
+    out = {}
+    for r in range(w.rows):
+        b, g = divmod(r, w.n_kv_heads)
+        K, V = row_kv(w, 0, b, g)
+        K, V = K[:N], V[:N]
+        for _ in range(256):
+            e = synth.evict_row(w, 0, b, g, ov)
+            E = [oracle.block_evict(e, 64, 16, j) for j in range(max(nqb - 1, 0))]
+            bad = None
+            for c in range(1, nqb):
+                ok, lower = boundary_ok(np.array(E[:c]), w.k_e)
+                if not ok:
+                    bad = lower
+                    break
+            if bad is None:
+                break
+            key = (0, b, g, bad)
+            ov.evict[key] = ov.evict.get(key, 0) + 1
+        else:
+            raise RuntimeError("eviction margins")
+        for i in range(1, nqb):
+            ge = sorted(sorted(range(i), key=lambda j: (-E[j], j))[:w.k_e])
+            for _ in range(64):
+                q = synth.prefill_queries(w, 0, N, ov)[b, :, g * G:(g + 1) * G]
+                qb = oracle.pool_queries(q[64 * i:64 * i + 64], pooled_bf16=True)
+                S = np.array([oracle.block_score(qb, K, 64, 16, j, sc, pooled_bf16=True)
+                              for j in range(i)])
+                rest = np.array([j not in ge for j in range(i)], bool)
+                ok, _ = boundary_ok(S[rest], w.k_q)
+                if ok:
+                    break
+                key = ("prefill", 0, b, g, i)
+                ov.query[key] = ov.query.get(key, 0) + 1
+            else:
+                raise RuntimeError("query margins")
+        q = synth.prefill_queries(w, 0, N, ov)[b, :, g * G:(g + 1) * G]
+        out[r] = oracle.prefill_row(q, K, V, e[:N], 64, 16, w.k_e, w.k_q, sc, pooled_bf16=True)
+    return ov, out
+
+
+@pytest.mark.parametrize("name", list(PREFILL))
+def test_prefill_parity(name):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gpu_harness as gh
+    w = PREFILL[name]
+    N, G = w.context, w.group
+    ov, ref = _prefill_trace(w)
+    inp = gh.upload(w, ov=ov, steps=1)
+    q_all = gh.to_device(gh.storage(synth.prefill_queries(w, 0, N, ov), w), w)
+    layer = gh.make_layer(w, inp)
+    out, sel, n_sel = layer.prefill(q_all, N)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    sel, n_sel = sel.cpu().numpy(), n_sel.cpu().numpy()
+    for r in range(w.rows):
+        b, g = divmod(r, w.n_kv_heads)
+        for i in range(ref[r].sel.shape[0]):
+            want = [j for j in ref[r].sel[i] if j >= 0]
+            n = int(n_sel[i, r])
+            assert sel[i, r, :n].tolist() == want, f"{name} row {r} query block {i}"
+        np.testing.assert_allclose(out[b, :, g * G:(g + 1) * G], ref[r].out,
+                                   err_msg=f"{name} row {r}", **TOL)

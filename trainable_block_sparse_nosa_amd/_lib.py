@@ -31,7 +31,8 @@ NOSA_DECODE_MFMA = 2
 EXPORTS = (
     "nosa_pool_blocks", "nosa_score_blocks", "nosa_select", "nosa_select_swap", "nosa_swap_diff",
     "nosa_select_parts", "nosa_score_select", "nosa_fetch_blocks", "nosa_append_tokens",
-    "nosa_ingest_tokens", "nosa_decode_workspace_size", "nosa_decode_chunks",
+    "nosa_ingest_tokens", "nosa_prefill_pool_queries", "nosa_prefill_select",
+    "nosa_prefill_attention", "nosa_decode_workspace_size", "nosa_decode_chunks",
     "nosa_sparse_decode", "nosa_decode_partial", "nosa_decode_combine",
     "nosa_host_alloc", "nosa_host_free", "nosa_status_string", "nosa_last_error",
     "nosa_version",
@@ -75,6 +76,9 @@ def _load() -> ctypes.CDLL:
         "nosa_decode_chunks": [SH, I32, I32],
         "nosa_append_tokens": [SH, P, P, I32, P, I64, I32, P],
         "nosa_ingest_tokens": [SH, P, P, P, P, I32, I32, P, P, I64, I32, P, I64, P, P, P],
+        "nosa_prefill_pool_queries": [SH, P, I32, P, P],
+        "nosa_prefill_select": [SH, P, P, P, I32, P, P, P, P, P],
+        "nosa_prefill_attention": [SH, P, I32, P, I64, P, I64, P, P, P, P],
         "nosa_decode_partial": [SH, P, P, I64, I32, P, P, I32, I32, I32, P, I64, ST, P, I64, P, SZ,
                                 I32, P],
         "nosa_decode_combine": [SH, I32, P, P, SZ, P],
@@ -228,6 +232,24 @@ def nosa_ingest_tokens(shape, qkv, x, w_evict, b_evict, hidden, n_tokens, q_out,
         ctypes.byref(shape), _p(qkv), _p(x), _p(w_evict), _p(b_evict), hidden, n_tokens,
         _p(q_out), _p(kv), kv_row_blocks, block, _p(e_tok), e_row_stride, _p(kbar), _p(e_blk),
         _s(stream)))
+
+
+def nosa_prefill_pool_queries(shape, q, n_tokens, qbar, stream=None):
+    _chk("nosa_prefill_pool_queries", _L.nosa_prefill_pool_queries(
+        ctypes.byref(shape), _p(q), n_tokens, _p(qbar), _s(stream)))
+
+
+def nosa_prefill_select(shape, qbar, kbar, e_blk, n_tokens, s_q, state, sel, n_sel, stream=None):
+    _chk("nosa_prefill_select", _L.nosa_prefill_select(
+        ctypes.byref(shape), _p(qbar), _p(kbar), _p(e_blk), n_tokens, _p(s_q), _p(state),
+        _p(sel), _p(n_sel), _s(stream)))
+
+
+def nosa_prefill_attention(shape, q, n_tokens, kv, kv_row_blocks, e_tok, e_row_stride, sel, n_sel,
+                           out, stream=None):
+    _chk("nosa_prefill_attention", _L.nosa_prefill_attention(
+        ctypes.byref(shape), _p(q), n_tokens, _p(kv), kv_row_blocks, _p(e_tok), e_row_stride,
+        _p(sel), _p(n_sel), _p(out), _s(stream)))
 
 
 def nosa_decode_workspace_size(shape) -> int:

@@ -346,6 +346,74 @@ nosa_status nosa_ingest_tokens(const nosa_shape *shape, const void *qkv, const v
     });
 }
 
+nosa_status nosa_prefill_pool_queries(const nosa_shape *shape, const void *q, int32_t n_tokens,
+                                      void *qbar, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!q || !qbar || n_tokens <= 0) return NOSA_ERR_INVALID_ARGUMENT;
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        constexpr int D = decltype(dc)::value;
+        return hip_status(launch_pool_queries<T, D>(dm, q, n_tokens, qbar, (hipStream_t)stream));
+    });
+}
+
+nosa_status nosa_prefill_select(const nosa_shape *shape, const void *qbar, const void *kbar,
+                                const float *e_blk, int32_t n_tokens, float *s_q,
+                                uint32_t *state, int32_t *sel, int32_t *n_sel, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!qbar || !kbar || !e_blk || !s_q || !state || !sel || !n_sel || n_tokens <= 0)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    const int nqb = (n_tokens + dm.S - 1) / dm.S;
+    if (nqb - 1 >= dm.max_blocks) return NOSA_ERR_INVALID_ARGUMENT;
+    const int64_t qstride = (int64_t)dm.B * dm.Hq * dm.D;
+    const int elem = dm.dtype == NOSA_BF16 ? 2 : 4;
+    uint32_t *ge = state, *ev = state + (int64_t)dm.rows * dm.W, *sb = ev + (int64_t)dm.rows * dm.W;
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        constexpr int D = decltype(dc)::value;
+        return by_group(dm, [&](auto gc) -> nosa_status {
+            for (int i = 0; i < nqb; ++i) {
+                // query block i: candidates 0..i-1, selected afresh (no previous step)
+                const void *qi = static_cast<const char *>(qbar) + i * qstride * elem;
+                const hipError_t e = launch_score_select<T, D, decltype(gc)::value>(
+                    dm, qi, kbar, s_q, e_blk, i, -1, ge, ev, sel + (int64_t)i * dm.rows * dm.k,
+                    n_sel + (int64_t)i * dm.rows, sb, nullptr, (hipStream_t)stream);
+                if (e != hipSuccess) return hip_status(e);
+            }
+            return NOSA_OK;
+        });
+    });
+}
+
+nosa_status nosa_prefill_attention(const nosa_shape *shape, const void *q, int32_t n_tokens,
+                                   const void *kv, int64_t kv_row_blocks, const float *e_tok,
+                                   int64_t e_row_stride, const int32_t *sel, const int32_t *n_sel,
+                                   void *out, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!q || !kv || !e_tok || !sel || !n_sel || !out || n_tokens <= 0)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (dm.dtype != NOSA_BF16) return NOSA_ERR_UNSUPPORTED;
+    const int nqb = (n_tokens + dm.S - 1) / dm.S;
+    if (kv_row_blocks < nqb || e_row_stride < (int64_t)nqb * dm.S) return NOSA_ERR_INVALID_ARGUMENT;
+    if (((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv) |
+          reinterpret_cast<uintptr_t>(e_tok)) & 15) != 0 || (e_row_stride & 3) != 0)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    return by_type_dim(dm, [&](auto, auto dc) -> nosa_status {
+        constexpr int D = decltype(dc)::value;
+        return by_group(dm, [&](auto gc) -> nosa_status {
+            return hip_status(launch_prefill<D, decltype(gc)::value>(
+                dm, q, n_tokens, kv, kv_row_blocks, e_tok, e_row_stride, sel, n_sel, out,
+                (hipStream_t)stream));
+        });
+    });
+}
+
 nosa_status nosa_append_tokens(const nosa_shape *shape, const void *k_new, const void *v_new,
                                int32_t pos, void *kv, int64_t kv_row_blocks, int32_t block,
                                void *stream) {

@@ -37,6 +37,22 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
     return (bf16_t)(u >> 16);
 }
 
+// x (double) rounded to the nearest bfloat16, ties to even, with one
+// rounding: x is first rounded to float32 by rounding to odd (truncate, then
+// set the last bit if anything was dropped), which float32's 16 extra bits
+// make innocuous for the final round-to-nearest-even (Boldo and Melquiond,
+// "Emulation of FMA and correctly rounded sums: proved algorithms using
+// rounding to odd", IEEE Trans. Computers 57(4), 2008).
+__device__ __forceinline__ bf16_t bf16_rne_from_double(double x) {
+    float f = (float)x;
+    if ((double)f != x) {
+        uint32_t u = __float_as_uint(f);
+        if (fabs((double)f) > fabs(x)) u -= 1u;  // rounded away from zero: step back
+        f = __uint_as_float(u | 1u);
+    }
+    return f2bf(f);
+}
+
 template <typename T> __device__ __forceinline__ float ldf(const T *p);
 template <> __device__ __forceinline__ float ldf<float>(const float *p) { return *p; }
 template <> __device__ __forceinline__ float ldf<bf16_t>(const bf16_t *p) { return bf2f(*p); }

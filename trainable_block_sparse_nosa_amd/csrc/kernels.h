@@ -96,6 +96,13 @@ hipError_t launch_decode_valu(const Dims &dm, const DecodePlan &pl, const Decode
 template <int D, int G>
 hipError_t launch_decode_mfma(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
                               hipStream_t st);
+template <typename T, int D>
+hipError_t launch_pool_queries(const Dims &dm, const void *q, int n_tokens, void *qbar,
+                               hipStream_t st);
+template <int D, int G>
+hipError_t launch_prefill(const Dims &dm, const void *q, int n_tokens, const void *kv,
+                          int64_t kv_row_blocks, const float *e_tok, int64_t e_stride,
+                          const int32_t *sel, const int32_t *n_sel, void *out, hipStream_t st);
 template <typename T, int D, int G>
 hipError_t launch_combine(const Dims &dm, int n_chunks, int chunk_cap, const float *ws_o,
                           const float *ws_ml, void *out, hipStream_t st);

@@ -175,8 +175,8 @@ __device__ __forceinline__ void load_block(BlockRegs<D> &br, const bf16_t *blk, 
 
 template <int D>
 __device__ __forceinline__ void attend_block(const BlockRegs<D> &br, const bf16x8 (&qop)[D / 32],
-                                             float scale, int grp, float &m_run, float &l_run,
-                                             f32x4 (&o)[D / 16]) {
+                                             float scale, int grp, int lim, float &m_run,
+                                             float &l_run, f32x4 (&o)[D / 16]) {
     constexpr int KS = D / 32, DT = D / 16;
     // S^T tile t: lane holds logits of tokens 16t + 4grp + u for head col
     f32x4 sc[4];
@@ -193,7 +193,8 @@ __device__ __forceinline__ void attend_block(const BlockRegs<D> &br, const bf16x
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const bool ok = 16 * t + 4 * grp + u < br.valid;
+            // tokens of the block from lim on are masked for this lane's column
+            const bool ok = 16 * t + 4 * grp + u < lim;
             z[t][u] = ok ? fmaf(sc[t][u], scale, br.e[t][u]) : -INFINITY;
             mx = fmaxf(mx, z[t][u]);
         }
@@ -278,7 +279,7 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
             // scheduler interleaves loads with MFMAs to save registers and the
             // block is no longer in flight at once
             __builtin_amdgcn_sched_barrier(0);
-            attend_block<D>(br, qop, dm.scale, grp, m_run, l_run, o);
+            attend_block<D>(br, qop, dm.scale, grp, br.valid, m_run, l_run, o);
         }
     }
 
@@ -320,6 +321,138 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
         }
     }
 }
+
+// ---------------------------------------------------------------------------
+// Prefill (training-time forward) with the selection per query block.
+//
+// Pooled queries: qbar[i][b][hq][d] = mean of q[b][64 i + u][hq][d] over the
+// query block's tokens, in the input dtype (exact mean rounded once).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(D)
+pool_queries_kernel(Dims dm, const T *__restrict__ q, int n_tokens, T *__restrict__ qbar) {
+    const int i = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
+    const int b = bh / dm.Hq, hq = bh % dm.Hq;
+    const int lo = 64 * i, n = min(64, n_tokens - lo);
+    double s = 0.0;
+    for (int u = 0; u < n; ++u) s += (double)ldf(q + (((int64_t)b * n_tokens + lo + u) * dm.Hq + hq) * D + d);
+    const double mean = s / (double)n;
+    T *out = qbar + (((int64_t)i * dm.B + b) * dm.Hq + hq) * D + d;
+    if constexpr (std::is_same_v<T, float>) *out = (float)mean;
+    else *out = bf16_rne_from_double(mean);
+}
+
+// Block-sparse causal attention (bf16, MFMA). Workgroup (query block i,
+// column group cg, row r), 4 waves; wave w owns 16 query rows qr = 16 (4 cg +
+// w) + col of the query block's 64 G query rows (token qr / G, head qr % G),
+// as the 16 columns of S^T = K Q^T. Each wave walks the query block's
+// selected blocks and then its own block (causal: a column sees its own
+// block's tokens up to its token) with a running softmax state, and writes
+// its normalized outputs. The eviction score is an additive logit as in the
+// decode kernel.
+struct PrefillArgs {
+    const void *q;          // [B][N][Hq][D]
+    const void *kv;         // block-unit KV [rows][kv_row_blocks][2*S*D]
+    int64_t kv_row_blocks;
+    const float *e_tok;     // [rows][e_stride]
+    int64_t e_stride;
+    const int32_t *sel;     // [n_qb][rows][k], ascending
+    const int32_t *n_sel;   // [n_qb][rows]
+    int n_tokens;
+    void *out;              // [B][N][Hq][D]
+};
+
+template <int D, int G>
+__global__ void __launch_bounds__(256)
+prefill_mfma_kernel(Dims dm, PrefillArgs a) {
+    constexpr int S = 64, KS = D / 32, DT = D / 16;
+    constexpr int64_t BE = 2 * S * D;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+    const int r = blockIdx.y, i = blockIdx.x / G, cg = blockIdx.x % G;
+    const int b = r / dm.Hkv, g = r % dm.Hkv;
+    const int qr = (4 * cg + wave) * 16 + col;
+    const int u = qr / G, h = qr % G;
+    const int p = S * i + u;
+    const bool live = p < a.n_tokens;
+    const int pc = live ? p : a.n_tokens - 1;
+    const bf16_t *q = static_cast<const bf16_t *>(a.q);
+    bf16x8 qop[KS];
+    {
+        const bf16_t *qh = q + (((int64_t)b * a.n_tokens + pc) * dm.Hq + (int64_t)g * G + h) * D + 8 * grp;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qop[s] = *reinterpret_cast<const bf16x8 *>(qh + 32 * s);
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int64_t li = (int64_t)i * dm.rows + r;
+    const int nsel = min(a.n_sel[li], dm.k);
+    const bf16_t *kvr = static_cast<const bf16_t *>(a.kv) + (int64_t)r * a.kv_row_blocks * BE;
+    const float *er = a.e_tok + (int64_t)r * a.e_stride;
+    for (int e = 0; e <= nsel; ++e) {
+        int bid, lim;
+        if (e < nsel) {
+            bid = a.sel[li * dm.k + e];
+            lim = S;
+            if (bid < 0 || bid >= i) continue;  // only blocks before the query block are listed
+        } else {
+            bid = i;
+            lim = u + 1;  // causal inside the query block
+        }
+        BlockRegs<D> br;
+        load_block<D>(br, kvr + (int64_t)bid * BE, er + (int64_t)bid * S, S, col, grp);
+        __builtin_amdgcn_sched_barrier(0);
+        attend_block<D>(br, qop, dm.scale, grp, lim, m_run, l_run, o);
+    }
+    if (live) {
+        const float inv = 1.0f / l_run;
+        bf16_t *out = static_cast<bf16_t *>(a.out) +
+                      (((int64_t)b * a.n_tokens + p) * dm.Hq + (int64_t)g * G + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) out[16 * dt + 4 * grp + v] = f2bf(o[dt][v] * inv);
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_pool_queries(const Dims &dm, const void *q, int n_tokens, void *qbar,
+                               hipStream_t st) {
+    const int nqb = (n_tokens + 63) / 64;
+    hipLaunchKernelGGL((pool_queries_kernel<T, D>), dim3(nqb, dm.B * dm.Hq), dim3(D), 0, st, dm,
+                       static_cast<const T *>(q), n_tokens, static_cast<T *>(qbar));
+    return hipGetLastError();
+}
+template hipError_t launch_pool_queries<float, 64>(const Dims &, const void *, int, void *,
+                                                   hipStream_t);
+template hipError_t launch_pool_queries<bf16_t, 64>(const Dims &, const void *, int, void *,
+                                                    hipStream_t);
+template hipError_t launch_pool_queries<bf16_t, 128>(const Dims &, const void *, int, void *,
+                                                     hipStream_t);
+
+template <int D, int G>
+hipError_t launch_prefill(const Dims &dm, const void *q, int n_tokens, const void *kv,
+                          int64_t kv_row_blocks, const float *e_tok, int64_t e_stride,
+                          const int32_t *sel, const int32_t *n_sel, void *out, hipStream_t st) {
+    const int nqb = (n_tokens + 63) / 64;
+    const PrefillArgs a{q, kv, kv_row_blocks, e_tok, e_stride, sel, n_sel, n_tokens, out};
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), dim3(nqb * G, dm.rows), dim3(256), 0, st, dm,
+                       a);
+    return hipGetLastError();
+}
+#define NOSA_PREFILL_INST(D, G)                                                                \
+    template hipError_t launch_prefill<D, G>(const Dims &, const void *, int, const void *,     \
+                                             int64_t, const float *, int64_t, const int32_t *,  \
+                                             const int32_t *, void *, hipStream_t);
+#define NOSA_PREFILL_ALLG(D)                                                                   \
+    NOSA_PREFILL_INST(D, 1) NOSA_PREFILL_INST(D, 2) NOSA_PREFILL_INST(D, 3)                    \
+    NOSA_PREFILL_INST(D, 4) NOSA_PREFILL_INST(D, 5) NOSA_PREFILL_INST(D, 6)                    \
+    NOSA_PREFILL_INST(D, 7) NOSA_PREFILL_INST(D, 8)
+NOSA_PREFILL_ALLG(64)
+NOSA_PREFILL_ALLG(128)
 
 // ---------------------------------------------------------------------------
 // VALU partial kernel (float32 and bf16): K and V^T tiles staged in LDS.

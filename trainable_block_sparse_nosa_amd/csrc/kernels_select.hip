@@ -53,22 +53,6 @@ __device__ __forceinline__ int64_t kbar_vec(const Dims &dm, int r, int sb, int d
     return (((int64_t)r * quads + (sb >> 4)) * (D / V) + dv) * (16 * V) + (int64_t)(sb & 15) * V;
 }
 
-// x (double) rounded to the nearest bfloat16, ties to even, with one
-// rounding: x is first rounded to float32 by rounding to odd (truncate, then
-// set the last bit if anything was dropped), which float32's 16 extra bits
-// make innocuous for the final round-to-nearest-even (Boldo and Melquiond,
-// "Emulation of FMA and correctly rounded sums: proved algorithms using
-// rounding to odd", IEEE Trans. Computers 57(4), 2008).
-__device__ __forceinline__ bf16_t bf16_rne_from_double(double x) {
-    float f = (float)x;
-    if ((double)f != x) {
-        uint32_t u = __float_as_uint(f);
-        if (fabs((double)f) > fabs(x)) u -= 1u;  // rounded away from zero: step back
-        f = __uint_as_float(u | 1u);
-    }
-    return f2bf(f);
-}
-
 // Sub-block mean of 16 keys in the storage type, key u from get(u): float32
 // keys sum in float32; bfloat16 keys sum exactly in double (16 values with 8
 // significant bits) and the exact mean is rounded once to bfloat16. Tokens

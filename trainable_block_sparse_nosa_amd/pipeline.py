@@ -209,6 +209,33 @@ class DecodeLayer:
         self.n_cand_prev = -1
         self.pooled = c0
 
+    def prefill(self, q_all: torch.Tensor, n_tokens: int, stream=None):
+        """Causal prefill of the first n_tokens tokens of the resident KV with
+        the selection per query block: q_all [batch, n_tokens, Hq, D] (bf16).
+        Returns (out [batch, n_tokens, Hq, D], sel [n_qb, rows, k], n_sel
+        [n_qb, rows]). Leaves K̄ and e_blk pooled for the complete blocks
+        before the last query block; a decode run starts with start()."""
+        if self.offload:
+            raise ValueError("prefill reads a resident KV")
+        nqb = -(-n_tokens // BLOCK)
+        dev = self.kbar.device
+        if nqb > 1:
+            L.nosa_pool_blocks(self.shape, self.kv, self.kv_row_blocks, 0, self.e_tok,
+                               self.e_stride, 0, nqb - 1, self.kbar, self.e_blk, stream)
+        qbar = torch.empty(nqb, *q_all.shape[:1], *q_all.shape[2:], dtype=q_all.dtype, device=dev)
+        self._run("pool_queries", L.nosa_prefill_pool_queries, self.shape, q_all, n_tokens, qbar,
+                  stream)
+        sel = torch.empty(nqb, self.rows, self.k, dtype=torch.int32, device=dev)
+        n_sel = torch.empty(nqb, self.rows, dtype=torch.int32, device=dev)
+        state = torch.empty(3, self.rows, self.W, dtype=torch.int32, device=dev)
+        self._run("prefill_select", L.nosa_prefill_select, self.shape, qbar, self.kbar,
+                  self.e_blk, n_tokens, self.s_q, state, sel, n_sel, stream)
+        out = torch.empty_like(q_all)
+        self._run("prefill_attention", L.nosa_prefill_attention, self.shape, q_all, n_tokens,
+                  self.kv, self.kv_row_blocks, self.e_tok, self.e_stride, sel, n_sel, out, stream)
+        self.n_cand_prev = -1
+        return out, sel, n_sel
+
     def _write_back(self, block: int, stream=None):
         """Newest-block buffer -> host KV block `block` (offloaded KV)."""
         self._fill(self.wb_fs[:, 0], block, stream)
