@@ -197,7 +197,8 @@ nosa_status nosa_prefill_select(const nosa_shape *shape, const void *qbar, const
  * out[b][p][h] = softmax over the tokens of query block i = p / S's selected
  * blocks and of tokens S*i .. p of z = scale * q.k + e (e_tok as an additive
  * logit, ED-DMA), times V. kv is the block-unit KV [rows][kv_row_blocks][2*S*D]
- * (kv_row_blocks >= n_qb; the last block may be partial), e_tok [rows][stride]
+ * (kv_row_blocks >= n_qb; the last block may be partial: its slots past
+ * n_tokens are read as zeros, whatever they hold), e_tok [rows][stride]
  * (stride >= n_qb * S, a multiple of 4), q and out [batch][n_tokens][Hq][D].
  * float32: NOSA_ERR_UNSUPPORTED. */
 nosa_status nosa_prefill_attention(const nosa_shape *shape, const void *q, int32_t n_tokens,

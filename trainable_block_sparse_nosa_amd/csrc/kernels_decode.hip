@@ -342,14 +342,17 @@ pool_queries_kernel(Dims dm, const T *__restrict__ q, int n_tokens, T *__restric
     else *out = bf16_rne_from_double(mean);
 }
 
-// Block-sparse causal attention (bf16, MFMA). Workgroup (query block i,
-// column group cg, row r), 4 waves; wave w owns 16 query rows qr = 16 (4 cg +
-// w) + col of the query block's 64 G query rows (token qr / G, head qr % G),
-// as the 16 columns of S^T = K Q^T. Each wave walks the query block's
-// selected blocks and then its own block (causal: a column sees its own
-// block's tokens up to its token) with a running softmax state, and writes
-// its normalized outputs. The eviction score is an additive logit as in the
-// decode kernel.
+// Block-sparse causal attention (bf16, MFMA). A workgroup takes ROWS query
+// rows of one query block i of row r (query row qr = G u + h: token u, head
+// h); each of its W waves owns CT tiles of 16 query rows, the 16 columns of
+// S^T = K Q^T. The workgroup walks the query block's selected blocks and then
+// its own block (causal: a column sees its own block's tokens up to its own
+// token). Each block is loaded once per workgroup into LDS, laid out in MFMA
+// fragment order (a wave's fragment read is 1 KiB contiguous), and double
+// buffered: the next block's loads are in flight while the current one is
+// used. Every K and V fragment read from LDS feeds the CT tiles of the wave.
+// The eviction score is an additive logit as in the decode kernel; the
+// output is normalized and stored in bf16.
 struct PrefillArgs {
     const void *q;          // [B][N][Hq][D]
     const void *kv;         // block-unit KV [rows][kv_row_blocks][2*S*D]
@@ -362,59 +365,265 @@ struct PrefillArgs {
     void *out;              // [B][N][Hq][D]
 };
 
+template <int G>
+struct PrefillShape {
+    static constexpr int CT = G == 1 ? 1 : 2;                       // tiles per wave
+    static constexpr int W = G == 1 ? 4 : (2 * G < 8 ? 2 * G : 8);  // waves per workgroup
+    static constexpr int ROWS = 16 * CT * W;                        // query rows per workgroup
+    static constexpr int NG = (64 * G + ROWS - 1) / ROWS;           // workgroups per query block
+    static_assert((64 * G) % (16 * CT) == 0, "a wave's tiles are all live or all idle");
+};
+
+// One KV block in LDS: K fragments (t, s) at t*KS + s, then V^T fragments
+// (dt, s) at 4 KS + 2 dt + s; lane l of fragment f holds the 16 bytes the
+// MFMA A operand of lane l needs. Then the block's 64 eviction scores.
+template <int D>
+struct PrefillTile {
+    static constexpr int KS = D / 32, DT = D / 16;
+    static constexpr int NF = 4 * KS + 2 * DT;
+    bf16x8 frag[NF][64];
+    float e[64];
+};
+
+template <int D, int NT>
+struct PrefillStage {
+    static constexpr int NF = PrefillTile<D>::NF;
+    static constexpr int CH = (NF * 64 + NT - 1) / NT;  // 16-byte chunks per thread
+    bf16x8 v[CH];
+    f32x4 e;
+};
+
+// Issue the global loads of one block (chunk x = tid + j NT is lane x % 64 of
+// fragment x / 64).
+template <int D, int NT>
+__device__ __forceinline__ void prefill_load(PrefillStage<D, NT> &st, const bf16_t *blk,
+                                             const float *eb, int tid) {
+    constexpr int S = 64, KS = D / 32, NF = PrefillTile<D>::NF;
+#pragma unroll
+    for (int j = 0; j < PrefillStage<D, NT>::CH; ++j) {
+        const int x = tid + j * NT;
+        if (NF * 64 % NT == 0 || x < NF * 64) {
+            const int f = x / 64, l = x % 64, col = l % 16, grp = l / 16;
+            const bf16_t *src;
+            if (f < 4 * KS) {
+                src = blk + (16 * (f / KS) + col) * D + 32 * (f % KS) + 8 * grp;
+            } else {
+                const int fv = f - 4 * KS;
+                src = blk + S * D + (16 * (fv / 2) + col) * S + 32 * (fv % 2) + 8 * grp;
+            }
+            st.v[j] = *reinterpret_cast<const bf16x8 *>(src);
+        }
+    }
+    if (tid < 16) st.e = *reinterpret_cast<const f32x4 *>(eb + 4 * tid);
+}
+
+// Write a staged block to LDS. Tokens from `valid` on (the tail of a
+// sequence's last block) are written as zeros, so that whatever the KV
+// storage holds there cannot reach the MFMA sums.
+template <int D, int NT>
+__device__ __forceinline__ void prefill_store(PrefillTile<D> &tl, const PrefillStage<D, NT> &st,
+                                              int valid, int tid) {
+    constexpr int KS = D / 32, NF = PrefillTile<D>::NF;
+#pragma unroll
+    for (int j = 0; j < PrefillStage<D, NT>::CH; ++j) {
+        const int x = tid + j * NT;
+        if (NF * 64 % NT == 0 || x < NF * 64) {
+            const int f = x / 64, l = x % 64, col = l % 16, grp = l / 16;
+            bf16x8 v = st.v[j];
+            if (valid < 64) {
+                if (f < 4 * KS) {
+                    if (16 * (f / KS) + col >= valid) v = bf16x8{};
+                } else {
+                    const int base = 32 * ((f - 4 * KS) % 2) + 8 * grp;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m)
+                        if (vt_token_at(base + m) >= valid) v[m] = 0;
+                }
+            }
+            tl.frag[f][l] = v;
+        }
+    }
+    if (tid < 16) *reinterpret_cast<f32x4 *>(&tl.e[4 * tid]) = st.e;
+}
+
+// One block against the wave's CT tiles, with running softmax states.
+template <int D, int CT>
+__device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
+                                              const bf16x8 (&qop)[CT][D / 32], float scale,
+                                              int lane, const int (&lim)[CT], float (&m_run)[CT],
+                                              float (&l_run)[CT], f32x4 (&o)[CT][D / 16]) {
+    constexpr int KS = D / 32, DT = D / 16;
+    const int grp = lane >> 4;
+    f32x4 sc[CT][4];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const bf16x8 kf = tl.frag[t * KS + s][lane];
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+                sc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qop[c][s], sc[c][t], 0, 0, 0);
+        }
+    f32x4 ev[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ev[t] = *reinterpret_cast<const f32x4 *>(&tl.e[16 * t + 4 * grp]);
+    bf16x8 phi[CT][2], plo[CT][2];
+    float alpha[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        float z[4][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool ok = 16 * t + 4 * grp + u < lim[c];
+                z[t][u] = ok ? fmaf(sc[c][t][u], scale, ev[t][u]) : -INFINITY;
+                mx = fmaxf(mx, z[t][u]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run[c], mx);
+        alpha[c] = m_run[c] == -INFINITY ? 0.f : __expf(m_run[c] - m_new);
+        float ps = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float p = z[t][u] == -INFINITY ? 0.f : __expf(z[t][u] - m_new);
+                const __bf16 hi = (__bf16)p;
+                phi[c][t / 2][(t % 2) * 4 + u] = hi;
+                plo[c][t / 2][(t % 2) * 4 + u] = (__bf16)(p - (float)hi);
+                ps += p;
+            }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        l_run[c] = l_run[c] * alpha[c] + ps;
+        m_run[c] = m_new;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 v0 = tl.frag[4 * KS + 2 * dt][lane];
+        const bf16x8 v1 = tl.frag[4 * KS + 2 * dt + 1][lane];
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            f32x4 acc = o[c][dt] * alpha[c];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, phi[c][0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, plo[c][0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, phi[c][1], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, plo[c][1], acc, 0, 0, 0);
+            o[c][dt] = acc;
+        }
+    }
+}
+
+// Workgroups are handed to the 8 XCDs in turn; give each XCD a contiguous
+// range of work items (the query blocks of a few rows), so that the blocks
+// those query blocks share are read from one L2.
+__device__ __forceinline__ int xcd_contiguous(int id, int total) {
+    constexpr int X = 8;
+    const int per = total / X, rem = total % X, x = id % X;
+    return x * per + min(x, rem) + id / X;
+}
+
 template <int D, int G>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * PrefillShape<G>::W)
 prefill_mfma_kernel(Dims dm, PrefillArgs a) {
-    constexpr int S = 64, KS = D / 32, DT = D / 16;
+    using Sh = PrefillShape<G>;
+    constexpr int S = 64, KS = D / 32, DT = D / 16, CT = Sh::CT, NT = 64 * Sh::W;
     constexpr int64_t BE = 2 * S * D;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __shared__ PrefillTile<D> tile[2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, grp = lane >> 4;
-    const int r = blockIdx.y, i = blockIdx.x / G, cg = blockIdx.x % G;
+    const int nqb = (a.n_tokens + S - 1) / S;
+    const int item = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int cg = item % Sh::NG, i = (item / Sh::NG) % nqb, r = item / (Sh::NG * nqb);
     const int b = r / dm.Hkv, g = r % dm.Hkv;
-    const int qr = (4 * cg + wave) * 16 + col;
-    const int u = qr / G, h = qr % G;
-    const int p = S * i + u;
-    const bool live = p < a.n_tokens;
-    const int pc = live ? p : a.n_tokens - 1;
+    const int row0 = Sh::ROWS * cg + 16 * CT * wave;  // first query row of the wave
+    const bool active = row0 < S * G;                 // wave-uniform
+    const int valid_own = min(S, a.n_tokens - S * i);
+
     const bf16_t *q = static_cast<const bf16_t *>(a.q);
-    bf16x8 qop[KS];
-    {
+    bf16x8 qop[CT][KS];
+    int lim[CT], u_of[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        const int qr = min(row0 + 16 * c + col, S * G - 1);
+        const int u = qr / G, h = qr % G;
+        const int pc = min(S * i + u, a.n_tokens - 1);
+        u_of[c] = u;
+        lim[c] = S;
         const bf16_t *qh = q + (((int64_t)b * a.n_tokens + pc) * dm.Hq + (int64_t)g * G + h) * D + 8 * grp;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) qop[s] = *reinterpret_cast<const bf16x8 *>(qh + 32 * s);
+        for (int s = 0; s < KS; ++s) qop[c][s] = *reinterpret_cast<const bf16x8 *>(qh + 32 * s);
     }
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 o[DT];
+    float m_run[CT], l_run[CT];
+    f32x4 o[CT][DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CT; ++c) {
+        m_run[c] = -INFINITY;
+        l_run[c] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
     const int64_t li = (int64_t)i * dm.rows + r;
-    const int nsel = min(a.n_sel[li], dm.k);
+    const int nsel = max(0, min(a.n_sel[li], dm.k));
+    const int32_t *sl = a.sel + li * dm.k;
     const bf16_t *kvr = static_cast<const bf16_t *>(a.kv) + (int64_t)r * a.kv_row_blocks * BE;
     const float *er = a.e_tok + (int64_t)r * a.e_stride;
-    for (int e = 0; e <= nsel; ++e) {
-        int bid, lim;
-        if (e < nsel) {
-            bid = a.sel[li * dm.k + e];
-            lim = S;
-            if (bid < 0 || bid >= i) continue;  // only blocks before the query block are listed
-        } else {
-            bid = i;
-            lim = u + 1;  // causal inside the query block
-        }
-        BlockRegs<D> br;
-        load_block<D>(br, kvr + (int64_t)bid * BE, er + (int64_t)bid * S, S, col, grp);
-        __builtin_amdgcn_sched_barrier(0);
-        attend_block<D>(br, qop, dm.scale, grp, lim, m_run, l_run, o);
+    // item e: selected block e for e < nsel (only blocks before the query
+    // block are listed; anything else is skipped), then the own block
+    auto block_of = [&](int e) {
+        const int bid = e < nsel ? sl[e] : i;
+        return (e == nsel || (bid >= 0 && bid < i)) ? bid : -1;
+    };
+
+    PrefillStage<D, NT> st;
+    int bid = block_of(0);
+    if (bid >= 0) {
+        prefill_load<D, NT>(st, kvr + (int64_t)bid * BE, er + (int64_t)bid * S, tid);
+        prefill_store<D, NT>(tile[0], st, nsel == 0 ? valid_own : S, tid);
     }
-    if (live) {
-        const float inv = 1.0f / l_run;
-        bf16_t *out = static_cast<bf16_t *>(a.out) +
-                      (((int64_t)b * a.n_tokens + p) * dm.Hq + (int64_t)g * G + h) * D;
+    __syncthreads();
+    for (int e = 0; e <= nsel; ++e) {
+        const int nb = e < nsel ? block_of(e + 1) : -1;
+        if (nb >= 0)
+            prefill_load<D, NT>(st, kvr + (int64_t)nb * BE, er + (int64_t)nb * S, tid);
+        if (active && bid >= 0) {
+            if (e == nsel) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+                for (int c = 0; c < CT; ++c) lim[c] = u_of[c] + 1;  // causal in the own block
+            }
+            prefill_block<D, CT>(tile[e & 1], qop, dm.scale, lane, lim, m_run, l_run, o);
+        }
+        if (nb >= 0) prefill_store<D, NT>(tile[(e + 1) & 1], st, e + 1 == nsel ? valid_own : S, tid);
+        __syncthreads();
+        bid = nb;
+    }
+
+    if (active) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) out[16 * dt + 4 * grp + v] = f2bf(o[dt][v] * inv);
+        for (int c = 0; c < CT; ++c) {
+            const int qr = row0 + 16 * c + col;
+            const int u = qr / G, h = qr % G, p = S * i + u;
+            if (qr < S * G && p < a.n_tokens) {
+                const float inv = 1.0f / l_run[c];
+                bf16_t *out = static_cast<bf16_t *>(a.out) +
+                              (((int64_t)b * a.n_tokens + p) * dm.Hq + (int64_t)g * G + h) * D;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        out[16 * dt + 4 * grp + v] = f2bf(o[c][dt][v] * inv);
+            }
+        }
     }
 }
 
@@ -437,10 +646,13 @@ template <int D, int G>
 hipError_t launch_prefill(const Dims &dm, const void *q, int n_tokens, const void *kv,
                           int64_t kv_row_blocks, const float *e_tok, int64_t e_stride,
                           const int32_t *sel, const int32_t *n_sel, void *out, hipStream_t st) {
-    const int nqb = (n_tokens + 63) / 64;
+    using Sh = PrefillShape<G>;
+    const int64_t nqb = (n_tokens + 63) / 64;
+    const int64_t wgs = nqb * Sh::NG * dm.rows;
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
     const PrefillArgs a{q, kv, kv_row_blocks, e_tok, e_stride, sel, n_sel, n_tokens, out};
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), dim3(nqb * G, dm.rows), dim3(256), 0, st, dm,
-                       a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), dim3((unsigned)wgs), dim3(64 * Sh::W), 0, st,
+                       dm, a);
     return hipGetLastError();
 }
 #define NOSA_PREFILL_INST(D, G)                                                                \
