@@ -365,6 +365,8 @@ struct PrefillArgs {
     void *out;              // [B][N][Hq][D]
 };
 
+constexpr float LOG2E = 1.4426950408889634f;
+
 template <int G>
 struct PrefillShape {
     static constexpr int CT = G == 1 ? 1 : 2;                       // tiles per wave
@@ -376,7 +378,8 @@ struct PrefillShape {
 
 // One KV block in LDS: K fragments (t, s) at t*KS + s, then V^T fragments
 // (dt, s) at 4 KS + 2 dt + s; lane l of fragment f holds the 16 bytes the
-// MFMA A operand of lane l needs. Then the block's 64 eviction scores.
+// MFMA A operand of lane l needs. Then the block's 64 eviction scores,
+// multiplied by log2(e) for the base-2 softmax.
 template <int D>
 struct PrefillTile {
     static constexpr int KS = D / 32, DT = D / 16;
@@ -443,13 +446,17 @@ __device__ __forceinline__ void prefill_store(PrefillTile<D> &tl, const PrefillS
             tl.frag[f][l] = v;
         }
     }
-    if (tid < 16) *reinterpret_cast<f32x4 *>(&tl.e[4 * tid]) = st.e;
+    if (tid < 16) *reinterpret_cast<f32x4 *>(&tl.e[4 * tid]) = st.e * LOG2E;
 }
 
-// One block against the wave's CT tiles, with running softmax states.
-template <int D, int CT>
+// One block against the wave's CT tiles, with running softmax states kept in
+// the base-2 domain: z2 = log2(e) (scale q.k + e). The block's eviction
+// scores arrive already multiplied by log2(e). CAUSAL masks, per column, the
+// tokens from lim[c] on (the own block); the other blocks are whole. P
+// enters P V as bf16 (the outputs are bf16), its row sums stay in float32.
+template <int D, int CT, bool CAUSAL>
 __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
-                                              const bf16x8 (&qop)[CT][D / 32], float scale,
+                                              const bf16x8 (&qop)[CT][D / 32], float scale2,
                                               int lane, const int (&lim)[CT], float (&m_run)[CT],
                                               float (&l_run)[CT], f32x4 (&o)[CT][D / 16]) {
     constexpr int KS = D / 32, DT = D / 16;
@@ -471,8 +478,9 @@ __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
     f32x4 ev[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) ev[t] = *reinterpret_cast<const f32x4 *>(&tl.e[16 * t + 4 * grp]);
-    bf16x8 phi[CT][2], plo[CT][2];
+    bf16x8 pb[CT][2];
     float alpha[CT];
+    bool rescale = false;
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
         float z[4][4];
@@ -481,23 +489,24 @@ __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const bool ok = 16 * t + 4 * grp + u < lim[c];
-                z[t][u] = ok ? fmaf(sc[c][t][u], scale, ev[t][u]) : -INFINITY;
+                z[t][u] = fmaf(sc[c][t][u], scale2, ev[t][u]);
+                if (CAUSAL && 16 * t + 4 * grp + u >= lim[c]) z[t][u] = -INFINITY;
                 mx = fmaxf(mx, z[t][u]);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_run[c], mx);
-        alpha[c] = m_run[c] == -INFINITY ? 0.f : __expf(m_run[c] - m_new);
+        // a column with no token yet subtracts 0: exp2(-inf - 0) = 0, no NaN
+        const float m_sub = m_new == -INFINITY ? 0.f : m_new;
+        alpha[c] = __builtin_amdgcn_exp2f(m_run[c] - m_sub);
+        rescale |= alpha[c] != 1.f;
         float ps = 0.f;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const float p = z[t][u] == -INFINITY ? 0.f : __expf(z[t][u] - m_new);
-                const __bf16 hi = (__bf16)p;
-                phi[c][t / 2][(t % 2) * 4 + u] = hi;
-                plo[c][t / 2][(t % 2) * 4 + u] = (__bf16)(p - (float)hi);
+                const float p = __builtin_amdgcn_exp2f(z[t][u] - m_sub);
+                pb[c][t / 2][(t % 2) * 4 + u] = (__bf16)p;
                 ps += p;
             }
         ps += __shfl_xor(ps, 16, 64);
@@ -505,18 +514,21 @@ __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
         l_run[c] = l_run[c] * alpha[c] + ps;
         m_run[c] = m_new;
     }
+    // most blocks move no column's maximum: skip the rescale then
+    if (__any(rescale)) {
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[c][dt] *= alpha[c];
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
         const bf16x8 v0 = tl.frag[4 * KS + 2 * dt][lane];
         const bf16x8 v1 = tl.frag[4 * KS + 2 * dt + 1][lane];
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-            f32x4 acc = o[c][dt] * alpha[c];
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, phi[c][0], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, plo[c][0], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, phi[c][1], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, plo[c][1], acc, 0, 0, 0);
-            o[c][dt] = acc;
+            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb[c][0], o[c][dt], 0, 0, 0);
+            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pb[c][1], o[c][dt], 0, 0, 0);
         }
     }
 }
@@ -548,6 +560,7 @@ prefill_mfma_kernel(Dims dm, PrefillArgs a) {
     const int row0 = Sh::ROWS * cg + 16 * CT * wave;  // first query row of the wave
     const bool active = row0 < S * G;                 // wave-uniform
     const int valid_own = min(S, a.n_tokens - S * i);
+    const float scale2 = dm.scale * LOG2E;
 
     const bf16_t *q = static_cast<const bf16_t *>(a.q);
     bf16x8 qop[CT][KS];
@@ -592,20 +605,21 @@ prefill_mfma_kernel(Dims dm, PrefillArgs a) {
         prefill_store<D, NT>(tile[0], st, nsel == 0 ? valid_own : S, tid);
     }
     __syncthreads();
-    for (int e = 0; e <= nsel; ++e) {
-        const int nb = e < nsel ? block_of(e + 1) : -1;
+    for (int e = 0; e < nsel; ++e) {
+        const int nb = block_of(e + 1);
         if (nb >= 0)
             prefill_load<D, NT>(st, kvr + (int64_t)nb * BE, er + (int64_t)nb * S, tid);
-        if (active && bid >= 0) {
-            if (e == nsel) {
-#pragma unroll
-                for (int c = 0; c < CT; ++c) lim[c] = u_of[c] + 1;  // causal in the own block
-            }
-            prefill_block<D, CT>(tile[e & 1], qop, dm.scale, lane, lim, m_run, l_run, o);
-        }
+        if (active && bid >= 0)
+            prefill_block<D, CT, false>(tile[e & 1], qop, scale2, lane, lim, m_run, l_run, o);
         if (nb >= 0) prefill_store<D, NT>(tile[(e + 1) & 1], st, e + 1 == nsel ? valid_own : S, tid);
         __syncthreads();
         bid = nb;
+    }
+    // the own block, item nsel, causal per column
+    if (active) {
+#pragma unroll
+        for (int c = 0; c < CT; ++c) lim[c] = u_of[c] + 1;
+        prefill_block<D, CT, true>(tile[nsel & 1], qop, scale2, lane, lim, m_run, l_run, o);
     }
 
     if (active) {
