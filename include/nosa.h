@@ -187,11 +187,11 @@ nosa_status nosa_prefill_pool_queries(const nosa_shape *shape, const void *q, in
 
 /* Selection of every query block i (candidates 0..i-1): sel [n_qb][rows][k]
  * ascending, -1 padded, and n_sel [n_qb][rows], as nosa_score_select with no
- * previous step would select for query qbar[i] (one launch per query block).
- * s_q [rows][max_blocks] and state uint32 [3][rows][W] are scratch. */
+ * previous step would select for query qbar[i]. One launch for all query
+ * blocks; n_qb <= max_blocks + 1 and n_qb <= 65535. */
 nosa_status nosa_prefill_select(const nosa_shape *shape, const void *qbar, const void *kbar,
-                                const float *e_blk, int32_t n_tokens, float *s_q,
-                                uint32_t *state, int32_t *sel, int32_t *n_sel, void *stream);
+                                const float *e_blk, int32_t n_tokens, int32_t *sel,
+                                int32_t *n_sel, void *stream);
 
 /* Causal block-sparse attention of the whole sequence (bf16, matrix cores):
  * out[b][p][h] = softmax over the tokens of query block i = p / S's selected

@@ -77,7 +77,7 @@ def _load() -> ctypes.CDLL:
         "nosa_append_tokens": [SH, P, P, I32, P, I64, I32, P],
         "nosa_ingest_tokens": [SH, P, P, P, P, I32, I32, P, P, I64, I32, P, I64, P, P, P],
         "nosa_prefill_pool_queries": [SH, P, I32, P, P],
-        "nosa_prefill_select": [SH, P, P, P, I32, P, P, P, P, P],
+        "nosa_prefill_select": [SH, P, P, P, I32, P, P, P],
         "nosa_prefill_attention": [SH, P, I32, P, I64, P, I64, P, P, P, P],
         "nosa_decode_partial": [SH, P, P, I64, I32, P, P, I32, I32, I32, P, I64, ST, P, I64, P, SZ,
                                 I32, P],
@@ -239,10 +239,10 @@ def nosa_prefill_pool_queries(shape, q, n_tokens, qbar, stream=None):
         ctypes.byref(shape), _p(q), n_tokens, _p(qbar), _s(stream)))
 
 
-def nosa_prefill_select(shape, qbar, kbar, e_blk, n_tokens, s_q, state, sel, n_sel, stream=None):
+def nosa_prefill_select(shape, qbar, kbar, e_blk, n_tokens, sel, n_sel, stream=None):
     _chk("nosa_prefill_select", _L.nosa_prefill_select(
-        ctypes.byref(shape), _p(qbar), _p(kbar), _p(e_blk), n_tokens, _p(s_q), _p(state),
-        _p(sel), _p(n_sel), _s(stream)))
+        ctypes.byref(shape), _p(qbar), _p(kbar), _p(e_blk), n_tokens, _p(sel), _p(n_sel),
+        _s(stream)))
 
 
 def nosa_prefill_attention(shape, q, n_tokens, kv, kv_row_blocks, e_tok, e_row_stride, sel, n_sel,

@@ -360,31 +360,21 @@ nosa_status nosa_prefill_pool_queries(const nosa_shape *shape, const void *q, in
 }
 
 nosa_status nosa_prefill_select(const nosa_shape *shape, const void *qbar, const void *kbar,
-                                const float *e_blk, int32_t n_tokens, float *s_q,
-                                uint32_t *state, int32_t *sel, int32_t *n_sel, void *stream) {
+                                const float *e_blk, int32_t n_tokens, int32_t *sel,
+                                int32_t *n_sel, void *stream) {
     Dims dm;
     nosa_status s = make_dims(shape, &dm);
     if (s != NOSA_OK) return s;
-    if (!qbar || !kbar || !e_blk || !s_q || !state || !sel || !n_sel || n_tokens <= 0)
+    if (!qbar || !kbar || !e_blk || !sel || !n_sel || n_tokens <= 0)
         return NOSA_ERR_INVALID_ARGUMENT;
     const int nqb = (n_tokens + dm.S - 1) / dm.S;
-    if (nqb - 1 >= dm.max_blocks) return NOSA_ERR_INVALID_ARGUMENT;
-    const int64_t qstride = (int64_t)dm.B * dm.Hq * dm.D;
-    const int elem = dm.dtype == NOSA_BF16 ? 2 : 4;
-    uint32_t *ge = state, *ev = state + (int64_t)dm.rows * dm.W, *sb = ev + (int64_t)dm.rows * dm.W;
+    if (nqb - 1 >= dm.max_blocks || nqb > 65535) return NOSA_ERR_INVALID_ARGUMENT;
     return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
         using T = std::remove_pointer_t<decltype(tp)>;
         constexpr int D = decltype(dc)::value;
         return by_group(dm, [&](auto gc) -> nosa_status {
-            for (int i = 0; i < nqb; ++i) {
-                // query block i: candidates 0..i-1, selected afresh (no previous step)
-                const void *qi = static_cast<const char *>(qbar) + i * qstride * elem;
-                const hipError_t e = launch_score_select<T, D, decltype(gc)::value>(
-                    dm, qi, kbar, s_q, e_blk, i, -1, ge, ev, sel + (int64_t)i * dm.rows * dm.k,
-                    n_sel + (int64_t)i * dm.rows, sb, nullptr, (hipStream_t)stream);
-                if (e != hipSuccess) return hip_status(e);
-            }
-            return NOSA_OK;
+            return hip_status(launch_prefill_select<T, D, decltype(gc)::value>(
+                dm, qbar, kbar, e_blk, nqb, sel, n_sel, (hipStream_t)stream));
         });
     });
 }

@@ -38,6 +38,13 @@ hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, 
                                uint32_t *ev, int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
                                const SwapPtrs *swap, hipStream_t st);
 
+// Selection of every query block i < n_qb of a sequence (candidates 0..i-1,
+// no previous step) in one launch: sel [n_qb][rows][k], n_sel [n_qb][rows].
+template <typename T, int D, int G>
+hipError_t launch_prefill_select(const Dims &dm, const void *qbar, const void *kbar,
+                                 const float *e_blk, int n_qb, int32_t *sel, int32_t *n_sel,
+                                 hipStream_t st);
+
 hipError_t launch_swap(const Dims &dm, const int32_t *sel, const int32_t *n_sel,
                        const uint32_t *sel_bits, const SwapPtrs &swap, hipStream_t st);
 

@@ -450,18 +450,19 @@ template <typename T, int D, int G>
 struct ScoresFused {
     const T *q;
     const T *kbar;
-    float *s_q;
+    float *s_q;          // may be null: scores stay in LDS
+    int64_t q_step = 0;  // query offset per workgroup row y (batched selections)
     __device__ const float *row(const Dims &dm, int r, int n_cand) const {
         constexpr int M = 4, V = KbarVec<T>::V, NV = D / V, U = sizeof(T) == 2 ? 2 : 1;
         __shared__ float qs[G][D];
         __shared__ float sc[MAX_W * 32];
         const int tid = threadIdx.x, nt = blockDim.x;
         const int b = r / dm.Hkv, g = r % dm.Hkv;
-        const T *qr = q + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
+        const T *qr = q + blockIdx.y * q_step + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
         for (int p = tid; p < G * D; p += nt) (&qs[0][0])[p] = ldf(qr + p) * dm.scale;
         __syncthreads();
         const int nsb = M * n_cand;
-        float *out = s_q + (int64_t)r * dm.max_blocks;
+        float *out = s_q ? s_q + (int64_t)r * dm.max_blocks : nullptr;
         for (int base = 0; base < nsb; base += U * nt) {
             // compiler-only memory barrier: keeps the LDS reads of q inside the
             // pass (hoisted out of it, G * D floats would not fit in registers)
@@ -500,7 +501,7 @@ struct ScoresFused {
                 for (int h = 0; h < G; ++h) sum += quad_max(acc[h]);
                 if (sb < nsb && (sb & (M - 1)) == 0) {
                     sc[sb / M] = sum;
-                    out[sb / M] = sum;
+                    if (out) out[sb / M] = sum;
                 }
             }
         }
@@ -522,7 +523,8 @@ template <int D, int G>
 struct ScoresFusedMfma {
     const bf16_t *q;
     const bf16_t *kbar;
-    float *s_q;
+    float *s_q;          // may be null: scores stay in LDS
+    int64_t q_step = 0;  // query offset per workgroup row y (batched selections)
     __device__ const float *row(const Dims &dm, int r, int n_cand) const {
         constexpr int KS = D / 32, TPI = 4;  // k-steps; tiles per pass per wave
         static_assert(G <= 16, "the group is one 16-wide MFMA tile");
@@ -535,7 +537,8 @@ struct ScoresFusedMfma {
         // B operand: lane holds q[head col][32 s + 8 grp .. + 7]; zero past G
         bf16x8 qop[KS];
         {
-            const bf16_t *qh = q + ((int64_t)b * dm.Hq + (int64_t)g * G + (col < G ? col : 0)) * D +
+            const bf16_t *qh = q + blockIdx.y * q_step +
+                               ((int64_t)b * dm.Hq + (int64_t)g * G + (col < G ? col : 0)) * D +
                                8 * grp;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
@@ -546,7 +549,7 @@ struct ScoresFusedMfma {
         const int nsb = 4 * n_cand;
         // row r's quads of 16 sub-blocks, in bf16x8 vectors: [Q][D/8][16]
         const bf16x8 *kb = reinterpret_cast<const bf16x8 *>(kbar + kbar_vec<bf16_t, D>(dm, r, 0, 0));
-        float *out = s_q + (int64_t)r * dm.max_blocks;
+        float *out = s_q ? s_q + (int64_t)r * dm.max_blocks : nullptr;
         const int n_tiles = (nsb + 15) / 16;
         for (int t0 = wave * TPI; t0 < n_tiles; t0 += nw * TPI) {
             bf16x8 a[TPI][KS];
@@ -575,7 +578,7 @@ struct ScoresFusedMfma {
                 const int blk = 4 * (t0 + u) + grp;
                 if (col == 0 && blk < n_cand) {
                     sc[blk] = m;
-                    out[blk] = m;
+                    if (out) out[blk] = m;
                 }
             }
         }
@@ -584,12 +587,20 @@ struct ScoresFusedMfma {
     }
 };
 
+// Independent selections in one launch (workgroup row y = blockIdx.y): y
+// has n_cand + y * cand_step candidates and writes sel / n_sel shifted by y
+// steps. A single selection has gridDim.y = 1.
+struct BatchArgs {
+    int cand_step;
+    int64_t sel_step, nsel_step;
+};
+
 template <typename Src>
 __global__ void __launch_bounds__(SELECT_THREADS)
-select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand,
+select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
               int n_prev, int P, uint32_t *__restrict__ ge_bits, uint32_t *__restrict__ ev_bits,
               int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
-              uint32_t *__restrict__ sel_bits, SwapArgs sw, ListArgs lists) {
+              uint32_t *__restrict__ sel_bits, SwapArgs sw, ListArgs lists, BatchArgs bt) {
     extern __shared__ uint64_t keys[];  // P keys, only when a budget exceeds 64
     __shared__ uint32_t ge[MAX_W], ev[MAX_W], sb[MAX_W], res[MAX_W];
     __shared__ __attribute__((aligned(16))) uint64_t surv[SELECT_WAVES * WAVE_TOPK + 2];
@@ -602,9 +613,13 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand,
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int W = dm.W;
+    const int n_cand = n_cand0 + blockIdx.y * bt.cand_step;
+    sel += blockIdx.y * bt.sel_step;
+    n_sel += blockIdx.y * bt.nsel_step;
     const float *E = e_blk + (int64_t)r * dm.max_blocks;
-    uint32_t *ge_g = ge_bits + (int64_t)r * W;
-    uint32_t *ev_g = ev_bits + (int64_t)r * W;
+    // eviction state and selection bitmap: absent (null) for batched selections
+    uint32_t *ge_g = ge_bits ? ge_bits + (int64_t)r * W : nullptr;
+    uint32_t *ev_g = ev_bits ? ev_bits + (int64_t)r * W : nullptr;
 
     // independent loads first: the cache's slot table and counters, then this
     // thread's scores
@@ -617,7 +632,7 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand,
     }
     // the eviction state: word tid (W <= MAX_W <= the workgroup size)
     uint32_t ge_w = 0u, ev_w = 0u;
-    if (n_prev >= 0 && tid < W) {
+    if (n_prev >= 0 && ge_g && tid < W) {
         ge_w = ge_g[tid];
         ev_w = ev_g[tid];
     }
@@ -726,10 +741,12 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand,
     __syncthreads();
 
     // ---- state and the ascending selection ----
-    for (int w = tid; w < W; w += nt) {
-        ge_g[w] = ge[w];
-        ev_g[w] = ev[w];
-        sel_bits[(int64_t)r * W + w] = sb[w];
+    if (ge_g) {
+        for (int w = tid; w < W; w += nt) {
+            ge_g[w] = ge[w];
+            ev_g[w] = ev[w];
+            sel_bits[(int64_t)r * W + w] = sb[w];
+        }
     }
     if (wave != 0) return;
     // wave 0 writes the ascending lists: the union, and each part when asked
@@ -956,12 +973,14 @@ static hipError_t launch_select_from(const Dims &dm, const Src &src, const float
                                      int n_cand, int n_prev, uint32_t *ge, uint32_t *ev,
                                      int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
                                      const SwapPtrs *swap, const SelectLists *parts,
-                                     hipStream_t st) {
+                                     hipStream_t st, int batch = 1) {
     // LDS keys only when a budget is above what the register top-k holds
+    // (batch > 1: selections y = 0..batch-1 with y candidates each)
+    const int max_cand = batch > 1 ? batch - 1 : n_cand;
     int P = 0;
     if ((n_prev < 0 && dm.k_e > WAVE_TOPK) || dm.k_q > WAVE_TOPK) {
         P = 2;
-        while (P < n_cand) P <<= 1;
+        while (P < max_cand) P <<= 1;
     }
     SwapArgs sw{};
     if (swap) {
@@ -974,9 +993,11 @@ static hipError_t launch_select_from(const Dims &dm, const Src &src, const float
     }
     ListArgs li{};
     if (parts) li = ListArgs{parts->ge_list, parts->n_ge, parts->gq_list, parts->n_gq};
-    hipLaunchKernelGGL(select_kernel<Src>, dim3(dm.rows), dim3(SELECT_THREADS),
-                       P * sizeof(uint64_t), st, dm, src, e_blk, n_cand, n_prev, P, ge, ev, sel,
-                       n_sel, sel_bits, sw, li);
+    const BatchArgs bt = batch > 1 ? BatchArgs{1, (int64_t)dm.rows * dm.k, dm.rows}
+                                   : BatchArgs{0, 0, 0};
+    hipLaunchKernelGGL(select_kernel<Src>, dim3(dm.rows, batch), dim3(SELECT_THREADS),
+                       P * sizeof(uint64_t), st, dm, src, e_blk, batch > 1 ? 0 : n_cand, n_prev, P,
+                       ge, ev, sel, n_sel, sel_bits, sw, li, bt);
     return hipGetLastError();
 }
 
@@ -1003,6 +1024,24 @@ hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, 
                                        s_q};
         return launch_select_from(dm, src, e_blk, n_cand, n_prev, ge, ev, sel, n_sel, sel_bits,
                                   swap, nullptr, st);
+    }
+}
+
+template <typename T, int D, int G>
+hipError_t launch_prefill_select(const Dims &dm, const void *qbar, const void *kbar,
+                                 const float *e_blk, int n_qb, int32_t *sel, int32_t *n_sel,
+                                 hipStream_t st) {
+    const int64_t q_step = (int64_t)dm.B * dm.Hq * D;
+    if constexpr (std::is_same_v<T, bf16_t>) {
+        const ScoresFusedMfma<D, G> src{static_cast<const bf16_t *>(qbar),
+                                        static_cast<const bf16_t *>(kbar), nullptr, q_step};
+        return launch_select_from(dm, src, e_blk, 0, -1, nullptr, nullptr, sel, n_sel, nullptr,
+                                  nullptr, nullptr, st, n_qb);
+    } else {
+        const ScoresFused<T, D, G> src{static_cast<const T *>(qbar), static_cast<const T *>(kbar),
+                                       nullptr, q_step};
+        return launch_select_from(dm, src, e_blk, 0, -1, nullptr, nullptr, sel, n_sel, nullptr,
+                                  nullptr, nullptr, st, n_qb);
     }
 }
 
@@ -1074,7 +1113,10 @@ NOSA_POOL_INST(bf16_t, 128)
                                                float *, hipStream_t);                          \
     template hipError_t launch_score_select<T, D, G>(                                          \
         const Dims &, const void *, const void *, float *, const float *, int, int, uint32_t *, \
-        uint32_t *, int32_t *, int32_t *, uint32_t *, const SwapPtrs *, hipStream_t);
+        uint32_t *, int32_t *, int32_t *, uint32_t *, const SwapPtrs *, hipStream_t);          \
+    template hipError_t launch_prefill_select<T, D, G>(                                        \
+        const Dims &, const void *, const void *, const float *, int, int32_t *, int32_t *,    \
+        hipStream_t);
 #define NOSA_SCORE_ALLG(T, D)                                                                  \
     NOSA_SCORE_INST(T, D, 1) NOSA_SCORE_INST(T, D, 2) NOSA_SCORE_INST(T, D, 3)                 \
     NOSA_SCORE_INST(T, D, 4) NOSA_SCORE_INST(T, D, 5) NOSA_SCORE_INST(T, D, 6)                 \

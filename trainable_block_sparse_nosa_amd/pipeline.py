@@ -227,9 +227,8 @@ class DecodeLayer:
                   stream)
         sel = torch.empty(nqb, self.rows, self.k, dtype=torch.int32, device=dev)
         n_sel = torch.empty(nqb, self.rows, dtype=torch.int32, device=dev)
-        state = torch.empty(3, self.rows, self.W, dtype=torch.int32, device=dev)
         self._run("prefill_select", L.nosa_prefill_select, self.shape, qbar, self.kbar,
-                  self.e_blk, n_tokens, self.s_q, state, sel, n_sel, stream)
+                  self.e_blk, n_tokens, sel, n_sel, stream)
         out = torch.empty_like(q_all)
         self._run("prefill_attention", L.nosa_prefill_attention, self.shape, q_all, n_tokens,
                   self.kv, self.kv_row_blocks, self.e_tok, self.e_stride, sel, n_sel, out, stream)
