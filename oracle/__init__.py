@@ -74,6 +74,10 @@ def lib():
             L.oracle_prefill_row.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_int,
                                                                  _f, _f, _f, _f, _d, _i]
             L.oracle_prefill_row.restype = ctypes.c_int
+            L.oracle_prefill_qblock.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_int,
+                                                                      _f, _f, _f, _f, ctypes.c_int,
+                                                                      _d, _i]
+            L.oracle_prefill_qblock.restype = None
             L.oracle_step_row.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_int,
                                                               _f, _f, _f, _f,
                                                               _i, _i, _i, _i, _d, _d, _d]
@@ -302,4 +306,21 @@ def prefill_row(q, K, V, e, block: int, sub: int, k_e: int, k_q: int, scale: flo
     sel = np.full((nqb, max(k_e + k_q, 1)), -1, np.int32)
     lib().oracle_prefill_row(N, G, D, block, sub, k_e, k_q, scale, int(pooled_bf16), _pf(q),
                              _pf(K), _pf(V), _pf(e), _pd(out), _pi(sel))
+    return Prefill(out, sel[:, :k_e + k_q])
+
+
+def prefill_qblock(q, K, V, e, i: int, block: int, sub: int, k_e: int, k_q: int, scale: float,
+                   pooled_bf16: bool = False) -> Prefill:
+    """Query block i alone of a row's prefill (what prefill_row computes for
+    it): out [tokens of block i, G, D], sel [1, k]. q [N, G, D]; K, V [N, D];
+    e [N]."""
+    q, K, V, e = _f32(q), _f32(K), _f32(V), _f32(e)
+    N, G, D = q.shape
+    if not 0 <= i < -(-N // block):
+        raise ValueError("query block out of range")
+    n = min(block, N - i * block)
+    out = np.zeros((n, G, D), np.float64)
+    sel = np.full((1, max(k_e + k_q, 1)), -1, np.int32)
+    lib().oracle_prefill_qblock(N, G, D, block, sub, k_e, k_q, scale, int(pooled_bf16), _pf(q),
+                                _pf(K), _pf(V), _pf(e), i, _pd(out), _pi(sel))
     return Prefill(out, sel[:, :k_e + k_q])

@@ -299,16 +299,20 @@ void oracle_pool_queries(const float *q, int n, int G, int D, int pooled_bf16, f
         }
 }
 
-/* Prefill of one row: N tokens, q [N][G][D], K and V [N][D], e [N].
-   Writes out [N][G][D] and, for every query block i, its ascending selection
-   sel[i * (k_e + k_q) ...] (-1 padded). Returns the number of query blocks. */
-int oracle_prefill_row(int N, int G, int D, int block, int sub, int k_e, int k_q, double scale,
-                       int pooled_bf16, const float *q, const float *K, const float *V,
-                       const float *e, double *out, int *sel)
+/* Query block i of a row's prefill (N tokens, q [N][G][D], K and V [N][D],
+   e [N]): its tokens lo = i*block .. hi-1 select among the blocks before it,
+   Gamma_e by pooled eviction score and Gamma_q by the score of the block's
+   pooled query, and attend the selected blocks' tokens plus, causally, their
+   own block up to themselves. Writes out [hi - lo][G][D] and the ascending
+   selection sel[0 .. k_e + k_q - 1] (-1 padded). */
+void oracle_prefill_qblock(int N, int G, int D, int block, int sub, int k_e, int k_q,
+                           double scale, int pooled_bf16, const float *q, const float *K,
+                           const float *V, const float *e, int i, double *out, int *sel)
 {
-    int nqb = (N + block - 1) / block;
     int k = k_e + k_q;
-    int cmax = nqb > 1 ? nqb - 1 : 1;
+    int c = i;  /* candidates: blocks 0..i-1 */
+    int lo = i * block, hi = lo + block < N ? lo + block : N;
+    int cmax = c > 0 ? c : 1;
     double *Eb = (double *)malloc(sizeof(double) * (size_t)cmax);
     double *Sb = (double *)malloc(sizeof(double) * (size_t)cmax);
     unsigned char *rest = (unsigned char *)malloc((size_t)cmax);
@@ -317,42 +321,38 @@ int oracle_prefill_row(int N, int G, int D, int block, int sub, int k_e, int k_q
     int *gq = (int *)malloc(sizeof(int) * (size_t)(k_q > 0 ? k_q : 1));
     int *tok = (int *)malloc(sizeof(int) * (size_t)(k * block + block));
     float *qbar = (float *)malloc(sizeof(float) * (size_t)G * (size_t)D);
-    for (int j = 0; j + 1 < nqb; ++j)
+    for (int j = 0; j < c; ++j)
         Eb[j] = oracle_block_evict(e, block, sub, j);
-    for (int i = 0; i < nqb; ++i) {
-        int lo = i * block, hi = lo + block < N ? lo + block : N;
-        int c = i;  /* candidates: blocks 0..i-1 */
-        oracle_pool_queries(q + (int64_t)lo * G * D, hi - lo, G, D, pooled_bf16, qbar);
-        for (int j = 0; j < c; ++j)
-            Sb[j] = oracle_block_score(qbar, G, D, K, block, sub, j, scale, pooled_bf16);
-        int n_ge = oracle_topk(Eb, NULL, c, k_e, ge);
-        for (int j = 0; j < c; ++j)
-            rest[j] = 1;
-        for (int t = 0; t < n_ge; ++t)
-            rest[ge[t]] = 0;
-        int n_gq = oracle_topk(Sb, rest, c, k_q, gq);
-        for (int j = 0; j < c; ++j)
-            pick[j] = 0;
-        for (int t = 0; t < n_ge; ++t)
-            pick[ge[t]] = 1;
-        for (int t = 0; t < n_gq; ++t)
-            pick[gq[t]] = 1;
-        int ns = 0, nt = 0;
-        for (int j = 0; j < c; ++j)
-            if (pick[j]) {
-                sel[i * k + ns++] = j;
-                for (int u = 0; u < block; ++u)
-                    tok[nt++] = j * block + u;
-            }
-        for (int t = ns; t < k; ++t)
-            sel[i * k + t] = -1;
-        for (int p = lo; p < hi; ++p) {
-            int m = nt;
-            for (int u = lo; u <= p; ++u)
-                tok[m++] = u;
-            oracle_attend_tokens(q + (int64_t)p * G * D, G, D, K, V, e, tok, m, scale,
-                                 out + (int64_t)p * G * D);
+    oracle_pool_queries(q + (int64_t)lo * G * D, hi - lo, G, D, pooled_bf16, qbar);
+    for (int j = 0; j < c; ++j)
+        Sb[j] = oracle_block_score(qbar, G, D, K, block, sub, j, scale, pooled_bf16);
+    int n_ge = oracle_topk(Eb, NULL, c, k_e, ge);
+    for (int j = 0; j < c; ++j)
+        rest[j] = 1;
+    for (int t = 0; t < n_ge; ++t)
+        rest[ge[t]] = 0;
+    int n_gq = oracle_topk(Sb, rest, c, k_q, gq);
+    for (int j = 0; j < c; ++j)
+        pick[j] = 0;
+    for (int t = 0; t < n_ge; ++t)
+        pick[ge[t]] = 1;
+    for (int t = 0; t < n_gq; ++t)
+        pick[gq[t]] = 1;
+    int ns = 0, nt = 0;
+    for (int j = 0; j < c; ++j)
+        if (pick[j]) {
+            sel[ns++] = j;
+            for (int u = 0; u < block; ++u)
+                tok[nt++] = j * block + u;
         }
+    for (int t = ns; t < k; ++t)
+        sel[t] = -1;
+    for (int p = lo; p < hi; ++p) {
+        int m = nt;
+        for (int u = lo; u <= p; ++u)
+            tok[m++] = u;
+        oracle_attend_tokens(q + (int64_t)p * G * D, G, D, K, V, e, tok, m, scale,
+                             out + (int64_t)(p - lo) * G * D);
     }
     free(qbar);
     free(tok);
@@ -362,5 +362,18 @@ int oracle_prefill_row(int N, int G, int D, int block, int sub, int k_e, int k_q
     free(rest);
     free(Sb);
     free(Eb);
+}
+
+/* Prefill of one row: every query block in turn. Writes out [N][G][D] and
+   sel [n_qb][k_e + k_q]. Returns the number of query blocks. */
+int oracle_prefill_row(int N, int G, int D, int block, int sub, int k_e, int k_q, double scale,
+                       int pooled_bf16, const float *q, const float *K, const float *V,
+                       const float *e, double *out, int *sel)
+{
+    int nqb = (N + block - 1) / block;
+    int k = k_e + k_q;
+    for (int i = 0; i < nqb; ++i)
+        oracle_prefill_qblock(N, G, D, block, sub, k_e, k_q, scale, pooled_bf16, q, K, V, e, i,
+                              out + (int64_t)i * block * G * D, sel + i * k);
     return nqb;
 }

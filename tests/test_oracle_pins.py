@@ -465,6 +465,42 @@ def test_prefill_query_selection_by_brute_force():
         assert res.sel[i][:len(best)].tolist() == best
 
 
+def test_prefill_qblock_by_brute_force():
+    """One query block alone, both parts of the budget: its selection is the
+    k_e best eviction blocks plus the k_q best query-scored blocks of the
+    rest; its tokens attend those blocks and their own block causally. The
+    ragged last query block included."""
+    rng = np.random.default_rng(44)
+    N, G, D, ke, kq, sc = 64 * 7 + 20, 2, 8, 2, 2, 0.3
+    q = rng.normal(size=(N, G, D)).astype(np.float32)
+    K = rng.normal(size=(N, D)).astype(np.float32)
+    V = rng.normal(size=(N, D)).astype(np.float32)
+    e = rng.normal(size=N).astype(np.float32)
+    Kd = K.astype(np.float64)
+    E = [max(float(np.mean(e[64 * j + 16 * s:64 * j + 16 * s + 16].astype(np.float64)))
+             for s in range(4)) for j in range(N // 64)]
+    full = oracle.prefill_row(q, K, V, e, 64, 16, ke, kq, sc)
+    for i in (0, 1, 4, 7):
+        lo, hi = 64 * i, min(64 * i + 64, N)
+        qb = q[lo:hi].astype(np.float64).mean(axis=0).astype(np.float32)
+        S = [sum(max(sc * float(Kd[64 * j + 16 * s:64 * j + 16 * s + 16].mean(axis=0)
+                                @ qb[h].astype(np.float64)) for s in range(4))
+                 for h in range(G)) for j in range(i)]
+        ge = sorted(range(i), key=lambda j: (-E[j], j))[:ke]
+        gq = sorted((j for j in range(i) if j not in ge), key=lambda j: (-S[j], j))[:kq]
+        want_sel = sorted(ge + gq)
+        res = oracle.prefill_qblock(q, K, V, e, i, 64, 16, ke, kq, sc)
+        assert res.sel[0][:len(want_sel)].tolist() == want_sel
+        assert all(x == -1 for x in res.sel[0][len(want_sel):])
+        want = _np_causal(q[lo:hi], K, V, e, sc,
+                          lambda p: [64 * j + u for j in want_sel for u in range(64)]
+                          + list(range(lo, lo + p + 1)))
+        np.testing.assert_allclose(res.out, want, rtol=1e-12, atol=1e-12)
+        # the same block of the whole-row call
+        np.testing.assert_array_equal(res.out, full.out[lo:hi])
+        assert res.sel[0].tolist() == full.sel[i].tolist()
+
+
 def test_pool_queries_bf16():
     """Integer inputs: the exact means are floats, so rounding them to bf16 is
     the bit-level rounding of those floats."""
