@@ -231,6 +231,12 @@ EDGE = {
     "k128": dict(context=9000, steps=4, k_e=96, k_q=32),
     # query-aware budget above 64: LDS top-k every step
     "kq_large": dict(context=9000, steps=70, k_e=20, k_q=80),
+    # 65..67 candidates: the second wave of the select kernel holds one to
+    # three keys, fewer than the budget, while the first holds more than it;
+    # the threshold must still be the exact k-th key
+    "wave_tail_evict": dict(context=4161, steps=3, k_e=40, k_q=16, n_q_heads=16,
+                            n_kv_heads=8),
+    "wave_tail_query": dict(context=4161, steps=130, k_e=8, k_q=40),
 }
 
 

@@ -219,14 +219,24 @@ __device__ uint64_t wave_kth_key(const uint64_t (&x)[M], int k) {
 // sets the selected indices' bits in `bits` (LDS). Returns nothing; the
 // caller synchronises before reading `bits`.
 // k-th key (k <= 64) among the survivors surv[0..ns) by wave 0, with M2
-// survivors per lane.
+// survivors per lane. The search may stop at a value between the (k+1)-th
+// and the k-th survivor; keys that did not survive (below their own wave's
+// k-th) can lie in that gap when another wave held fewer than k keys, so the
+// k-th survivor itself is returned: the smallest survivor at or above it.
 template <int M2>
 __device__ uint64_t survivors_kth(const uint64_t *surv, int ns, int k) {
     const int lane = threadIdx.x & 63;
     uint64_t y[M2];
 #pragma unroll
     for (int i = 0; i < M2; ++i) y[i] = lane + 64 * i < ns ? surv[lane + 64 * i] : 0ull;
-    return wave_kth_key<M2>(y, k);
+    const uint64_t t = wave_kth_key<M2>(y, k);
+    uint64_t mn = ~0ull;
+#pragma unroll
+    for (int i = 0; i < M2; ++i)
+        if (y[i] != 0ull && y[i] >= t) mn = umin64(mn, y[i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mn = umin64(mn, __shfl_xor(mn, o, 64));
+    return mn;
 }
 
 template <int M>
