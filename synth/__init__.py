@@ -230,20 +230,26 @@ def queries_step(w: Workload, layer: int, t: int, ov: Overrides | None = None) -
     return _to_dtype(z, w.dtype)
 
 
-def prefill_queries(w: Workload, layer: int, n_tokens: int, ov: Overrides | None = None) -> np.ndarray:
+def prefill_queries(w: Workload, layer: int, n_tokens: int, ov: Overrides | None = None,
+                    batch: int | None = None, workers: int = 8) -> np.ndarray:
     """Queries of every token of a prefilled sequence: [batch, n_tokens, n_q_heads, D]
-    ~ N(0, 1) in the input dtype. ``ov.query[("prefill", layer, b, g, i)] = a``
-    regenerates query block i (its 64 tokens) of KV head g's query heads from
-    attempt a."""
-    z = stream(w.seed, "QP", layer, n_tokens).standard_normal(
-        (w.batch, n_tokens, w.n_q_heads, w.head_dim), dtype=np.float32)
+    ~ N(0, 1) in the input dtype, one stream per batch entry (``batch=b``:
+    entry b alone, [n_tokens, n_q_heads, D]). ``ov.query[("prefill", layer, b,
+    g, i)] = a`` regenerates query block i (its 64 tokens) of KV head g's query
+    heads from attempt a."""
+    if batch is None:
+        return np.stack(parallel_map(lambda b: prefill_queries(w, layer, n_tokens, ov, b),
+                                     range(w.batch), workers))
+    b0 = batch
+    z = stream(w.seed, "QP", layer, n_tokens, b0).standard_normal(
+        (n_tokens, w.n_q_heads, w.head_dim), dtype=np.float32)
     if ov is not None:
         G = w.group
         for key, a in list(ov.query.items()):
-            if len(key) == 5 and key[0] == "prefill" and key[1] == layer and a > 0:
+            if len(key) == 5 and key[0] == "prefill" and key[1] == layer and key[2] == b0 and a > 0:
                 _, _, b, g, i = key
                 lo, hi = 64 * i, min(64 * i + 64, n_tokens)
-                z[b, lo:hi, g * G:(g + 1) * G] = stream(w.seed, "QP", layer, b, g, i, a).standard_normal(
+                z[lo:hi, g * G:(g + 1) * G] = stream(w.seed, "QP", layer, b, g, i, a).standard_normal(
                     (hi - lo, G, w.head_dim), dtype=np.float32)
     return _to_dtype(z, w.dtype)
 

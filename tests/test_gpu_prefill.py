@@ -100,3 +100,95 @@ def test_prefill_parity(name):
             assert sel[i, r, :n].tolist() == want, f"{name} row {r} query block {i}"
         np.testing.assert_allclose(out[b, :, g * G:(g + 1) * G], ref[r].out,
                                    err_msg=f"{name} row {r}", **TOL)
+
+
+# Full size: the 32k-token context of the 8-sequence, 32/8-head, D 128
+# workload (k = 48 + 16), in the launch configuration the benchmark times.
+# Every (query block, row) is checked for properties that hold at any size;
+# sampled rows and query blocks (first, small, around k, middle, last) are
+# checked against the oracle, with their selection margins enforced.
+FULL_ROWS = (0, 29, 63)
+FULL_QBLOCKS = (0, 1, 47, 64, 65, 200, 511)
+
+
+def _fullsize_margins(w: Workload):
+    N, G = w.context, w.group
+    sc = 1.0 / math.sqrt(w.head_dim)
+    ov = Overrides()
+    cmax = max(FULL_QBLOCKS)
+    for r in FULL_ROWS:
+        b, g = divmod(r, w.n_kv_heads)
+        K, _ = row_kv(w, 0, b, g)
+        for _ in range(256):
+            e = synth.evict_row(w, 0, b, g, ov)
+            E = np.array([oracle.block_evict(e, 64, 16, j) for j in range(cmax)])
+            bad = None
+            for i in FULL_QBLOCKS:
+                ok, lower = boundary_ok(E[:i], w.k_e)
+                if not ok:
+                    bad = lower
+                    break
+            if bad is None:
+                break
+            key = (0, b, g, bad)
+            ov.evict[key] = ov.evict.get(key, 0) + 1
+        else:
+            raise RuntimeError("eviction margins")
+        qrow = synth.prefill_queries(w, 0, N, ov, batch=b)
+        for i in FULL_QBLOCKS:
+            if i <= w.k:
+                continue  # every candidate is selected
+            ge = set(sorted(range(i), key=lambda j: (-E[j], j))[:w.k_e])
+            rest = [j for j in range(i) if j not in ge]
+            for _ in range(64):
+                q = qrow[64 * i:64 * i + 64, g * G:(g + 1) * G]
+                qb = oracle.pool_queries(q, pooled_bf16=True)
+                S = np.array([oracle.block_score(qb, K, 64, 16, j, sc, pooled_bf16=True)
+                              for j in rest])
+                if boundary_ok(S, w.k_q)[0]:
+                    break
+                key = ("prefill", 0, b, g, i)
+                ov.query[key] = ov.query.get(key, 0) + 1
+                qrow = synth.prefill_queries(w, 0, N, ov, batch=b)
+            else:
+                raise RuntimeError("query margins")
+    return ov
+
+
+def test_prefill_fullsize_sampled():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gpu_harness as gh
+    w = synth.WORKLOADS["bf16_1layer_32k"]
+    N, G, k = w.context, w.group, w.k
+    sc = 1.0 / math.sqrt(w.head_dim)
+    ov = _fullsize_margins(w)
+    inp = gh.upload(w, ov=ov, steps=1)
+    q_all = gh.to_device(gh.storage(synth.prefill_queries(w, 0, N, ov), w), w)
+    layer = gh.make_layer(w, inp)
+    out, sel, n_sel = layer.prefill(q_all, N)
+    torch.cuda.synchronize()
+    sel, n_sel = sel.cpu().numpy(), n_sel.cpu().numpy()
+    nqb = N // 64
+    # any size: query block i selects min(k, i) distinct earlier blocks, ascending
+    for i in range(nqb):
+        want_n = min(k, i)
+        assert (n_sel[i] == want_n).all(), f"query block {i}"
+        s = sel[i]
+        if want_n:
+            assert (s[:, :want_n] >= 0).all() and (s[:, :want_n] < i).all()
+            assert (np.diff(s[:, :want_n], axis=1) > 0).all()
+        assert (s[:, want_n:] == -1).all()
+    assert torch.isfinite(out).all()
+    for r in FULL_ROWS:
+        b, g = divmod(r, w.n_kv_heads)
+        K, V = row_kv(w, 0, b, g)
+        e = synth.evict_row(w, 0, b, g, ov)
+        q = synth.prefill_queries(w, 0, N, ov, batch=b)[:, g * G:(g + 1) * G]
+        for i in FULL_QBLOCKS:
+            ref = oracle.prefill_qblock(q, K[:N], V[:N], e[:N], i, 64, 16, w.k_e, w.k_q, sc,
+                                        pooled_bf16=True)
+            want = [j for j in ref.sel[0] if j >= 0]
+            assert sel[i, r, :len(want)].tolist() == want, f"row {r} query block {i}"
+            got = out[b, 64 * i:64 * i + 64, g * G:(g + 1) * G].float().cpu().numpy()
+            np.testing.assert_allclose(got, ref.out, err_msg=f"row {r} query block {i}", **TOL)
