@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the leg that prefills the workload's context with the selection "
                          "per query block (block-sparse causal attention on the matrix cores)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the resident runs with the Infinity Cache flushed before each "
+                         "step (a 1 GiB scratch read, then a 512 MiB scratch write)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 4 device-to-device copies of 512 MiB (a reference kernel "
                          "of known traffic for hardware byte counters)")
@@ -463,6 +466,83 @@ def h2d_peak_gbs(dev, nbytes=1 << 30, reps=5):
     return best
 
 
+def read_probe_gbs(dev, nbytes=2 << 30, reps=10):
+    """Achievable streaming HBM read bandwidth: the library's read probe over a
+    buffer 8x the 256 MB Infinity Cache, best of `reps` launches (HIP events
+    on the launch stream)."""
+    import torch
+    from trainable_block_sparse_nosa_amd import _lib as L
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream()
+    L.nosa_read_probe(src, nbytes, sink, 2048, st)
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        L.nosa_read_probe(src, nbytes, sink, 2048, st)
+        e1.record(st)
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, sink
+    torch.cuda.empty_cache()
+    return best
+
+
+def cold_cache_run(layer, w, q, args, stream, n_steps: int, scratch_mib: int = 1024,
+                   mode: str = "read"):
+    """The resident workload with the Infinity Cache (256 MB) flushed before
+    every step by touching scratch_mib MiB of scratch memory: mode "read"
+    streams it through the read probe (clean lines: nothing to write back),
+    mode "write" fills it (the dirty lines it leaves are written back while the
+    next kernel runs, and that cost lands on the step's first kernels). HIP
+    events around the attention partial launch of each step."""
+    import torch
+    from trainable_block_sparse_nosa_amd import _lib as L
+    scratch = torch.zeros(scratch_mib << 20, dtype=torch.uint8, device=torch.device("cuda"))
+    sink = torch.zeros(1, dtype=torch.int32, device=scratch.device)
+    n = min(n_steps, args.warmup + args.steps)
+    ev = HipTimingEvents(2 * n + 2)
+    done = []
+
+    def hook(name, fn, *a):
+        if name == "decode":
+            on = a[-1] if a[-1] is not None else torch.cuda.current_stream()
+            h = on.cuda_stream if hasattr(on, "cuda_stream") else int(on)
+            i0 = 2 * len(done)
+            ev.record(i0, h)
+            fn(*a)
+            ev.record(i0 + 1, h)
+            done.append((t, i0))
+        else:
+            fn(*a)
+
+    layer.start(w.n_tokens(0), stream)
+    on = stream if stream is not None else torch.cuda.current_stream()
+    layer.stage_hook = hook
+    for t in range(n):
+        if mode == "read":
+            L.nosa_read_probe(scratch, scratch.numel(), sink, 2048, on)
+        else:
+            with torch.cuda.stream(on):
+                scratch.fill_(t & 0xFF)
+        run_step(layer, q, None, t, w.n_tokens(t), stream)
+    torch.cuda.synchronize()
+    layer.stage_hook = None
+    c0 = w.n_cand(0)
+    n_blk = min(w.k_e, c0) + min(w.k_q, c0 - min(w.k_e, c0))
+    # the first step's launch includes the eviction top-k start; skip it
+    res = [(ev.elapsed_ms(i0, i0 + 1), attn_bytes(w, "decode", w.n_tokens(t), n_blk))
+           for t, i0 in done[1:]]
+    ev.close()
+    del scratch, sink
+    ms = sum(a for a, _ in res) / len(res)
+    gbs = sum(b for _, b in res) / (sum(a for a, _ in res) / 1e3) / 1e9
+    return {"flush": mode, "scratch_mib": scratch_mib, "steps": len(res),
+            "avg_launch_us": ms * 1e3, "achieved_gbs": gbs, "frac": gbs / HBM_PEAK_GBS}
+
+
 def offload_leg(args, dev, stream):
     """The 128k-context offloaded workload: steps/s and swap GB/s of the fetch
     kernel against the measured pinned-host-to-HBM copy bandwidth. Each step's
@@ -481,6 +561,7 @@ def offload_leg(args, dev, stream):
     block_bytes = 2 * 64 * w.head_dim * 2
     swap_gbs = fetched * block_bytes / fetch_s / 1e9
     peak = h2d_peak_gbs(dev)
+    zc = zero_copy_contiguous_gbs(layer, w, stream)
     counters = layer.counters.cpu().numpy()
     T = sub.warmup + sub.steps
     out = {
@@ -489,6 +570,7 @@ def offload_leg(args, dev, stream):
         "fetched_mib_per_step": fetched * block_bytes / sub.steps / 2**20,
         "fetch_us_per_step": fetch_s / sub.steps * 1e6,
         "swap_gbs": swap_gbs, "h2d_memcpy_gbs": peak, "frac_of_h2d": swap_gbs / peak,
+        "zero_copy_contiguous_gbs": zc,
         "attn_partial_us_per_step": sum(dec_ms) / len(dec_ms) * 1e3,
         "gamma_mean": float(counters[:, 1].sum()) / (w.rows * w.k * T),
         "device_append": True,
@@ -499,6 +581,29 @@ def offload_leg(args, dev, stream):
     kv.free()
     del layer, q
     return out
+
+
+def zero_copy_contiguous_gbs(layer, w, stream, reps=3):
+    """The fetch kernel over contiguous host blocks (blocks 0..k-1 of every row
+    into slots 0..k-1): the zero-copy read rate without the scatter of a
+    selection."""
+    import torch
+    from trainable_block_sparse_nosa_amd import _lib as L
+    dev = layer.cache.device
+    k = w.k
+    fb = torch.arange(k, dtype=torch.int32, device=dev).repeat(w.rows, 1).contiguous()
+    nf = torch.full((w.rows,), k, dtype=torch.int32, device=dev)
+    on = stream if stream is not None else torch.cuda.current_stream()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(on)
+        L.nosa_fetch_blocks(layer.shape, layer.kv, layer.kv_row_blocks, fb, fb, nf, k,
+                            layer.cache, k, on)
+        e1.record(on)
+        torch.cuda.synchronize()
+        best = max(best, w.rows * k * 2 * 64 * w.head_dim * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    return best
 
 
 def locality_ablation(w, layer, q, kv, sub, dev, stream, nosa_run, block_bytes, new):
@@ -627,6 +732,15 @@ def main():
     stages = None
     if not args.no_stage_breakdown:
         stages = stage_breakdown(layer, w, q, args.warmup, min(args.steps, 50), stream)
+    cold = None
+    if not w.offload and not args.no_cold:
+        cold = {m: cold_cache_run(layer, w, q, args, stream, 21, mib, m)
+                for m, mib in (("read", 1024), ("write", 512))}
+        for m, c in cold.items():
+            log(f"cache flushed by a {c['scratch_mib']} MiB scratch {m} before each step: "
+                f"attention partial {c['avg_launch_us']:.1f} us, {c['achieved_gbs']:.0f} GB/s")
+    probe = read_probe_gbs(dev)
+    log(f"streaming-read probe: {probe:.0f} GB/s")
     if not w.offload:
         del layer, q, kv
         torch.cuda.empty_cache()
@@ -683,7 +797,9 @@ def main():
             "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name),
             "avg_launch_us": dec_avg_s * 1e6, "algorithmic_bytes_per_launch": bytes_avg,
             "launches_per_step": len(ev) / args.steps,
+            "read_probe_gbs": probe, "frac_of_read_probe": achieved / probe,
         },
+        "cold_cache": cold,
         "attn_partial_us_per_step": attn_step_us,
         "overlap": overlapped,
         "gamma_mean": gamma_mean,

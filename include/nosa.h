@@ -364,6 +364,15 @@ nosa_status nosa_decode_combine(const nosa_shape *shape, int32_t n_chunks, void 
 nosa_status nosa_host_alloc(size_t bytes, int32_t coherent, void **host, void **dev);
 nosa_status nosa_host_free(void *host);
 
+/* Measurement utility, not a step of the method: reads `bytes` (> 0, a
+ * multiple of 16) of device memory at src (16-byte aligned) once with
+ * `workgroups` workgroups of 256 threads, 16-byte loads, eight in flight per
+ * thread; sink (one uint32, device memory) is written only on a magic value.
+ * Timing it gives the achievable streaming-read bandwidth, the second
+ * denominator for the HBM-bound kernels. */
+nosa_status nosa_read_probe(const void *src, int64_t bytes, uint32_t *sink, int32_t workgroups,
+                            void *stream);
+
 const char *nosa_status_string(nosa_status s);
 /* Text of the last HIP error seen by a call on this thread ("" if none). */
 const char *nosa_last_error(void);

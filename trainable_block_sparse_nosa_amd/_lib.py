@@ -34,8 +34,8 @@ EXPORTS = (
     "nosa_ingest_tokens", "nosa_prefill_pool_queries", "nosa_prefill_select",
     "nosa_prefill_attention", "nosa_decode_workspace_size", "nosa_decode_chunks",
     "nosa_sparse_decode", "nosa_decode_partial", "nosa_decode_combine",
-    "nosa_host_alloc", "nosa_host_free", "nosa_status_string", "nosa_last_error",
-    "nosa_version",
+    "nosa_host_alloc", "nosa_host_free", "nosa_read_probe", "nosa_status_string",
+    "nosa_last_error", "nosa_version",
 )
 
 
@@ -84,6 +84,7 @@ def _load() -> ctypes.CDLL:
         "nosa_decode_combine": [SH, I32, P, P, SZ, P],
         "nosa_host_alloc": [SZ, I32, ctypes.POINTER(P), ctypes.POINTER(P)],
         "nosa_host_free": [P],
+        "nosa_read_probe": [P, I64, P, I32, P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -276,6 +277,11 @@ def nosa_host_alloc(nbytes: int, coherent: bool = False) -> tuple[int, int]:
 
 def nosa_host_free(host: int):
     _chk("nosa_host_free", _L.nosa_host_free(host))
+
+
+def nosa_read_probe(src, nbytes: int, sink, workgroups: int = 2048, stream=None):
+    _chk("nosa_read_probe", _L.nosa_read_probe(_p(src), nbytes, _p(sink), workgroups,
+                                               _s(stream)))
 
 
 def nosa_version() -> int:

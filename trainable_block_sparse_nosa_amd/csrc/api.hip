@@ -550,6 +550,14 @@ const char *nosa_status_string(nosa_status s) {
 
 const char *nosa_last_error(void) { return g_last_error.c_str(); }
 
+nosa_status nosa_read_probe(const void *src, int64_t bytes, uint32_t *sink, int32_t workgroups,
+                            void *stream) {
+    if (!src || !sink || bytes <= 0 || (bytes & 15) || workgroups <= 0 ||
+        (reinterpret_cast<uintptr_t>(src) & 15))
+        return NOSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_read_probe(src, bytes, sink, workgroups, (hipStream_t)stream));
+}
+
 int32_t nosa_version(void) { return 100; }
 
 }  // extern "C"

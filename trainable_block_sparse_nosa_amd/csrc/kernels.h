@@ -114,4 +114,8 @@ template <typename T, int D, int G>
 hipError_t launch_combine(const Dims &dm, int n_chunks, int chunk_cap, const float *ws_o,
                           const float *ws_ml, void *out, hipStream_t st);
 
+// Streaming read of `bytes` (a multiple of 16) from src by `wgs` workgroups.
+hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, int wgs,
+                             hipStream_t st);
+
 }  // namespace nosa
