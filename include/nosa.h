@@ -124,7 +124,10 @@ typedef struct nosa_shape {
     float scale;           /* logit scale; 0 means 1/sqrt(head_dim) */
 } nosa_shape;
 
-/* Where the decode is: read on the host during each call. */
+/* Where the decode is. The entry points below that take `const nosa_step
+ * *step` read it on the host during the call; the *_step entry points
+ * (graph-replayable steps, at the end of this header) take it in device
+ * memory instead and read it in their kernels. */
 typedef struct nosa_step {
     int32_t n_tokens;    /* tokens present, including the one appended this step */
     int32_t n_cand_prev; /* candidate blocks at the previous step; -1: no previous
@@ -357,6 +360,57 @@ nosa_status nosa_decode_partial(const nosa_shape *shape, const void *q, const vo
  * chunk order and writes out [batch][n_q_heads][D]. */
 nosa_status nosa_decode_combine(const nosa_shape *shape, int32_t n_chunks, void *out, void *ws,
                                 size_t ws_bytes, void *stream);
+
+/* ---- steps replayed from a captured graph ----
+ * The step record lives in device memory (step_dev: a nosa_step, 8 bytes,
+ * 4-byte aligned) and every call of a step reads it in its kernels, so one
+ * decode step, captured once into a hipGraph, can be replayed step after
+ * step: nosa_step_advance, the step's last call, moves the record on. The
+ * calls take the same arguments as their host-step forms and compute the same
+ * results for the same record. No call allocates, synchronises or memsets.
+ * Values the record holds are clamped to the shape's capacity (n_tokens to
+ * 1 .. max_blocks * S), so buffers sized for max_blocks are never left; the
+ * caller keeps n_tokens within that capacity for meaningful results. One
+ * token per step: at most one block completes per step. */
+
+/* step_dev->n_cand_prev = (n_tokens - 1) / S; step_dev->n_tokens += 1. */
+nosa_status nosa_step_advance(const nosa_shape *shape, nosa_step *step_dev, void *stream);
+
+/* nosa_pool_blocks for the block completed since the previous step: when
+ * n_cand_prev >= 0 and n_cand = (n_tokens - 1) / S exceeds it, pools block
+ * n_cand_prev of kv (the full block-unit KV, kv_row_blocks >= max_blocks);
+ * otherwise does nothing. e_row_stride >= max_blocks * S. */
+nosa_status nosa_pool_step(const nosa_shape *shape, const void *kv, int64_t kv_row_blocks,
+                           const float *e_tok, int64_t e_row_stride, const nosa_step *step_dev,
+                           void *kbar, float *e_blk, void *stream);
+
+/* nosa_append_tokens with pos = (n_tokens - 1) % S and block = (n_tokens - 1) / S
+ * of the full KV (kv_row_blocks >= max_blocks). */
+nosa_status nosa_append_step(const nosa_shape *shape, const void *k_new, const void *v_new,
+                             void *kv, int64_t kv_row_blocks, const nosa_step *step_dev,
+                             void *stream);
+
+/* nosa_score_select with the step record in device memory. */
+nosa_status nosa_score_select_step(const nosa_shape *shape, const void *q, const void *kbar,
+                                   const float *e_blk, const nosa_step *step_dev, float *s_q,
+                                   uint32_t *ge_bits, uint32_t *ev_bits, int32_t *sel,
+                                   int32_t *n_sel, uint32_t *sel_bits, int32_t *slot_block,
+                                   int32_t *block_slot, int32_t *fetch_block,
+                                   int32_t *fetch_slot, int32_t *n_fetch, uint64_t *counters,
+                                   void *stream);
+
+/* nosa_decode_partial with the step record in device memory. With
+ * NOSA_KV_FULL, cur_kv is the full KV (cur_row_blocks >= max_blocks) and the
+ * newest block is its block n_cand; with NOSA_KV_CACHE, block 0 of cur_kv (the
+ * newest-block buffer). Validated against the capacity: e_row_stride >=
+ * max_blocks * S, and with NOSA_KV_FULL kv_row_blocks >= max_blocks. */
+nosa_status nosa_decode_partial_step(const nosa_shape *shape, const void *q, const void *kv,
+                                     int64_t kv_row_blocks, int32_t kv_mode, const int32_t *list,
+                                     const int32_t *n_list, int32_t list_stride,
+                                     int32_t list_len, int32_t with_newest, const void *cur_kv,
+                                     int64_t cur_row_blocks, const nosa_step *step_dev,
+                                     const float *e_tok, int64_t e_row_stride, void *ws,
+                                     size_t ws_bytes, int32_t chunk0, void *stream);
 
 /* Pinned host memory readable by GPU kernels: *host is the host address,
  * *dev the device alias to pass as a kernel source. coherent != 0 asks for

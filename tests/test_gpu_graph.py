@@ -1,0 +1,72 @@
+"""Decode steps replayed from a captured graph: the step record lives in
+device memory, every call of the step reads it in its kernels and the step's
+last call moves it on. Each replayed step is compared with the fp64 oracle
+like an eagerly launched one: selections, swap lists and slot tables
+bit-exact, outputs within the dtype's tolerance."""
+import pytest
+
+import synth
+from harness import oracle_trace
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gpu_harness
+    return gpu_harness
+
+
+@pytest.mark.parametrize("name,append", [("small_bf16", False), ("small_bf16", True),
+                                         ("small_f32", False), ("small_f32", True)])
+def test_graph_replayed_steps(name, append):
+    gh = _gpu()
+    from test_gpu_parity import _compare_step
+    w = synth.WORKLOADS[name]
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov, prefix_only=append)
+    layer = gh.make_layer(w, inp, fuse_score=True, device_append=append)
+    layer.start(w.n_tokens(0))
+    q_buf = torch.empty_like(inp.q[0])
+    kb = torch.empty_like(inp.k_new[0]) if append else None
+    vb = torch.empty_like(inp.v_new[0]) if append else None
+    graph = layer.graph_capture(w.n_tokens(0), q_buf, kb, vb)
+    for t in range(w.steps):
+        q_buf.copy_(inp.q[t])
+        if append:
+            kb.copy_(inp.k_new[t])
+            vb.copy_(inp.v_new[t])
+        graph.replay()
+        got = gh.snapshot(layer, w)
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, got)
+    last = w.steps - 1
+    assert layer.step_dev.cpu().tolist() == [w.n_tokens(last) + 1, w.n_cand(last)]
+
+
+def test_eager_steps_continue_after_replays():
+    """Half the steps replayed, the rest launched eagerly on the same layer."""
+    gh = _gpu()
+    from test_gpu_parity import _compare_step
+    w = synth.WORKLOADS["small_bf16"]
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov)
+    layer = gh.make_layer(w, inp, fuse_score=True)
+    layer.start(w.n_tokens(0))
+    q_buf = torch.empty_like(inp.q[0])
+    graph = layer.graph_capture(w.n_tokens(0), q_buf)
+    half = w.steps // 2
+    for t in range(w.steps):
+        if t < half:
+            q_buf.copy_(inp.q[t])
+            graph.replay()
+            if t == half - 1:
+                torch.cuda.synchronize()
+                layer.graph_done(w.n_tokens(t))
+        else:
+            layer.step(inp.q[t], w.n_tokens(t))
+        got = gh.snapshot(layer, w)
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, got)

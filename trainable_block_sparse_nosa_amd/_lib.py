@@ -34,6 +34,8 @@ EXPORTS = (
     "nosa_ingest_tokens", "nosa_prefill_pool_queries", "nosa_prefill_select",
     "nosa_prefill_attention", "nosa_decode_workspace_size", "nosa_decode_chunks",
     "nosa_sparse_decode", "nosa_decode_partial", "nosa_decode_combine",
+    "nosa_step_advance", "nosa_pool_step", "nosa_append_step", "nosa_score_select_step",
+    "nosa_decode_partial_step",
     "nosa_host_alloc", "nosa_host_free", "nosa_read_probe", "nosa_status_string",
     "nosa_last_error", "nosa_version",
 )
@@ -85,6 +87,12 @@ def _load() -> ctypes.CDLL:
         "nosa_host_alloc": [SZ, I32, ctypes.POINTER(P), ctypes.POINTER(P)],
         "nosa_host_free": [P],
         "nosa_read_probe": [P, I64, P, I32, P],
+        "nosa_step_advance": [SH, P, P],
+        "nosa_pool_step": [SH, P, I64, P, I64, P, P, P, P],
+        "nosa_append_step": [SH, P, P, P, I64, P, P],
+        "nosa_score_select_step": [SH, P, P, P, P] + [P] * 12 + [P],
+        "nosa_decode_partial_step": [SH, P, P, I64, I32, P, P, I32, I32, I32, P, I64, P, P, I64,
+                                     P, SZ, I32, P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -277,6 +285,44 @@ def nosa_host_alloc(nbytes: int, coherent: bool = False) -> tuple[int, int]:
 
 def nosa_host_free(host: int):
     _chk("nosa_host_free", _L.nosa_host_free(host))
+
+
+# Steps replayed from a captured graph: `step_dev` is a device buffer holding a
+# nosa_step (int32 n_tokens, n_cand_prev), e.g. torch.int32 tensor of 2.
+
+def nosa_step_advance(shape, step_dev, stream=None):
+    _chk("nosa_step_advance", _L.nosa_step_advance(ctypes.byref(shape), _p(step_dev), _s(stream)))
+
+
+def nosa_pool_step(shape, kv, kv_row_blocks, e_tok, e_row_stride, step_dev, kbar, e_blk,
+                   stream=None):
+    _chk("nosa_pool_step", _L.nosa_pool_step(
+        ctypes.byref(shape), _p(kv), kv_row_blocks, _p(e_tok), e_row_stride, _p(step_dev),
+        _p(kbar), _p(e_blk), _s(stream)))
+
+
+def nosa_append_step(shape, k_new, v_new, kv, kv_row_blocks, step_dev, stream=None):
+    _chk("nosa_append_step", _L.nosa_append_step(
+        ctypes.byref(shape), _p(k_new), _p(v_new), _p(kv), kv_row_blocks, _p(step_dev),
+        _s(stream)))
+
+
+def nosa_score_select_step(shape, q, kbar, e_blk, step_dev, s_q, ge_bits, ev_bits, sel, n_sel,
+                           sel_bits, slot_block=None, block_slot=None, fetch_block=None,
+                           fetch_slot=None, n_fetch=None, counters=None, stream=None):
+    _chk("nosa_score_select_step", _L.nosa_score_select_step(
+        ctypes.byref(shape), _p(q), _p(kbar), _p(e_blk), _p(step_dev), _p(s_q), _p(ge_bits),
+        _p(ev_bits), _p(sel), _p(n_sel), _p(sel_bits), _p(slot_block), _p(block_slot),
+        _p(fetch_block), _p(fetch_slot), _p(n_fetch), _p(counters), _s(stream)))
+
+
+def nosa_decode_partial_step(shape, q, kv, kv_row_blocks, kv_mode, list_, n_list, list_stride,
+                             list_len, with_newest, cur_kv, cur_row_blocks, step_dev, e_tok,
+                             e_row_stride, ws, ws_bytes, chunk0, stream=None):
+    _chk("nosa_decode_partial_step", _L.nosa_decode_partial_step(
+        ctypes.byref(shape), _p(q), _p(kv), kv_row_blocks, kv_mode, _p(list_), _p(n_list),
+        list_stride, list_len, with_newest, _p(cur_kv), cur_row_blocks, _p(step_dev), _p(e_tok),
+        e_row_stride, _p(ws), ws_bytes, chunk0, _s(stream)))
 
 
 def nosa_read_probe(src, nbytes: int, sink, workgroups: int = 2048, stream=None):

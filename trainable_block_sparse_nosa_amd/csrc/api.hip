@@ -498,6 +498,120 @@ nosa_status nosa_decode_partial(const nosa_shape *shape, const void *q, const vo
     return launch_partial(dm, kind, pl, a, (hipStream_t)stream);
 }
 
+// ---- steps replayed from a captured graph: the step record in device memory ----
+
+nosa_status nosa_step_advance(const nosa_shape *shape, nosa_step *step_dev, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!step_dev) return NOSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_step_advance(dm, reinterpret_cast<int32_t *>(step_dev),
+                                          (hipStream_t)stream));
+}
+
+nosa_status nosa_pool_step(const nosa_shape *shape, const void *kv, int64_t kv_row_blocks,
+                           const float *e_tok, int64_t e_row_stride, const nosa_step *step_dev,
+                           void *kbar, float *e_blk, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!kv || !e_tok || !kbar || !e_blk || !step_dev) return NOSA_ERR_INVALID_ARGUMENT;
+    if (kv_row_blocks < dm.max_blocks || e_row_stride < (int64_t)dm.max_blocks * dm.S)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        return hip_status(launch_pool_step<T, decltype(dc)::value>(
+            dm, kv, kv_row_blocks, e_tok, e_row_stride,
+            reinterpret_cast<const int32_t *>(step_dev), kbar, e_blk, (hipStream_t)stream));
+    });
+}
+
+nosa_status nosa_append_step(const nosa_shape *shape, const void *k_new, const void *v_new,
+                             void *kv, int64_t kv_row_blocks, const nosa_step *step_dev,
+                             void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!k_new || !v_new || !kv || !step_dev || kv_row_blocks < dm.max_blocks)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        constexpr int D = decltype(dc)::value;
+        return hip_status(launch_append<T, D>(dm, k_new, v_new, 0, kv, kv_row_blocks, 0,
+                                              (hipStream_t)stream,
+                                              reinterpret_cast<const int32_t *>(step_dev)));
+    });
+}
+
+nosa_status nosa_score_select_step(const nosa_shape *shape, const void *q, const void *kbar,
+                                   const float *e_blk, const nosa_step *step_dev, float *s_q,
+                                   uint32_t *ge_bits, uint32_t *ev_bits, int32_t *sel,
+                                   int32_t *n_sel, uint32_t *sel_bits, int32_t *slot_block,
+                                   int32_t *block_slot, int32_t *fetch_block,
+                                   int32_t *fetch_slot, int32_t *n_fetch, uint64_t *counters,
+                                   void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!q || !kbar || !s_q || !e_blk || !ge_bits || !ev_bits || !sel || !n_sel || !sel_bits ||
+        !step_dev)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    const bool any_swap = slot_block || block_slot || fetch_block || fetch_slot || n_fetch || counters;
+    const bool all_swap = slot_block && block_slot && fetch_block && fetch_slot && n_fetch && counters;
+    if (any_swap && !all_swap) return NOSA_ERR_INVALID_ARGUMENT;
+    const SwapPtrs sw{slot_block, block_slot, fetch_block, fetch_slot, n_fetch, counters};
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        constexpr int D = decltype(dc)::value;
+        return by_group(dm, [&](auto gc) -> nosa_status {
+            return hip_status(launch_score_select<T, D, decltype(gc)::value>(
+                dm, q, kbar, s_q, e_blk, 0, -1, ge_bits, ev_bits, sel, n_sel, sel_bits,
+                all_swap ? &sw : nullptr, (hipStream_t)stream,
+                reinterpret_cast<const int32_t *>(step_dev)));
+        });
+    });
+}
+
+nosa_status nosa_decode_partial_step(const nosa_shape *shape, const void *q, const void *kv,
+                                     int64_t kv_row_blocks, int32_t kv_mode, const int32_t *list,
+                                     const int32_t *n_list, int32_t list_stride,
+                                     int32_t list_len, int32_t with_newest, const void *cur_kv,
+                                     int64_t cur_row_blocks, const nosa_step *step_dev,
+                                     const float *e_tok, int64_t e_row_stride, void *ws,
+                                     size_t ws_bytes, int32_t chunk0, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!step_dev || list_len < 0 || list_len > dm.k || (with_newest != 0 && with_newest != 1))
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (list_len > 0 && (!kv || !list || list_stride < list_len ||
+                         (kv_mode == NOSA_KV_FULL && !n_list)))
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (kv_mode == NOSA_KV_CACHE && list_len > 0 && kv_row_blocks < list_len)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    // with the full KV the newest block is block n_cand of cur_kv's rows
+    if (kv_mode == NOSA_KV_FULL && cur_row_blocks < dm.max_blocks) return NOSA_ERR_INVALID_ARGUMENT;
+    const int kind = decode_kind(dm, shape->decode_kernel);
+    // every step value the device record can hold: validate against the capacity
+    const nosa_step cap{dm.max_blocks * dm.S, -1};
+    DecodeArgs a;
+    s = decode_common(dm, kind, q, kv ? kv : cur_kv, kv ? kv_row_blocks : cur_row_blocks,
+                      kv_mode, cur_kv, cur_row_blocks, &cap, e_tok, e_row_stride, ws, ws_bytes, a);
+    if (s != NOSA_OK) return s;
+    const DecodePlan pl = decode_plan(dm, kind, list_len + with_newest);
+    if (chunk0 < 0 || chunk0 + pl.n_chunks > a.chunk_cap) return NOSA_ERR_INVALID_ARGUMENT;
+    a.list = list;
+    a.n_list = kv_mode == NOSA_KV_FULL ? n_list : nullptr;
+    a.list_stride = list_stride;
+    a.list_len = list_len;
+    a.with_newest = with_newest;
+    a.chunk0 = chunk0;
+    a.cb = pl.cb;
+    a.dstep = reinterpret_cast<const int32_t *>(step_dev);
+    a.cur_at_step = kv_mode == NOSA_KV_FULL ? 1 : 0;
+    return launch_partial(dm, kind, pl, a, (hipStream_t)stream);
+}
+
 nosa_status nosa_decode_combine(const nosa_shape *shape, int32_t n_chunks, void *out, void *ws,
                                 size_t ws_bytes, void *stream) {
     Dims dm;

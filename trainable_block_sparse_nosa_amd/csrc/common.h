@@ -20,11 +20,26 @@ struct Dims {
     float scale;
 };
 
+// The step record in device memory ({n_tokens, n_cand_prev}, nosa_step's
+// layout) for steps replayed from a captured graph: kernels read it instead
+// of taking the values as launch arguments. n_tokens is clamped to the
+// shape's capacity so that no index derived from it leaves the buffers.
+struct StepVals {
+    int n_tokens, n_cand, n_prev;
+};
+__device__ __forceinline__ StepVals read_step(const int32_t *dstep, const struct Dims &dm);
+
 using bf16_t = uint16_t;  // bfloat16 storage
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // MFMA operand types: eight bf16 (A/B of 16x16x32 bf16), four fp32 (C/D)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ StepVals read_step(const int32_t *dstep, const Dims &dm) {
+    const int n = min(max(dstep[0], 1), dm.max_blocks * dm.S);
+    const int c = (n - 1) / dm.S;
+    return StepVals{n, c, min(max(dstep[1], -1), c)};
+}
 
 __device__ __forceinline__ float bf2f(uint32_t h16) { return __uint_as_float(h16 << 16); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }

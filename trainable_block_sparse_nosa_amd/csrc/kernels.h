@@ -9,6 +9,13 @@ template <typename T, int D>
 hipError_t launch_pool(const Dims &dm, const void *kv, int64_t kv_row_blocks, int kv_first,
                        const float *e_tok, int64_t e_stride, int blk_begin, int blk_end,
                        void *kbar, float *e_blk, hipStream_t st);
+// Pool the block completed at the device step, if any (candidates went from
+// n_cand_prev >= 0 to n_cand_prev + 1): block j of kv's rows (the full KV).
+template <typename T, int D>
+hipError_t launch_pool_step(const Dims &dm, const void *kv, int64_t kv_row_blocks,
+                            const float *e_tok, int64_t e_stride, const int32_t *dstep,
+                            void *kbar, float *e_blk, hipStream_t st);
+hipError_t launch_step_advance(const Dims &dm, int32_t *dstep, hipStream_t st);
 
 template <typename T, int D, int G>
 hipError_t launch_score(const Dims &dm, const void *q, const void *kbar, int n_cand, float *s_q,
@@ -32,11 +39,13 @@ hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, i
 
 // Scores computed by the selecting workgroup (one per row), written to s_q
 // as well, then the selection (and the set difference when swap != nullptr).
+// dstep != nullptr: n_cand and n_prev come from the device step record.
 template <typename T, int D, int G>
 hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, float *s_q,
                                const float *e_blk, int n_cand, int n_prev, uint32_t *ge,
                                uint32_t *ev, int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
-                               const SwapPtrs *swap, hipStream_t st);
+                               const SwapPtrs *swap, hipStream_t st,
+                               const int32_t *dstep = nullptr);
 
 // Selection of every query block i < n_qb of a sequence (candidates 0..i-1,
 // no previous step) in one launch: sel [n_qb][rows][k], n_sel [n_qb][rows].
@@ -54,9 +63,12 @@ hipError_t launch_ingest(const Dims &dm, const void *qkv, const void *x, const v
                          int64_t kv_row_blocks, int block, float *e_tok, int64_t e_stride,
                          void *kbar, float *e_blk, hipStream_t st);
 
+// dstep != nullptr: pos and block come from the device step record (the
+// newest token n_tokens - 1: slot (n_tokens - 1) % S of block (n_tokens - 1) / S).
 template <typename T, int D>
 hipError_t launch_append(const Dims &dm, const void *k_new, const void *v_new, int pos, void *kv,
-                         int64_t kv_row_blocks, int block, hipStream_t st);
+                         int64_t kv_row_blocks, int block, hipStream_t st,
+                         const int32_t *dstep = nullptr);
 
 hipError_t launch_fetch(const Dims &dm, const void *src, int64_t src_row_blocks,
                         const int32_t *fblk, const int32_t *fslot, const int32_t *nfetch,
@@ -95,6 +107,8 @@ struct DecodeArgs {
     int chunk0;    // first workspace chunk of this call
     int chunk_cap;
     int cb;        // entries per chunk (from the plan)
+    const int32_t *dstep = nullptr;  // device step record: overrides n_tokens / n_cand
+    int cur_at_step = 0;             // 1: the newest block is block n_cand of cur's rows
 };
 
 template <typename T, int D, int G>

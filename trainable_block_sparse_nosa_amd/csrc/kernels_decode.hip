@@ -118,17 +118,21 @@ combine_kernel(Dims dm, int n_chunks, int chunk_cap, const float *__restrict__ w
 // Resolve entry e of row r: data pointer, block id and valid tokens.
 // Returns false when the entry holds no block.
 template <typename T>
-__device__ __forceinline__ bool resolve_entry(const DecodeArgs &a, int e, int cnt_e, int r,
-                                              int64_t BE, const T *&blk, int &bid, int &valid) {
+__device__ __forceinline__ bool resolve_entry(const DecodeArgs &a, const StepVals &sv, int e,
+                                              int cnt_e, int r, int64_t BE, const T *&blk,
+                                              int &bid, int &valid) {
     if (a.with_newest && e == a.list_len) {
-        blk = static_cast<const T *>(a.cur) + (int64_t)r * a.cur_row_blocks * BE;
-        bid = a.n_cand;
-        valid = a.n_tokens - a.n_cand * 64;
+        // the newest block: block cur_block of cur's row (n_cand when it
+        // follows the device step: cur is then the full KV)
+        const int64_t cb = a.cur_at_step ? sv.n_cand : 0;
+        blk = static_cast<const T *>(a.cur) + ((int64_t)r * a.cur_row_blocks + cb) * BE;
+        bid = sv.n_cand;
+        valid = sv.n_tokens - sv.n_cand * 64;
         return true;
     }
     if (e >= a.list_len) return false;
     bid = a.list[(int64_t)r * a.list_stride + e];  // issued before the count is known
-    if (e >= cnt_e || bid < 0 || bid >= a.n_cand) return false;  // only candidates are listed
+    if (e >= cnt_e || bid < 0 || bid >= sv.n_cand) return false;  // only candidates are listed
     const int64_t at = a.kv_mode == NOSA_KV_FULL ? bid : e;
     blk = static_cast<const T *>(a.kv) + ((int64_t)r * a.kv_row_blocks + at) * BE;
     valid = 64;
@@ -247,6 +251,7 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
     const int col = lane & 15, grp = lane >> 4;
     const int r = blockIdx.y, chunk = blockIdx.x;
     const int b = r / dm.Hkv, g = r % dm.Hkv;
+    const StepVals sv = a.dstep ? read_step(a.dstep, dm) : StepVals{a.n_tokens, a.n_cand, 0};
     const int cnt_e = a.n_list ? min(a.n_list[r], a.list_len) : a.list_len;
     const float *er = a.e_tok + (int64_t)r * a.e_stride;
     const int e_beg = chunk * a.cb;
@@ -273,7 +278,7 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
         BlockRegs<D> br;
         const bf16_t *blk;
         int bid, valid;
-        if (resolve_entry<bf16_t>(a, e, cnt_e, r, BE, blk, bid, valid)) {
+        if (resolve_entry<bf16_t>(a, sv, e, cnt_e, r, BE, blk, bid, valid)) {
             load_block<D>(br, blk, er + (int64_t)bid * S, valid, col, grp);
             // keep every load of the block ahead of the math: without this the
             // scheduler interleaves loads with MFMAs to save registers and the
@@ -708,6 +713,7 @@ decode_valu_kernel(Dims dm, DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) o[i] = 0.f;
 
+    const StepVals sv = a.dstep ? read_step(a.dstep, dm) : StepVals{a.n_tokens, a.n_cand, 0};
     const int cnt_e = a.n_list ? min(a.n_list[r], a.list_len) : a.list_len;
     const int e0 = chunk * a.cb, e1 = min(e0 + a.cb, a.list_len + a.with_newest);
     const float *er = a.e_tok + (int64_t)r * a.e_stride;
@@ -715,7 +721,7 @@ decode_valu_kernel(Dims dm, DecodeArgs a) {
     for (int e = e0; e < e1; ++e) {
         const T *blk;
         int bid, valid;
-        if (!resolve_entry<T>(a, e, cnt_e, r, BE, blk, bid, valid))
+        if (!resolve_entry<T>(a, sv, e, cnt_e, r, BE, blk, bid, valid))
             continue;  // uniform over the workgroup
         __syncthreads();  // the previous block's readers are done with LDS
         constexpr int KV_VEC = S * D / EPV;

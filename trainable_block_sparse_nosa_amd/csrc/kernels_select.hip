@@ -84,13 +84,19 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256)
 pool_kernel(Dims dm, const T *__restrict__ kv, int64_t kv_row_blocks, int kv_first,
             const float *__restrict__ e_tok, int64_t e_stride, int blk_begin,
-            T *__restrict__ kbar, float *__restrict__ e_blk) {
+            T *__restrict__ kbar, float *__restrict__ e_blk, const int32_t *__restrict__ dstep) {
     constexpr int S = 64, SUB = 16, M = S / SUB, V = KbarVec<T>::V;
     static_assert(SUB == 16, "pooled_mean sums 16 tokens");
     __shared__ float emean[M];
     const int r = blockIdx.y;
-    const int j = blk_begin + blockIdx.x;
-    const T *K = kv + ((int64_t)r * kv_row_blocks + kv_first + blockIdx.x) * (int64_t)(2 * S * D);
+    int j = blk_begin + blockIdx.x, src = kv_first + blockIdx.x;
+    if (dstep) {
+        // the blocks completed since the previous step: n_cand_prev .. n_cand - 1
+        const StepVals sv = read_step(dstep, dm);
+        if (sv.n_prev < 0 || sv.n_prev + (int)blockIdx.x >= sv.n_cand) return;
+        j = src = sv.n_prev + blockIdx.x;
+    }
+    const T *K = kv + ((int64_t)r * kv_row_blocks + src) * (int64_t)(2 * S * D);
     for (int p = threadIdx.x; p < M * D; p += blockDim.x) {
         const int i = p / D, d = p % D;
         kbar[kbar_vec<T, D>(dm, r, M * j + i, d / V) + (d % V)] =
@@ -603,12 +609,13 @@ struct ScoresFusedMfma {
 struct BatchArgs {
     int cand_step;
     int64_t sel_step, nsel_step;
+    const int32_t *dstep;  // device step record: n_cand and n_prev from it
 };
 
 template <typename Src>
 __global__ void __launch_bounds__(SELECT_THREADS)
 select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
-              int n_prev, int P, uint32_t *__restrict__ ge_bits, uint32_t *__restrict__ ev_bits,
+              int n_prev_arg, int P, uint32_t *__restrict__ ge_bits, uint32_t *__restrict__ ev_bits,
               int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
               uint32_t *__restrict__ sel_bits, SwapArgs sw, ListArgs lists, BatchArgs bt) {
     extern __shared__ uint64_t keys[];  // P keys, only when a budget exceeds 64
@@ -623,7 +630,9 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int W = dm.W;
-    const int n_cand = n_cand0 + blockIdx.y * bt.cand_step;
+    StepVals stp{0, n_cand0 + (int)blockIdx.y * bt.cand_step, n_prev_arg};
+    if (bt.dstep) stp = read_step(bt.dstep, dm);
+    const int n_cand = stp.n_cand, n_prev = stp.n_prev;
     sel += blockIdx.y * bt.sel_step;
     n_sel += blockIdx.y * bt.nsel_step;
     const float *E = e_blk + (int64_t)r * dm.max_blocks;
@@ -946,10 +955,16 @@ ingest_kernel(Dims dm, const T *__restrict__ qkv, const T *__restrict__ x,
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ void __launch_bounds__(D)
-append_kernel(const T *__restrict__ k_new, const T *__restrict__ v_new, int pos,
-              T *__restrict__ kv, int64_t kv_row_blocks, int block) {
+append_kernel(Dims dm, const T *__restrict__ k_new, const T *__restrict__ v_new, int pos,
+              T *__restrict__ kv, int64_t kv_row_blocks, int block,
+              const int32_t *__restrict__ dstep) {
     constexpr int S = 64;
     const int r = blockIdx.x, d = threadIdx.x;
+    if (dstep) {
+        const StepVals sv = read_step(dstep, dm);
+        pos = (sv.n_tokens - 1) % S;
+        block = sv.n_cand;
+    }
     T *blk = kv + ((int64_t)r * kv_row_blocks + block) * (int64_t)(2 * S * D);
     blk[pos * D + d] = k_new[(int64_t)r * D + d];
     blk[S * D + d * S + vt_pos_of(pos)] = v_new[(int64_t)r * D + d];
@@ -965,7 +980,33 @@ hipError_t launch_pool(const Dims &dm, const void *kv, int64_t kv_row_blocks, in
     dim3 grid(blk_end - blk_begin, dm.rows);
     hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(256), 0, st, dm,
                        static_cast<const T *>(kv), kv_row_blocks, kv_first, e_tok, e_stride,
-                       blk_begin, static_cast<T *>(kbar), e_blk);
+                       blk_begin, static_cast<T *>(kbar), e_blk, nullptr);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_pool_step(const Dims &dm, const void *kv, int64_t kv_row_blocks,
+                            const float *e_tok, int64_t e_stride, const int32_t *dstep,
+                            void *kbar, float *e_blk, hipStream_t st) {
+    // one token per step completes at most one block
+    hipLaunchKernelGGL((pool_kernel<T, D>), dim3(1, dm.rows), dim3(256), 0, st, dm,
+                       static_cast<const T *>(kv), kv_row_blocks, 0, e_tok, e_stride, 0,
+                       static_cast<T *>(kbar), e_blk, dstep);
+    return hipGetLastError();
+}
+
+// The step record moves to the next step: the candidates of this step become
+// the previous ones, one more token.
+__global__ void step_advance_kernel(Dims dm, int32_t *dstep) {
+    if (threadIdx.x == 0) {
+        const StepVals sv = read_step(dstep, dm);
+        dstep[1] = sv.n_cand;
+        dstep[0] = sv.n_tokens + 1;
+    }
+}
+
+hipError_t launch_step_advance(const Dims &dm, int32_t *dstep, hipStream_t st) {
+    hipLaunchKernelGGL(step_advance_kernel, dim3(1), dim3(64), 0, st, dm, dstep);
     return hipGetLastError();
 }
 
@@ -983,12 +1024,14 @@ static hipError_t launch_select_from(const Dims &dm, const Src &src, const float
                                      int n_cand, int n_prev, uint32_t *ge, uint32_t *ev,
                                      int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
                                      const SwapPtrs *swap, const SelectLists *parts,
-                                     hipStream_t st, int batch = 1) {
+                                     hipStream_t st, int batch = 1,
+                                     const int32_t *dstep = nullptr) {
     // LDS keys only when a budget is above what the register top-k holds
-    // (batch > 1: selections y = 0..batch-1 with y candidates each)
-    const int max_cand = batch > 1 ? batch - 1 : n_cand;
+    // (batch > 1: selections y = 0..batch-1 with y candidates each; a device
+    // step: up to the capacity)
+    const int max_cand = dstep ? dm.max_blocks : batch > 1 ? batch - 1 : n_cand;
     int P = 0;
-    if ((n_prev < 0 && dm.k_e > WAVE_TOPK) || dm.k_q > WAVE_TOPK) {
+    if (((n_prev < 0 || dstep) && dm.k_e > WAVE_TOPK) || dm.k_q > WAVE_TOPK) {
         P = 2;
         while (P < max_cand) P <<= 1;
     }
@@ -1003,8 +1046,8 @@ static hipError_t launch_select_from(const Dims &dm, const Src &src, const float
     }
     ListArgs li{};
     if (parts) li = ListArgs{parts->ge_list, parts->n_ge, parts->gq_list, parts->n_gq};
-    const BatchArgs bt = batch > 1 ? BatchArgs{1, (int64_t)dm.rows * dm.k, dm.rows}
-                                   : BatchArgs{0, 0, 0};
+    const BatchArgs bt = batch > 1 ? BatchArgs{1, (int64_t)dm.rows * dm.k, dm.rows, nullptr}
+                                   : BatchArgs{0, 0, 0, dstep};
     hipLaunchKernelGGL(select_kernel<Src>, dim3(dm.rows, batch), dim3(SELECT_THREADS),
                        P * sizeof(uint64_t), st, dm, src, e_blk, batch > 1 ? 0 : n_cand, n_prev, P,
                        ge, ev, sel, n_sel, sel_bits, sw, li, bt);
@@ -1023,17 +1066,17 @@ template <typename T, int D, int G>
 hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, float *s_q,
                                const float *e_blk, int n_cand, int n_prev, uint32_t *ge,
                                uint32_t *ev, int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
-                               const SwapPtrs *swap, hipStream_t st) {
+                               const SwapPtrs *swap, hipStream_t st, const int32_t *dstep) {
     if constexpr (std::is_same_v<T, bf16_t>) {
         const ScoresFusedMfma<D, G> src{static_cast<const bf16_t *>(q),
                                         static_cast<const bf16_t *>(kbar), s_q};
         return launch_select_from(dm, src, e_blk, n_cand, n_prev, ge, ev, sel, n_sel, sel_bits,
-                                  swap, nullptr, st);
+                                  swap, nullptr, st, 1, dstep);
     } else {
         const ScoresFused<T, D, G> src{static_cast<const T *>(q), static_cast<const T *>(kbar),
                                        s_q};
         return launch_select_from(dm, src, e_blk, n_cand, n_prev, ge, ev, sel, n_sel, sel_bits,
-                                  swap, nullptr, st);
+                                  swap, nullptr, st, 1, dstep);
     }
 }
 
@@ -1080,18 +1123,18 @@ hipError_t launch_ingest(const Dims &dm, const void *qkv, const void *x, const v
 
 template <typename T, int D>
 hipError_t launch_append(const Dims &dm, const void *k_new, const void *v_new, int pos, void *kv,
-                         int64_t kv_row_blocks, int block, hipStream_t st) {
-    hipLaunchKernelGGL((append_kernel<T, D>), dim3(dm.rows), dim3(D), 0, st,
+                         int64_t kv_row_blocks, int block, hipStream_t st, const int32_t *dstep) {
+    hipLaunchKernelGGL((append_kernel<T, D>), dim3(dm.rows), dim3(D), 0, st, dm,
                        static_cast<const T *>(k_new), static_cast<const T *>(v_new), pos,
-                       static_cast<T *>(kv), kv_row_blocks, block);
+                       static_cast<T *>(kv), kv_row_blocks, block, dstep);
     return hipGetLastError();
 }
 template hipError_t launch_append<float, 64>(const Dims &, const void *, const void *, int, void *,
-                                            int64_t, int, hipStream_t);
+                                            int64_t, int, hipStream_t, const int32_t *);
 template hipError_t launch_append<bf16_t, 64>(const Dims &, const void *, const void *, int,
-                                             void *, int64_t, int, hipStream_t);
+                                             void *, int64_t, int, hipStream_t, const int32_t *);
 template hipError_t launch_append<bf16_t, 128>(const Dims &, const void *, const void *, int,
-                                              void *, int64_t, int, hipStream_t);
+                                              void *, int64_t, int, hipStream_t, const int32_t *);
 
 hipError_t launch_fetch(const Dims &dm, const void *src, int64_t src_row_blocks,
                         const int32_t *fblk, const int32_t *fslot, const int32_t *nfetch,
@@ -1108,7 +1151,10 @@ hipError_t launch_fetch(const Dims &dm, const void *src, int64_t src_row_blocks,
 #define NOSA_POOL_INST(T, D)                                                                   \
     template hipError_t launch_pool<T, D>(const Dims &, const void *, int64_t, int,            \
                                           const float *, int64_t, int, int, void *, float *,   \
-                                          hipStream_t);
+                                          hipStream_t);                                        \
+    template hipError_t launch_pool_step<T, D>(const Dims &, const void *, int64_t,            \
+                                               const float *, int64_t, const int32_t *, void *, \
+                                               float *, hipStream_t);
 NOSA_POOL_INST(float, 64)
 NOSA_POOL_INST(float, 128)
 NOSA_POOL_INST(bf16_t, 64)
@@ -1123,7 +1169,8 @@ NOSA_POOL_INST(bf16_t, 128)
                                                float *, hipStream_t);                          \
     template hipError_t launch_score_select<T, D, G>(                                          \
         const Dims &, const void *, const void *, float *, const float *, int, int, uint32_t *, \
-        uint32_t *, int32_t *, int32_t *, uint32_t *, const SwapPtrs *, hipStream_t);          \
+        uint32_t *, int32_t *, int32_t *, uint32_t *, const SwapPtrs *, hipStream_t,           \
+        const int32_t *);                                                                      \
     template hipError_t launch_prefill_select<T, D, G>(                                        \
         const Dims &, const void *, const void *, const float *, int, int32_t *, int32_t *,    \
         hipStream_t);

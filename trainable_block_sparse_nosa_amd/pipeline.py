@@ -337,6 +337,58 @@ class DecodeLayer:
         self.n_tokens = n_tokens
         return self.out
 
+    # -- steps replayed from a captured graph ----------------------------------
+    def graph_capture(self, n_tokens: int, q_buf: torch.Tensor, k_new_buf=None, v_new_buf=None,
+                      swap: bool = True):
+        """Capture one decode step of the resident KV into a hipGraph (through
+        torch.cuda.CUDAGraph). Its calls read the step record from device
+        memory (self.step_dev: n_tokens, n_cand_prev), and the step's last
+        call moves the record on, so each replay is the next step. The step
+        reads q from q_buf [batch][Hq][D] and, with device_append, the newest
+        token from k_new_buf / v_new_buf [rows][D]: fill them before each
+        replay. n_tokens is the first replayed step's token count; the layer
+        continues from its current state (start() or earlier steps)."""
+        if self.offload or self.overlap or self.evict_head is not None:
+            raise ValueError("graph-replayed steps cover the resident KV path")
+        if self.device_append and (k_new_buf is None or v_new_buf is None):
+            raise ValueError("device_append needs the step's k_new_buf and v_new_buf")
+        dev = self.kbar.device
+        self.step_dev = torch.tensor([n_tokens, self.n_cand_prev], dtype=torch.int32, device=dev)
+        # load every kernel of the step once outside the capture (on a scratch
+        # record the advance kernel may move)
+        scratch = torch.tensor([n_tokens, self.n_cand_prev], dtype=torch.int32, device=dev)
+        L.nosa_step_advance(self.shape, scratch, None)
+        torch.cuda.synchronize()
+        cache = (self.slot_block, self.block_slot, self.fetch_block, self.fetch_slot,
+                 self.n_fetch, self.counters) if swap else (None,) * 6
+        rb = self.kv_row_blocks
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            if self.device_append:
+                L.nosa_append_step(self.shape, k_new_buf, v_new_buf, self.kv, rb, self.step_dev)
+            L.nosa_pool_step(self.shape, self.kv, rb, self.e_tok, self.e_stride, self.step_dev,
+                             self.kbar, self.e_blk)
+            L.nosa_score_select_step(self.shape, q_buf, self.kbar, self.e_blk, self.step_dev,
+                                     self.s_q, self.ge_bits, self.ev_bits, self.sel, self.n_sel,
+                                     self.sel_bits, *cache)
+            L.nosa_decode_partial_step(self.shape, q_buf, self.kv, rb, L.NOSA_KV_FULL, self.sel,
+                                       self.n_sel, self.k, self.k, 1, self.kv, rb, self.step_dev,
+                                       self.e_tok, self.e_stride, self.ws, self.ws_bytes, 0)
+            L.nosa_decode_combine(self.shape, self.chunks_all, self.out, self.ws, self.ws_bytes)
+            L.nosa_step_advance(self.shape, self.step_dev)
+        torch.cuda.current_stream().wait_stream(side)
+        return graph
+
+    def graph_done(self, n_tokens_last: int):
+        """Bring the host-side step state up to date after replays whose last
+        step had n_tokens_last tokens (before eager steps follow)."""
+        c = (n_tokens_last - 1) // BLOCK
+        self.pooled = max(self.pooled, c)
+        self.n_cand_prev = c
+        self.n_tokens = n_tokens_last
+
     def _step_overlap(self, q, n_tokens, c, st, stream, swap):
         main = stream if stream is not None else torch.cuda.current_stream()
         cur, prev = self.parity, self.parity ^ 1
