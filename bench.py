@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the leg that prefills the workload's context with the selection "
                          "per query block (block-sparse causal attention on the matrix cores)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the run with the step captured into a hipGraph and replayed")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the resident runs with the Infinity Cache flushed before each "
                          "step (a 1 GiB scratch read, then a 512 MiB scratch write)")
@@ -466,6 +468,33 @@ def h2d_peak_gbs(dev, nbytes=1 << 30, reps=5):
     return best
 
 
+def graph_leg(w, args, dev):
+    """The resident workload's decode step captured once into a hipGraph and
+    replayed step after step: the step's calls read the step record from
+    device memory and its last call advances it. Before each replay the
+    step's query is copied into the captured query buffer (inside the timed
+    region, as a serving loop would do)."""
+    import torch
+    layer, q, kv, _ = setup(w, args, dev)
+    layer.start(w.n_tokens(0))
+    for t in range(args.warmup):
+        run_step(layer, q, None, t, w.n_tokens(t), None)
+    torch.cuda.synchronize()
+    q_buf = torch.empty_like(q[0])
+    graph = layer.graph_capture(w.n_tokens(args.warmup), q_buf)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        q_buf.copy_(q[args.warmup + i])
+        graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    del graph, layer, q, kv
+    torch.cuda.empty_cache()
+    return {"steps": args.steps, "steps_per_s": args.steps / elapsed,
+            "ms_per_step": elapsed / args.steps * 1e3}
+
+
 def read_probe_gbs(dev, nbytes=2 << 30, reps=10):
     """Achievable streaming HBM read bandwidth: the library's read probe over a
     buffer 8x the 256 MB Infinity Cache, best of `reps` launches (HIP events
@@ -745,6 +774,13 @@ def main():
         del layer, q, kv
         torch.cuda.empty_cache()
 
+    graph = None
+    if not args.no_graph and not w.offload:
+        graph = graph_leg(w, args, dev)
+        graph["vs_eager"] = graph["steps_per_s"] / steps_per_s
+        log(f"graph-replayed steps: {graph['steps_per_s']:.1f} steps/s "
+            f"({graph['vs_eager']:.3f}x the eager launches)")
+
     ingest = None
     if not args.no_ingest and not w.offload and w.dtype == "bf16":
         log(f"ingest leg: {w.name} with the fused ingest launch")
@@ -800,6 +836,7 @@ def main():
             "read_probe_gbs": probe, "frac_of_read_probe": achieved / probe,
         },
         "cold_cache": cold,
+        "graph": graph,
         "attn_partial_us_per_step": attn_step_us,
         "overlap": overlapped,
         "gamma_mean": gamma_mean,
