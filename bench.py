@@ -609,6 +609,21 @@ def offload_leg(args, dev, stream):
         "gamma_mean": float(counters[:, 1].sum()) / (w.rows * w.k * T),
         "device_append": True,
     }
+    # the same loop in two batch halves, the second half's fetch overlapping
+    # the first half's attention
+    from trainable_block_sparse_nosa_amd.pipeline import DecodeLayer
+    from trainable_block_sparse_nosa_amd import _lib as L
+    lay = DecodeLayer(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                      head_dim=w.head_dim, k_e=w.k_e, k_q=w.k_q, max_blocks=w.nb_max,
+                      dtype=L.NOSA_BF16, kv=kv.dev, kv_row_blocks=w.nb_max, e_tok=layer.e_tok,
+                      offload=True, device_append=new is not None, overlap=True)
+    el2, _, _ = timed_run(lay, w, q, sub, stream, event_stages=(), new=new)
+    out["overlap_halves"] = {"steps_per_s": sub.steps / el2,
+                             "vs_serial": sub.steps / el2 / out["steps_per_s"]}
+    log(f"offload in two batch halves, fetch overlapping attention: "
+        f"{out['overlap_halves']['steps_per_s']:.1f} steps/s "
+        f"({out['overlap_halves']['vs_serial']:.3f}x)")
+    del lay
     if not args.no_ablation:
         out["ablation"] = locality_ablation(w, layer, q, kv, sub, dev, stream, out, block_bytes,
                                             new)

@@ -214,6 +214,23 @@ def test_parity_overlapped_decode(name):
             _compare_step(w, tr, t, r, res[t])
 
 
+@pytest.mark.parametrize("append", [False, True])
+def test_parity_offload_overlap(append):
+    """Offloaded KV in two batch halves: the second half's fetch overlaps the
+    first half's attention; every step and row against the oracle, with
+    pre-generated tokens and with the device-side append and write-back."""
+    gh = _gpu()
+    w = synth.WORKLOADS["small_offload"]
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov, prefix_only=append)
+    layer = gh.make_layer(w, inp, overlap=True, device_append=append)
+    assert layer.overlap_fetch
+    _, res = gh.run(w, inp, list(range(w.steps)), layer=layer)
+    for t in range(w.steps):
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, res[t])
+
+
 EDGE = {
     # fewer tokens than one block at the start: no candidates, then one
     "short_context": dict(context=10, steps=70, k_e=2, k_q=2),

@@ -128,6 +128,24 @@ class DecodeLayer:
         # the caller's stream; the query-aware part follows the selection and a
         # combine merges both.
         self.overlap = overlap and not offload
+        # Overlap (offloaded KV): the rows go in two halves of the batch; the
+        # second half's fetch runs on a side stream while the first half's
+        # attention (over its cache and newest block) and merge run on the
+        # caller's stream, then the second half's attention follows its fetch.
+        self.overlap_fetch = overlap and offload
+        if self.overlap_fetch:
+            if batch % 2:
+                raise ValueError("the offload overlap splits the batch in two halves")
+            self.half_shape = L.make_shape(batch // 2, n_q_heads, n_kv_heads, head_dim, k_e, k_q,
+                                           max_blocks, dtype, decode_kernel=decode_kernel,
+                                           scale=scale)
+            self.ws_half_bytes = L.nosa_decode_workspace_size(self.half_shape)
+            self.ws_half = [torch.empty(self.ws_half_bytes // 4 + 4, dtype=f32, device=dev)
+                            for _ in range(2)]
+            self.chunks_half = L.nosa_decode_chunks(self.half_shape, self.k, 1)
+            self.side = torch.cuda.Stream(device=dev)
+            self.fetch_a_done = torch.cuda.Event()
+            self.fetch_b_done = torch.cuda.Event()
         if self.overlap:
             ke, kq = max(k_e, 1), max(k_q, 1)
             self.side = torch.cuda.Stream(device=dev)
@@ -319,6 +337,11 @@ class DecodeLayer:
                     self._run("swap", L.nosa_swap_diff, self.shape, self.sel, self.n_sel,
                               self.sel_bits, self.slot_block, self.block_slot, self.fetch_block,
                               self.fetch_slot, self.n_fetch, self.counters, stream)
+        if self.overlap_fetch:
+            self._offload_halves(q, st, stream)
+            self.n_cand_prev = c
+            self.n_tokens = n_tokens
+            return self.out
         if self.offload:
             self._run("fetch", L.nosa_fetch_blocks, self.shape, self.kv, self.kv_row_blocks,
                       self.fetch_block, self.fetch_slot, self.n_fetch, self.k, self.cache, self.k,
@@ -336,6 +359,38 @@ class DecodeLayer:
         self.n_cand_prev = c
         self.n_tokens = n_tokens
         return self.out
+
+    def _offload_halves(self, q, st, stream):
+        """Fetch, attention and merge of an offloaded step in two batch halves,
+        the second half's fetch overlapping the first half's attention."""
+        main = stream if stream is not None else torch.cuda.current_stream()
+        Rh, Bh, k, sh = self.rows // 2, q.shape[0] // 2, self.k, self.half_shape
+        base = self.kv if isinstance(self.kv, int) else self.kv.data_ptr()
+        kv_b = base + Rh * self.kv_row_blocks * self.block_elems * self.elem_bytes
+        halves = ((slice(0, Rh), slice(0, Bh), base), (slice(Rh, 2 * Rh), slice(Bh, 2 * Bh), kv_b))
+
+        def fetch(h, on):
+            rs, _, src = halves[h]
+            self._run("fetch", L.nosa_fetch_blocks, sh, src, self.kv_row_blocks,
+                      self.fetch_block[rs], self.fetch_slot[rs], self.n_fetch[rs], k,
+                      self.cache[rs], k, on)
+
+        def attend(h):
+            rs, bs, _ = halves[h]
+            self._run("decode", L.nosa_decode_partial, sh, q[bs], self.cache[rs], k,
+                      L.NOSA_KV_CACHE, self.slot_block[rs], None, k, k, 1, self.cur[rs], 1, st,
+                      self.e_tok[rs], self.e_stride, self.ws_half[h], self.ws_half_bytes, 0, main)
+            self._run("combine", L.nosa_decode_combine, sh, self.chunks_half, self.out[bs],
+                      self.ws_half[h], self.ws_half_bytes, main)
+
+        fetch(0, main)
+        self.fetch_a_done.record(main)
+        self.side.wait_event(self.fetch_a_done)
+        fetch(1, self.side)
+        self.fetch_b_done.record(self.side)
+        attend(0)
+        main.wait_event(self.fetch_b_done)
+        attend(1)
 
     # -- steps replayed from a captured graph ----------------------------------
     def graph_capture(self, n_tokens: int, q_buf: torch.Tensor, k_new_buf=None, v_new_buf=None,
