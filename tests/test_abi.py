@@ -137,3 +137,41 @@ def test_invalid_pointers_and_steps_rejected():
     f32 = _shape(dtype=L.NOSA_F32, head_dim=64, decode_kernel=L.NOSA_DECODE_MFMA)
     assert lib.nosa_sparse_decode(ctypes.byref(f32), 16, 16, 64, 0, 16, 16, 16, 64,
                                   ctypes.byref(st), 16, 4096, 16, 16, 1 << 30, None) == 2
+
+
+@fake_pointers
+def test_device_step_calls_validate_against_the_capacity():
+    """The *_step calls cannot read the record on the host: they check their
+    buffers against the shape's capacity (max_blocks) before any launch."""
+    from trainable_block_sparse_nosa_amd import _lib as L
+    lib = L.lib()
+    sh = _shape()
+    mb = sh.max_blocks
+    # null record
+    assert lib.nosa_step_advance(ctypes.byref(sh), None, None) == 1
+    assert lib.nosa_pool_step(ctypes.byref(sh), 16, mb, 16, mb * 64, None, 16, 16, None) == 1
+    # KV rows or eviction rows shorter than the capacity
+    assert lib.nosa_pool_step(ctypes.byref(sh), 16, mb - 1, 16, mb * 64, 16, 16, 16, None) == 1
+    assert lib.nosa_pool_step(ctypes.byref(sh), 16, mb, 16, mb * 64 - 4, 16, 16, 16, None) == 1
+    assert lib.nosa_append_step(ctypes.byref(sh), 16, 16, 16, mb - 1, 16, None) == 1
+    assert lib.nosa_append_step(ctypes.byref(sh), None, 16, 16, mb, 16, None) == 1
+    # fused score + select: null record, cache pointers given only in part
+    P = [16] * 12
+    assert lib.nosa_score_select_step(ctypes.byref(sh), 16, 16, 16, None, *P, None) == 1
+    part = [16] * 6 + [16, 16, 16, None, 16, 16]
+    assert lib.nosa_score_select_step(ctypes.byref(sh), 16, 16, 16, 16, *part, None) == 1
+    # decode: newest block taken from a full KV shorter than the capacity, e
+    # stride shorter than the capacity, null record
+    ws = lib.nosa_decode_workspace_size(ctypes.byref(sh))
+    args = lambda **o: dict(dict(q=16, kv=16, rb=mb, mode=0, lst=16, nl=16, cur=16, crb=mb,
+                                 st=16, e=16, es=mb * 64, ws=16, wsb=ws), **o)
+
+    def call(a):
+        return lib.nosa_decode_partial_step(ctypes.byref(sh), a["q"], a["kv"], a["rb"],
+                                            a["mode"], a["lst"], a["nl"], sh.k_e + sh.k_q,
+                                            sh.k_e + sh.k_q, 1, a["cur"], a["crb"], a["st"],
+                                            a["e"], a["es"], a["ws"], a["wsb"], 0, None)
+    assert call(args(crb=mb - 1)) == 1
+    assert call(args(es=mb * 64 - 4)) == 1
+    assert call(args(st=None)) == 1
+    assert call(args(rb=mb - 1)) == 1
