@@ -535,6 +535,8 @@ def cold_cache_run(layer, w, q, args, stream, n_steps: int, scratch_mib: int = 1
     scratch = torch.zeros(scratch_mib << 20, dtype=torch.uint8, device=torch.device("cuda"))
     sink = torch.zeros(1, dtype=torch.int32, device=scratch.device)
     n = min(n_steps, args.warmup + args.steps)
+    if n < 2:
+        return None   # the first step (eviction top-k start) is not counted
     ev = HipTimingEvents(2 * n + 2)
     done = []
 
