@@ -270,12 +270,15 @@ nosa_status nosa_select_swap(const nosa_shape *shape, const float *s_q, const fl
                              void *stream);
 
 /* nosa_score_blocks and nosa_select (and, when the six cache pointers are
- * given, the set difference as in nosa_select_swap) in one launch: one
- * workgroup per row computes the row's query-aware scores into on-chip memory
- * and selects from them, with no round trip of the scores through memory
- * between two launches. s_q still receives the scores. Outputs and state
- * updates are those of the separate calls. The cache pointers are all NULL
- * or all non-NULL. */
+ * given, the set difference as in nosa_select_swap) in one call. With more
+ * than 128 rows (bf16), or float32 inputs, it is one launch: one workgroup
+ * per row computes the row's query-aware scores into on-chip memory and
+ * selects from them. With bf16 and at most 128 rows, too few workgroups to
+ * fill the GPU that way, the scores are computed on a grid split over each
+ * row's candidates and the selection follows as a second launch on the same
+ * stream. s_q receives the scores either way. Outputs and state updates are
+ * those of the separate calls. The cache pointers are all NULL or all
+ * non-NULL. */
 nosa_status nosa_score_select(const nosa_shape *shape, const void *q, const void *kbar,
                               const float *e_blk, const nosa_step *step, float *s_q,
                               uint32_t *ge_bits, uint32_t *ev_bits, int32_t *sel, int32_t *n_sel,

@@ -19,7 +19,7 @@ hipError_t launch_step_advance(const Dims &dm, int32_t *dstep, hipStream_t st);
 
 template <typename T, int D, int G>
 hipError_t launch_score(const Dims &dm, const void *q, const void *kbar, int n_cand, float *s_q,
-                        hipStream_t st);
+                        hipStream_t st, const int32_t *dstep = nullptr);
 
 struct SwapPtrs {
     int32_t *slot_block, *block_slot, *fetch_block, *fetch_slot, *n_fetch;

@@ -166,11 +166,12 @@ score_kernel(Dims dm, const T *__restrict__ q, const T *__restrict__ kbar, int n
 // keys are equal; 0 marks "not a candidate".
 //  * top-k with k <= 64: every thread holds its candidates' keys in registers
 //    (candidate j = tid + 512 i). Each wave finds the smallest key T of its own
-//    top-k by a most-significant-bit-first search with ballots and popcounts
-//    (stopping as soon as exactly k of its keys are >= the prefix); its keys
-//    >= T go to LDS; each of these <= 8k survivors then counts how many
-//    survivors are larger, and the ones with fewer than k above them are the
-//    row's top-k. No sorting, two barriers.
+//    top-k by a most-significant-bit-first search with ballots and popcounts,
+//    two bits per step (stopping as soon as exactly k of its keys are >= the
+//    prefix); its keys >= T go to LDS; then the survivors' ranks among
+//    themselves are counted by all threads at once (up to 8 per survivor),
+//    and the ones with fewer than k above them are the row's top-k. No
+//    sorting, two barriers.
 //  * top-k with k > 64 (an eviction budget above 64 at initialisation, or a
 //    query budget above 64): bitonic sort of all keys in LDS.
 //  * Gamma_e after initialisation: each new candidate in turn replaces the
@@ -189,9 +190,29 @@ static_assert(MAX_W <= SELECT_THREADS, "one bitmap word per thread");
 
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
+// Inclusive prefix sum over the 64 lanes of a wave on DPP: a log-step scan
+// inside each row of 16 lanes (row_shr 1, 2, 4, 8; lanes shifted in from
+// outside the row read 0), then the row totals carried across rows with the
+// GFX9 row broadcasts (lane 15 of rows 0 and 2 into rows 1 and 3, then lane
+// 31 into rows 2 and 3). Every lane must be active.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
 // Smallest key of the wave's top-k among the keys held in x[0..M) of every
 // lane (0 = no key). When the wave holds at most k keys, all of them qualify
-// and the smallest is returned.
+// and the smallest is returned. Otherwise a most-significant-bit-first search
+// builds the largest prefix value t with at least k keys >= t and stops early
+// once exactly k keys are >= t. With one or two keys per lane it takes two
+// bits per step (the three candidate extensions are counted independently, so
+// their ballots overlap); with more keys per lane the three-fold ballots cost
+// more than the halved chain saves, and it takes one bit per step.
 template <int M>
 __device__ uint64_t wave_kth_key(const uint64_t (&x)[M], int k) {
     int n = 0;
@@ -208,15 +229,35 @@ __device__ uint64_t wave_kth_key(const uint64_t (&x)[M], int k) {
         return mn;
     }
     uint64_t t = 0ull;
-    for (int b = 63; b >= 0; --b) {
-        const uint64_t cand = t | (1ull << b);
-        int c = 0;
+    if constexpr (M > 2) {
+        for (int b = 63; b >= 0; --b) {
+            const uint64_t cand = t | (1ull << b);
+            int c = 0;
 #pragma unroll
-        for (int i = 0; i < M; ++i) c += __popcll(__ballot(x[i] >= cand));
-        if (c >= k) {
-            t = cand;
-            if (c == k) break;  // exactly the top-k are >= t
+            for (int i = 0; i < M; ++i) c += __popcll(__ballot(x[i] >= cand));
+            if (c >= k) {
+                t = cand;
+                if (c == k) break;  // exactly the top-k are >= t
+            }
         }
+        return t;
+    }
+    for (int b = 62; b >= 0; b -= 2) {
+        const uint64_t c3 = t | (3ull << b), c2 = t | (2ull << b), c1 = t | (1ull << b);
+        int n3 = 0, n2 = 0, n1 = 0;
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            n3 += __popcll(__ballot(x[i] >= c3));
+            n2 += __popcll(__ballot(x[i] >= c2));
+            n1 += __popcll(__ballot(x[i] >= c1));
+        }
+        // n3 <= n2 <= n1: extend by the largest pair of bits that keeps k keys
+        int c;
+        if (n3 >= k) { t = c3; c = n3; }
+        else if (n2 >= k) { t = c2; c = n2; }
+        else if (n1 >= k) { t = c1; c = n1; }
+        else c = -1;
+        if (c == k) break;  // exactly the top-k are >= t
     }
     return t;
 }
@@ -224,31 +265,22 @@ __device__ uint64_t wave_kth_key(const uint64_t (&x)[M], int k) {
 // Top-k (k <= 64) of the keys x[0..M) held by every thread of the block:
 // sets the selected indices' bits in `bits` (LDS). Returns nothing; the
 // caller synchronises before reading `bits`.
-// k-th key (k <= 64) among the survivors surv[0..ns) by wave 0, with M2
-// survivors per lane. The search may stop at a value between the (k+1)-th
-// and the k-th survivor; keys that did not survive (below their own wave's
-// k-th) can lie in that gap when another wave held fewer than k keys, so the
-// k-th survivor itself is returned: the smallest survivor at or above it.
-template <int M2>
-__device__ uint64_t survivors_kth(const uint64_t *surv, int ns, int k) {
-    const int lane = threadIdx.x & 63;
-    uint64_t y[M2];
-#pragma unroll
-    for (int i = 0; i < M2; ++i) y[i] = lane + 64 * i < ns ? surv[lane + 64 * i] : 0ull;
-    const uint64_t t = wave_kth_key<M2>(y, k);
-    uint64_t mn = ~0ull;
-#pragma unroll
-    for (int i = 0; i < M2; ++i)
-        if (y[i] != 0ull && y[i] >= t) mn = umin64(mn, y[i]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mn = umin64(mn, __shfl_xor(mn, o, 64));
-    return mn;
-}
-
+// Each wave keeps its own top k as survivors (at most 8k): every key of the
+// row's top k is among them, since it has fewer than k keys of the row, so
+// of its wave, above it. A survivor is then selected iff fewer than k
+// survivors exceed it: a row top-k key has fewer than k keys of the row above
+// it at all, and any other survivor has the k row top-k keys, all survivors,
+// above it. Keys are unique (the index is part of the key), so the count is
+// exact. The counts run in parallel: P threads per survivor (P = 8, 4, 2 or
+// 1 as the survivors fill 64, 128, 256 or 512), each over every P-th run of
+// 8 survivors (two 16-byte LDS reads per 4 keys; the array is zero-filled
+// first, and a zero key exceeds nothing), summed across the P adjacent lanes.
 template <int M>
 __device__ void block_topk(const uint64_t (&x)[M], int k, uint64_t *surv, int *n_surv,
-                           uint64_t *thr, uint32_t *bits) {
+                           uint32_t *bits) {
     const int lane = threadIdx.x & 63;
+    static_assert(SELECT_THREADS <= SELECT_WAVES * WAVE_TOPK, "one zero per thread covers surv");
+    surv[threadIdx.x] = 0ull;
     if (threadIdx.x == 0) *n_surv = 0;
     __syncthreads();
     // each wave's own top-k go to LDS: together they hold the row's top-k
@@ -264,31 +296,34 @@ __device__ void block_topk(const uint64_t (&x)[M], int k, uint64_t *surv, int *n
         if (keep) surv[base + __popcll(m & lt)] = x[i];
     }
     __syncthreads();
-    // the row's k-th key is the k-th among the survivors (a key left out by
-    // its wave has k survivors of that wave above it); wave 0 finds it
-    if (threadIdx.x < 64) {
-        const int ns = *n_surv;  // <= SELECT_WAVES * k
-        uint64_t T;
-        if (ns <= 64) T = survivors_kth<1>(surv, ns, k);
-        else if (ns <= 128) T = survivors_kth<2>(surv, ns, k);
-        else if (ns <= 256) T = survivors_kth<4>(surv, ns, k);
-        else T = survivors_kth<8>(surv, ns, k);
-        if (threadIdx.x == 0) *thr = T;
-    }
-    __syncthreads();
-    const uint64_t T = *thr;
+    const int ns = *n_surv;  // <= SELECT_WAVES * k <= SELECT_THREADS
+    const int lp = ns <= 64 ? 3 : ns <= 128 ? 2 : ns <= 256 ? 1 : 0;  // log2 P
+    const int s = threadIdx.x >> lp, part = threadIdx.x & ((1 << lp) - 1);
+    const uint64_t mine = s < ns ? surv[s] : ~0ull;
+    // runs of 8 keys up to a whole number of rounds over the P parts (<= 512)
+    const int runs = ((ns + (8 << lp) - 1) >> (3 + lp)) << lp;
+    const ulonglong2 *sv2 = reinterpret_cast<const ulonglong2 *>(surv);
+    int above = 0;
+    for (int c = part; c < runs; c += 1 << lp) {
+        ulonglong2 y[4];
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-        if (x[i] != 0ull && x[i] >= T) {
-            const int idx = key_index(x[i]);
-            atomicOr(&bits[idx >> 5], 1u << (idx & 31));
-        }
+        for (int u = 0; u < 4; ++u) y[u] = sv2[4 * c + u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) above += (y[u].x > mine ? 1 : 0) + (y[u].y > mine ? 1 : 0);
+    }
+    // sum over the P lanes of this survivor (aligned groups of P lanes)
+    if (lp >= 1) above += __shfl_xor(above, 1, 64);
+    if (lp >= 2) above += __shfl_xor(above, 2, 64);
+    if (lp >= 3) above += __shfl_xor(above, 4, 64);
+    if (s < ns && part == 0 && above < k) {
+        const int idx = key_index(mine);
+        atomicOr(&bits[idx >> 5], 1u << (idx & 31));
     }
 }
 
 // Keys of candidates tid + 512 i (i < M) from key_of(j, i); then block_topk.
 template <int M, typename KeyFn>
-__device__ void topk_m(int n, int k, KeyFn key_of, uint64_t *surv, int *n_surv, uint64_t *thr,
+__device__ void topk_m(int n, int k, KeyFn key_of, uint64_t *surv, int *n_surv,
                        uint32_t *bits) {
     uint64_t x[M];
 #pragma unroll
@@ -296,17 +331,17 @@ __device__ void topk_m(int n, int k, KeyFn key_of, uint64_t *surv, int *n_surv, 
         const int j = threadIdx.x + SELECT_THREADS * i;
         x[i] = j < n ? key_of(j, i) : 0ull;
     }
-    block_topk<M>(x, k, surv, n_surv, thr, bits);
+    block_topk<M>(x, k, surv, n_surv, bits);
 }
 
 // Dispatch on how many keys each thread holds (uniform over the block).
 template <typename KeyFn>
 __device__ void topk_dispatch(int n, int k, KeyFn key_of, uint64_t *surv, int *n_surv,
-                              uint64_t *thr, uint32_t *bits) {
-    if (n <= SELECT_THREADS) topk_m<1>(n, k, key_of, surv, n_surv, thr, bits);
-    else if (n <= 2 * SELECT_THREADS) topk_m<2>(n, k, key_of, surv, n_surv, thr, bits);
-    else if (n <= 4 * SELECT_THREADS) topk_m<4>(n, k, key_of, surv, n_surv, thr, bits);
-    else topk_m<8>(n, k, key_of, surv, n_surv, thr, bits);
+                              uint32_t *bits) {
+    if (n <= SELECT_THREADS) topk_m<1>(n, k, key_of, surv, n_surv, bits);
+    else if (n <= 2 * SELECT_THREADS) topk_m<2>(n, k, key_of, surv, n_surv, bits);
+    else if (n <= 4 * SELECT_THREADS) topk_m<4>(n, k, key_of, surv, n_surv, bits);
+    else topk_m<8>(n, k, key_of, surv, n_surv, bits);
 }
 
 __device__ void bitonic_desc(uint64_t *keys, int P) {
@@ -389,18 +424,13 @@ __device__ void swap_row(const Dims &dm, int r, const uint32_t *bits, int s0, in
         const uint32_t f1 = b1 & ~(w1 < W ? res[w1] : 0u);
         kept += __popc(b0 & ~f0) + __popc(b1 & ~f1);
         const int cnt = __popc(f0) + __popc(f1);
-        int inc = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += y;
-        }
+        const int inc = wave_incl_sum(cnt);
         int pos = nf + inc - cnt;
         uint32_t m = f0;
         while (m && pos < MAX_K) { fb[pos++] = w0 * 32 + __ffs(m) - 1; m &= m - 1u; }
         m = f1;
         while (m && pos < MAX_K) { fb[pos++] = w1 * 32 + __ffs(m) - 1; m &= m - 1u; }
-        nf += __shfl(inc, 63, 64);
+        nf += __builtin_amdgcn_readlane(inc, 63);
     }
     for (int o = 32; o > 0; o >>= 1) kept += __shfl_xor(kept, o, 64);
     nf = min(nf, k);
@@ -526,15 +556,75 @@ struct ScoresFused {
     }
 };
 
-// ScoresFusedMfma (bf16): the same scores with the dot products on the
-// matrix cores. A wave takes tiles of 16 sub-blocks (a quad of blocks): S =
-// K̄ Q^T on v_mfma_f32_16x16x32_bf16, the A operand being one 16-byte vector of
-// the pooled keys per lane (sub-block 16 tile + l % 16, dimensions 32 s +
-// 8 (l / 16) .. + 7: the quad's vectors as stored), B the group's queries with
-// the heads padded to 16 by zeros. The output tile puts a block's 4 sub-blocks
-// in one lane's 4 accumulators (rows 4 (l / 16) + r), so the block max is
-// in-lane, and the head sum a reduction over the 16 lanes of a row group.
-// The scale multiplies the fp32 dot product.
+// Block scores of a row on the matrix cores (bf16). A wave takes tiles of 16
+// sub-blocks (a quad of blocks): S = K̄ Q^T on v_mfma_f32_16x16x32_bf16, the
+// A operand being one 16-byte vector of the pooled keys per lane (sub-block
+// 16 tile + l % 16, dimensions 32 s + 8 (l / 16) .. + 7: the quad's vectors as
+// stored), B the group's queries with the heads padded to 16 by zeros. The
+// output tile puts a block's 4 sub-blocks in one lane's 4 accumulators (rows
+// 4 (l / 16) + r), so the block max is in-lane, and the head sum a reduction
+// over the 16 lanes of a row group. The scale multiplies the fp32 dot
+// product. The wave takes the TPI tiles from t0 on in each of its passes
+// (t0 = t_first, t_first + t_stride, ... below t_end), all their loads in
+// flight together; block j's score goes to lds[j] and/or out[j] (either may
+// be null).
+template <int D, int G, int TPI>
+__device__ __forceinline__ void mfma_block_scores(const Dims &dm, const bf16_t *qg,
+                                                  const bf16_t *kbar, int r, int n_cand,
+                                                  int t_first, int t_stride, int t_end,
+                                                  float *lds, float *out) {
+    constexpr int KS = D / 32;  // k-steps
+    static_assert(G <= 16, "the group is one 16-wide MFMA tile");
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15, grp = lane >> 4;
+    // B operand: lane holds q[head col][32 s + 8 grp .. + 7]; zero past G
+    bf16x8 qop[KS];
+    {
+        const bf16_t *qh = qg + (int64_t)(col < G ? col : 0) * D + 8 * grp;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            qop[s] = *reinterpret_cast<const bf16x8 *>(qh + 32 * s);
+            if (col >= G) qop[s] = bf16x8{};
+        }
+    }
+    const int nsb = 4 * n_cand;
+    // row r's quads of 16 sub-blocks, in bf16x8 vectors: [Q][D/8][16]
+    const bf16x8 *kb = reinterpret_cast<const bf16x8 *>(kbar + kbar_vec<bf16_t, D>(dm, r, 0, 0));
+    for (int t0 = t_first; t0 < t_end; t0 += t_stride) {
+        bf16x8 a[TPI][KS];
+#pragma unroll
+        for (int u = 0; u < TPI; ++u) {
+            const int sb = 16 * (t0 + u) + col;
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                a[u][s] = sb < nsb ? kb[((int64_t)(t0 + u) * (D / 8) + 4 * s + grp) * 16 + col]
+                                   : bf16x8{};
+        }
+#pragma unroll
+        for (int u = 0; u < TPI; ++u) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][s], qop[s], acc, 0, 0, 0);
+            // rows 4 grp .. 4 grp + 3 = the sub-blocks of block 4 (t0 + u) + grp
+            const float sc4 = dm.scale;
+            float m = fmaxf(fmaxf(acc[0] * sc4, acc[1] * sc4), fmaxf(acc[2] * sc4, acc[3] * sc4));
+            m = col < G ? m : 0.f;
+            m += __shfl_xor(m, 8, 16);
+            m += __shfl_xor(m, 4, 16);
+            m += __shfl_xor(m, 2, 16);
+            m += __shfl_xor(m, 1, 16);
+            const int blk = 4 * (t0 + u) + grp;
+            if (col == 0 && blk < n_cand) {
+                if (lds) lds[blk] = m;
+                if (out) out[blk] = m;
+            }
+        }
+    }
+}
+
+// ScoresFusedMfma (bf16): the selecting workgroup computes its row's scores
+// itself, its waves taking turns over the row's tiles, into LDS.
 template <int D, int G>
 struct ScoresFusedMfma {
     const bf16_t *q;
@@ -542,66 +632,45 @@ struct ScoresFusedMfma {
     float *s_q;          // may be null: scores stay in LDS
     int64_t q_step = 0;  // query offset per workgroup row y (batched selections)
     __device__ const float *row(const Dims &dm, int r, int n_cand) const {
-        constexpr int KS = D / 32, TPI = 4;  // k-steps; tiles per pass per wave
-        static_assert(G <= 16, "the group is one 16-wide MFMA tile");
+        constexpr int TPI = 4;  // tiles per pass per wave
         __shared__ float sc[MAX_W * 32];
-        const int lane = threadIdx.x & 63;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int nw = blockDim.x >> 6;
-        const int col = lane & 15, grp = lane >> 4;
         const int b = r / dm.Hkv, g = r % dm.Hkv;
-        // B operand: lane holds q[head col][32 s + 8 grp .. + 7]; zero past G
-        bf16x8 qop[KS];
-        {
-            const bf16_t *qh = q + blockIdx.y * q_step +
-                               ((int64_t)b * dm.Hq + (int64_t)g * G + (col < G ? col : 0)) * D +
-                               8 * grp;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                qop[s] = *reinterpret_cast<const bf16x8 *>(qh + 32 * s);
-                if (col >= G) qop[s] = bf16x8{};
-            }
-        }
-        const int nsb = 4 * n_cand;
-        // row r's quads of 16 sub-blocks, in bf16x8 vectors: [Q][D/8][16]
-        const bf16x8 *kb = reinterpret_cast<const bf16x8 *>(kbar + kbar_vec<bf16_t, D>(dm, r, 0, 0));
+        const bf16_t *qg = q + blockIdx.y * q_step + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
         float *out = s_q ? s_q + (int64_t)r * dm.max_blocks : nullptr;
-        const int n_tiles = (nsb + 15) / 16;
-        for (int t0 = wave * TPI; t0 < n_tiles; t0 += nw * TPI) {
-            bf16x8 a[TPI][KS];
-#pragma unroll
-            for (int u = 0; u < TPI; ++u) {
-                const int sb = 16 * (t0 + u) + col;
-#pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    a[u][s] = sb < nsb ? kb[((int64_t)(t0 + u) * (D / 8) + 4 * s + grp) * 16 + col]
-                                       : bf16x8{};
-            }
-#pragma unroll
-            for (int u = 0; u < TPI; ++u) {
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][s], qop[s], acc, 0, 0, 0);
-                // rows 4 grp .. 4 grp + 3 = the sub-blocks of block 4 (t0 + u) + grp
-                const float sc4 = dm.scale;
-                float m = fmaxf(fmaxf(acc[0] * sc4, acc[1] * sc4), fmaxf(acc[2] * sc4, acc[3] * sc4));
-                m = col < G ? m : 0.f;
-                m += __shfl_xor(m, 8, 16);
-                m += __shfl_xor(m, 4, 16);
-                m += __shfl_xor(m, 2, 16);
-                m += __shfl_xor(m, 1, 16);
-                const int blk = 4 * (t0 + u) + grp;
-                if (col == 0 && blk < n_cand) {
-                    sc[blk] = m;
-                    if (out) out[blk] = m;
-                }
-            }
-        }
+        mfma_block_scores<D, G, TPI>(dm, qg, kbar, r, n_cand, wave * TPI, nw * TPI,
+                                     (n_cand + 3) / 4, sc, out);
         __syncthreads();
         return sc;
     }
 };
+
+// Block scores on the matrix cores with the row split over workgroups
+// (blockIdx.x = chunk of SCORE_TILES_PER_WG tiles, blockIdx.y = row), so that
+// a launch has many more workgroups than rows: each wave loads its 4 tiles
+// (4 KiB of pooled keys) at once, and the grid covers the row in one pass.
+// With dstep, n_cand comes from the step record and the grid is sized for the
+// capacity; chunks past the candidates exit at once.
+constexpr int SCORE_WAVES = 4;
+constexpr int SCORE_TPI = 4;
+constexpr int SCORE_TILES_PER_WG = SCORE_WAVES * SCORE_TPI;
+template <int D, int G>
+__global__ void __launch_bounds__(64 * SCORE_WAVES)
+score_mfma_kernel(Dims dm, const bf16_t *__restrict__ q, const bf16_t *__restrict__ kbar,
+                  int n_cand, float *__restrict__ s_q, const int32_t *__restrict__ dstep) {
+    if (dstep) n_cand = read_step(dstep, dm).n_cand;
+    const int n_tiles = (n_cand + 3) / 4;
+    const int t_begin = blockIdx.x * SCORE_TILES_PER_WG;
+    if (t_begin >= n_tiles) return;
+    const int r = blockIdx.y;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int b = r / dm.Hkv, g = r % dm.Hkv;
+    const bf16_t *qg = q + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
+    const int t0 = t_begin + wave * SCORE_TPI;
+    mfma_block_scores<D, G, SCORE_TPI>(dm, qg, kbar, r, n_cand, t0, n_tiles, min(t0 + 1, n_tiles),
+                                       nullptr, s_q + (int64_t)r * dm.max_blocks);
+}
 
 // Independent selections in one launch (workgroup row y = blockIdx.y): y
 // has n_cand + y * cand_step candidates and writes sel / n_sel shifted by y
@@ -622,7 +691,6 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
     __shared__ uint32_t ge[MAX_W], ev[MAX_W], sb[MAX_W], res[MAX_W];
     __shared__ __attribute__((aligned(16))) uint64_t surv[SELECT_WAVES * WAVE_TOPK + 2];
     __shared__ int n_surv;
-    __shared__ uint64_t thr;
     __shared__ uint64_t red64[SELECT_WAVES];
     __shared__ int red32[SELECT_WAVES];
     __shared__ int fb[MAX_K], fs[MAX_K], fo[MAX_K];
@@ -670,7 +738,7 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
         const int ke = min(dm.k_e, n_cand);
         if (ke > 0 && dm.k_e <= WAVE_TOPK) {
             topk_dispatch(n_cand, ke, [&](int j, int) { return rank_key(E[j], j); }, surv,
-                          &n_surv, &thr, ge);
+                          &n_surv, ge);
         } else if (ke > 0) {
             for (int i = tid; i < P; i += nt) keys[i] = i < n_cand ? rank_key(E[i], i) : 0ull;
             __syncthreads();
@@ -744,7 +812,7 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
     if (kq > 0 && dm.k_q <= WAVE_TOPK) {
         topk_dispatch(n_cand, kq, [&](int j, int i) -> uint64_t {
             return ((ge[j >> 5] >> (j & 31)) & 1u) ? 0ull : rank_key(sv[i], j);
-        }, surv, &n_surv, &thr, sb);
+        }, surv, &n_surv, sb);
     } else if (kq > 0) {
         for (int i = tid; i < P; i += nt) {
             const bool ok = i < n_cand && !((ge[i >> 5] >> (i & 31)) & 1u);
@@ -774,18 +842,13 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
     const int w0 = 2 * lane, w1 = 2 * lane + 1;
     auto place = [&](uint32_t a0, uint32_t a1, int32_t *dst, int cap) -> int {
         const int cnt = __popc(a0) + __popc(a1);
-        int inc = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += y;
-        }
+        const int inc = wave_incl_sum(cnt);
         int pos = inc - cnt;
         for (uint32_t m = a0; m; m &= m - 1u, ++pos)
             if (pos < cap) dst[pos] = 32 * w0 + __ffs(m) - 1;
         for (uint32_t m = a1; m; m &= m - 1u, ++pos)
             if (pos < cap) dst[pos] = 32 * w1 + __ffs(m) - 1;
-        const int n = __shfl(inc, 63, 64);
+        const int n = __builtin_amdgcn_readlane(inc, 63);
         for (int i = min(n, cap) + lane; i < cap; i += 64) dst[i] = -1;
         return min(n, cap);
     };
@@ -1012,10 +1075,22 @@ hipError_t launch_step_advance(const Dims &dm, int32_t *dstep, hipStream_t st) {
 
 template <typename T, int D, int G>
 hipError_t launch_score(const Dims &dm, const void *q, const void *kbar, int n_cand, float *s_q,
-                        hipStream_t st) {
-    dim3 grid((4 * n_cand + 255) / 256, dm.rows);
-    hipLaunchKernelGGL((score_kernel<T, D, G>), grid, dim3(256), 0, st, dm,
-                       static_cast<const T *>(q), static_cast<const T *>(kbar), n_cand, s_q);
+                        hipStream_t st, const int32_t *dstep) {
+    if constexpr (std::is_same_v<T, bf16_t>) {
+        // with a device step record the grid covers the capacity
+        const int n_tiles = ((dstep ? dm.max_blocks : n_cand) + 3) / 4;
+        if (n_tiles == 0) return hipSuccess;  // no candidates: nothing to score
+        dim3 grid((n_tiles + SCORE_TILES_PER_WG - 1) / SCORE_TILES_PER_WG, dm.rows);
+        hipLaunchKernelGGL((score_mfma_kernel<D, G>), grid, dim3(64 * SCORE_WAVES), 0, st, dm,
+                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(kbar),
+                           n_cand, s_q, dstep);
+    } else {
+        if (dstep) return hipErrorInvalidValue;  // float32 scores take the step by value
+        if (n_cand == 0) return hipSuccess;
+        dim3 grid((4 * n_cand + 255) / 256, dm.rows);
+        hipLaunchKernelGGL((score_kernel<T, D, G>), grid, dim3(256), 0, st, dm,
+                           static_cast<const T *>(q), static_cast<const T *>(kbar), n_cand, s_q);
+    }
     return hipGetLastError();
 }
 
@@ -1062,12 +1137,28 @@ hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, i
                               sel_bits, swap, parts, st);
 }
 
+// Rows up to which nosa_score_select scores on the split grid and selects in
+// a second launch (bf16); above it one workgroup per row does both. Measured
+// with HIP events on 256 CUs, score + select vs one launch: 64 rows x 512
+// candidates 8.8 + 8.7 vs 19.3 us; 128 rows x 2048 51 + 10.4 vs 72 us; 256
+// rows x 1024 53 + 10.8 vs 59-62 us (with a workgroup per CU the fused form
+// hides each row's selection behind other rows' scoring).
+constexpr int SPLIT_SCORE_MAX_ROWS = 128;
+
 template <typename T, int D, int G>
 hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, float *s_q,
                                const float *e_blk, int n_cand, int n_prev, uint32_t *ge,
                                uint32_t *ev, int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
                                const SwapPtrs *swap, hipStream_t st, const int32_t *dstep) {
     if constexpr (std::is_same_v<T, bf16_t>) {
+        if (dm.rows <= SPLIT_SCORE_MAX_ROWS) {
+            // too few rows to fill the chip with one workgroup each: score on
+            // a grid split over the row's candidates, then select from s_q
+            const hipError_t e = launch_score<T, D, G>(dm, q, kbar, n_cand, s_q, st, dstep);
+            if (e != hipSuccess) return e;
+            return launch_select_from(dm, ScoresGlobal{s_q}, e_blk, n_cand, n_prev, ge, ev, sel,
+                                      n_sel, sel_bits, swap, nullptr, st, 1, dstep);
+        }
         const ScoresFusedMfma<D, G> src{static_cast<const bf16_t *>(q),
                                         static_cast<const bf16_t *>(kbar), s_q};
         return launch_select_from(dm, src, e_blk, n_cand, n_prev, ge, ev, sel, n_sel, sel_bits,
@@ -1162,7 +1253,7 @@ NOSA_POOL_INST(bf16_t, 128)
 
 #define NOSA_SCORE_INST(T, D, G)                                                               \
     template hipError_t launch_score<T, D, G>(const Dims &, const void *, const void *, int,   \
-                                              float *, hipStream_t);                           \
+                                              float *, hipStream_t, const int32_t *);          \
     template hipError_t launch_ingest<T, D, G>(const Dims &, const void *, const void *,       \
                                                const void *, const float *, int, int, void *,  \
                                                void *, int64_t, int, float *, int64_t, void *, \
