@@ -50,6 +50,9 @@ def parse():
                          "becomes a latency-bound launch of its own)")
     ap.add_argument("--offload-steps", type=int, default=60,
                     help="steps of the offloaded 128k-context leg (0 = skip)")
+    ap.add_argument("--model-steps", type=int, default=6,
+                    help="timed steps of the 32-layer 8B-shaped offload leg, after a cold "
+                         "step and a warm one (0 = skip)")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the locality ablation of the offload leg (budget splits "
                          "k_e + k_q = k with k_e = 32 and 0, and per-block / per-token "
@@ -634,6 +637,127 @@ def offload_leg(args, dev, stream):
     return out
 
 
+def model_leg(args, dev, stream, h2d_gbs=None):
+    """The 32-layer 8B-shaped decode step (batch 64, 32 / 8 heads, 32k context,
+    k = 48 + 16, KV in pinned host memory): all five stages in every layer of
+    every step, layer after layer on one stream. The host KV of 32 layers
+    would take 279 GB of pinned memory; layers share two host slabs (layer l
+    reads slab l % 2), which leaves every shape and the bytes moved per step
+    unchanged. Step 0 fills the empty HBM caches (every selected block is
+    fetched) and is reported apart; step 1 is a warm-up; then
+    args.model_steps steps are timed, with HIP events around every layer's
+    fetch and attention launches."""
+    import numpy as np
+    import torch
+
+    import synth
+    from trainable_block_sparse_nosa_amd import _lib as L
+    from trainable_block_sparse_nosa_amd.hostmem import PinnedBuffer
+    from trainable_block_sparse_nosa_amd.pipeline import DecodeLayer, pack_blocks
+
+    w = synth.WORKLOADS["offload_8b_32layer_32k"]
+    n, warm = args.model_steps, 2
+    T = warm + n
+    nb, BE = w.nb_max, 2 * 64 * w.head_dim
+    t0 = time.time()
+    slabs = []
+    for sl in range(w.kv_slabs):
+        buf = PinnedBuffer(w.rows * nb * BE * 2)
+        view = buf.array(np.uint16, (w.rows, nb, BE))
+
+        def fill(r, sl=sl, view=view):
+            b, g = divmod(r, w.n_kv_heads)
+            view[r] = pack_blocks(synth.bf16_bits(synth.keys_row(w, sl, b, g)),
+                                  synth.bf16_bits(synth.values_row(w, sl, b, g)), nb)
+        synth.parallel_map(fill, range(w.rows), 16)
+        slabs.append(buf)
+    layers, qs = [], []
+    for li in range(w.n_layers):
+        e = np.zeros((w.rows, nb * 64), np.float32)
+        e[:, :w.n_max] = np.stack(synth.parallel_map(
+            lambda r: synth.evict_row(w, li, *divmod(r, w.n_kv_heads)), range(w.rows), 16))
+        e_tok = torch.from_numpy(e).to(dev)
+        qh = np.stack(synth.parallel_map(lambda t: synth.bf16_bits(synth.queries_step(w, li, t)),
+                                         range(T), 16))
+        qs.append(torch.from_numpy(qh.view(np.int16)).to(dev).view(torch.bfloat16))
+        layers.append(DecodeLayer(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                                  head_dim=w.head_dim, k_e=w.k_e, k_q=w.k_q, max_blocks=nb,
+                                  dtype=L.NOSA_BF16, kv=slabs[li % w.kv_slabs].dev,
+                                  kv_row_blocks=nb, e_tok=e_tok, offload=True))
+    torch.cuda.synchronize()
+    log(f"{w.name}: {w.n_layers} layers ready in {time.time() - t0:.1f} s "
+        f"({w.kv_slabs} pinned host slabs of {slabs[0].nbytes / 2**30:.1f} GiB)")
+
+    def fetched_blocks():
+        return sum(int(layer.counters[:, 0].sum().item()) for layer in layers)
+
+    for layer in layers:
+        layer.start(w.n_tokens(0), stream)
+    torch.cuda.synchronize()
+    tc = time.perf_counter()
+    for li, layer in enumerate(layers):
+        layer.step(qs[li][0], w.n_tokens(0), stream)
+    torch.cuda.synchronize()
+    cold_s = time.perf_counter() - tc
+    cold_blocks = fetched_blocks()
+    for t in range(1, warm):
+        for li, layer in enumerate(layers):
+            layer.step(qs[li][t], w.n_tokens(t), stream)
+    torch.cuda.synchronize()
+    f0 = fetched_blocks()
+    ev = HipTimingEvents(2 * 2 * w.n_layers * n + 8)
+    pending = []
+
+    def hook(name, fn, *a):
+        if name in ("fetch", "decode"):
+            on = a[-1] if a[-1] is not None else torch.cuda.current_stream()
+            h = on.cuda_stream if hasattr(on, "cuda_stream") else int(on)
+            i0 = 2 * len(pending)
+            ev.record(i0, h)
+            fn(*a)
+            ev.record(i0 + 1, h)
+            pending.append((name, i0, i0 + 1))
+        else:
+            fn(*a)
+
+    for layer in layers:
+        layer.stage_hook = hook
+    torch.cuda.synchronize()
+    ts = time.perf_counter()
+    for t in range(warm, T):
+        for li, layer in enumerate(layers):
+            layer.step(qs[li][t], w.n_tokens(t), stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - ts
+    for layer in layers:
+        layer.stage_hook = None
+    fetched = fetched_blocks() - f0
+    fetch_ms = sum(ev.elapsed_ms(a, b) for nm, a, b in pending if nm == "fetch")
+    dec = [ev.elapsed_ms(a, b) for nm, a, b in pending if nm == "decode"]
+    ev.close()
+    kept = sum(float(layer.counters[:, 1].sum().item()) for layer in layers)
+    block_bytes = 2 * 64 * w.head_dim * 2
+    swap_gbs = fetched * block_bytes / (fetch_ms / 1e3) / 1e9
+    out = {
+        "workload": w.name, "layers": w.n_layers, "host_kv_slabs": w.kv_slabs,
+        "steps": n, "steps_per_s": n / elapsed, "ms_per_step": elapsed / n * 1e3,
+        "fetched_gib_per_step": fetched * block_bytes / n / 2**30,
+        "fetch_ms_per_step": fetch_ms / n, "swap_gbs": swap_gbs,
+        "attn_partial_us_per_layer": sum(dec) / len(dec) * 1e3,
+        # over steps 1 .. T-1: step 0 finds every cache empty by construction
+        "gamma_mean": kept / (w.n_layers * w.rows * w.k * (T - 1)),
+        "cold_step_s": cold_s, "cold_fetched_gib": cold_blocks * block_bytes / 2**30,
+    }
+    if h2d_gbs:
+        out["h2d_memcpy_gbs"] = h2d_gbs
+        out["frac_of_h2d"] = swap_gbs / h2d_gbs
+    del layers, qs
+    for buf in slabs:
+        buf.free()
+    torch.cuda.empty_cache()
+    return out
+
+
 def zero_copy_contiguous_gbs(layer, w, stream, reps=3):
     """The fetch kernel over contiguous host blocks (blocks 0..k-1 of every row
     into slots 0..k-1): the zero-copy read rate without the scatter of a
@@ -825,6 +949,15 @@ def main():
         log(f"offload: {swap['steps_per_s']:.1f} steps/s, swap {swap['swap_gbs']:.1f} GB/s "
             f"= {100 * swap['frac_of_h2d']:.1f} % of hipMemcpy H2D {swap['h2d_memcpy_gbs']:.1f} GB/s")
 
+    model = None
+    if args.model_steps > 0 and not w.offload:
+        log("32-layer leg: offload_8b_32layer_32k")
+        model = model_leg(args, dev, stream, swap["h2d_memcpy_gbs"] if swap else None)
+        log(f"32 layers: {model['steps_per_s']:.2f} steps/s ({model['ms_per_step']:.1f} ms), "
+            f"{model['fetched_gib_per_step']:.2f} GiB fetched per step at "
+            f"{model['swap_gbs']:.1f} GB/s, attention {model['attn_partial_us_per_layer']:.1f} us "
+            f"per layer; cold step {model['cold_step_s']:.2f} s")
+
     cpu = None
     if args.cpu_seconds > 0:
         log("timing the oracle sample on the host")
@@ -864,6 +997,7 @@ def main():
         "overlap": overlapped,
         "gamma_mean": gamma_mean,
         "swap": swap,
+        "model_8b_32layer": model,
         "ingest": ingest,
         "prefill": prefill,
         "cpu_baseline": cpu,
