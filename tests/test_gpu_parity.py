@@ -321,3 +321,39 @@ def test_deterministic_rerun():
     for t in a:
         for key in a[t]:
             np.testing.assert_array_equal(a[t][key], b[t][key], err_msg=f"{key} t={t}")
+
+
+def test_select_signed_zero_ties():
+    """Scores of exactly +0 and -0 at both budget boundaries. The oracle
+    compares them as equal numbers, so the lower block id ranks first; the
+    kernel's integer keys must order them the same way (Gamma_e from the
+    eviction scores, then Gamma_q from the query scores of the rest)."""
+    _gpu()
+    import oracle
+    from trainable_block_sparse_nosa_amd import _lib as L
+    n_cand, k_e, k_q, nb = 12, 3, 3, 16
+    shape = L.make_shape(1, 4, 1, 128, k_e, k_q, nb, L.NOSA_BF16)
+    e = np.zeros(nb, np.float32)
+    s = np.zeros(nb, np.float32)
+    e[:n_cand] = [-1.0, 0.0, -0.0, 0.0, -0.0, 0.0, -0.0, -1.0, -2.0, 0.0, -3.0, -4.0]
+    s[:n_cand] = [-0.0, 0.0, 0.0, 0.0, 0.0, -0.0, 0.0, -5.0, -5.0, 0.0, -5.0, -5.0]
+    ge_ref = oracle.topk(e[:n_cand], k_e)
+    allowed = np.ones(n_cand, np.uint8)
+    allowed[ge_ref] = 0
+    gq_ref = oracle.topk(s[:n_cand], k_q, allowed)
+    assert ge_ref == [1, 2, 3] and gq_ref == [0, 4, 5]
+    dev = "cuda"
+    e_d = torch.from_numpy(e).to(dev)[None]
+    s_d = torch.from_numpy(s).to(dev)[None]
+    ge = torch.zeros(1, 1, dtype=torch.int32, device=dev)
+    ev = torch.zeros_like(ge)
+    bits = torch.zeros_like(ge)
+    sel = torch.full((1, k_e + k_q), -7, dtype=torch.int32, device=dev)
+    n_sel = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = L.make_step(64 * n_cand + 1, -1)
+    L.nosa_select(shape, s_d, e_d, st, ge, ev, sel, n_sel, bits, None)
+    torch.cuda.synchronize()
+    assert int(n_sel[0]) == k_e + k_q
+    assert sel[0].tolist() == sorted(ge_ref + gq_ref)
+    ge_bits = int(ge[0, 0].item()) & 0xFFFFFFFF
+    assert [j for j in range(n_cand) if (ge_bits >> j) & 1] == ge_ref

@@ -113,8 +113,10 @@ static_assert(vt_order_is_inverse(), "vt_pos_of inverts vt_token_at");
 
 // Total order used by every selection: a higher score ranks first, an equal
 // score ranks the lower block id first. Keys compare as unsigned integers.
+// -0 and +0 are equal scores, so -0 is mapped to +0 first (the id decides).
 __device__ __forceinline__ uint32_t orderable(float f) {
     uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 __device__ __forceinline__ uint64_t rank_key(float score, int j) {
