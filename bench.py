@@ -348,6 +348,20 @@ def ingest_leg(w, args, dev, stream, main_steps_per_s):
 ATTN_STAGES = ("decode", "decode_e", "decode_q")
 
 
+def bracket(ev, i0: int, h: int, fn, a):
+    """Run fn(*a) between events i0 and i0 + 1 of ev on stream handle h. The
+    attention partial call goes through its timed entry point, which records
+    the two events at the partial kernel's own start and end (so they agree
+    with a kernel trace); any other call sits between two event records."""
+    from trainable_block_sparse_nosa_amd import _lib as L
+    if fn is L.nosa_decode_partial:
+        L.nosa_decode_partial_timed(*a[:-1], ev.handle(i0), ev.handle(i0 + 1), a[-1])
+    else:
+        ev.record(i0, h)
+        fn(*a)
+        ev.record(i0 + 1, h)
+
+
 class HipTimingEvents:
     """A pool of HIP timing events created with hipEventDisableSystemFence:
     recording one does not write back and invalidate the caches, so bracketing
@@ -388,6 +402,10 @@ class HipTimingEvents:
     def record(self, i: int, stream_handle: int):
         self._chk(self.hip.hipEventRecord(self.events[i], stream_handle))
 
+    def handle(self, i: int) -> int:
+        """The hipEvent_t of event i, as an integer."""
+        return self.events[i].value
+
     def elapsed_ms(self, i: int, j: int) -> float:
         ms = self._c.c_float()
         self._chk(self.hip.hipEventElapsedTime(self._c.byref(ms), self.events[i], self.events[j]))
@@ -400,12 +418,12 @@ class HipTimingEvents:
 
 
 def timed_run(layer, w, q, args, stream, event_stages=ATTN_STAGES, new=None, sample_every=8):
-    """Warm up, then time exactly args.steps steps. HIP events, recorded on the
-    stream each call runs on, bracket the listed stages in every
-    sample_every-th timed step (a pair of event records costs the step about
-    4 us on the 32k workload, so bracketing every step would understate the
-    throughput by ~8 %). Returns (elapsed s, [(stage, step, ms)], blocks
-    fetched in the timed steps)."""
+    """Warm up, then time exactly args.steps steps. HIP events bracket the
+    listed stages in every sample_every-th timed step (see bracket(): the
+    attention partial kernel's events mark its own start and end; timing
+    every step would understate the throughput by ~8 % on the 32k workload).
+    Returns (elapsed s, [(stage, step, ms)], blocks fetched in the timed
+    steps)."""
     import torch
     layer.start(w.n_tokens(0), stream)
     for t in range(args.warmup):
@@ -421,9 +439,7 @@ def timed_run(layer, w, q, args, stream, event_stages=ATTN_STAGES, new=None, sam
             on = a[-1] if a[-1] is not None else torch.cuda.current_stream()
             h = on.cuda_stream if hasattr(on, "cuda_stream") else int(on)
             i0 = 2 * len(pending)
-            ev.record(i0, h)
-            fn(*a)
-            ev.record(i0 + 1, h)
+            bracket(ev, i0, h, fn, a)
             pending.append((name, cur["i"], i0, i0 + 1))
         else:
             fn(*a)
@@ -548,9 +564,7 @@ def cold_cache_run(layer, w, q, args, stream, n_steps: int, scratch_mib: int = 1
             on = a[-1] if a[-1] is not None else torch.cuda.current_stream()
             h = on.cuda_stream if hasattr(on, "cuda_stream") else int(on)
             i0 = 2 * len(done)
-            ev.record(i0, h)
-            fn(*a)
-            ev.record(i0 + 1, h)
+            bracket(ev, i0, h, fn, a)
             done.append((t, i0))
         else:
             fn(*a)
@@ -713,9 +727,7 @@ def model_leg(args, dev, stream, h2d_gbs=None):
             on = a[-1] if a[-1] is not None else torch.cuda.current_stream()
             h = on.cuda_stream if hasattr(on, "cuda_stream") else int(on)
             i0 = 2 * len(pending)
-            ev.record(i0, h)
-            fn(*a)
-            ev.record(i0 + 1, h)
+            bracket(ev, i0, h, fn, a)
             pending.append((name, i0, i0 + 1))
         else:
             fn(*a)

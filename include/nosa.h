@@ -359,6 +359,25 @@ nosa_status nosa_decode_partial(const nosa_shape *shape, const void *q, const vo
                                 const nosa_step *step, const float *e_tok, int64_t e_row_stride,
                                 void *ws, size_t ws_bytes, int32_t chunk0, void *stream);
 
+/* nosa_decode_partial with its partial kernel bracketed by two HIP events
+ * (hipEvent_t, created by the caller with hipEventCreate or
+ * hipEventCreateWithFlags): the kernel is launched through
+ * hipExtLaunchKernelGGL, which records start_event when the kernel starts
+ * and stop_event when it ends, so hipEventElapsedTime of the pair is the
+ * kernel's own duration, without the launch in front of it. For measuring
+ * the attention kernel inside a running decode loop. Both events must be
+ * non-NULL (NOSA_ERR_INVALID_ARGUMENT otherwise); everything else is as in
+ * nosa_decode_partial. */
+nosa_status nosa_decode_partial_timed(const nosa_shape *shape, const void *q, const void *kv,
+                                      int64_t kv_row_blocks, int32_t kv_mode,
+                                      const int32_t *list, const int32_t *n_list,
+                                      int32_t list_stride, int32_t list_len, int32_t with_newest,
+                                      const void *cur_kv, int64_t cur_row_blocks,
+                                      const nosa_step *step, const float *e_tok,
+                                      int64_t e_row_stride, void *ws, size_t ws_bytes,
+                                      int32_t chunk0, void *start_event, void *stop_event,
+                                      void *stream);
+
 /* The second half: merges workspace chunks 0 .. n_chunks-1 of every row in
  * chunk order and writes out [batch][n_q_heads][D]. */
 nosa_status nosa_decode_combine(const nosa_shape *shape, int32_t n_chunks, void *out, void *ws,

@@ -98,6 +98,11 @@ def test_invalid_pointers_and_steps_rejected():
     assert lib.nosa_append_tokens(ctypes.byref(sh), 16, 16, 3, 16, 4, 4, None) == 1
     assert lib.nosa_append_tokens(ctypes.byref(sh), 16, 16, -1, 16, 4, 0, None) == 1
     assert lib.nosa_append_tokens(ctypes.byref(sh), 16, 16, 3, None, 4, 0, None) == 1
+    # timed partial decode without its two events
+    args = [ctypes.byref(sh), 16, 16, 64, L.NOSA_KV_FULL, 16, 16, 64, 64, 1, 16, 64,
+            ctypes.byref(ok_step), 16, 64 * 64, 16, 1 << 30, 0]
+    assert lib.nosa_decode_partial_timed(*args, None, 16, None) == 1
+    assert lib.nosa_decode_partial_timed(*args, 16, None, None) == 1
     # a step beyond the block capacity
     big = L.make_step(64 * 64 + 1, -1)
     assert lib.nosa_score_blocks(ctypes.byref(sh), 16, 16, ctypes.byref(big), 16, None) == 1

@@ -357,3 +357,40 @@ def test_select_signed_zero_ties():
     assert sel[0].tolist() == sorted(ge_ref + gq_ref)
     ge_bits = int(ge[0, 0].item()) & 0xFFFFFFFF
     assert [j for j in range(n_cand) if (ge_bits >> j) & 1] == ge_ref
+
+
+def test_timed_partial_matches_untimed():
+    """nosa_decode_partial_timed (the attention partial kernel bracketed by two
+    events at its own start and end) writes the same bits as
+    nosa_decode_partial, and the events give a positive duration per call."""
+    gh = _gpu()
+    import bench
+    from trainable_block_sparse_nosa_amd import _lib as L
+    w = synth.WORKLOADS["small_bf16"]
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov)
+    outs = []
+    for timed in (False, True):
+        layer = gh.make_layer(w, inp)
+        ev = bench.HipTimingEvents(2 * w.steps)
+        n = [0]
+
+        def hook(name, fn, *a):
+            if timed and fn is L.nosa_decode_partial:
+                bench.bracket(ev, 2 * n[0], 0, fn, a)
+                n[0] += 1
+            else:
+                fn(*a)
+        layer.stage_hook = hook
+        layer.start(w.n_tokens(0))
+        res = []
+        for t in range(w.steps):
+            layer.step(inp.q[t], w.n_tokens(t))
+            res.append(layer.out.clone())
+        torch.cuda.synchronize()
+        outs.append(torch.stack(res).cpu())
+        if timed:
+            assert n[0] == w.steps
+            assert all(ev.elapsed_ms(2 * i, 2 * i + 1) > 0 for i in range(n[0]))
+        ev.close()
+    assert torch.equal(outs[0], outs[1])

@@ -33,7 +33,8 @@ EXPORTS = (
     "nosa_select_parts", "nosa_score_select", "nosa_fetch_blocks", "nosa_append_tokens",
     "nosa_ingest_tokens", "nosa_prefill_pool_queries", "nosa_prefill_select",
     "nosa_prefill_attention", "nosa_decode_workspace_size", "nosa_decode_chunks",
-    "nosa_sparse_decode", "nosa_decode_partial", "nosa_decode_combine",
+    "nosa_sparse_decode", "nosa_decode_partial", "nosa_decode_partial_timed",
+    "nosa_decode_combine",
     "nosa_step_advance", "nosa_pool_step", "nosa_append_step", "nosa_score_select_step",
     "nosa_decode_partial_step",
     "nosa_host_alloc", "nosa_host_free", "nosa_read_probe", "nosa_status_string",
@@ -83,6 +84,8 @@ def _load() -> ctypes.CDLL:
         "nosa_prefill_attention": [SH, P, I32, P, I64, P, I64, P, P, P, P],
         "nosa_decode_partial": [SH, P, P, I64, I32, P, P, I32, I32, I32, P, I64, ST, P, I64, P, SZ,
                                 I32, P],
+        "nosa_decode_partial_timed": [SH, P, P, I64, I32, P, P, I32, I32, I32, P, I64, ST, P, I64,
+                                      P, SZ, I32, P, P, P],
         "nosa_decode_combine": [SH, I32, P, P, SZ, P],
         "nosa_host_alloc": [SZ, I32, ctypes.POINTER(P), ctypes.POINTER(P)],
         "nosa_host_free": [P],
@@ -209,6 +212,18 @@ def nosa_decode_partial(shape, q, kv, kv_row_blocks, kv_mode, list_, n_list, lis
         ctypes.byref(shape), _p(q), _p(kv), kv_row_blocks, kv_mode, _p(list_), _p(n_list),
         list_stride, list_len, with_newest, _p(cur_kv), cur_row_blocks, ctypes.byref(step),
         _p(e_tok), e_row_stride, _p(ws), ws_bytes, chunk0, _s(stream)))
+
+
+def nosa_decode_partial_timed(shape, q, kv, kv_row_blocks, kv_mode, list_, n_list, list_stride,
+                              list_len, with_newest, cur_kv, cur_row_blocks, step, e_tok,
+                              e_row_stride, ws, ws_bytes, chunk0, start_event, stop_event,
+                              stream=None):
+    """start_event / stop_event: hipEvent_t handles (ints or ctypes pointers)."""
+    _chk("nosa_decode_partial_timed", _L.nosa_decode_partial_timed(
+        ctypes.byref(shape), _p(q), _p(kv), kv_row_blocks, kv_mode, _p(list_), _p(n_list),
+        list_stride, list_len, with_newest, _p(cur_kv), cur_row_blocks, ctypes.byref(step),
+        _p(e_tok), e_row_stride, _p(ws), ws_bytes, chunk0, _p(start_event), _p(stop_event),
+        _s(stream)))
 
 
 def nosa_decode_combine(shape, n_chunks, out, ws, ws_bytes, stream=None):

@@ -131,7 +131,7 @@ nosa_status decode_common(const Dims &dm, int kind, const void *q, const void *k
 }
 
 nosa_status launch_partial(const Dims &dm, int kind, const DecodePlan &pl, const DecodeArgs &a,
-                           hipStream_t st) {
+                           hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
     return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
         using T = std::remove_pointer_t<decltype(tp)>;
         constexpr int D = decltype(dc)::value;
@@ -139,9 +139,9 @@ nosa_status launch_partial(const Dims &dm, int kind, const DecodePlan &pl, const
             constexpr int G = decltype(gc)::value;
             if constexpr (std::is_same<T, bf16_t>::value) {
                 if (kind == NOSA_DECODE_MFMA)
-                    return hip_status(launch_decode_mfma<D, G>(dm, pl, a, st));
+                    return hip_status(launch_decode_mfma<D, G>(dm, pl, a, st, ev0, ev1));
             }
-            return hip_status(launch_decode_valu<T, D, G>(dm, pl, a, st));
+            return hip_status(launch_decode_valu<T, D, G>(dm, pl, a, st, ev0, ev1));
         });
     });
 }
@@ -465,12 +465,15 @@ nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const voi
     return launch_merge(dm, pl.n_chunks, a, out, st);
 }
 
-nosa_status nosa_decode_partial(const nosa_shape *shape, const void *q, const void *kv,
-                                int64_t kv_row_blocks, int32_t kv_mode, const int32_t *list,
-                                const int32_t *n_list, int32_t list_stride, int32_t list_len,
-                                int32_t with_newest, const void *cur_kv, int64_t cur_row_blocks,
-                                const nosa_step *step, const float *e_tok, int64_t e_row_stride,
-                                void *ws, size_t ws_bytes, int32_t chunk0, void *stream) {
+static nosa_status decode_partial_impl(const nosa_shape *shape, const void *q, const void *kv,
+                                       int64_t kv_row_blocks, int32_t kv_mode,
+                                       const int32_t *list, const int32_t *n_list,
+                                       int32_t list_stride, int32_t list_len, int32_t with_newest,
+                                       const void *cur_kv, int64_t cur_row_blocks,
+                                       const nosa_step *step, const float *e_tok,
+                                       int64_t e_row_stride, void *ws, size_t ws_bytes,
+                                       int32_t chunk0, hipEvent_t ev0, hipEvent_t ev1,
+                                       void *stream) {
     Dims dm;
     nosa_status s = make_dims(shape, &dm);
     if (s != NOSA_OK) return s;
@@ -495,7 +498,34 @@ nosa_status nosa_decode_partial(const nosa_shape *shape, const void *q, const vo
     a.with_newest = with_newest;
     a.chunk0 = chunk0;
     a.cb = pl.cb;
-    return launch_partial(dm, kind, pl, a, (hipStream_t)stream);
+    return launch_partial(dm, kind, pl, a, (hipStream_t)stream, ev0, ev1);
+}
+
+nosa_status nosa_decode_partial(const nosa_shape *shape, const void *q, const void *kv,
+                                int64_t kv_row_blocks, int32_t kv_mode, const int32_t *list,
+                                const int32_t *n_list, int32_t list_stride, int32_t list_len,
+                                int32_t with_newest, const void *cur_kv, int64_t cur_row_blocks,
+                                const nosa_step *step, const float *e_tok, int64_t e_row_stride,
+                                void *ws, size_t ws_bytes, int32_t chunk0, void *stream) {
+    return decode_partial_impl(shape, q, kv, kv_row_blocks, kv_mode, list, n_list, list_stride,
+                               list_len, with_newest, cur_kv, cur_row_blocks, step, e_tok,
+                               e_row_stride, ws, ws_bytes, chunk0, nullptr, nullptr, stream);
+}
+
+nosa_status nosa_decode_partial_timed(const nosa_shape *shape, const void *q, const void *kv,
+                                      int64_t kv_row_blocks, int32_t kv_mode,
+                                      const int32_t *list, const int32_t *n_list,
+                                      int32_t list_stride, int32_t list_len, int32_t with_newest,
+                                      const void *cur_kv, int64_t cur_row_blocks,
+                                      const nosa_step *step, const float *e_tok,
+                                      int64_t e_row_stride, void *ws, size_t ws_bytes,
+                                      int32_t chunk0, void *start_event, void *stop_event,
+                                      void *stream) {
+    if (!start_event || !stop_event) return NOSA_ERR_INVALID_ARGUMENT;
+    return decode_partial_impl(shape, q, kv, kv_row_blocks, kv_mode, list, n_list, list_stride,
+                               list_len, with_newest, cur_kv, cur_row_blocks, step, e_tok,
+                               e_row_stride, ws, ws_bytes, chunk0, (hipEvent_t)start_event,
+                               (hipEvent_t)stop_event, stream);
 }
 
 // ---- steps replayed from a captured graph: the step record in device memory ----

@@ -113,10 +113,10 @@ struct DecodeArgs {
 
 template <typename T, int D, int G>
 hipError_t launch_decode_valu(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
-                              hipStream_t st);
+                              hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 template <int D, int G>
 hipError_t launch_decode_mfma(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
-                              hipStream_t st);
+                              hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 template <typename T, int D>
 hipError_t launch_pool_queries(const Dims &dm, const void *q, int n_tokens, void *qbar,
                                hipStream_t st);

@@ -26,6 +26,8 @@
 //  * VALU (float32 and bf16): K and V tiles staged in LDS, fp32 FMAs.
 #include "kernels.h"
 
+#include <hip/hip_ext.h>
+
 namespace nosa {
 
 
@@ -816,21 +818,29 @@ decode_valu_kernel(Dims dm, DecodeArgs a) {
     }
 }
 
+// With ev0 / ev1 (timing events), the launch goes through
+// hipExtLaunchKernelGGL, which records them at the kernel's own start and end.
 template <typename T, int D, int G>
 hipError_t launch_decode_valu(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
-                              hipStream_t st) {
+                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     if (pl.n_chunks == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, G>), dim3(pl.n_chunks, dm.rows), dim3(256), 0, st,
-                       dm, a);
+    const dim3 grid(pl.n_chunks, dm.rows), block(256);
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL((decode_valu_kernel<T, D, G>), grid, block, 0, st, ev0, ev1, 0, dm, a);
+    else
+        hipLaunchKernelGGL((decode_valu_kernel<T, D, G>), grid, block, 0, st, dm, a);
     return hipGetLastError();
 }
 
 template <int D, int G>
 hipError_t launch_decode_mfma(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
-                              hipStream_t st) {
+                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     if (pl.n_chunks == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_mfma_kernel<D, G>), dim3(pl.n_chunks, dm.rows),
-                       dim3(64 * WAVES), 0, st, dm, a);
+    const dim3 grid(pl.n_chunks, dm.rows), block(64 * WAVES);
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL((decode_mfma_kernel<D, G>), grid, block, 0, st, ev0, ev1, 0, dm, a);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<D, G>), grid, block, 0, st, dm, a);
     return hipGetLastError();
 }
 
@@ -844,7 +854,8 @@ hipError_t launch_combine(const Dims &dm, int n_chunks, int chunk_cap, const flo
 
 #define NOSA_DEC_INST(T, D, G)                                                                 \
     template hipError_t launch_decode_valu<T, D, G>(const Dims &, const DecodePlan &,          \
-                                                    const DecodeArgs &, hipStream_t);          \
+                                                    const DecodeArgs &, hipStream_t,           \
+                                                    hipEvent_t, hipEvent_t);                   \
     template hipError_t launch_combine<T, D, G>(const Dims &, int, int, const float *,         \
                                                 const float *, void *, hipStream_t);
 #define NOSA_DEC_ALLG(T, D)                                                                    \
@@ -857,7 +868,8 @@ NOSA_DEC_ALLG(bf16_t, 128)
 
 #define NOSA_MFMA_INST(D, G)                                                                   \
     template hipError_t launch_decode_mfma<D, G>(const Dims &, const DecodePlan &,             \
-                                                 const DecodeArgs &, hipStream_t);
+                                                 const DecodeArgs &, hipStream_t, hipEvent_t,  \
+                                                 hipEvent_t);
 #define NOSA_MFMA_ALLG(D)                                                                      \
     NOSA_MFMA_INST(D, 1) NOSA_MFMA_INST(D, 2) NOSA_MFMA_INST(D, 3) NOSA_MFMA_INST(D, 4)        \
     NOSA_MFMA_INST(D, 5) NOSA_MFMA_INST(D, 6) NOSA_MFMA_INST(D, 7) NOSA_MFMA_INST(D, 8)
