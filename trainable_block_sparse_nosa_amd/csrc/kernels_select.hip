@@ -178,7 +178,8 @@ score_kernel(Dims dm, const T *__restrict__ q, const T *__restrict__ kbar, int n
 //    lowest-ranked member if it ranks above it, else it is evicted.
 //  * the ascending selection list comes from a popcount prefix scan.
 //  * optionally the set difference against the block cache runs in the same
-//    workgroup (wave 0), from the selection bitmap and the slot table alone.
+//    workgroup (wave 1, beside wave 0's lists), from the selection bitmap and
+//    the slot table alone.
 // ---------------------------------------------------------------------------
 constexpr int SELECT_THREADS = 512;
 constexpr int SELECT_WAVES = SELECT_THREADS / 64;
@@ -708,11 +709,11 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
     uint32_t *ge_g = ge_bits ? ge_bits + (int64_t)r * W : nullptr;
     uint32_t *ev_g = ev_bits ? ev_bits + (int64_t)r * W : nullptr;
 
-    // independent loads first: the cache's slot table and counters, then this
-    // thread's scores
+    // independent loads first: the cache's slot table and counters (for wave
+    // 1, which runs the set difference), then this thread's scores
     int s0 = -1, s1 = -1;
     uint64_t cnt = 0ull;
-    if (sw.slot_block && wave == 0) {
+    if (sw.slot_block && wave == 1) {
         if (lane < dm.k) s0 = sw.slot_block[(int64_t)r * dm.k + lane];
         if (lane + 64 < dm.k) s1 = sw.slot_block[(int64_t)r * dm.k + lane + 64];
         if (lane < 2) cnt = sw.counters[2 * r + lane];
@@ -835,6 +836,12 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
             sel_bits[(int64_t)r * W + w] = sb[w];
         }
     }
+    // the set difference (wave 1) and the ascending lists (wave 0) both work
+    // from the selection bitmap in LDS alone, so they run side by side
+    if (wave == 1) {
+        if (sw.slot_block) swap_row(dm, r, sb, s0, s1, cnt, res, fb, fs, fo, sw);
+        return;
+    }
     if (wave != 0) return;
     // wave 0 writes the ascending lists: the union, and each part when asked
     // for. Lane l holds bitmap words 2l and 2l+1 (<= 128 words); a prefix sum
@@ -864,7 +871,6 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
         }
     }
     if (lane == 0) n_sel[r] = total;
-    if (sw.slot_block) swap_row(dm, r, sb, s0, s1, cnt, res, fb, fs, fo, sw);
 }
 
 // Stand-alone set difference: one wave per row, selection bitmap and slot
