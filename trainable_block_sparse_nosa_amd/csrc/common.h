@@ -139,15 +139,38 @@ __device__ __forceinline__ float quad_max(float v) {
     return v;
 }
 
+// One DPP move of v (lanes without a source, or in rows outside ROWS, get
+// `old`, or 0 with BOUND_ZERO).
+template <int CTRL, int ROWS, bool BOUND_ZERO>
+__device__ __forceinline__ float dpp_move(float old, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL,
+                                                      ROWS, 0xF, BOUND_ZERO));
+}
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114,
+              DPP_ROW_SHR8 = 0x118, DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+
+// Max / sum over the 64 lanes of a wave on DPP: a log-step scan inside each
+// row of 16 lanes (row_shr 1, 2, 4, 8), the row results carried across rows
+// by the GFX9 row broadcasts (lane 15 of rows 0 and 2 into rows 1 and 3,
+// then lane 31 into rows 2 and 3), so lane 63 ends with the whole wave's;
+// every lane gets that value. Every lane must be active.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, dpp_move<DPP_ROW_SHR1, 0xF, false>(v, v));
+    v = fmaxf(v, dpp_move<DPP_ROW_SHR2, 0xF, false>(v, v));
+    v = fmaxf(v, dpp_move<DPP_ROW_SHR4, 0xF, false>(v, v));
+    v = fmaxf(v, dpp_move<DPP_ROW_SHR8, 0xF, false>(v, v));
+    v = fmaxf(v, dpp_move<DPP_ROW_BCAST15, 0xA, false>(v, v));
+    v = fmaxf(v, dpp_move<DPP_ROW_BCAST31, 0xC, false>(v, v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_move<DPP_ROW_SHR1, 0xF, true>(0.f, v);
+    v += dpp_move<DPP_ROW_SHR2, 0xF, true>(0.f, v);
+    v += dpp_move<DPP_ROW_SHR4, 0xF, true>(0.f, v);
+    v += dpp_move<DPP_ROW_SHR8, 0xF, true>(0.f, v);
+    v += dpp_move<DPP_ROW_BCAST15, 0xA, false>(0.f, v);
+    v += dpp_move<DPP_ROW_BCAST31, 0xC, false>(0.f, v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {

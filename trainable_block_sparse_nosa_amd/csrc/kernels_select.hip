@@ -433,7 +433,7 @@ __device__ void swap_row(const Dims &dm, int r, const uint32_t *bits, int s0, in
         while (m && pos < MAX_K) { fb[pos++] = w1 * 32 + __ffs(m) - 1; m &= m - 1u; }
         nf += __builtin_amdgcn_readlane(inc, 63);
     }
-    for (int o = 32; o > 0; o >>= 1) kept += __shfl_xor(kept, o, 64);
+    kept = __builtin_amdgcn_readlane(wave_incl_sum(kept), 63);
     nf = min(nf, k);
     // free slots, ascending
     int nfree = 0;
@@ -805,10 +805,8 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
     // every wave counts Gamma_e itself (no barrier); the copies into sb are
     // ordered before the top-k's updates by the top-k's first barrier
     for (int w = tid; w < W; w += nt) sb[w] = ge[w];
-    int ne_loc = (lane < W ? __popc(ge[lane]) : 0) + (lane + 64 < W ? __popc(ge[lane + 64]) : 0);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ne_loc += __shfl_xor(ne_loc, o, 64);
-    const int n_e = __builtin_amdgcn_readfirstlane(ne_loc);
+    const int ne_loc = (lane < W ? __popc(ge[lane]) : 0) + (lane + 64 < W ? __popc(ge[lane + 64]) : 0);
+    const int n_e = __builtin_amdgcn_readlane(wave_incl_sum(ne_loc), 63);
     const int kq = min(dm.k_q, n_cand - n_e);
     if (kq > 0 && dm.k_q <= WAVE_TOPK) {
         topk_dispatch(n_cand, kq, [&](int j, int i) -> uint64_t {
