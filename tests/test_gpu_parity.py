@@ -254,6 +254,10 @@ EDGE = {
     "wave_tail_evict": dict(context=4161, steps=3, k_e=40, k_q=16, n_q_heads=16,
                             n_kv_heads=8),
     "wave_tail_query": dict(context=4161, steps=130, k_e=8, k_q=40),
+    # near the capacity: 4093 blocks per row, 4091 then (a block completes at
+    # step 2) 4092 candidates, 128 bitmap words in use, the largest budget
+    # 96 + 32
+    "max_capacity": dict(context=4092 * 64 - 2, steps=4, k_e=96, k_q=32),
 }
 
 
