@@ -461,11 +461,23 @@ __device__ __forceinline__ void prefill_store(PrefillTile<D> &tl, const PrefillS
 // scores arrive already multiplied by log2(e). CAUSAL masks, per column, the
 // tokens from lim[c] on (the own block); the other blocks are whole. P
 // enters P V as bf16 (the outputs are bf16), its row sums stay in float32.
+// Max of v over the four rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48) on
+// the gfx950 row-swap instructions: with both operands holding v, each lane
+// of the swapped pair holds v at its own lane and at the lane 16 (32) away.
+__device__ __forceinline__ float max_over_rows(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __float_as_uint(v);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int D, int CT, bool CAUSAL>
 __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
                                               const bf16x8 (&qop)[CT][D / 32], float scale2,
                                               int lane, const int (&lim)[CT], float (&m_run)[CT],
-                                              float (&l_run)[CT], f32x4 (&o)[CT][D / 16]) {
+                                              f32x4 (&l_run)[CT], f32x4 (&o)[CT][D / 16]) {
     constexpr int KS = D / 32, DT = D / 16;
     const int grp = lane >> 4;
     f32x4 sc[CT][4];
@@ -500,33 +512,37 @@ __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
                 if (CAUSAL && 16 * t + 4 * grp + u >= lim[c]) z[t][u] = -INFINITY;
                 mx = fmaxf(mx, z[t][u]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = max_over_rows(mx);
         const float m_new = fmaxf(m_run[c], mx);
         // a column with no token yet subtracts 0: exp2(-inf - 0) = 0, no NaN
         const float m_sub = m_new == -INFINITY ? 0.f : m_new;
         alpha[c] = __builtin_amdgcn_exp2f(m_run[c] - m_sub);
         rescale |= alpha[c] != 1.f;
-        float ps = 0.f;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float p = __builtin_amdgcn_exp2f(z[t][u] - m_sub);
-                pb[c][t / 2][(t % 2) * 4 + u] = (__bf16)p;
-                ps += p;
-            }
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
-        l_run[c] = l_run[c] * alpha[c] + ps;
+            for (int u = 0; u < 4; ++u)
+                pb[c][t / 2][(t % 2) * 4 + u] = (__bf16)__builtin_amdgcn_exp2f(z[t][u] - m_sub);
         m_run[c] = m_new;
     }
     // most blocks move no column's maximum: skip the rescale then
     if (__any(rescale)) {
 #pragma unroll
-        for (int c = 0; c < CT; ++c)
+        for (int c = 0; c < CT; ++c) {
+            l_run[c] *= alpha[c];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) o[c][dt] *= alpha[c];
+        }
+    }
+    // the denominator on the matrix cores: an all-ones A operand sums the
+    // column of P^T (the same bf16 probabilities P.V uses) into every row of
+    // l_run[c], rescaled with O above
+    const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        l_run[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[c][0], l_run[c], 0, 0, 0);
+        l_run[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[c][1], l_run[c], 0, 0, 0);
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -583,12 +599,13 @@ prefill_mfma_kernel(Dims dm, PrefillArgs a) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) qop[c][s] = *reinterpret_cast<const bf16x8 *>(qh + 32 * s);
     }
-    float m_run[CT], l_run[CT];
+    float m_run[CT];
+    f32x4 l_run[CT];  // the softmax denominator of column c, in all four entries
     f32x4 o[CT][DT];
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
         m_run[c] = -INFINITY;
-        l_run[c] = 0.f;
+        l_run[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -635,7 +652,7 @@ prefill_mfma_kernel(Dims dm, PrefillArgs a) {
             const int qr = row0 + 16 * c + col;
             const int u = qr / G, h = qr % G, p = S * i + u;
             if (qr < S * G && p < a.n_tokens) {
-                const float inv = 1.0f / l_run[c];
+                const float inv = 1.0f / l_run[c][0];
                 bf16_t *out = static_cast<bf16_t *>(a.out) +
                               (((int64_t)b * a.n_tokens + p) * dm.Hq + (int64_t)g * G + h) * D;
 #pragma unroll
