@@ -6,6 +6,8 @@
 // cache, set difference for block swapping, host-to-device copy kernels).
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace nosa {
 
 // ---------------------------------------------------------------------------
@@ -885,31 +887,43 @@ swap_kernel(Dims dm, const uint32_t *__restrict__ sel_bits, SwapArgs sw) {
 }
 
 // ---------------------------------------------------------------------------
-// Fetch: one workgroup per (list entry, row); entries past n_fetch exit.
-// Each thread keeps eight 16-byte loads in flight before storing them.
+// Fetch: a bounded grid of workgroups walks the work items (list entry i, row
+// r) = item, item + gridDim.x, ... in entry-major order, so the valid ones
+// (i < n_fetch[r]) come first and spread over every workgroup; a workgroup
+// copies one block at a time, each thread keeping eight 16-byte loads in
+// flight before storing them. FETCH_WGS workgroups keep far more reads in
+// flight than the PCIe link needs (128 x 32 KiB), while a grid of one
+// workgroup per item filled every CU with copies waiting on PCIe, so that
+// attention workgroups launched beside the copy (another half of the batch)
+// found no room until it drained.
 // ---------------------------------------------------------------------------
+constexpr int FETCH_WGS = 128;
 __global__ void __launch_bounds__(256)
 fetch_kernel(const u32x4 *__restrict__ src, int64_t src_row_blocks, const int32_t *__restrict__ fblk,
              const int32_t *__restrict__ fslot, const int32_t *__restrict__ nfetch, int k,
-             u32x4 *__restrict__ dst, int64_t dst_row_blocks, int vec_per_block) {
-    const int r = blockIdx.y, i = blockIdx.x;
-    if (i >= nfetch[r]) return;
-    const int b = fblk[(int64_t)r * k + i];
-    const int s = fslot[(int64_t)r * k + i];
-    if (b < 0 || b >= src_row_blocks || s < 0 || s >= dst_row_blocks) return;  // not a block
-    const u32x4 *sp = src + ((int64_t)r * src_row_blocks + b) * vec_per_block;
-    u32x4 *dp = dst + ((int64_t)r * dst_row_blocks + s) * vec_per_block;
-    for (int base = 0; base < vec_per_block; base += 8 * 256) {
-        u32x4 v[8];
+             int max_fetch, int rows, u32x4 *__restrict__ dst, int64_t dst_row_blocks,
+             int vec_per_block) {
+    const int total = max_fetch * rows;
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        const int i = item / rows, r = item % rows;
+        if (i >= nfetch[r]) continue;
+        const int b = fblk[(int64_t)r * k + i];
+        const int s = fslot[(int64_t)r * k + i];
+        if (b < 0 || b >= src_row_blocks || s < 0 || s >= dst_row_blocks) continue;  // not a block
+        const u32x4 *sp = src + ((int64_t)r * src_row_blocks + b) * vec_per_block;
+        u32x4 *dp = dst + ((int64_t)r * dst_row_blocks + s) * vec_per_block;
+        for (int base = 0; base < vec_per_block; base += 8 * 256) {
+            u32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int idx = base + u * 256 + threadIdx.x;
-            if (idx < vec_per_block) v[u] = __builtin_nontemporal_load(sp + idx);
-        }
+            for (int u = 0; u < 8; ++u) {
+                const int idx = base + u * 256 + threadIdx.x;
+                if (idx < vec_per_block) v[u] = __builtin_nontemporal_load(sp + idx);
+            }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int idx = base + u * 256 + threadIdx.x;
-            if (idx < vec_per_block) dp[idx] = v[u];
+            for (int u = 0; u < 8; ++u) {
+                const int idx = base + u * 256 + threadIdx.x;
+                if (idx < vec_per_block) dp[idx] = v[u];
+            }
         }
     }
 }
@@ -1236,10 +1250,12 @@ hipError_t launch_fetch(const Dims &dm, const void *src, int64_t src_row_blocks,
                         int max_fetch, void *dst, int64_t dst_row_blocks, hipStream_t st) {
     const int elem = dm.dtype == NOSA_BF16 ? 2 : 4;
     const int vec = 2 * dm.S * dm.D * elem / 16;
-    dim3 grid(max_fetch, dm.rows);
-    hipLaunchKernelGGL(fetch_kernel, grid, dim3(256), 0, st, static_cast<const u32x4 *>(src),
-                       src_row_blocks, fblk, fslot, nfetch, dm.k, static_cast<u32x4 *>(dst),
-                       dst_row_blocks, vec);
+    const int64_t items = (int64_t)max_fetch * dm.rows;
+    if (items <= 0) return hipSuccess;
+    const int wgs = (int)std::min<int64_t>(items, FETCH_WGS);
+    hipLaunchKernelGGL(fetch_kernel, dim3(wgs), dim3(256), 0, st, static_cast<const u32x4 *>(src),
+                       src_row_blocks, fblk, fslot, nfetch, dm.k, max_fetch, dm.rows,
+                       static_cast<u32x4 *>(dst), dst_row_blocks, vec);
     return hipGetLastError();
 }
 
