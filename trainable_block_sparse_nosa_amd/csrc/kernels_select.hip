@@ -190,6 +190,7 @@ constexpr int MAX_K = 128;
 constexpr int WAVE_TOPK = 64;
 constexpr int KEYS_PER_THREAD = 4096 / SELECT_THREADS;
 static_assert(MAX_W <= SELECT_THREADS, "one bitmap word per thread");
+static_assert(SELECT_WAVES >= 2, "the set difference runs on wave 1 beside wave 0's lists");
 
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
