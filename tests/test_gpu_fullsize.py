@@ -14,11 +14,19 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-def _fullsize(name, rows, steps, w=None):
+def _fullsize(name, rows, steps, w=None, all_rows_at=()):
+    """Sampled rows at every step (selections, swap lists, slot tables,
+    outputs); with all_rows_at, every row at those steps too (selections and
+    outputs: the oracle's selection and attention need no history)."""
     gh = _gpu()
     w = w or synth.WORKLOADS[name]
     print(f"[fullsize] {name}: oracle on rows {rows}, steps 0..{steps - 1}", flush=True)
     tr = oracle_trace(w, rows=rows, steps=list(range(steps)))
+    tr_all = None
+    if all_rows_at:
+        print(f"[fullsize] {name}: oracle on all {w.rows} rows at steps {list(all_rows_at)}",
+              flush=True)
+        tr_all = oracle_trace(w, steps=list(all_rows_at), ov=tr.ov, swaps=False)
     print(f"[fullsize] {name}: uploading inputs", flush=True)
     inp = gh.upload(w, ov=tr.ov, steps=steps)
     print(f"[fullsize] {name}: running the GPU path", flush=True)
@@ -26,6 +34,9 @@ def _fullsize(name, rows, steps, w=None):
     for t in range(steps):
         for r in rows:
             _compare_step(w, tr, t, r, res[t])
+    for t in all_rows_at:
+        for r in range(w.rows):
+            _compare_step(w, tr_all, t, r, res[t], check_swap=False)
     # every row's selection is a valid one: sizes, ascending, candidates only
     last = res[steps - 1]
     c = w.n_cand(steps - 1)
@@ -41,15 +52,15 @@ def _fullsize(name, rows, steps, w=None):
 
 
 def test_fullsize_bf16_1layer_32k():
-    _fullsize("bf16_1layer_32k", rows=[0, 21, 63], steps=128)
+    _fullsize("bf16_1layer_32k", rows=[0, 21, 63], steps=128, all_rows_at=(0, 63, 64, 127))
 
 
 def test_fullsize_bf16_3b_64k():
-    _fullsize("bf16_3b_64k", rows=[0, 131, 255], steps=256)
+    _fullsize("bf16_3b_64k", rows=[0, 131, 255], steps=256, all_rows_at=(0, 255))
 
 
 def test_fullsize_offload_1layer_128k():
-    _fullsize("offload_1layer_128k", rows=[0, 77, 127], steps=256)
+    _fullsize("offload_1layer_128k", rows=[0, 77, 127], steps=256, all_rows_at=(0, 200))
 
 
 @pytest.mark.parametrize("k_e", [32, 0])
