@@ -106,7 +106,7 @@ def test_fullsize_offload_128k_device_append():
 def test_fullsize_offload_8b_32layer_32k():
     """32 layers x batch 64 x 8 KV heads, all five stages per layer per step,
     steps 0..65 (a block completes at step 64); sampled layers and rows are
-    checked at every step."""
+    checked at every step, and every row of layer 17 at step 64."""
     gh = _gpu()
     w = synth.WORKLOADS["offload_8b_32layer_32k"]
     steps = 66
@@ -115,6 +115,10 @@ def test_fullsize_offload_8b_32layer_32k():
     for l, rows in layers_checked.items():
         print(f"[fullsize] 8b: oracle layer {l} rows {rows}", flush=True)
         traces[l] = oracle_trace(w, layer=l, rows=rows, steps=list(range(steps)))
+    # every row of one layer at the step that completes a block
+    all_l, all_t = 17, 64
+    print(f"[fullsize] 8b: oracle layer {all_l}, all {w.rows} rows, step {all_t}", flush=True)
+    tr_all = oracle_trace(w, layer=all_l, steps=[all_t], ov=traces[all_l].ov, swaps=False)
     print("[fullsize] 8b: pinned host KV slabs", flush=True)
     slabs = gh.upload_slabs(w)
     layers, inputs = [], []
@@ -133,6 +137,9 @@ def test_fullsize_offload_8b_32layer_32k():
                 got = gh.snapshot(layer, w)
                 for r in layers_checked[l]:
                     _compare_step(w, traces[l], t, r, got)
+                if l == all_l and t == all_t:
+                    for r in range(w.rows):
+                        _compare_step(w, tr_all, t, r, got, check_swap=False)
         if t % 16 == 0:
             print(f"[fullsize] 8b: step {t} done", flush=True)
     for buf, _ in slabs:
