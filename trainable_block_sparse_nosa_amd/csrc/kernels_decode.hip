@@ -513,11 +513,17 @@ __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
                 mx = fmaxf(mx, z[t][u]);
             }
         mx = max_over_rows(mx);
-        const float m_new = fmaxf(m_run[c], mx);
+        // lazy base: the running base moves only when the block's maximum
+        // exceeds it by more than 8 (log2 units), so probabilities stay below
+        // 2^8 (exact in the fp32 sums, the same relative precision in bf16)
+        // and the accumulators are rescaled only on those rare moves; the
+        // softmax itself does not depend on the base
+        const bool move = mx > m_run[c] + 8.f;  // also the first finite maximum
+        const float m_new = move ? mx : m_run[c];
         // a column with no token yet subtracts 0: exp2(-inf - 0) = 0, no NaN
         const float m_sub = m_new == -INFINITY ? 0.f : m_new;
         alpha[c] = __builtin_amdgcn_exp2f(m_run[c] - m_sub);
-        rescale |= alpha[c] != 1.f;
+        rescale |= move;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
