@@ -184,7 +184,8 @@ nosa_status nosa_ingest_tokens(const nosa_shape *shape, const void *qkv, const v
 
 /* Pooled query of every query block: qbar [n_qb][batch][Hq][D] (KV dtype,
  * n_qb = ceil(n_tokens / S)) is the mean over the block's tokens of q
- * [batch][n_tokens][Hq][D], rounded once to the KV dtype. */
+ * [batch][n_tokens][Hq][D], rounded once to the KV dtype. q and qbar must be
+ * 16-byte aligned (NOSA_ERR_INVALID_ARGUMENT otherwise). */
 nosa_status nosa_prefill_pool_queries(const nosa_shape *shape, const void *q, int32_t n_tokens,
                                       void *qbar, void *stream);
 

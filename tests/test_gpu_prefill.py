@@ -210,3 +210,30 @@ def test_prefill_fullsize_sampled():
             assert sel[i, r, :len(want)].tolist() == want, f"row {r} query block {i}"
             got = out[b, 64 * i:64 * i + 64, g * G:(g + 1) * G].float().cpu().numpy()
             np.testing.assert_allclose(got, ref.out, err_msg=f"row {r} query block {i}", **TOL)
+
+
+@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_g3_d64"])
+def test_pooled_queries_bit_exact(name):
+    """nosa_prefill_pool_queries against the oracle's pooled query of every
+    (query block, sequence, head), the last block ragged: bit for bit (the
+    mean of bf16 values is exact in double and rounded once)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gpu_harness as gh
+    from trainable_block_sparse_nosa_amd import _lib as L
+    w = PREFILL[name]
+    N = w.context
+    nqb = -(-N // 64)
+    qh = synth.prefill_queries(w, 0, N)                     # [batch][N][Hq][D]
+    q_all = gh.to_device(gh.storage(qh, w), w)
+    qbar = torch.empty(nqb, w.batch, w.n_q_heads, w.head_dim, dtype=torch.bfloat16,
+                       device="cuda")
+    shape = L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.k_e, w.k_q,
+                         -(-w.n_max // 64), L.NOSA_BF16)
+    L.nosa_prefill_pool_queries(shape, q_all, N, qbar, None)
+    torch.cuda.synchronize()
+    got = qbar.float().cpu().numpy()
+    for i in range(nqb):
+        for b in range(w.batch):
+            ref = oracle.pool_queries(qh[b, 64 * i:64 * i + 64], pooled_bf16=True)
+            np.testing.assert_array_equal(got[i, b], ref, err_msg=f"{name} block {i} b {b}")

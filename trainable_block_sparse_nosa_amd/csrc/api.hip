@@ -352,6 +352,9 @@ nosa_status nosa_prefill_pool_queries(const nosa_shape *shape, const void *q, in
     nosa_status s = make_dims(shape, &dm);
     if (s != NOSA_OK) return s;
     if (!q || !qbar || n_tokens <= 0) return NOSA_ERR_INVALID_ARGUMENT;
+    // the kernel reads and writes 16-byte vectors
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(qbar)) & 15)
+        return NOSA_ERR_INVALID_ARGUMENT;
     return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
         using T = std::remove_pointer_t<decltype(tp)>;
         constexpr int D = decltype(dc)::value;

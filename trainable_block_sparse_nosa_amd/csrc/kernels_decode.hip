@@ -336,17 +336,46 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
 // query block's tokens, in the input dtype (exact mean rounded once).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(256)
 pool_queries_kernel(Dims dm, const T *__restrict__ q, int n_tokens, T *__restrict__ qbar) {
-    const int i = blockIdx.x, bh = blockIdx.y, d = threadIdx.x;
-    const int b = bh / dm.Hq, hq = bh % dm.Hq;
+    // one workgroup per (query block i, sequence b); thread t owns the
+    // 16-byte vectors t, t + 256, ... of a token's Hq * D elements and sums
+    // each element over the block's tokens in order, in double (exact for
+    // bf16 inputs), eight tokens' loads in flight; the mean is rounded once
+    constexpr int EV = 16 / sizeof(T);
+    const int i = blockIdx.x, b = blockIdx.y;
     const int lo = 64 * i, n = min(64, n_tokens - lo);
-    double s = 0.0;
-    for (int u = 0; u < n; ++u) s += (double)ldf(q + (((int64_t)b * n_tokens + lo + u) * dm.Hq + hq) * D + d);
-    const double mean = s / (double)n;
-    T *out = qbar + (((int64_t)i * dm.B + b) * dm.Hq + hq) * D + d;
-    if constexpr (std::is_same_v<T, float>) *out = (float)mean;
-    else *out = bf16_rne_from_double(mean);
+    const int64_t tok = (int64_t)dm.Hq * D;  // elements per token
+    const int nv = (int)(tok / EV);
+    const T *qb = q + ((int64_t)b * n_tokens + lo) * tok;
+    T *ob = qbar + ((int64_t)i * dm.B + b) * tok;
+    for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+        double s[EV];
+#pragma unroll
+        for (int e = 0; e < EV; ++e) s[e] = 0.0;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(qb) + v;
+        const int64_t stride = tok / EV;  // vectors per token
+#pragma unroll 8
+        for (int u = 0; u < n; ++u) {
+            const u32x4 raw = src[(int64_t)u * stride];
+            float x[EV];
+            if constexpr (std::is_same_v<T, float>) {
+                x[0] = __uint_as_float(raw.x); x[1] = __uint_as_float(raw.y);
+                x[2] = __uint_as_float(raw.z); x[3] = __uint_as_float(raw.w);
+            } else {
+                x[0] = bf_lo(raw.x); x[1] = bf_hi(raw.x); x[2] = bf_lo(raw.y); x[3] = bf_hi(raw.y);
+                x[4] = bf_lo(raw.z); x[5] = bf_hi(raw.z); x[6] = bf_lo(raw.w); x[7] = bf_hi(raw.w);
+            }
+#pragma unroll
+            for (int e = 0; e < EV; ++e) s[e] += (double)x[e];
+        }
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+            const double mean = s[e] / (double)n;
+            if constexpr (std::is_same_v<T, float>) ob[(int64_t)v * EV + e] = (float)mean;
+            else ob[(int64_t)v * EV + e] = bf16_rne_from_double(mean);
+        }
+    }
 }
 
 // Block-sparse causal attention (bf16, MFMA). A workgroup takes ROWS query
@@ -675,7 +704,8 @@ template <typename T, int D>
 hipError_t launch_pool_queries(const Dims &dm, const void *q, int n_tokens, void *qbar,
                                hipStream_t st) {
     const int nqb = (n_tokens + 63) / 64;
-    hipLaunchKernelGGL((pool_queries_kernel<T, D>), dim3(nqb, dm.B * dm.Hq), dim3(D), 0, st, dm,
+    if (nqb == 0) return hipSuccess;
+    hipLaunchKernelGGL((pool_queries_kernel<T, D>), dim3(nqb, dm.B), dim3(256), 0, st, dm,
                        static_cast<const T *>(q), n_tokens, static_cast<T *>(qbar));
     return hipGetLastError();
 }
