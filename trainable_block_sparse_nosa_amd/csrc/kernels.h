@@ -17,6 +17,9 @@ hipError_t launch_pool_step(const Dims &dm, const void *kv, int64_t kv_row_block
                             void *kbar, float *e_blk, hipStream_t st);
 hipError_t launch_step_advance(const Dims &dm, int32_t *dstep, hipStream_t st);
 
+// Block scores of candidates 0..n_cand-1 into s_q: bf16 on the matrix cores
+// over a grid split along each row's candidates (dstep: n_cand from the
+// device step record, the grid sized for the capacity); float32 on the VALU.
 template <typename T, int D, int G>
 hipError_t launch_score(const Dims &dm, const void *q, const void *kbar, int n_cand, float *s_q,
                         hipStream_t st, const int32_t *dstep = nullptr);
@@ -37,9 +40,12 @@ hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, i
                          uint32_t *sel_bits, const SwapPtrs *swap, const SelectLists *parts,
                          hipStream_t st);
 
-// Scores computed by the selecting workgroup (one per row), written to s_q
-// as well, then the selection (and the set difference when swap != nullptr).
-// dstep != nullptr: n_cand and n_prev come from the device step record.
+// Scores and selection (and the set difference when swap != nullptr): with
+// bf16 and at most SPLIT_SCORE_MAX_ROWS rows, the scores come from a grid
+// split over each row's candidates into s_q and a second launch selects from
+// them; otherwise the selecting workgroup (one per row) computes its row's
+// scores itself, writing them to s_q as well. dstep != nullptr: n_cand and
+// n_prev come from the device step record.
 template <typename T, int D, int G>
 hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, float *s_q,
                                const float *e_blk, int n_cand, int n_prev, uint32_t *ge,
