@@ -384,6 +384,15 @@ nosa_status nosa_decode_partial_timed(const nosa_shape *shape, const void *q, co
 nosa_status nosa_decode_combine(const nosa_shape *shape, int32_t n_chunks, void *out, void *ws,
                                 size_t ws_bytes, void *stream);
 
+/* nosa_decode_combine that then moves the device step record step_dev on, as
+ * nosa_step_advance does: the last call of a step replayed from a captured
+ * graph, one kernel fewer per replay. Its merge reads no step record, and
+ * every kernel of the step that does is enqueued before it on the stream.
+ * step_dev must be non-NULL (NOSA_ERR_INVALID_ARGUMENT otherwise). */
+nosa_status nosa_decode_combine_step(const nosa_shape *shape, int32_t n_chunks, void *out,
+                                     void *ws, size_t ws_bytes, nosa_step *step_dev,
+                                     void *stream);
+
 /* ---- steps replayed from a captured graph ----
  * The step record lives in device memory (step_dev: a nosa_step, 8 bytes,
  * 4-byte aligned) and every call of a step reads it in its kernels, so one

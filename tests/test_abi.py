@@ -98,6 +98,8 @@ def test_invalid_pointers_and_steps_rejected():
     assert lib.nosa_append_tokens(ctypes.byref(sh), 16, 16, 3, 16, 4, 4, None) == 1
     assert lib.nosa_append_tokens(ctypes.byref(sh), 16, 16, -1, 16, 4, 0, None) == 1
     assert lib.nosa_append_tokens(ctypes.byref(sh), 16, 16, 3, None, 4, 0, None) == 1
+    # merge that advances the device step record, without the record
+    assert lib.nosa_decode_combine_step(ctypes.byref(sh), 1, 16, 16, 1 << 30, None, None) == 1
     # timed partial decode without its two events
     args = [ctypes.byref(sh), 16, 16, 64, L.NOSA_KV_FULL, 16, 16, 64, 64, 1, 16, 64,
             ctypes.byref(ok_step), 16, 64 * 64, 16, 1 << 30, 0]

@@ -34,7 +34,7 @@ EXPORTS = (
     "nosa_ingest_tokens", "nosa_prefill_pool_queries", "nosa_prefill_select",
     "nosa_prefill_attention", "nosa_decode_workspace_size", "nosa_decode_chunks",
     "nosa_sparse_decode", "nosa_decode_partial", "nosa_decode_partial_timed",
-    "nosa_decode_combine",
+    "nosa_decode_combine", "nosa_decode_combine_step",
     "nosa_step_advance", "nosa_pool_step", "nosa_append_step", "nosa_score_select_step",
     "nosa_decode_partial_step",
     "nosa_host_alloc", "nosa_host_free", "nosa_read_probe", "nosa_status_string",
@@ -87,6 +87,7 @@ def _load() -> ctypes.CDLL:
         "nosa_decode_partial_timed": [SH, P, P, I64, I32, P, P, I32, I32, I32, P, I64, ST, P, I64,
                                       P, SZ, I32, P, P, P],
         "nosa_decode_combine": [SH, I32, P, P, SZ, P],
+        "nosa_decode_combine_step": [SH, I32, P, P, SZ, P, P],
         "nosa_host_alloc": [SZ, I32, ctypes.POINTER(P), ctypes.POINTER(P)],
         "nosa_host_free": [P],
         "nosa_read_probe": [P, I64, P, I32, P],
@@ -229,6 +230,11 @@ def nosa_decode_partial_timed(shape, q, kv, kv_row_blocks, kv_mode, list_, n_lis
 def nosa_decode_combine(shape, n_chunks, out, ws, ws_bytes, stream=None):
     _chk("nosa_decode_combine", _L.nosa_decode_combine(
         ctypes.byref(shape), n_chunks, _p(out), _p(ws), ws_bytes, _s(stream)))
+
+
+def nosa_decode_combine_step(shape, n_chunks, out, ws, ws_bytes, step_dev, stream=None):
+    _chk("nosa_decode_combine_step", _L.nosa_decode_combine_step(
+        ctypes.byref(shape), n_chunks, _p(out), _p(ws), ws_bytes, _p(step_dev), _s(stream)))
 
 
 def nosa_swap_diff(shape, sel, n_sel, sel_bits, slot_block, block_slot, fetch_block, fetch_slot,

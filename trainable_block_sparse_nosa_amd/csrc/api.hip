@@ -147,14 +147,15 @@ nosa_status launch_partial(const Dims &dm, int kind, const DecodePlan &pl, const
 }
 
 nosa_status launch_merge(const Dims &dm, int n_chunks, const DecodeArgs &a, void *out,
-                         hipStream_t st) {
+                         hipStream_t st, int32_t *dstep_adv = nullptr) {
     return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
         using T = std::remove_pointer_t<decltype(tp)>;
         constexpr int D = decltype(dc)::value;
         return by_group(dm, [&](auto gc) -> nosa_status {
             constexpr int G = decltype(gc)::value;
             return hip_status(
-                launch_combine<T, D, G>(dm, n_chunks, a.chunk_cap, a.ws_o, a.ws_ml, out, st));
+                launch_combine<T, D, G>(dm, n_chunks, a.chunk_cap, a.ws_o, a.ws_ml, out, st,
+                                        dstep_adv));
         });
     });
 }
@@ -645,8 +646,9 @@ nosa_status nosa_decode_partial_step(const nosa_shape *shape, const void *q, con
     return launch_partial(dm, kind, pl, a, (hipStream_t)stream);
 }
 
-nosa_status nosa_decode_combine(const nosa_shape *shape, int32_t n_chunks, void *out, void *ws,
-                                size_t ws_bytes, void *stream) {
+static nosa_status decode_combine_impl(const nosa_shape *shape, int32_t n_chunks, void *out,
+                                       void *ws, size_t ws_bytes, int32_t *dstep_adv,
+                                       void *stream) {
     Dims dm;
     nosa_status s = make_dims(shape, &dm);
     if (s != NOSA_OK) return s;
@@ -657,7 +659,20 @@ nosa_status nosa_decode_combine(const nosa_shape *shape, int32_t n_chunks, void 
     a.chunk_cap = decode_chunk_cap(dm);
     a.ws_o = static_cast<float *>(ws);
     a.ws_ml = a.ws_o + (size_t)dm.rows * a.chunk_cap * dm.G * dm.D;
-    return launch_merge(dm, n_chunks, a, out, (hipStream_t)stream);
+    return launch_merge(dm, n_chunks, a, out, (hipStream_t)stream, dstep_adv);
+}
+
+nosa_status nosa_decode_combine(const nosa_shape *shape, int32_t n_chunks, void *out, void *ws,
+                                size_t ws_bytes, void *stream) {
+    return decode_combine_impl(shape, n_chunks, out, ws, ws_bytes, nullptr, stream);
+}
+
+nosa_status nosa_decode_combine_step(const nosa_shape *shape, int32_t n_chunks, void *out,
+                                     void *ws, size_t ws_bytes, nosa_step *step_dev,
+                                     void *stream) {
+    if (!step_dev) return NOSA_ERR_INVALID_ARGUMENT;
+    return decode_combine_impl(shape, n_chunks, out, ws, ws_bytes,
+                               reinterpret_cast<int32_t *>(step_dev), stream);
 }
 
 nosa_status nosa_host_alloc(size_t bytes, int32_t coherent, void **host, void **dev) {

@@ -131,8 +131,10 @@ hipError_t launch_prefill(const Dims &dm, const void *q, int n_tokens, const voi
                           int64_t kv_row_blocks, const float *e_tok, int64_t e_stride,
                           const int32_t *sel, const int32_t *n_sel, void *out, hipStream_t st);
 template <typename T, int D, int G>
+// dstep_adv != nullptr: the device step record is advanced at the end.
 hipError_t launch_combine(const Dims &dm, int n_chunks, int chunk_cap, const float *ws_o,
-                          const float *ws_ml, void *out, hipStream_t st);
+                          const float *ws_ml, void *out, hipStream_t st,
+                          int32_t *dstep_adv = nullptr);
 
 // Streaming read of `bytes` (a multiple of 16) from src by `wgs` workgroups.
 hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, int wgs,

@@ -81,7 +81,7 @@ int decode_kind(const Dims &dm, int requested) {
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(D)
 combine_kernel(Dims dm, int n_chunks, int chunk_cap, const float *__restrict__ ws_o,
-               const float *__restrict__ ws_ml, T *__restrict__ out) {
+               const float *__restrict__ ws_ml, T *__restrict__ out, int32_t *dstep_adv) {
     constexpr int CREG = 33;  // chunks held in registers (every MFMA plan fits)
     const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x, lane = threadIdx.x & 63;
     const float *ml = ws_ml + ((int64_t)r * chunk_cap * G + h) * 2;  // chunk c at ml[c*G*2]
@@ -115,6 +115,13 @@ combine_kernel(Dims dm, int n_chunks, int chunk_cap, const float *__restrict__ w
     }
     const int b = r / dm.Hkv, g = r % dm.Hkv;
     out[((int64_t)b * dm.Hq + (int64_t)g * G + h) * D + d] = stf<T>(O / L);
+    // the step's last kernel moves the device step record on: no workgroup of
+    // this kernel reads it, and every kernel that does ran before it
+    if (dstep_adv && r == 0 && h == 0 && d == 0) {
+        const StepVals sv = read_step(dstep_adv, dm);
+        dstep_adv[1] = sv.n_cand;
+        dstep_adv[0] = sv.n_tokens + 1;
+    }
 }
 
 // Resolve entry e of row r: data pointer, block id and valid tokens.
@@ -899,9 +906,9 @@ hipError_t launch_decode_mfma(const Dims &dm, const DecodePlan &pl, const Decode
 
 template <typename T, int D, int G>
 hipError_t launch_combine(const Dims &dm, int n_chunks, int chunk_cap, const float *ws_o,
-                          const float *ws_ml, void *out, hipStream_t st) {
+                          const float *ws_ml, void *out, hipStream_t st, int32_t *dstep_adv) {
     hipLaunchKernelGGL((combine_kernel<T, D, G>), dim3(dm.rows, G), dim3(D), 0, st, dm, n_chunks,
-                       chunk_cap, ws_o, ws_ml, static_cast<T *>(out));
+                       chunk_cap, ws_o, ws_ml, static_cast<T *>(out), dstep_adv);
     return hipGetLastError();
 }
 
@@ -910,7 +917,7 @@ hipError_t launch_combine(const Dims &dm, int n_chunks, int chunk_cap, const flo
                                                     const DecodeArgs &, hipStream_t,           \
                                                     hipEvent_t, hipEvent_t);                   \
     template hipError_t launch_combine<T, D, G>(const Dims &, int, int, const float *,         \
-                                                const float *, void *, hipStream_t);
+                                                const float *, void *, hipStream_t, int32_t *);
 #define NOSA_DEC_ALLG(T, D)                                                                    \
     NOSA_DEC_INST(T, D, 1) NOSA_DEC_INST(T, D, 2) NOSA_DEC_INST(T, D, 3)                       \
     NOSA_DEC_INST(T, D, 4) NOSA_DEC_INST(T, D, 5) NOSA_DEC_INST(T, D, 6)                       \

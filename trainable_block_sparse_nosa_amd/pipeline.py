@@ -431,8 +431,9 @@ class DecodeLayer:
             L.nosa_decode_partial_step(self.shape, q_buf, self.kv, rb, L.NOSA_KV_FULL, self.sel,
                                        self.n_sel, self.k, self.k, 1, self.kv, rb, self.step_dev,
                                        self.e_tok, self.e_stride, self.ws, self.ws_bytes, 0)
-            L.nosa_decode_combine(self.shape, self.chunks_all, self.out, self.ws, self.ws_bytes)
-            L.nosa_step_advance(self.shape, self.step_dev)
+            # the merge also moves the step record on (one kernel fewer per replay)
+            L.nosa_decode_combine_step(self.shape, self.chunks_all, self.out, self.ws,
+                                       self.ws_bytes, self.step_dev)
         torch.cuda.current_stream().wait_stream(side)
         return graph
 
