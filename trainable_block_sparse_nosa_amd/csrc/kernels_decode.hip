@@ -76,7 +76,8 @@ int decode_kind(const Dims &dm, int requested) {
 // the row's chunk partials in chunk order. Lane c of each wave loads chunk
 // c's (max, sum); wave reductions give the row maximum and the denominator,
 // and each chunk's weight is read back from its lane. The partial outputs'
-// loads are issued together with those: one memory round trip, no LDS.
+// loads are issued together with those: one memory round trip, no LDS. With
+// dstep_adv, the first workgroup also moves the device step record on.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(D)
@@ -394,8 +395,11 @@ pool_queries_kernel(Dims dm, const T *__restrict__ q, int n_tokens, T *__restric
 // fragment order (a wave's fragment read is 1 KiB contiguous), and double
 // buffered: the next block's loads are in flight while the current one is
 // used. Every K and V fragment read from LDS feeds the CT tiles of the wave.
-// The eviction score is an additive logit as in the decode kernel; the
-// output is normalized and stored in bf16.
+// The eviction score is an additive logit as in the decode kernel. The
+// softmax runs in base 2 with a lazy base per column (moved only when a
+// block's maximum passes it by more than 8), P enters P.V as bf16 and the
+// denominator sums the same bf16 values on the matrix cores; the output is
+// normalized and stored in bf16.
 struct PrefillArgs {
     const void *q;          // [B][N][Hq][D]
     const void *kv;         // block-unit KV [rows][kv_row_blocks][2*S*D]

@@ -169,16 +169,16 @@ score_kernel(Dims dm, const T *__restrict__ q, const T *__restrict__ kbar, int n
 //  * top-k with k <= 64: every thread holds its candidates' keys in registers
 //    (candidate j = tid + 512 i). Each wave finds the smallest key T of its own
 //    top-k by a most-significant-bit-first search with ballots and popcounts,
-//    two bits per step (stopping as soon as exactly k of its keys are >= the
-//    prefix); its keys >= T go to LDS; then the survivors' ranks among
-//    themselves are counted by all threads at once (up to 8 per survivor),
-//    and the ones with fewer than k above them are the row's top-k. No
-//    sorting, two barriers.
+//    two bits per step with one or two keys per lane, one bit with more
+//    (stopping as soon as exactly k of its keys are >= the prefix); its keys
+//    >= T go to LDS; then the survivors' ranks among themselves are counted
+//    by all threads at once (up to 8 per survivor), and the ones with fewer
+//    than k above them are the row's top-k. No sorting, two barriers.
 //  * top-k with k > 64 (an eviction budget above 64 at initialisation, or a
 //    query budget above 64): bitonic sort of all keys in LDS.
 //  * Gamma_e after initialisation: each new candidate in turn replaces the
 //    lowest-ranked member if it ranks above it, else it is evicted.
-//  * the ascending selection list comes from a popcount prefix scan.
+//  * the ascending selection list comes from a popcount prefix scan (DPP).
 //  * optionally the set difference against the block cache runs in the same
 //    workgroup (wave 1, beside wave 0's lists), from the selection bitmap and
 //    the slot table alone.
