@@ -70,3 +70,29 @@ def test_eager_steps_continue_after_replays():
         got = gh.snapshot(layer, w)
         for r in range(w.rows):
             _compare_step(w, tr, t, r, got)
+
+
+def test_graph_replayed_steps_fullsize_32k():
+    """The 8 x 32/8-head, 32k-context workload (the benchmark's) replayed from
+    one captured graph for 70 steps, across the block boundary at step 63;
+    sampled rows compared with the oracle at every step, the record at the
+    end. With 64 rows, the step's scoring runs on the split grid and the
+    selection as its own launch, both reading the step record."""
+    gh = _gpu()
+    from test_gpu_parity import _compare_step
+    w = synth.WORKLOADS["bf16_1layer_32k"]
+    steps, rows = 70, [0, 21, 63]
+    tr = oracle_trace(w, rows=rows, steps=list(range(steps)))
+    inp = gh.upload(w, ov=tr.ov, steps=steps)
+    layer = gh.make_layer(w, inp)
+    layer.start(w.n_tokens(0))
+    q_buf = torch.empty_like(inp.q[0])
+    graph = layer.graph_capture(w.n_tokens(0), q_buf)
+    for t in range(steps):
+        q_buf.copy_(inp.q[t])
+        graph.replay()
+        got = gh.snapshot(layer, w)
+        for r in rows:
+            _compare_step(w, tr, t, r, got)
+    assert w.n_cand(steps - 1) > w.n_cand(0), "a block completes during the replays"
+    assert layer.step_dev.cpu().tolist() == [w.n_tokens(steps - 1) + 1, w.n_cand(steps - 1)]
