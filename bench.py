@@ -356,6 +356,8 @@ def bracket(ev, i0: int, h: int, fn, a):
     from trainable_block_sparse_nosa_amd import _lib as L
     if fn is L.nosa_decode_partial:
         L.nosa_decode_partial_timed(*a[:-1], ev.handle(i0), ev.handle(i0 + 1), a[-1])
+    elif fn is L.nosa_decode_attend:
+        L.nosa_decode_attend(*a[:-3], ev.handle(i0), ev.handle(i0 + 1), a[-1])
     else:
         ev.record(i0, h)
         fn(*a)

@@ -393,6 +393,26 @@ nosa_status nosa_decode_combine_step(const nosa_shape *shape, int32_t n_chunks, 
                                      void *ws, size_t ws_bytes, nosa_step *step_dev,
                                      void *stream);
 
+/* nosa_decode_partial over every chunk (chunk0 = 0) and the merge, as one
+ * call: NOSA's sparse attention for the given list (Methodology, "ED-DMA"),
+ * output out [batch][n_q_heads][D] in the input dtype, workspace ws as for
+ * nosa_decode_partial. When the matrix-core kernel (bf16) serves each row
+ * with a single chunk (nosa_decode_chunks() == 1: many rows), it is one
+ * launch: each workgroup normalizes its row's output and writes it, and ws
+ * is not used. Otherwise the partial kernel is followed by the merge kernel,
+ * as nosa_decode_partial + nosa_decode_combine. start_event / stop_event:
+ * both NULL, or both hipEvent_t recorded at the attention kernel's own start
+ * and end, as in nosa_decode_partial_timed. list_len + with_newest must be
+ * at least 1. Errors: NOSA_ERR_INVALID_ARGUMENT for a NULL out, one event
+ * without the other or nothing to attend, else as nosa_decode_partial. */
+nosa_status nosa_decode_attend(const nosa_shape *shape, const void *q, const void *kv,
+                               int64_t kv_row_blocks, int32_t kv_mode, const int32_t *list,
+                               const int32_t *n_list, int32_t list_stride, int32_t list_len,
+                               int32_t with_newest, const void *cur_kv, int64_t cur_row_blocks,
+                               const nosa_step *step, const float *e_tok, int64_t e_row_stride,
+                               void *ws, size_t ws_bytes, void *out, void *start_event,
+                               void *stop_event, void *stream);
+
 /* ---- steps replayed from a captured graph ----
  * The step record lives in device memory (step_dev: a nosa_step, 8 bytes,
  * 4-byte aligned) and every call of a step reads it in its kernels, so one

@@ -105,6 +105,15 @@ def test_invalid_pointers_and_steps_rejected():
             ctypes.byref(ok_step), 16, 64 * 64, 16, 1 << 30, 0]
     assert lib.nosa_decode_partial_timed(*args, None, 16, None) == 1
     assert lib.nosa_decode_partial_timed(*args, 16, None, None) == 1
+    # attention with its merge: no out, one event without the other, an
+    # empty list with no newest block
+    a17 = args[:-1]
+    assert lib.nosa_decode_attend(*a17, None, None, None, None) == 1
+    assert lib.nosa_decode_attend(*a17, 16, 16, None, None) == 1
+    assert lib.nosa_decode_attend(*a17, 16, None, 16, None) == 1
+    empty = list(a17)
+    empty[8], empty[9] = 0, 0
+    assert lib.nosa_decode_attend(*empty, 16, None, None, None) == 1
     # a step beyond the block capacity
     big = L.make_step(64 * 64 + 1, -1)
     assert lib.nosa_score_blocks(ctypes.byref(sh), 16, 16, ctypes.byref(big), 16, None) == 1

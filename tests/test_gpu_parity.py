@@ -367,9 +367,10 @@ def test_select_signed_zero_ties():
 
 
 def test_timed_partial_matches_untimed():
-    """nosa_decode_partial_timed (the attention partial kernel bracketed by two
-    events at its own start and end) writes the same bits as
-    nosa_decode_partial, and the events give a positive duration per call."""
+    """The attention call with events recorded at its kernel's own start and
+    end (nosa_decode_attend with events; nosa_decode_partial_timed for a
+    split step) writes the same bits as without them, and the events give a
+    positive duration per call."""
     gh = _gpu()
     import bench
     from trainable_block_sparse_nosa_amd import _lib as L
@@ -383,7 +384,7 @@ def test_timed_partial_matches_untimed():
         n = [0]
 
         def hook(name, fn, *a):
-            if timed and fn is L.nosa_decode_partial:
+            if timed and fn in (L.nosa_decode_partial, L.nosa_decode_attend):
                 bench.bracket(ev, 2 * n[0], 0, fn, a)
                 n[0] += 1
             else:
@@ -427,3 +428,39 @@ def test_parity_large_eviction_logits(name):
         assert np.isfinite(res[t]["out"]).all()
         for r in range(w.rows):
             _compare_step(w, tr, t, r, res[t])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", ["bf16_1layer_32k", "bf16_3b_64k", "small_f32"])
+def test_attend_matches_partial_then_merge(name):
+    """nosa_decode_attend against nosa_decode_partial + nosa_decode_combine on
+    the same selection: 64k (256 rows, one chunk per row: the matrix-
+    core workgroup writes the output itself, in one launch), 32k (4 chunks
+    per row: partials, then the merge kernel) and float32. With one chunk the
+    merge's weight is exp(0) = 1, so the direct write is the same division of
+    the same values: every case must agree bit for bit. Two calls, the second
+    over the eviction set only (fewer chunks)."""
+    gh = _gpu()
+    from trainable_block_sparse_nosa_amd import _lib as L
+    w = synth.WORKLOADS[name]
+    inp = gh.upload(w, steps=1)
+    layer = gh.make_layer(w, inp)
+    layer.start(w.n_tokens(0))
+    layer.step(inp.q[0], w.n_tokens(0))
+    torch.cuda.synchronize()
+    c = (w.n_tokens(0) - 1) // 64
+    st = L.make_step(w.n_tokens(0), c)
+    for list_len in (layer.k, w.k_e):
+        args = (layer.shape, inp.q[0], layer.kv, layer.kv_row_blocks, L.NOSA_KV_FULL, layer.sel,
+                layer.n_sel, layer.k, list_len, 1, layer._kv_ptr(c), layer.kv_row_blocks, st,
+                layer.e_tok, layer.e_stride, layer.ws, layer.ws_bytes)
+        got = torch.full_like(layer.out, 7)
+        L.nosa_decode_attend(*args, got)
+        want = torch.full_like(layer.out, 7)
+        L.nosa_decode_partial(*args, 0)
+        L.nosa_decode_combine(layer.shape, L.nosa_decode_chunks(layer.shape, list_len, 1), want,
+                              layer.ws, layer.ws_bytes)
+        torch.cuda.synchronize()
+        g, x = got.cpu(), want.cpu()
+        assert torch.isfinite(g.float()).all()
+        assert torch.equal(g, x)

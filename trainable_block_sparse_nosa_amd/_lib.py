@@ -34,7 +34,7 @@ EXPORTS = (
     "nosa_ingest_tokens", "nosa_prefill_pool_queries", "nosa_prefill_select",
     "nosa_prefill_attention", "nosa_decode_workspace_size", "nosa_decode_chunks",
     "nosa_sparse_decode", "nosa_decode_partial", "nosa_decode_partial_timed",
-    "nosa_decode_combine", "nosa_decode_combine_step",
+    "nosa_decode_combine", "nosa_decode_combine_step", "nosa_decode_attend",
     "nosa_step_advance", "nosa_pool_step", "nosa_append_step", "nosa_score_select_step",
     "nosa_decode_partial_step",
     "nosa_host_alloc", "nosa_host_free", "nosa_read_probe", "nosa_status_string",
@@ -86,6 +86,8 @@ def _load() -> ctypes.CDLL:
                                 I32, P],
         "nosa_decode_partial_timed": [SH, P, P, I64, I32, P, P, I32, I32, I32, P, I64, ST, P, I64,
                                       P, SZ, I32, P, P, P],
+        "nosa_decode_attend": [SH, P, P, I64, I32, P, P, I32, I32, I32, P, I64, ST, P, I64,
+                               P, SZ, P, P, P, P],
         "nosa_decode_combine": [SH, I32, P, P, SZ, P],
         "nosa_decode_combine_step": [SH, I32, P, P, SZ, P, P],
         "nosa_host_alloc": [SZ, I32, ctypes.POINTER(P), ctypes.POINTER(P)],
@@ -225,6 +227,17 @@ def nosa_decode_partial_timed(shape, q, kv, kv_row_blocks, kv_mode, list_, n_lis
         list_stride, list_len, with_newest, _p(cur_kv), cur_row_blocks, ctypes.byref(step),
         _p(e_tok), e_row_stride, _p(ws), ws_bytes, chunk0, _p(start_event), _p(stop_event),
         _s(stream)))
+
+
+def nosa_decode_attend(shape, q, kv, kv_row_blocks, kv_mode, list_, n_list, list_stride,
+                       list_len, with_newest, cur_kv, cur_row_blocks, step, e_tok, e_row_stride,
+                       ws, ws_bytes, out, start_event=None, stop_event=None, stream=None):
+    """start_event / stop_event: both None, or hipEvent_t handles."""
+    _chk("nosa_decode_attend", _L.nosa_decode_attend(
+        ctypes.byref(shape), _p(q), _p(kv), kv_row_blocks, kv_mode, _p(list_), _p(n_list),
+        list_stride, list_len, with_newest, _p(cur_kv), cur_row_blocks, ctypes.byref(step),
+        _p(e_tok), e_row_stride, _p(ws), ws_bytes, _p(out), _p(start_event),
+        _p(stop_event), _s(stream)))
 
 
 def nosa_decode_combine(shape, n_chunks, out, ws, ws_bytes, stream=None):

@@ -477,7 +477,7 @@ static nosa_status decode_partial_impl(const nosa_shape *shape, const void *q, c
                                        const nosa_step *step, const float *e_tok,
                                        int64_t e_row_stride, void *ws, size_t ws_bytes,
                                        int32_t chunk0, hipEvent_t ev0, hipEvent_t ev1,
-                                       void *stream) {
+                                       void *stream, void *out = nullptr) {
     Dims dm;
     nosa_status s = make_dims(shape, &dm);
     if (s != NOSA_OK) return s;
@@ -502,7 +502,16 @@ static nosa_status decode_partial_impl(const nosa_shape *shape, const void *q, c
     a.with_newest = with_newest;
     a.chunk0 = chunk0;
     a.cb = pl.cb;
-    return launch_partial(dm, kind, pl, a, (hipStream_t)stream, ev0, ev1);
+    if (!out) return launch_partial(dm, kind, pl, a, (hipStream_t)stream, ev0, ev1);
+    // with the output: one launch when the MFMA kernel serves each row with a
+    // single chunk, else the partials and then the merge kernel
+    if (kind == NOSA_DECODE_MFMA && pl.n_chunks == 1) {
+        a.out = out;
+        return launch_partial(dm, kind, pl, a, (hipStream_t)stream, ev0, ev1);
+    }
+    s = launch_partial(dm, kind, pl, a, (hipStream_t)stream, ev0, ev1);
+    if (s != NOSA_OK || pl.n_chunks == 0) return s;
+    return launch_merge(dm, pl.n_chunks, a, out, (hipStream_t)stream);
 }
 
 nosa_status nosa_decode_partial(const nosa_shape *shape, const void *q, const void *kv,
@@ -530,6 +539,21 @@ nosa_status nosa_decode_partial_timed(const nosa_shape *shape, const void *q, co
                                list_len, with_newest, cur_kv, cur_row_blocks, step, e_tok,
                                e_row_stride, ws, ws_bytes, chunk0, (hipEvent_t)start_event,
                                (hipEvent_t)stop_event, stream);
+}
+
+nosa_status nosa_decode_attend(const nosa_shape *shape, const void *q, const void *kv,
+                               int64_t kv_row_blocks, int32_t kv_mode, const int32_t *list,
+                               const int32_t *n_list, int32_t list_stride, int32_t list_len,
+                               int32_t with_newest, const void *cur_kv, int64_t cur_row_blocks,
+                               const nosa_step *step, const float *e_tok, int64_t e_row_stride,
+                               void *ws, size_t ws_bytes, void *out, void *start_event,
+                               void *stop_event, void *stream) {
+    if (!out || (!start_event != !stop_event)) return NOSA_ERR_INVALID_ARGUMENT;
+    if (list_len + with_newest == 0) return NOSA_ERR_INVALID_ARGUMENT;  // nothing to normalize
+    return decode_partial_impl(shape, q, kv, kv_row_blocks, kv_mode, list, n_list, list_stride,
+                               list_len, with_newest, cur_kv, cur_row_blocks, step, e_tok,
+                               e_row_stride, ws, ws_bytes, 0, (hipEvent_t)start_event,
+                               (hipEvent_t)stop_event, stream, out);
 }
 
 // ---- steps replayed from a captured graph: the step record in device memory ----

@@ -115,6 +115,9 @@ struct DecodeArgs {
     int cb;        // entries per chunk (from the plan)
     const int32_t *dstep = nullptr;  // device step record: overrides n_tokens / n_cand
     int cur_at_step = 0;             // 1: the newest block is block n_cand of cur's rows
+    // MFMA kernel with one chunk per row: with out set, each workgroup
+    // normalizes its row's output and writes it, leaving no partials
+    void *out = nullptr;
 };
 
 template <typename T, int D, int G>

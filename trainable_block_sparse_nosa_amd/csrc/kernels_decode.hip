@@ -11,9 +11,13 @@
 // keeps an online-softmax state (max, sum, output) per head and writes it to
 // the workspace as its chunk's partial; a second kernel merges each row's
 // partials in chunk order and writes the output. The merge order is fixed,
-// so results do not depend on scheduling. (Merging inside the first kernel
+// so results do not depend on scheduling. Merging inside the first kernel
 // would need device-scope fences, which on a multi-XCD part write back and
-// invalidate L2; the kernel boundary gives the same ordering for free.)
+// invalidate L2 under the other workgroups' streaming reads (a last-arriving-
+// workgroup merge measured over three times slower on a 64-row, 4-chunk
+// step); the kernel boundary gives the same ordering for free. A row served
+// by a single chunk needs no merge: its workgroup can normalize and write the
+// output itself.
 //
 // Two kernels compute the partials:
 //  * MFMA (bf16): the G query heads of a row are padded to a 16-wide tile
@@ -312,6 +316,9 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
     __syncthreads();
     const int64_t base = ((int64_t)r * a.chunk_cap + a.chunk0 + chunk) * G;
     float *ws_o = a.ws_o, *ws_ml = a.ws_ml;
+    bf16_t *out = static_cast<bf16_t *>(a.out);
+    const int64_t out_row = ((int64_t)b * dm.Hq + (int64_t)g * G) * D;  // head 0 of the row's group
+    const bool direct = out && gridDim.x == 1;  // the row's only chunk: normalize here
     for (int p = threadIdx.x; p < G * D; p += blockDim.x) {
         const int h = p / D, d = p % D;
         float mw[WAVES], lw[WAVES];
@@ -328,6 +335,10 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
             const float c = lw[w] > 0.f ? __expf(mw[w] - M) : 0.f;
             O = fmaf(wo[w][d][h], c, O);
             L = fmaf(lw[w], c, L);
+        }
+        if (direct) {
+            out[out_row + p] = stf<bf16_t>(O / L);
+            continue;
         }
         ws_o[base * D + p] = O;
         if (d == 0) {

@@ -346,16 +346,15 @@ class DecodeLayer:
             self._run("fetch", L.nosa_fetch_blocks, self.shape, self.kv, self.kv_row_blocks,
                       self.fetch_block, self.fetch_slot, self.n_fetch, self.k, self.cache, self.k,
                       stream)
-            self._run("decode", L.nosa_decode_partial, self.shape, q, self.cache, self.k,
+            self._run("decode", L.nosa_decode_attend, self.shape, q, self.cache, self.k,
                       L.NOSA_KV_CACHE, self.slot_block, None, self.k, self.k, 1, self.cur, 1, st,
-                      self.e_tok, self.e_stride, self.ws, self.ws_bytes, 0, stream)
-        else:
-            self._run("decode", L.nosa_decode_partial, self.shape, q, self.kv, self.kv_row_blocks,
-                      L.NOSA_KV_FULL, self.sel, self.n_sel, self.k, self.k, 1, self._kv_ptr(c),
-                      self.kv_row_blocks, st, self.e_tok, self.e_stride, self.ws, self.ws_bytes, 0,
+                      self.e_tok, self.e_stride, self.ws, self.ws_bytes, self.out, None, None,
                       stream)
-        self._run("combine", L.nosa_decode_combine, self.shape, self.chunks_all, self.out,
-                  self.ws, self.ws_bytes, stream)
+        else:
+            self._run("decode", L.nosa_decode_attend, self.shape, q, self.kv, self.kv_row_blocks,
+                      L.NOSA_KV_FULL, self.sel, self.n_sel, self.k, self.k, 1, self._kv_ptr(c),
+                      self.kv_row_blocks, st, self.e_tok, self.e_stride, self.ws, self.ws_bytes,
+                      self.out, None, None, stream)
         self.n_cand_prev = c
         self.n_tokens = n_tokens
         return self.out
