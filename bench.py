@@ -350,9 +350,9 @@ ATTN_STAGES = ("decode", "decode_e", "decode_q")
 
 def bracket(ev, i0: int, h: int, fn, a):
     """Run fn(*a) between events i0 and i0 + 1 of ev on stream handle h. The
-    attention partial call goes through its timed entry point, which records
-    the two events at the partial kernel's own start and end (so they agree
-    with a kernel trace); any other call sits between two event records."""
+    attention calls pass the two events to the library, which records them at
+    the attention kernel's own start and end (so they agree with a kernel
+    trace); any other call sits between two event records."""
     from trainable_block_sparse_nosa_amd import _lib as L
     if fn is L.nosa_decode_partial:
         L.nosa_decode_partial_timed(*a[:-1], ev.handle(i0), ev.handle(i0 + 1), a[-1])
@@ -422,7 +422,7 @@ class HipTimingEvents:
 def timed_run(layer, w, q, args, stream, event_stages=ATTN_STAGES, new=None, sample_every=8):
     """Warm up, then time exactly args.steps steps. HIP events bracket the
     listed stages in every sample_every-th timed step (see bracket(): the
-    attention partial kernel's events mark its own start and end; timing
+    attention kernel's events mark its own start and end; timing
     every step would understate the throughput by ~8 % on the 32k workload).
     Returns (elapsed s, [(stage, step, ms)], blocks fetched in the timed
     steps)."""
@@ -997,7 +997,8 @@ def main():
             "kv": "pinned host" if w.offload else "hbm", "decode_kernel": args.decode_kernel,
         },
         "roofline": {
-            "kernel": "split-K attention partial kernel (decode_mfma_kernel; with overlap, two "
+            "kernel": "split-K attention kernel (decode_mfma_kernel: partials for the merge "
+                      "kernel, or with one chunk per row the output itself; with overlap, two "
                       "launches per step: eviction set + newest block, then query set)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name),
