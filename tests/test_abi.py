@@ -191,3 +191,22 @@ def test_device_step_calls_validate_against_the_capacity():
     assert call(args(es=mb * 64 - 4)) == 1
     assert call(args(st=None)) == 1
     assert call(args(rb=mb - 1)) == 1
+
+
+def test_decode_chunk_plan():
+    """The attention plan, host logic only: about one 8-wave workgroup per CU
+    (256), so ceil(256 / rows) chunks per row, at least one block per wave;
+    one chunk per row from 256 rows on, where nosa_decode_attend writes the
+    output in the attention launch with no merge launch."""
+    from trainable_block_sparse_nosa_amd import _lib as L
+    # 64 rows (batch 8 x 8 KV heads), 64 + 1 entries: 4 chunks
+    sh = _shape(batch=8, n_q_heads=32, n_kv_heads=8, k_e=48, k_q=16, max_blocks=1024)
+    assert L.nosa_decode_chunks(sh, 64, 1) == 4
+    # few entries cap the chunks at one block per wave: 9 entries -> 2 chunks
+    assert L.nosa_decode_chunks(sh, 8, 1) == 2
+    # 256 rows (batch 32 x 8 KV heads), 128 + 1 entries: one chunk per row
+    sh = _shape(batch=32, n_q_heads=24, n_kv_heads=8, k_e=96, k_q=32, max_blocks=1024)
+    assert L.nosa_decode_chunks(sh, 128, 1) == 1
+    # 128 rows: 2 chunks
+    sh = _shape(batch=16, n_q_heads=32, n_kv_heads=8, k_e=48, k_q=16, max_blocks=2048)
+    assert L.nosa_decode_chunks(sh, 64, 1) == 2
