@@ -336,7 +336,9 @@ int32_t nosa_decode_chunks(const nosa_shape *shape, int32_t list_len, int32_t wi
  *   blocks per row); for the full KV pass kv advanced by n_cand blocks.
  * Split-K partials go to ws (at least nosa_decode_workspace_size bytes); a
  * second kernel merges each row's partials in a fixed order and writes out
- * (float32 accumulation, bf16 stores round to nearest even). shape.decode_kernel picks the partial kernel: MFMA (bf16
+ * (float32 accumulation, bf16 stores round to nearest even). When the MFMA
+ * kernel serves each row with a single chunk (nosa_decode_chunks(shape, k, 1)
+ * == 1), that kernel normalizes and writes out itself, in one launch. shape.decode_kernel picks the partial kernel: MFMA (bf16
  * only; the default for bf16) or VALU (the default for float32). */
 nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *kv,
                                int64_t kv_row_blocks, int32_t kv_mode, const int32_t *list,

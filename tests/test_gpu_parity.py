@@ -294,7 +294,7 @@ def test_offload_edge_gqa1_short():
 @pytest.mark.parametrize("name", ["small_bf16", "small_offload", "small_f32"])
 def test_one_call_decode_matches_split_calls(name):
     """nosa_sparse_decode (partial + merge in one call) gives the same bits as
-    the pipeline's nosa_decode_partial + nosa_decode_combine."""
+    the pipeline's attention call."""
     gh = _gpu()
     from trainable_block_sparse_nosa_amd import _lib as L
     w = synth.WORKLOADS[name]
@@ -439,7 +439,9 @@ def test_attend_matches_partial_then_merge(name):
     per row: partials, then the merge kernel) and float32. With one chunk the
     merge's weight is exp(0) = 1, so the direct write is the same division of
     the same values: every case must agree bit for bit. Two calls, the second
-    over the eviction set only (fewer chunks)."""
+    over the eviction set only (fewer chunks). The one-call nosa_sparse_decode
+    takes the same single launch on one chunk per row: checked on the full
+    list."""
     gh = _gpu()
     from trainable_block_sparse_nosa_amd import _lib as L
     w = synth.WORKLOADS[name]
@@ -464,3 +466,11 @@ def test_attend_matches_partial_then_merge(name):
         g, x = got.cpu(), want.cpu()
         assert torch.isfinite(g.float()).all()
         assert torch.equal(g, x)
+        if list_len == layer.k:
+            one = torch.full_like(layer.out, 7)
+            L.nosa_sparse_decode(layer.shape, inp.q[0], layer.kv, layer.kv_row_blocks,
+                                 L.NOSA_KV_FULL, layer.sel, layer.n_sel, layer._kv_ptr(c),
+                                 layer.kv_row_blocks, st, layer.e_tok, layer.e_stride, one,
+                                 layer.ws, layer.ws_bytes)
+            torch.cuda.synchronize()
+            assert torch.equal(one.cpu(), x)

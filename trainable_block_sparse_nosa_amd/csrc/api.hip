@@ -464,6 +464,10 @@ nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const voi
     const DecodePlan pl = decode_plan(dm, kind, dm.k + 1);
     a.cb = pl.cb;
     const hipStream_t st = (hipStream_t)stream;
+    if (kind == NOSA_DECODE_MFMA && pl.n_chunks == 1) {
+        a.out = out;  // one chunk per row: the attention launch writes the output
+        return launch_partial(dm, kind, pl, a, st);
+    }
     s = launch_partial(dm, kind, pl, a, st);
     if (s != NOSA_OK) return s;
     return launch_merge(dm, pl.n_chunks, a, out, st);
