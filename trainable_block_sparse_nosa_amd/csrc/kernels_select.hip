@@ -653,7 +653,8 @@ struct ScoresFusedMfma {
 // Block scores on the matrix cores with the row split over workgroups
 // (blockIdx.x = chunk of SCORE_TILES_PER_WG tiles, blockIdx.y = row), so that
 // a launch has many more workgroups than rows: each wave loads its 4 tiles
-// (4 KiB of pooled keys) at once, and the grid covers the row in one pass.
+// (4 x 16 sub-blocks x D: 16 KiB of bf16 pooled keys at D = 128) at once,
+// and the grid covers the row in one pass.
 // With dstep, n_cand comes from the step record and the grid is sized for the
 // capacity; chunks past the candidates exit at once.
 constexpr int SCORE_WAVES = 4;
