@@ -401,7 +401,7 @@ nosa_status nosa_decode_combine_step(const nosa_shape *shape, int32_t n_chunks, 
  * nosa_decode_partial. When the matrix-core kernel (bf16) serves each row
  * with a single chunk (nosa_decode_chunks() == 1: many rows), it is one
  * launch: each workgroup normalizes its row's output and writes it, and ws
- * is not used. Otherwise the partial kernel is followed by the merge kernel,
+ * (still required and validated) is not written. Otherwise the partial kernel is followed by the merge kernel,
  * as nosa_decode_partial + nosa_decode_combine. start_event / stop_event:
  * both NULL, or both hipEvent_t recorded at the attention kernel's own start
  * and end, as in nosa_decode_partial_timed. list_len + with_newest must be
