@@ -1024,7 +1024,10 @@ def main():
 
 def stage_breakdown(layer, w, q, t0: int, n: int, stream):
     """Per-stage GPU time (us per call) from events placed around each stage's
-    launch, on a replay of the timed steps from a fresh start."""
+    launch, on a replay of the timed steps from a fresh start. The "decode"
+    stage is the whole attention call: with several chunks per row it holds
+    the partial kernel and the merge kernel, with one chunk per row a single
+    launch."""
     import torch
     pending = []
 
