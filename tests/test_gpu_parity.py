@@ -439,7 +439,8 @@ def test_attend_matches_partial_then_merge(name):
     per row: partials, then the merge kernel) and float32. With one chunk the
     merge's weight is exp(0) = 1, so the direct write is the same division of
     the same values: every case must agree bit for bit. Two calls, the second
-    over the eviction set only (fewer chunks). The one-call nosa_sparse_decode
+    over the eviction set only (fewer chunks), each also with its two timing
+    events (the bench's timed form). The one-call nosa_sparse_decode
     takes the same single launch on one chunk per row: checked on the full
     list."""
     gh = _gpu()
@@ -466,6 +467,15 @@ def test_attend_matches_partial_then_merge(name):
         g, x = got.cpu(), want.cpu()
         assert torch.isfinite(g.float()).all()
         assert torch.equal(g, x)
+        # the same call with its two events (the bench's timed form)
+        import bench
+        ev = bench.HipTimingEvents(2)
+        timed = torch.full_like(layer.out, 7)
+        L.nosa_decode_attend(*args, timed, ev.handle(0), ev.handle(1))
+        torch.cuda.synchronize()
+        assert ev.elapsed_ms(0, 1) > 0
+        ev.close()
+        assert torch.equal(timed.cpu(), x)
         if list_len == layer.k:
             one = torch.full_like(layer.out, 7)
             L.nosa_sparse_decode(layer.shape, inp.q[0], layer.kv, layer.kv_row_blocks,
