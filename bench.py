@@ -118,7 +118,7 @@ def cpu_baseline(w, seconds: float, steps_avail: int):
             q = q_t[b, g * w.group:(g + 1) * w.group]
             t0 = time.perf_counter()
             oracle.step_row(w.n_tokens(t), q, K, V, e, 64, 16, w.k_e, w.k_q, sc,
-                            pooled_bf16=w.dtype == "bf16")
+                            pooled_bf16=w.pooled == "bf16")
             t_used += time.perf_counter() - t0
             done += 1
             if t_used >= seconds:

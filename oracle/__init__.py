@@ -59,7 +59,7 @@ def lib():
             L.oracle_evict_logit.restype = ctypes.c_double
             L.oracle_block_evict.argtypes = [_f, ctypes.c_int, ctypes.c_int, ctypes.c_int]
             L.oracle_block_evict.restype = ctypes.c_double
-            L.oracle_block_score.argtypes = [_f, ctypes.c_int, ctypes.c_int, _f, ctypes.c_int,
+            L.oracle_block_score.argtypes = [_d, ctypes.c_int, ctypes.c_int, _f, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                              ctypes.c_int]
             L.oracle_block_score.restype = ctypes.c_double
@@ -69,7 +69,7 @@ def lib():
                                                ctypes.c_int, ctypes.c_double, _d]
             L.oracle_attend_tokens.restype = None
             L.oracle_pool_queries.argtypes = [_f, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                              ctypes.c_int, _f]
+                                              ctypes.c_int, _d]
             L.oracle_pool_queries.restype = None
             L.oracle_prefill_row.argtypes = [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_int,
                                                                  _f, _f, _f, _f, _d, _i]
@@ -115,8 +115,8 @@ def round_bf16(x: float) -> float:
 
 
 def pool_keys(K: np.ndarray, block: int, sub: int, j: int, pooled_bf16: bool = False) -> np.ndarray:
-    """Sub-block means of block j's keys: [block // sub, D] fp64 (rounded to
-    the nearest bfloat16 when pooled_bf16)."""
+    """Sub-block means of block j's keys: [block // sub, D] fp64, exact
+    (rounded to the nearest bfloat16 when pooled_bf16)."""
     K = _f32(K)
     D = K.shape[1]
     out = np.zeros((block // sub, D), dtype=np.float64)
@@ -152,10 +152,11 @@ def block_evict(e: np.ndarray, block: int, sub: int, j: int) -> float:
 
 def block_score(q: np.ndarray, K: np.ndarray, block: int, sub: int, j: int, scale: float,
                 pooled_bf16: bool = False) -> float:
-    """Query-aware pooled score of block j for the query heads q [G, D]."""
-    q, K = _f32(q), _f32(K)
+    """Query-aware pooled score of block j for the query heads q [G, D]
+    (taken as fp64: float32 queries exactly, pooled queries as they are)."""
+    q, K = np.ascontiguousarray(q, dtype=np.float64), _f32(K)
     G, D = q.shape
-    return lib().oracle_block_score(_pf(q), G, D, _pf(K), block, sub, j, scale, int(pooled_bf16))
+    return lib().oracle_block_score(_pd(q), G, D, _pf(K), block, sub, j, scale, int(pooled_bf16))
 
 
 def topk(x, k: int, allowed=None) -> list[int]:
@@ -208,8 +209,9 @@ def step_row(n_tokens: int, q, K, V, e, block: int, sub: int, k_e: int, k_q: int
              scale: float, pooled_bf16: bool = False) -> RowStep:
     """Selection and attention output of one row at one decode step.
 
-    q [G, D]; K, V [>= n_tokens, D]; e [>= n_tokens]. All fp64 inside;
-    pooled_bf16 keeps the pooled key means in bfloat16 (bfloat16 keys).
+    q [G, D]; K, V [>= n_tokens, D]; e [>= n_tokens]. All fp64 inside, the
+    pooled keys exact; pooled_bf16 rounds them to the nearest bfloat16 (the
+    variant that stores pooled keys in the model's dtype).
     """
     q, K, V, e = _f32(q), _f32(K), _f32(V), _f32(e)
     G, D = q.shape
@@ -280,12 +282,12 @@ class SlotCache:
 # ---------------------------------------------------------------------------
 
 def pool_queries(q: np.ndarray, pooled_bf16: bool = False) -> np.ndarray:
-    """Pooled query of a query block, q [n, G, D] -> [G, D] (float32 values:
-    the exact mean rounded to bfloat16 with pooled_bf16, else to float)."""
+    """Pooled query of a query block, q [n, G, D] -> [G, D] fp64: the exact
+    mean (rounded to the nearest bfloat16 with pooled_bf16)."""
     q = _f32(q)
     n, G, D = q.shape
-    out = np.zeros((G, D), np.float32)
-    lib().oracle_pool_queries(_pf(q), n, G, D, int(pooled_bf16), _pf(out))
+    out = np.zeros((G, D), np.float64)
+    lib().oracle_pool_queries(_pf(q), n, G, D, int(pooled_bf16), _pd(out))
     return out
 
 

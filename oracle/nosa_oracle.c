@@ -32,13 +32,14 @@
  * its per-head block scores; per-head max over sub-blocks comes before that
  * sum; scores are scaled by `scale` with no softmax; the newest block is
  * always attended and is not a candidate; equal scores rank the lower block
- * index first; with bfloat16 keys the pooled sub-block means are kept in
- * bfloat16, i.e. the exact mean rounded to the nearest bfloat16, ties to
- * even, and the query-aware score is computed from those rounded means) are
- * listed in the repository's design notes. The one rounding step, the
- * pooled means with `pooled_bf16` set, is a quantisation of the stored
- * pooled keys, not an arithmetic shortcut: the score is still computed in
- * double from the quantised means.
+ * index first; pooled keys and pooled queries are the exact means) are
+ * listed in the repository's design notes. Nothing is rounded by default.
+ * One variant is offered for a stack that stores its pooled keys in the
+ * model's dtype: with `pooled_bf16` set, each pooled mean (key, and the
+ * pooled query of a prefill query block) is the exact mean rounded to the
+ * nearest bfloat16, ties to even; that is a quantisation of the stored
+ * pooled values, not an arithmetic shortcut, and the score is still
+ * computed in double from the quantised means.
  */
 #include <math.h>
 #include <stdint.h>
@@ -113,9 +114,9 @@ double oracle_block_evict(const float *e, int block, int sub, int j)
     return best;
 }
 
-/* Query-aware pooled score of block j for a group of G query heads q[h][D]:
-   sum over heads of (max over sub-blocks of scale * q_h . kbar_i). */
-double oracle_block_score(const float *q, int G, int D, const float *K, int block, int sub,
+/* Query-aware pooled score of block j for a group of G query heads q[h][D]
+   (double): sum over heads of (max over sub-blocks of scale * q_h . kbar_i). */
+double oracle_block_score(const double *q, int G, int D, const float *K, int block, int sub,
                           int j, double scale, int pooled_bf16)
 {
     int m = block / sub;
@@ -127,7 +128,7 @@ double oracle_block_score(const float *q, int G, int D, const float *K, int bloc
         for (int i = 0; i < m; ++i) {
             double dot = 0.0;
             for (int d = 0; d < D; ++d)
-                dot += (double)q[h * D + d] * kbar[i * D + d];
+                dot += q[h * D + d] * kbar[i * D + d];
             double a = scale * dot;
             if (a > best)
                 best = a;
@@ -228,10 +229,14 @@ int oracle_step_row(int n_tokens, int G, int D, int block, int sub, int k_e, int
     double *Sb = (double *)malloc(sizeof(double) * (size_t)cc);
     unsigned char *rest = (unsigned char *)malloc((size_t)cc);
 
+    double *qd = (double *)malloc(sizeof(double) * (size_t)G * (size_t)D);
+    for (int i = 0; i < G * D; ++i)
+        qd[i] = (double)q[i];
     for (int j = 0; j < c; ++j) {
         Eb[j] = oracle_block_evict(e, block, sub, j);
-        Sb[j] = oracle_block_score(q, G, D, K, block, sub, j, scale, pooled_bf16);
+        Sb[j] = oracle_block_score(qd, G, D, K, block, sub, j, scale, pooled_bf16);
     }
+    free(qd);
 
     /* Gamma_e: the k_e greatest candidates by pooled eviction score. */
     *n_ge = oracle_topk(Eb, NULL, c, k_e, ge);
@@ -280,14 +285,15 @@ int oracle_step_row(int n_tokens, int G, int D, int block, int sub, int k_e, int
  * as a decode step with those candidates does (Gamma_e: the k_e greatest
  * pooled eviction scores; Gamma_q: the k_q greatest of the rest by the
  * query-aware score), the query-aware score being that of the block's pooled
- * query (the mean of its tokens' queries per head, kept in the input dtype:
- * rounded to the nearest bfloat16 for bfloat16 inputs, to the nearest float
- * otherwise); every query token of the block attends the tokens of the
- * selected blocks and, causally, the tokens of its own block up to itself.
+ * query (the exact mean of its tokens' queries per head; rounded to the
+ * nearest bfloat16 with `pooled_bf16`, as the pooled keys are); every query
+ * token of the block attends the tokens of the selected blocks and, causally,
+ * the tokens of its own block up to itself.
  * ------------------------------------------------------------------------ */
 
-/* Pooled query of n tokens q[u][h][d] (u < n): per (h, d) the mean over u. */
-void oracle_pool_queries(const float *q, int n, int G, int D, int pooled_bf16, float *out)
+/* Pooled query of n tokens q[u][h][d] (u < n): per (h, d) the mean over u
+   (rounded to the nearest bfloat16 with pooled_bf16). */
+void oracle_pool_queries(const float *q, int n, int G, int D, int pooled_bf16, double *out)
 {
     for (int h = 0; h < G; ++h)
         for (int d = 0; d < D; ++d) {
@@ -295,7 +301,7 @@ void oracle_pool_queries(const float *q, int n, int G, int D, int pooled_bf16, f
             for (int u = 0; u < n; ++u)
                 s += (double)q[((int64_t)u * G + h) * D + d];
             double mean = s / (double)n;
-            out[h * D + d] = (float)(pooled_bf16 ? oracle_round_bf16(mean) : mean);
+            out[h * D + d] = pooled_bf16 ? oracle_round_bf16(mean) : mean;
         }
 }
 
@@ -320,7 +326,7 @@ void oracle_prefill_qblock(int N, int G, int D, int block, int sub, int k_e, int
     int *ge = (int *)malloc(sizeof(int) * (size_t)(k_e > 0 ? k_e : 1));
     int *gq = (int *)malloc(sizeof(int) * (size_t)(k_q > 0 ? k_q : 1));
     int *tok = (int *)malloc(sizeof(int) * (size_t)(k * block + block));
-    float *qbar = (float *)malloc(sizeof(float) * (size_t)G * (size_t)D);
+    double *qbar = (double *)malloc(sizeof(double) * (size_t)G * (size_t)D);
     for (int j = 0; j < c; ++j)
         Eb[j] = oracle_block_evict(e, block, sub, j);
     oracle_pool_queries(q + (int64_t)lo * G * D, hi - lo, G, D, pooled_bf16, qbar);

@@ -53,6 +53,10 @@ class Workload:
     sub_block: int = 16
     key_offset_std: float = 0.0  # std of the per-block mean offset added to K
     host_kv_slabs: int = 0     # >0: layers share this many host KV slabs (layer l uses l % slabs)
+    # dtype of the pooled keys (and of a prefill's pooled queries): "f32", the
+    # exact means rounded once to float32 (the oracle keeps them exact), or
+    # "bf16", the variant that stores them in the model's dtype
+    pooled: str = "f32"
 
     @property
     def group(self) -> int:

@@ -121,7 +121,7 @@ def oracle_trace(w: Workload, layer: int = 0, rows=None, steps=None, ov: Overrid
             for _ in range(64):
                 q = group_q(w, layer, t, b, g, ov)
                 res = oracle.step_row(w.n_tokens(t), q, K, V, e, w.block, w.sub_block,
-                                      w.k_e, w.k_q, sc, pooled_bf16=w.dtype == "bf16")
+                                      w.k_e, w.k_q, sc, pooled_bf16=w.pooled == "bf16")
                 if not margins:
                     break
                 rest = np.array([j not in set(res.gamma_e) for j in range(res.n_cand)], bool)

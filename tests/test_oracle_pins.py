@@ -444,7 +444,7 @@ def test_prefill_eviction_selection_by_brute_force():
 
 def test_prefill_query_selection_by_brute_force():
     """k_e = 0: the k_q blocks with the largest score of the block's pooled
-    query (mean of its queries, as a float) against the sub-block key means."""
+    query (the exact mean of its queries) against the sub-block key means."""
     rng = np.random.default_rng(43)
     N, G, D, kq, sc = 64 * 5 + 30, 2, 4, 2, 0.4
     q = rng.normal(size=(N, G, D)).astype(np.float32)
@@ -454,12 +454,14 @@ def test_prefill_query_selection_by_brute_force():
     res = oracle.prefill_row(q, K, V, e, 64, 16, 0, kq, sc)
     Kd = K.astype(np.float64)
     for i in range(1, N // 64 + 1):
-        qb = q[64 * i:64 * i + 64].astype(np.float64).mean(axis=0).astype(np.float32)
+        # sums of at most 64 float32 draws are exact in double, so the mean is
+        # the exact mean, whatever order numpy adds in
+        qb = q[64 * i:64 * i + 64].astype(np.float64).mean(axis=0)
         np.testing.assert_array_equal(oracle.pool_queries(q[64 * i:64 * i + 64]), qb)
         S = []
         for j in range(i):
             kb = Kd[64 * j:64 * j + 64].reshape(4, 16, D).mean(axis=1)
-            S.append(sum(max(sc * float(kb[s] @ qb[h].astype(np.float64)) for s in range(4))
+            S.append(sum(max(sc * float(kb[s] @ qb[h]) for s in range(4))
                          for h in range(G)))
         best = sorted(sorted(range(i), key=lambda j: (-S[j], j))[:kq])
         assert res.sel[i][:len(best)].tolist() == best
@@ -482,9 +484,9 @@ def test_prefill_qblock_by_brute_force():
     full = oracle.prefill_row(q, K, V, e, 64, 16, ke, kq, sc)
     for i in (0, 1, 4, 7):
         lo, hi = 64 * i, min(64 * i + 64, N)
-        qb = q[lo:hi].astype(np.float64).mean(axis=0).astype(np.float32)
+        qb = q[lo:hi].astype(np.float64).mean(axis=0)
         S = [sum(max(sc * float(Kd[64 * j + 16 * s:64 * j + 16 * s + 16].mean(axis=0)
-                                @ qb[h].astype(np.float64)) for s in range(4))
+                                @ qb[h]) for s in range(4))
                  for h in range(G)) for j in range(i)]
         ge = sorted(range(i), key=lambda j: (-E[j], j))[:ke]
         gq = sorted((j for j in range(i) if j not in ge), key=lambda j: (-S[j], j))[:kq]
