@@ -61,13 +61,14 @@
  *            pre-exponential. nosa_sparse_decode reads them a block at a
  *            time: e_tok is 16-byte aligned, e_row_stride a multiple of 4 and
  *            at least S * (n_cand + 1) (values past n_tokens are ignored).
- * kbar       pooled keys in the KV dtype, V = 16 / element size dimensions
- *            per 16-byte vector (4 for float32, 8 for bfloat16), in quads of
- *            4 blocks: [rows][Q][D/V][16][V], Q = ceil(max_blocks / 4); the
- *            mean key of sub-block i of block j (sb = 4*j + i) is at
- *            [.][sb/16][d/V][sb%16][d%V]. bfloat16
- *            means are the exact mean rounded once to the nearest bfloat16
- *            (ties to even); float32 means are a float32 sum times 1/16.
+ * kbar       pooled keys in the pooled dtype (shape.pooled_dtype), V = 16 /
+ *            element size dimensions per 16-byte vector (4 for float32, 8 for
+ *            bfloat16), in quads of 4 blocks: [rows][Q][D/V][16][V], Q =
+ *            ceil(max_blocks / 4); the mean key of sub-block i of block j
+ *            (sb = 4*j + i) is at [.][sb/16][d/V][sb%16][d%V]. Each mean is
+ *            the sub-block's keys summed in double and rounded once to the
+ *            pooled dtype (nearest, ties to even): for bfloat16 keys the
+ *            exact mean rounded once.
  * e_blk      float32 [rows][max_blocks]: pooled eviction score per block.
  * s_q        float32 [rows][max_blocks]: query-aware score per block.
  * bitmaps    uint32 [rows][W], W = (max_blocks + 31) / 32; bit j%32 of word
@@ -108,7 +109,16 @@ enum { NOSA_DECODE_AUTO = 0, NOSA_DECODE_VALU = 1, NOSA_DECODE_MFMA = 2 };
 /* Problem shape, in the pages' terms: block size, sub-block size, budgets
  * k = k_e + k_q, and GQA groups (n_q_heads / n_kv_heads).
  * Supported: block_size 64, sub_block 16, head_dim 64 or 128, G <= 8,
- * k <= 128, max_blocks <= 4096. */
+ * k <= 128, max_blocks <= 4096.
+ * pooled_dtype: element type of the pooled keys (kbar) and of a prefill's
+ * pooled queries (qbar). The pages fix the pooling (mean inside sub-blocks,
+ * then max over the block; Methodology, "Block-Wise Implementation"), not
+ * its precision. NOSA_F32 (0, the default of a zeroed shape): the means
+ * rounded once to float32, which selects what the exact means select up to
+ * float32 rounding of the scores. NOSA_BF16 (bfloat16 KV only): the means
+ * rounded once to bfloat16, the variant for a stack that keeps pooled keys
+ * in the model's dtype; it halves the scoring reads, and it changes which
+ * blocks Gamma_q selects on a few percent of the steps of a long decode. */
 typedef struct nosa_shape {
     int32_t batch;
     int32_t n_q_heads;
@@ -122,6 +132,7 @@ typedef struct nosa_shape {
     int32_t dtype;         /* NOSA_F32 or NOSA_BF16 */
     int32_t decode_kernel; /* NOSA_DECODE_* */
     float scale;           /* logit scale; 0 means 1/sqrt(head_dim) */
+    int32_t pooled_dtype;  /* NOSA_F32 (default) or NOSA_BF16: kbar and qbar */
 } nosa_shape;
 
 /* Where the decode is. The entry points below that take `const nosa_step
@@ -135,7 +146,7 @@ typedef struct nosa_step {
 } nosa_step;
 
 /* Pool blocks [blk_begin, blk_end) of every row: kbar gets each sub-block's
- * mean key in the KV dtype (layout and rounding above), e_blk the max over the
+ * mean key in the pooled dtype (layout and rounding above), e_blk the max over the
  * block's sub-blocks of the mean per-token eviction score (Methodology,
  * "Block-Wise Implementation": mean inside sub-blocks, then max over the
  * block). Block j of row r is read from the KV buffer `kv` at block index
@@ -182,9 +193,10 @@ nosa_status nosa_ingest_tokens(const nosa_shape *shape, const void *qkv, const v
  * complete blocks, nosa_prefill_pool_queries, nosa_prefill_select,
  * nosa_prefill_attention. */
 
-/* Pooled query of every query block: qbar [n_qb][batch][Hq][D] (KV dtype,
- * n_qb = ceil(n_tokens / S)) is the mean over the block's tokens of q
- * [batch][n_tokens][Hq][D], rounded once to the KV dtype. q and qbar must be
+/* Pooled query of every query block: qbar [n_qb][batch][Hq][D] (pooled
+ * dtype, n_qb = ceil(n_tokens / S)) is the mean over the block's tokens of q
+ * [batch][n_tokens][Hq][D] (KV dtype), summed in double and rounded once to
+ * the pooled dtype. q and qbar must be
  * 16-byte aligned (NOSA_ERR_INVALID_ARGUMENT otherwise). */
 nosa_status nosa_prefill_pool_queries(const nosa_shape *shape, const void *q, int32_t n_tokens,
                                       void *qbar, void *stream);

@@ -22,6 +22,10 @@ def nosa_dtype(w: Workload) -> int:
     return L.NOSA_F32 if w.dtype == "f32" else L.NOSA_BF16
 
 
+def pooled_dtype(w: Workload) -> int:
+    return L.NOSA_BF16 if w.pooled == "bf16" else L.NOSA_F32
+
+
 def storage(x: np.ndarray, w: Workload) -> np.ndarray:
     """float32 values (already in the input dtype) -> storage array."""
     return np.ascontiguousarray(x, np.float32) if w.dtype == "f32" else synth.bf16_bits(x)
@@ -144,7 +148,8 @@ def make_layer(w: Workload, inp: GpuInputs, decode_kernel=L.NOSA_DECODE_AUTO,
                        dtype=nosa_dtype(w), kv=inp.kv_ptr, kv_row_blocks=inp.nb,
                        e_tok=inp.e_tok, offload=w.offload, decode_kernel=decode_kernel,
                        fuse_select_swap=fuse_select_swap, fuse_score=fuse_score,
-                       overlap=overlap, device_append=device_append)
+                       overlap=overlap, device_append=device_append,
+                       pooled_dtype=pooled_dtype(w))
 
 
 def bits_to_list(words: np.ndarray) -> list:

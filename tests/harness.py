@@ -21,6 +21,18 @@ from synth import Overrides, Workload
 MARGIN_REL = 1e-4
 
 
+def workload(name: str) -> Workload:
+    """A named workload; the suffix ":pbf16" selects its variant with pooled
+    keys (and pooled queries) kept in bfloat16."""
+    base, _, variant = name.partition(":")
+    w = synth.WORKLOADS[base]
+    if variant == "pbf16":
+        return w.scaled(name=base + "_pbf16", pooled="bf16")
+    if variant:
+        raise ValueError(name)
+    return w
+
+
 def scale_of(w: Workload) -> float:
     return 1.0 / math.sqrt(w.head_dim)
 
@@ -145,3 +157,44 @@ def oracle_trace(w: Workload, layer: int = 0, rows=None, steps=None, ov: Overrid
         tr.swap.update(sw)
         tr.term_scale.update(ts)
     return tr
+
+
+def trace_violations(w: Workload, tr: OracleTrace) -> list:
+    """Invariants the pages state, checked over the steps of a trace (an
+    oracle trace, or a copy with a planted mistake). Returns (kind, t, row)
+    for every breach:
+
+    readmitted  a block that left Gamma_e is back in it (strict eviction:
+                Methodology, Dual-Selection Mechanism)
+    locality    gamma(t) = |Gamma(t) & Gamma(t-1)| / k below k_e / k on a step
+                that completes no new block (Locality Guarantee)
+    overlap     Gamma_q shares a block with Gamma_e (it ranks the rest)
+    size        |Gamma_e| != min(k_e, c) or |Gamma| != min(k, c)
+    cache       after the swap the cache does not hold exactly Gamma(t)
+    fetch       the fetch list is not Gamma(t) minus the blocks cached before
+    """
+    out = []
+    for r in tr.rows:
+        evicted, prev = set(), None
+        for t in tr.steps:
+            res = tr.step[(t, r)]
+            ge, gq = set(res.gamma_e), set(res.gamma_q)
+            sel = sorted(ge | gq)
+            if ge & evicted:
+                out.append(("readmitted", t, r))
+            evicted |= set(range(res.n_cand)) - ge
+            if ge & gq:
+                out.append(("overlap", t, r))
+            if len(ge) != min(w.k_e, res.n_cand) or len(sel) != min(w.k, res.n_cand):
+                out.append(("size", t, r))
+            if prev is not None and w.n_cand(t) == w.n_cand(t - 1) and res.n_cand >= w.k:
+                if len(set(sel) & set(prev)) / w.k < w.k_e / w.k:
+                    out.append(("locality", t, r))
+            sw = tr.swap.get((t, r))
+            if sw is not None:
+                if sorted(b for b in sw.slot_block if b >= 0) != sel:
+                    out.append(("cache", t, r))
+                if sw.fetch_block != sorted(set(sel) - set(prev or [])):
+                    out.append(("fetch", t, r))
+            prev = sel
+    return out

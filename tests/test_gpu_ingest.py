@@ -17,12 +17,14 @@ def _vt_token_at(pos: int) -> int:
     return 32 * (pos // 32) + 16 * ((pos % 8) // 4) + 4 * ((pos % 32) // 8) + pos % 4
 
 
-@pytest.mark.parametrize("dtype,D,G,pos", [("bf16", 128, 4, 10), ("bf16", 128, 4, 63),
-                                           ("bf16", 64, 3, 63), ("f32", 64, 2, 63)])
-def test_ingest_outputs(dtype, D, G, pos):
+@pytest.mark.parametrize("dtype,D,G,pos,pooled", [
+    ("bf16", 128, 4, 10, "f32"), ("bf16", 128, 4, 63, "f32"), ("bf16", 64, 3, 63, "f32"),
+    ("f32", 64, 2, 63, "f32"), ("bf16", 128, 4, 63, "bf16"), ("bf16", 64, 3, 63, "bf16")])
+def test_ingest_outputs(dtype, D, G, pos, pooled):
     """One launch: q split and the K/V slot bit for bit, the eviction logit
     within float32 summation error of the double sum, and (pos 63) the block's
-    pooled keys bit for bit and its pooled eviction score."""
+    pooled keys bit for bit (the oracle's exact means rounded once to the
+    pooled dtype) and its pooled eviction score."""
     import oracle
     gh = _gpu()
     from trainable_block_sparse_nosa_amd import _lib as L
@@ -54,10 +56,12 @@ def test_ingest_outputs(dtype, D, G, pos):
     kv = dev(conv(kv_host))
     q_out = torch.zeros(B, Hq, D, dtype=kv.dtype, device="cuda")
     e_dev = torch.from_numpy(e_tok).cuda()
-    V8 = 16 // (4 if dtype == "f32" else 2)
-    kbar = torch.zeros(rows, nb // 4, D // V8, 16, V8, dtype=kv.dtype, device="cuda")
+    V8 = 16 // (4 if pooled == "f32" else 2)
+    kbar = torch.zeros(rows, nb // 4, D // V8, 16, V8,
+                       dtype=torch.float32 if pooled == "f32" else torch.bfloat16, device="cuda")
     e_blk = torch.zeros(rows, nb, dtype=torch.float32, device="cuda")
-    shape = L.make_shape(B, Hq, Hkv, D, 2, 2, nb, L.NOSA_F32 if dtype == "f32" else L.NOSA_BF16)
+    shape = L.make_shape(B, Hq, Hkv, D, 2, 2, nb, L.NOSA_F32 if dtype == "f32" else L.NOSA_BF16,
+                         pooled_dtype=L.NOSA_F32 if pooled == "f32" else L.NOSA_BF16)
     L.nosa_ingest_tokens(shape, dev(conv(qkv)), dev(conv(x)), dev(conv(W)),
                          torch.from_numpy(bias).cuda(), hidden, tok + 1, q_out, kv, nb, j, e_dev,
                          nb * 64, kbar, e_blk)
@@ -82,11 +86,9 @@ def test_ingest_outputs(dtype, D, G, pos):
             if pos == 63:
                 Kfull = K[r].copy()
                 Kfull[63] = k[g]
-                ref = oracle.pool_keys(Kfull, 64, 16, 0, pooled_bf16=dtype == "bf16")
-                if dtype == "bf16":
-                    np.testing.assert_array_equal(kb[r, 4 * j:4 * j + 4], ref)
-                else:
-                    np.testing.assert_allclose(kb[r, 4 * j:4 * j + 4], ref, rtol=0, atol=2e-6)
+                ref = oracle.pool_keys(Kfull, 64, 16, 0, pooled_bf16=pooled == "bf16")
+                # float32 pooled keys: the exact mean rounded once to float32
+                np.testing.assert_array_equal(kb[r, 4 * j:4 * j + 4], ref.astype(np.float32))
                 e_blockrow = e_tok[r, 64 * j:64 * j + 64].copy()
                 e_blockrow[63] = np.float32(e_ref)
                 assert abs(got_eb[r, j] - oracle.block_evict(e_blockrow, 64, 16, 0)) <= 2e-6

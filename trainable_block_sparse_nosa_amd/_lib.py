@@ -53,7 +53,8 @@ class NosaError(RuntimeError):
 class nosa_shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "block_size", "sub_block", "k_e", "k_q",
-        "max_blocks", "dtype", "decode_kernel")] + [("scale", ctypes.c_float)]
+        "max_blocks", "dtype", "decode_kernel")] + [("scale", ctypes.c_float),
+                                                     ("pooled_dtype", ctypes.c_int32)]
 
 
 class nosa_step(ctypes.Structure):
@@ -146,9 +147,10 @@ def _chk(fn: str, status: int):
 
 
 def make_shape(batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks, dtype,
-               block_size=64, sub_block=16, decode_kernel=NOSA_DECODE_AUTO, scale=0.0) -> nosa_shape:
+               block_size=64, sub_block=16, decode_kernel=NOSA_DECODE_AUTO, scale=0.0,
+               pooled_dtype=NOSA_F32) -> nosa_shape:
     return nosa_shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, sub_block, k_e, k_q,
-                      max_blocks, dtype, decode_kernel, scale)
+                      max_blocks, dtype, decode_kernel, scale, pooled_dtype)
 
 
 def make_step(n_tokens: int, n_cand_prev: int) -> nosa_step:

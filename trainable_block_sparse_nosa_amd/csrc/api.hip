@@ -31,6 +31,9 @@ nosa_status make_dims(const nosa_shape *s, Dims *dm) {
     if (s->decode_kernel < NOSA_DECODE_AUTO || s->decode_kernel > NOSA_DECODE_MFMA)
         return NOSA_ERR_INVALID_ARGUMENT;
     if (!(s->scale >= 0.f) || isinf(s->scale)) return NOSA_ERR_INVALID_ARGUMENT;
+    if (s->pooled_dtype != NOSA_F32 && s->pooled_dtype != NOSA_BF16)
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (s->pooled_dtype == NOSA_BF16 && s->dtype != NOSA_BF16) return NOSA_ERR_UNSUPPORTED;
     const int G = s->n_q_heads / s->n_kv_heads;
     if (s->block_size != 64 || s->sub_block != 16) return NOSA_ERR_UNSUPPORTED;
     if (s->head_dim != 64 && s->head_dim != 128) return NOSA_ERR_UNSUPPORTED;
@@ -52,6 +55,7 @@ nosa_status make_dims(const nosa_shape *s, Dims *dm) {
     dm->W = (s->max_blocks + 31) / 32;
     dm->rows = s->batch * s->n_kv_heads;
     dm->dtype = s->dtype;
+    dm->pdtype = s->pooled_dtype;
     dm->scale = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
     return NOSA_OK;
 }
@@ -70,6 +74,17 @@ template <typename F> nosa_status by_type_dim(const Dims &dm, F &&f) {
         return f((float *)nullptr, std::integral_constant<int, 64>{});
     if (dm.D == 64) return f((bf16_t *)nullptr, std::integral_constant<int, 64>{});
     return f((bf16_t *)nullptr, std::integral_constant<int, 128>{});
+}
+
+// f(T *, TK *, D): KV dtype, pooled dtype (kbar, qbar) and head dim.
+template <typename F> nosa_status by_types(const Dims &dm, F &&f) {
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        if constexpr (std::is_same_v<T, bf16_t>) {
+            if (dm.pdtype == NOSA_BF16) return f(tp, (bf16_t *)nullptr, dc);
+        }
+        return f(tp, (float *)nullptr, dc);
+    });
 }
 
 template <typename F> nosa_status by_group(const Dims &dm, F &&f) {
@@ -177,9 +192,10 @@ nosa_status nosa_pool_blocks(const nosa_shape *shape, const void *kv, int64_t kv
         e_row_stride < (int64_t)blk_end * dm.S)
         return NOSA_ERR_INVALID_ARGUMENT;
     if (blk_end == blk_begin) return NOSA_OK;
-    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+    return by_types(dm, [&](auto tp, auto tk, auto dc) -> nosa_status {
         using T = std::remove_pointer_t<decltype(tp)>;
-        return hip_status(launch_pool<T, decltype(dc)::value>(
+        using TK = std::remove_pointer_t<decltype(tk)>;
+        return hip_status(launch_pool<T, TK, decltype(dc)::value>(
             dm, kv, kv_row_blocks, kv_first_block, e_tok, e_row_stride, blk_begin, blk_end, kbar,
             e_blk, (hipStream_t)stream));
     });
@@ -194,12 +210,13 @@ nosa_status nosa_score_blocks(const nosa_shape *shape, const void *q, const void
     const int n_cand = step_cand(dm, step);
     if (n_cand < 0) return NOSA_ERR_INVALID_ARGUMENT;
     if (n_cand == 0) return NOSA_OK;
-    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+    return by_types(dm, [&](auto tp, auto tk, auto dc) -> nosa_status {
         using T = std::remove_pointer_t<decltype(tp)>;
+        using TK = std::remove_pointer_t<decltype(tk)>;
         constexpr int D = decltype(dc)::value;
         return by_group(dm, [&](auto gc) -> nosa_status {
-            return hip_status(launch_score<T, D, decltype(gc)::value>(dm, q, kbar, n_cand, s_q,
-                                                                       (hipStream_t)stream));
+            return hip_status(launch_score<T, TK, D, decltype(gc)::value>(
+                dm, q, kbar, n_cand, s_q, (hipStream_t)stream));
         });
     });
 }
@@ -279,11 +296,12 @@ nosa_status nosa_score_select(const nosa_shape *shape, const void *q, const void
     const int n_cand = step_cand(dm, step);
     if (n_cand < 0) return NOSA_ERR_INVALID_ARGUMENT;
     const SwapPtrs sw{slot_block, block_slot, fetch_block, fetch_slot, n_fetch, counters};
-    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+    return by_types(dm, [&](auto tp, auto tk, auto dc) -> nosa_status {
         using T = std::remove_pointer_t<decltype(tp)>;
+        using TK = std::remove_pointer_t<decltype(tk)>;
         constexpr int D = decltype(dc)::value;
         return by_group(dm, [&](auto gc) -> nosa_status {
-            return hip_status(launch_score_select<T, D, decltype(gc)::value>(
+            return hip_status(launch_score_select<T, TK, D, decltype(gc)::value>(
                 dm, q, kbar, s_q, e_blk, n_cand, step->n_cand_prev, ge_bits, ev_bits, sel, n_sel,
                 sel_bits, all_swap ? &sw : nullptr, (hipStream_t)stream));
         });
@@ -336,11 +354,12 @@ nosa_status nosa_ingest_tokens(const nosa_shape *shape, const void *qkv, const v
     if (hidden <= 0 || n_tokens <= 0 || kv_row_blocks <= 0 || block < 0 ||
         block >= kv_row_blocks || e_row_stride < n_tokens || tok / dm.S >= dm.max_blocks)
         return NOSA_ERR_INVALID_ARGUMENT;
-    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+    return by_types(dm, [&](auto tp, auto tk, auto dc) -> nosa_status {
         using T = std::remove_pointer_t<decltype(tp)>;
+        using TK = std::remove_pointer_t<decltype(tk)>;
         constexpr int D = decltype(dc)::value;
         return by_group(dm, [&](auto gc) -> nosa_status {
-            return hip_status(launch_ingest<T, D, decltype(gc)::value>(
+            return hip_status(launch_ingest<T, TK, D, decltype(gc)::value>(
                 dm, qkv, x, w_evict, b_evict, hidden, tok, q_out, kv, kv_row_blocks, block, e_tok,
                 e_row_stride, kbar, e_blk, (hipStream_t)stream));
         });
@@ -356,10 +375,12 @@ nosa_status nosa_prefill_pool_queries(const nosa_shape *shape, const void *q, in
     // the kernel reads and writes 16-byte vectors
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(qbar)) & 15)
         return NOSA_ERR_INVALID_ARGUMENT;
-    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+    return by_types(dm, [&](auto tp, auto tk, auto dc) -> nosa_status {
         using T = std::remove_pointer_t<decltype(tp)>;
+        using TK = std::remove_pointer_t<decltype(tk)>;
         constexpr int D = decltype(dc)::value;
-        return hip_status(launch_pool_queries<T, D>(dm, q, n_tokens, qbar, (hipStream_t)stream));
+        return hip_status(
+            launch_pool_queries<T, TK, D>(dm, q, n_tokens, qbar, (hipStream_t)stream));
     });
 }
 
@@ -373,11 +394,12 @@ nosa_status nosa_prefill_select(const nosa_shape *shape, const void *qbar, const
         return NOSA_ERR_INVALID_ARGUMENT;
     const int nqb = (n_tokens + dm.S - 1) / dm.S;
     if (nqb - 1 >= dm.max_blocks || nqb > 65535) return NOSA_ERR_INVALID_ARGUMENT;
-    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+    return by_types(dm, [&](auto tp, auto tk, auto dc) -> nosa_status {
         using T = std::remove_pointer_t<decltype(tp)>;
+        using TK = std::remove_pointer_t<decltype(tk)>;
         constexpr int D = decltype(dc)::value;
         return by_group(dm, [&](auto gc) -> nosa_status {
-            return hip_status(launch_prefill_select<T, D, decltype(gc)::value>(
+            return hip_status(launch_prefill_select<T, TK, D, decltype(gc)::value>(
                 dm, qbar, kbar, e_blk, nqb, sel, n_sel, (hipStream_t)stream));
         });
     });
@@ -580,9 +602,10 @@ nosa_status nosa_pool_step(const nosa_shape *shape, const void *kv, int64_t kv_r
     if (!kv || !e_tok || !kbar || !e_blk || !step_dev) return NOSA_ERR_INVALID_ARGUMENT;
     if (kv_row_blocks < dm.max_blocks || e_row_stride < (int64_t)dm.max_blocks * dm.S)
         return NOSA_ERR_INVALID_ARGUMENT;
-    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+    return by_types(dm, [&](auto tp, auto tk, auto dc) -> nosa_status {
         using T = std::remove_pointer_t<decltype(tp)>;
-        return hip_status(launch_pool_step<T, decltype(dc)::value>(
+        using TK = std::remove_pointer_t<decltype(tk)>;
+        return hip_status(launch_pool_step<T, TK, decltype(dc)::value>(
             dm, kv, kv_row_blocks, e_tok, e_row_stride,
             reinterpret_cast<const int32_t *>(step_dev), kbar, e_blk, (hipStream_t)stream));
     });
@@ -622,11 +645,12 @@ nosa_status nosa_score_select_step(const nosa_shape *shape, const void *q, const
     const bool all_swap = slot_block && block_slot && fetch_block && fetch_slot && n_fetch && counters;
     if (any_swap && !all_swap) return NOSA_ERR_INVALID_ARGUMENT;
     const SwapPtrs sw{slot_block, block_slot, fetch_block, fetch_slot, n_fetch, counters};
-    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+    return by_types(dm, [&](auto tp, auto tk, auto dc) -> nosa_status {
         using T = std::remove_pointer_t<decltype(tp)>;
+        using TK = std::remove_pointer_t<decltype(tk)>;
         constexpr int D = decltype(dc)::value;
         return by_group(dm, [&](auto gc) -> nosa_status {
-            return hip_status(launch_score_select<T, D, decltype(gc)::value>(
+            return hip_status(launch_score_select<T, TK, D, decltype(gc)::value>(
                 dm, q, kbar, s_q, e_blk, 0, -1, ge_bits, ev_bits, sel, n_sel, sel_bits,
                 all_swap ? &sw : nullptr, (hipStream_t)stream,
                 reinterpret_cast<const int32_t *>(step_dev)));

@@ -17,6 +17,7 @@ struct Dims {
     int max_blocks, W;  // per-row block capacity, bitmap words per row
     int rows;
     int dtype;
+    int pdtype;  // pooled dtype (kbar, qbar): NOSA_F32 or NOSA_BF16
     float scale;
 };
 

@@ -5,22 +5,26 @@
 
 namespace nosa {
 
-template <typename T, int D>
+// Template parameters: T is the KV dtype (q, K, V, out), TK the pooled dtype
+// (kbar, and the pooled queries of a prefill): float32, or bfloat16 with
+// bfloat16 KV.
+template <typename T, typename TK, int D>
 hipError_t launch_pool(const Dims &dm, const void *kv, int64_t kv_row_blocks, int kv_first,
                        const float *e_tok, int64_t e_stride, int blk_begin, int blk_end,
                        void *kbar, float *e_blk, hipStream_t st);
 // Pool the block completed at the device step, if any (candidates went from
 // n_cand_prev >= 0 to n_cand_prev + 1): block j of kv's rows (the full KV).
-template <typename T, int D>
+template <typename T, typename TK, int D>
 hipError_t launch_pool_step(const Dims &dm, const void *kv, int64_t kv_row_blocks,
                             const float *e_tok, int64_t e_stride, const int32_t *dstep,
                             void *kbar, float *e_blk, hipStream_t st);
 hipError_t launch_step_advance(const Dims &dm, int32_t *dstep, hipStream_t st);
 
-// Block scores of candidates 0..n_cand-1 into s_q: bf16 on the matrix cores
-// over a grid split along each row's candidates (dstep: n_cand from the
-// device step record, the grid sized for the capacity); float32 on the VALU.
-template <typename T, int D, int G>
+// Block scores of candidates 0..n_cand-1 into s_q over a grid split along
+// each row's candidates (dstep: n_cand from the device step record, the grid
+// sized for the capacity): bfloat16 pooled keys on the matrix cores, float32
+// pooled keys on the VALU.
+template <typename T, typename TK, int D, int G>
 hipError_t launch_score(const Dims &dm, const void *q, const void *kbar, int n_cand, float *s_q,
                         hipStream_t st, const int32_t *dstep = nullptr);
 
@@ -41,12 +45,12 @@ hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, i
                          hipStream_t st);
 
 // Scores and selection (and the set difference when swap != nullptr): with
-// bf16 and at most SPLIT_SCORE_MAX_ROWS rows, the scores come from a grid
+// bf16 KV and at most SPLIT_SCORE_MAX_ROWS rows, the scores come from a grid
 // split over each row's candidates into s_q and a second launch selects from
 // them; otherwise the selecting workgroup (one per row) computes its row's
 // scores itself, writing them to s_q as well. dstep != nullptr: n_cand and
 // n_prev come from the device step record.
-template <typename T, int D, int G>
+template <typename T, typename TK, int D, int G>
 hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, float *s_q,
                                const float *e_blk, int n_cand, int n_prev, uint32_t *ge,
                                uint32_t *ev, int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
@@ -55,7 +59,7 @@ hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, 
 
 // Selection of every query block i < n_qb of a sequence (candidates 0..i-1,
 // no previous step) in one launch: sel [n_qb][rows][k], n_sel [n_qb][rows].
-template <typename T, int D, int G>
+template <typename T, typename TK, int D, int G>
 hipError_t launch_prefill_select(const Dims &dm, const void *qbar, const void *kbar,
                                  const float *e_blk, int n_qb, int32_t *sel, int32_t *n_sel,
                                  hipStream_t st);
@@ -63,7 +67,7 @@ hipError_t launch_prefill_select(const Dims &dm, const void *qbar, const void *k
 hipError_t launch_swap(const Dims &dm, const int32_t *sel, const int32_t *n_sel,
                        const uint32_t *sel_bits, const SwapPtrs &swap, hipStream_t st);
 
-template <typename T, int D, int G>
+template <typename T, typename TK, int D, int G>
 hipError_t launch_ingest(const Dims &dm, const void *qkv, const void *x, const void *w_e,
                          const float *b_e, int hidden, int tok, void *q_out, void *kv,
                          int64_t kv_row_blocks, int block, float *e_tok, int64_t e_stride,
@@ -126,7 +130,8 @@ hipError_t launch_decode_valu(const Dims &dm, const DecodePlan &pl, const Decode
 template <int D, int G>
 hipError_t launch_decode_mfma(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
                               hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
-template <typename T, int D>
+// qbar in the pooled dtype TK.
+template <typename T, typename TK, int D>
 hipError_t launch_pool_queries(const Dims &dm, const void *q, int n_tokens, void *qbar,
                                hipStream_t st);
 template <int D, int G>

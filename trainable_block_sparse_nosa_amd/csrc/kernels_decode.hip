@@ -239,13 +239,40 @@ __device__ __forceinline__ void attend_block(const BlockRegs<D> &br, const bf16x
     l_run = l_run * alpha + ps;
     m_run = m_new;
     // O^T tile dt: lane holds dims 16dt + 4grp + u for head col
+    if (lim >= 64) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            o[dt] *= alpha;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(br.v[dt][s], phi[s], o[dt], 0, 0, 0);
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(br.v[dt][s], plo[s], o[dt], 0, 0, 0);
+            }
+        }
+        return;
+    }
+    // a partly filled block (the newest): the value slots of tokens from lim
+    // on hold whatever the buffer held before, possibly not finite, and a
+    // zero weight times a NaN or an infinity is a NaN; they enter as zeros.
+    // Element i of the lane's operand for token half s is stored position
+    // 32s + 8grp + i; a 32-bit mask per element pair keeps the live ones.
+    u32x4 keep[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int p0 = 32 * s + 8 * grp + 2 * j;
+            keep[s][j] = (vt_token_at(p0) < lim ? 0x0000FFFFu : 0u) |
+                         (vt_token_at(p0 + 1) < lim ? 0xFFFF0000u : 0u);
+        }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
         o[dt] *= alpha;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(br.v[dt][s], phi[s], o[dt], 0, 0, 0);
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(br.v[dt][s], plo[s], o[dt], 0, 0, 0);
+            const bf16x8 v = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, br.v[dt][s]) & keep[s]);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, phi[s], o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, plo[s], o[dt], 0, 0, 0);
         }
     }
 }
@@ -352,11 +379,11 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
 // Prefill (training-time forward) with the selection per query block.
 //
 // Pooled queries: qbar[i][b][hq][d] = mean of q[b][64 i + u][hq][d] over the
-// query block's tokens, in the input dtype (exact mean rounded once).
+// query block's tokens, in the pooled dtype TK (exact mean rounded once).
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, typename TK, int D>
 __global__ void __launch_bounds__(256)
-pool_queries_kernel(Dims dm, const T *__restrict__ q, int n_tokens, T *__restrict__ qbar) {
+pool_queries_kernel(Dims dm, const T *__restrict__ q, int n_tokens, TK *__restrict__ qbar) {
     // one workgroup per (query block i, sequence b); thread t owns the
     // 16-byte vectors t, t + 256, ... of a token's Hq * D elements and sums
     // each element over the block's tokens in order, in double (exact for
@@ -367,7 +394,7 @@ pool_queries_kernel(Dims dm, const T *__restrict__ q, int n_tokens, T *__restric
     const int64_t tok = (int64_t)dm.Hq * D;  // elements per token
     const int nv = (int)(tok / EV);
     const T *qb = q + ((int64_t)b * n_tokens + lo) * tok;
-    T *ob = qbar + ((int64_t)i * dm.B + b) * tok;
+    TK *ob = qbar + ((int64_t)i * dm.B + b) * tok;
     for (int v = threadIdx.x; v < nv; v += blockDim.x) {
         double s[EV];
 #pragma unroll
@@ -391,7 +418,7 @@ pool_queries_kernel(Dims dm, const T *__restrict__ q, int n_tokens, T *__restric
 #pragma unroll
         for (int e = 0; e < EV; ++e) {
             const double mean = s[e] / (double)n;
-            if constexpr (std::is_same_v<T, float>) ob[(int64_t)v * EV + e] = (float)mean;
+            if constexpr (std::is_same_v<TK, float>) ob[(int64_t)v * EV + e] = (float)mean;
             else ob[(int64_t)v * EV + e] = bf16_rne_from_double(mean);
         }
     }
@@ -511,7 +538,9 @@ __device__ __forceinline__ void prefill_store(PrefillTile<D> &tl, const PrefillS
 // the base-2 domain: z2 = log2(e) (scale q.k + e). The block's eviction
 // scores arrive already multiplied by log2(e). CAUSAL masks, per column, the
 // tokens from lim[c] on (the own block); the other blocks are whole. P
-// enters P V as bf16 (the outputs are bf16), its row sums stay in float32.
+// enters P V as a bf16 hi + lo pair (about 16 significant bits: when a few
+// tokens dominate a softmax, one bf16 rounding of their weights would show
+// in the output), and the denominator sums the same pair.
 // Max of v over the four rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48) on
 // the gfx950 row-swap instructions: with both operands holding v, each lane
 // of the swapped pair holds v at its own lane and at the lane 16 (32) away.
@@ -548,7 +577,7 @@ __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
     f32x4 ev[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) ev[t] = *reinterpret_cast<const f32x4 *>(&tl.e[16 * t + 4 * grp]);
-    bf16x8 pb[CT][2];
+    bf16x8 ph[CT][2], pl[CT][2];
     float alpha[CT];
     bool rescale = false;
 #pragma unroll
@@ -578,8 +607,12 @@ __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                pb[c][t / 2][(t % 2) * 4 + u] = (__bf16)__builtin_amdgcn_exp2f(z[t][u] - m_sub);
+            for (int u = 0; u < 4; ++u) {
+                const float p = __builtin_amdgcn_exp2f(z[t][u] - m_sub);
+                const __bf16 hi = (__bf16)p;
+                ph[c][t / 2][(t % 2) * 4 + u] = hi;
+                pl[c][t / 2][(t % 2) * 4 + u] = (__bf16)(p - (float)hi);
+            }
         m_run[c] = m_new;
     }
     // most blocks move no column's maximum: skip the rescale then
@@ -592,14 +625,17 @@ __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
         }
     }
     // the denominator on the matrix cores: an all-ones A operand sums the
-    // column of P^T (the same bf16 probabilities P.V uses) into every row of
+    // column of P^T (the same hi + lo pair P.V uses) into every row of
     // l_run[c], rescaled with O above
     const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
-        l_run[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[c][0], l_run[c], 0, 0, 0);
-        l_run[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[c][1], l_run[c], 0, 0, 0);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            l_run[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ph[c][s2], l_run[c], 0, 0, 0);
+            l_run[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl[c][s2], l_run[c], 0, 0, 0);
+        }
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -607,8 +643,10 @@ __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
         const bf16x8 v1 = tl.frag[4 * KS + 2 * dt + 1][lane];
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb[c][0], o[c][dt], 0, 0, 0);
-            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pb[c][1], o[c][dt], 0, 0, 0);
+            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, ph[c][0], o[c][dt], 0, 0, 0);
+            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pl[c][0], o[c][dt], 0, 0, 0);
+            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, ph[c][1], o[c][dt], 0, 0, 0);
+            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pl[c][1], o[c][dt], 0, 0, 0);
         }
     }
 }
@@ -722,21 +760,23 @@ prefill_mfma_kernel(Dims dm, PrefillArgs a) {
     }
 }
 
-template <typename T, int D>
+template <typename T, typename TK, int D>
 hipError_t launch_pool_queries(const Dims &dm, const void *q, int n_tokens, void *qbar,
                                hipStream_t st) {
     const int nqb = (n_tokens + 63) / 64;
     if (nqb == 0) return hipSuccess;
-    hipLaunchKernelGGL((pool_queries_kernel<T, D>), dim3(nqb, dm.B), dim3(256), 0, st, dm,
-                       static_cast<const T *>(q), n_tokens, static_cast<T *>(qbar));
+    hipLaunchKernelGGL((pool_queries_kernel<T, TK, D>), dim3(nqb, dm.B), dim3(256), 0, st, dm,
+                       static_cast<const T *>(q), n_tokens, static_cast<TK *>(qbar));
     return hipGetLastError();
 }
-template hipError_t launch_pool_queries<float, 64>(const Dims &, const void *, int, void *,
-                                                   hipStream_t);
-template hipError_t launch_pool_queries<bf16_t, 64>(const Dims &, const void *, int, void *,
-                                                    hipStream_t);
-template hipError_t launch_pool_queries<bf16_t, 128>(const Dims &, const void *, int, void *,
-                                                     hipStream_t);
+#define NOSA_POOLQ_INST(T, TK, D)                                                              \
+    template hipError_t launch_pool_queries<T, TK, D>(const Dims &, const void *, int, void *, \
+                                                      hipStream_t);
+NOSA_POOLQ_INST(float, float, 64)
+NOSA_POOLQ_INST(bf16_t, float, 64)
+NOSA_POOLQ_INST(bf16_t, float, 128)
+NOSA_POOLQ_INST(bf16_t, bf16_t, 64)
+NOSA_POOLQ_INST(bf16_t, bf16_t, 128)
 
 template <int D, int G>
 hipError_t launch_prefill(const Dims &dm, const void *q, int n_tokens, const void *kv,
@@ -808,8 +848,19 @@ decode_valu_kernel(Dims dm, DecodeArgs a) {
         }
         for (int v = tid; v < KV_VEC; v += 256) {
             const int row = v / (S / EPV), c = (v % (S / EPV)) * EPV;
-            *reinterpret_cast<uint4 *>(Vs + row * VP + c) =
-                reinterpret_cast<const uint4 *>(blk + S * D)[v];
+            uint4 x = reinterpret_cast<const uint4 *>(blk + S * D)[v];
+            if (valid < S) {
+                // value slots of tokens from `valid` on (a partly filled
+                // block) may hold anything; a zero weight times a NaN is a
+                // NaN, so they enter as zeros
+                T el[EPV];
+                __builtin_memcpy(el, &x, sizeof(x));
+#pragma unroll
+                for (int m = 0; m < EPV; ++m)
+                    if (vt_token_at(c + m) >= valid) el[m] = T{};
+                __builtin_memcpy(&x, el, sizeof(x));
+            }
+            *reinterpret_cast<uint4 *>(Vs + row * VP + c) = x;
         }
         __syncthreads();
 

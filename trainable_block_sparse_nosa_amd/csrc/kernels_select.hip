@@ -11,13 +11,15 @@
 namespace nosa {
 
 // ---------------------------------------------------------------------------
-// Pooled keys are stored in the KV dtype T, V = 16 / sizeof(T) dimensions per
-// 16-byte vector, grouped by quads of blocks (16 sub-blocks):
-// kbar[row][Q][D/V][16][V], Q = ceil(max_blocks / 4); sub-block sb = 4 j + i
-// of block j is slot sb % 16 of quad sb / 16. A quad is 16 * D elements in one
-// piece, laid out as the A operand tiles of a 16 x 16 x 32 MFMA want them: one
-// load instruction of a wave (16 sub-blocks x 4 dimension vectors) reads 1 KiB
-// contiguous.
+// Pooled keys are stored in the pooled dtype TK (float32 by default: the
+// exact sub-block means rounded once; bfloat16 for the model-dtype variant),
+// V = 16 / sizeof(TK) dimensions per 16-byte vector, grouped by quads of
+// blocks (16 sub-blocks): kbar[row][Q][D/V][16][V], Q = ceil(max_blocks / 4);
+// sub-block sb = 4 j + i of block j is slot sb % 16 of quad sb / 16. A quad is
+// 16 * D elements in one piece: for bfloat16 laid out as the A operand tiles
+// of a 16 x 16 x 32 MFMA want them (one load instruction of a wave, 16
+// sub-blocks x 4 dimension vectors, reads 1 KiB contiguous); for float32 a
+// wave's 64 lanes (one sub-block each) read 4 pieces of 256 B per load.
 // ---------------------------------------------------------------------------
 template <typename T> struct KbarVec;
 template <> struct KbarVec<float> {
@@ -55,39 +57,39 @@ __device__ __forceinline__ int64_t kbar_vec(const Dims &dm, int r, int sb, int d
     return (((int64_t)r * quads + (sb >> 4)) * (D / V) + dv) * (16 * V) + (int64_t)(sb & 15) * V;
 }
 
-// Sub-block mean of 16 keys in the storage type, key u from get(u): float32
-// keys sum in float32; bfloat16 keys sum exactly in double (16 values with 8
-// significant bits) and the exact mean is rounded once to bfloat16. Tokens
-// are summed in order, so every caller gets identical bits.
-template <typename T, typename Get>
-__device__ __forceinline__ T pooled_mean_of(Get get) {
-    if constexpr (std::is_same_v<T, float>) {
-        float s = 0.f;
+// Sub-block mean of 16 keys of type T (key u from get(u)) in the pooled type
+// TK: the keys are summed in order in double (exact for bfloat16 keys, 16
+// values with 8 significant bits; for float32 keys within one rounding of
+// double) and the mean is rounded once, to the nearest float32 or to the
+// nearest bfloat16. Every caller gets identical bits.
+template <typename T> __device__ __forceinline__ double dbl(T v);
+template <> __device__ __forceinline__ double dbl<float>(float v) { return (double)v; }
+template <> __device__ __forceinline__ double dbl<bf16_t>(bf16_t v) { return (double)bf2f(v); }
+
+template <typename T, typename TK, typename Get>
+__device__ __forceinline__ TK pooled_mean_of(Get get) {
+    double s = 0.0;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) s += get(u);
-        return s * (1.0f / 16);
-    } else {
-        double s = 0.0;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) s += (double)bf2f(get(u));
-        return bf16_rne_from_double(s * (1.0 / 16));
-    }
+    for (int u = 0; u < 16; ++u) s += dbl<T>(get(u));
+    const double mean = s * (1.0 / 16);
+    if constexpr (std::is_same_v<TK, float>) return (float)mean;
+    else return bf16_rne_from_double(mean);
 }
-template <typename T>
-__device__ __forceinline__ T pooled_mean(const T *k, int stride) {
-    return pooled_mean_of<T>([&](int u) { return k[u * stride]; });
+template <typename T, typename TK>
+__device__ __forceinline__ TK pooled_mean(const T *k, int stride) {
+    return pooled_mean_of<T, TK>([&](int u) { return k[u * stride]; });
 }
 
 // ---------------------------------------------------------------------------
 // Pool: one workgroup per (block, row). Sub-block means of the keys go to the
 // kbar layout above; the eviction scores get mean-then-max pooling.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, typename TK, int D>
 __global__ void __launch_bounds__(256)
 pool_kernel(Dims dm, const T *__restrict__ kv, int64_t kv_row_blocks, int kv_first,
             const float *__restrict__ e_tok, int64_t e_stride, int blk_begin,
-            T *__restrict__ kbar, float *__restrict__ e_blk, const int32_t *__restrict__ dstep) {
-    constexpr int S = 64, SUB = 16, M = S / SUB, V = KbarVec<T>::V;
+            TK *__restrict__ kbar, float *__restrict__ e_blk, const int32_t *__restrict__ dstep) {
+    constexpr int S = 64, SUB = 16, M = S / SUB, V = KbarVec<TK>::V;
     static_assert(SUB == 16, "pooled_mean sums 16 tokens");
     __shared__ float emean[M];
     const int r = blockIdx.y;
@@ -101,8 +103,8 @@ pool_kernel(Dims dm, const T *__restrict__ kv, int64_t kv_row_blocks, int kv_fir
     const T *K = kv + ((int64_t)r * kv_row_blocks + src) * (int64_t)(2 * S * D);
     for (int p = threadIdx.x; p < M * D; p += blockDim.x) {
         const int i = p / D, d = p % D;
-        kbar[kbar_vec<T, D>(dm, r, M * j + i, d / V) + (d % V)] =
-            pooled_mean<T>(K + (i * SUB) * D + d, D);
+        kbar[kbar_vec<TK, D>(dm, r, M * j + i, d / V) + (d % V)] =
+            pooled_mean<T, TK>(K + (i * SUB) * D + d, D);
     }
     if (threadIdx.x < M) {
         const float *e = e_tok + (int64_t)r * e_stride + (int64_t)j * S + threadIdx.x * SUB;
@@ -121,25 +123,30 @@ pool_kernel(Dims dm, const T *__restrict__ kv, int64_t kv_row_blocks, int kv_fir
 }
 
 // ---------------------------------------------------------------------------
-// Score: lane <-> sub-block. Each lane walks the head dimension one 16-byte
-// vector at a time; a wave's loads cover 64 consecutive sub-blocks (1 KiB).
-// The group's G dot products stay in registers; the block max over the 4
-// sub-blocks is a DPP quad reduction, then the heads are summed.
+// Score on the VALU (float32 pooled keys): lane <-> sub-block. Each lane walks
+// the head dimension one 16-byte vector at a time; a wave's loads cover 64
+// consecutive sub-blocks. The group's G dot products stay in registers
+// (float32 FMAs of the queries, of type TQ, and the pooled keys, of type TK);
+// the block max over the 4 sub-blocks is a DPP quad reduction, then the heads
+// are summed. With dstep, n_cand comes from the step record (the grid covers
+// the capacity; workgroups past the candidates exit at once).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int G>
+template <typename TQ, typename TK, int D, int G>
 __global__ void __launch_bounds__(256)
-score_kernel(Dims dm, const T *__restrict__ q, const T *__restrict__ kbar, int n_cand,
-             float *__restrict__ s_q) {
-    constexpr int M = 4, V = KbarVec<T>::V;
+score_kernel(Dims dm, const TQ *__restrict__ q, const TK *__restrict__ kbar, int n_cand,
+             float *__restrict__ s_q, const int32_t *__restrict__ dstep) {
+    constexpr int M = 4, V = KbarVec<TK>::V;
+    if (dstep) n_cand = read_step(dstep, dm).n_cand;
+    const int nsb = M * n_cand;
+    if ((int)(blockIdx.x * blockDim.x) >= nsb) return;
     __shared__ float qs[G][D];
     const int r = blockIdx.y;
     const int b = r / dm.Hkv, g = r % dm.Hkv;
-    const T *qr = q + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
+    const TQ *qr = q + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
     for (int p = threadIdx.x; p < G * D; p += blockDim.x)
         (&qs[0][0])[p] = ldf(qr + p) * dm.scale;
     __syncthreads();
 
-    const int nsb = M * n_cand;
     const int sb = blockIdx.x * blockDim.x + threadIdx.x;
     float acc[G];
 #pragma unroll
@@ -148,7 +155,7 @@ score_kernel(Dims dm, const T *__restrict__ q, const T *__restrict__ kbar, int n
 #pragma unroll 8
         for (int dv = 0; dv < D / V; ++dv) {
             float x[V];
-            KbarVec<T>::load(kbar + kbar_vec<T, D>(dm, r, sb, dv), x);
+            KbarVec<TK>::load(kbar + kbar_vec<TK, D>(dm, r, sb, dv), x);
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -496,19 +503,19 @@ struct ScoresGlobal {
 // sub-block, U sub-blocks per thread per pass with all their 16-byte loads in
 // flight, DPP quad max over a block's sub-blocks, then the head sum. Needs the
 // whole workgroup (barriers inside).
-template <typename T, int D, int G>
+template <typename TQ, typename TK, int D, int G>
 struct ScoresFused {
-    const T *q;
-    const T *kbar;
+    const TQ *q;
+    const TK *kbar;
     float *s_q;          // may be null: scores stay in LDS
     int64_t q_step = 0;  // query offset per workgroup row y (batched selections)
     __device__ const float *row(const Dims &dm, int r, int n_cand) const {
-        constexpr int M = 4, V = KbarVec<T>::V, NV = D / V, U = sizeof(T) == 2 ? 2 : 1;
+        constexpr int M = 4, V = KbarVec<TK>::V, NV = D / V, U = sizeof(TK) == 2 ? 2 : 1;
         __shared__ float qs[G][D];
         __shared__ float sc[MAX_W * 32];
         const int tid = threadIdx.x, nt = blockDim.x;
         const int b = r / dm.Hkv, g = r % dm.Hkv;
-        const T *qr = q + blockIdx.y * q_step + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
+        const TQ *qr = q + blockIdx.y * q_step + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
         for (int p = tid; p < G * D; p += nt) (&qs[0][0])[p] = ldf(qr + p) * dm.scale;
         __syncthreads();
         const int nsb = M * n_cand;
@@ -524,7 +531,7 @@ struct ScoresFused {
                 if (sb < nsb) {
 #pragma unroll
                     for (int dv = 0; dv < NV; ++dv)
-                        raw[u][dv] = *reinterpret_cast<const uint4 *>(kbar + kbar_vec<T, D>(dm, r, sb, dv));
+                        raw[u][dv] = *reinterpret_cast<const uint4 *>(kbar + kbar_vec<TK, D>(dm, r, sb, dv));
                 }
             }
 #pragma unroll
@@ -537,7 +544,7 @@ struct ScoresFused {
 #pragma unroll
                     for (int dv = 0; dv < NV; ++dv) {
                         float x[V];
-                        KbarVec<T>::unpack(raw[u][dv], x);
+                        KbarVec<TK>::unpack(raw[u][dv], x);
 #pragma unroll
                         for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -943,14 +950,14 @@ fetch_kernel(const u32x4 *__restrict__ src, int64_t src_row_blocks, const int32_
 //    max-of-means eviction score, with the new token taken from LDS and the
 //    block's other 63 tokens from memory.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int G>
+template <typename T, typename TK, int D, int G>
 __global__ void __launch_bounds__(256)
 ingest_kernel(Dims dm, const T *__restrict__ qkv, const T *__restrict__ x,
               const T *__restrict__ w_e, const float *__restrict__ b_e, int hidden, int tok,
               T *__restrict__ q_out, T *__restrict__ kv, int64_t kv_row_blocks, int block,
-              float *__restrict__ e_tok, int64_t e_stride, T *__restrict__ kbar,
+              float *__restrict__ e_tok, int64_t e_stride, TK *__restrict__ kbar,
               float *__restrict__ e_blk) {
-    constexpr int S = 64, M = 4, V = KbarVec<T>::V, NW = 256 / 64;
+    constexpr int S = 64, M = 4, V = KbarVec<TK>::V, NW = 256 / 64;
     __shared__ T knew[D];
     __shared__ float red[NW];
     __shared__ float e_new, emean[M];
@@ -1009,7 +1016,7 @@ ingest_kernel(Dims dm, const T *__restrict__ qkv, const T *__restrict__ x,
     // the block is complete: pool it
     for (int p = tid; p < M * D; p += blockDim.x) {
         const int i = p / D, d = p % D;
-        kbar[kbar_vec<T, D>(dm, r, M * j + i, d / V) + (d % V)] = pooled_mean_of<T>([&](int u) {
+        kbar[kbar_vec<TK, D>(dm, r, M * j + i, d / V) + (d % V)] = pooled_mean_of<T, TK>([&](int u) {
             const int t = 16 * i + u;
             return t == S - 1 ? knew[d] : blk[t * D + d];
         });
@@ -1056,25 +1063,25 @@ append_kernel(Dims dm, const T *__restrict__ k_new, const T *__restrict__ v_new,
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, typename TK, int D>
 hipError_t launch_pool(const Dims &dm, const void *kv, int64_t kv_row_blocks, int kv_first,
                        const float *e_tok, int64_t e_stride, int blk_begin, int blk_end,
                        void *kbar, float *e_blk, hipStream_t st) {
     dim3 grid(blk_end - blk_begin, dm.rows);
-    hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(256), 0, st, dm,
+    hipLaunchKernelGGL((pool_kernel<T, TK, D>), grid, dim3(256), 0, st, dm,
                        static_cast<const T *>(kv), kv_row_blocks, kv_first, e_tok, e_stride,
-                       blk_begin, static_cast<T *>(kbar), e_blk, nullptr);
+                       blk_begin, static_cast<TK *>(kbar), e_blk, nullptr);
     return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, typename TK, int D>
 hipError_t launch_pool_step(const Dims &dm, const void *kv, int64_t kv_row_blocks,
                             const float *e_tok, int64_t e_stride, const int32_t *dstep,
                             void *kbar, float *e_blk, hipStream_t st) {
     // one token per step completes at most one block
-    hipLaunchKernelGGL((pool_kernel<T, D>), dim3(1, dm.rows), dim3(256), 0, st, dm,
+    hipLaunchKernelGGL((pool_kernel<T, TK, D>), dim3(1, dm.rows), dim3(256), 0, st, dm,
                        static_cast<const T *>(kv), kv_row_blocks, 0, e_tok, e_stride, 0,
-                       static_cast<T *>(kbar), e_blk, dstep);
+                       static_cast<TK *>(kbar), e_blk, dstep);
     return hipGetLastError();
 }
 
@@ -1093,23 +1100,24 @@ hipError_t launch_step_advance(const Dims &dm, int32_t *dstep, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <typename T, int D, int G>
+// With a device step record the grid covers the capacity.
+template <typename T, typename TK, int D, int G>
 hipError_t launch_score(const Dims &dm, const void *q, const void *kbar, int n_cand, float *s_q,
                         hipStream_t st, const int32_t *dstep) {
-    if constexpr (std::is_same_v<T, bf16_t>) {
-        // with a device step record the grid covers the capacity
-        const int n_tiles = ((dstep ? dm.max_blocks : n_cand) + 3) / 4;
-        if (n_tiles == 0) return hipSuccess;  // no candidates: nothing to score
+    const int cand = dstep ? dm.max_blocks : n_cand;
+    if (cand == 0) return hipSuccess;  // no candidates: nothing to score
+    if constexpr (std::is_same_v<TK, bf16_t>) {
+        // bfloat16 pooled keys (and queries): the matrix cores
+        const int n_tiles = (cand + 3) / 4;
         dim3 grid((n_tiles + SCORE_TILES_PER_WG - 1) / SCORE_TILES_PER_WG, dm.rows);
         hipLaunchKernelGGL((score_mfma_kernel<D, G>), grid, dim3(64 * SCORE_WAVES), 0, st, dm,
                            static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(kbar),
                            n_cand, s_q, dstep);
     } else {
-        if (dstep) return hipErrorInvalidValue;  // float32 scores take the step by value
-        if (n_cand == 0) return hipSuccess;
-        dim3 grid((4 * n_cand + 255) / 256, dm.rows);
-        hipLaunchKernelGGL((score_kernel<T, D, G>), grid, dim3(256), 0, st, dm,
-                           static_cast<const T *>(q), static_cast<const T *>(kbar), n_cand, s_q);
+        dim3 grid((4 * cand + 255) / 256, dm.rows);
+        hipLaunchKernelGGL((score_kernel<T, TK, D, G>), grid, dim3(256), 0, st, dm,
+                           static_cast<const T *>(q), static_cast<const TK *>(kbar), n_cand, s_q,
+                           dstep);
     }
     return hipGetLastError();
 }
@@ -1165,45 +1173,46 @@ hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, i
 // hides each row's selection behind other rows' scoring).
 constexpr int SPLIT_SCORE_MAX_ROWS = 128;
 
-template <typename T, int D, int G>
+template <typename T, typename TK, int D, int G>
 hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, float *s_q,
                                const float *e_blk, int n_cand, int n_prev, uint32_t *ge,
                                uint32_t *ev, int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
                                const SwapPtrs *swap, hipStream_t st, const int32_t *dstep) {
-    if constexpr (std::is_same_v<T, bf16_t>) {
-        if (dm.rows <= SPLIT_SCORE_MAX_ROWS) {
-            // too few rows to fill the chip with one workgroup each: score on
-            // a grid split over the row's candidates, then select from s_q
-            const hipError_t e = launch_score<T, D, G>(dm, q, kbar, n_cand, s_q, st, dstep);
-            if (e != hipSuccess) return e;
-            return launch_select_from(dm, ScoresGlobal{s_q}, e_blk, n_cand, n_prev, ge, ev, sel,
-                                      n_sel, sel_bits, swap, nullptr, st, 1, dstep);
-        }
+    if (std::is_same_v<T, bf16_t> && dm.rows <= SPLIT_SCORE_MAX_ROWS) {
+        // too few rows to fill the chip with one workgroup each: score on a
+        // grid split over the row's candidates, then select from s_q
+        const hipError_t e = launch_score<T, TK, D, G>(dm, q, kbar, n_cand, s_q, st, dstep);
+        if (e != hipSuccess) return e;
+        return launch_select_from(dm, ScoresGlobal{s_q}, e_blk, n_cand, n_prev, ge, ev, sel,
+                                  n_sel, sel_bits, swap, nullptr, st, 1, dstep);
+    }
+    if constexpr (std::is_same_v<TK, bf16_t>) {
         const ScoresFusedMfma<D, G> src{static_cast<const bf16_t *>(q),
                                         static_cast<const bf16_t *>(kbar), s_q};
         return launch_select_from(dm, src, e_blk, n_cand, n_prev, ge, ev, sel, n_sel, sel_bits,
                                   swap, nullptr, st, 1, dstep);
     } else {
-        const ScoresFused<T, D, G> src{static_cast<const T *>(q), static_cast<const T *>(kbar),
-                                       s_q};
+        const ScoresFused<T, TK, D, G> src{static_cast<const T *>(q),
+                                           static_cast<const TK *>(kbar), s_q};
         return launch_select_from(dm, src, e_blk, n_cand, n_prev, ge, ev, sel, n_sel, sel_bits,
                                   swap, nullptr, st, 1, dstep);
     }
 }
 
-template <typename T, int D, int G>
+// The pooled queries qbar have the pooled dtype TK, like the pooled keys.
+template <typename T, typename TK, int D, int G>
 hipError_t launch_prefill_select(const Dims &dm, const void *qbar, const void *kbar,
                                  const float *e_blk, int n_qb, int32_t *sel, int32_t *n_sel,
                                  hipStream_t st) {
     const int64_t q_step = (int64_t)dm.B * dm.Hq * D;
-    if constexpr (std::is_same_v<T, bf16_t>) {
+    if constexpr (std::is_same_v<TK, bf16_t>) {
         const ScoresFusedMfma<D, G> src{static_cast<const bf16_t *>(qbar),
                                         static_cast<const bf16_t *>(kbar), nullptr, q_step};
         return launch_select_from(dm, src, e_blk, 0, -1, nullptr, nullptr, sel, n_sel, nullptr,
                                   nullptr, nullptr, st, n_qb);
     } else {
-        const ScoresFused<T, D, G> src{static_cast<const T *>(qbar), static_cast<const T *>(kbar),
-                                       nullptr, q_step};
+        const ScoresFused<TK, TK, D, G> src{static_cast<const TK *>(qbar),
+                                            static_cast<const TK *>(kbar), nullptr, q_step};
         return launch_select_from(dm, src, e_blk, 0, -1, nullptr, nullptr, sel, n_sel, nullptr,
                                   nullptr, nullptr, st, n_qb);
     }
@@ -1219,16 +1228,16 @@ hipError_t launch_swap(const Dims &dm, const int32_t *sel, const int32_t *n_sel,
     return hipGetLastError();
 }
 
-template <typename T, int D, int G>
+template <typename T, typename TK, int D, int G>
 hipError_t launch_ingest(const Dims &dm, const void *qkv, const void *x, const void *w_e,
                          const float *b_e, int hidden, int tok, void *q_out, void *kv,
                          int64_t kv_row_blocks, int block, float *e_tok, int64_t e_stride,
                          void *kbar, float *e_blk, hipStream_t st) {
-    hipLaunchKernelGGL((ingest_kernel<T, D, G>), dim3(dm.rows), dim3(256), 0, st, dm,
+    hipLaunchKernelGGL((ingest_kernel<T, TK, D, G>), dim3(dm.rows), dim3(256), 0, st, dm,
                        static_cast<const T *>(qkv), static_cast<const T *>(x),
                        static_cast<const T *>(w_e), b_e, hidden, tok, static_cast<T *>(q_out),
                        static_cast<T *>(kv), kv_row_blocks, block, e_tok, e_stride,
-                       static_cast<T *>(kbar), e_blk);
+                       static_cast<TK *>(kbar), e_blk);
     return hipGetLastError();
 }
 
@@ -1261,39 +1270,43 @@ hipError_t launch_fetch(const Dims &dm, const void *src, int64_t src_row_blocks,
     return hipGetLastError();
 }
 
-#define NOSA_POOL_INST(T, D)                                                                   \
-    template hipError_t launch_pool<T, D>(const Dims &, const void *, int64_t, int,            \
-                                          const float *, int64_t, int, int, void *, float *,   \
-                                          hipStream_t);                                        \
-    template hipError_t launch_pool_step<T, D>(const Dims &, const void *, int64_t,            \
-                                               const float *, int64_t, const int32_t *, void *, \
-                                               float *, hipStream_t);
-NOSA_POOL_INST(float, 64)
-NOSA_POOL_INST(float, 128)
-NOSA_POOL_INST(bf16_t, 64)
-NOSA_POOL_INST(bf16_t, 128)
+// (KV dtype, pooled dtype, D): float32 keys pool to float32; bfloat16 keys to
+// float32 (the default) or to bfloat16 (the model-dtype variant).
+#define NOSA_POOL_INST(T, TK, D)                                                               \
+    template hipError_t launch_pool<T, TK, D>(const Dims &, const void *, int64_t, int,        \
+                                              const float *, int64_t, int, int, void *,        \
+                                              float *, hipStream_t);                           \
+    template hipError_t launch_pool_step<T, TK, D>(const Dims &, const void *, int64_t,        \
+                                                   const float *, int64_t, const int32_t *,    \
+                                                   void *, float *, hipStream_t);
+NOSA_POOL_INST(float, float, 64)
+NOSA_POOL_INST(bf16_t, float, 64)
+NOSA_POOL_INST(bf16_t, float, 128)
+NOSA_POOL_INST(bf16_t, bf16_t, 64)
+NOSA_POOL_INST(bf16_t, bf16_t, 128)
 
-#define NOSA_SCORE_INST(T, D, G)                                                               \
-    template hipError_t launch_score<T, D, G>(const Dims &, const void *, const void *, int,   \
-                                              float *, hipStream_t, const int32_t *);          \
-    template hipError_t launch_ingest<T, D, G>(const Dims &, const void *, const void *,       \
-                                               const void *, const float *, int, int, void *,  \
-                                               void *, int64_t, int, float *, int64_t, void *, \
-                                               float *, hipStream_t);                          \
-    template hipError_t launch_score_select<T, D, G>(                                          \
+#define NOSA_SCORE_INST(T, TK, D, G)                                                           \
+    template hipError_t launch_score<T, TK, D, G>(const Dims &, const void *, const void *,    \
+                                                  int, float *, hipStream_t, const int32_t *); \
+    template hipError_t launch_ingest<T, TK, D, G>(const Dims &, const void *, const void *,   \
+                                                   const void *, const float *, int, int,      \
+                                                   void *, void *, int64_t, int, float *,      \
+                                                   int64_t, void *, float *, hipStream_t);     \
+    template hipError_t launch_score_select<T, TK, D, G>(                                      \
         const Dims &, const void *, const void *, float *, const float *, int, int, uint32_t *, \
         uint32_t *, int32_t *, int32_t *, uint32_t *, const SwapPtrs *, hipStream_t,           \
         const int32_t *);                                                                      \
-    template hipError_t launch_prefill_select<T, D, G>(                                        \
+    template hipError_t launch_prefill_select<T, TK, D, G>(                                    \
         const Dims &, const void *, const void *, const float *, int, int32_t *, int32_t *,    \
         hipStream_t);
-#define NOSA_SCORE_ALLG(T, D)                                                                  \
-    NOSA_SCORE_INST(T, D, 1) NOSA_SCORE_INST(T, D, 2) NOSA_SCORE_INST(T, D, 3)                 \
-    NOSA_SCORE_INST(T, D, 4) NOSA_SCORE_INST(T, D, 5) NOSA_SCORE_INST(T, D, 6)                 \
-    NOSA_SCORE_INST(T, D, 7) NOSA_SCORE_INST(T, D, 8)
-NOSA_SCORE_ALLG(float, 64)
-NOSA_SCORE_ALLG(float, 128)
-NOSA_SCORE_ALLG(bf16_t, 64)
-NOSA_SCORE_ALLG(bf16_t, 128)
+#define NOSA_SCORE_ALLG(T, TK, D)                                                              \
+    NOSA_SCORE_INST(T, TK, D, 1) NOSA_SCORE_INST(T, TK, D, 2) NOSA_SCORE_INST(T, TK, D, 3)     \
+    NOSA_SCORE_INST(T, TK, D, 4) NOSA_SCORE_INST(T, TK, D, 5) NOSA_SCORE_INST(T, TK, D, 6)     \
+    NOSA_SCORE_INST(T, TK, D, 7) NOSA_SCORE_INST(T, TK, D, 8)
+NOSA_SCORE_ALLG(float, float, 64)
+NOSA_SCORE_ALLG(bf16_t, float, 64)
+NOSA_SCORE_ALLG(bf16_t, float, 128)
+NOSA_SCORE_ALLG(bf16_t, bf16_t, 64)
+NOSA_SCORE_ALLG(bf16_t, bf16_t, 128)
 
 }  // namespace nosa

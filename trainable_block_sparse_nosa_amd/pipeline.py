@@ -67,9 +67,11 @@ class DecodeLayer:
     def __init__(self, *, batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks, dtype,
                  kv, kv_row_blocks, e_tok, offload=False, decode_kernel=L.NOSA_DECODE_AUTO,
                  scale=0.0, device="cuda", fuse_select_swap=True, fuse_score=None,
-                 overlap=False, device_append=False, evict_head=None):
+                 overlap=False, device_append=False, evict_head=None, pooled_dtype=L.NOSA_F32):
         self.shape = L.make_shape(batch, n_q_heads, n_kv_heads, head_dim, k_e, k_q, max_blocks,
-                                  dtype, decode_kernel=decode_kernel, scale=scale)
+                                  dtype, decode_kernel=decode_kernel, scale=scale,
+                                  pooled_dtype=pooled_dtype)
+        self.pooled_dtype = pooled_dtype
         self.rows = batch * n_kv_heads
         self.k = k_e + k_q
         self.D = head_dim
@@ -87,11 +89,12 @@ class DecodeLayer:
         dev = torch.device(device)
         R, k, W = self.rows, self.k, self.W
         f32, i32 = torch.float32, torch.int32
-        # pooled keys in the KV dtype: quads of 4 blocks (16 sub-blocks), each
-        # [D / V][16][V] with V dimensions per 16-byte vector
-        V = 16 // (4 if dtype == L.NOSA_F32 else 2)
+        # pooled keys in the pooled dtype (float32 unless bfloat16 is asked
+        # for): quads of 4 blocks (16 sub-blocks), each [D / V][16][V] with V
+        # dimensions per 16-byte vector
+        V = 16 // (4 if pooled_dtype == L.NOSA_F32 else 2)
         self.kbar = torch.zeros(R, (max_blocks + 3) // 4, head_dim // V, 16, V,
-                                dtype=f32 if dtype == L.NOSA_F32 else torch.bfloat16, device=dev)
+                                dtype=torch_dtype(pooled_dtype), device=dev)
         self.e_blk = torch.zeros(R, max_blocks, dtype=f32, device=dev)
         self.s_q = torch.zeros(R, max_blocks, dtype=f32, device=dev)
         self.ge_bits = torch.zeros(R, W, dtype=i32, device=dev)
@@ -117,8 +120,9 @@ class DecodeLayer:
             self.cur_fs = torch.zeros(R, k, dtype=i32, device=dev)
             self.cur_nf = torch.ones(R, dtype=i32, device=dev)
         self.fuse_select_swap = fuse_select_swap
-        # scoring and selection in one launch (one workgroup per row); by
-        # default for bf16, whose scores run on the matrix cores there
+        # scoring and selection through nosa_score_select (one launch with a
+        # workgroup per row, or a split scoring grid and the selection when
+        # the rows are too few to fill the chip); the default for bf16
         if fuse_score is None:
             fuse_score = dtype == L.NOSA_BF16
         self.fuse_score = fuse_score and fuse_select_swap
@@ -138,7 +142,7 @@ class DecodeLayer:
                 raise ValueError("the offload overlap splits the batch in two halves")
             self.half_shape = L.make_shape(batch // 2, n_q_heads, n_kv_heads, head_dim, k_e, k_q,
                                            max_blocks, dtype, decode_kernel=decode_kernel,
-                                           scale=scale)
+                                           scale=scale, pooled_dtype=pooled_dtype)
             self.ws_half_bytes = L.nosa_decode_workspace_size(self.half_shape)
             self.ws_half = [torch.empty(self.ws_half_bytes // 4 + 4, dtype=f32, device=dev)
                             for _ in range(2)]
@@ -240,7 +244,8 @@ class DecodeLayer:
         if nqb > 1:
             L.nosa_pool_blocks(self.shape, self.kv, self.kv_row_blocks, 0, self.e_tok,
                                self.e_stride, 0, nqb - 1, self.kbar, self.e_blk, stream)
-        qbar = torch.empty(nqb, *q_all.shape[:1], *q_all.shape[2:], dtype=q_all.dtype, device=dev)
+        qbar = torch.empty(nqb, *q_all.shape[:1], *q_all.shape[2:],
+                           dtype=torch_dtype(self.pooled_dtype), device=dev)
         self._run("pool_queries", L.nosa_prefill_pool_queries, self.shape, q_all, n_tokens, qbar,
                   stream)
         sel = torch.empty(nqb, self.rows, self.k, dtype=torch.int32, device=dev)
@@ -390,6 +395,49 @@ class DecodeLayer:
         attend(0)
         main.wait_event(self.fetch_b_done)
         attend(1)
+
+    # -- checkpoint / resume ---------------------------------------------------
+    # The decode state a step leaves behind, all of it caller-owned device
+    # memory plus three host counters: pooled keys and eviction scores, the
+    # eviction / selection bitmaps (strict eviction is a property of this
+    # state), the last selection, the cache's slot tables and, offloaded, the
+    # cache and the newest-block buffer themselves.
+    STATE = ("kbar", "e_blk", "ge_bits", "ev_bits", "sel_bits", "sel", "n_sel", "slot_block",
+             "block_slot", "fetch_block", "fetch_slot", "n_fetch", "counters")
+
+    def state_dict(self) -> dict:
+        """A copy of the layer's decode state (device tensors cloned in stream
+        order on the current stream; host counters as ints). A layer built
+        with the same arguments continues from it with load_state_dict."""
+        d = {n: getattr(self, n).clone() for n in self.STATE}
+        if self.offload:
+            d["cache"] = self.cache.clone()
+            d["cur"] = self.cur.clone()
+        d["host"] = {"n_cand_prev": self.n_cand_prev, "pooled": getattr(self, "pooled", 0),
+                     "n_tokens": self.n_tokens}
+        return d
+
+    def load_state_dict(self, d: dict):
+        """Continue from a state_dict() of a layer with the same shape."""
+        names = self.STATE + (("cache", "cur") if self.offload else ())
+        for n in names:
+            dst = getattr(self, n)
+            if tuple(d[n].shape) != tuple(dst.shape) or d[n].dtype != dst.dtype:
+                raise ValueError(f"state {n}: shape or dtype differs from this layer's")
+            dst.copy_(d[n])
+        h = d["host"]
+        self.n_cand_prev, self.pooled, self.n_tokens = h["n_cand_prev"], h["pooled"], h["n_tokens"]
+
+    def reset(self):
+        """Forget the decode state (selections, eviction state, cache tables
+        and counters); start() then begins a new decode."""
+        for t in (self.ge_bits, self.ev_bits, self.sel_bits, self.n_sel, self.n_fetch,
+                  self.counters):
+            t.zero_()
+        for t in (self.sel, self.slot_block, self.block_slot, self.fetch_block, self.fetch_slot):
+            t.fill_(-1)
+        self.n_cand_prev = -1
+        self.n_tokens = 0
 
     # -- steps replayed from a captured graph ----------------------------------
     def graph_capture(self, n_tokens: int, q_buf: torch.Tensor, k_new_buf=None, v_new_buf=None,
