@@ -26,6 +26,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nosa_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# a test that plants a mistake in a copy of the oracle's source points this
+# at the copy's build, in a process of its own
+_VARIANT = os.environ.get("NOSA_ORACLE_LIB")
 _lock = threading.Lock()
 _lib = None
 
@@ -35,13 +38,21 @@ _i = ctypes.POINTER(ctypes.c_int)
 _u8 = ctypes.POINTER(ctypes.c_ubyte)
 
 
+def compile_source(src: str, out: str) -> str:
+    """gcc -O2, no fast-math, no FMA contraction, no threads."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
+                           "-ffp-contract=off", "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc: -O2, no fast-math, no threads."""
+    """Compile the oracle (see compile_source) unless it is up to date."""
+    if _VARIANT:
+        return _VARIANT
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
-                               "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
+        compile_source(_SRC, _LIB)
     return _LIB
 
 
