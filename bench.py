@@ -6,10 +6,17 @@ just became complete (every 64 steps), block scoring, dual selection (Gamma_e
 and Gamma_q), set difference against the cached blocks, block fetch from
 pinned host memory (offloaded workloads only) and sparse decode attention.
 
-Default workload: batch 8, 32 query / 8 KV heads, head_dim 128, 32k-token
-context, blocks of 64 with sub-blocks of 16, budget k = 48 + 16, bf16, KV in
-HBM. Inputs are synthetic (seeded Philox streams), already resident in HBM
-when the timed region starts.
+Headline workload (the largest one-GPU configuration): the 8B-shaped decode
+step, 32 layers, batch 64, 32 query / 8 KV heads, head_dim 128, 32k-token
+context, blocks of 64 with sub-blocks of 16, budget k = 48 + 16, bf16, the
+full KV in pinned host memory and an HBM cache of k blocks per row and layer.
+`value` is its 32-layer decode steps/s over exactly --steps timed steps after
+--warmup untimed ones (the first of which fills the empty caches). Legs, each
+timed on its own: the 64k 3B-shaped and the 32k single-layer workloads with
+the KV in HBM (attention against the HBM roofline), the 128k offloaded
+single layer, prefill, the fused ingest launch and graph replay. Inputs are
+synthetic (seeded Philox streams), resident in HBM (or pinned host memory for
+the offloaded KV) when the timed region starts.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -27,6 +34,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse decode steps/s + attn HBM GB/s (% peak); swap GB/s (% PCIe)"
 HBM_PEAK_GBS = 8000.0
+# the MI355X host link, PCIe 5.0 x16: 32 GT/s per lane, 64 GB/s per direction
+PCIE_PEAK_GBS = 64.0
 
 
 def log(*a):
@@ -36,9 +45,14 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="bf16_1layer_32k")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="offload_8b_32layer_32k",
+                    help="headline workload: offload_8b_32layer_32k (default) or a single-layer "
+                         "workload with the KV in HBM")
+    ap.add_argument("--resident-steps", type=int, default=200,
+                    help="timed steps of each resident leg (64k 3B-shaped, 32k single layer); "
+                         "their attention launches are timed in 25 or more of them")
     ap.add_argument("--decode-kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle sample (0 = skip)")
@@ -50,9 +64,6 @@ def parse():
                          "becomes a latency-bound launch of its own)")
     ap.add_argument("--offload-steps", type=int, default=60,
                     help="steps of the offloaded 128k-context leg (0 = skip)")
-    ap.add_argument("--model-steps", type=int, default=6,
-                    help="timed steps of the 32-layer 8B-shaped offload leg, after a cold "
-                         "step and a warm one (0 = skip)")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the locality ablation of the offload leg (budget splits "
                          "k_e + k_q = k with k_e = 32 and 0, and per-block / per-token "
@@ -97,17 +108,19 @@ def recorded_traffic(workload: str):
     return float(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(w, seconds: float, steps_avail: int):
-    """Time the fp64 oracle (single thread) on a bounded sample of row-steps of
-    the same workload (rows in order, step 0 first, then step 1, ...) and scale
-    the mean time per row-step to whole steps of all rows."""
+def cpu_baseline(w, seconds: float):
+    """Time the fp64 oracle as it stands (one thread) on a bounded sample of
+    row-steps of the same workload (layer 0's rows in order at step 0, then
+    step 1, ...) and scale the mean time per row-step to whole steps: all rows
+    of every layer. The oracle is stateless per step, so each row-step pools
+    and scores every candidate again."""
     import oracle
     import synth
     sc = 1.0 / math.sqrt(w.head_dim)
     done, t_used = 0, 0.0
     rows = {}
     t = 0
-    while t_used < seconds and t < steps_avail:
+    while t_used < seconds and t < w.steps:
         q_t = synth.queries_step(w, 0, t)
         for r in range(w.rows):
             b, g = divmod(r, w.n_kv_heads)
@@ -125,12 +138,16 @@ def cpu_baseline(w, seconds: float, steps_avail: int):
                 break
         t += 1
     per_row_step = t_used / done
-    return {
-        "value": 1.0 / (per_row_step * w.rows), "unit": "steps/s", "cores": 1, "kind": "oracle",
-        "sample": f"{done} row-steps of {w.name} (all {w.rows} rows of steps 0..{t - 1}, "
-                  f"row-major), {t_used:.1f} s of single-threaded fp64 oracle time, scaled "
-                  f"to {w.rows} rows per step",
+    per_step = w.rows * w.n_layers
+    out = {
+        "value": 1.0 / (per_row_step * per_step), "unit": "steps/s", "cores": 1, "kind": "oracle",
+        "sample": f"{done} row-steps of {w.name} (layer 0, rows in order from step 0), "
+                  f"{t_used:.1f} s of single-threaded fp64 oracle time, scaled to "
+                  f"{w.rows} rows x {w.n_layers} layer(s) per step",
+        "s_per_row_step": per_row_step,
     }
+    out.update(cpu_info())
+    return out
 
 
 def setup(w, args, dev, device_append=False):
@@ -419,17 +436,22 @@ class HipTimingEvents:
         self.events = []
 
 
-def timed_run(layer, w, q, args, stream, event_stages=ATTN_STAGES, new=None, sample_every=8):
+def timed_run(layer, w, q, args, stream, event_stages=ATTN_STAGES, new=None, sample_every=8,
+              hist=None):
     """Warm up, then time exactly args.steps steps. HIP events bracket the
     listed stages in every sample_every-th timed step (see bracket(): the
     attention kernel's events mark its own start and end; timing
     every step would understate the throughput by ~8 % on the 32k workload).
-    Returns (elapsed s, [(stage, step, ms)], blocks fetched in the timed
-    steps)."""
+    hist [warmup + steps][rows][k] (optional): each step's selection is copied
+    there after the step (for the locality statistics; one small device copy
+    per step, inside the timed region). Returns (elapsed s, [(stage, step,
+    ms)], blocks fetched in the timed steps)."""
     import torch
     layer.start(w.n_tokens(0), stream)
     for t in range(args.warmup):
         run_step(layer, q, new, t, w.n_tokens(t), stream)
+        if hist is not None:
+            hist[t].copy_(layer.sel)
     torch.cuda.synchronize()
     fetched0 = int(layer.counters[:, 0].sum().item())
     pending = []
@@ -452,6 +474,8 @@ def timed_run(layer, w, q, args, stream, event_stages=ATTN_STAGES, new=None, sam
     for i in range(args.steps):
         cur["i"] = i
         run_step(layer, q, new, args.warmup + i, w.n_tokens(args.warmup + i), stream)
+        if hist is not None:
+            hist[args.warmup + i].copy_(layer.sel)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     layer.stage_hook = None
@@ -607,18 +631,21 @@ def offload_leg(args, dev, stream):
     sub = argparse.Namespace(**vars(args))
     sub.steps = args.offload_steps
     layer, q, kv, new = setup(w, sub, dev, device_append=True)
+    import torch
+    T = sub.warmup + sub.steps
+    hist = torch.empty(T, w.rows, w.k, dtype=torch.int32, device=dev)
     # every step bracketed: the swap rate needs the fetch time of every step
     # (a step here takes ~1.3 ms, so the records cost it little)
     elapsed, ev, fetched = timed_run(layer, w, q, sub, stream, event_stages=("fetch", "decode"),
-                                     new=new, sample_every=1)
+                                     new=new, sample_every=1, hist=hist)
     fetch_s = sum(ms for n, _, ms in ev if n == "fetch") / 1e3
     dec_ms = [ms for n, _, ms in ev if n == "decode"]
     block_bytes = 2 * 64 * w.head_dim * 2
     swap_gbs = fetched * block_bytes / fetch_s / 1e9
     peak = h2d_peak_gbs(dev)
     zc = zero_copy_contiguous_gbs(layer, w, stream)
-    counters = layer.counters.cpu().numpy()
-    T = sub.warmup + sub.steps
+    gam = gamma_stats(hist.cpu().numpy(), [w.n_cand(t) for t in range(T)], w.k, w.k_e)
+    del hist
     out = {
         "workload": w.name, "steps": sub.steps, "steps_per_s": sub.steps / elapsed,
         "ms_per_step": elapsed / sub.steps * 1e3,
@@ -627,7 +654,7 @@ def offload_leg(args, dev, stream):
         "swap_gbs": swap_gbs, "h2d_memcpy_gbs": peak, "frac_of_h2d": swap_gbs / peak,
         "zero_copy_contiguous_gbs": zc,
         "attn_partial_us_per_step": sum(dec_ms) / len(dec_ms) * 1e3,
-        "gamma_mean": float(counters[:, 1].sum()) / (w.rows * w.k * T),
+        "gamma_mean": gam["mean"], "gamma": gam,
         "device_append": True,
     }
     # the same loop in two batch halves, the second half's fetch overlapping
@@ -653,16 +680,50 @@ def offload_leg(args, dev, stream):
     return out
 
 
+def gamma_stats(hist, n_cand, k: int, k_e: int) -> dict:
+    """Locality from recorded selections: hist [T][..., k] int32 ascending
+    block ids (-1 padded) of consecutive steps, n_cand[T] their candidate
+    counts. gamma(t) = |Gamma(t) & Gamma(t-1)| / k per row (Methodology,
+    Locality Guarantee), for t >= 1 of the record; the bound k_e / k is
+    checked on the steps that complete no new block."""
+    import numpy as np
+    h = np.asarray(hist).reshape(len(hist), -1, k)
+    T, R = h.shape[0], h.shape[1]
+    nb = int(max(h.max(), 0)) + 2
+    prev = None
+    gam, gam_nn = [], []
+    rows = np.arange(R)[:, None]
+    for t in range(T):
+        cur = np.zeros((R, nb), bool)
+        cur[rows, np.where(h[t] >= 0, h[t], nb - 1)] = True
+        cur[:, nb - 1] = False
+        if prev is not None:
+            g = (cur & prev).sum(axis=1) / k
+            gam.append(g)
+            if n_cand[t] == n_cand[t - 1]:
+                gam_nn.append(g)
+        prev = cur
+    g_all = np.concatenate(gam) if gam else np.zeros(0)
+    g_nn = np.concatenate(gam_nn) if gam_nn else np.zeros(0)
+    bound = k_e / k
+    return {"steps": T - 1, "rows": R, "mean": float(g_all.mean()) if g_all.size else None,
+            "min": float(g_all.min()) if g_all.size else None,
+            "min_no_new_block": float(g_nn.min()) if g_nn.size else None,
+            "bound": bound, "bound_holds": bool(g_nn.size == 0 or g_nn.min() >= bound - 1e-12)}
+
+
 def model_leg(args, dev, stream, h2d_gbs=None):
     """The 32-layer 8B-shaped decode step (batch 64, 32 / 8 heads, 32k context,
     k = 48 + 16, KV in pinned host memory): all five stages in every layer of
     every step, layer after layer on one stream. The host KV of 32 layers
     would take 279 GB of pinned memory; layers share two host slabs (layer l
     reads slab l % 2), which leaves every shape and the bytes moved per step
-    unchanged. Step 0 fills the empty HBM caches (every selected block is
-    fetched) and is reported apart; step 1 is a warm-up; then
-    args.model_steps steps are timed, with HIP events around every layer's
-    fetch and attention launches."""
+    unchanged. max(--warmup, 1) untimed steps come first (step 0 fills the
+    empty HBM caches: every selected block is fetched, reported apart), then
+    exactly --steps steps are timed, with HIP events at the start and end of
+    every layer's fetch and attention kernels, and each layer's selection
+    copied aside after its step (one small device copy per layer) for the
+    locality statistics."""
     import numpy as np
     import torch
 
@@ -671,9 +732,10 @@ def model_leg(args, dev, stream, h2d_gbs=None):
     from trainable_block_sparse_nosa_amd.hostmem import PinnedBuffer
     from trainable_block_sparse_nosa_amd.pipeline import DecodeLayer, pack_blocks
 
-    w = synth.WORKLOADS["offload_8b_32layer_32k"]
-    n, warm = args.model_steps, 2
+    base = synth.WORKLOADS["offload_8b_32layer_32k"]
+    n, warm = args.steps, max(args.warmup, 1)
     T = warm + n
+    w = base.scaled(steps=max(base.steps, T))
     nb, BE = w.nb_max, 2 * 64 * w.head_dim
     t0 = time.time()
     slabs = []
@@ -719,6 +781,10 @@ def model_leg(args, dev, stream, h2d_gbs=None):
     for t in range(1, warm):
         for li, layer in enumerate(layers):
             layer.step(qs[li][t], w.n_tokens(t), stream)
+    # selections of the last untimed step and of every timed step
+    hist = torch.empty(n + 1, w.n_layers, w.rows, w.k, dtype=torch.int32, device=dev)
+    for li, layer in enumerate(layers):
+        hist[0, li].copy_(layer.sel)
     torch.cuda.synchronize()
     f0 = fetched_blocks()
     ev = HipTimingEvents(2 * 2 * w.n_layers * n + 8)
@@ -738,34 +804,53 @@ def model_leg(args, dev, stream, h2d_gbs=None):
         layer.stage_hook = hook
     torch.cuda.synchronize()
     ts = time.perf_counter()
-    for t in range(warm, T):
+    for i, t in enumerate(range(warm, T)):
         for li, layer in enumerate(layers):
             layer.step(qs[li][t], w.n_tokens(t), stream)
+            hist[i + 1, li].copy_(layer.sel)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - ts
     for layer in layers:
         layer.stage_hook = None
     fetched = fetched_blocks() - f0
-    fetch_ms = sum(ev.elapsed_ms(a, b) for nm, a, b in pending if nm == "fetch")
+    fetch_ms = [ev.elapsed_ms(a, b) for nm, a, b in pending if nm == "fetch"]
     dec = [ev.elapsed_ms(a, b) for nm, a, b in pending if nm == "decode"]
     ev.close()
-    kept = sum(float(layer.counters[:, 1].sum().item()) for layer in layers)
     block_bytes = 2 * 64 * w.head_dim * 2
-    swap_gbs = fetched * block_bytes / (fetch_ms / 1e3) / 1e9
+    fetch_bytes = fetched * block_bytes
+    swap_gbs = fetch_bytes / (sum(fetch_ms) / 1e3) / 1e9
+    # attention: every layer's selection holds the full budget (512 candidates)
+    attn_b = attn_bytes(w, "decode", w.n_tokens(warm), w.k)
+    dec_avg_s = sum(dec) / len(dec) / 1e3
+    attn_gbs = attn_b / dec_avg_s / 1e9
+    gam = gamma_stats(hist.cpu().numpy(), [w.n_cand(t) for t in range(warm - 1, T)], w.k, w.k_e)
     out = {
         "workload": w.name, "layers": w.n_layers, "host_kv_slabs": w.kv_slabs,
-        "steps": n, "steps_per_s": n / elapsed, "ms_per_step": elapsed / n * 1e3,
-        "fetched_gib_per_step": fetched * block_bytes / n / 2**30,
-        "fetch_ms_per_step": fetch_ms / n, "swap_gbs": swap_gbs,
-        "attn_partial_us_per_layer": sum(dec) / len(dec) * 1e3,
-        # over steps 1 .. T-1: step 0 finds every cache empty by construction
-        "gamma_mean": kept / (w.n_layers * w.rows * w.k * (T - 1)),
+        "steps": n, "warmup": warm, "steps_per_s": n / elapsed, "ms_per_step": elapsed / n * 1e3,
+        "fetched_gib_per_step": fetch_bytes / n / 2**30,
+        "fetch_ms_per_step": sum(fetch_ms) / n, "swap_gbs": swap_gbs,
+        "attn_us_per_layer": dec_avg_s * 1e6,
+        "gamma": gam,
         "cold_step_s": cold_s, "cold_fetched_gib": cold_blocks * block_bytes / 2**30,
+        "fetch_roofline": {
+            "kernel": "fetch_kernel (blocks of the swap list, pinned host memory to the HBM "
+                      "cache, over PCIe)",
+            "bound": "pcie", "achieved": swap_gbs, "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+            "frac": swap_gbs / PCIE_PEAK_GBS, "traffic": None,
+            "measured_h2d_gbs": h2d_gbs, "frac_of_measured_h2d": swap_gbs / h2d_gbs if h2d_gbs else None,
+            "avg_launch_us": sum(fetch_ms) / len(fetch_ms) * 1e3,
+            "algorithmic_bytes_per_launch": fetch_bytes / len(fetch_ms),
+            "launches_timed": len(fetch_ms),
+        },
+        "attn_roofline": {
+            "kernel": "decode_mfma_kernel (one chunk per row: the launch writes the output)",
+            "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": attn_gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name),
+            "avg_launch_us": dec_avg_s * 1e6, "algorithmic_bytes_per_launch": attn_b,
+            "launches_timed": len(dec),
+        },
     }
-    if h2d_gbs:
-        out["h2d_memcpy_gbs"] = h2d_gbs
-        out["frac_of_h2d"] = swap_gbs / h2d_gbs
-    del layers, qs
+    del layers, qs, hist
     for buf in slabs:
         buf.free()
     torch.cuda.empty_cache()
@@ -806,9 +891,11 @@ def locality_ablation(w, layer, q, kv, sub, dev, stream, nosa_run, block_bytes, 
     from trainable_block_sparse_nosa_amd.pipeline import DecodeLayer
     k = w.k
     rows = [dict(k_e=w.k_e, k_q=w.k_q, gamma_bound=w.k_e / k, gamma_mean=nosa_run["gamma_mean"],
+                 gamma_min_no_new_block=nosa_run["gamma"]["min_no_new_block"],
                  fetched_mib_per_step=nosa_run["fetched_mib_per_step"],
                  steps_per_s=nosa_run["steps_per_s"], ms_per_step=nosa_run["ms_per_step"])]
     T = sub.warmup + sub.steps
+    hist = torch.empty(T, w.rows, k, dtype=torch.int32, device=dev)
     for ke in (k // 2, 0):
         if ke == w.k_e:
             continue
@@ -816,10 +903,11 @@ def locality_ablation(w, layer, q, kv, sub, dev, stream, nosa_run, block_bytes, 
                           head_dim=w.head_dim, k_e=ke, k_q=k - ke, max_blocks=w.nb_max,
                           dtype=L.NOSA_BF16, kv=kv.dev, kv_row_blocks=w.nb_max,
                           e_tok=layer.e_tok, offload=True, device_append=new is not None)
-        elapsed, _, fetched = timed_run(lay, w, q, sub, stream, event_stages=(), new=new)
-        cnt = lay.counters.cpu().numpy()
-        rows.append(dict(k_e=ke, k_q=k - ke, gamma_bound=ke / k,
-                         gamma_mean=float(cnt[:, 1].sum()) / (w.rows * k * T),
+        elapsed, _, fetched = timed_run(lay, w, q, sub, stream, event_stages=(), new=new,
+                                        hist=hist)
+        gam = gamma_stats(hist.cpu().numpy(), [w.n_cand(t) for t in range(T)], k, ke)
+        rows.append(dict(k_e=ke, k_q=k - ke, gamma_bound=ke / k, gamma_mean=gam["mean"],
+                         gamma_min_no_new_block=gam["min_no_new_block"],
                          fetched_mib_per_step=fetched * block_bytes / sub.steps / 2**20,
                          steps_per_s=sub.steps / elapsed, ms_per_step=elapsed / sub.steps * 1e3))
         log(f"ablation k_e={ke} k_q={k - ke}: {rows[-1]['steps_per_s']:.1f} steps/s, "
@@ -862,6 +950,89 @@ def locality_ablation(w, layer, q, kv, sub, dev, stream, nosa_run, block_bytes, 
                             "blocks": len(pairs), "token_copies_sampled": n_tok}}
 
 
+def resident_leg(name, args, dev, stream, probe, steps, sample_every, extras=True):
+    """A single-layer workload with the KV in HBM: `steps` timed steps after
+    args.warmup untimed ones, the attention call bracketed by HIP events at its
+    kernel's own start and end in every sample_every-th timed step, then
+    (untimed) the per-stage breakdown, the locality statistics of a fresh
+    replay of the same steps and, with extras, the cold-cache runs."""
+    import torch
+    import synth
+    sub = argparse.Namespace(**vars(args))
+    sub.steps = steps
+    base = synth.WORKLOADS[name]
+    T = sub.warmup + steps
+    w = base.scaled(steps=max(base.steps, T))
+    log(f"leg {w.name}: rows={w.rows} G={w.group} D={w.head_dim} ctx={w.context} "
+        f"k={w.k_e}+{w.k_q} steps={T}")
+    layer, q, kv, _ = setup(w, sub, dev)
+    elapsed, ev, _ = timed_run(layer, w, q, sub, stream, sample_every=sample_every)
+    c0 = w.n_cand(sub.warmup)
+    n_e = min(w.k_e, c0)
+    n_q = min(w.k_q, c0 - n_e)
+    blocks = {"decode": n_e + n_q, "decode_e": n_e, "decode_q": n_q}
+    tot_bytes = sum(attn_bytes(w, n, w.n_tokens(sub.warmup + i), blocks[n]) for n, i, _ in ev)
+    tot_ms = sum(ms for _, _, ms in ev)
+    dec_avg_s = tot_ms / len(ev) / 1e3
+    achieved = tot_bytes / (tot_ms / 1e3) / 1e9
+    sampled = len({i for _, i, _ in ev})
+    steps_per_s = steps / elapsed
+    log(f"{w.name}: {steps} steps in {elapsed * 1e3:.1f} ms: {steps_per_s:.1f} steps/s, "
+        f"attention {dec_avg_s * 1e6:.1f} us avg over {len(ev)} launches, {achieved:.0f} GB/s")
+    out = {
+        "workload": w.name, "steps": steps, "warmup": sub.warmup, "steps_per_s": steps_per_s,
+        "ms_per_step": elapsed / steps * 1e3,
+        "roofline": {
+            "kernel": "split-K attention kernel (decode_mfma_kernel: partials for the merge "
+                      "kernel, or with one chunk per row the output itself)",
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name),
+            "avg_launch_us": dec_avg_s * 1e6, "algorithmic_bytes_per_launch": tot_bytes / len(ev),
+            "launches_per_step": len(ev) / sampled, "launches_timed": len(ev),
+            "read_probe_gbs": probe, "frac_of_read_probe": achieved / probe,
+        },
+        "attn_us_per_step": tot_ms / sampled * 1e3,
+    }
+    if not args.no_stage_breakdown:
+        out["stages_us"] = stage_breakdown(layer, w, q, sub.warmup, min(steps, 50), stream)
+    # locality: a fresh decode of the same steps, each step's selection copied aside
+    layer.reset()
+    layer.start(w.n_tokens(0), stream)
+    hist = torch.empty(T, w.rows, w.k, dtype=torch.int32, device=dev)
+    for t in range(T):
+        layer.step(q[t], w.n_tokens(t), stream)
+        hist[t].copy_(layer.sel)
+    out["gamma"] = gamma_stats(hist.cpu().numpy(), [w.n_cand(t) for t in range(T)], w.k, w.k_e)
+    if extras and not args.no_cold:
+        out["cold_cache"] = {m: cold_cache_run(layer, w, q, sub, stream, 26, mib, m)
+                             for m, mib in (("read", 1024), ("write", 512))}
+        for m, c in out["cold_cache"].items():
+            log(f"cache flushed by a {c['scratch_mib']} MiB scratch {m} before each step: "
+                f"attention {c['avg_launch_us']:.1f} us, {c['achieved_gbs']:.0f} GB/s")
+    del layer, q, kv, hist
+    torch.cuda.empty_cache()
+    if extras and not args.no_graph:
+        g = graph_leg(w, sub, dev)
+        g["vs_eager"] = g["steps_per_s"] / steps_per_s
+        out["graph"] = g
+        log(f"graph-replayed steps: {g['steps_per_s']:.1f} steps/s ({g['vs_eager']:.3f}x eager)")
+    return w, out
+
+
+def cpu_info() -> dict:
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -870,7 +1041,6 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import synth
@@ -882,13 +1052,6 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
-    base = synth.WORKLOADS[args.workload]
-    T = args.warmup + args.steps
-    w = base.scaled(steps=max(base.steps, T))
-    log(f"workload {w.name}: rows={w.rows} G={w.group} D={w.head_dim} ctx={w.context} "
-        f"k={w.k_e}+{w.k_q} steps={T} offload={w.offload}")
-    layer, q, kv, _ = setup(w, args, dev)
-
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -898,127 +1061,103 @@ def main():
         del src, dst
         log("copy calibration: 4 x 512 MiB device-to-device")
 
-    elapsed, ev, _ = timed_run(layer, w, q, args, stream)
-    # selection sizes: every row holds the full budget once it has that many candidates
-    c0 = w.n_cand(args.warmup)
-    n_e = min(w.k_e, c0)
-    n_q = min(w.k_q, c0 - n_e)
-    blocks = {"decode": n_e + n_q, "decode_e": n_e, "decode_q": n_q}
-    tot_bytes = sum(attn_bytes(w, n, w.n_tokens(args.warmup + i), blocks[n]) for n, i, _ in ev)
-    tot_ms = sum(ms for _, _, ms in ev)
-    dec_avg_s = tot_ms / len(ev) / 1e3
-    bytes_avg = tot_bytes / len(ev)
-    achieved = tot_bytes / (tot_ms / 1e3) / 1e9
-    sampled = len({i for _, i, _ in ev})   # steps whose attention launches were bracketed
-    attn_step_us = tot_ms / sampled * 1e3
-    steps_per_s = args.steps / elapsed
-    log(f"timed {args.steps} steps in {elapsed * 1e3:.1f} ms: {steps_per_s:.1f} steps/s, "
-        f"attention partial launches {dec_avg_s * 1e6:.1f} us avg, {achieved:.0f} GB/s")
-
-    overlapped = bool(getattr(layer, "overlap", False))
-    counters = layer.counters.cpu().numpy()
-    gamma_mean = float(counters[:, 1].sum()) / (w.rows * w.k * T)
-
-    stages = None
-    if not args.no_stage_breakdown:
-        stages = stage_breakdown(layer, w, q, args.warmup, min(args.steps, 50), stream)
-    cold = None
-    if not w.offload and not args.no_cold:
-        cold = {m: cold_cache_run(layer, w, q, args, stream, 21, mib, m)
-                for m, mib in (("read", 1024), ("write", 512))}
-        for m, c in cold.items():
-            log(f"cache flushed by a {c['scratch_mib']} MiB scratch {m} before each step: "
-                f"attention partial {c['avg_launch_us']:.1f} us, {c['achieved_gbs']:.0f} GB/s")
     probe = read_probe_gbs(dev)
     log(f"streaming-read probe: {probe:.0f} GB/s")
-    if not w.offload:
-        del layer, q, kv
-        torch.cuda.empty_cache()
+    h2d = h2d_peak_gbs(dev)
+    log(f"pinned hipMemcpy H2D: {h2d:.1f} GB/s")
 
-    graph = None
-    if not args.no_graph and not w.offload:
-        graph = graph_leg(w, args, dev)
-        graph["vs_eager"] = graph["steps_per_s"] / steps_per_s
-        log(f"graph-replayed steps: {graph['steps_per_s']:.1f} steps/s "
-            f"({graph['vs_eager']:.3f}x the eager launches)")
+    legs = {}
+    hw = synth.WORKLOADS[args.workload]
+    if hw.offload and hw.n_layers > 1:
+        head = model_leg(args, dev, stream, h2d)
+        log(f"{head['workload']}: {head['steps_per_s']:.2f} steps/s ({head['ms_per_step']:.1f} ms "
+            f"per 32-layer step), {head['fetched_gib_per_step']:.2f} GiB fetched per step at "
+            f"{head['swap_gbs']:.1f} GB/s, attention {head['attn_us_per_layer']:.1f} us per layer; "
+            f"gamma mean {head['gamma']['mean']:.4f}, min on no-new-block steps "
+            f"{head['gamma']['min_no_new_block']}")
+        value, w_head = head["steps_per_s"], hw
+        roofline, attn_roofline = head.pop("fetch_roofline"), head.pop("attn_roofline")
+        ms_per_step = head["ms_per_step"]
+        legs[hw.name] = head
+    elif not hw.offload:
+        w_head, head = resident_leg(args.workload, argparse.Namespace(**{**vars(args)}), dev,
+                                    stream, probe, args.steps, max(1, args.steps // 25))
+        value, ms_per_step = head["steps_per_s"], head["ms_per_step"]
+        roofline, attn_roofline = head.pop("roofline"), None
+        legs[hw.name] = head
+    else:
+        print("the headline workload is the 32-layer offload step or a resident one",
+              file=sys.stderr)
+        sys.exit(2)
 
-    ingest = None
-    if not args.no_ingest and not w.offload and w.dtype == "bf16":
-        log(f"ingest leg: {w.name} with the fused ingest launch")
-        ingest = ingest_leg(w, args, dev, stream, steps_per_s)
-        log(f"ingest: {ingest['steps_per_s']:.1f} steps/s, launch {ingest['ingest_us_avg']:.1f} us")
+    # resident legs: the 64k 3B-shaped workload (1.6 GB of HBM reads per step,
+    # the bandwidth of record) and the 32k one (its working set fits the 256 MB
+    # Infinity Cache); 25 or more attention launches timed in each
+    for name, extras in (("bf16_3b_64k", False), ("bf16_1layer_32k", True)):
+        if name in legs:
+            continue
+        rs = args.resident_steps
+        _, legs[name] = resident_leg(name, args, dev, stream, probe, rs, max(1, rs // 25), extras)
 
-    prefill = None
-    if not args.no_prefill and not w.offload and w.dtype == "bf16":
-        log(f"prefill leg: {w.name}, {w.context} tokens")
-        prefill = prefill_leg(w, args, dev, stream)
-        log(f"prefill: {prefill['tokens_per_s']:.0f} tokens/s, attention "
-            f"{prefill['ms_attention']:.1f} ms = {prefill['roofline']['achieved']:.0f} TFLOP/s, "
-            f"selection {prefill['ms_select']:.1f} ms")
-
-    swap = None
-    if args.offload_steps > 0 and not w.offload:
+    w32 = synth.WORKLOADS["bf16_1layer_32k"]
+    if not args.no_ingest:
+        sub = argparse.Namespace(**vars(args))
+        sub.steps = args.resident_steps
+        log(f"ingest leg: {w32.name} with the fused ingest launch")
+        legs["ingest"] = ingest_leg(w32.scaled(steps=max(w32.steps, sub.warmup + sub.steps)), sub,
+                                    dev, stream, legs["bf16_1layer_32k"]["steps_per_s"])
+        log(f"ingest: {legs['ingest']['steps_per_s']:.1f} steps/s, launch "
+            f"{legs['ingest']['ingest_us_avg']:.1f} us")
+    if not args.no_prefill:
+        log(f"prefill leg: {w32.name}, {w32.context} tokens")
+        legs["prefill"] = prefill_leg(w32, args, dev, stream)
+        p = legs["prefill"]
+        log(f"prefill: {p['tokens_per_s']:.0f} tokens/s, attention {p['ms_attention']:.1f} ms = "
+            f"{p['roofline']['achieved']:.0f} TFLOP/s, selection {p['ms_select']:.1f} ms")
+    if args.offload_steps > 0:
         log("offload leg: offload_1layer_128k")
-        swap = offload_leg(args, dev, stream)
-        log(f"offload: {swap['steps_per_s']:.1f} steps/s, swap {swap['swap_gbs']:.1f} GB/s "
-            f"= {100 * swap['frac_of_h2d']:.1f} % of hipMemcpy H2D {swap['h2d_memcpy_gbs']:.1f} GB/s")
-
-    model = None
-    if args.model_steps > 0 and not w.offload:
-        log("32-layer leg: offload_8b_32layer_32k")
-        model = model_leg(args, dev, stream, swap["h2d_memcpy_gbs"] if swap else None)
-        log(f"32 layers: {model['steps_per_s']:.2f} steps/s ({model['ms_per_step']:.1f} ms), "
-            f"{model['fetched_gib_per_step']:.2f} GiB fetched per step at "
-            f"{model['swap_gbs']:.1f} GB/s, attention {model['attn_partial_us_per_layer']:.1f} us "
-            f"per layer; cold step {model['cold_step_s']:.2f} s")
+        legs["offload_1layer_128k"] = offload_leg(args, dev, stream)
+        o = legs["offload_1layer_128k"]
+        log(f"offload: {o['steps_per_s']:.1f} steps/s, swap {o['swap_gbs']:.1f} GB/s = "
+            f"{100 * o['frac_of_h2d']:.1f} % of hipMemcpy H2D {o['h2d_memcpy_gbs']:.1f} GB/s")
 
     cpu = None
     if args.cpu_seconds > 0:
-        log("timing the oracle sample on the host")
-        cpu = cpu_baseline(w, args.cpu_seconds, T)
+        log("timing the oracle samples on the host")
+        cpu = cpu_baseline(w_head, args.cpu_seconds)
+        cpu["by_workload"] = {n: cpu_baseline(synth.WORKLOADS[n], args.cpu_seconds / 4)
+                              for n in ("bf16_1layer_32k", "bf16_3b_64k")}
+        for n, c in cpu["by_workload"].items():
+            c.pop("by_workload", None)
 
     result = {
         "metric": METRIC,
-        "value": steps_per_s,
+        "value": value,
         "unit": "steps/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": elapsed / args.steps * 1e3,
+        "warmup": legs[w_head.name].get("warmup", args.warmup),
+        "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": w_head.dtype,
         "data": "synthetic",
         "config": {
-            "workload": w.name, "layers": w.n_layers, "batch": w.batch, "n_q_heads": w.n_q_heads,
-            "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "context": w.context,
-            "block": 64, "sub_block": 16, "k_e": w.k_e, "k_q": w.k_q,
-            "kv": "pinned host" if w.offload else "hbm", "decode_kernel": args.decode_kernel,
+            "workload": w_head.name, "layers": w_head.n_layers, "batch": w_head.batch,
+            "n_q_heads": w_head.n_q_heads, "n_kv_heads": w_head.n_kv_heads,
+            "head_dim": w_head.head_dim, "context": w_head.context, "block": 64,
+            "sub_block": 16, "k_e": w_head.k_e, "k_q": w_head.k_q,
+            "kv": "pinned host" if w_head.offload else "hbm", "pooled_keys": "f32",
+            "decode_kernel": args.decode_kernel,
         },
-        "roofline": {
-            "kernel": "split-K attention kernel (decode_mfma_kernel: partials for the merge "
-                      "kernel, or with one chunk per row the output itself; with overlap, two "
-                      "launches per step: eviction set + newest block, then query set)",
-            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name),
-            "avg_launch_us": dec_avg_s * 1e6, "algorithmic_bytes_per_launch": bytes_avg,
-            "launches_per_step": len(ev) / sampled, "launches_timed": len(ev),
-            "read_probe_gbs": probe, "frac_of_read_probe": achieved / probe,
-        },
-        "cold_cache": cold,
-        "graph": graph,
-        "attn_partial_us_per_step": attn_step_us,
-        "overlap": overlapped,
-        "gamma_mean": gamma_mean,
-        "swap": swap,
-        "model_8b_32layer": model,
-        "ingest": ingest,
-        "prefill": prefill,
+        "roofline": roofline,
+        "attn_roofline": attn_roofline,
+        "read_probe_gbs": probe,
+        "h2d_memcpy_gbs": h2d,
+        "legs": legs,
         "cpu_baseline": cpu,
     }
-    if stages:
-        result["stages_us"] = stages
     print(json.dumps(result), flush=True)
 
 

@@ -47,3 +47,35 @@ def test_prefill_flops_by_counting_pairs():
                 pairs += t - 64 * i + 1                    # own block up to itself
     expect = pairs * w.group * 4 * w.head_dim
     assert bench.prefill_flops(w, n_tokens, n_sel) == expect
+
+
+def test_gamma_stats_by_counting():
+    """gamma(t) = |Gamma(t) & Gamma(t-1)| / k per row for t >= 1 (Methodology,
+    Locality Guarantee), recomputed with Python sets; the bound is checked on
+    the steps that complete no block only."""
+    import random
+    rng = random.Random(3)
+    k, k_e, R, T = 6, 4, 5, 9
+    n_cand = [20, 20, 21, 21, 21, 22, 22, 22, 22]
+    hist = []
+    for t in range(T):
+        rows = []
+        for r in range(R):
+            sel = sorted(rng.sample(range(n_cand[t]), rng.randint(k - 2, k)))
+            rows.append(sel + [-1] * (k - len(sel)))
+        hist.append(rows)
+    want, want_nn = [], []
+    for t in range(1, T):
+        for r in range(R):
+            a = {b for b in hist[t][r] if b >= 0}
+            p = {b for b in hist[t - 1][r] if b >= 0}
+            g = len(a & p) / k
+            want.append(g)
+            if n_cand[t] == n_cand[t - 1]:
+                want_nn.append(g)
+    got = bench.gamma_stats(np.array(hist, np.int32), n_cand, k, k_e)
+    assert got["steps"] == T - 1 and got["rows"] == R
+    assert abs(got["mean"] - sum(want) / len(want)) < 1e-12
+    assert got["min"] == min(want)
+    assert got["min_no_new_block"] == min(want_nn)
+    assert got["bound_holds"] == (min(want_nn) >= k_e / k)
