@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--workload", default="offload_8b_32layer_32k",
                     help="headline workload: offload_8b_32layer_32k (default) or a single-layer "
                          "workload with the KV in HBM")
+    ap.add_argument("--legs", default="all", choices=["all", "none"],
+                    help="none: the headline workload alone (for profiler runs)")
     ap.add_argument("--resident-steps", type=int, default=200,
                     help="timed steps of each resident leg (64k 3B-shaped, 32k single layer); "
                          "their attention launches are timed in 25 or more of them")
@@ -1093,14 +1095,19 @@ def main():
     # resident legs: the 64k 3B-shaped workload (1.6 GB of HBM reads per step,
     # the bandwidth of record) and the 32k one (its working set fits the 256 MB
     # Infinity Cache); 25 or more attention launches timed in each
+    if args.legs == "none":
+        args.no_ingest = args.no_prefill = True
+        args.offload_steps = 0
     for name, extras in (("bf16_3b_64k", False), ("bf16_1layer_32k", True)):
+        if args.legs == "none":
+            break
         if name in legs:
             continue
         rs = args.resident_steps
         _, legs[name] = resident_leg(name, args, dev, stream, probe, rs, max(1, rs // 25), extras)
 
     w32 = synth.WORKLOADS["bf16_1layer_32k"]
-    if not args.no_ingest:
+    if not args.no_ingest and "bf16_1layer_32k" in legs:
         sub = argparse.Namespace(**vars(args))
         sub.steps = args.resident_steps
         log(f"ingest leg: {w32.name} with the fused ingest launch")

@@ -103,22 +103,37 @@ def test_fullsize_offload_128k_device_append():
     inp.kv.free()
 
 
+# Steps of the 512-step 32-layer run checked against the oracle: the start,
+# the first boundaries (a new candidate block at steps 64 and 128), the
+# middle, the boundary at step 448 and the end of the run.
+C4_STEPS = (0, 1, 2, 62, 63, 64, 65, 66, 126, 127, 128, 129, 130, 255, 256, 447, 448, 449,
+            510, 511)
+
+
 def test_fullsize_offload_8b_32layer_32k():
     """32 layers x batch 64 x 8 KV heads, all five stages per layer per step,
-    steps 0..65 (a block completes at step 64); sampled layers and rows are
-    checked at every step, and every row of layer 17 at step 64."""
+    the whole run of 512 steps (a new candidate block at steps 64, 128, ...,
+    448).
+    Layers 0, 17 and 31 are checked at the steps above on sampled rows, with
+    the oracle replaying those rows from step 0 so that swap lists and slot
+    tables compare bit for bit, and every row of layer 17 at step 64 and of
+    layer 31 at step 511."""
     gh = _gpu()
     w = synth.WORKLOADS["offload_8b_32layer_32k"]
-    steps = 66
+    steps = w.steps
+    assert steps == 512 and max(C4_STEPS) == steps - 1
     layers_checked = {0: [0, 300, 511], 17: [5, 257], 31: [0, 511]}
-    traces = {}
-    for l, rows in layers_checked.items():
-        print(f"[fullsize] 8b: oracle layer {l} rows {rows}", flush=True)
-        traces[l] = oracle_trace(w, layer=l, rows=rows, steps=list(range(steps)))
-    # every row of one layer at the step that completes a block
-    all_l, all_t = 17, 64
-    print(f"[fullsize] 8b: oracle layer {all_l}, all {w.rows} rows, step {all_t}", flush=True)
-    tr_all = oracle_trace(w, layer=all_l, steps=[all_t], ov=traces[all_l].ov, swaps=False)
+    print(f"[fullsize] 8b: oracle layers {sorted(layers_checked)}, steps 0..{steps - 1}",
+          flush=True)
+    # the layers' traces side by side (the oracle's C calls release the GIL)
+    traces = dict(zip(layers_checked, synth.parallel_map(
+        lambda l: oracle_trace(w, layer=l, rows=layers_checked[l], steps=list(range(steps))),
+        list(layers_checked), len(layers_checked))))
+    all_at = {17: 64, 31: steps - 1}     # every row of a layer at one step
+    tr_all = {}
+    for l, t in all_at.items():
+        print(f"[fullsize] 8b: oracle layer {l}, all {w.rows} rows, step {t}", flush=True)
+        tr_all[l] = oracle_trace(w, layer=l, steps=[t], ov=traces[l].ov, swaps=False, workers=16)
     print("[fullsize] 8b: pinned host KV slabs", flush=True)
     slabs = gh.upload_slabs(w)
     layers, inputs = [], []
@@ -130,17 +145,27 @@ def test_fullsize_offload_8b_32layer_32k():
     print("[fullsize] 8b: running 32 layers", flush=True)
     for layer in layers:
         layer.start(w.n_tokens(0))
+    checked = 0
     for t in range(steps):
         for l, layer in enumerate(layers):
             layer.step(inputs[l].q[t], w.n_tokens(t))
-            if l in traces:
+            if l in traces and t in C4_STEPS:
                 got = gh.snapshot(layer, w)
                 for r in layers_checked[l]:
                     _compare_step(w, traces[l], t, r, got)
-                if l == all_l and t == all_t:
+                    checked += 1
+                if all_at.get(l) == t:
                     for r in range(w.rows):
-                        _compare_step(w, tr_all, t, r, got, check_swap=False)
-        if t % 16 == 0:
+                        _compare_step(w, tr_all[l], t, r, got, check_swap=False)
+                    # every row's selection is a valid one at any size
+                    c = w.n_cand(t)
+                    for r in range(w.rows):
+                        n = int(got["n_sel"][r])
+                        sel = got["sel"][r, :n]
+                        assert n == min(w.k, c)
+                        assert (np.diff(sel) > 0).all() and sel[0] >= 0 and sel[-1] < c
+        if t % 64 == 0:
             print(f"[fullsize] 8b: step {t} done", flush=True)
+    assert checked == len(C4_STEPS) * sum(len(r) for r in layers_checked.values())
     for buf, _ in slabs:
         buf.free()
