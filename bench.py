@@ -87,9 +87,11 @@ def parse():
     return ap.parse_args()
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per attention call recorded from rocprofv3 byte counters for
-    this workload, if the kernel sources are unchanged since; else None."""
+def recorded_traffic(workload: str, key: str = "traffic_bytes_per_launch"):
+    """HBM bytes per launch recorded from rocprofv3 byte counters for this
+    workload (key: traffic_bytes_per_launch, the attention kernel;
+    fetch_hbm_bytes_per_launch, the fetch kernel's writes into the HBM cache),
+    if the kernel sources are unchanged since; else None."""
     import hashlib
     prof = os.path.join(ROOT, "profiles", f"decode_step_{workload}.md")
     csrc = os.path.join(ROOT, "trainable_block_sparse_nosa_amd", "csrc")
@@ -102,12 +104,12 @@ def recorded_traffic(workload: str):
     fields = {}
     with open(prof) as fh:
         for line in fh:
-            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256_16"):
+            if ":" in line and line.split(":")[0] in (key, "source_sha256_16"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("source_sha256_16") != h.hexdigest()[:16]:
+    if fields.get("source_sha256_16") != h.hexdigest()[:16] or key not in fields:
         return None
-    return float(fields["traffic_bytes_per_launch"])
+    return float(fields[key])
 
 
 def cpu_baseline(w, seconds: float):
@@ -838,7 +840,8 @@ def model_leg(args, dev, stream, h2d_gbs=None):
             "kernel": "fetch_kernel (blocks of the swap list, pinned host memory to the HBM "
                       "cache, over PCIe)",
             "bound": "pcie", "achieved": swap_gbs, "peak": PCIE_PEAK_GBS, "unit": "GB/s",
-            "frac": swap_gbs / PCIE_PEAK_GBS, "traffic": None,
+            "frac": swap_gbs / PCIE_PEAK_GBS,
+            "traffic": recorded_traffic(w.name, "fetch_hbm_bytes_per_launch"),
             "measured_h2d_gbs": h2d_gbs, "frac_of_measured_h2d": swap_gbs / h2d_gbs if h2d_gbs else None,
             "avg_launch_us": sum(fetch_ms) / len(fetch_ms) * 1e3,
             "algorithmic_bytes_per_launch": fetch_bytes / len(fetch_ms),
