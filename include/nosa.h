@@ -358,6 +358,28 @@ nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const voi
                                const nosa_step *step, const float *e_tok, int64_t e_row_stride,
                                void *out, void *ws, size_t ws_bytes, void *stream);
 
+/* nosa_sparse_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same attention with the same arguments minus the
+ * workspace. The split-K partials go to a scratch array the library holds in
+ * device memory, NOSA_NOALLOC_SCRATCH_BYTES per GPU (its address is taken
+ * once per device, on the first call there), with a row's partials packed
+ * at the chunk count this call uses. Needs rows * chunks * G * (D + 2) * 4
+ * bytes (chunks = nosa_decode_chunks(shape, k, 1); none when the MFMA kernel
+ * serves each row with a single chunk); a shape that needs more returns
+ * NOSA_ERR_WORKSPACE before any launch. The call allocates nothing and
+ * synchronises nothing. Every call on one GPU shares that GPU's scratch: two
+ * calls whose kernels overlap in time (other streams, other threads) race on
+ * it and give undefined results. Results are bit for bit those of
+ * nosa_sparse_decode. */
+#define NOSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+nosa_status nosa_sparse_decode_noalloc(const nosa_shape *shape, const void *q, const void *kv,
+                                       int64_t kv_row_blocks, int32_t kv_mode,
+                                       const int32_t *list, const int32_t *n_list,
+                                       const void *cur_kv, int64_t cur_row_blocks,
+                                       const nosa_step *step, const float *e_tok,
+                                       int64_t e_row_stride, void *out, void *stream);
+
 /* The first half of nosa_sparse_decode over an arbitrary block list: for
  * every row, attention partials (running max, sum and weighted values per
  * head) over list entries 0 .. list_len-1 of row r (list[r*list_stride + i];

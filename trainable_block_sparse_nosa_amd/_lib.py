@@ -33,7 +33,7 @@ EXPORTS = (
     "nosa_select_parts", "nosa_score_select", "nosa_fetch_blocks", "nosa_append_tokens",
     "nosa_ingest_tokens", "nosa_prefill_pool_queries", "nosa_prefill_select",
     "nosa_prefill_attention", "nosa_decode_workspace_size", "nosa_decode_chunks",
-    "nosa_sparse_decode", "nosa_decode_partial", "nosa_decode_partial_timed",
+    "nosa_sparse_decode", "nosa_sparse_decode_noalloc", "nosa_decode_partial", "nosa_decode_partial_timed",
     "nosa_decode_combine", "nosa_decode_combine_step", "nosa_decode_attend",
     "nosa_step_advance", "nosa_pool_step", "nosa_append_step", "nosa_score_select_step",
     "nosa_decode_partial_step",
@@ -75,6 +75,7 @@ def _load() -> ctypes.CDLL:
         "nosa_swap_diff": [SH, P, P, P, P, P, P, P, P, P, P],
         "nosa_fetch_blocks": [SH, P, I64, P, P, P, I32, P, I64, P],
         "nosa_sparse_decode": [SH, P, P, I64, I32, P, P, P, I64, ST, P, I64, P, P, SZ, P],
+        "nosa_sparse_decode_noalloc": [SH, P, P, I64, I32, P, P, P, I64, ST, P, I64, P, P],
         "nosa_select_parts": [SH, P, P, ST] + [P] * 15 + [P],
         "nosa_score_select": [SH, P, P, P, ST] + [P] * 12 + [P],
         "nosa_decode_chunks": [SH, I32, I32],
@@ -310,6 +311,17 @@ def nosa_sparse_decode(shape, q, kv, kv_row_blocks, kv_mode, list_, n_list, cur_
         ctypes.byref(shape), _p(q), _p(kv), kv_row_blocks, kv_mode, _p(list_), _p(n_list),
         _p(cur_kv), cur_row_blocks, ctypes.byref(step), _p(e_tok), e_row_stride, _p(out), _p(ws),
         ws_bytes, _s(stream)))
+
+
+def nosa_sparse_decode_noalloc(shape, q, kv, kv_row_blocks, kv_mode, list_, n_list, cur_kv,
+                               cur_row_blocks, step, e_tok, e_row_stride, out, stream=None):
+    _chk("nosa_sparse_decode_noalloc", _L.nosa_sparse_decode_noalloc(
+        ctypes.byref(shape), _p(q), _p(kv), kv_row_blocks, kv_mode, _p(list_), _p(n_list),
+        _p(cur_kv), cur_row_blocks, ctypes.byref(step), _p(e_tok), e_row_stride, _p(out),
+        _s(stream)))
+
+
+NOSA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def nosa_host_alloc(nbytes: int, coherent: bool = False) -> tuple[int, int]:

@@ -4,11 +4,42 @@
 #include <string>
 #include <type_traits>
 
+#include <mutex>
+
 #include "kernels.h"
 
 using namespace nosa;
 
+// Scratch of nosa_sparse_decode_noalloc: split-K partials for callers that
+// cannot allocate. Each GPU the library runs on holds its own copy, for the
+// life of the process. In host code `noalloc_scratch` is a host-side stand-in
+// for the symbol, not a device address: kernels get the per-device address
+// that hipGetSymbolAddress returns, never the name.
+static __device__ __align__(256) unsigned char noalloc_scratch[NOSA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES];  // device address of noalloc_scratch, per device
+
+// The current device's scratch address, taken on the first call there.
+hipError_t noalloc_scratch_ptr(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 thread_local std::string g_last_error;
 
@@ -487,6 +518,54 @@ nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const voi
     a.cb = pl.cb;
     const hipStream_t st = (hipStream_t)stream;
     if (kind == NOSA_DECODE_MFMA && pl.n_chunks == 1) {
+        a.out = out;  // one chunk per row: the attention launch writes the output
+        return launch_partial(dm, kind, pl, a, st);
+    }
+    s = launch_partial(dm, kind, pl, a, st);
+    if (s != NOSA_OK) return s;
+    return launch_merge(dm, pl.n_chunks, a, out, st);
+}
+
+nosa_status nosa_sparse_decode_noalloc(const nosa_shape *shape, const void *q, const void *kv,
+                                       int64_t kv_row_blocks, int32_t kv_mode,
+                                       const int32_t *list, const int32_t *n_list,
+                                       const void *cur_kv, int64_t cur_row_blocks,
+                                       const nosa_step *step, const float *e_tok,
+                                       int64_t e_row_stride, void *out, void *stream) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!out || !kv || !list || (kv_mode == NOSA_KV_FULL && !n_list))
+        return NOSA_ERR_INVALID_ARGUMENT;
+    if (kv_mode == NOSA_KV_CACHE && kv_row_blocks < dm.k) return NOSA_ERR_INVALID_ARGUMENT;
+    const int kind = decode_kind(dm, shape->decode_kernel);
+    const DecodePlan pl = decode_plan(dm, kind, dm.k + 1);
+    const bool direct = kind == NOSA_DECODE_MFMA && pl.n_chunks == 1;
+    // partials packed at this call's chunk count: [rows][chunks][G][D], then
+    // [rows][chunks][G][2]
+    const size_t parts = direct ? 0 : (size_t)dm.rows * pl.n_chunks * dm.G;
+    const size_t need = parts * dm.D * sizeof(float) + parts * 2 * sizeof(float);
+    if (need > NOSA_NOALLOC_SCRATCH_BYTES) return NOSA_ERR_WORKSPACE;
+    void *scratch = nullptr;
+    s = hip_status(noalloc_scratch_ptr(&scratch));
+    if (s != NOSA_OK) return s;
+    DecodeArgs a;
+    // validation as nosa_sparse_decode's (the scratch stands for ws)
+    s = decode_common(dm, kind, q, kv, kv_row_blocks, kv_mode, cur_kv, cur_row_blocks, step, e_tok,
+                      e_row_stride, scratch, decode_ws_bytes(dm), a);
+    if (s != NOSA_OK) return s;
+    a.chunk_cap = direct ? 1 : pl.n_chunks;
+    a.ws_o = static_cast<float *>(scratch);
+    a.ws_ml = a.ws_o + parts * dm.D;
+    a.list = list;
+    a.n_list = kv_mode == NOSA_KV_FULL ? n_list : nullptr;
+    a.list_stride = dm.k;
+    a.list_len = dm.k;
+    a.with_newest = 1;
+    a.chunk0 = 0;
+    a.cb = pl.cb;
+    const hipStream_t st = (hipStream_t)stream;
+    if (direct) {
         a.out = out;  // one chunk per row: the attention launch writes the output
         return launch_partial(dm, kind, pl, a, st);
     }
