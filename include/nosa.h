@@ -68,7 +68,13 @@
  *            (sb = 4*j + i) is at [.][sb/16][d/V][sb%16][d%V]. Each mean is
  *            the sub-block's keys summed in double and rounded once to the
  *            pooled dtype (nearest, ties to even): for bfloat16 keys the
- *            exact mean rounded once.
+ *            exact mean rounded once. With bfloat16 keys and float32 pooled
+ *            keys, the buffer continues (nosa_kbar_bytes bytes in all) with
+ *            a bfloat16 rounding of every mean, in the bfloat16 layout, then
+ *            a float32 radius per block [rows][max_blocks]: scores from the
+ *            bfloat16 copy are within scale * sum_h ||q_h||_2 * radius of
+ *            the float32 ones, which lets nosa_score_select rank on the
+ *            copy and settle the near ties on float32 scores.
  * e_blk      float32 [rows][max_blocks]: pooled eviction score per block.
  * s_q        float32 [rows][max_blocks]: query-aware score per block.
  * bitmaps    uint32 [rows][W], W = (max_blocks + 31) / 32; bit j%32 of word
@@ -152,6 +158,8 @@ typedef struct nosa_step {
  * block). Block j of row r is read from the KV buffer `kv` at block index
  * kv_first_block + (j - blk_begin) of that row (kv_row_blocks blocks per row),
  * so the same call pools from the full KV or from the newest-block buffer.
+ * With bf16 keys and float32 pooled keys it also writes the blocks' bfloat16
+ * copies and radii (kbar must then hold nosa_kbar_bytes bytes).
  * kv may be a device pointer or the device alias of pinned host memory. */
 nosa_status nosa_pool_blocks(const nosa_shape *shape, const void *kv, int64_t kv_row_blocks,
                              int32_t kv_first_block, const float *e_tok, int64_t e_row_stride,
@@ -289,7 +297,14 @@ nosa_status nosa_select_swap(const nosa_shape *shape, const float *s_q, const fl
  * selects from them. With bf16 and at most 128 rows, too few workgroups to
  * fill the GPU that way, the scores are computed on a grid split over each
  * row's candidates and the selection follows as a second launch on the same
- * stream. s_q receives the scores either way. Outputs and state updates are
+ * stream. With bf16 keys and float32 pooled keys the scores come from the
+ * pooled keys' bfloat16 copy (half the bytes); every candidate whose score
+ * interval (copy score +- scale * sum_h ||q_h|| * radius) reaches the lowest
+ * lower bound of that first top k_q is then scored again from the float32
+ * means (float32 dot products, partial sums in a fixed order), and Gamma_q
+ * is the top k_q of those: the selection is the one float32 scores give,
+ * and s_q receives the copy's scores (within the radius bound of the
+ * float32 ones). Otherwise s_q receives the scores. Selections and state updates are
  * those of the separate calls. The cache pointers are all NULL or all
  * non-NULL. */
 nosa_status nosa_score_select(const nosa_shape *shape, const void *q, const void *kbar,
@@ -325,6 +340,10 @@ nosa_status nosa_fetch_blocks(const nosa_shape *shape, const void *src_kv, int64
                               const int32_t *fetch_block, const int32_t *fetch_slot,
                               const int32_t *n_fetch, int32_t max_fetch, void *dst_kv,
                               int64_t dst_row_blocks, void *stream);
+
+/* Bytes of the kbar buffer for this shape (layout above); 0 for an invalid
+ * shape. */
+size_t nosa_kbar_bytes(const nosa_shape *shape);
 
 /* Workspace bytes the attention calls need for this shape: split-K partials
  * of up to k + 2 chunks per row (one call over the whole selection, or two

@@ -57,6 +57,7 @@ class Workload:
     # exact means rounded once to float32 (the oracle keeps them exact), or
     # "bf16", the variant that stores them in the model's dtype
     pooled: str = "f32"
+    key_common: float = 0.0    # a constant added to every key element (near-tied scores)
 
     @property
     def group(self) -> int:
@@ -188,14 +189,17 @@ class Overrides:
 def keys_row(w: Workload, slab: int, b: int, g: int) -> np.ndarray:
     """Keys of row (b, g) in host-KV slab ``slab``: [n_max, D] in the input dtype.
 
-    K = z + mu_block with z ~ N(0, 1) per element and, per block, a D-vector
-    mu ~ N(0, key_offset_std^2) added to every key of that block.
+    K = z + mu_block + key_common with z ~ N(0, 1) per element and, per
+    block, a D-vector mu ~ N(0, key_offset_std^2) added to every key of that
+    block.
     """
     z = stream(w.seed, "K", slab, b, g).standard_normal((w.n_max, w.head_dim), dtype=np.float32)
     if w.key_offset_std > 0:
         mu = stream(w.seed, "Kmu", slab, b, g).standard_normal(
             (w.nb_max, w.head_dim), dtype=np.float32) * np.float32(w.key_offset_std)
         z = z + np.repeat(mu, w.block, axis=0)[: w.n_max]
+    if w.key_common:
+        z = z + np.float32(w.key_common)
     return _to_dtype(z, w.dtype)
 
 

@@ -173,6 +173,7 @@ def snapshot(layer: DecodeLayer, w: Workload) -> dict:
         "n_fetch": layer.n_fetch.cpu().numpy().copy(),
         "slot_block": layer.slot_block.cpu().numpy().copy(),
         "counters": layer.counters.cpu().numpy().copy(),
+        "s_q_certified": bool(getattr(layer, "scores_certified", False)),
         "out": layer.out.float().cpu().numpy().astype(np.float64),
     }
 

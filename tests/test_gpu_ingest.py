@@ -57,11 +57,13 @@ def test_ingest_outputs(dtype, D, G, pos, pooled):
     q_out = torch.zeros(B, Hq, D, dtype=kv.dtype, device="cuda")
     e_dev = torch.from_numpy(e_tok).cuda()
     V8 = 16 // (4 if pooled == "f32" else 2)
-    kbar = torch.zeros(rows, nb // 4, D // V8, 16, V8,
-                       dtype=torch.float32 if pooled == "f32" else torch.bfloat16, device="cuda")
     e_blk = torch.zeros(rows, nb, dtype=torch.float32, device="cuda")
     shape = L.make_shape(B, Hq, Hkv, D, 2, 2, nb, L.NOSA_F32 if dtype == "f32" else L.NOSA_BF16,
                          pooled_dtype=L.NOSA_F32 if pooled == "f32" else L.NOSA_BF16)
+    kdt = torch.float32 if pooled == "f32" else torch.bfloat16
+    esz = 4 if pooled == "f32" else 2
+    kbar_buf = torch.zeros(L.nosa_kbar_bytes(shape) // esz, dtype=kdt, device="cuda")
+    kbar = kbar_buf[:rows * (nb // 4) * D * 16].view(rows, nb // 4, D // V8, 16, V8)
     L.nosa_ingest_tokens(shape, dev(conv(qkv)), dev(conv(x)), dev(conv(W)),
                          torch.from_numpy(bias).cuda(), hidden, tok + 1, q_out, kv, nb, j, e_dev,
                          nb * 64, kbar, e_blk)

@@ -35,12 +35,17 @@ def _compare_step(w, tr, t, r, got, check_swap=True, check_slots=True):
     # scale covers D = 128 with room, and stays far inside the 1e-4 selection
     # margin the inputs are drawn with. The eviction scores are float32 means
     # of 16 logits: 2e-6 of the row's largest pooled magnitude (at least 1).
+    # With certified scoring (bf16 keys, float32 pooled keys, nosa_score_select)
+    # s_q holds the scores of the pooled keys' bf16 copy, within
+    # scale * sum_h |q_h| * |copy - mean| <= 2^-8 of the term scale of the
+    # float32 ones; the selection itself is settled on float32 scores.
     if c:
         e_scale = max(1.0, float(np.max(np.abs(ref.E))))
         np.testing.assert_allclose(got["e_blk"][r, :c], ref.E, rtol=0, atol=2e-6 * e_scale,
                                    err_msg=where)
+        s_tol = 2.0 ** -8 if got.get("s_q_certified") else 2e-6
         np.testing.assert_allclose(got["s_q"][r, :c], ref.S, rtol=0,
-                                   atol=2e-6 * tr.term_scale[(t, r)], err_msg=where)
+                                   atol=s_tol * tr.term_scale[(t, r)], err_msg=where)
     # selections: bit-exact
     assert gh.bits_to_list(got["ge_bits"][r]) == ref.gamma_e, where
     n = int(got["n_sel"][r])
@@ -275,6 +280,44 @@ def test_parity_edge_cases(edge, overlap):
     for t in range(w.steps):
         for r in range(w.rows):
             _compare_step(w, tr, t, r, res[t])
+
+
+# Near-ties under certified scoring (bf16 keys, float32 pooled keys): every
+# key element carries a common offset of 64, so each pooled key's bf16 copy
+# sits up to 0.25 per element from its float32 mean, while the blocks' scores
+# differ by far less than the bound that follows from it. The copy's intervals
+# then cover nearly every candidate: the exact rescoring runs over all of them
+# (two passes of 128 blocks), and the copy's own top k_q is wrong at most steps.
+NEAR_TIES = {
+    # 4 rows: scores on the split grid, then the selection
+    "split": dict(context=10000, steps=12, key_common=64.0),
+    # 132 rows: scores inside the selecting workgroup
+    "fused": dict(batch=33, n_q_heads=8, n_kv_heads=4, context=10000, steps=4, key_common=64.0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(NEAR_TIES))
+def test_certified_scoring_near_ties(case):
+    gh = _gpu()
+    base = synth.WORKLOADS["small_bf16"]
+    w = base.scaled(name="ties_" + case, seed=3400 + sorted(NEAR_TIES).index(case),
+                    **NEAR_TIES[case])
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov)
+    _, res = gh.run(w, inp, list(range(w.steps)))
+    copy_wrong = 0
+    for t in range(w.steps):
+        assert res[t]["s_q_certified"]
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, res[t])
+            ref = tr.step[(t, r)]
+            ge = set(ref.gamma_e)
+            s = res[t]["s_q"][r]
+            rest = [j for j in range(ref.n_cand) if j not in ge]
+            top = sorted(sorted(rest, key=lambda j: (-s[j], j))[:w.k_q])
+            copy_wrong += top != sorted(ref.gamma_q)
+    # the bf16 copy alone would have selected wrongly at most (step, row)s
+    assert copy_wrong >= w.steps * w.rows // 2, copy_wrong
 
 
 @pytest.mark.parametrize("edge", ["gqa1_d64", "gqa8", "k128", "kq_large", "max_capacity"])

@@ -32,7 +32,8 @@ EXPORTS = (
     "nosa_pool_blocks", "nosa_score_blocks", "nosa_select", "nosa_select_swap", "nosa_swap_diff",
     "nosa_select_parts", "nosa_score_select", "nosa_fetch_blocks", "nosa_append_tokens",
     "nosa_ingest_tokens", "nosa_prefill_pool_queries", "nosa_prefill_select",
-    "nosa_prefill_attention", "nosa_decode_workspace_size", "nosa_decode_chunks",
+    "nosa_prefill_attention", "nosa_kbar_bytes", "nosa_decode_workspace_size",
+    "nosa_decode_chunks",
     "nosa_sparse_decode", "nosa_sparse_decode_noalloc", "nosa_decode_partial", "nosa_decode_partial_timed",
     "nosa_decode_combine", "nosa_decode_combine_step", "nosa_decode_attend",
     "nosa_step_advance", "nosa_pool_step", "nosa_append_step", "nosa_score_select_step",
@@ -109,6 +110,8 @@ def _load() -> ctypes.CDLL:
     L.nosa_decode_chunks.restype = ctypes.c_int32
     L.nosa_decode_workspace_size.argtypes = [SH]
     L.nosa_decode_workspace_size.restype = SZ
+    L.nosa_kbar_bytes.argtypes = [SH]
+    L.nosa_kbar_bytes.restype = SZ
     L.nosa_status_string.argtypes = [ctypes.c_int32]
     L.nosa_status_string.restype = ctypes.c_char_p
     L.nosa_last_error.argtypes = []
@@ -296,6 +299,13 @@ def nosa_prefill_attention(shape, q, n_tokens, kv, kv_row_blocks, e_tok, e_row_s
     _chk("nosa_prefill_attention", _L.nosa_prefill_attention(
         ctypes.byref(shape), _p(q), n_tokens, _p(kv), kv_row_blocks, _p(e_tok), e_row_stride,
         _p(sel), _p(n_sel), _p(out), _s(stream)))
+
+
+def nosa_kbar_bytes(shape) -> int:
+    n = _L.nosa_kbar_bytes(ctypes.byref(shape))
+    if n == 0:
+        raise NosaError("nosa_kbar_bytes", NOSA_ERR_INVALID_ARGUMENT)
+    return n
 
 
 def nosa_decode_workspace_size(shape) -> int:

@@ -478,6 +478,12 @@ nosa_status nosa_append_tokens(const nosa_shape *shape, const void *k_new, const
     });
 }
 
+size_t nosa_kbar_bytes(const nosa_shape *shape) {
+    Dims dm;
+    if (make_dims(shape, &dm) != NOSA_OK) return 0;
+    return (size_t)kbar_bytes(dm);
+}
+
 size_t nosa_decode_workspace_size(const nosa_shape *shape) {
     Dims dm;
     if (make_dims(shape, &dm) != NOSA_OK) return 0;

@@ -36,6 +36,24 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Pooled keys of bfloat16 KV kept in float32 (pooled dtype NOSA_F32) are
+// scored in certified form: the kbar buffer holds, after the float32 means
+// (region 0, [rows][Q][D/4][16][4]), their bfloat16 roundings (region 1, the
+// bfloat16 pooled-key layout [rows][Q][D/8][16][8]) and a float32 radius per
+// block (region 2, [rows][max_blocks]). Element counts and byte offsets:
+__host__ __device__ inline int64_t kbar_elems(const Dims &dm) {
+    return (int64_t)dm.rows * ((dm.max_blocks + 3) / 4) * 16 * dm.D;
+}
+__host__ __device__ inline bool kbar_certified(const Dims &dm) {
+    return dm.dtype == NOSA_BF16 && dm.pdtype == NOSA_F32;
+}
+__host__ __device__ inline int64_t kbar_shadow_offset(const Dims &dm) { return kbar_elems(dm) * 4; }
+__host__ __device__ inline int64_t kbar_radius_offset(const Dims &dm) { return kbar_elems(dm) * 6; }
+__host__ __device__ inline int64_t kbar_bytes(const Dims &dm) {
+    if (!kbar_certified(dm)) return kbar_elems(dm) * (dm.pdtype == NOSA_F32 ? 4 : 2);
+    return kbar_radius_offset(dm) + (int64_t)dm.rows * dm.max_blocks * 4;
+}
+
 __device__ __forceinline__ StepVals read_step(const int32_t *dstep, const Dims &dm) {
     const int n = min(max(dstep[0], 1), dm.max_blocks * dm.S);
     const int c = (n - 1) / dm.S;

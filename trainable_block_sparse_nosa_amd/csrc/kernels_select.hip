@@ -80,6 +80,76 @@ __device__ __forceinline__ TK pooled_mean(const T *k, int stride) {
     return pooled_mean_of<T, TK>([&](int u) { return k[u * stride]; });
 }
 
+// Write the pooled keys of block j of row r, run by a whole workgroup of 256
+// threads: mean_at(i, d) gives dimension d of sub-block i's mean in the pooled
+// type. With certified scoring (bfloat16 KV, float32 pooled keys; kbar's
+// regions in common.h) each mean's bfloat16 rounding goes to the shadow and
+// the block's radius r = max over its sub-blocks of ||shadow - mean||_2 +
+// 2^-14 ||mean||_2, enlarged by 2^-10 for the float32 sums behind it. For any
+// query q, the score of a sub-block from the shadow then differs from the
+// float32 score by at most scale * ||q||_2 * r: the first term bounds
+// q . (shadow - mean) (Cauchy-Schwarz), the second the rounding of the two
+// float32 dot products of D <= 128 terms ((2 D + 19) 2^-24 < 2^-14 of
+// ||q|| ||mean||, head sum included). Sums of squares reduce in a fixed
+// order, so the radius is the same bits on every run.
+template <typename T, typename TK, int D, typename MeanAt>
+__device__ __forceinline__ void pool_write(const Dims &dm, TK *kbar, int r, int j, MeanAt mean_at) {
+    constexpr int M = 4, V = KbarVec<TK>::V, NW = 256 / 64;
+    constexpr bool CERT = std::is_same_v<T, bf16_t> && std::is_same_v<TK, float>;
+    float dd[M], xx[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) dd[i] = xx[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < M * D / 256; ++k) {
+        const int p = threadIdx.x + 256 * k;
+        const int i = p / D, d = p % D;
+        const TK x = mean_at(i, d);
+        kbar[kbar_vec<TK, D>(dm, r, M * j + i, d / V) + (d % V)] = x;
+        if constexpr (CERT) {
+            bf16_t *shadow = reinterpret_cast<bf16_t *>(reinterpret_cast<char *>(kbar) +
+                                                        kbar_shadow_offset(dm));
+            const bf16_t xb = f2bf(x);
+            shadow[kbar_vec<bf16_t, D>(dm, r, M * j + i, d / 8) + (d % 8)] = xb;
+            const float dl = bf2f(xb) - x;  // exact: x minus its rounding
+#pragma unroll
+            for (int ii = 0; ii < M; ++ii)
+                if (ii == i) {
+                    dd[ii] = fmaf(dl, dl, dd[ii]);
+                    xx[ii] = fmaf(x, x, xx[ii]);
+                }
+        }
+    }
+    if constexpr (CERT) {
+        __shared__ float red[2 * M][NW];
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            const float a = wave_sum(dd[i]), b = wave_sum(xx[i]);
+            if (lane == 0) {
+                red[i][wave] = a;
+                red[M + i][wave] = b;
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float rad = 0.f;
+#pragma unroll
+            for (int i = 0; i < M; ++i) {
+                float a = 0.f, b = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    a += red[i][w];
+                    b += red[M + i][w];
+                }
+                rad = fmaxf(rad, sqrtf(a) + sqrtf(b) * (1.0f / 16384.0f));
+            }
+            float *radius = reinterpret_cast<float *>(reinterpret_cast<char *>(kbar) +
+                                                      kbar_radius_offset(dm));
+            radius[(int64_t)r * dm.max_blocks + j] = rad * (1.0f + 1.0f / 1024.0f);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Pool: one workgroup per (block, row). Sub-block means of the keys go to the
 // kbar layout above; the eviction scores get mean-then-max pooling.
@@ -101,11 +171,9 @@ pool_kernel(Dims dm, const T *__restrict__ kv, int64_t kv_row_blocks, int kv_fir
         j = src = sv.n_prev + blockIdx.x;
     }
     const T *K = kv + ((int64_t)r * kv_row_blocks + src) * (int64_t)(2 * S * D);
-    for (int p = threadIdx.x; p < M * D; p += blockDim.x) {
-        const int i = p / D, d = p % D;
-        kbar[kbar_vec<TK, D>(dm, r, M * j + i, d / V) + (d % V)] =
-            pooled_mean<T, TK>(K + (i * SUB) * D + d, D);
-    }
+    static_assert(V > 0, "pooled-key vector width");
+    pool_write<T, TK, D>(dm, kbar, r, j,
+                         [&](int i, int d) { return pooled_mean<T, TK>(K + (i * SUB) * D + d, D); });
     if (threadIdx.x < M) {
         const float *e = e_tok + (int64_t)r * e_stride + (int64_t)j * S + threadIdx.x * SUB;
         float s = 0.f;
@@ -492,6 +560,7 @@ __device__ void swap_row(const Dims &dm, int r, const uint32_t *bits, int s0, in
 // Where a row's query-aware scores come from.
 // ScoresGlobal: s_q as written by score_kernel.
 struct ScoresGlobal {
+    static constexpr bool kCert = false;
     const float *s_q;
     __device__ __forceinline__ const float *row(const Dims &dm, int r, int) const {
         return s_q + (int64_t)r * dm.max_blocks;
@@ -505,6 +574,7 @@ struct ScoresGlobal {
 // whole workgroup (barriers inside).
 template <typename TQ, typename TK, int D, int G>
 struct ScoresFused {
+    static constexpr bool kCert = false;
     const TQ *q;
     const TK *kbar;
     float *s_q;          // may be null: scores stay in LDS
@@ -638,6 +708,7 @@ __device__ __forceinline__ void mfma_block_scores(const Dims &dm, const bf16_t *
 // itself, its waves taking turns over the row's tiles, into LDS.
 template <int D, int G>
 struct ScoresFusedMfma {
+    static constexpr bool kCert = false;
     const bf16_t *q;
     const bf16_t *kbar;
     float *s_q;          // may be null: scores stay in LDS
@@ -656,6 +727,198 @@ struct ScoresFusedMfma {
         return sc;
     }
 };
+
+// Certified scoring (bfloat16 KV, float32 pooled keys; kbar's regions in
+// common.h). The selection first ranks scores taken from the pooled keys'
+// bfloat16 shadow, each within eps_j = scale * sum_h ||q_h||_2 * radius_j of
+// any float32 evaluation of its score (pool_write). cert_refine then takes
+// every candidate whose interval reaches the lowest lower bound of that first
+// top-k_q, scores it again from the float32 means, and keeps the top k_q of
+// those: every other candidate has k_q candidates certainly above it, so the
+// selection is the top k_q by float32 scores while the scoring reads half the
+// bytes.
+struct CertArgs {
+    const bf16_t *q;      // [B][Hq][D], the step's queries
+    const float *kbar32;  // region 0: the float32 means
+    const float *radius;  // region 2: [rows][max_blocks]
+    int64_t q_step;       // query offset per workgroup row y (batched selections)
+};
+
+// Shadow scores from s_q (written by the split scoring grid on the shadow).
+template <int D_, int G_>
+struct ScoresCert {
+    static constexpr bool kCert = true;
+    static constexpr int D = D_, G = G_;
+    const float *s_q;
+    CertArgs c;
+    __device__ __forceinline__ const float *row(const Dims &dm, int r, int) const {
+        return s_q + (int64_t)r * dm.max_blocks;
+    }
+};
+
+// Shadow scores computed by the selecting workgroup on the matrix cores, into
+// LDS (and s_q).
+template <int D_, int G_>
+struct ScoresCertFused {
+    static constexpr bool kCert = true;
+    static constexpr int D = D_, G = G_;
+    const bf16_t *shadow;
+    float *s_q;
+    CertArgs c;
+    __device__ const float *row(const Dims &dm, int r, int n_cand) const {
+        const ScoresFusedMfma<D, G> f{c.q, shadow, s_q, c.q_step};
+        return f.row(dm, r, n_cand);
+    }
+};
+
+// What cert_refine reads that depends on nothing before it: the row's
+// queries (raw bfloat16) and its candidates' radii, loaded at the start of
+// the selection so that their latency hides behind the scoring and top-k.
+// The loads are unconditional (indexes clamped into the arrays), so that
+// nothing waits for them before cert_refine; entries past the queries or
+// the candidates are never used.
+template <int D, int G>
+struct CertPre {
+    static constexpr int QPT = (G * D + SELECT_THREADS - 1) / SELECT_THREADS;
+    bf16_t q[QPT];                // query element tid + SELECT_THREADS u of the group
+    float rad[KEYS_PER_THREAD];   // radius of candidate tid + SELECT_THREADS i
+};
+template <int D, int G>
+__device__ __forceinline__ void cert_prefetch(const Dims &dm, const CertArgs &ca, int r,
+                                              int n_cand, CertPre<D, G> &p) {
+    const int b = r / dm.Hkv, g = r % dm.Hkv;
+    const bf16_t *qr = ca.q + blockIdx.y * ca.q_step + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
+#pragma unroll
+    for (int u = 0; u < CertPre<D, G>::QPT; ++u)
+        p.q[u] = qr[min((int)threadIdx.x + SELECT_THREADS * u, G * D - 1)];
+    const float *rad = ca.radius + (int64_t)r * dm.max_blocks;
+    const int last = max(n_cand - 1, 0);
+#pragma unroll
+    for (int i = 0; i < KEYS_PER_THREAD; ++i)
+        p.rad[i] = rad[min((int)threadIdx.x + SELECT_THREADS * i, last)];
+}
+
+template <typename Src, bool = Src::kCert> struct CertPreOf { struct type {}; };
+template <typename Src> struct CertPreOf<Src, true> { using type = CertPre<Src::D, Src::G>; };
+
+// DPP rotations inside each row of 16 lanes.
+constexpr int DPP_ROW_ROR4 = 0x124, DPP_ROW_ROR8 = 0x128;
+
+// Gamma_q from certified scores, by the whole selecting workgroup, after the
+// top-k_q of the shadow scores sv (in sb, beside Gamma_e in ge): see
+// CertArgs. Rewrites sb's Gamma_q bits; the caller synchronises after.
+template <int D, int G>
+__device__ void cert_refine(const Dims &dm, const CertArgs &ca, int r, int n_cand, int kq,
+                            const uint32_t *ge, uint32_t *sb,
+                            const float (&sv)[KEYS_PER_THREAD], const CertPre<D, G> &pre) {
+    constexpr int M = 4, V = 4, NQ = D / V / 4;  // float4 vectors per quarter of D
+    static_assert(D % 64 == 0, "a wave's query elements lie in one head");
+    __shared__ float qs[G * D];
+    __shared__ float qn[G * D / 64];
+    __shared__ float red[SELECT_WAVES];
+    __shared__ int rl[MAX_W * 32];
+    __shared__ uint64_t rk[MAX_W * 32 + 8];  // R's rank keys by float32 score, 0-padded
+    __shared__ int n_r;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the queries as the scoring takes them (q * scale), and per wave the sum
+    // of squares of its 64 elements, all of one head
+#pragma unroll
+    for (int u = 0; u < CertPre<D, G>::QPT; ++u) {
+        const int e = tid + SELECT_THREADS * u;
+        if ((e & ~63) < G * D) {  // the whole wave
+            const float x = bf2f(pre.q[u]) * dm.scale;
+            qs[e] = x;
+            const float s2 = wave_sum(x * x);
+            if (lane == 0) qn[e >> 6] = s2;
+        }
+    }
+    if (tid == 0) n_r = 0;
+    __syncthreads();
+    // scale * sum_h ||q_h||_2, enlarged by 2^-10
+    float cq = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float s2 = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) s2 += qn[h * (D / 64) + c];
+        cq += sqrtf(s2);
+    }
+    cq *= 1.0f + 1.0f / 1024.0f;
+    // the lowest lower bound over the shadow's top k_q
+    float eps[KEYS_PER_THREAD];
+    float lbmin = INFINITY;
+#pragma unroll
+    for (int i = 0; i < KEYS_PER_THREAD; ++i) {
+        const int j = tid + SELECT_THREADS * i;
+        eps[i] = 0.f;
+        if (j < n_cand && !((ge[j >> 5] >> (j & 31)) & 1u)) {
+            eps[i] = cq * pre.rad[i];
+            if ((sb[j >> 5] >> (j & 31)) & 1u) lbmin = fminf(lbmin, sv[i] - eps[i]);
+        }
+    }
+    lbmin = -wave_max(-lbmin);
+    if (lane == 0) red[wave] = lbmin;
+    __syncthreads();
+    float T = red[0];
+#pragma unroll
+    for (int w = 1; w < SELECT_WAVES; ++w) T = fminf(T, red[w]);
+    // R: the candidates outside Gamma_e whose upper bound reaches T
+#pragma unroll
+    for (int i = 0; i < KEYS_PER_THREAD; ++i) {
+        const int j = tid + SELECT_THREADS * i;
+        if (j < n_cand && !((ge[j >> 5] >> (j & 31)) & 1u) && sv[i] + eps[i] >= T)
+            rl[atomicAdd(&n_r, 1)] = j;
+    }
+    __syncthreads();
+    const int nr = n_r;
+    // their float32 scores: 16 lanes per block, lane 4 i + c holding sub-block
+    // i and the c-th quarter of D (all 8 of its 16-byte loads in flight at
+    // once); a head's dot product is the sum of the four quarters' float32
+    // partial sums, in a fixed order, and the block takes the max over its
+    // sub-blocks per head and sums the heads in order
+    constexpr int TPB = 16, BPP = SELECT_THREADS / TPB;
+    const int c = tid & 3, i = (tid >> 2) & 3;
+    for (int base = 0; base < nr; base += BPP) {
+        const int m = base + tid / TPB;
+        const int blk = rl[m < nr ? m : nr - 1];
+        const int sbk = M * blk + i;
+        float x[NQ][V];
+#pragma unroll
+        for (int v = 0; v < NQ; ++v)
+            KbarVec<float>::load(ca.kbar32 + kbar_vec<float, D>(dm, r, sbk, c * NQ + v), x[v]);
+        float sc = 0.f;
+#pragma unroll 1
+        for (int h = 0; h < G; ++h) {
+            float a = 0.f;
+#pragma unroll
+            for (int v = 0; v < NQ; ++v)
+#pragma unroll
+                for (int u = 0; u < V; ++u) a = fmaf(qs[h * D + (c * NQ + v) * V + u], x[v][u], a);
+            a += dpp_f<QUAD_SWAP1>(a);
+            a += dpp_f<QUAD_SWAP2>(a);
+            a = fmaxf(a, dpp_f<DPP_ROW_ROR4>(a));
+            a = fmaxf(a, dpp_f<DPP_ROW_ROR8>(a));
+            sc += a;
+        }
+        if (m < nr && (tid & (TPB - 1)) == 0) rk[m] = rank_key(sc, blk);
+    }
+    if (tid < 8) rk[nr + tid] = 0ull;
+    // Gamma_q anew: the k_q best of R by float32 score, lower id first on ties
+    for (int w = tid; w < dm.W; w += SELECT_THREADS) sb[w] = ge[w];
+    __syncthreads();
+    for (int m = tid; m < nr; m += SELECT_THREADS) {
+        const uint64_t km = rk[m];
+        int above = 0;
+        for (int m2 = 0; m2 < nr; m2 += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) above += rk[m2 + u] > km ? 1 : 0;
+        }
+        if (above < kq) {
+            const int j = key_index(km);
+            atomicOr(&sb[j >> 5], 1u << (j & 31));
+        }
+    }
+}
 
 // Block scores on the matrix cores with the row split over workgroups
 // (blockIdx.x = chunk of SCORE_TILES_PER_WG tiles, blockIdx.y = row), so that
@@ -735,6 +998,8 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
         ge_w = ge_g[tid];
         ev_w = ev_g[tid];
     }
+    [[maybe_unused]] typename CertPreOf<Src>::type cpre;
+    if constexpr (Src::kCert) cert_prefetch(dm, src.c, r, n_cand, cpre);
     const float *Sq = src.row(dm, r, n_cand);
     float sv[KEYS_PER_THREAD];
 #pragma unroll
@@ -836,6 +1101,13 @@ select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
         }
     }
     __syncthreads();
+    if constexpr (Src::kCert) {
+        // the top k_q above ranks shadow scores: settle it on float32 scores
+        if (kq > 0 && n_cand - n_e > kq) {
+            cert_refine<Src::D, Src::G>(dm, src.c, r, n_cand, kq, ge, sb, sv, cpre);
+            __syncthreads();
+        }
+    }
 
     // ---- state and the ascending selection ----
     if (ge_g) {
@@ -1014,13 +1286,13 @@ ingest_kernel(Dims dm, const T *__restrict__ qkv, const T *__restrict__ x,
     if (pos != S - 1) return;
     __syncthreads();
     // the block is complete: pool it
-    for (int p = tid; p < M * D; p += blockDim.x) {
-        const int i = p / D, d = p % D;
-        kbar[kbar_vec<TK, D>(dm, r, M * j + i, d / V) + (d % V)] = pooled_mean_of<T, TK>([&](int u) {
+    static_assert(V > 0, "pooled-key vector width");
+    pool_write<T, TK, D>(dm, kbar, r, j, [&](int i, int d) {
+        return pooled_mean_of<T, TK>([&](int u) {
             const int t = 16 * i + u;
             return t == S - 1 ? knew[d] : blk[t * D + d];
         });
-    }
+    });
     if (tid < M) {
         const float *er = e_tok + (int64_t)r * e_stride + (int64_t)j * S + tid * 16;
         float s = 0.f;
@@ -1178,6 +1450,24 @@ hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, 
                                const float *e_blk, int n_cand, int n_prev, uint32_t *ge,
                                uint32_t *ev, int32_t *sel, int32_t *n_sel, uint32_t *sel_bits,
                                const SwapPtrs *swap, hipStream_t st, const int32_t *dstep) {
+    if constexpr (std::is_same_v<T, bf16_t> && std::is_same_v<TK, float>) {
+        // certified scoring: shadow scores on the matrix cores, settled on
+        // float32 scores inside the selection (s_q receives the shadow scores)
+        const char *kb = static_cast<const char *>(kbar);
+        const bf16_t *shadow = reinterpret_cast<const bf16_t *>(kb + kbar_shadow_offset(dm));
+        const CertArgs ca{static_cast<const bf16_t *>(q), static_cast<const float *>(kbar),
+                          reinterpret_cast<const float *>(kb + kbar_radius_offset(dm)), 0};
+        if (dm.rows <= SPLIT_SCORE_MAX_ROWS) {
+            const hipError_t e =
+                launch_score<bf16_t, bf16_t, D, G>(dm, q, shadow, n_cand, s_q, st, dstep);
+            if (e != hipSuccess) return e;
+            return launch_select_from(dm, ScoresCert<D, G>{s_q, ca}, e_blk, n_cand, n_prev, ge,
+                                      ev, sel, n_sel, sel_bits, swap, nullptr, st, 1, dstep);
+        }
+        return launch_select_from(dm, ScoresCertFused<D, G>{shadow, s_q, ca}, e_blk, n_cand,
+                                  n_prev, ge, ev, sel, n_sel, sel_bits, swap, nullptr, st, 1,
+                                  dstep);
+    }
     if (std::is_same_v<T, bf16_t> && dm.rows <= SPLIT_SCORE_MAX_ROWS) {
         // too few rows to fill the chip with one workgroup each: score on a
         // grid split over the row's candidates, then select from s_q

@@ -92,9 +92,19 @@ class DecodeLayer:
         # pooled keys in the pooled dtype (float32 unless bfloat16 is asked
         # for): quads of 4 blocks (16 sub-blocks), each [D / V][16][V] with V
         # dimensions per 16-byte vector
+        # (with bf16 keys and float32 pooled keys the buffer goes on with the
+        # bf16 copy and the radii of certified scoring; self.kbar views the
+        # float32 means at its start)
         V = 16 // (4 if pooled_dtype == L.NOSA_F32 else 2)
-        self.kbar = torch.zeros(R, (max_blocks + 3) // 4, head_dim // V, 16, V,
-                                dtype=torch_dtype(pooled_dtype), device=dev)
+        kdt = torch_dtype(pooled_dtype)
+        kshape = (R, (max_blocks + 3) // 4, head_dim // V, 16, V)
+        n_kbar = int(np.prod(kshape))
+        esz = 4 if pooled_dtype == L.NOSA_F32 else 2
+        self.kbar_buf = torch.zeros(-(-L.nosa_kbar_bytes(self.shape) // esz), dtype=kdt,
+                                    device=dev)
+        self.kbar = self.kbar_buf[:n_kbar].view(kshape)
+        # scores in s_q come from the bf16 copy on the nosa_score_select path
+        self.scores_certified = dtype == L.NOSA_BF16 and pooled_dtype == L.NOSA_F32
         self.e_blk = torch.zeros(R, max_blocks, dtype=f32, device=dev)
         self.s_q = torch.zeros(R, max_blocks, dtype=f32, device=dev)
         self.ge_bits = torch.zeros(R, W, dtype=i32, device=dev)
@@ -126,6 +136,7 @@ class DecodeLayer:
         if fuse_score is None:
             fuse_score = dtype == L.NOSA_BF16
         self.fuse_score = fuse_score and fuse_select_swap
+        self.scores_certified = self.scores_certified and self.fuse_score
         # Overlap (KV in HBM): on a step that completes no block, attention over
         # the eviction set (unchanged since the previous step) and the newest
         # block runs on a side stream while the scores and the selection run on
@@ -402,7 +413,7 @@ class DecodeLayer:
     # eviction / selection bitmaps (strict eviction is a property of this
     # state), the last selection, the cache's slot tables and, offloaded, the
     # cache and the newest-block buffer themselves.
-    STATE = ("kbar", "e_blk", "ge_bits", "ev_bits", "sel_bits", "sel", "n_sel", "slot_block",
+    STATE = ("kbar_buf", "e_blk", "ge_bits", "ev_bits", "sel_bits", "sel", "n_sel", "slot_block",
              "block_slot", "fetch_block", "fetch_slot", "n_fetch", "counters")
 
     def state_dict(self) -> dict:
