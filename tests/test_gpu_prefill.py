@@ -247,3 +247,64 @@ def test_pooled_queries_bit_exact(name):
             ref = oracle.pool_queries(qh[b, 64 * i:64 * i + 64], pooled_bf16=pb)
             np.testing.assert_array_equal(got[i, b], ref.astype(np.float32),
                                           err_msg=f"{name} block {i} b {b}")
+
+
+def test_prefill_large_values():
+    """Large values in a few blocks, three whole blocks times 2^17 (one of them
+    the ragged last block, attended causally by its own queries) and one token
+    times 2^40: P enters P.V as a bf16 hi + lo pair over the full float32
+    exponent range, so a small weight on a huge value keeps its ~16 bits and
+    each output matches the oracle within the bf16 tolerance plus 2^-14 of the
+    size of its terms (sum_t p_t |v_t| / l). (A single fp16 P, tried, loses
+    such a weight below fp16's normal range and fails this case.)"""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gpu_harness as gh
+    w = PREFILL["prefill_bf16"]
+    N, G, D = w.context, w.group, w.head_dim
+    nqb = -(-N // 64)
+    big_blocks, big_token = (2, 9, nqb - 1), 64 * 5 + 7
+    sc = 1.0 / math.sqrt(D)
+    ov, _ = _prefill_trace(w)
+
+    def scaled_v(V):
+        V = V.copy()
+        for j in big_blocks:
+            V[64 * j:64 * j + 64] *= np.float32(2.0 ** 17)
+        V[big_token] *= np.float32(2.0 ** 40)
+        return V
+
+    inp = gh.upload(w, ov=ov, steps=1)
+    kv = inp.kv.cpu()
+    pos_of = {(32 * (p // 32) + 16 * ((p % 8) // 4) + 4 * ((p % 32) // 8) + p % 4): p
+              for p in range(64)}
+    for r in range(w.rows):
+        for j in big_blocks:
+            for u in range(64):
+                kv[r, j, 64 * D + pos_of[u]::64] *= 2.0 ** 17
+        j, u = divmod(big_token, 64)
+        kv[r, j, 64 * D + pos_of[u]::64] *= 2.0 ** 40
+    inp.kv.copy_(kv.to(inp.kv.device))
+    q_all = gh.to_device(gh.storage(synth.prefill_queries(w, 0, N, ov), w), w)
+    layer = gh.make_layer(w, inp)
+    out, sel, n_sel = layer.prefill(q_all, N)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    for r in range(w.rows):
+        b, g = divmod(r, w.n_kv_heads)
+        K, V = row_kv(w, 0, b, g)
+        e = synth.evict_row(w, 0, b, g, ov)
+        q = synth.prefill_queries(w, 0, N, ov)[b, :, g * G:(g + 1) * G]
+        Vs = scaled_v(V[:N])
+        ref = oracle.prefill_row(q, K[:N], Vs, e[:N], 64, 16, w.k_e, w.k_q, sc)
+        # the size of the terms behind each output, sum_t p_t |v_t| / l: where
+        # large terms cancel, P's error (about 2^-18 of each weight, hi + lo)
+        # is bounded by this, not by the small result
+        mag = oracle.prefill_row(q, K[:N], np.abs(Vs), e[:N], 64, 16, w.k_e, w.k_q, sc).out
+        got = out[b, :, g * G:(g + 1) * G]
+        assert np.isfinite(got).all()
+        bound = TOL["atol"] + TOL["rtol"] * np.abs(ref.out) + 2.0 ** -14 * mag
+        bad = np.abs(got - ref.out) > bound
+        assert not bad.any(), (f"row {r}: {int(bad.sum())} outputs, worst excess "
+                               f"{float(np.max((np.abs(got - ref.out) - bound)[bad]))}")
+        assert np.abs(ref.out).max() > 2.0 ** 16     # the planted values reach the outputs
