@@ -648,6 +648,9 @@ def offload_leg(args, dev, stream):
     swap_gbs = fetched * block_bytes / fetch_s / 1e9
     peak = h2d_peak_gbs(dev)
     zc = zero_copy_contiguous_gbs(layer, w, stream)
+    hk = host_memory_kinds(layer, w, stream)
+    log(f"fetch kernel from coherent pinned memory {hk['coherent_gbs']:.1f} GB/s, "
+        f"non-coherent {hk['noncoherent_gbs']:.1f} GB/s")
     gam = gamma_stats(hist.cpu().numpy(), [w.n_cand(t) for t in range(T)], w.k, w.k_e)
     del hist
     out = {
@@ -656,7 +659,7 @@ def offload_leg(args, dev, stream):
         "fetched_mib_per_step": fetched * block_bytes / sub.steps / 2**20,
         "fetch_us_per_step": fetch_s / sub.steps * 1e6,
         "swap_gbs": swap_gbs, "h2d_memcpy_gbs": peak, "frac_of_h2d": swap_gbs / peak,
-        "zero_copy_contiguous_gbs": zc,
+        "zero_copy_contiguous_gbs": zc, "host_memory_kinds": hk,
         "attn_partial_us_per_step": sum(dec_ms) / len(dec_ms) * 1e3,
         "gamma_mean": gam["mean"], "gamma": gam,
         "device_append": True,
@@ -883,6 +886,39 @@ def zero_copy_contiguous_gbs(layer, w, stream, reps=3):
         torch.cuda.synchronize()
         best = max(best, w.rows * k * 2 * 64 * w.head_dim * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     return best
+
+
+def host_memory_kinds(layer, w, stream, reps=3):
+    """The fetch kernel reading k blocks per row (256 MiB on the 128k shape)
+    from pinned host memory allocated coherent (fine-grained) and
+    non-coherent (coarse-grained, the default here): GB/s of each, best of
+    `reps`."""
+    import numpy as np
+    import torch
+    from trainable_block_sparse_nosa_amd import _lib as L
+    from trainable_block_sparse_nosa_amd.hostmem import PinnedBuffer
+    dev = layer.cache.device
+    k = w.k
+    nbytes = w.rows * k * 2 * 64 * w.head_dim * 2
+    fb = torch.arange(k, dtype=torch.int32, device=dev).repeat(w.rows, 1).contiguous()
+    nf = torch.full((w.rows,), k, dtype=torch.int32, device=dev)
+    on = stream if stream is not None else torch.cuda.current_stream()
+    out = {}
+    for name, coherent in (("coherent_gbs", True), ("noncoherent_gbs", False)):
+        buf = PinnedBuffer(nbytes, coherent=coherent)
+        buf.array(np.uint8, (nbytes,))[:] = 1
+        best = 0.0
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(on)
+            L.nosa_fetch_blocks(layer.shape, buf.dev, k, fb, fb, nf, k, layer.cache, k, on)
+            e1.record(on)
+            torch.cuda.synchronize()
+            best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        buf.free()
+        out[name] = best
+    out["bytes"] = nbytes
+    return out
 
 
 def locality_ablation(w, layer, q, kv, sub, dev, stream, nosa_run, block_bytes, new):
