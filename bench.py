@@ -50,8 +50,9 @@ def parse():
     ap.add_argument("--workload", default="offload_8b_32layer_32k",
                     help="headline workload: offload_8b_32layer_32k (default) or a single-layer "
                          "workload with the KV in HBM")
-    ap.add_argument("--legs", default="all", choices=["all", "none"],
-                    help="none: the headline workload alone (for profiler runs)")
+    ap.add_argument("--legs", default="all", choices=["all", "none", "prefill"],
+                    help="none: the headline workload alone (for profiler runs); prefill: the "
+                         "headline workload, then the prefill leg alone")
     ap.add_argument("--resident-steps", type=int, default=200,
                     help="timed steps of each resident leg (64k 3B-shaped, 32k single layer); "
                          "their attention launches are timed in 25 or more of them")
@@ -1134,11 +1135,12 @@ def main():
     # resident legs: the 64k 3B-shaped workload (1.6 GB of HBM reads per step,
     # the bandwidth of record) and the 32k one (its working set fits the 256 MB
     # Infinity Cache); 25 or more attention launches timed in each
-    if args.legs == "none":
-        args.no_ingest = args.no_prefill = True
+    if args.legs in ("none", "prefill"):
+        args.no_ingest = True
+        args.no_prefill = args.legs == "none"
         args.offload_steps = 0
     for name, extras in (("bf16_3b_64k", False), ("bf16_1layer_32k", True)):
-        if args.legs == "none":
+        if args.legs in ("none", "prefill"):
             break
         if name in legs:
             continue

@@ -541,6 +541,15 @@ __device__ __forceinline__ void prefill_store(PrefillTile<D> &tl, const PrefillS
 // enters P V as a bf16 hi + lo pair (about 16 significant bits: when a few
 // tokens dominate a softmax, one bf16 rounding of their weights would show
 // in the output), and the denominator sums the same pair.
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Two floats rounded to bf16 (nearest, ties to even), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // Max of v over the four rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48) on
 // the gfx950 row-swap instructions: with both operands holding v, each lane
 // of the swapped pair holds v at its own lane and at the lane 16 (32) away.
@@ -577,7 +586,7 @@ __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
     f32x4 ev[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) ev[t] = *reinterpret_cast<const f32x4 *>(&tl.e[16 * t + 4 * grp]);
-    bf16x8 ph[CT][2], pl[CT][2];
+    u32x4 ph[CT][2], pl[CT][2];  // bf16 pairs, as the MFMA B operand
     float alpha[CT];
     bool rescale = false;
 #pragma unroll
@@ -604,14 +613,22 @@ __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
         const float m_sub = m_new == -INFINITY ? 0.f : m_new;
         alpha[c] = __builtin_amdgcn_exp2f(m_run[c] - m_sub);
         rescale |= move;
+        // P as hi + lo, two weights at a time: hi is p with its low 16 bits
+        // cleared (p truncated to bf16, relative error below 2^-7), two his
+        // packed by one byte permute; lo = p - hi exactly in float32, two
+        // los rounded to bf16 by one packed conversion: hi + lo is within
+        // 2^-16 of p
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float p = __builtin_amdgcn_exp2f(z[t][u] - m_sub);
-                const __bf16 hi = (__bf16)p;
-                ph[c][t / 2][(t % 2) * 4 + u] = hi;
-                pl[c][t / 2][(t % 2) * 4 + u] = (__bf16)(p - (float)hi);
+            for (int u = 0; u < 4; u += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(z[t][u] - m_sub);
+                const float p1 = __builtin_amdgcn_exp2f(z[t][u + 1] - m_sub);
+                const uint32_t b0 = __float_as_uint(p0) & 0xFFFF0000u;
+                const uint32_t b1 = __float_as_uint(p1) & 0xFFFF0000u;
+                const int w = (t % 2) * 2 + u / 2;
+                ph[c][t / 2][w] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+                pl[c][t / 2][w] = pack_bf16x2(p0 - __uint_as_float(b0), p1 - __uint_as_float(b1));
             }
         m_run[c] = m_new;
     }
@@ -633,8 +650,8 @@ __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
     for (int c = 0; c < CT; ++c) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            l_run[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ph[c][s2], l_run[c], 0, 0, 0);
-            l_run[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl[c][s2], l_run[c], 0, 0, 0);
+            l_run[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(ph[c][s2]), l_run[c], 0, 0, 0);
+            l_run[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pl[c][s2]), l_run[c], 0, 0, 0);
         }
     }
 #pragma unroll
@@ -643,10 +660,10 @@ __device__ __forceinline__ void prefill_block(const PrefillTile<D> &tl,
         const bf16x8 v1 = tl.frag[4 * KS + 2 * dt + 1][lane];
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, ph[c][0], o[c][dt], 0, 0, 0);
-            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pl[c][0], o[c][dt], 0, 0, 0);
-            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, ph[c][1], o[c][dt], 0, 0, 0);
-            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pl[c][1], o[c][dt], 0, 0, 0);
+            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, as_bf16x8(ph[c][0]), o[c][dt], 0, 0, 0);
+            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, as_bf16x8(pl[c][0]), o[c][dt], 0, 0, 0);
+            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, as_bf16x8(ph[c][1]), o[c][dt], 0, 0, 0);
+            o[c][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, as_bf16x8(pl[c][1]), o[c][dt], 0, 0, 0);
         }
     }
 }
