@@ -922,13 +922,15 @@ __device__ void cert_refine(const Dims &dm, const CertArgs &ca, int r, int n_can
 
 // Block scores on the matrix cores with the row split over workgroups
 // (blockIdx.x = chunk of SCORE_TILES_PER_WG tiles, blockIdx.y = row), so that
-// a launch has many more workgroups than rows: each wave loads its 4 tiles
-// (4 x 16 sub-blocks x D: 16 KiB of bf16 pooled keys at D = 128) at once,
-// and the grid covers the row in one pass.
+// a launch has many more workgroups than rows: each wave loads its tile (16
+// sub-blocks x D: 4 KiB of bf16 pooled keys at D = 128) at once, and the
+// grid covers the row in one pass. Swept on the 32k workload (64 rows x 512
+// candidates): 8 waves of one tile 7.3 us, 4 waves of two 7.5, 4 of four
+// 7.9, 4 of eight 9.5.
 // With dstep, n_cand comes from the step record and the grid is sized for the
 // capacity; chunks past the candidates exit at once.
-constexpr int SCORE_WAVES = 4;
-constexpr int SCORE_TPI = 4;
+constexpr int SCORE_WAVES = 8;
+constexpr int SCORE_TPI = 1;
 constexpr int SCORE_TILES_PER_WG = SCORE_WAVES * SCORE_TPI;
 template <int D, int G>
 __global__ void __launch_bounds__(64 * SCORE_WAVES)
