@@ -210,3 +210,28 @@ def test_decode_chunk_plan():
     # 128 rows: 2 chunks
     sh = _shape(batch=16, n_q_heads=32, n_kv_heads=8, k_e=48, k_q=16, max_blocks=2048)
     assert L.nosa_decode_chunks(sh, 64, 1) == 2
+
+
+def test_kbar_bytes_by_dtype():
+    """Size of the pooled-key buffer per row and quad of 4 blocks (16 sub-blocks
+    x D means): float32 keys and means 4 bytes each; bf16 keys with bf16 means
+    2 bytes; bf16 keys with float32 means (certified scoring) the float32 means,
+    then their bf16 copy in the same layout, then a float32 radius per block.
+    The radius region sits after whole quads, so a max_blocks that is not a
+    multiple of 4 still rounds the means up."""
+    from trainable_block_sparse_nosa_amd import _lib as L
+    rows, D = 2 * 2, 128
+    for nb in (64, 63):
+        quads = (nb + 3) // 4
+        means = rows * quads * 16 * D
+        assert L.nosa_kbar_bytes(_shape(max_blocks=nb, pooled_dtype=L.NOSA_BF16)) == 2 * means
+        assert (L.nosa_kbar_bytes(_shape(max_blocks=nb, pooled_dtype=L.NOSA_F32))
+                == 4 * means + 2 * means + 4 * rows * nb)
+        f32 = _shape(max_blocks=nb, dtype=L.NOSA_F32, head_dim=64, pooled_dtype=L.NOSA_F32)
+        assert L.nosa_kbar_bytes(f32) == 4 * rows * quads * 16 * 64
+    # an invalid shape has no buffer: the C call returns 0, the binding raises
+    import ctypes
+    bad = _shape(n_q_heads=7)
+    assert L.lib().nosa_kbar_bytes(ctypes.byref(bad)) == 0
+    with pytest.raises(L.NosaError):
+        L.nosa_kbar_bytes(bad)
