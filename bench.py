@@ -891,8 +891,8 @@ def zero_copy_contiguous_gbs(layer, w, stream, reps=3):
 
 def host_memory_kinds(layer, w, stream, reps=3):
     """The fetch kernel reading k blocks per row (256 MiB on the 128k shape)
-    from pinned host memory allocated coherent (fine-grained) and
-    non-coherent (coarse-grained, the default here): GB/s of each, best of
+    from pinned host memory allocated coherent (fine-grained, the default
+    here) and non-coherent (coarse-grained): GB/s of each, best of
     `reps`."""
     import numpy as np
     import torch

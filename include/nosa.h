@@ -521,7 +521,9 @@ nosa_status nosa_decode_partial_step(const nosa_shape *shape, const void *q, con
 
 /* Pinned host memory readable by GPU kernels: *host is the host address,
  * *dev the device alias to pass as a kernel source. coherent != 0 asks for
- * fine-grained (coherent) memory. Free with nosa_host_free. */
+ * fine-grained (host-coherent) memory, the form the Python layer uses for
+ * the host KV; coherent == 0 for coarse-grained memory. Free with
+ * nosa_host_free. */
 nosa_status nosa_host_alloc(size_t bytes, int32_t coherent, void **host, void **dev);
 nosa_status nosa_host_free(void *host);
 

@@ -334,7 +334,7 @@ def nosa_sparse_decode_noalloc(shape, q, kv, kv_row_blocks, kv_mode, list_, n_li
 NOSA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
-def nosa_host_alloc(nbytes: int, coherent: bool = False) -> tuple[int, int]:
+def nosa_host_alloc(nbytes: int, coherent: bool = True) -> tuple[int, int]:
     h, d = ctypes.c_void_p(), ctypes.c_void_p()
     _chk("nosa_host_alloc", _L.nosa_host_alloc(nbytes, 1 if coherent else 0,
                                                ctypes.byref(h), ctypes.byref(d)))
