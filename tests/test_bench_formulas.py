@@ -79,3 +79,16 @@ def test_gamma_stats_by_counting():
     assert got["min"] == min(want)
     assert got["min_no_new_block"] == min(want_nn)
     assert got["bound_holds"] == (min(want_nn) >= k_e / k)
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU's share: --gpus N > 1 exits with status 2 and
+    says so, before touching a GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stdout + r.stderr
