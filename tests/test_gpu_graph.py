@@ -96,3 +96,28 @@ def test_graph_replayed_steps_fullsize_32k():
             _compare_step(w, tr, t, r, got)
     assert w.n_cand(steps - 1) > w.n_cand(0), "a block completes during the replays"
     assert layer.step_dev.cpu().tolist() == [w.n_tokens(steps - 1) + 1, w.n_cand(steps - 1)]
+
+
+@pytest.mark.parametrize("case", ["split", "fused"])
+def test_graph_replayed_certified_near_ties(case):
+    """Certified scoring with the step record in device memory: the near-tie
+    workloads of the parity tests (every candidate inside the bf16 copy's
+    window, the rescoring in two passes) replayed from a captured graph."""
+    gh = _gpu()
+    from test_gpu_parity import NEAR_TIES, _compare_step
+    base = synth.WORKLOADS["small_bf16"]
+    w = base.scaled(name="graph_ties_" + case, seed=3500 + ["split", "fused"].index(case),
+                    **NEAR_TIES[case])
+    tr = oracle_trace(w)
+    inp = gh.upload(w, ov=tr.ov)
+    layer = gh.make_layer(w, inp, fuse_score=True)
+    assert layer.scores_certified
+    layer.start(w.n_tokens(0))
+    q_buf = torch.empty_like(inp.q[0])
+    graph = layer.graph_capture(w.n_tokens(0), q_buf)
+    for t in range(w.steps):
+        q_buf.copy_(inp.q[t])
+        graph.replay()
+        got = gh.snapshot(layer, w)
+        for r in range(w.rows):
+            _compare_step(w, tr, t, r, got)
