@@ -68,6 +68,10 @@ def test_ingest_outputs(dtype, D, G, pos, pooled):
                          torch.from_numpy(bias).cuda(), hidden, tok + 1, q_out, kv, nb, j, e_dev,
                          nb * 64, kbar, e_blk)
     torch.cuda.synchronize()
+    if dtype == "bf16" and pooled == "f32" and pos == 63:
+        # the certificate of certified scoring, written by the same launch
+        from test_gpu_parity import check_certificate
+        check_certificate(kbar_buf, rows, nb, D, j + 1)
     got_q = q_out.float().cpu().numpy()
     got_kv = kv.float().cpu().numpy()
     got_e = e_dev.cpu().numpy()

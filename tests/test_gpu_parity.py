@@ -95,6 +95,34 @@ def test_pooled_keys(name):
             where = f"{name} row={r} block={j}"
             np.testing.assert_array_equal(got, ref.astype(np.float32).astype(np.float64),
                                           err_msg=where)
+    if layer.scores_certified:
+        check_certificate(layer.kbar_buf, w.rows, layer.max_blocks, w.head_dim, c)
+
+
+def check_certificate(kbar_buf, rows, max_blocks, D, c):
+    """The stored certificate of certified scoring (bf16 keys, float32 pooled
+    keys): the bf16 copy is each float32 mean rounded to the nearest bf16
+    (ties to even), and each block's radius is at least max over its
+    sub-blocks of ||copy - mean||_2 + 2^-14 ||mean||_2, the bound the
+    selection's scoring intervals rest on."""
+    quads = (max_blocks + 3) // 4
+    n = rows * quads * 16 * D  # float32 means
+    buf = kbar_buf.view(torch.int32).cpu().numpy().view(np.uint32)  # float32 words
+    mean = buf[:n].view(np.float32).reshape(rows, quads, D // 4, 16, 4)
+    mean = mean.transpose(0, 1, 3, 2, 4).reshape(rows, -1, D).astype(np.float64)
+    sh16 = buf[n:n + n // 2].view(np.uint16).reshape(rows, quads, D // 8, 16, 8)
+    sh = (sh16.astype(np.uint32) << 16).view(np.float32)
+    sh = sh.transpose(0, 1, 3, 2, 4).reshape(rows, -1, D).astype(np.float64)
+    rad = buf[n + n // 2:n + n // 2 + rows * max_blocks].view(np.float32)
+    rad = rad.reshape(rows, max_blocks).astype(np.float64)
+    want_sh = synth.rne_bf16(mean[:, :4 * c].astype(np.float32)).astype(np.float64)
+    np.testing.assert_array_equal(sh[:, :4 * c], want_sh, err_msg="bf16 copy of the means")
+    need = (np.sqrt(((sh[:, :4 * c] - mean[:, :4 * c]) ** 2).sum(-1))
+            + 2.0 ** -14 * np.sqrt((mean[:, :4 * c] ** 2).sum(-1)))
+    need = need.reshape(rows, c, 4).max(-1)
+    assert (rad[:, :c] >= need).all(), float(np.max(need - rad[:, :c]))
+    # and not loose: within 2^-9 of the bound (the enlargement is 2^-10)
+    assert (rad[:, :c] <= need * (1 + 2.0 ** -9) + 1e-30).all()
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "small_f32", "small_bf16", "small_offload",
