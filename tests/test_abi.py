@@ -197,13 +197,22 @@ def test_decode_chunk_plan():
     """The attention plan, host logic only: about one 8-wave workgroup per CU
     (256), so ceil(256 / rows) chunks per row, at least one block per wave;
     one chunk per row from 256 rows on, where nosa_decode_attend writes the
-    output in the attention launch with no merge launch."""
+    output in the attention launch with no merge launch. The list splits
+    evenly over the chunks and the newest block joins the last one."""
     from trainable_block_sparse_nosa_amd import _lib as L
     # 64 rows (batch 8 x 8 KV heads), 64 + 1 entries: 4 chunks
     sh = _shape(batch=8, n_q_heads=32, n_kv_heads=8, k_e=48, k_q=16, max_blocks=1024)
     assert L.nosa_decode_chunks(sh, 64, 1) == 4
     # few entries cap the chunks at one block per wave: 9 entries -> 2 chunks
     assert L.nosa_decode_chunks(sh, 8, 1) == 2
+    # the query-aware part alone (16 blocks, no newest): 2 chunks of 8
+    assert L.nosa_decode_chunks(sh, 16, 0) == 2
+    # the newest block alone, or with one listed block: one chunk
+    assert L.nosa_decode_chunks(sh, 0, 1) == 1
+    assert L.nosa_decode_chunks(sh, 1, 1) == 1
+    # 17 + 1 entries: 3 chunks (6, 6 and 5 + the newest)
+    assert L.nosa_decode_chunks(sh, 17, 1) == 3
+    assert L.nosa_decode_chunks(sh, 0, 0) == 0
     # 256 rows (batch 32 x 8 KV heads), 128 + 1 entries: one chunk per row
     sh = _shape(batch=32, n_q_heads=24, n_kv_heads=8, k_e=96, k_q=32, max_blocks=1024)
     assert L.nosa_decode_chunks(sh, 128, 1) == 1

@@ -495,7 +495,7 @@ int32_t nosa_decode_chunks(const nosa_shape *shape, int32_t list_len, int32_t wi
     if (make_dims(shape, &dm) != NOSA_OK || list_len < 0 || list_len > dm.k ||
         (with_newest != 0 && with_newest != 1))
         return -1;
-    return decode_plan(dm, decode_kind(dm, shape->decode_kernel), list_len + with_newest).n_chunks;
+    return decode_plan(dm, decode_kind(dm, shape->decode_kernel), list_len, with_newest).n_chunks;
 }
 
 nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const void *kv,
@@ -520,7 +520,7 @@ nosa_status nosa_sparse_decode(const nosa_shape *shape, const void *q, const voi
     a.list_len = dm.k;
     a.with_newest = 1;
     a.chunk0 = 0;
-    const DecodePlan pl = decode_plan(dm, kind, dm.k + 1);
+    const DecodePlan pl = decode_plan(dm, kind, dm.k, 1);
     a.cb = pl.cb;
     const hipStream_t st = (hipStream_t)stream;
     if (kind == NOSA_DECODE_MFMA && pl.n_chunks == 1) {
@@ -545,7 +545,7 @@ nosa_status nosa_sparse_decode_noalloc(const nosa_shape *shape, const void *q, c
         return NOSA_ERR_INVALID_ARGUMENT;
     if (kv_mode == NOSA_KV_CACHE && kv_row_blocks < dm.k) return NOSA_ERR_INVALID_ARGUMENT;
     const int kind = decode_kind(dm, shape->decode_kernel);
-    const DecodePlan pl = decode_plan(dm, kind, dm.k + 1);
+    const DecodePlan pl = decode_plan(dm, kind, dm.k, 1);
     const bool direct = kind == NOSA_DECODE_MFMA && pl.n_chunks == 1;
     // partials packed at this call's chunk count: [rows][chunks][G][D], then
     // [rows][chunks][G][2]
@@ -604,7 +604,7 @@ static nosa_status decode_partial_impl(const nosa_shape *shape, const void *q, c
     s = decode_common(dm, kind, q, kv ? kv : cur_kv, kv ? kv_row_blocks : cur_row_blocks,
                       kv_mode, cur_kv, cur_row_blocks, step, e_tok, e_row_stride, ws, ws_bytes, a);
     if (s != NOSA_OK) return s;
-    const DecodePlan pl = decode_plan(dm, kind, list_len + with_newest);
+    const DecodePlan pl = decode_plan(dm, kind, list_len, with_newest);
     if (chunk0 < 0 || chunk0 + pl.n_chunks > a.chunk_cap) return NOSA_ERR_INVALID_ARGUMENT;
     a.list = list;
     a.n_list = kv_mode == NOSA_KV_FULL ? n_list : nullptr;
@@ -769,7 +769,7 @@ nosa_status nosa_decode_partial_step(const nosa_shape *shape, const void *q, con
     s = decode_common(dm, kind, q, kv ? kv : cur_kv, kv ? kv_row_blocks : cur_row_blocks,
                       kv_mode, cur_kv, cur_row_blocks, &cap, e_tok, e_row_stride, ws, ws_bytes, a);
     if (s != NOSA_OK) return s;
-    const DecodePlan pl = decode_plan(dm, kind, list_len + with_newest);
+    const DecodePlan pl = decode_plan(dm, kind, list_len, with_newest);
     if (chunk0 < 0 || chunk0 + pl.n_chunks > a.chunk_cap) return NOSA_ERR_INVALID_ARGUMENT;
     a.list = list;
     a.n_list = kv_mode == NOSA_KV_FULL ? n_list : nullptr;

@@ -86,13 +86,14 @@ hipError_t launch_fetch(const Dims &dm, const void *src, int64_t src_row_blocks,
 
 // Split-K plan of one partial-attention call: its entries are list entries
 // 0..list_len-1 plus (optionally) the newest block as entry list_len; a
-// chunk of `cb` consecutive entries is one workgroup.
+// chunk of `cb` consecutive entries is one workgroup (the MFMA kernel's last
+// chunk runs to the end, newest block included).
 struct DecodePlan {
     int cb;        // entries per chunk
     int n_chunks;  // chunks of this call
 };
 int decode_kind(const Dims &dm, int requested);  // NOSA_DECODE_VALU or _MFMA
-DecodePlan decode_plan(const Dims &dm, int kind, int entries);
+DecodePlan decode_plan(const Dims &dm, int kind, int list_len, int with_newest);
 // Workspace rows hold this many chunk partials: enough for the whole
 // selection plus the newest block in one call, or split over two calls.
 inline int decode_chunk_cap(const Dims &dm) { return dm.k + 2; }

@@ -40,8 +40,9 @@ namespace nosa {
 constexpr int WAVES = 8;
 constexpr int MFMA_TARGET_WGS = 256;
 
-DecodePlan decode_plan(const Dims &dm, int kind, int entries) {
+DecodePlan decode_plan(const Dims &dm, int kind, int list_len, int with_newest) {
     DecodePlan p;
+    const int entries = list_len + with_newest;
     if (entries <= 0) {
         p.cb = 1;
         p.n_chunks = 0;
@@ -57,8 +58,17 @@ DecodePlan decode_plan(const Dims &dm, int kind, int entries) {
         int nc = (MFMA_TARGET_WGS + dm.rows - 1) / dm.rows;
         const int maxc = (entries + WAVES - 1) / WAVES;  // at least a block per wave
         nc = nc < 1 ? 1 : (nc > maxc ? maxc : nc);
-        p.n_chunks = nc;
-        p.cb = (entries + nc - 1) / nc;
+        // The list splits evenly over the chunks and the newest block (often
+        // partly filled) joins the last one, so that at most one wave of a
+        // chunk walks an extra block: 64 listed blocks over 4 chunks of 8
+        // waves are 2 blocks per wave, plus the newest in one wave of the last.
+        if (list_len == 0) {
+            p.cb = 1;
+            p.n_chunks = 1;
+        } else {
+            p.cb = (list_len + nc - 1) / nc;
+            p.n_chunks = (list_len + p.cb - 1) / p.cb;
+        }
     } else {
         // enough workgroups to cover 256 CUs several times over
         const long total = (long)dm.rows * entries;
@@ -296,7 +306,8 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
     const int cnt_e = a.n_list ? min(a.n_list[r], a.list_len) : a.list_len;
     const float *er = a.e_tok + (int64_t)r * a.e_stride;
     const int e_beg = chunk * a.cb;
-    const int e_end = min(e_beg + a.cb, a.list_len + a.with_newest);
+    // the last chunk also takes the newest block (decode_plan)
+    const int e_end = chunk == (int)gridDim.x - 1 ? a.list_len + a.with_newest : e_beg + a.cb;
     const bf16_t *q = static_cast<const bf16_t *>(a.q);
 
     // B operand of S^T = K Q^T: lane holds q[head col][32s + 8grp .. +7].
