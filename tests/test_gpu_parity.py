@@ -277,6 +277,11 @@ EDGE = {
     # GQA extremes and head_dim 64 in bf16
     "gqa1_d64": dict(n_q_heads=3, n_kv_heads=3, head_dim=64, context=1300, steps=20),
     "gqa8": dict(n_q_heads=16, n_kv_heads=2, context=1300, steps=20),
+    # the other group sizes: 2, 5 (640 query elements: the certified
+    # rescoring's second query pass is partial) and 6 at head_dim 64
+    "gqa2": dict(n_q_heads=4, n_kv_heads=2, context=1300, steps=12),
+    "gqa5": dict(n_q_heads=10, n_kv_heads=2, context=1300, steps=12),
+    "gqa6_d64": dict(n_q_heads=12, n_kv_heads=2, head_dim=64, context=1300, steps=12),
     # ragged: context ends one token before a block boundary
     "ragged_boundary": dict(context=2047, steps=3, k_e=5, k_q=5),
     # the largest supported budget (eviction budget above 64: LDS top-k at start)

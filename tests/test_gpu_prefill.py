@@ -29,6 +29,15 @@ PREFILL = {
                                key_offset_std=0.5),
     # the budget covers every earlier block: dense causal attention
     "prefill_dense": Workload("prefill_dense", 3003, 1, 4, 1, 128, 200, 1, 4, 4, "bf16"),
+    # GQA 8: a query block's 512 query rows take two workgroups of the kernel
+    "prefill_g8": Workload("prefill_g8", 3004, 1, 8, 1, 128, 600, 1, 2, 3, "bf16",
+                           key_offset_std=0.5),
+    # no grouping (G 1, D 64): one 16-column tile per wave, four waves
+    "prefill_g1_d64": Workload("prefill_g1_d64", 3005, 2, 2, 2, 64, 450, 1, 3, 2, "bf16",
+                               key_offset_std=0.5),
+    # GQA 2: four waves of two tiles
+    "prefill_g2": Workload("prefill_g2", 3006, 1, 4, 2, 128, 330, 1, 2, 2, "bf16",
+                           key_offset_std=0.5),
 }
 
 
@@ -88,7 +97,8 @@ def _prefill_trace(w: Workload, e_scale: float = 1.0):
 
 
 @pytest.mark.parametrize("name,e_scale", [(n, 1.0) for n in PREFILL] + [
-    ("prefill_bf16", 40.0), ("prefill_bf16:pbf16", 1.0), ("prefill_g3_d64:pbf16", 1.0)])
+    ("prefill_bf16", 40.0), ("prefill_g8", 40.0), ("prefill_bf16:pbf16", 1.0),
+    ("prefill_g3_d64:pbf16", 1.0)])
 def test_prefill_parity(name, e_scale):
     """e_scale 40: eviction logits up to ~150 in magnitude, past float32's exp
     range; the softmax's running base keeps every exponential bounded, and a
@@ -218,8 +228,8 @@ def test_prefill_fullsize_sampled():
             np.testing.assert_allclose(got, ref.out, err_msg=f"row {r} query block {i}", **TOL)
 
 
-@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_g3_d64", "prefill_bf16:pbf16",
-                                  "prefill_g3_d64:pbf16"])
+@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_g3_d64", "prefill_g8",
+                                  "prefill_bf16:pbf16", "prefill_g3_d64:pbf16"])
 def test_pooled_queries_bit_exact(name):
     """nosa_prefill_pool_queries against the oracle's pooled query of every
     (query block, sequence, head), the last block ragged: bit for bit (the
