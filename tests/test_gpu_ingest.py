@@ -17,10 +17,15 @@ def _vt_token_at(pos: int) -> int:
     return 32 * (pos // 32) + 16 * ((pos % 8) // 4) + 4 * ((pos % 32) // 8) + pos % 4
 
 
-@pytest.mark.parametrize("dtype,D,G,pos,pooled", [
-    ("bf16", 128, 4, 10, "f32"), ("bf16", 128, 4, 63, "f32"), ("bf16", 64, 3, 63, "f32"),
-    ("f32", 64, 2, 63, "f32"), ("bf16", 128, 4, 63, "bf16"), ("bf16", 64, 3, 63, "bf16")])
-def test_ingest_outputs(dtype, D, G, pos, pooled):
+@pytest.mark.parametrize("dtype,D,G,pos,pooled,hidden", [
+    ("bf16", 128, 4, 10, "f32", 384), ("bf16", 128, 4, 63, "f32", 384),
+    ("bf16", 64, 3, 63, "f32", 384), ("f32", 64, 2, 63, "f32", 384),
+    ("bf16", 128, 4, 63, "bf16", 384), ("bf16", 64, 3, 63, "bf16", 384),
+    ("bf16", 128, 8, 63, "f32", 384), ("bf16", 64, 1, 63, "f32", 384),
+    # hidden sizes that are not a whole number of 16-byte vectors: the
+    # eviction head's element-wise loop
+    ("bf16", 128, 4, 63, "f32", 389), ("f32", 64, 2, 30, "f32", 390)])
+def test_ingest_outputs(dtype, D, G, pos, pooled, hidden):
     """One launch: q split and the K/V slot bit for bit, the eviction logit
     within float32 summation error of the double sum, and (pos 63) the block's
     pooled keys bit for bit (the oracle's exact means rounded once to the
@@ -28,7 +33,7 @@ def test_ingest_outputs(dtype, D, G, pos, pooled):
     import oracle
     gh = _gpu()
     from trainable_block_sparse_nosa_amd import _lib as L
-    B, Hkv, nb, hidden = 2, 2, 8, 384
+    B, Hkv, nb = 2, 2, 8
     Hq = G * Hkv
     rows = B * Hkv
     w = synth.Workload("ingest_probe", 77, B, Hq, Hkv, D, 0, 1, 2, 2, dtype)
