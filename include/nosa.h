@@ -30,7 +30,9 @@
  * ---------------------------------------
  * Ownership: the caller owns every buffer. Device buffers are plain device
  *   pointers; "pinned host" buffers come from nosa_host_alloc. The library
- *   keeps no allocation and no mutable state between calls.
+ *   keeps no allocation and no mutable state between calls, except the
+ *   scratch array of nosa_sparse_decode_noalloc (one per GPU, for the life
+ *   of the process) and the device addresses of that array it caches.
  * Streams: every call only enqueues work on `stream` (a hipStream_t, may be
  *   NULL for the null stream) and never synchronises. Host-side arguments
  *   (shape, step) are read during the call and may be reused afterwards.
