@@ -244,3 +244,51 @@ def test_kbar_bytes_by_dtype():
     assert L.lib().nosa_kbar_bytes(ctypes.byref(bad)) == 0
     with pytest.raises(L.NosaError):
         L.nosa_kbar_bytes(bad)
+
+
+def test_plan_and_sizes_over_random_shapes():
+    """Host-side sizing over random valid shapes: every split-K plan fits the
+    workspace the library asks for, including the two partial calls of an
+    overlapped step (the eviction set with the newest block, then the
+    query-aware set) in one workspace; a plan has at least one chunk when
+    anything is attended and never more chunks than entries; with the
+    matrix-core kernel at most ceil(256 / rows) chunks per row."""
+    hypothesis = pytest.importorskip("hypothesis")
+    from hypothesis import given, settings, strategies as st
+    from trainable_block_sparse_nosa_amd import _lib as L
+
+    @st.composite
+    def shapes(draw):
+        D = draw(st.sampled_from([64, 128]))
+        dtype = L.NOSA_F32 if D == 64 and draw(st.booleans()) else L.NOSA_BF16
+        kind = draw(st.sampled_from([L.NOSA_DECODE_AUTO, L.NOSA_DECODE_VALU]
+                                    + ([L.NOSA_DECODE_MFMA] if dtype == L.NOSA_BF16 else [])))
+        k_e = draw(st.integers(0, 128))
+        k_q = draw(st.integers(1 if k_e == 0 else 0, 128 - k_e))
+        hkv = draw(st.integers(1, 8))
+        G = draw(st.integers(1, 8))
+        return L.make_shape(draw(st.integers(1, 64)), G * hkv, hkv, D, k_e, k_q,
+                            draw(st.integers(k_e + k_q, 4096)), dtype, decode_kernel=kind)
+
+    @settings(max_examples=300, deadline=None)
+    @given(shapes(), st.data())
+    def check(sh, data):
+        k = sh.k_e + sh.k_q
+        rows, G, D = sh.batch * sh.n_kv_heads, sh.n_q_heads // sh.n_kv_heads, sh.head_dim
+        cap = k + 2
+        assert L.nosa_decode_workspace_size(sh) >= rows * cap * G * (D + 2) * 4
+        mfma = sh.decode_kernel == L.NOSA_DECODE_MFMA or (
+            sh.decode_kernel == L.NOSA_DECODE_AUTO and sh.dtype == L.NOSA_BF16)
+        n = data.draw(st.integers(0, k))
+        for newest in (0, 1):
+            c = L.nosa_decode_chunks(sh, n, newest)
+            if n + newest == 0:
+                assert c == 0
+                continue
+            assert 1 <= c <= min(n + newest, cap)
+            if mfma:
+                assert c <= max(1, -(-256 // rows))
+        assert L.nosa_decode_chunks(sh, sh.k_e, 1) + L.nosa_decode_chunks(sh, sh.k_q, 0) <= cap
+        assert L.lib().nosa_decode_chunks(ctypes.byref(sh), k + 1, 1) == -1
+
+    check()
