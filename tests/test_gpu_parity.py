@@ -282,6 +282,7 @@ EDGE = {
     "gqa2": dict(n_q_heads=4, n_kv_heads=2, context=1300, steps=12),
     "gqa5": dict(n_q_heads=10, n_kv_heads=2, context=1300, steps=12),
     "gqa6_d64": dict(n_q_heads=12, n_kv_heads=2, head_dim=64, context=1300, steps=12),
+    "gqa8_d64": dict(n_q_heads=16, n_kv_heads=2, head_dim=64, context=1300, steps=12),
     # ragged: context ends one token before a block boundary
     "ragged_boundary": dict(context=2047, steps=3, k_e=5, k_q=5),
     # the largest supported budget (eviction budget above 64: LDS top-k at start)
@@ -377,11 +378,23 @@ def test_parity_edge_cases_pooled_bf16(edge):
             _compare_step(w, tr, t, r, res[t])
 
 
-def test_offload_edge_gqa1_short():
+OFFLOAD_EDGE = {
+    # fewer tokens than two blocks at the start, one query head per KV head
+    "gqa1_short": dict(seed=3100, n_q_heads=2, n_kv_heads=2, context=100, steps=40, k_e=2,
+                       k_q=3),
+    # head_dim 64 (16 KiB blocks) with eight query heads per KV head
+    "d64_gqa8": dict(seed=3101, n_q_heads=16, n_kv_heads=2, head_dim=64, context=1500,
+                     steps=20),
+    # float32 KV over the HBM cache (the VALU attention kernel)
+    "f32_d64": dict(seed=3102, dtype="f32", head_dim=64, context=1200, steps=20),
+}
+
+
+@pytest.mark.parametrize("edge", sorted(OFFLOAD_EDGE))
+def test_offload_edge_cases(edge):
     gh = _gpu()
-    w = synth.WORKLOADS["small_offload"].scaled(name="edge_offload_short", seed=3100,
-                                               n_q_heads=2, n_kv_heads=2, context=100, steps=40,
-                                               k_e=2, k_q=3)
+    w = synth.WORKLOADS["small_offload"].scaled(name="edge_offload_" + edge,
+                                               **OFFLOAD_EDGE[edge])
     tr = oracle_trace(w)
     inp = gh.upload(w, ov=tr.ov)
     _, res = gh.run(w, inp, list(range(w.steps)))
