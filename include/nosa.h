@@ -294,12 +294,13 @@ nosa_status nosa_select_swap(const nosa_shape *shape, const float *s_q, const fl
 
 /* nosa_score_blocks and nosa_select (and, when the six cache pointers are
  * given, the set difference as in nosa_select_swap) in one call. With more
- * than 128 rows (bf16), or float32 inputs, it is one launch: one workgroup
- * per row computes the row's query-aware scores into on-chip memory and
- * selects from them. With bf16 and at most 128 rows, too few workgroups to
- * fill the GPU that way, the scores are computed on a grid split over each
- * row's candidates and the selection follows as a second launch on the same
- * stream. With bf16 keys and float32 pooled keys the scores come from the
+ * than 128 rows (bf16; more than 256 with bf16 keys and float32 pooled
+ * keys), or float32 inputs, it is one launch: one workgroup per row computes
+ * the row's query-aware scores into on-chip memory and selects from them.
+ * With fewer bf16 rows, too few workgroups to fill the GPU that way, the
+ * scores are computed on a grid split over each row's candidates and the
+ * selection follows as a second launch on the same stream. With bf16 keys
+ * and float32 pooled keys the scores come from the
  * pooled keys' bfloat16 copy (half the bytes); every candidate whose score
  * interval (copy score +- scale * sum_h ||q_h|| * radius) reaches the lowest
  * lower bound of that first top k_q is then scored again from the float32

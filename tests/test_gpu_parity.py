@@ -325,13 +325,13 @@ def test_parity_edge_cases(edge, overlap):
 NEAR_TIES = {
     # 4 rows: scores on the split grid, then the selection
     "split": dict(context=10000, steps=12, key_common=64.0),
-    # 132 rows: scores inside the selecting workgroup
-    "fused": dict(batch=33, n_q_heads=8, n_kv_heads=4, context=10000, steps=4, key_common=64.0),
+    # 260 rows: scores inside the selecting workgroup
+    "fused": dict(batch=65, n_q_heads=8, n_kv_heads=4, context=10000, steps=4, key_common=64.0),
     # head_dim 64 (a quarter of D is four 16-byte loads per lane), one query head per
     # KV head; split and fused
     "d64_g1": dict(n_q_heads=3, n_kv_heads=3, head_dim=64, context=10000, steps=6,
                    key_common=64.0),
-    "d64_g1_fused": dict(batch=44, n_q_heads=3, n_kv_heads=3, head_dim=64, context=10000,
+    "d64_g1_fused": dict(batch=86, n_q_heads=3, n_kv_heads=3, head_dim=64, context=10000,
                          steps=3, key_common=64.0),
     # eight query heads per KV head
     "gqa8": dict(n_q_heads=16, n_kv_heads=2, context=10000, steps=6, key_common=64.0),

@@ -45,7 +45,8 @@ hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, i
                          hipStream_t st);
 
 // Scores and selection (and the set difference when swap != nullptr): with
-// bf16 KV and at most SPLIT_SCORE_MAX_ROWS rows, the scores come from a grid
+// bf16 KV and at most SPLIT_SCORE_MAX_ROWS rows (CERT_SPLIT_MAX_ROWS with
+// float32 pooled keys, certified scoring), the scores come from a grid
 // split over each row's candidates into s_q and a second launch selects from
 // them; otherwise the selecting workgroup (one per row) computes its row's
 // scores itself, writing them to s_q as well. dstep != nullptr: n_cand and

@@ -1446,6 +1446,11 @@ hipError_t launch_select(const Dims &dm, const float *s_q, const float *e_blk, i
 // rows x 1024 53 + 10.8 vs 59-62 us (with a workgroup per CU the fused form
 // hides each row's selection behind other rows' scoring).
 constexpr int SPLIT_SCORE_MAX_ROWS = 128;
+// The same for certified scoring, whose selection also rescores the rows'
+// near ties: at 256 rows x 1024 candidates the split form took 65.5-66.0 us
+// against 70.5-70.6 (whole score + select stage), at 512 rows x 512 the two
+// are level (rocprof: 44.1 + 18.3 against 63.8 us).
+constexpr int CERT_SPLIT_MAX_ROWS = 256;
 
 template <typename T, typename TK, int D, int G>
 hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, float *s_q,
@@ -1459,7 +1464,7 @@ hipError_t launch_score_select(const Dims &dm, const void *q, const void *kbar, 
         const bf16_t *shadow = reinterpret_cast<const bf16_t *>(kb + kbar_shadow_offset(dm));
         const CertArgs ca{static_cast<const bf16_t *>(q), static_cast<const float *>(kbar),
                           reinterpret_cast<const float *>(kb + kbar_radius_offset(dm)), 0};
-        if (dm.rows <= SPLIT_SCORE_MAX_ROWS) {
+        if (dm.rows <= CERT_SPLIT_MAX_ROWS) {
             const hipError_t e =
                 launch_score<bf16_t, bf16_t, D, G>(dm, q, shadow, n_cand, s_q, st, dstep);
             if (e != hipSuccess) return e;
