@@ -683,3 +683,51 @@ def test_resume_from_state_dict(name, append):
         got = gh.snapshot(second, w)
         for key, want in ref[t].items():
             np.testing.assert_array_equal(got[key], want, err_msg=f"{name} t={t} {key}")
+
+
+@pytest.mark.parametrize("case", ["rows4", "rows64"])
+def test_attend_any_list_length(case):
+    """nosa_decode_attend over the first n candidate blocks of every row, with
+    and without the newest block, for list lengths that split unevenly over
+    the chunks (4 rows: up to n + 1 chunks of one block per wave; 64 rows:
+    4 chunks, the newest joining the last), against the oracle's softmax over
+    exactly those tokens: every entry is attended once, whatever the length."""
+    import math
+    import oracle
+    from harness import row_kv
+    gh = _gpu()
+    from trainable_block_sparse_nosa_amd import _lib as L
+    base = synth.WORKLOADS["small_bf16"]
+    w = base if case == "rows4" else base.scaled(name="attend_rows64", seed=3600, batch=32,
+                                                 context=1500, steps=1)
+    inp = gh.upload(w, steps=1)
+    layer = gh.make_layer(w, inp)
+    n_tok = w.n_tokens(0)
+    c = (n_tok - 1) // 64
+    k = layer.k
+    assert c >= k
+    st = L.make_step(n_tok, c)
+    blocks = torch.arange(k, dtype=torch.int32, device="cuda").repeat(w.rows, 1).contiguous()
+    q = inp.q[0].float().cpu().numpy()
+    G, D = w.group, w.head_dim
+    rows = {}
+    for r in range(w.rows):
+        b, g = divmod(r, w.n_kv_heads)
+        K, V = row_kv(w, 0, b, g)
+        rows[r] = (q[b, g * G:(g + 1) * G], K, V, synth.evict_row(w, 0, b, g))
+    for n in sorted({1, 2, 7, 8, 9, k // 2, k - 1, k}):
+        for newest in (1, 0):
+            n_list = torch.full((w.rows,), n, dtype=torch.int32, device="cuda")
+            out = torch.full_like(layer.out, 7)
+            L.nosa_decode_attend(layer.shape, inp.q[0], layer.kv, layer.kv_row_blocks,
+                                 L.NOSA_KV_FULL, blocks, n_list, k, n, newest,
+                                 layer._kv_ptr(c), layer.kv_row_blocks, st, layer.e_tok,
+                                 layer.e_stride, layer.ws, layer.ws_bytes, out)
+            torch.cuda.synchronize()
+            got = out.float().cpu().numpy()
+            tokens = list(range(64 * n)) + (list(range(64 * c, n_tok)) if newest else [])
+            for r, (qr, K, V, e) in rows.items():
+                b, g = divmod(r, w.n_kv_heads)
+                ref = oracle.attend_tokens(qr, K, V, e, tokens, 1.0 / math.sqrt(D))
+                np.testing.assert_allclose(got[b, g * G:(g + 1) * G], ref, rtol=2e-2, atol=2e-3,
+                                           err_msg=f"{case} n={n} newest={newest} row {r}")
