@@ -569,9 +569,8 @@ struct ScoresGlobal {
 
 // ScoresFused: computed by the selecting workgroup itself into LDS (and
 // written to s_q as well), with the same arithmetic as score_kernel: lane <->
-// sub-block, U sub-blocks per thread per pass with all their 16-byte loads in
-// flight, DPP quad max over a block's sub-blocks, then the head sum. Needs the
-// whole workgroup (barriers inside).
+// sub-block, U sub-blocks per thread per pass, DPP quad max over a block's
+// sub-blocks, then the head sum. Needs the whole workgroup (barriers inside).
 template <typename TQ, typename TK, int D, int G>
 struct ScoresFused {
     static constexpr bool kCert = false;
@@ -590,42 +589,58 @@ struct ScoresFused {
         __syncthreads();
         const int nsb = M * n_cand;
         float *out = s_q ? s_q + (int64_t)r * dm.max_blocks : nullptr;
+        // With a whole sub-block per thread at D = 128 the loads of a pass
+        // would take 128 registers, which leaves one 512-thread workgroup per
+        // CU: the dimension vectors are taken in halves instead (each half's
+        // loads in flight together), the sums running on in the same order.
+        constexpr int HV = U * NV > 16 ? 2 : 1, NVH = NV / HV;
         for (int base = 0; base < nsb; base += U * nt) {
             // compiler-only memory barrier: keeps the LDS reads of q inside the
             // pass (hoisted out of it, G * D floats would not fit in registers)
             __asm__ volatile("" ::: "memory");
-            uint4 raw[U][NV];
+            float acc[U][G];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int sb = base + u * nt + tid;
-                if (sb < nsb) {
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-                    for (int dv = 0; dv < NV; ++dv)
-                        raw[u][dv] = *reinterpret_cast<const uint4 *>(kbar + kbar_vec<TK, D>(dm, r, sb, dv));
+                for (int h = 0; h < G; ++h) acc[u][h] = 0.f;
+#pragma unroll
+            for (int hv = 0; hv < HV; ++hv) {
+                uint4 raw[U][NVH];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int sb = base + u * nt + tid;
+                    if (sb < nsb) {
+#pragma unroll
+                        for (int i = 0; i < NVH; ++i)
+                            raw[u][i] = *reinterpret_cast<const uint4 *>(
+                                kbar + kbar_vec<TK, D>(dm, r, sb, hv * NVH + i));
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int sb = base + u * nt + tid;
+                    if (sb < nsb) {
+#pragma unroll
+                        for (int i = 0; i < NVH; ++i) {
+                            const int dv = hv * NVH + i;
+                            float x[V];
+                            KbarVec<TK>::unpack(raw[u][i], x);
+#pragma unroll
+                            for (int h = 0; h < G; ++h)
+#pragma unroll
+                                for (int e = 0; e < V; ++e)
+                                    acc[u][h] = fmaf(qs[h][dv * V + e], x[e], acc[u][h]);
+                        }
+                    }
                 }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int sb = base + u * nt + tid;
-                float acc[G];
-#pragma unroll
-                for (int h = 0; h < G; ++h) acc[h] = 0.f;
-                if (sb < nsb) {
-#pragma unroll
-                    for (int dv = 0; dv < NV; ++dv) {
-                        float x[V];
-                        KbarVec<TK>::unpack(raw[u][dv], x);
-#pragma unroll
-                        for (int h = 0; h < G; ++h)
-#pragma unroll
-                            for (int e = 0; e < V; ++e)
-                                acc[h] = fmaf(qs[h][dv * V + e], x[e], acc[h]);
-                    }
-                }
                 // every lane takes part in the quad reductions (nt keeps quads whole)
                 float sum = 0.f;
 #pragma unroll
-                for (int h = 0; h < G; ++h) sum += quad_max(acc[h]);
+                for (int h = 0; h < G; ++h) sum += quad_max(acc[u][h]);
                 if (sb < nsb && (sb & (M - 1)) == 0) {
                     sc[sb / M] = sum;
                     if (out) out[sb / M] = sum;
@@ -959,8 +974,13 @@ struct BatchArgs {
     const int32_t *dstep;  // device step record: n_cand and n_prev from it
 };
 
+// Four waves per SIMD at most 128 registers each: two selecting workgroups
+// share a CU, so that one's selection (latency-bound) runs beside the other's
+// scoring. The batched prefill selection over float32 pooled keys went from
+// 2.57-2.61 to 1.16-1.17 ms on the 32k context when it reached that (its
+// scoring's loads had taken 162 registers).
 template <typename Src>
-__global__ void __launch_bounds__(SELECT_THREADS)
+__global__ void __launch_bounds__(SELECT_THREADS, 4)
 select_kernel(Dims dm, Src src, const float *__restrict__ e_blk, int n_cand0,
               int n_prev_arg, int P, uint32_t *__restrict__ ge_bits, uint32_t *__restrict__ ev_bits,
               int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
