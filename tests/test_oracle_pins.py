@@ -6,7 +6,6 @@ routine, brute force, a closed form, or an invariant the NOSA pages state
 """
 import itertools
 import json
-import math
 import os
 
 import numpy as np
