@@ -51,14 +51,25 @@
  * Layouts (element type = shape.dtype unless stated)
  * --------------------------------------------------
  * q, out     [batch][n_q_heads][D]
- * KV block   one block-unit of 2*S*D elements: the K tile [S][D] (token
- *            major) followed by the V tile stored transposed, [D][S], whose
- *            row positions hold the block's tokens in this order: inside
- *            each half of 32, positions 8j..8j+7 hold tokens 4j..4j+3 and
- *            16+4j..16+4j+3 of that half (the order the MFMA decode consumes
- *            them in). A "KV buffer" is [rows][row_blocks][2*S*D]; the full
- *            KV, an HBM block cache (k slots per row) and the newest-block
- *            buffer (one block per row) all use it with their own row_blocks.
+ * KV block   one block-unit of 2*S*D elements (S = 64): the K tile, S*D
+ *            elements, then the V tile transposed (V^T, D rows of S
+ *            positions), D*S elements. Position p of a V^T row holds token
+ *            vt(p) of the block: inside each half of 32, positions 8j..8j+7
+ *            hold tokens 4j..4j+3 and 16+4j..16+4j+3 of that half. Both tiles
+ *            are stored as 1 KiB fragments of 64 16-byte vectors (E = 16 /
+ *            element size elements each; vector l has col = l % 16, grp =
+ *            l / 16), each fragment one matrix-core operand of a wave:
+ *              K   fragment t*(D/4E) + s, vector l: token 16t + col,
+ *                  dimensions (4s + grp)*E .. + E-1;
+ *              V^T fragment dt*(S/4E) + s, vector l: dimension 16dt + col,
+ *                  positions (4s + grp)*E .. + E-1.
+ *            So K[tok][d] is at element
+ *              ((tok/16 * D/4E + d/4E) * 64 + tok%16 + 16 * (d/E % 4)) * E + d%E
+ *            and V[tok][d], with p the position of tok, at S*D +
+ *              ((d/16 * S/4E + p/4E) * 64 + d%16 + 16 * (p/E % 4)) * E + p%E.
+ *            A "KV buffer" is [rows][row_blocks][2*S*D]; the full KV, an HBM
+ *            block cache (k slots per row) and the newest-block buffer (one
+ *            block per row) all use it with their own row_blocks.
  * e_tok      float32 [rows][e_row_stride]: per-token eviction scores,
  *            pre-exponential. nosa_sparse_decode reads them a block at a
  *            time: e_tok is 16-byte aligned, e_row_stride a multiple of 4 and
@@ -235,8 +246,8 @@ nosa_status nosa_prefill_attention(const nosa_shape *shape, const void *q, int32
 /* Write the newest token of every row into the block-unit KV buffer `kv`
  * (device memory or the device alias of pinned host memory; kv_row_blocks
  * blocks per row): token slot pos (0..S-1) of block `block` receives
- * k_new[row][D] as row pos of the K tile and v_new[row][D] as column pos of
- * the V^T tile in its stored token order. k_new and v_new are [rows][D] in the
+ * k_new[row][D] as token pos of the K tile and v_new[row][D] as token pos of
+ * the V^T tile (the block layout above). k_new and v_new are [rows][D] in the
  * KV dtype, rows = batch * n_kv_heads. This is the KV-cache write the
  * decode step assumes (the pages keep the cache in block-sized units;
  * "2. System: NOSI", Optimized Memory Layout): with the newest-block buffer
@@ -347,6 +358,13 @@ nosa_status nosa_fetch_blocks(const nosa_shape *shape, const void *src_kv, int64
 /* Bytes of the kbar buffer for this shape (layout above); 0 for an invalid
  * shape. */
 size_t nosa_kbar_bytes(const nosa_shape *shape);
+
+/* Element offsets inside one KV block-unit of K[tok][d] (k_off) and of
+ * V[tok][d] (v_off) for the shape's head_dim and dtype, the layout under
+ * "KV block" above: each a host array of S*D int64 written as [tok][d].
+ * Host only (no device work). Errors: the shape's (NOSA_ERR_INVALID_ARGUMENT,
+ * NOSA_ERR_UNSUPPORTED), NOSA_ERR_INVALID_ARGUMENT for a NULL array. */
+nosa_status nosa_block_offsets(const nosa_shape *shape, int64_t *k_off, int64_t *v_off);
 
 /* Workspace bytes the attention calls need for this shape: split-K partials
  * of up to k + 2 chunks per row (one call over the whole selection, or two

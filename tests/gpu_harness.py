@@ -15,7 +15,8 @@ import synth
 from synth import Overrides, Workload
 from trainable_block_sparse_nosa_amd import _lib as L
 from trainable_block_sparse_nosa_amd.hostmem import PinnedBuffer
-from trainable_block_sparse_nosa_amd.pipeline import DecodeLayer, pack_blocks
+from trainable_block_sparse_nosa_amd.pipeline import (DecodeLayer, block_offsets,  # noqa: F401
+                                                      pack_blocks, unpack_blocks)
 
 
 def nosa_dtype(w: Workload) -> int:

@@ -292,3 +292,52 @@ def test_plan_and_sizes_over_random_shapes():
         assert L.lib().nosa_decode_chunks(ctypes.byref(sh), k + 1, 1) == -1
 
     check()
+
+
+@pytest.mark.parametrize("D,dt", [(64, "bf16"), (128, "bf16"), (64, "f32")])
+def test_block_layout(D, dt):
+    """The block layout the library reports equals the packing the Python layer
+    uses, places every element once, and makes each bf16 fragment exactly the
+    A operand of v_mfma_f32_16x16x32_bf16 (lane l: row l % 16, k-elements
+    8 (l / 16) .. + 7 of a 32-wide step), for K and for the transposed V."""
+    import numpy as np
+    from trainable_block_sparse_nosa_amd import _lib as L
+    from trainable_block_sparse_nosa_amd.pipeline import (VT_TOKEN_AT, block_offsets, pack_blocks,
+                                                          unpack_blocks)
+    dtype = L.NOSA_BF16 if dt == "bf16" else L.NOSA_F32
+    itemsize = 2 if dt == "bf16" else 4
+    k_off, v_off = L.nosa_block_offsets(_shape(head_dim=D, dtype=dtype))
+    k_py, v_py = block_offsets(D, itemsize)
+    np.testing.assert_array_equal(k_off, k_py)
+    np.testing.assert_array_equal(v_off, v_py)
+    every = np.sort(np.concatenate([k_off.ravel(), v_off.ravel()]))
+    np.testing.assert_array_equal(every, np.arange(2 * 64 * D))
+    assert k_off.max() < 64 * D <= v_off.min()
+    # pack / unpack agree with the offsets and invert each other
+    rng = np.random.default_rng(7)
+    npt = np.uint16 if dt == "bf16" else np.float32
+    K = rng.integers(1, 1 << 15, (130, D)).astype(npt)
+    V = rng.integers(1, 1 << 15, (130, D)).astype(npt)
+    P = pack_blocks(K, V, 3)
+    for b in range(2):
+        np.testing.assert_array_equal(P[b][k_off], K[64 * b:64 * b + 64])
+        np.testing.assert_array_equal(P[b][v_off], V[64 * b:64 * b + 64])
+    K2, V2 = unpack_blocks(P, D)
+    np.testing.assert_array_equal(K2[:130], K)
+    np.testing.assert_array_equal(V2[:130], V)
+    assert not K2[130:].any() and not V2[130:].any()
+    if dt != "bf16":
+        return
+    # fragment f, lane l = the 8 elements at 8 (64 f + l)
+    for t in range(4):
+        for s in range(D // 32):
+            for lane in range(64):
+                at = 8 * (64 * (t * (D // 32) + s) + lane)
+                row, k0 = 16 * t + lane % 16, 32 * s + 8 * (lane // 16)
+                np.testing.assert_array_equal(P[0][at:at + 8], K[row, k0:k0 + 8])
+    for dtile in range(D // 16):
+        for s in range(2):
+            for lane in range(64):
+                at = 64 * D + 8 * (64 * (2 * dtile + s) + lane)
+                d, p0 = 16 * dtile + lane % 16, 32 * s + 8 * (lane // 16)
+                np.testing.assert_array_equal(P[0][at:at + 8], V[VT_TOKEN_AT[p0:p0 + 8], d])

@@ -91,15 +91,14 @@ def test_fullsize_offload_128k_device_append():
     D, j = w.head_dim, w.n_cand(0)
     assert w.n_cand(steps - 1) == j + 1
     host = inp.kv.array(np.uint16, (w.rows, inp.nb, 2 * 64 * D))
-    vt = np.array([32 * (p // 32) + 16 * ((p % 8) // 4) + 4 * ((p % 32) // 8) + p % 4
-                   for p in range(64)])
     for r in range(w.rows):
         b, g = divmod(r, w.n_kv_heads)
         K, V = row_kv(w, 0, b, g)
-        np.testing.assert_array_equal(host[r, j, :64 * D].reshape(64, D),
-                                      synth.bf16_bits(K[64 * j:64 * j + 64]), err_msg=f"row {r} K")
-        np.testing.assert_array_equal(host[r, j, 64 * D:].reshape(D, 64),
-                                      synth.bf16_bits(V[64 * j + vt]).T, err_msg=f"row {r} V")
+        k_blk, v_blk = gh.unpack_blocks(host[r, j:j + 1], D)
+        np.testing.assert_array_equal(k_blk, synth.bf16_bits(K[64 * j:64 * j + 64]),
+                                      err_msg=f"row {r} K")
+        np.testing.assert_array_equal(v_blk, synth.bf16_bits(V[64 * j:64 * j + 64]),
+                                      err_msg=f"row {r} V")
     inp.kv.free()
 
 

@@ -12,11 +12,6 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-def _vt_token_at(pos: int) -> int:
-    # stored V^T token order (the layout include/nosa.h documents)
-    return 32 * (pos // 32) + 16 * ((pos % 8) // 4) + 4 * ((pos % 32) // 8) + pos % 4
-
-
 @pytest.mark.parametrize("dtype,D,G,pos,pooled,hidden", [
     ("bf16", 128, 4, 10, "f32", 384), ("bf16", 128, 4, 63, "f32", 384),
     ("bf16", 64, 3, 63, "f32", 384), ("f32", 64, 2, 63, "f32", 384),
@@ -46,19 +41,18 @@ def test_ingest_outputs(dtype, D, G, pos, pooled, hidden):
     V = cast(rng.normal(size=(rows, 64, D)).astype(np.float32))
     e_tok = np.zeros((rows, nb * 64), np.float32)
     e_tok[:, 64 * j:64 * j + 64] = rng.normal(size=(rows, 64)).astype(np.float32)
-    kv_host = np.zeros((rows, nb, 2 * 64 * D), np.float32)
+    conv = (lambda a: a) if dtype == "f32" else synth.bf16_bits
+    kv_host = np.zeros((rows, nb, 2 * 64 * D), np.float32 if dtype == "f32" else np.uint16)
     for r in range(rows):
         Kp, Vp = K[r].copy(), V[r].copy()
         Kp[pos:], Vp[pos:] = 0, 0               # slots from pos on are not written yet
-        kv_host[r, j, :64 * D] = Kp.reshape(-1)
-        kv_host[r, j, 64 * D:] = Vp[[_vt_token_at(p) for p in range(64)]].T.reshape(-1)
+        kv_host[r, j] = gh.pack_blocks(conv(Kp), conv(Vp), 1)[0]
     qkv = cast(rng.normal(size=(B, (Hq + 2 * Hkv) * D)).astype(np.float32))
     x = cast(rng.normal(size=(B, hidden)).astype(np.float32))
     W = cast((rng.normal(size=(Hkv, hidden)) / np.sqrt(hidden)).astype(np.float32))
     bias = np.array([0.25, -1.5], np.float32)
     dev = lambda a: gh.to_device(np.ascontiguousarray(a), w)
-    conv = (lambda a: a) if dtype == "f32" else synth.bf16_bits
-    kv = dev(conv(kv_host))
+    kv = dev(kv_host)
     q_out = torch.zeros(B, Hq, D, dtype=kv.dtype, device="cuda")
     e_dev = torch.from_numpy(e_tok).cuda()
     V8 = 16 // (4 if pooled == "f32" else 2)
@@ -82,15 +76,15 @@ def test_ingest_outputs(dtype, D, G, pos, pooled, hidden):
     got_e = e_dev.cpu().numpy()
     kb = kbar.float().cpu().numpy().transpose(0, 1, 3, 2, 4).reshape(rows, -1, D)
     got_eb = e_blk.cpu().numpy()
-    vt = np.array([_vt_token_at(p) for p in range(64)])
+    k_off, v_off = gh.block_offsets(D, 4 if dtype == "f32" else 2)
     for b in range(B):
         q, k, v = oracle.qkv_split(qkv[b], Hq, Hkv, D)
         np.testing.assert_array_equal(got_q[b], q)
         for g in range(Hkv):
             r = b * Hkv + g
             blk = got_kv[r, j]
-            np.testing.assert_array_equal(blk[pos * D:(pos + 1) * D], k[g])
-            np.testing.assert_array_equal(blk[64 * D:].reshape(D, 64)[:, int(np.where(vt == pos)[0][0])], v[g])
+            np.testing.assert_array_equal(blk[k_off[pos]], k[g])
+            np.testing.assert_array_equal(blk[v_off[pos]], v[g])
             e_ref = oracle.evict_logit(x[b], W[g], bias[g])
             scale = float(np.sum(np.abs(x[b].astype(np.float64) * W[g].astype(np.float64))))
             assert abs(got_e[r, tok] - e_ref) <= 1e-6 * max(scale, 1.0)

@@ -152,11 +152,6 @@ def test_parity_valu_kernel_bf16(name):
             _compare_step(w, tr, t, r, res[t])
 
 
-def _vt_token_at(pos: int) -> int:
-    # stored V^T token order (the layout include/nosa.h documents)
-    return 32 * (pos // 32) + 16 * ((pos % 8) // 4) + 4 * ((pos % 32) // 8) + pos % 4
-
-
 @pytest.mark.parametrize("name", ["small_f32", "small_bf16", "small_offload"])
 def test_parity_device_append(name):
     """The KV holds the context only; every step's token enters on the GPU
@@ -178,18 +173,14 @@ def test_parity_device_append(name):
         return
     D = w.head_dim
     host = inp.kv.array(np.uint16, (w.rows, inp.nb, 2 * 64 * D))
-    pos = np.arange(64)
-    vt = np.array([_vt_token_at(p) for p in pos])
     for r in range(w.rows):
         b, g = divmod(r, w.n_kv_heads)
         K, V = row_kv(w, 0, b, g)
         for j in range(c0, c1):
-            blk = host[r, j]
-            k_tile = blk[:64 * D].reshape(64, D)
-            v_tile = blk[64 * D:].reshape(D, 64)
+            k_tile, v_tile = gh.unpack_blocks(host[r, j:j + 1], D)
             np.testing.assert_array_equal(k_tile, synth.bf16_bits(K[64 * j:64 * j + 64]),
                                           err_msg=f"row {r} block {j} K")
-            np.testing.assert_array_equal(v_tile, synth.bf16_bits(V[64 * j + vt]).T,
+            np.testing.assert_array_equal(v_tile, synth.bf16_bits(V[64 * j:64 * j + 64]),
                                           err_msg=f"row {r} block {j} V")
 
 
@@ -623,7 +614,7 @@ def test_newest_block_tail_not_finite(base, kernel):
     D = w.head_dim
     kv = inp.kv.cpu()
     bits = kv.view(torch.int16 if w.dtype == "bf16" else torch.int32)
-    pos_of = {_vt_token_at(p): p for p in range(64)}
+    k_off, v_off = gh.block_offsets(D, 2 if w.dtype == "bf16" else 4)
     if w.dtype == "bf16":
         bad = [0x7FC0, 0x7F80, -128]           # NaN, +inf, -inf (0xFF80)
     else:
@@ -631,8 +622,8 @@ def test_newest_block_tail_not_finite(base, kernel):
     for r in range(w.rows):
         for u in range(lo, 64):
             x = bad[u % 3]
-            bits[r, c, u * D:(u + 1) * D] = x
-            bits[r, c, 64 * D + pos_of[u]::64] = x
+            bits[r, c, torch.from_numpy(k_off[u])] = x
+            bits[r, c, torch.from_numpy(v_off[u])] = x
     inp.kv.copy_(kv.to(inp.kv.device))
     e = inp.e_tok.cpu()
     e[:, 64 * c + lo:64 * c + 64] = float("nan")

@@ -286,14 +286,12 @@ def test_prefill_large_values():
 
     inp = gh.upload(w, ov=ov, steps=1)
     kv = inp.kv.cpu()
-    pos_of = {(32 * (p // 32) + 16 * ((p % 8) // 4) + 4 * ((p % 32) // 8) + p % 4): p
-              for p in range(64)}
+    v_off = torch.from_numpy(gh.block_offsets(D, 2)[1])   # V[token][d] in a block
     for r in range(w.rows):
         for j in big_blocks:
-            for u in range(64):
-                kv[r, j, 64 * D + pos_of[u]::64] *= 2.0 ** 17
+            kv[r, j, v_off.reshape(-1)] *= 2.0 ** 17
         j, u = divmod(big_token, 64)
-        kv[r, j, 64 * D + pos_of[u]::64] *= 2.0 ** 40
+        kv[r, j, v_off[u]] *= 2.0 ** 40
     inp.kv.copy_(kv.to(inp.kv.device))
     q_all = gh.to_device(gh.storage(synth.prefill_queries(w, 0, N, ov), w), w)
     layer = gh.make_layer(w, inp)

@@ -11,6 +11,8 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
+
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # NOSA_LIB_PATH may point at another build of the same library (same ABI)
 LIB_PATH = os.environ.get("NOSA_LIB_PATH") or os.path.join(_PKG, "libnosa.so")
@@ -33,7 +35,7 @@ EXPORTS = (
     "nosa_select_parts", "nosa_score_select", "nosa_fetch_blocks", "nosa_append_tokens",
     "nosa_ingest_tokens", "nosa_prefill_pool_queries", "nosa_prefill_select",
     "nosa_prefill_attention", "nosa_kbar_bytes", "nosa_decode_workspace_size",
-    "nosa_decode_chunks",
+    "nosa_decode_chunks", "nosa_block_offsets",
     "nosa_sparse_decode", "nosa_sparse_decode_noalloc", "nosa_decode_partial", "nosa_decode_partial_timed",
     "nosa_decode_combine", "nosa_decode_combine_step", "nosa_decode_attend",
     "nosa_step_advance", "nosa_pool_step", "nosa_append_step", "nosa_score_select_step",
@@ -97,6 +99,7 @@ def _load() -> ctypes.CDLL:
         "nosa_host_free": [P],
         "nosa_read_probe": [P, I64, P, I32, P],
         "nosa_step_advance": [SH, P, P],
+        "nosa_block_offsets": [SH, P, P],
         "nosa_pool_step": [SH, P, I64, P, I64, P, P, P, P],
         "nosa_append_step": [SH, P, P, P, I64, P, P],
         "nosa_score_select_step": [SH, P, P, P, P] + [P] * 12 + [P],
@@ -306,6 +309,17 @@ def nosa_kbar_bytes(shape) -> int:
     if n == 0:
         raise NosaError("nosa_kbar_bytes", NOSA_ERR_INVALID_ARGUMENT)
     return n
+
+
+def nosa_block_offsets(shape):
+    """(k_off, v_off): int64 arrays [64, head_dim], the element offsets of
+    K[tok][d] and V[tok][d] inside one KV block-unit (host only)."""
+    D = shape.head_dim
+    k_off = np.zeros((64, D), np.int64)
+    v_off = np.zeros((64, D), np.int64)
+    _chk("nosa_block_offsets", _L.nosa_block_offsets(
+        ctypes.byref(shape), k_off.ctypes.data, v_off.ctypes.data))
+    return k_off, v_off
 
 
 def nosa_decode_workspace_size(shape) -> int:

@@ -484,6 +484,23 @@ size_t nosa_kbar_bytes(const nosa_shape *shape) {
     return (size_t)kbar_bytes(dm);
 }
 
+nosa_status nosa_block_offsets(const nosa_shape *shape, int64_t *k_off, int64_t *v_off) {
+    Dims dm;
+    nosa_status s = make_dims(shape, &dm);
+    if (s != NOSA_OK) return s;
+    if (!k_off || !v_off) return NOSA_ERR_INVALID_ARGUMENT;
+    return by_type_dim(dm, [&](auto tp, auto dc) -> nosa_status {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        constexpr int D = decltype(dc)::value;
+        for (int t = 0; t < 64; ++t)
+            for (int d = 0; d < D; ++d) {
+                k_off[t * D + d] = kv_k_off<T, D>(t, d);
+                v_off[t * D + d] = kv_v_off<T, D>(t, d);
+            }
+        return NOSA_OK;
+    });
+}
+
 size_t nosa_decode_workspace_size(const nosa_shape *shape) {
     Dims dm;
     if (make_dims(shape, &dm) != NOSA_OK) return 0;

@@ -130,6 +130,71 @@ constexpr bool vt_order_is_inverse() {
 }
 static_assert(vt_order_is_inverse(), "vt_pos_of inverts vt_token_at");
 
+// Block-unit KV layout: a block of 64 tokens is the K tile, S * D elements,
+// then the V^T tile, D * S elements, each stored as 1 KiB fragments of 64
+// 16-byte vectors (E = 16 / sizeof(T) elements each). Vector l of a fragment
+// holds what lane l of a wave loads for a matrix-core operand, with col =
+// l % 16 and grp = l / 16:
+//  K fragment t * NS + s (NS = D / 4E): token 16 t + col, dimensions
+//    (4 s + grp) E .. + E - 1;
+//  V^T fragment dt * NP + s (NP = 64 / 4E): dimension 16 dt + col, stored
+//    positions (4 s + grp) E .. + E - 1 of the V^T row, whose tokens are
+//    vt_token_at(position).
+// For bfloat16 a fragment is exactly one A operand of v_mfma_f32_16x16x32_bf16,
+// so each load instruction of a wave reads 1 KiB of consecutive whole cache
+// lines. Element offsets within the block:
+template <typename T, int D>
+__host__ __device__ constexpr int kv_k_off(int tok, int d) {
+    constexpr int E = 16 / sizeof(T), NS = D / (4 * E);
+    return (((tok / 16) * NS + d / (4 * E)) * 64 + tok % 16 + 16 * ((d / E) % 4)) * E + d % E;
+}
+template <typename T, int D>
+__host__ __device__ constexpr int kv_v_off(int tok, int d) {
+    constexpr int E = 16 / sizeof(T), NP = 64 / (4 * E);
+    const int pos = vt_pos_of(tok);
+    return 64 * D +
+           (((d / 16) * NP + pos / (4 * E)) * 64 + d % 16 + 16 * ((pos / E) % 4)) * E + pos % E;
+}
+// The inverse for the VALU kernel's staging: 16-byte vector v of the K (or
+// V^T) tile holds token (dimension) row and dimensions (positions) col0 ..
+template <typename T, int D>
+__host__ __device__ constexpr void kv_k_vec(int v, int &tok, int &d0) {
+    constexpr int E = 16 / sizeof(T), NS = D / (4 * E);
+    const int f = v / 64, l = v % 64;
+    tok = 16 * (f / NS) + l % 16;
+    d0 = (4 * (f % NS) + l / 16) * E;
+}
+template <typename T, int D>
+__host__ __device__ constexpr void kv_v_vec(int v, int &d, int &pos0) {
+    constexpr int E = 16 / sizeof(T), NP = 64 / (4 * E);
+    const int f = v / 64, l = v % 64;
+    d = 16 * (f / NP) + l % 16;
+    pos0 = (4 * (f % NP) + l / 16) * E;
+}
+template <typename T, int D>
+constexpr bool kv_layout_is_bijective() {
+    // every element lands once, and the vector inverses agree
+    constexpr int E = 16 / sizeof(T);
+    bool seen[2 * 64 * D] = {};
+    for (int t = 0; t < 64; ++t)
+        for (int d = 0; d < D; ++d) {
+            const int a = kv_k_off<T, D>(t, d), b = kv_v_off<T, D>(t, d);
+            if (a < 0 || a >= 64 * D || b < 64 * D || b >= 128 * D || seen[a] || seen[b]) return false;
+            seen[a] = seen[b] = true;
+        }
+    for (int v = 0; v < 64 * D / E; ++v) {
+        int t = 0, d0 = 0, dd = 0, p0 = 0;
+        kv_k_vec<T, D>(v, t, d0);
+        kv_v_vec<T, D>(v, dd, p0);
+        if (kv_k_off<T, D>(t, d0) != v * E) return false;
+        if (kv_v_off<T, D>(vt_token_at(p0), dd) != 64 * D + v * E) return false;
+    }
+    return true;
+}
+static_assert(kv_layout_is_bijective<uint16_t, 64>() && kv_layout_is_bijective<uint16_t, 128>() &&
+                  kv_layout_is_bijective<float, 64>() && kv_layout_is_bijective<float, 128>(),
+              "block layout");
+
 // Total order used by every selection: a higher score ranks first, an equal
 // score ranks the lower block id first. Keys compare as unsigned integers.
 // -0 and +0 are equal scores, so -0 is mapped to +0 first (the id decides).

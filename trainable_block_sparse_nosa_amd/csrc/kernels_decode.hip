@@ -181,12 +181,23 @@ struct BlockRegs {
     int valid;            // tokens of this block that exist (0: no block)
 };
 
-template <int D>
+// One 16-byte operand vector; NT marks the load non-temporal (streamed once:
+// the lines are not kept in the caches).
+template <bool NT>
+__device__ __forceinline__ bf16x8 load_frag(const bf16_t *p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(p));
+    else return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+// The block's K and V^T fragments (the block layout in common.h: fragment f,
+// lane l at 16 bytes (64 f + l)), so each load instruction of the wave reads
+// 1 KiB of whole cache lines.
+template <int D, bool NT>
 __device__ __forceinline__ void load_block(BlockRegs<D> &br, const bf16_t *blk, const float *eb,
                                            int valid, int col, int grp) {
     constexpr int S = 64, KS = D / 32, DT = D / 16;
-    const bf16_t *Kt = blk;          // [64][D]
-    const bf16_t *Vt = blk + S * D;  // [D][64], token order vt_token_at
+    const bf16_t *Kt = blk + 8 * (col + 16 * grp);  // K fragment t KS + s
+    const bf16_t *Vt = Kt + S * D;                  // V^T fragment 2 dt + s
     // eviction scores first: the QK^T MFMAs and the softmax then wait only for
     // the K loads (waits are in issue order), not for V as well
 #pragma unroll
@@ -194,13 +205,11 @@ __device__ __forceinline__ void load_block(BlockRegs<D> &br, const bf16_t *blk, 
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            br.k[t][s] = *reinterpret_cast<const bf16x8 *>(Kt + (16 * t + col) * D + 32 * s + 8 * grp);
+        for (int s = 0; s < KS; ++s) br.k[t][s] = load_frag<NT>(Kt + 512 * (t * KS + s));
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-            br.v[dt][s] = *reinterpret_cast<const bf16x8 *>(Vt + (16 * dt + col) * S + 32 * s + 8 * grp);
+        for (int s = 0; s < 2; ++s) br.v[dt][s] = load_frag<NT>(Vt + 512 * (2 * dt + s));
     br.valid = valid;
 }
 
@@ -290,7 +299,7 @@ __device__ __forceinline__ void attend_block(const BlockRegs<D> &br, const bf16x
     }
 }
 
-template <int D, int G>
+template <int D, int G, bool NT>
 __global__ void __launch_bounds__(64 * WAVES)
 decode_mfma_kernel(Dims dm, DecodeArgs a) {
     static_assert(G <= 16, "the group is one 16-wide MFMA tile");
@@ -334,7 +343,7 @@ decode_mfma_kernel(Dims dm, DecodeArgs a) {
         const bf16_t *blk;
         int bid, valid;
         if (resolve_entry<bf16_t>(a, sv, e, cnt_e, r, BE, blk, bid, valid)) {
-            load_block<D>(br, blk, er + (int64_t)bid * S, valid, col, grp);
+            load_block<D, NT>(br, blk, er + (int64_t)bid * S, valid, col, grp);
             // keep every load of the block ahead of the math: without this the
             // scheduler interleaves loads with MFMAs to save registers and the
             // block is no longer in flight at once
@@ -496,25 +505,16 @@ struct PrefillStage {
 };
 
 // Issue the global loads of one block (chunk x = tid + j NT is lane x % 64 of
-// fragment x / 64).
+// fragment x / 64). The stored block is in this fragment order already (the
+// layout in common.h): the loads are one contiguous 16-byte vector per thread.
 template <int D, int NT>
 __device__ __forceinline__ void prefill_load(PrefillStage<D, NT> &st, const bf16_t *blk,
                                              const float *eb, int tid) {
-    constexpr int S = 64, KS = D / 32, NF = PrefillTile<D>::NF;
+    constexpr int NF = PrefillTile<D>::NF;
 #pragma unroll
     for (int j = 0; j < PrefillStage<D, NT>::CH; ++j) {
         const int x = tid + j * NT;
-        if (NF * 64 % NT == 0 || x < NF * 64) {
-            const int f = x / 64, l = x % 64, col = l % 16, grp = l / 16;
-            const bf16_t *src;
-            if (f < 4 * KS) {
-                src = blk + (16 * (f / KS) + col) * D + 32 * (f % KS) + 8 * grp;
-            } else {
-                const int fv = f - 4 * KS;
-                src = blk + S * D + (16 * (fv / 2) + col) * S + 32 * (fv % 2) + 8 * grp;
-            }
-            st.v[j] = *reinterpret_cast<const bf16x8 *>(src);
-        }
+        if (NF * 64 % NT == 0 || x < NF * 64) st.v[j] = *reinterpret_cast<const bf16x8 *>(blk + 8 * x);
     }
     if (tid < 16) st.e = *reinterpret_cast<const f32x4 *>(eb + 4 * tid);
 }
@@ -872,13 +872,17 @@ decode_valu_kernel(Dims dm, DecodeArgs a) {
         if (!resolve_entry<T>(a, sv, e, cnt_e, r, BE, blk, bid, valid))
             continue;  // uniform over the workgroup
         __syncthreads();  // the previous block's readers are done with LDS
+        // the block's 16-byte vectors in stored order (coalesced), each to its
+        // place in the row-major LDS tiles (the layout in common.h)
         constexpr int KV_VEC = S * D / EPV;
         for (int v = tid; v < KV_VEC; v += 256) {
-            const int row = v / (D / EPV), c = (v % (D / EPV)) * EPV;
+            int row, c;
+            kv_k_vec<T, D>(v, row, c);
             *reinterpret_cast<uint4 *>(Ks + row * KP + c) = reinterpret_cast<const uint4 *>(blk)[v];
         }
         for (int v = tid; v < KV_VEC; v += 256) {
-            const int row = v / (S / EPV), c = (v % (S / EPV)) * EPV;
+            int row, c;
+            kv_v_vec<T, D>(v, row, c);
             uint4 x = reinterpret_cast<const uint4 *>(blk + S * D)[v];
             if (valid < S) {
                 // value slots of tokens from `valid` on (a partly filled
@@ -989,16 +993,33 @@ hipError_t launch_decode_valu(const Dims &dm, const DecodePlan &pl, const Decode
     return hipGetLastError();
 }
 
+// Non-temporal K/V loads when a launch reads more KV than the 256 MB
+// Infinity Cache holds: nothing it reads survives to the next step there
+// anyway, and streamed whole-line fragments then arrive faster. Measured on
+// the 64k workload (256 rows x 129 blocks, 1.08 GB per launch): 162 against
+// 182 us. On the 32k workload (64 rows x 65 blocks, 136 MB, which the
+// Infinity Cache keeps from step to step) the cached loads are faster: 23.0
+// against 24.2 us.
+constexpr int64_t NT_MIN_BYTES = (int64_t)256 << 20;
+
+template <int D, int G, bool NT>
+hipError_t launch_decode_mfma_nt(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
+                                 hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    const dim3 grid(pl.n_chunks, dm.rows), block(64 * WAVES);
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL((decode_mfma_kernel<D, G, NT>), grid, block, 0, st, ev0, ev1, 0, dm, a);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<D, G, NT>), grid, block, 0, st, dm, a);
+    return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t launch_decode_mfma(const Dims &dm, const DecodePlan &pl, const DecodeArgs &a,
                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     if (pl.n_chunks == 0) return hipSuccess;
-    const dim3 grid(pl.n_chunks, dm.rows), block(64 * WAVES);
-    if (ev0 || ev1)
-        hipExtLaunchKernelGGL((decode_mfma_kernel<D, G>), grid, block, 0, st, ev0, ev1, 0, dm, a);
-    else
-        hipLaunchKernelGGL((decode_mfma_kernel<D, G>), grid, block, 0, st, dm, a);
-    return hipGetLastError();
+    const int64_t kv_bytes = (int64_t)dm.rows * (a.list_len + a.with_newest) * (2 * 64 * D) * 2;
+    return kv_bytes > NT_MIN_BYTES ? launch_decode_mfma_nt<D, G, true>(dm, pl, a, st, ev0, ev1)
+                                   : launch_decode_mfma_nt<D, G, false>(dm, pl, a, st, ev0, ev1);
 }
 
 template <typename T, int D, int G>

@@ -75,10 +75,6 @@ __device__ __forceinline__ TK pooled_mean_of(Get get) {
     if constexpr (std::is_same_v<TK, float>) return (float)mean;
     else return bf16_rne_from_double(mean);
 }
-template <typename T, typename TK>
-__device__ __forceinline__ TK pooled_mean(const T *k, int stride) {
-    return pooled_mean_of<T, TK>([&](int u) { return k[u * stride]; });
-}
 
 // Write the pooled keys of block j of row r, run by a whole workgroup of 256
 // threads: mean_at(i, d) gives dimension d of sub-block i's mean in the pooled
@@ -172,8 +168,9 @@ pool_kernel(Dims dm, const T *__restrict__ kv, int64_t kv_row_blocks, int kv_fir
     }
     const T *K = kv + ((int64_t)r * kv_row_blocks + src) * (int64_t)(2 * S * D);
     static_assert(V > 0, "pooled-key vector width");
-    pool_write<T, TK, D>(dm, kbar, r, j,
-                         [&](int i, int d) { return pooled_mean<T, TK>(K + (i * SUB) * D + d, D); });
+    pool_write<T, TK, D>(dm, kbar, r, j, [&](int i, int d) {
+        return pooled_mean_of<T, TK>([&](int u) { return K[kv_k_off<T, D>(i * SUB + u, d)]; });
+    });
     if (threadIdx.x < M) {
         const float *e = e_tok + (int64_t)r * e_stride + (int64_t)j * S + threadIdx.x * SUB;
         float s = 0.f;
@@ -1238,7 +1235,7 @@ fetch_kernel(const u32x4 *__restrict__ src, int64_t src_row_blocks, const int32_
 // row, for the token `tok` of every row:
 //  * split: the row's G query heads of the fused projection output go to
 //    q_out; its key and value heads go into token slot tok % 64 of a block of
-//    the block-unit KV buffer (K row, V^T column in the stored order);
+//    the block-unit KV buffer (the layout in common.h);
 //  * eviction head: e = x . w_g + b_g (float32 sum), written to e_tok;
 //  * when the token completes its block: the block's sub-block key means
 //    (pooled_mean_of, the same arithmetic and order as pool_kernel) and its
@@ -1273,8 +1270,8 @@ ingest_kernel(Dims dm, const T *__restrict__ qkv, const T *__restrict__ x,
     for (int d = tid; d < D; d += blockDim.x) {
         const T kval = src[(int64_t)(dm.Hq + g) * D + d];
         const T vval = src[(int64_t)(dm.Hq + dm.Hkv + g) * D + d];
-        blk[pos * D + d] = kval;
-        blk[S * D + d * S + vt_pos_of(pos)] = vval;
+        blk[kv_k_off<T, D>(pos, d)] = kval;
+        blk[kv_v_off<T, D>(pos, d)] = vval;
         knew[d] = kval;
     }
     // eviction head: 16-byte vectors when the rows allow them, else elements
@@ -1313,7 +1310,7 @@ ingest_kernel(Dims dm, const T *__restrict__ qkv, const T *__restrict__ x,
     pool_write<T, TK, D>(dm, kbar, r, j, [&](int i, int d) {
         return pooled_mean_of<T, TK>([&](int u) {
             const int t = 16 * i + u;
-            return t == S - 1 ? knew[d] : blk[t * D + d];
+            return t == S - 1 ? knew[d] : blk[kv_k_off<T, D>(t, d)];
         });
     });
     if (tid < M) {
@@ -1334,9 +1331,9 @@ ingest_kernel(Dims dm, const T *__restrict__ qkv, const T *__restrict__ x,
 
 // ---------------------------------------------------------------------------
 // Append: the newest token of every row enters token slot `pos` of block
-// `block` of a KV buffer: its key as row pos of the K tile, its value as
-// column vt_pos_of(pos) of the V^T tile. One workgroup per row, thread d
-// writes dimension d.
+// `block` of a KV buffer: its key as token pos of the K tile, its value as
+// column vt_pos_of(pos) of the V^T tile (the layout in common.h). One
+// workgroup per row, thread d writes dimension d.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ void __launch_bounds__(D)
@@ -1351,8 +1348,8 @@ append_kernel(Dims dm, const T *__restrict__ k_new, const T *__restrict__ v_new,
         block = sv.n_cand;
     }
     T *blk = kv + ((int64_t)r * kv_row_blocks + block) * (int64_t)(2 * S * D);
-    blk[pos * D + d] = k_new[(int64_t)r * D + d];
-    blk[S * D + d * S + vt_pos_of(pos)] = v_new[(int64_t)r * D + d];
+    blk[kv_k_off<T, D>(pos, d)] = k_new[(int64_t)r * D + d];
+    blk[kv_v_off<T, D>(pos, d)] = v_new[(int64_t)r * D + d];
 }
 
 // ---------------------------------------------------------------------------

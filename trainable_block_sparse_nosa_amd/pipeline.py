@@ -31,13 +31,25 @@ SUB_BLOCK = 16
 # positions 8j..8j+7 hold tokens 4j..4j+3 and 16+4j..16+4j+3.
 VT_TOKEN_AT = np.array([32 * (p // 32) + 16 * ((p % 8) // 4) + 4 * ((p % 32) // 8) + p % 4
                         for p in range(BLOCK)])
+VT_POS_OF = np.argsort(VT_TOKEN_AT)
+
+
+def _geometry(D: int, itemsize: int):
+    e = 16 // itemsize  # elements per 16-byte vector
+    if D % (4 * e) or D % 16:
+        raise ValueError("head_dim must be a multiple of 16 and of 4 vectors")
+    return e, D // (4 * e), BLOCK // (4 * e), D // 16
 
 
 def pack_blocks(K: np.ndarray, V: np.ndarray, n_blocks: int) -> np.ndarray:
-    """Block-unit layout of one row: [n_blocks, 2*64*D] with, per block, the K
-    tile [64][D] followed by the V tile transposed, [D][64], its positions in
-    the VT_TOKEN_AT token order. Tokens beyond the input are zero. Works on
-    float32 or bfloat16-bit (uint16) arrays."""
+    """Block-unit layout of one row (include/nosa.h): [n_blocks, 2*64*D] with,
+    per block, the K tile and then the V^T tile (positions in the VT_TOKEN_AT
+    token order), both as 1 KiB fragments of 16-byte vectors: K fragment
+    t*NS + s, vector col + 16 grp holds token 16t + col, dimensions
+    (4s + grp)E .. + E-1; V^T fragment dt*NP + s, vector col + 16 grp holds
+    dimension 16dt + col, positions (4s + grp)E .. + E-1 (E elements per
+    vector, NS = D/4E, NP = 64/4E). Tokens beyond the input are zero. Works
+    on float32 or bfloat16-bit (uint16) arrays."""
     n, D = K.shape
     pad = n_blocks * BLOCK - n
     if pad < 0:
@@ -45,10 +57,39 @@ def pack_blocks(K: np.ndarray, V: np.ndarray, n_blocks: int) -> np.ndarray:
     if pad:
         K = np.concatenate([K, np.zeros((pad, D), K.dtype)])
         V = np.concatenate([V, np.zeros((pad, D), V.dtype)])
-    Kb = K.reshape(n_blocks, BLOCK * D)
-    Vb = V.reshape(n_blocks, BLOCK, D)[:, VT_TOKEN_AT, :]
-    Vt = Vb.transpose(0, 2, 1).reshape(n_blocks, D * BLOCK)
-    return np.ascontiguousarray(np.concatenate([Kb, Vt], axis=1))
+    e, ns, npos, dt = _geometry(D, K.dtype.itemsize)
+    # K[tok = 16t + col][d = (4s + grp)e + x] -> (t, s, grp, col, x)
+    Kf = K.reshape(n_blocks, 4, 16, ns, 4, e).transpose(0, 1, 3, 4, 2, 5)
+    # V^T[d = 16dt + col][pos = (4s + grp)e + x] -> (dt, s, grp, col, x)
+    Vp = V.reshape(n_blocks, BLOCK, D)[:, VT_TOKEN_AT, :]
+    Vf = Vp.reshape(n_blocks, npos, 4, e, dt, 16).transpose(0, 4, 1, 2, 5, 3)
+    return np.ascontiguousarray(np.concatenate(
+        [Kf.reshape(n_blocks, BLOCK * D), Vf.reshape(n_blocks, BLOCK * D)], axis=1))
+
+
+def unpack_blocks(packed: np.ndarray, D: int):
+    """The inverse of pack_blocks: (K, V), each [n_blocks * 64, D], from
+    packed [n_blocks, 2*64*D]."""
+    packed = np.asarray(packed)
+    n = packed.shape[0]
+    e, ns, npos, dt = _geometry(D, packed.dtype.itemsize)
+    K = packed[:, :BLOCK * D].reshape(n, 4, ns, 4, 16, e).transpose(0, 1, 4, 2, 3, 5)
+    Vp = packed[:, BLOCK * D:].reshape(n, dt, npos, 4, 16, e).transpose(0, 2, 3, 5, 1, 4)
+    V = Vp.reshape(n, BLOCK, D)[:, VT_POS_OF, :]
+    return K.reshape(n * BLOCK, D), V.reshape(n * BLOCK, D)
+
+
+def block_offsets(D: int, itemsize: int):
+    """Element offsets inside one packed block of K[tok][d] and of V[tok][d]:
+    two int64 arrays [64, D] (the formulas of include/nosa.h)."""
+    e, ns, npos, _ = _geometry(D, itemsize)
+    tok = np.arange(BLOCK)[:, None]
+    d = np.arange(D)[None, :]
+    k_off = (((tok // 16) * ns + d // (4 * e)) * 64 + tok % 16 + 16 * ((d // e) % 4)) * e + d % e
+    p = VT_POS_OF[tok]
+    v_off = BLOCK * D + (((d // 16) * npos + p // (4 * e)) * 64 + d % 16
+                         + 16 * ((p // e) % 4)) * e + p % e
+    return k_off.astype(np.int64), v_off.astype(np.int64)
 
 
 def torch_dtype(dtype: int):
