@@ -341,3 +341,22 @@ def test_block_layout(D, dt):
                 at = 64 * D + 8 * (64 * (2 * dtile + s) + lane)
                 d, p0 = 16 * dtile + lane % 16, 32 * s + 8 * (lane // 16)
                 np.testing.assert_array_equal(P[0][at:at + 8], V[VT_TOKEN_AT[p0:p0 + 8], d])
+
+
+def test_block_offsets_rejects_bad_arguments():
+    """nosa_block_offsets is host only: NULL arrays and unsupported shapes come
+    back as errors before anything is written."""
+    import numpy as np
+    from trainable_block_sparse_nosa_amd import _lib as L
+    lib = L.lib()
+    good = np.zeros(64 * 128, np.int64)
+    sh = _shape()
+    assert lib.nosa_block_offsets(ctypes.byref(sh), None, good.ctypes.data) == L.NOSA_ERR_INVALID_ARGUMENT
+    assert lib.nosa_block_offsets(ctypes.byref(sh), good.ctypes.data, None) == L.NOSA_ERR_INVALID_ARGUMENT
+    bad = _shape(head_dim=96)
+    k = np.full(64 * 96, -7, np.int64)
+    v = np.full(64 * 96, -7, np.int64)
+    assert lib.nosa_block_offsets(ctypes.byref(bad), k.ctypes.data, v.ctypes.data) == L.NOSA_ERR_UNSUPPORTED
+    assert (k == -7).all() and (v == -7).all()
+    with pytest.raises(L.NosaError):
+        L.nosa_block_offsets(_shape(head_dim=128, dtype=L.NOSA_F32))   # float32 supports D = 64
