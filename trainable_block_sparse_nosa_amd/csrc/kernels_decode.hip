@@ -997,9 +997,10 @@ hipError_t launch_decode_valu(const Dims &dm, const DecodePlan &pl, const Decode
 // Infinity Cache holds: nothing it reads survives to the next step there
 // anyway, and streamed whole-line fragments then arrive faster. Measured on
 // the 64k workload (256 rows x 129 blocks, 1.08 GB per launch): 162 against
-// 182 us. On the 32k workload (64 rows x 65 blocks, 136 MB, which the
-// Infinity Cache keeps from step to step) the cached loads are faster: 23.0
-// against 24.2 us.
+// 182 us; on the 32-layer offload step (512 rows x 65 cache slots per layer):
+// 158 against 187 us. On the 32k workload (64 rows x 65 blocks, 136 MB, which
+// the Infinity Cache keeps from step to step) the cached loads are faster:
+// 23.0 against 24.2 us.
 constexpr int64_t NT_MIN_BYTES = (int64_t)256 << 20;
 
 template <int D, int G, bool NT>

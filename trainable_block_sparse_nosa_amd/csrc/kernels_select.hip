@@ -660,8 +660,8 @@ struct ScoresFused {
 // product. The wave takes the TPI tiles from t0 on in each of its passes
 // (t0 = t_first, t_first + t_stride, ... below t_end), all their loads in
 // flight together; block j's score goes to lds[j] and/or out[j] (either may
-// be null).
-template <int D, int G, int TPI>
+// be null). NT makes the pooled-key loads non-temporal.
+template <int D, int G, int TPI, bool NT = false>
 __device__ __forceinline__ void mfma_block_scores(const Dims &dm, const bf16_t *qg,
                                                   const bf16_t *kbar, int r, int n_cand,
                                                   int t_first, int t_stride, int t_end,
@@ -689,9 +689,10 @@ __device__ __forceinline__ void mfma_block_scores(const Dims &dm, const bf16_t *
         for (int u = 0; u < TPI; ++u) {
             const int sb = 16 * (t0 + u) + col;
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-                a[u][s] = sb < nsb ? kb[((int64_t)(t0 + u) * (D / 8) + 4 * s + grp) * 16 + col]
-                                   : bf16x8{};
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 *p = kb + ((int64_t)(t0 + u) * (D / 8) + 4 * s + grp) * 16 + col;
+                a[u][s] = sb >= nsb ? bf16x8{} : (NT ? __builtin_nontemporal_load(p) : *p);
+            }
         }
 #pragma unroll
         for (int u = 0; u < TPI; ++u) {
@@ -939,13 +940,19 @@ __device__ void cert_refine(const Dims &dm, const CertArgs &ca, int r, int n_can
 // grid covers the row in one pass. Swept on the 32k workload (64 rows x 512
 // candidates): 8 waves of one tile 7.3 us, 4 waves of two 7.5, 4 of four
 // 7.9, 4 of eight 9.5, 8 of two 7.7, 16 of one 7.9, 16 of two 8.4. At 256
-// rows x 1024 candidates it streams the pooled keys at 6.2 TB/s.
+// rows x 1024 candidates it streams the pooled keys at 6.7 TB/s.
 // With dstep, n_cand comes from the step record and the grid is sized for the
 // capacity; chunks past the candidates exit at once.
 constexpr int SCORE_WAVES = 8;
 constexpr int SCORE_TPI = 1;
 constexpr int SCORE_TILES_PER_WG = SCORE_WAVES * SCORE_TPI;
-template <int D, int G>
+// Non-temporal pooled-key loads once a launch reads more than half of the
+// 256 MB Infinity Cache, which the step's attention reads compete for: at
+// 256 rows x 1024 candidates (268 MB) 4,505-4,513 against 4,465-4,470
+// steps/s; at 64 rows x 512 (34 MB, kept in the cache from step to step) the
+// cached loads are faster.
+constexpr int64_t SCORE_NT_MIN_BYTES = (int64_t)128 << 20;
+template <int D, int G, bool NT>
 __global__ void __launch_bounds__(64 * SCORE_WAVES)
 score_mfma_kernel(Dims dm, const bf16_t *__restrict__ q, const bf16_t *__restrict__ kbar,
                   int n_cand, float *__restrict__ s_q, const int32_t *__restrict__ dstep) {
@@ -958,8 +965,9 @@ score_mfma_kernel(Dims dm, const bf16_t *__restrict__ q, const bf16_t *__restric
     const int b = r / dm.Hkv, g = r % dm.Hkv;
     const bf16_t *qg = q + ((int64_t)b * dm.Hq + (int64_t)g * G) * D;
     const int t0 = t_begin + wave * SCORE_TPI;
-    mfma_block_scores<D, G, SCORE_TPI>(dm, qg, kbar, r, n_cand, t0, n_tiles, min(t0 + 1, n_tiles),
-                                       nullptr, s_q + (int64_t)r * dm.max_blocks);
+    mfma_block_scores<D, G, SCORE_TPI, NT>(dm, qg, kbar, r, n_cand, t0, n_tiles,
+                                           min(t0 + 1, n_tiles), nullptr,
+                                           s_q + (int64_t)r * dm.max_blocks);
 }
 
 // Independent selections in one launch (workgroup row y = blockIdx.y): y
@@ -1402,9 +1410,14 @@ hipError_t launch_score(const Dims &dm, const void *q, const void *kbar, int n_c
         // bfloat16 pooled keys (and queries): the matrix cores
         const int n_tiles = (cand + 3) / 4;
         dim3 grid((n_tiles + SCORE_TILES_PER_WG - 1) / SCORE_TILES_PER_WG, dm.rows);
-        hipLaunchKernelGGL((score_mfma_kernel<D, G>), grid, dim3(64 * SCORE_WAVES), 0, st, dm,
-                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(kbar),
-                           n_cand, s_q, dstep);
+        const bool nt = (int64_t)dm.rows * cand * 4 * D * 2 > SCORE_NT_MIN_BYTES;
+        const bf16_t *qb = static_cast<const bf16_t *>(q), *kb = static_cast<const bf16_t *>(kbar);
+        if (nt)
+            hipLaunchKernelGGL((score_mfma_kernel<D, G, true>), grid, dim3(64 * SCORE_WAVES), 0,
+                               st, dm, qb, kb, n_cand, s_q, dstep);
+        else
+            hipLaunchKernelGGL((score_mfma_kernel<D, G, false>), grid, dim3(64 * SCORE_WAVES), 0,
+                               st, dm, qb, kb, n_cand, s_q, dstep);
     } else {
         dim3 grid((4 * cand + 255) / 256, dm.rows);
         hipLaunchKernelGGL((score_kernel<T, TK, D, G>), grid, dim3(256), 0, st, dm,
