@@ -8,6 +8,7 @@ been built: there is no fallback implementation.
 from . import _lib  # noqa: F401  (loads libnosa.so or raises ImportError)
 from ._lib import NosaError  # noqa: F401
 from .hostmem import PinnedBuffer  # noqa: F401
-from .pipeline import DecodeLayer, pack_blocks  # noqa: F401
+from .pipeline import DecodeLayer, block_offsets, pack_blocks, unpack_blocks  # noqa: F401
 
-__all__ = ["DecodeLayer", "NosaError", "PinnedBuffer", "pack_blocks"]
+__all__ = ["DecodeLayer", "NosaError", "PinnedBuffer", "block_offsets", "pack_blocks",
+           "unpack_blocks"]
