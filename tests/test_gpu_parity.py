@@ -138,12 +138,19 @@ def test_parity_all_steps_all_rows(name):
             _compare_step(w, tr, t, r, res[t])
 
 
-@pytest.mark.parametrize("name", ["small_bf16", "small_offload"])
+@pytest.mark.parametrize("name", ["small_bf16", "small_offload", "d64"])
 def test_parity_valu_kernel_bf16(name):
-    """The VALU decode kernel on bf16 inputs (the default there is MFMA)."""
+    """The VALU decode kernel on bf16 inputs (the default there is MFMA); at
+    head_dim 64 too, where a block's K and V^T vectors map back to the LDS
+    tiles with two dimension groups per fragment row instead of four."""
     gh = _gpu()
     from trainable_block_sparse_nosa_amd import _lib as L
-    w = synth.WORKLOADS[name]
+    if name == "d64":
+        w = synth.WORKLOADS["small_bf16"].scaled(name="valu_bf16_d64", seed=3200, n_q_heads=6,
+                                                 n_kv_heads=2, head_dim=64, context=1300,
+                                                 steps=12)
+    else:
+        w = synth.WORKLOADS[name]
     tr = oracle_trace(w)
     inp = gh.upload(w, ov=tr.ov)
     _, res = gh.run(w, inp, list(range(w.steps)), decode_kernel=L.NOSA_DECODE_VALU)
